@@ -1,0 +1,237 @@
+"""Synthetic decode-step workloads.
+
+Each ``Case`` describes one decode step over a batch of sequences whose earlier
+tokens already sit in a paged KV cache:
+
+* ``script``: set-up operations to replay on a block manager before the step,
+  ``("add", sid, n)``, ``("fork", parent, child)``, ``("extend", sid, n)``,
+  ``("free", sid)``.  ``add``/``extend`` write the next ``n`` logical positions
+  of ``sid`` with the token rows ``rows[sid][pos]``.
+* the step itself: every sequence of ``batch`` reserves one more position
+  (``lens[b] - 1``), writes token row ``rows[sid][lens[b] - 1]`` there, then
+  attends with ``q[b]`` over all ``lens[b]`` positions.
+
+Context lengths therefore count the new token (append first, then attend).
+
+Random draws: a NumPy ``default_rng(seed)`` draws the structure in the order
+lengths -> pool permutation -> (long-context key mask) -> (sample tails); a
+``torch.Generator`` seeded from the same seed draws q, then K, then V as
+float32 normals, rounded once (round-to-nearest-even) into the KV dtype.  All
+consumers read the same stored bits.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+import torch
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+ELT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+CONFIG_NAMES = ("tiny_fp32", "llama3_8b_bf16", "opt13b_fp16", "cow_parallel_bf16",
+                "long_context_bf16")
+
+
+@dataclass
+class Case:
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    free_order: np.ndarray          # int32 [N]: order in which a fresh pool hands out blocks
+    script: list                    # set-up ops (see module docstring)
+    batch: np.ndarray               # int64 [B]: sequence ids decoded in this step
+    lens: np.ndarray                # int32 [B]: context length after the step's append
+    rows: dict                      # sid -> int64 [len]: token row of every logical position
+    q: torch.Tensor                 # [B][Hq][D] in the KV dtype
+    k_tok: torch.Tensor             # [R][Hkv][D] in the KV dtype
+    v_tok: torch.Tensor             # [R][Hkv][D] in the KV dtype
+    partition_size: int = 0         # 0 = let the library choose
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.batch.shape[0])
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def elt_bytes(self) -> int:
+        return ELT_BYTES[self.dtype]
+
+    def kv_bytes(self) -> int:
+        """Logical K+V bytes one decode step reads: sum(L) * Hkv * 2 * D * elt."""
+        return int(self.lens.astype(np.int64).sum()) * self.num_kv_heads * 2 * \
+            self.head_dim * self.elt_bytes
+
+    def new_rows(self) -> np.ndarray:
+        """Token row written by this step's append, per batch entry."""
+        return np.array([self.rows[int(s)][int(L) - 1] for s, L in zip(self.batch, self.lens)],
+                        dtype=np.int64)
+
+
+def _draw_values(seed: int, nq: tuple, nkv: tuple, dtype: str, device, q_std: float = 1.0,
+                 key_boost=None):
+    """q, K, V as float32 normals (in that order), rounded once to ``dtype``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(1_000_003 * seed + 17)
+    td = TORCH_DTYPE[dtype]
+    q = torch.randn(nq, generator=g, device=device, dtype=torch.float32)
+    if q_std != 1.0:
+        q.mul_(q_std)
+    q = q.to(td)
+    k = torch.randn(nkv, generator=g, device=device, dtype=torch.float32)
+    if key_boost is not None:
+        # key_boost: bool [R][Hkv]; the chosen key vectors are multiplied by 8
+        # (a power of two, so the rounded value is the rounded original x 8).
+        kb = torch.as_tensor(key_boost, device=device)
+        k[kb] *= 8.0
+    k = k.to(td)
+    v = torch.randn(nkv, generator=g, device=device, dtype=torch.float32).to(td)
+    return q, k, v
+
+
+def _pool_size(lens, block_size, extra_blocks=0, factor=1.2):
+    need = int(sum(-(-int(L) // block_size) for L in lens)) + extra_blocks
+    return int(math.ceil(factor * need))
+
+
+def _independent(name, seed, dtype, lens, hq, hkv, d, device, *, num_blocks=None,
+                 q_std=1.0, boost_prob=0.0, partition_size=0, bs=16, rng=None):
+    """Batch of unrelated sequences; sequence b has id b and cached lens[b]-1 tokens."""
+    lens = np.asarray(lens, dtype=np.int32)
+    if num_blocks is None:
+        num_blocks = _pool_size(lens, bs)
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(lens.astype(np.int64))])
+    R = int(offs[-1])
+    boost = None
+    if boost_prob > 0:
+        boost = rng.random((R, hkv)) < boost_prob
+    q, k, v = _draw_values(seed, (len(lens), hq, d), (R, hkv, d), dtype, device, q_std, boost)
+    rows = {b: np.arange(offs[b], offs[b + 1], dtype=np.int64) for b in range(len(lens))}
+    script = [("add", b, int(lens[b]) - 1) for b in range(len(lens))]
+    notes = {}
+    if boost is not None:
+        notes["boosted_keys"] = int(boost.sum())
+    return Case(name, dtype, hq, hkv, d, bs, int(num_blocks), free_order, script,
+                np.arange(len(lens), dtype=np.int64), lens, rows, q, k, v,
+                partition_size, notes)
+
+
+def _parallel_sampling(name, seed, dtype, n_prompts, n_samples, prompt_len, tail_max, hq, hkv,
+                       d, device, *, parked_forks=True, bs=16, rng=None):
+    """Prompts shared by n_samples forks each, plus a private tail per sample.
+
+    With ``parked_forks`` each sample whose last block is partly filled is forked
+    once more into a parked sequence that is never decoded, so that block is
+    shared (reference count 2) when the step writes into it and must be copied
+    first.  Without it no step write lands on a shared block.
+    """
+    tails = rng.integers(0, tail_max + 1, size=n_prompts * n_samples)
+    B = n_prompts * n_samples
+    lens = (prompt_len + tails + 1).astype(np.int32)
+    # unique token rows: every prompt once, then every sample's tail (+ new token)
+    prompt_base = np.arange(n_prompts, dtype=np.int64) * prompt_len
+    tail_sizes = tails + 1
+    tail_base = n_prompts * prompt_len + np.concatenate([[0], np.cumsum(tail_sizes)[:-1]])
+    R = int(n_prompts * prompt_len + tail_sizes.sum())
+    rows, script = {}, []
+    parent_id = lambda p: 100_000 + p  # noqa: E731
+    parked_id = lambda s: 200_000 + s  # noqa: E731
+    for p in range(n_prompts):
+        pid = parent_id(p)
+        rows[pid] = prompt_base[p] + np.arange(prompt_len, dtype=np.int64)
+        script.append(("add", pid, prompt_len))
+        for s in range(n_samples):
+            sid = p * n_samples + s
+            rows[sid] = np.concatenate([rows[pid], tail_base[sid] +
+                                        np.arange(tail_sizes[sid], dtype=np.int64)])
+            script.append(("fork", pid, sid))
+        script.append(("free", pid))
+    n_parked = 0
+    for sid in range(B):
+        if tails[sid] > 0:
+            script.append(("extend", sid, int(tails[sid])))
+        if parked_forks and (prompt_len + tails[sid]) % bs != 0:
+            script.append(("fork", sid, parked_id(sid)))
+            n_parked += 1
+    unique_blocks = n_prompts * (-(-prompt_len // bs)) + int(
+        sum(-(-int(L) // bs) - prompt_len // bs for L in lens))
+    num_blocks = int(math.ceil(1.2 * (unique_blocks + n_parked)))
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    q, k, v = _draw_values(seed, (B, hq, d), (R, hkv, d), dtype, device)
+    notes = {"parked_forks": n_parked, "tails": tails, "unique_blocks": unique_blocks}
+    return Case(name, dtype, hq, hkv, d, bs, num_blocks, free_order, script,
+                np.arange(B, dtype=np.int64), lens, rows, q, k, v, 0, notes)
+
+
+def make_case(name: str, seed: int | None = None, device="cpu", **kw) -> Case:
+    """One of the five decode workloads at full size."""
+    idx = CONFIG_NAMES.index(name) + 1
+    seed = idx if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if name == "tiny_fp32":
+        # 4 sequences, contexts {1,15,16,37}, 4 heads, D=64, pool of 16 blocks.
+        return _independent(name, seed, "f32", [1, 15, 16, 37], 4, 4, 64, device,
+                            num_blocks=16, rng=rng)
+    if name == "llama3_8b_bf16":
+        lens = rng.integers(256, 2048 + 1, size=64)
+        return _independent(name, seed, "bf16", lens, 32, 8, 128, device, rng=rng)
+    if name == "opt13b_fp16":
+        z = rng.standard_normal(256)
+        lens = np.clip(np.rint(600.0 * np.exp(0.9 * z)), 16, 2048).astype(np.int64)
+        return _independent(name, seed, "f16", lens, 40, 40, 128, device, q_std=0.5, rng=rng)
+    if name == "cow_parallel_bf16":
+        return _parallel_sampling(name, seed, "bf16", 32, 8, 1024, 512, 32, 8, 128, device,
+                                  parked_forks=kw.get("parked_forks", True), rng=rng)
+    if name == "long_context_bf16":
+        lens = rng.integers(32768, 131072 + 1, size=16)
+        return _independent(name, seed, "bf16", lens, 32, 8, 128, device, boost_prob=0.01,
+                            partition_size=512, rng=rng)
+    raise KeyError(name)
+
+
+def small_case(name: str, seed: int | None = None, device="cpu", **kw) -> Case:
+    """Reduced versions of the five workloads: same head shapes, dtypes and
+    length structure, sized so the fp64 oracle finishes in well under a second,
+    while still spanning several blocks, several partitions and ragged tails."""
+    idx = CONFIG_NAMES.index(name) + 1
+    seed = 100 + idx if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if name == "tiny_fp32":
+        return make_case(name, seed=1, device=device)
+    if name == "llama3_8b_bf16":
+        lens = np.concatenate([[1, 16, 17, 32], rng.integers(1, 600, size=4)])
+        return _independent(name, seed, "bf16", lens, 32, 8, 128, device, rng=rng)
+    if name == "opt13b_fp16":
+        z = rng.standard_normal(8)
+        lens = np.clip(np.rint(60.0 * np.exp(0.9 * z)), 1, 400).astype(np.int64)
+        return _independent(name, seed, "f16", lens, 40, 40, 128, device, q_std=0.5, rng=rng)
+    if name == "cow_parallel_bf16":
+        return _parallel_sampling(name, seed, "bf16", 2, 4, 64, 40, 32, 8, 128, device,
+                                  parked_forks=kw.get("parked_forks", True), rng=rng)
+    if name == "long_context_bf16":
+        lens = rng.integers(1100, 2600, size=3)
+        return _independent(name, seed, "bf16", lens, 32, 8, 128, device, boost_prob=0.05,
+                            partition_size=512, rng=rng)
+    raise KeyError(name)
+
+
+def custom_case(seed, dtype, lens, hq, hkv, d, device="cpu", *, num_blocks=None,
+                partition_size=0, q_std=1.0, boost_prob=0.0, pool_factor=1.2) -> Case:
+    """Free-form batch of independent sequences (edge cases, sweeps)."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    if num_blocks is None:
+        num_blocks = max(1, _pool_size(lens, 16, factor=pool_factor))
+    return _independent(f"custom_{dtype}_{hq}x{hkv}x{d}", seed, dtype, lens, hq, hkv, d, device,
+                        num_blocks=num_blocks, q_std=q_std, boost_prob=boost_prob,
+                        partition_size=partition_size, rng=rng)
