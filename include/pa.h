@@ -1,0 +1,240 @@
+/*
+ * pa.h — C ABI of the MI355X (gfx950) paged KV-cache library.
+ *
+ * What the library implements, from the PagedAttention pages:
+ *   - a KV cache stored as a pool of fixed-size physical blocks (16 tokens by
+ *     default), each sequence seeing its tokens as consecutive logical blocks
+ *     mapped to physical blocks through a block table, with no contiguity
+ *     needed (page 1, jisaku.com glossary "PagedAttention", section
+ *     「PagedAttentionの解決策」; page 3, abeam.tech paper review, section
+ *     「用語解説」);
+ *   - a block manager that takes one new block each time 16 tokens fill up,
+ *     returns a finished sequence's blocks to the pool, shares blocks between
+ *     forked sequences by reference count and copies a shared block only when
+ *     a write must land in it (page 2, hubblespacetelescope blog, section
+ *     「OSの知恵をGPUへ…」; page 3, sections 「KV キャッシュマネージャ」 and
+ *     「並列サンプリングやビームサーチでの共有」);
+ *   - the attention kernel that follows the block table to read a sequence's
+ *     keys and values in logical order, giving the same result as attention
+ *     over a contiguous cache (page 3, sections
+ *     「モデル構造ではなくサービング基盤の変更」 and 「よくある質問」).
+ *
+ * Conventions shared by every device call
+ * ---------------------------------------
+ * All pointers to device data are device pointers owned by the caller; the
+ * library never allocates device memory.  Device calls are asynchronous on the
+ * HIP stream passed as `stream` (a hipStream_t; NULL = the default stream) and
+ * return after the launch.  Scalar arguments are validated on the host: on a
+ * bad value the call returns an error, sets pa_last_error() and launches
+ * nothing.  Data-dependent preconditions (slot numbers, table entries, copy
+ * pairs) cannot be checked on the host; kernels check them and never access
+ * memory outside the pools: an out-of-range slot or copy pair is skipped, and a
+ * sequence whose table entry is out of range, or whose length exceeds
+ * max_context_len or max_blocks_per_seq*block_size, gets NaN outputs.
+ *
+ * Pool layout (block_size = bs = 16, x = 16 / element_bytes: 4 for fp32,
+ * 8 for fp16/bf16; Hkv = num_kv_heads, D = head_dim):
+ *   K pool: [num_blocks][Hkv][D/x][bs][x]   element (b,h,t,d) at
+ *           (((b*Hkv + h)*(D/x) + d/x)*bs + t)*x + d%x
+ *   V pool: [num_blocks][Hkv][D][bs]        element (b,h,t,d) at
+ *           ((b*Hkv + h)*D + d)*bs + t
+ * A token at logical position p of a sequence lives in physical block
+ * table[p / bs] at in-block offset t = p % bs; its slot number is
+ * table[p / bs]*bs + p % bs.
+ *
+ * Activations: q [num_seqs][Hq][D] in the KV dtype; out [num_seqs][Hq][D]
+ * float32; new tokens [num_tokens][Hkv][D] in the KV dtype; block tables int32
+ * [num_seqs][max_blocks_per_seq]; context lengths int32 [num_seqs].
+ * Grouped-query attention: G = Hq / Hkv, query head h reads KV head h / G.
+ *
+ * Thread safety: the block manager is single-owner (not thread-safe); device
+ * calls are reentrant.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,   /* bad scalar argument or null pointer              */
+  PA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head_dim 96)     */
+  PA_ERR_OUT_OF_BLOCKS = 3, /* block manager: not enough free blocks; no change */
+  PA_ERR_UNKNOWN_SEQ = 4,   /* block manager: sequence id not present           */
+  PA_ERR_SEQ_EXISTS = 5,    /* block manager: sequence id already present       */
+  PA_ERR_HIP = 6,           /* HIP runtime error while launching                */
+  PA_ERR_WORKSPACE = 7      /* decode workspace missing or too small            */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Message for the last error on the calling thread ("" if none). */
+const char* pa_last_error(void);
+/* Library version string. */
+const char* pa_version(void);
+
+/* ------------------------------------------------------------------------
+ * Host block manager (pure CPU).
+ *
+ * Free list: a LIFO stack; a fresh manager hands blocks out in free_order
+ * (a permutation of [0, num_blocks); NULL = ascending).  Released blocks
+ * (count reaching zero, in table order) go on top.  A write to position p of a
+ * sequence takes a new block when p % block_size == 0; otherwise it lands in
+ * the existing block table[p / block_size], which is first copied if its
+ * reference count is above one (the copy is reported as a (src, dst) pair and
+ * the sequence's table entry is changed to dst; the last remaining holder
+ * writes in place).  Every call either succeeds completely or changes nothing.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_bm pa_bm;
+
+typedef struct pa_bm_stats_t {
+  int32_t num_blocks;    /* pool size                                        */
+  int32_t free_blocks;   /* blocks on the free list                          */
+  int32_t used_blocks;   /* blocks with reference count > 0                  */
+  int32_t shared_blocks; /* blocks with reference count > 1                  */
+  int32_t num_seqs;      /* live sequences                                   */
+  int32_t reserved;
+  int64_t tokens;        /* sum of sequence lengths                          */
+  int64_t slack_slots;   /* sum over sequences of blocks*block_size - length */
+} pa_bm_stats_t;
+
+/* Creates a manager for num_blocks blocks of block_size tokens.  free_order
+ * (host, [num_blocks]) is copied.  *out receives the handle. */
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       pa_bm** out);
+void pa_bm_destroy(pa_bm* bm);
+
+/* New sequence with num_tokens tokens; writes their slots to slots_out
+ * (host, [num_tokens], may be NULL). */
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id, int32_t num_tokens, int64_t* slots_out);
+
+/* child shares every block of parent (reference counts +1); no block is taken. */
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id);
+
+/* Reserves the next num_tokens positions of one sequence.  slots_out (host,
+ * [num_tokens], may be NULL); cow_pairs_out (host, [1][2] at most, may be NULL
+ * only if no copy can arise) receives (src, dst) block pairs to copy before
+ * writing; *num_cow_out their count (0 or 1). */
+pa_status pa_bm_extend(pa_bm* bm, int64_t seq_id, int32_t num_tokens, int64_t* slots_out,
+                       int32_t* cow_pairs_out, int32_t* num_cow_out);
+
+/* Decode-step reservation: one more position for each of n distinct sequences,
+ * in the order given.  slots_out (host, [n]); cow_pairs_out (host, [n][2]);
+ * *num_cow_out = number of pairs written. */
+pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n, int64_t* slots_out,
+                             int32_t* cow_pairs_out, int32_t* num_cow_out);
+
+/* Releases a sequence: counts -1, blocks reaching zero return to the pool. */
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
+
+/* Block tables of n sequences into tables_out (host, [n][max_blocks], padded
+ * with -1) and lengths into lens_out (host, [n], may be NULL). */
+pa_status pa_bm_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                             int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
+
+pa_status pa_bm_seq_len(const pa_bm* bm, int64_t seq_id, int32_t* len_out);
+pa_status pa_bm_refcount(const pa_bm* bm, int32_t block_id, int32_t* count_out);
+pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out);
+
+/* ------------------------------------------------------------------------
+ * Device operations.
+ * ---------------------------------------------------------------------- */
+
+/* Writes token i's K and V (all heads, bit for bit, no conversion) into slot
+ * slot_mapping[i] of the pools (page 3, section 「KV キャッシュマネージャ」:
+ * generated tokens go into the sequence's last block).
+ *   k_new, v_new: device [num_tokens][Hkv][D]; slot_mapping: device int64
+ *   [num_tokens], -1 = skip; slots outside [0, num_blocks*block_size) skipped.
+ * Supported: block_size 16, head_dim a multiple of 16 in [16, 256]. */
+pa_status pa_cache_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                          const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          pa_dtype dtype, void* stream);
+
+/* Copy-on-write: for each pair (src, dst) of block_pairs (device int32
+ * [num_pairs][2]), block dst := block src in both pools, all heads, bit for
+ * bit (page 3, section 「用語解説」, Copy-on-Write).  Pairs run concurrently: no
+ * dst may equal another pair's src or dst.  Out-of-range pairs are skipped. */
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, pa_dtype dtype, void* stream);
+
+/* Partition size (tokens) pa_decode uses for these arguments: the value passed
+ * if nonzero (a multiple of block_size), else the library's choice.  Returns 0
+ * for invalid arguments. */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size, pa_dtype dtype);
+
+/* Device workspace bytes pa_decode needs for these arguments (0 when every
+ * sequence fits in one partition).  Returns 0 for invalid arguments. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size, pa_dtype dtype);
+
+/* Decode attention over a paged cache: for each sequence b (length
+ * L = context_lens[b]) and query head h,
+ *   out[b][h] = softmax_t(scale * q[b][h] . K_b[t]) weighted sum of V_b[t],
+ * t in [0, L), where K_b/V_b are KV head h/G of the tokens reached through
+ * block_tables[b] in logical order; accumulation in fp32.  L = 0 gives zeros.
+ * Contexts longer than one partition are split into partitions whose partial
+ * (max, sum, weighted V) are merged with a log-sum-exp reduction.
+ *   out: device float [num_seqs][Hq][D].
+ *   workspace: device, at least pa_decode_workspace_bytes(...) bytes,
+ *   exclusively owned by this call until it completes on `stream`.
+ *   max_context_len: upper bound of context_lens (sizes the launch).
+ * Supported: block_size 16; head_dim 64 or 128; Hq a multiple of Hkv with
+ * G = Hq/Hkv <= 16.  fp16/bf16 run on the matrix cores, fp32 on plain FMAs;
+ * setting the environment variable PA_DECODE_KERNEL=generic makes fp16/bf16
+ * use the plain-FMA kernel too (read on every call). */
+pa_status pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, float scale, int32_t partition_size,
+                    pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two phases of pa_decode, same arguments and preconditions:
+ *   pa_decode_partial: the partition kernel.  Sequences that fit in one
+ *     partition get their final out rows; longer ones leave per-partition
+ *     partials (running max, running sum, weighted V sum) in the workspace.
+ *   pa_decode_merge: the log-sum-exp merge of those partials into out (no
+ *     launch when every sequence fits in one partition).
+ * pa_decode(...) == pa_decode_partial(...) then pa_decode_merge(...) on the
+ * same stream.  Separately, they let a caller time the partition pass or
+ * combine partials produced elsewhere (e.g. a context split across devices). */
+pa_status pa_decode_partial(float* out, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                            int32_t partition_size, pa_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+pa_status pa_decode_merge(float* out, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                          int32_t partition_size, pa_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Reassembles the logically contiguous cache through the block tables:
+ * k_out/v_out device [num_seqs][Hkv][max_context_len][D] in the KV dtype,
+ * positions >= context_lens[b] zero-filled.  Uses the same table walk as
+ * pa_decode; meant for checks and for handing a sequence to dense code. */
+pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_context_len, pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

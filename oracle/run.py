@@ -44,17 +44,18 @@ def run_script(am: AllocatorModel, script, rows, on_write=None, on_copy=None):
             raise ValueError(op)
 
 
-def run_case(case, with_pools=True, decode=True):
+def run_case(case, with_pools=True, decode=True, pool_fill=0):
     """Oracle results for one decode step.
 
     Returns a dict with tables, lens, step slots, step CoW pairs, and (when
     requested) the final pools (stored bits) and the fp64 output [B][Hq][D].
+    ``pool_fill`` is the bit pattern unused pool slots start with.
     """
     am = AllocatorModel(case.num_blocks, case.block_size, case.free_order)
     res = {}
     if with_pools:
         kp, vp = new_pools(case.num_blocks, case.num_kv_heads, case.head_dim, case.block_size,
-                           case.dtype)
+                           case.dtype, fill=pool_fill)
         kb = bits_of(case.k_tok, case.dtype)
         vb = bits_of(case.v_tok, case.dtype)
 

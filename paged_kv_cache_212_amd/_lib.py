@@ -1,0 +1,88 @@
+"""ctypes binding of ``libpa212.so`` (declared in ``include/pa.h``).
+
+Argument marshalling only: every computation happens in the library.  Loading
+fails loudly if the library has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa212.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OUT_OF_BLOCKS = 0, 1, 2, 3
+PA_ERR_UNKNOWN_SEQ, PA_ERR_SEQ_EXISTS, PA_ERR_HIP, PA_ERR_WORKSPACE = 4, 5, 6, 7
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
+                3: "PA_ERR_OUT_OF_BLOCKS", 4: "PA_ERR_UNKNOWN_SEQ", 5: "PA_ERR_SEQ_EXISTS",
+                6: "PA_ERR_HIP", 7: "PA_ERR_WORKSPACE"}
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+
+
+class PAError(RuntimeError):
+    def __init__(self, code: int, fn: str, msg: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class BmStats(C.Structure):
+    _fields_ = [("num_blocks", C.c_int32), ("free_blocks", C.c_int32),
+                ("used_blocks", C.c_int32), ("shared_blocks", C.c_int32),
+                ("num_seqs", C.c_int32), ("reserved", C.c_int32),
+                ("tokens", C.c_int64), ("slack_slots", C.c_int64)]
+
+
+_i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+_p_i32, _p_i64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
+
+# name -> (restype, argtypes); every symbol include/pa.h declares.
+SIGNATURES = {
+    "pa_last_error": (C.c_char_p, []),
+    "pa_version": (C.c_char_p, []),
+    "pa_bm_create": (C.c_int, [_i32, _i32, _p_i32, C.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_add_seq": (C.c_int, [_vp, _i64, _i32, _p_i64]),
+    "pa_bm_fork": (C.c_int, [_vp, _i64, _i64]),
+    "pa_bm_extend": (C.c_int, [_vp, _i64, _i32, _p_i64, _p_i32, _p_i32]),
+    "pa_bm_append_slots": (C.c_int, [_vp, _p_i64, _i32, _p_i64, _p_i32, _p_i32]),
+    "pa_bm_free_seq": (C.c_int, [_vp, _i64]),
+    "pa_bm_block_tables": (C.c_int, [_vp, _p_i64, _i32, _i32, _p_i32, _p_i32]),
+    "pa_bm_seq_len": (C.c_int, [_vp, _i64, _p_i32]),
+    "pa_bm_refcount": (C.c_int, [_vp, _i32, _p_i32]),
+    "pa_bm_stats": (C.c_int, [_vp, C.POINTER(BmStats)]),
+    "pa_cache_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int,
+                                  _vp]),
+    "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
+    "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, C.c_int]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, C.c_int]),
+    "pa_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                            _i32, _i32, _f32, _i32, C.c_int, _vp, _sz, _vp]),
+    "pa_decode_partial": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _f32, _i32, C.c_int, _vp, _sz, _vp]),
+    "pa_decode_merge": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _i32, _f32, _i32, C.c_int, _vp, _sz, _vp]),
+    "pa_gather_kv": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, C.c_int, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              f"`python -m paged_kv_cache_212_amd.build`")
+        h = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(h, name)
+            f.restype, f.argtypes = res, args
+        _lib = h
+    return _lib
+
+
+def check(status: int, fn: str):
+    if status != PA_OK:
+        raise PAError(status, fn, lib().pa_last_error().decode())

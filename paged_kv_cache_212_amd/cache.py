@@ -1,0 +1,114 @@
+"""A paged KV cache on one GPU: device pools plus the host block manager, and
+one decode step through the library (reserve -> copy-on-write -> append ->
+attend)."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import ops
+from .block_manager import BlockManager
+
+BLOCK_SIZE = ops.BLOCK_SIZE
+
+
+@dataclass
+class StepPlan:
+    """Host-side reservation for one decode step, with device copies of its arrays."""
+    seq_ids: np.ndarray
+    slots: np.ndarray          # int64 [B]
+    cows: np.ndarray           # int32 [n][2]
+    tables: np.ndarray         # int32 [B][max_blocks]
+    lens: np.ndarray           # int32 [B]
+    max_context_len: int
+    d_slots: torch.Tensor
+    d_cows: torch.Tensor
+    d_tables: torch.Tensor
+    d_lens: torch.Tensor
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+                 device="cuda", free_order=None, fill=None):
+        self.bm = BlockManager(num_blocks, BLOCK_SIZE, free_order)
+        self.k_pool, self.v_pool = ops.new_pools(num_blocks, num_kv_heads, head_dim, dtype,
+                                                 device, fill)
+        self.num_blocks, self.num_kv_heads, self.head_dim = num_blocks, num_kv_heads, head_dim
+        self.dtype, self.device = dtype, torch.device(device)
+
+    def _d(self, a: np.ndarray) -> torch.Tensor:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
+
+    # -- sequence set-up ----------------------------------------------------
+    def write(self, slots: np.ndarray, k: torch.Tensor, v: torch.Tensor):
+        if len(slots):
+            ops.cache_append(self.k_pool, self.v_pool, k.contiguous(), v.contiguous(),
+                             self._d(slots.astype(np.int64)))
+
+    def copy(self, pairs: np.ndarray):
+        if len(pairs):
+            ops.copy_blocks(self.k_pool, self.v_pool, self._d(pairs.astype(np.int32)))
+
+    def add_seq(self, seq_id: int, k: torch.Tensor, v: torch.Tensor):
+        slots = self.bm.add_seq(seq_id, k.shape[0])
+        self.write(slots, k, v)
+        return slots
+
+    def extend(self, seq_id: int, k: torch.Tensor, v: torch.Tensor):
+        slots, cows = self.bm.extend(seq_id, k.shape[0])
+        self.copy(cows)
+        self.write(slots, k, v)
+        return slots, cows
+
+    def fork(self, parent: int, child: int):
+        self.bm.fork(parent, child)
+
+    def free(self, seq_id: int):
+        self.bm.free_seq(seq_id)
+
+    def replay(self, script, rows, k_tok: torch.Tensor, v_tok: torch.Tensor):
+        """Runs set-up ops ("add", sid, n) / ("extend", sid, n) / ("fork", p, c) /
+        ("free", sid); written tokens are rows[sid][pos] of k_tok / v_tok."""
+        for op in script:
+            if op[0] == "add":
+                _, sid, n = op
+                idx = torch.as_tensor(rows[sid][:n], device=k_tok.device)
+                self.add_seq(sid, k_tok.index_select(0, idx), v_tok.index_select(0, idx))
+            elif op[0] == "extend":
+                _, sid, n = op
+                start = self.bm.seq_len(sid)
+                idx = torch.as_tensor(rows[sid][start:start + n], device=k_tok.device)
+                self.extend(sid, k_tok.index_select(0, idx), v_tok.index_select(0, idx))
+            elif op[0] == "fork":
+                self.fork(op[1], op[2])
+            elif op[0] == "free":
+                self.free(op[1])
+            else:
+                raise ValueError(op)
+
+    # -- decode step ----------------------------------------------------------
+    def plan_step(self, seq_ids, max_blocks: int | None = None) -> StepPlan:
+        """Reserve one position per sequence and export the tables (host work)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        slots, cows = self.bm.append_slots(ids)
+        if max_blocks is None:
+            max_blocks = max([1] + [-(-self.bm.seq_len(int(s)) // BLOCK_SIZE) for s in ids])
+        tables, lens = self.bm.block_tables(ids, max_blocks)
+        return StepPlan(ids, slots, cows, tables, lens, int(lens.max(initial=0)),
+                        self._d(slots), self._d(cows.reshape(-1, 2)), self._d(tables),
+                        self._d(lens))
+
+    def step(self, plan: StepPlan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+             out: torch.Tensor | None = None, scale=None, partition_size: int = 0,
+             workspace=None, stream=None):
+        """Copy-on-write, append the new tokens, then decode attention (all on device)."""
+        if plan.cows.shape[0]:
+            ops.copy_blocks(self.k_pool, self.v_pool, plan.d_cows, stream)
+        ops.cache_append(self.k_pool, self.v_pool, k_new, v_new, plan.d_slots, stream)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        ops.decode(out, q, self.k_pool, self.v_pool, plan.d_tables, plan.d_lens,
+                   plan.max_context_len, scale, partition_size, workspace, stream)
+        return out

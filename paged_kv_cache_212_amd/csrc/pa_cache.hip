@@ -1,0 +1,214 @@
+// Paged-cache data movement on gfx950: token append (the write into a
+// sequence's last block), copy-on-write block copy, and the table-walk gather.
+//
+// All three are pure bit moves (no dtype conversion), so their results are
+// exact.  Append follows page 3 (abeam.tech review), section
+// 「KV キャッシュマネージャ」: new tokens fill the sequence's last block; copy
+// follows the same page, section 「用語解説」 (Copy-on-Write): a shared block is
+// duplicated before it is written; the gather follows the block table in
+// logical order (page 1, jisaku.com glossary, section 「PagedAttentionの解決策」).
+#include <hip/hip_runtime.h>
+
+#include "pa_device.h"
+
+namespace pa {
+namespace {
+
+// One workgroup per new token.  K moves in 16-byte chunks (a chunk is x
+// consecutive dims of one head, contiguous in both source and pool); V is
+// transposed into the pool element by element.
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(typename T::bits* __restrict__ kpool,
+                                                     typename T::bits* __restrict__ vpool,
+                                                     const typename T::bits* __restrict__ knew,
+                                                     const typename T::bits* __restrict__ vnew,
+                                                     const int64_t* __restrict__ slots,
+                                                     int64_t num_slots_total, int Hkv, int D) {
+  using bits = typename T::bits;
+  const int64_t i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots_total) return;  // skipped or out of range
+  const int64_t blk = slot / kBlockSize;
+  const int t = static_cast<int>(slot % kBlockSize);
+  const int chunks_per_head = D / T::kVecElems;
+  const int nchunks = Hkv * chunks_per_head;
+  const bits* ksrc = knew + i * Hkv * static_cast<int64_t>(D);
+  const bits* vsrc = vnew + i * Hkv * static_cast<int64_t>(D);
+  for (int c = threadIdx.x; c < nchunks; c += blockDim.x) {
+    const int h = c / chunks_per_head, ch = c % chunks_per_head;
+    const uint4 val = *reinterpret_cast<const uint4*>(ksrc + static_cast<int64_t>(h) * D +
+                                                      ch * T::kVecElems);
+    bits* dst = kpool + tile_base(blk, h, Hkv, D) + (ch * kBlockSize + t) * T::kVecElems;
+    *reinterpret_cast<uint4*>(dst) = val;
+  }
+  const int nelem = Hkv * D;
+  for (int e = threadIdx.x; e < nelem; e += blockDim.x) {
+    const int h = e / D, d = e % D;
+    vpool[tile_base(blk, h, Hkv, D) + v_elem(t, d)] = vsrc[e];
+  }
+}
+
+// grid = (num_pairs, 2): y selects the K or the V pool.  Each workgroup copies
+// one whole physical block (all heads) with 16-byte loads and stores.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kpool,
+                                                          uint4* __restrict__ vpool,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int num_blocks,
+                                                          int64_t chunks_per_block) {
+  const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  uint4* pool = blockIdx.y == 0 ? kpool : vpool;
+  const uint4* s = pool + static_cast<int64_t>(src) * chunks_per_block;
+  uint4* d = pool + static_cast<int64_t>(dst) * chunks_per_block;
+  for (int64_t c = threadIdx.x; c < chunks_per_block; c += blockDim.x) d[c] = s[c];
+}
+
+// grid = (ceil(max_len/16), Hkv, B): one logical block of one head per
+// workgroup, written to [B][Hkv][max_len][D] in logical order.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(typename T::bits* __restrict__ kout,
+                                                     typename T::bits* __restrict__ vout,
+                                                     const typename T::bits* __restrict__ kpool,
+                                                     const typename T::bits* __restrict__ vpool,
+                                                     const int32_t* __restrict__ tables,
+                                                     const int32_t* __restrict__ lens, int Hkv,
+                                                     int D, int num_blocks, int max_blocks,
+                                                     int max_len) {
+  using bits = typename T::bits;
+  const int lb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int L = lens[b];
+  const bool len_ok = L >= 0 && L <= max_len && L <= max_blocks * kBlockSize;
+  const int phys = (len_ok && lb * kBlockSize < L) ? tables[static_cast<int64_t>(b) * max_blocks + lb]
+                                                   : -1;
+  const bool blk_ok = phys >= 0 && phys < num_blocks;
+  const int64_t row = (static_cast<int64_t>(b) * Hkv + g) * max_len;
+  for (int idx = threadIdx.x; idx < kBlockSize * D; idx += blockDim.x) {
+    const int t = idx / D, d = idx % D;
+    const int pos = lb * kBlockSize + t;
+    if (pos >= max_len) continue;
+    bits kv = 0, vv = 0;
+    if (!len_ok) {
+      kv = vv = static_cast<bits>(~bits(0));  // all-ones = NaN pattern: bad length
+    } else if (pos < L) {
+      if (blk_ok) {
+        const int64_t base = tile_base(phys, g, Hkv, D);
+        kv = kpool[base + k_elem<T>(t, d)];
+        vv = vpool[base + v_elem(t, d)];
+      } else {
+        kv = vv = static_cast<bits>(~bits(0));  // bad table entry
+      }
+    }
+    kout[(row + pos) * D + d] = kv;
+    vout[(row + pos) * D + d] = vv;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+pa_status check_common(const char* fn, int num_blocks, int Hkv, int D, int bs, pa_dtype dt) {
+  if (!dtype_ok(dt)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  if (bs != kBlockSize)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, bs);
+  if (num_blocks <= 0 || Hkv <= 0 || D <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_blocks/num_kv_heads/head_dim must be > 0", fn);
+  if (D % 16 != 0 || D > 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (multiple of 16 up to 256)", fn, D);
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" pa_status pa_cache_append(void* k_pool, void* v_pool, const void* k_new,
+                                     const void* v_new, const int64_t* slot_mapping,
+                                     int32_t num_tokens, int32_t num_blocks,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     pa_dtype dtype, void* stream) {
+  pa_status st = check_common("pa_cache_append", num_blocks, num_kv_heads, head_dim, block_size,
+                              dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "pa_cache_append: num_tokens < 0");
+  if (num_tokens == 0) return ok();
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "pa_cache_append: NULL pointer");
+  if (!aligned16(k_pool) || !aligned16(k_new))
+    return fail(PA_ERR_INVALID_ARG, "pa_cache_append: K pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t total = static_cast<int64_t>(num_blocks) * kBlockSize;
+  dim3 grid(num_tokens), block(256);
+  switch (dtype) {
+    case PA_F32:
+      append_kernel<F32><<<grid, block, 0, s>>>(
+          static_cast<uint32_t*>(k_pool), static_cast<uint32_t*>(v_pool),
+          static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new), slot_mapping,
+          total, num_kv_heads, head_dim);
+      break;
+    case PA_F16:
+      append_kernel<F16><<<grid, block, 0, s>>>(
+          static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
+          static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
+          total, num_kv_heads, head_dim);
+      break;
+    case PA_BF16:
+      append_kernel<BF16><<<grid, block, 0, s>>>(
+          static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
+          static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
+          total, num_kv_heads, head_dim);
+      break;
+  }
+  return launch_status("pa_cache_append");
+}
+
+extern "C" pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
+                                    int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                                    void* stream) {
+  pa_status st = check_common("pa_copy_blocks", num_blocks, num_kv_heads, head_dim, block_size,
+                              dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: num_pairs < 0");
+  if (num_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !block_pairs)
+    return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: NULL pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: pools must be 16-byte aligned");
+  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * kBlockSize *
+                              static_cast<int64_t>(dtype_bytes(dtype));
+  dim3 grid(num_pairs, 2), block(256);
+  copy_blocks_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), block_pairs, num_blocks,
+      block_bytes / 16);
+  return launch_status("pa_copy_blocks");
+}
+
+extern "C" pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, int32_t max_blocks_per_seq,
+                                  int32_t max_context_len, pa_dtype dtype, void* stream) {
+  pa_status st = check_common("pa_gather_kv", num_blocks, num_kv_heads, head_dim, block_size,
+                              dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_gather_kv: negative size");
+  if (num_seqs == 0 || max_context_len == 0) return ok();
+  if (!k_out || !v_out || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "pa_gather_kv: NULL pointer");
+  dim3 grid((max_context_len + kBlockSize - 1) / kBlockSize, num_kv_heads, num_seqs), block(256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define PA_GATHER(TAG, BITS)                                                                  \
+  gather_kernel<TAG><<<grid, block, 0, s>>>(                                                  \
+      static_cast<BITS*>(k_out), static_cast<BITS*>(v_out), static_cast<const BITS*>(k_pool), \
+      static_cast<const BITS*>(v_pool), block_tables, context_lens, num_kv_heads, head_dim,   \
+      num_blocks, max_blocks_per_seq, max_context_len)
+  switch (dtype) {
+    case PA_F32: PA_GATHER(F32, uint32_t); break;
+    case PA_F16: PA_GATHER(F16, uint16_t); break;
+    case PA_BF16: PA_GATHER(BF16, uint16_t); break;
+  }
+#undef PA_GATHER
+  return launch_status("pa_gather_kv");
+}

@@ -1,0 +1,64 @@
+// Device-side helpers shared by the library's HIP kernels: element types,
+// the pool layout and launch-checking plumbing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kBlockSize = 16;  // tokens per KV block
+
+// Element-type tags: `bits` is the stored integer type, kVecElems = elements
+// per 16-byte chunk (the `x` of the K layout).
+struct F32 {
+  using bits = uint32_t;
+  static constexpr int kBytes = 4;
+  static constexpr int kVecElems = 4;
+  __device__ static inline float to_float(bits v) { return __uint_as_float(v); }
+};
+struct F16 {
+  using bits = uint16_t;
+  static constexpr int kBytes = 2;
+  static constexpr int kVecElems = 8;
+  __device__ static inline float to_float(bits v) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, v));
+  }
+};
+struct BF16 {
+  using bits = uint16_t;
+  static constexpr int kBytes = 2;
+  static constexpr int kVecElems = 8;
+  __device__ static inline float to_float(bits v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+  }
+};
+
+// Element offsets inside one (block, kv-head) tile of D*16 elements.
+//   K tile: [D/x][16][x]      V tile: [D][16]
+template <typename T>
+__device__ __host__ inline int64_t k_elem(int t, int d) {
+  return (static_cast<int64_t>(d / T::kVecElems) * kBlockSize + t) * T::kVecElems +
+         d % T::kVecElems;
+}
+__device__ __host__ inline int64_t v_elem(int t, int d) {
+  return static_cast<int64_t>(d) * kBlockSize + t;
+}
+// First element of the (block, kv-head) tile.
+__device__ __host__ inline int64_t tile_base(int64_t block, int head, int num_kv_heads, int D) {
+  return (block * num_kv_heads + head) * static_cast<int64_t>(D) * kBlockSize;
+}
+
+inline size_t dtype_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : 2; }
+inline bool dtype_ok(pa_dtype dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+
+// Converts the state after a launch into a status.
+inline pa_status launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace pa

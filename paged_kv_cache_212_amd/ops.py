@@ -1,0 +1,151 @@
+"""Device operations on torch tensors, forwarded to the C ABI.
+
+torch provides device memory and the current HIP stream; each function checks
+shapes and dtypes, then passes raw pointers to the library.  Nothing here
+computes.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import PA_BF16, PA_F16, PA_F32, check, lib
+
+BLOCK_SIZE = 16
+_DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+
+def pa_dtype(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported KV dtype {t}")
+    return _DT[t]
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+              device="cuda", fill=None):
+    """K pool [N][Hkv][D/x][16][x] and V pool [N][Hkv][D][16] (x = 16 bytes / element)."""
+    x = 16 // torch.empty((), dtype=dtype).element_size()
+    k = torch.empty((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x), dtype=dtype,
+                    device=device)
+    v = torch.empty((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), dtype=dtype, device=device)
+    if fill is not None:
+        k.fill_(fill)
+        v.fill_(fill)
+    return k, v
+
+
+def _pool_dims(k_pool: torch.Tensor, v_pool: torch.Tensor):
+    N, H = k_pool.shape[0], k_pool.shape[1]
+    D = v_pool.shape[2]
+    if v_pool.shape != (N, H, D, BLOCK_SIZE) or k_pool.dtype != v_pool.dtype:
+        raise ValueError("k_pool/v_pool shapes or dtypes do not match the pool layout")
+    if k_pool.numel() != v_pool.numel():
+        raise ValueError("k_pool and v_pool sizes differ")
+    return N, H, D
+
+
+def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
+    """Write k_new/v_new [T][Hkv][D] into slots slot_mapping [T] (int64, -1 = skip)."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    T = k_new.shape[0]
+    if k_new.shape != (T, H, D) or v_new.shape != (T, H, D) or k_new.dtype != k_pool.dtype \
+            or v_new.dtype != k_pool.dtype:
+        raise ValueError("k_new/v_new must be [T][Hkv][D] in the pool dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    check(lib().pa_cache_append(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                _dev(slot_mapping, "slot_mapping"), T, N, H, D, BLOCK_SIZE,
+                                pa_dtype(k_pool.dtype), _stream(stream)), "pa_cache_append")
+
+
+def copy_blocks(k_pool, v_pool, block_pairs, stream=None):
+    """block dst := block src for each row (src, dst) of block_pairs (int32 [n][2])."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    n = block_pairs.shape[0]
+    if n == 0:
+        return
+    if block_pairs.dtype != torch.int32 or block_pairs.shape != (n, 2):
+        raise ValueError("block_pairs must be int32 [n][2]")
+    check(lib().pa_copy_blocks(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                               _dev(block_pairs, "block_pairs"), n, N, H, D, BLOCK_SIZE,
+                               pa_dtype(k_pool.dtype), _stream(stream)), "pa_copy_blocks")
+
+
+def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          partition_size, dtype) -> int:
+    return int(lib().pa_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              max_context_len, partition_size,
+                                              pa_dtype(dtype)))
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                           partition_size, dtype) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               max_context_len, partition_size,
+                                               pa_dtype(dtype)))
+
+
+def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                     partition_size, dtype, device="cuda"):
+    n = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                               partition_size, dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale=None,
+           partition_size=0, workspace=None, stream=None, phase="both"):
+    """out [B][Hq][D] float32 = paged decode attention of q [B][Hq][D].
+
+    phase: "both" (pa_decode), "partial" (pa_decode_partial) or "merge"
+    (pa_decode_merge)."""
+    fn = {"both": "pa_decode", "partial": "pa_decode_partial", "merge": "pa_decode_merge"}[phase]
+    N, H, D = _pool_dims(k_pool, v_pool)
+    B, Hq = q.shape[0], q.shape[1]
+    if q.shape != (B, Hq, D) or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [B][Hq][D] in the pool dtype")
+    if out.shape != (B, Hq, D) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [B][Hq][D]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    scale = D ** -0.5 if scale is None else float(scale)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size, q.dtype,
+                                     q.device)
+    check(getattr(lib(), fn)(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                          _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
+                          _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
+                          block_tables.shape[1], int(max_context_len), scale,
+                          int(partition_size), pa_dtype(q.dtype), _dev(workspace, "workspace"),
+                          workspace.numel() * workspace.element_size(), _stream(stream)),
+          fn)
+    return out
+
+
+def gather_kv(k_pool, v_pool, block_tables, context_lens, max_context_len, stream=None):
+    """Contiguous K, V [B][Hkv][max_context_len][D] reassembled through the tables."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    B = block_tables.shape[0]
+    k_out = torch.empty((B, H, max_context_len, D), dtype=k_pool.dtype, device=k_pool.device)
+    v_out = torch.empty_like(k_out)
+    check(lib().pa_gather_kv(_dev(k_out, "k_out"), _dev(v_out, "v_out"), _dev(k_pool, "k_pool"),
+                             _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
+                             _dev(context_lens, "context_lens"), B, H, D, BLOCK_SIZE, N,
+                             block_tables.shape[1], int(max_context_len),
+                             pa_dtype(k_pool.dtype), _stream(stream)), "pa_gather_kv")
+    return k_out, v_out

@@ -1,0 +1,58 @@
+"""Shared helpers for the GPU tests: run one workload step through the C ABI
+and collect everything the oracle comparison needs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+# canonical NaN bit patterns torch writes for fill_(nan): the oracle pools are
+# poisoned with the same bits so whole pools compare bit for bit
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2}
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU")
+    import paged_kv_cache_212_amd as pk
+    pk.lib()          # raises if the HIP library is not built
+    return pk
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None):
+    """Replays the case's set-up and runs one step on the GPU.
+
+    Returns dict(plan=StepPlan, out=np fp32, k_pool/v_pool=np bits, cache=PagedKVCache).
+    """
+    pk = require_gpu()
+    from oracle import bits_of  # test side only: stored-bit views for comparison
+    dev = torch.device("cuda")
+    td = case.k_tok.dtype
+    cache = pk.PagedKVCache(case.num_blocks, case.num_kv_heads, case.head_dim, td, dev,
+                            free_order=case.free_order, fill=float("nan") if poison else 0.0)
+    k_tok, v_tok = case.k_tok.to(dev), case.v_tok.to(dev)
+    cache.replay(case.script, case.rows, k_tok, v_tok)
+    plan = cache.plan_step(case.batch, max_blocks)
+    nr = torch.as_tensor(case.new_rows(), device=dev)
+    k_new, v_new = k_tok.index_select(0, nr), v_tok.index_select(0, nr)
+    q = case.q.to(dev)
+    ps = case.partition_size if partition_size is None else partition_size
+    out = cache.step(plan, q, k_new, v_new, partition_size=ps)
+    torch.cuda.synchronize()
+    return {"plan": plan, "out": out.cpu().numpy(), "cache": cache, "q": q,
+            "k_pool": bits_of(cache.k_pool, case.dtype),
+            "v_pool": bits_of(cache.v_pool, case.dtype)}
+
+
+def max_err(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert not np.isnan(a).any(), "NaN in GPU output"
+    return float(np.abs(a - b).max()) if a.size else 0.0

@@ -1,0 +1,208 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/pa.h declares, validates arguments before any launch, and its
+C++ block manager reproduces the oracle's allocator model bit for bit."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_212_amd as pk
+from paged_kv_cache_212_amd._lib import (PA_ERR_INVALID_ARG, PA_ERR_OUT_OF_BLOCKS,
+                                         PA_ERR_SEQ_EXISTS, PA_ERR_UNKNOWN_SEQ,
+                                         PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_BF16, PA_F16,
+                                         PA_F32, SIGNATURES)
+from oracle import AllocatorModel, AllocError
+from oracle import allocator as om
+from tests.test_allocator_model import random_ops
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 18
+    h = pk.lib()
+    for n in names:
+        assert hasattr(h, n), n
+        assert n in SIGNATURES, f"binding lacks {n}"
+    assert set(SIGNATURES) == set(names)
+    assert b"gfx950" in h.pa_version()
+
+
+def test_device_calls_reject_bad_scalars_without_launching():
+    h = pk.lib()
+    nul = None
+    # block size, head dim, dtype, G and workspace checks all happen before any launch
+    assert h.pa_decode(nul, nul, nul, nul, nul, nul, 1, 8, 2, 128, 32, 10, 4, 64, 0.1, 0,
+                       PA_BF16, nul, 0, nul) == PA_ERR_UNSUPPORTED
+    assert h.pa_decode(nul, nul, nul, nul, nul, nul, 1, 8, 2, 96, 16, 10, 4, 64, 0.1, 0,
+                       PA_BF16, nul, 0, nul) == PA_ERR_UNSUPPORTED
+    assert h.pa_decode(nul, nul, nul, nul, nul, nul, 1, 8, 3, 128, 16, 10, 4, 64, 0.1, 0,
+                       PA_BF16, nul, 0, nul) == PA_ERR_INVALID_ARG
+    assert h.pa_decode(nul, nul, nul, nul, nul, nul, 1, 64, 2, 128, 16, 10, 4, 64, 0.1, 0,
+                       PA_BF16, nul, 0, nul) == PA_ERR_UNSUPPORTED
+    assert h.pa_decode(nul, nul, nul, nul, nul, nul, 1, 8, 2, 128, 16, 10, 4, 64, 0.1, 24,
+                       PA_BF16, nul, 0, nul) == PA_ERR_INVALID_ARG
+    assert h.pa_decode(nul, nul, nul, nul, nul, nul, 1, 8, 2, 128, 16, 10, 4, 64, -1.0, 0,
+                       PA_BF16, nul, 0, nul) == PA_ERR_INVALID_ARG
+    assert h.pa_decode(nul, nul, nul, nul, nul, nul, 1, 8, 2, 128, 16, 10, 4, 64, 0.1, 0,
+                       7, nul, 0, nul) == PA_ERR_INVALID_ARG
+    # valid scalars but NULL device pointers: rejected, still no launch
+    assert h.pa_decode(nul, nul, nul, nul, nul, nul, 1, 8, 2, 128, 16, 10, 4, 64, 0.1, 0,
+                       PA_BF16, nul, 0, nul) == PA_ERR_INVALID_ARG
+    assert b"NULL" in h.pa_last_error()
+    # multi-partition case without workspace (pointers are fake but never dereferenced)
+    fake = C.c_void_p(1 << 20)
+    assert h.pa_decode(fake, fake, fake, fake, fake, fake, 2, 8, 2, 128, 16, 10, 400, 6000, 0.1,
+                       512, PA_BF16, nul, 0, nul) == PA_ERR_WORKSPACE
+    assert h.pa_cache_append(nul, nul, nul, nul, nul, 4, 10, 8, 128, 16, PA_BF16,
+                             nul) == PA_ERR_INVALID_ARG
+    assert h.pa_cache_append(nul, nul, nul, nul, nul, 0, 10, 8, 128, 16, PA_BF16, nul) == 0
+    assert h.pa_copy_blocks(nul, nul, nul, 3, 10, 8, 128, 8, PA_F16, nul) == PA_ERR_UNSUPPORTED
+    assert h.pa_copy_blocks(nul, nul, nul, 0, 10, 8, 128, 16, PA_F16, nul) == 0
+    assert h.pa_gather_kv(nul, nul, nul, nul, nul, nul, 2, 8, 128, 16, 10, 4, 64, PA_F32,
+                          nul) == PA_ERR_INVALID_ARG
+
+
+def test_workspace_and_partition_queries():
+    h = pk.lib()
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_BF16) > 0
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 256, PA_BF16) == 256
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 100, PA_BF16) == 0
+    # one partition -> no workspace
+    assert h.pa_decode_workspace_bytes(4, 8, 2, 64, 256, 512, PA_F32) == 0
+    # 3 partitions of 512: m, l and acc rows, each region 256-byte aligned
+    rows = 4 * 8 * 3
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert h.pa_decode_workspace_bytes(4, 8, 2, 64, 1100, 512, PA_F32) == \
+        2 * al(rows * 4) + al(rows * 64 * 4)
+
+
+def _c_apply(bm, op):
+    try:
+        if op[0] == "add":
+            return ("ok", bm.add_seq(op[1], op[2]).tolist())
+        if op[0] == "fork":
+            bm.fork(op[1], op[2])
+            return ("ok",)
+        if op[0] == "extend":
+            s, c = bm.extend(op[1], op[2])
+            return ("ok", s.tolist(), c.tolist())
+        if op[0] == "append":
+            s, c = bm.append_slots(op[1])
+            return ("ok", s.tolist(), c.tolist())
+        if op[0] == "free":
+            bm.free_seq(op[1])
+            return ("ok",)
+    except pk.PAError as e:
+        return ("err", e.code)
+
+
+_CODE = {om.OUT_OF_BLOCKS: PA_ERR_OUT_OF_BLOCKS, om.UNKNOWN_SEQ: PA_ERR_UNKNOWN_SEQ,
+         om.SEQ_EXISTS: PA_ERR_SEQ_EXISTS, om.INVALID_ARG: PA_ERR_INVALID_ARG}
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cpp_block_manager_matches_model(seed):
+    from tests.test_allocator_model import apply_model
+    ops_, N = random_ops(seed, n_ops=500, num_blocks=80)
+    order = np.random.default_rng(seed + 50).permutation(N)
+    am = AllocatorModel(N, 16, order)
+    bm = pk.BlockManager(N, 16, order)
+    live = set()
+    n_err = 0
+    for op in ops_:
+        want = apply_model(am, op)
+        got = _c_apply(bm, op)
+        if want[0] == "err":
+            n_err += 1
+            assert got == ("err", _CODE[want[1]]), (op, want, got)
+        else:
+            assert got == want, op
+            if op[0] in ("add", "fork"):
+                live.add(op[-1] if op[0] == "fork" else op[1])
+            if op[0] == "free":
+                live.discard(op[1])
+        st = bm.stats()
+        ms = am.stats()
+        for k in ("num_blocks", "free_blocks", "used_blocks", "shared_blocks", "tokens",
+                  "slack_slots"):
+            assert st[k] == ms[k], (k, op)
+    ids = sorted(am.tables)
+    mb = max([1] + [len(t) for t in am.tables.values()])
+    t_c, l_c = bm.block_tables(ids, mb)
+    t_m, l_m = am.block_tables(ids, mb)
+    assert np.array_equal(t_c, t_m) and np.array_equal(l_c, l_m)
+    for b in range(N):
+        assert bm.refcount(b) == am.ref[b]
+
+
+def test_cpp_block_manager_errors_and_atomicity():
+    bm = pk.BlockManager(4, 16)
+    bm.add_seq(1, 48)
+    bm.add_seq(2, 15)
+    before = (bm.stats(), bm.block_tables([1, 2], 4))
+    with pytest.raises(pk.PAError) as e:
+        bm.append_slots([2, 1])
+    assert e.value.code == PA_ERR_OUT_OF_BLOCKS
+    after = (bm.stats(), bm.block_tables([1, 2], 4))
+    assert before[0] == after[0] and all(np.array_equal(a, b) for a, b in
+                                         zip(before[1], after[1]))
+    with pytest.raises(pk.PAError) as e:
+        bm.append_slots([2, 2])
+    assert e.value.code == PA_ERR_INVALID_ARG
+    with pytest.raises(pk.PAError) as e:
+        bm.add_seq(1, 1)
+    assert e.value.code == PA_ERR_SEQ_EXISTS
+    with pytest.raises(pk.PAError) as e:
+        bm.free_seq(9)
+    assert e.value.code == PA_ERR_UNKNOWN_SEQ
+    with pytest.raises(pk.PAError):
+        pk.BlockManager(4, 16, [0, 1, 1, 2])
+    with pytest.raises(pk.PAError):
+        bm.block_tables([1], 2)          # seq 1 has 3 blocks
+
+
+def test_cpp_worked_example_100_tokens():
+    bm = pk.BlockManager(16, 16, [3, 7, 1] + [b for b in range(16) if b not in (3, 7, 1)])
+    slots = bm.add_seq(0, 100)
+    t, l = bm.block_tables([0], 8)
+    assert t[0, :3].tolist() == [3, 7, 1] and (t[0] >= 0).sum() == 7 and l[0] == 100
+    assert [slots[p] for p in (0, 15, 16, 20, 31, 32, 35, 47)] == [48, 63, 112, 116, 127, 16, 19,
+                                                                   31]
+    assert bm.stats()["slack_slots"] == 12
+
+
+def test_cpp_replays_workload_scripts_like_model():
+    from workloads import small_case
+    from workloads.configs import CONFIG_NAMES
+    for name in CONFIG_NAMES:
+        case = small_case(name)
+        am = AllocatorModel(case.num_blocks, 16, case.free_order)
+        bm = pk.BlockManager(case.num_blocks, 16, case.free_order)
+        for op in case.script:
+            if op[0] == "add":
+                assert np.array_equal(am.add_seq(op[1], op[2]), bm.add_seq(op[1], op[2]))
+            elif op[0] == "extend":
+                a, b = am.extend(op[1], op[2]), bm.extend(op[1], op[2])
+                assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+            elif op[0] == "fork":
+                am.fork(op[1], op[2])
+                bm.fork(op[1], op[2])
+            else:
+                am.free_seq(op[1])
+                bm.free_seq(op[1])
+        a, b = am.append_slots(case.batch), bm.append_slots(case.batch)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        mb = max(-(-int(L) // 16) for L in case.lens)
+        ta, la = am.block_tables(case.batch, mb)
+        tb, lb = bm.block_tables(case.batch, mb)
+        assert np.array_equal(ta, tb) and np.array_equal(la, lb)

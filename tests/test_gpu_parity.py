@@ -1,0 +1,238 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Bars: bit-exact block tables, slots, copy pairs, pools and gathers; decode
+outputs within max-abs 1e-5 (fp32 KV) and 1e-2 (fp16/bf16 KV, fp32
+accumulation).  Pools start poisoned with NaN so that any read of a slot that
+was never written shows up in the output."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import (bits_of, copy_ref, gather_ref, new_pools, run_case, to_f64)
+from oracle.run import oracle_sequence_out
+from tests.gpu_helpers import NAN_BITS, TOL, max_err, require_gpu, run_gpu_step, say
+from workloads import make_case, small_case
+from workloads.configs import CONFIG_NAMES, Case, custom_case
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = ["auto", "generic"]
+
+
+@pytest.fixture
+def kernel(request, monkeypatch):
+    if request.param == "generic":
+        monkeypatch.setenv("PA_DECODE_KERNEL", "generic")
+    else:
+        monkeypatch.delenv("PA_DECODE_KERNEL", raising=False)
+    return request.param
+
+
+def _oracle_poisoned(case):
+    """Oracle run whose pools start with the same NaN bits as the GPU pools."""
+    return run_case(case, pool_fill=NAN_BITS[case.dtype])
+
+
+def _compare_full(case, ref, got, tol):
+    plan = got["plan"]
+    assert np.array_equal(plan.slots, ref["step_slots"])
+    assert np.array_equal(plan.cows, ref["step_cows"].reshape(-1, 2))
+    assert np.array_equal(plan.tables, ref["tables"])
+    assert np.array_equal(plan.lens, ref["lens"])
+    assert np.array_equal(got["k_pool"], ref["k_pool"]), "K pool differs"
+    assert np.array_equal(got["v_pool"], ref["v_pool"]), "V pool differs"
+    err = max_err(got["out"], ref["out"])
+    say(f"  {case.name} {case.dtype}: max |gpu - oracle| = {err:.3e} (tol {tol})")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("kernel", KERNELS, indirect=True)
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_small_configs_match_oracle(name, kernel):
+    case = small_case(name)
+    say(f"[parity small] {name} kernel={kernel} lens={case.lens.tolist()}")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case)
+    _compare_full(case, ref, got, TOL[case.dtype])
+
+
+@pytest.mark.parametrize("kernel", KERNELS, indirect=True)
+def test_tiny_config_full_size(kernel):
+    case = make_case("tiny_fp32")
+    say(f"[parity full] tiny_fp32 kernel={kernel}")
+    _compare_full(case, _oracle_poisoned(case), run_gpu_step(case), TOL["f32"])
+
+
+def _sample_indices(case, k=3, seed=0):
+    L = case.lens
+    picks = {0, case.num_seqs - 1, int(np.argmax(L)), int(np.argmin(L))}
+    rng = np.random.default_rng(seed)
+    picks |= set(int(i) for i in rng.choice(case.num_seqs, size=min(k, case.num_seqs),
+                                            replace=False))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name,kw", [("llama3_8b_bf16", {}), ("opt13b_fp16", {}),
+                                     ("cow_parallel_bf16", {}),
+                                     ("cow_parallel_bf16", {"parked_forks": False}),
+                                     ("long_context_bf16", {})])
+def test_full_size_configs_sampled(name, kw):
+    """Full-size workloads in the bench's launch configuration: every table,
+    slot and copy pair bit-exact; sampled sequences' outputs within tolerance
+    and their gathered K/V bit-exact."""
+    require_gpu()
+    import paged_kv_cache_212_amd as pk
+    say(f"[parity full-size] {name} {kw}: generating on GPU")
+    case = make_case(name, device="cuda", **kw)
+    ref = run_case(case, with_pools=False)
+    got = run_gpu_step(case, poison=False)
+    plan = got["plan"]
+    assert np.array_equal(plan.slots, ref["step_slots"])
+    assert np.array_equal(plan.cows, ref["step_cows"].reshape(-1, 2))
+    assert np.array_equal(plan.tables, ref["tables"])
+    assert np.array_equal(plan.lens, ref["lens"])
+    say(f"  tables/slots/cows bit-exact; {len(plan.cows)} copies; sum L = {case.lens.sum()}")
+    cache = got["cache"]
+    for i in _sample_indices(case):
+        want = oracle_sequence_out(case, i)
+        err = max_err(got["out"][i], want)
+        say(f"  seq {i} L={case.lens[i]}: max err {err:.3e}")
+        assert err <= TOL[case.dtype]
+        L = int(case.lens[i])
+        kg, vg = pk.ops.gather_kv(cache.k_pool, cache.v_pool, plan.d_tables[i:i + 1].contiguous(),
+                                  plan.d_lens[i:i + 1].contiguous(), L)
+        idx = torch.as_tensor(case.rows[int(case.batch[i])][:L], device="cuda")
+        assert torch.equal(kg[0].transpose(0, 1).contiguous().view(torch.int16),
+                           case.k_tok.index_select(0, idx).view(torch.int16))
+        assert torch.equal(vg[0].transpose(0, 1).contiguous().view(torch.int16),
+                           case.v_tok.index_select(0, idx).view(torch.int16))
+    assert not np.isnan(got["out"]).any()
+
+
+def _with(case, **changes):
+    d = dict(case.__dict__)
+    d.update(changes)
+    return Case(**d)
+
+
+@pytest.mark.parametrize("kernel", KERNELS, indirect=True)
+def test_physical_permutation_gives_identical_bits(kernel):
+    case = small_case("llama3_8b_bf16")
+    say(f"[invariance] permutation kernel={kernel}")
+    a = run_gpu_step(case)
+    perm = np.random.default_rng(9).permutation(case.num_blocks).astype(np.int32)
+    b = run_gpu_step(_with(case, free_order=perm))
+    assert not np.array_equal(a["plan"].tables, b["plan"].tables)
+    assert np.array_equal(a["out"], b["out"])
+
+
+@pytest.mark.parametrize("kernel", KERNELS, indirect=True)
+def test_cow_shared_and_duplicated_give_identical_bits(kernel):
+    case = small_case("cow_parallel_bf16")
+    say(f"[invariance] shared vs duplicated kernel={kernel}")
+    shared = run_gpu_step(case)
+    assert len(shared["plan"].cows) > 0
+    need = sum(-(-int(L) // 16) for L in case.lens)
+    dup = _with(case, script=[("add", int(s), int(L) - 1) for s, L in zip(case.batch, case.lens)],
+                num_blocks=need, free_order=np.arange(need, dtype=np.int32))
+    d = run_gpu_step(dup)
+    assert len(d["plan"].cows) == 0
+    assert np.array_equal(shared["out"], d["out"])
+
+
+@pytest.mark.parametrize("kernel", KERNELS, indirect=True)
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_single_token_context_returns_value_exactly(dtype, kernel):
+    case = custom_case(21, dtype, [1, 1, 1, 1], 8, 2, 128)
+    say(f"[closed form] L=1 {dtype} kernel={kernel}")
+    got = run_gpu_step(case)
+    for i in range(4):
+        v = to_f64(bits_of(case.v_tok[case.rows[i][0]], dtype), dtype)
+        assert np.array_equal(got["out"][i].astype(np.float64), np.repeat(v, 4, axis=0))
+
+
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 511, 512, 513, 1023, 1024, 1025, 1600]
+
+
+@pytest.mark.parametrize("kernel", KERNELS, indirect=True)
+@pytest.mark.parametrize("dtype,hq,hkv,d,ps", [
+    ("bf16", 32, 8, 128, 0), ("bf16", 32, 8, 128, 16), ("bf16", 16, 1, 64, 512),
+    ("f16", 8, 8, 128, 512), ("f16", 16, 2, 64, 256), ("bf16", 4, 2, 64, 1024),
+    ("f32", 4, 4, 64, 512), ("f32", 8, 2, 128, 0), ("bf16", 2, 2, 128, 4096)])
+def test_edge_lengths_and_shapes(dtype, hq, hkv, d, ps, kernel):
+    case = custom_case(31, dtype, EDGE_LENS, hq, hkv, d, partition_size=ps, boost_prob=0.02)
+    say(f"[edge] {dtype} Hq={hq} Hkv={hkv} D={d} P={ps} kernel={kernel}")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case)
+    _compare_full(case, ref, got, TOL[dtype])
+
+
+@pytest.mark.parametrize("kernel", KERNELS, indirect=True)
+def test_bad_table_entry_and_length_give_nan_rows(kernel):
+    """Out-of-range table entries and lengths are caught by the kernels' own
+    bounds checks (no access outside the pools) and flagged with NaN rows."""
+    pk = require_gpu()
+    case = custom_case(41, "bf16", [40, 300, 700, 20, 33], 8, 2, 128, partition_size=256)
+    say(f"[errors] bad table entry / length kernel={kernel}")
+    got = run_gpu_step(case)
+    cache, plan = got["cache"], got["plan"]
+    tables = plan.d_tables.clone()
+    tables[1, 5] = case.num_blocks + 7          # seq 1: entry beyond the pool
+    tables[2, 0] = -3                           # seq 2: negative entry
+    lens = plan.d_lens.clone()
+    lens[3] = plan.max_context_len + 1          # seq 3: longer than declared bound
+    lens[4] = 0                                 # seq 4: empty row -> zeros
+    out = torch.empty_like(torch.from_numpy(got["out"])).cuda()
+    pk.ops.decode(out, got["q"], cache.k_pool, cache.v_pool, tables, lens, plan.max_context_len,
+                  partition_size=256)
+    o = out.cpu().numpy()
+    assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and np.isnan(o[3]).all()
+    assert np.array_equal(o[0], got["out"][0])
+    assert np.array_equal(o[4], np.zeros_like(o[4]))
+
+
+def test_append_skips_negative_and_out_of_range_slots():
+    pk = require_gpu()
+    say("[append] skipped slots")
+    k, v = pk.ops.new_pools(4, 2, 64, torch.bfloat16, "cuda", fill=0.0)
+    kn = torch.randn(3, 2, 64, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(3, 2, 64, device="cuda").to(torch.bfloat16)
+    pk.ops.cache_append(k, v, kn, vn, torch.tensor([-1, 4 * 16 + 3, 17], device="cuda"))
+    torch.cuda.synchronize()
+    kp, vp = new_pools(4, 2, 64, 16, "bf16")
+    from oracle import append_ref
+    append_ref(kp, vp, bits_of(kn, "bf16")[2:], bits_of(vn, "bf16")[2:], [17], 16)
+    assert np.array_equal(bits_of(k, "bf16"), kp) and np.array_equal(bits_of(v, "bf16"), vp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_copy_blocks_bitexact(dtype):
+    pk = require_gpu()
+    say(f"[copy] {dtype}")
+    td = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    k, v = pk.ops.new_pools(12, 8, 128, td, "cuda")
+    k.copy_(torch.randn(k.shape, device="cuda").to(td))
+    v.copy_(torch.randn(v.shape, device="cuda").to(td))
+    kp, vp = bits_of(k, dtype), bits_of(v, dtype)
+    pairs = np.array([[3, 7], [0, 11], [5, 2], [99, 1], [4, 4]], dtype=np.int32)
+    pk.ops.copy_blocks(k, v, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    copy_ref(kp, vp, pairs[:3])                 # out-of-range and src == dst pairs are skipped
+    assert np.array_equal(bits_of(k, dtype), kp) and np.array_equal(bits_of(v, dtype), vp)
+
+
+def test_gather_matches_oracle_table_walk():
+    pk = require_gpu()
+    case = small_case("opt13b_fp16")
+    say("[gather] opt small")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case)
+    plan = got["plan"]
+    kg, vg = pk.ops.gather_kv(got["cache"].k_pool, got["cache"].v_pool, plan.d_tables,
+                              plan.d_lens, plan.max_context_len)
+    kg, vg = bits_of(kg, "f16"), bits_of(vg, "f16")
+    for i in range(case.num_seqs):
+        L = int(case.lens[i])
+        K, V = gather_ref(ref["k_pool"], ref["v_pool"], ref["tables"][i], L, 16)
+        assert np.array_equal(kg[i, :, :L], K) and np.array_equal(vg[i, :, :L], V)
+        assert not kg[i, :, L:].any() and not vg[i, :, L:].any()
