@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV cache on one MI355X.
+
+A step is one pass of the whole device path over one batch: copy-on-write block
+copies (when the step's reservation produced any), append of the batch's new
+tokens into their slots, the decode partition pass and the log-sum-exp merge.
+The host reservation (slots, copy pairs, block tables) is done by the C++
+block manager before the timed region, and the same step is replayed every
+iteration (append and copy are idempotent, so every replay does the full work).
+Each iteration uses the next of ``--layers`` identical pool copies, as the
+layers of a model would, so that no pool is re-read before the others have
+streamed through the 256 MB memory-side cache.
+
+Prints one JSON line.  ``value`` is KV bytes read per step / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape"
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_212_amd", "csrc", "pa_decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="llama3_8b_bf16")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the CPU-oracle baseline (0 = skip)")
+    ap.add_argument("--no-events", action="store_true",
+                    help="time only the whole region (no per-launch events)")
+    return ap.parse_args()
+
+
+def kernel_src_hash() -> str:
+    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per partition launch from committed rocprofv3 counters, if they
+    were taken on the current decode kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_src_sha256_16") != kernel_src_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle on the same step: copy pairs, append, decode_ref.
+
+    Sample: whole decode steps over the full batch, repeated while the time
+    budget lasts (at least one)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import append_ref, bits_of, copy_ref, decode_ref, run_case
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        ref = run_case(case, decode=False)               # set-up state (not timed)
+        kp, vp = ref["k_pool"], ref["v_pool"]
+        kb, vb = bits_of(case.k_tok, case.dtype), bits_of(case.v_tok, case.dtype)
+        nr = case.new_rows()
+        qb = bits_of(case.q, case.dtype)
+        times, t_end = [], time.perf_counter() + budget_s
+        while not times or time.perf_counter() < t_end:
+            t0 = time.perf_counter()
+            copy_ref(kp, vp, ref["step_cows"])
+            append_ref(kp, vp, kb[nr], vb[nr], ref["step_slots"], case.block_size)
+            decode_ref(qb, kp, vp, ref["tables"], ref["lens"], case.dtype, case.scale,
+                       case.block_size)
+            times.append(time.perf_counter() - t0)
+    sec = float(np.mean(times))
+    return {"value": round(case.kv_bytes() / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "s_per_step": round(sec, 3),
+            "sample": f"{len(times)} full decode step(s) of the same workload (all "
+                      f"{case.num_seqs} sequences: copy pairs, append, fp64 decode_ref)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the decode path has "
+                                   "no multi-GPU sharding (see the design notes); run with "
+                                   "--gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_212_amd as pk
+    from paged_kv_cache_212_amd._lib import check, lib
+    from paged_kv_cache_212_amd.ops import pa_dtype
+    from workloads import make_case
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    case = make_case(args.workload, device=dev)
+    P = case.partition_size if args.partition_size is None else args.partition_size
+    td = case.k_tok.dtype
+    print(f"[bench] {case.name}: B={case.num_seqs} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+          f"D={case.head_dim} {case.dtype} sumL={int(case.lens.sum())} "
+          f"blocks={case.num_blocks}", file=sys.stderr, flush=True)
+
+    cache = pk.PagedKVCache(case.num_blocks, case.num_kv_heads, case.head_dim, td, dev,
+                            free_order=case.free_order, fill=0.0)
+    cache.replay(case.script, case.rows, case.k_tok, case.v_tok)
+    # host reservation for the step (C++ block manager), timed on its own
+    t0 = time.perf_counter()
+    plan = cache.plan_step(case.batch)
+    host_plan_us = (time.perf_counter() - t0) * 1e6
+    nr = torch.as_tensor(case.new_rows(), device=dev)
+    k_new = case.k_tok.index_select(0, nr).contiguous()
+    v_new = case.v_tok.index_select(0, nr).contiguous()
+    q = case.q.contiguous()
+    cpu_case = None
+    if args.cpu_seconds > 0:        # the oracle baseline reads the same stored bits
+        import dataclasses
+        cpu_case = dataclasses.replace(case, k_tok=case.k_tok.cpu(), v_tok=case.v_tok.cpu(),
+                                       q=case.q.cpu())
+    case.k_tok = case.v_tok = None
+    layers = [(cache.k_pool, cache.v_pool)] + [(cache.k_pool.clone(), cache.v_pool.clone())
+                                               for _ in range(args.layers - 1)]
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    B, Hq, D = q.shape
+    Hkv, N = case.num_kv_heads, case.num_blocks
+    MB = plan.tables.shape[1]
+    ws = pk.ops.decode_workspace(B, Hq, Hkv, D, plan.max_context_len, P, td, dev)
+    P_used = pk.ops.decode_partition_size(B, Hq, Hkv, D, plan.max_context_len, P, td)
+    ncow = int(plan.cows.shape[0])
+    torch.cuda.synchronize()
+
+    # Pre-bound C calls: the loop below only issues launches.
+    L = lib()
+    dt = pa_dtype(td)
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = []
+    for kp, vp in layers:
+        dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+               plan.d_tables.data_ptr(), plan.d_lens.data_ptr(), B, Hq, Hkv, D, 16, N, MB,
+               plan.max_context_len, case.scale, P, dt, ws.data_ptr(), ws.numel(), stream)
+        calls.append((
+            (kp.data_ptr(), vp.data_ptr(), plan.d_cows.data_ptr(), ncow, N, Hkv, D, 16, dt,
+             stream),
+            (kp.data_ptr(), vp.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+             plan.d_slots.data_ptr(), B, N, Hkv, D, 16, dt, stream),
+            dec))
+    f_copy, f_app = L.pa_copy_blocks, L.pa_cache_append
+    f_part, f_merge = L.pa_decode_partial, L.pa_decode_merge
+
+    def step(i, ev=None):
+        c_copy, c_app, c_dec = calls[i % len(calls)]
+        if ncow:
+            check(f_copy(*c_copy), "pa_copy_blocks")
+        check(f_app(*c_app), "pa_cache_append")
+        if ev is not None:
+            ev[0].record()
+        check(f_part(*c_dec), "pa_decode_partial")
+        if ev is not None:
+            ev[1].record()
+        check(f_merge(*c_dec), "pa_decode_merge")
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    evs = None if args.no_events else [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                                       for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i] if evs else None)
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr,
+          flush=True)
+
+    kv_bytes = case.kv_bytes()
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    res = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": case.dtype, "data": "synthetic",
+           "config": {"workload": f"{case.name}: one decode step, B={B}, Hq={Hq}, Hkv={Hkv}, "
+                                  f"D={D}, block 16, {case.dtype} KV, fp32 out",
+                      "global_batch": B, "context_tokens": int(case.lens.sum()),
+                      "max_context_len": plan.max_context_len, "partition_size": P_used,
+                      "cow_copies": ncow, "layers_rotated": args.layers,
+                      "parallelism": "single GPU"},
+           "us_per_step": round(ms_step * 1e3, 3),
+           "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+           "kv_bytes_per_step": kv_bytes,
+           "host_plan_us": round(host_plan_us, 1),
+           "wall_ms_timed_region": round(wall_ms, 3)}
+    if evs:
+        part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        dec_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+        tables_bytes = int(sum(-(-int(x) // 16) for x in case.lens)) * 4
+        alg = kv_bytes + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
+        achieved = alg / (part_ms * 1e-3) / 1e9
+        res["decode_us"] = round(dec_ms * 1e3, 3)
+        res["roofline"] = {"kernel": "decode partition pass (pa_decode_partial)",
+                           "bound": "hbm", "achieved": round(achieved, 2),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": traffic_for(case.name),
+                           "launch_us": round(part_ms * 1e3, 3),
+                           "algorithmic_bytes": alg}
+    if cpu_case is not None:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cpu_case, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -257,16 +257,21 @@ struct Mfma<F16> {
 // K tile bytes: chunk c = kk*4 + j of 8 dims is 256 B, token n at +16n, so
 // lane reads kk*1024 + 16*lane: one contiguous KiB per instruction.  V tile:
 // dim d row of 16 tokens is 32 B, so lane reads t*512 + 32n + 8j.
-template <typename T, int D, int W>
-__global__ __launch_bounds__(64 * W) void decode_mfma_kernel(Params pr) {
+//
+// One wave per (partition, KV head, sequence).  The wave keeps NBUF blocks in
+// flight in a register ring: the loads of block i + NBUF are issued right
+// after block i is consumed.  Loads are issued unconditionally so that the
+// wait counts are static; past the end of the partition (and for a table
+// entry out of range) they re-read an already fetched, valid block, which
+// costs no HBM traffic.
+template <typename T, int D, int NBUF, bool kSmallGroup>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
   constexpr int NKK = D / 32;
   constexpr int NTL = D / 16;
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
-  __shared__ float sm[W][kMaxGroup], sl[W][kMaxGroup];
-  __shared__ float sacc[W > 1 ? W : 1][kMaxGroup][D];
 
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int n = lane & 15, j = lane >> 4;
   const int G = pr.G;
   const int L = pr.lens[b];
@@ -279,7 +284,6 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(Params pr) {
   const int tok0 = p * pr.P, tok1 = min(L, tok0 + pr.P);
   const int blk0 = tok0 / kBlockSize;
   const int nblk = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
-  const int my_n = nblk > wave ? (nblk - wave + W - 1) / W : 0;
 
   uint4 qv[NKK];
   {
@@ -294,96 +298,123 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(Params pr) {
   const char* kbase = static_cast<const char*>(pr.kpool) + g * kTileBytes;
   const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
   const int64_t block_stride = static_cast<int64_t>(pr.Hkv) * kTileBytes;
-  const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks + blk0 + wave;
+  const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks + blk0;
+
+  // Table entries, 64 per register: lane i of `tcur` holds entry c*64 + i of
+  // chunk c = i / 64 currently being prefetched; `tnext` the following chunk.
+  bool bad = false;
+  auto load_chunk = [&](int c) -> int {
+    const int k = c * 64 + lane;
+    int e = k < nblk ? trow[k] : 0;
+    const bool lane_bad = k < nblk && (e < 0 || e >= pr.num_blocks);
+    if (__any(lane_bad)) bad = true;
+    return lane_bad ? 0 : e;
+  };
+  int chunk = 0;
+  int tcur = load_chunk(0);
+  int tnext = nblk > 64 ? load_chunk(1) : 0;
+  // physical block of logical block k of the partition (k < nblk), else the
+  // partition's last block, already read (no new HBM traffic).
+  auto phys_of = [&](int k) -> int {
+    if (k >= nblk) return __builtin_amdgcn_readlane(tcur, (nblk - 1) & 63);
+    const int c = k >> 6;
+    if (c != chunk) {          // crossed into the next chunk (k increases by one)
+      chunk = c;
+      tcur = tnext;
+      tnext = (c + 1) * 64 < nblk ? load_chunk(c + 1) : 0;
+    }
+    return __builtin_amdgcn_readlane(tcur, k & 63);
+  };
+
+  uint4 kb[NBUF][NKK];
+  uint2 vb[NBUF][NTL];
+  auto issue = [&](int u, int phys) {
+    const char* kt = kbase + phys * block_stride;
+    const char* vt = vbase + phys * block_stride;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      kb[u][kk] = *reinterpret_cast<const uint4*>(kt + kk * 1024 + lane * 16);
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+      vb[u][t] = *reinterpret_cast<const uint2*>(vt + t * 512 + n * 32 + j * 8);
+  };
 
   float m_run = -INFINITY, l_lane = 0.f;
   f32x4_t acc[NTL];
 #pragma unroll
   for (int t = 0; t < NTL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bool bad = false;
 
-  // Table entries of this wave's blocks, 64 at a time (lane i holds entry i).
-  int tent = 0;
-  auto refresh = [&](int i0) {
-    const int cnt = min(64, my_n - i0);
-    tent = lane < cnt ? trow[static_cast<int64_t>(i0 + lane) * W] : 0;
-    const bool lane_bad = lane < cnt && (tent < 0 || tent >= pr.num_blocks);
-    if (__any(lane_bad)) bad = true;
-  };
-  auto load = [&](int phys, uint4* kr, uint2* vr) {
-    const char* kt = kbase + phys * block_stride;
-    const char* vt = vbase + phys * block_stride;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      kr[kk] = *reinterpret_cast<const uint4*>(kt + kk * 1024 + lane * 16);
-#pragma unroll
-    for (int t = 0; t < NTL; ++t)
-      vr[t] = *reinterpret_cast<const uint2*>(vt + t * 512 + n * 32 + j * 8);
-  };
+  for (int u = 0; u < NBUF; ++u) issue(u, phys_of(u));
 
-  uint4 kc[NKK];
-  uint2 vc[NTL];
-  if (my_n > 0) {
-    refresh(0);
-    if (!bad) load(__builtin_amdgcn_readfirstlane(tent), kc, vc);
-  }
-  for (int i = 0; i < my_n && !bad; ++i) {
-    uint4 kn[NKK];
-    uint2 vn[NTL];
-    const bool has_next = i + 1 < my_n;
-    if (has_next) {
-      if (((i + 1) & 63) == 0) refresh(i + 1);
-      if (!bad) load(__builtin_amdgcn_readlane(tent, (i + 1) & 63), kn, vn);
-    }
-    const int blk = blk0 + wave + i * W;
-
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < nblk; i0 += NBUF) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) s = Mfma<T>::qk(kc[kk], qv[kk], s);
-    const int pos0 = blk * kBlockSize + 4 * j;
-    float sv[4];
+    for (int u = 0; u < NBUF; ++u) {
+      const int i = i0 + u;
+      if (i < nblk) {
+        const int blk = blk0 + i;
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sv[e] = (pos0 + e < tok1) ? s[e] * pr.scale_log2 : -INFINITY;
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m_run, bm);
-    const float alpha = exp2f(m_run - mn);
-    float pe[4];
+        for (int kk = 0; kk < NKK; ++kk) s = Mfma<T>::qk(kb[u][kk], qv[kk], s);
+        const int pos0 = blk * kBlockSize + 4 * j;
+        float sv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pe[e] = exp2f(sv[e] - mn);
-    l_lane = l_lane * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-    m_run = mn;
+        for (int e = 0; e < 4; ++e) sv[e] = (pos0 + e < tok1) ? s[e] * pr.scale_log2 : -INFINITY;
+        float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m_run, bm);
+        const float alpha = exp2f(m_run - mn);
+        float pe[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float ah = __shfl(alpha, 4 * j + e);
+        for (int e = 0; e < 4; ++e) pe[e] = exp2f(sv[e] - mn);
+        l_lane = l_lane * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
+        m_run = mn;
+        // Rescale the output rows: lane holds heads 4j+e; head h's factor sits
+        // in lane h (n = h).
+        if constexpr (kSmallGroup) {
+          // G <= 4: only rows 0..3 (lanes with j = 0) are real; broadcast the
+          // four factors through scalar registers.
 #pragma unroll
-      for (int t = 0; t < NTL; ++t) acc[t][e] *= ah;
-    }
-    uint2 phi, plo;
-    Mfma<T>::split(pe, phi, plo);
-    if (blk * kBlockSize + kBlockSize > tok1) {
-      // last block of the sequence: zero V of positions >= L so that garbage
-      // (even NaN) in unused slots cannot reach the output through 0 * v.
-      const int nv = tok1 - blk * kBlockSize;
-      const uint32_t m0 = (4 * j + 0 < nv ? 0x0000FFFFu : 0u) | (4 * j + 1 < nv ? 0xFFFF0000u : 0u);
-      const uint32_t m1 = (4 * j + 2 < nv ? 0x0000FFFFu : 0u) | (4 * j + 3 < nv ? 0xFFFF0000u : 0u);
+          for (int e = 0; e < 4; ++e) {
+            const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), e));
 #pragma unroll
-      for (int t = 0; t < NTL; ++t) {
-        vc[t].x &= m0;
-        vc[t].y &= m1;
+            for (int t = 0; t < NTL; ++t) acc[t][e] *= ah;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ah = __shfl(alpha, 4 * j + e);
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) acc[t][e] *= ah;
+          }
+        }
+        uint2 phi, plo;
+        Mfma<T>::split(pe, phi, plo);
+        uint2 vv[NTL];
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) vv[t] = vb[u][t];
+        if (blk * kBlockSize + kBlockSize > tok1) {
+          // last block of the sequence: zero V of positions >= L so that
+          // garbage (even NaN) in unused slots cannot reach the output via 0*v.
+          const int nv = tok1 - blk * kBlockSize;
+          const uint32_t m0 =
+              (4 * j + 0 < nv ? 0x0000FFFFu : 0u) | (4 * j + 1 < nv ? 0xFFFF0000u : 0u);
+          const uint32_t m1 =
+              (4 * j + 2 < nv ? 0x0000FFFFu : 0u) | (4 * j + 3 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int t = 0; t < NTL; ++t) {
+            vv[t].x &= m0;
+            vv[t].y &= m1;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+          acc[t] = Mfma<T>::pv(phi, vv[t], acc[t]);
+          acc[t] = Mfma<T>::pv(plo, vv[t], acc[t]);
+        }
       }
-    }
-#pragma unroll
-    for (int t = 0; t < NTL; ++t) {
-      acc[t] = Mfma<T>::pv(phi, vc[t], acc[t]);
-      acc[t] = Mfma<T>::pv(plo, vc[t], acc[t]);
-    }
-    if (has_next) {
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kc[kk] = kn[kk];
-#pragma unroll
-      for (int t = 0; t < NTL; ++t) vc[t] = vn[t];
+      issue(u, phys_of(i + NBUF));
     }
   }
 
@@ -396,63 +427,24 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(Params pr) {
     for (int t = 0; t < NTL; ++t) acc[t] = f32x4_t{l_lane, l_lane, l_lane, l_lane};
   }
 
-  if constexpr (W == 1) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int h = 4 * j + e;
-      const float mh = __shfl(m_run, h);
-      const float lh = __shfl(l_lane, h);
-      if (h < G) {
-        const int64_t row = static_cast<int64_t>(b) * pr.Hq + g * G + h;
-#pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-          const int d = t * 16 + n;
-          if (np == 1)
-            pr.out[row * D + d] = acc[t][e] / lh;
-          else
-            pr.part_acc[(row * pr.maxP + p) * D + d] = acc[t][e];
-        }
-        if (np > 1 && n == 0) {
-          pr.part_m[row * pr.maxP + p] = mh;
-          pr.part_l[row * pr.maxP + p] = lh;
-        }
-      }
-    }
-  } else {
-    if (j == 0 && n < G) {
-      sm[wave][n] = m_run;
-      sl[wave][n] = l_lane;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int h = 4 * j + e;
-      if (h < G) {
-#pragma unroll
-        for (int t = 0; t < NTL; ++t) sacc[wave][h][t * 16 + n] = acc[t][e];
-      }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
-      const int h = idx / D, d = idx % D;
-      float M = sm[0][h];
-#pragma unroll
-      for (int w = 1; w < W; ++w) M = fmaxf(M, sm[w][h]);
-      float a = 0.f, lsum = 0.f;
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float f = exp2f(sm[w][h] - M);
-        a = fmaf(f, sacc[w][h][d], a);
-        lsum = fmaf(f, sl[w][h], lsum);
-      }
+  for (int e = 0; e < 4; ++e) {
+    const int h = 4 * j + e;
+    const float mh = __shfl(m_run, h);
+    const float lh = __shfl(l_lane, h);
+    if (h < G) {
       const int64_t row = static_cast<int64_t>(b) * pr.Hq + g * G + h;
-      if (np == 1) {
-        pr.out[row * D + d] = a / lsum;
-      } else {
-        pr.part_acc[(row * pr.maxP + p) * D + d] = a;
-        if (d == 0) {
-          pr.part_m[row * pr.maxP + p] = M;
-          pr.part_l[row * pr.maxP + p] = lsum;
-        }
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        const int d = t * 16 + n;
+        if (np == 1)
+          pr.out[row * D + d] = acc[t][e] / lh;
+        else
+          pr.part_acc[(row * pr.maxP + p) * D + d] = acc[t][e];
+      }
+      if (np > 1 && n == 0) {
+        pr.part_m[row * pr.maxP + p] = mh;
+        pr.part_l[row * pr.maxP + p] = lh;
       }
     }
   }
@@ -518,8 +510,8 @@ Path path_from_env() {
   return (v && std::strcmp(v, "generic") == 0) ? Path::kGeneric : Path::kAuto;
 }
 
-constexpr int kDefaultPartition = 512;
-constexpr int kWavesPerGroup = 4;
+constexpr int kDefaultPartition = 256;
+constexpr int kPrefetch = 4;
 
 bool decode_args_ok(int B, int Hq, int Hkv, int D, int max_ctx, int P, pa_dtype dt) {
   return B >= 0 && B <= 65535 && Hkv > 0 && Hkv <= 65535 && Hq > 0 && Hq % Hkv == 0 &&
@@ -544,8 +536,10 @@ void launch_partitions(const Params& pr, bool generic, hipStream_t s) {
   dim3 grid(pr.maxP, pr.Hkv, pr.B);
   if (generic)
     decode_generic_kernel<T, D><<<grid, 256, 0, s>>>(pr);
+  else if (pr.G <= 4)
+    decode_mfma_kernel<T, D, kPrefetch, true><<<grid, 64, 0, s>>>(pr);
   else
-    decode_mfma_kernel<T, D, kWavesPerGroup><<<grid, 64 * kWavesPerGroup, 0, s>>>(pr);
+    decode_mfma_kernel<T, D, kPrefetch, false><<<grid, 64, 0, s>>>(pr);
 }
 
 template <>
