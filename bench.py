@@ -44,7 +44,24 @@ def parse():
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--no-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB elementwise copy 5 times (reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain fp32 elementwise copy of known size: reads 1 GiB, writes 1 GiB per launch."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": n * 4,
+                      "copy_calibration_bytes_written_per_launch": n * 4, "launches": 5}))
 
 
 def kernel_src_hash() -> str:
@@ -97,6 +114,9 @@ def cpu_baseline(case, budget_s: float):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the decode path has "

@@ -37,7 +37,9 @@
  *   K pool: [num_blocks][Hkv][D/x][bs][x]   element (b,h,t,d) at
  *           (((b*Hkv + h)*(D/x) + d/x)*bs + t)*x + d%x
  *   V pool: [num_blocks][Hkv][D][bs]        element (b,h,t,d) at
- *           ((b*Hkv + h)*D + d)*bs + t
+ *           ((b*Hkv + h)*D + d)*bs + slot(t), where slot(t) exchanges bits 2
+ *           and 3 of t: each 16-slot row holds tokens 0-3, 8-11, 4-7, 12-15
+ *           (so the matrix-core kernel reads 8 tokens with one 16-byte load)
  * A token at logical position p of a sequence lives in physical block
  * table[p / bs] at in-block offset t = p % bs; its slot number is
  * table[p / bs]*bs + p % bs.

@@ -207,6 +207,25 @@ struct Mfma<BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, p),
                                                      __builtin_bit_cast(i16x4_t, v), c, 0, 0, 0);
   }
+  // O tile (16 heads x 16 dims) += P (16 heads x 32 tokens) . V (32 tokens x 16 dims)
+  __device__ static inline f32x4_t pv8(uint4 p, uint4 v, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, p),
+                                                   __builtin_bit_cast(bf16x8_t, v), c, 0, 0, 0);
+  }
+  __device__ static inline void split8(const float pe[8], uint4& hi, uint4& lo) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t u = __float_as_uint(pe[e]);
+      h[e] = u >> 16;
+      const float r = pe[e] - __uint_as_float(u & 0xFFFF0000u);
+      l[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r));
+    }
+    hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                    h[6] | (h[7] << 16));
+    lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
+                    l[6] | (l[7] << 16));
+  }
   // p (>= 0) = hi + lo with hi = p truncated to bf16 (exact remainder) and
   // lo = remainder rounded to bf16.
   __device__ static inline void split(const float pe[4], uint2& hi, uint2& lo) {
@@ -225,6 +244,24 @@ struct Mfma<BF16> {
 
 template <>
 struct Mfma<F16> {
+  __device__ static inline f32x4_t pv8(uint4 p, uint4 v, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, p),
+                                                  __builtin_bit_cast(f16x8_t, v), c, 0, 0, 0);
+  }
+  __device__ static inline void split8(const float pe[8], uint4& hi, uint4& lo) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 hh = static_cast<_Float16>(pe[e]);
+      const float r = pe[e] - static_cast<float>(hh);
+      h[e] = __builtin_bit_cast(uint16_t, hh);
+      l[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
+    }
+    hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                    h[6] | (h[7] << 16));
+    lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
+                    l[6] | (l[7] << 16));
+  }
   __device__ static inline f32x4_t qk(uint4 k, uint4 q, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, k),
                                                   __builtin_bit_cast(f16x8_t, q), c, 0, 0, 0);
@@ -247,30 +284,34 @@ struct Mfma<F16> {
   }
 };
 
-// Lane roles (lane = 16*j + n, n = lane % 16, j = lane / 16):
-//   QK A operand (K):   token n of the block, dims kk*32 + 8j .. +8
-//   QK B operand (Q):   head n,               dims kk*32 + 8j .. +8
-//   QK result S^T:      head n, tokens 4j + e (e = 0..3)
-//   PV A operand (P):   head n, tokens 4j + e   (same registers as S^T)
-//   PV B operand (V):   dim t*16 + n, tokens 4j + e
-//   PV result O:        heads 4j + e, dim t*16 + n
-// K tile bytes: chunk c = kk*4 + j of 8 dims is 256 B, token n at +16n, so
-// lane reads kk*1024 + 16*lane: one contiguous KiB per instruction.  V tile:
-// dim d row of 16 tokens is 32 B, so lane reads t*512 + 32n + 8j.
+// Two blocks (A = logical block 2q, B = 2q+1 of the partition) per iteration.
+// Lane = 16*j + n (n = lane % 16, j = lane / 16).
+//   QK, half hh in {0,1}: S^T (16 rows x 16 heads) = K rows . Q^T where row
+//     i < 8 is token i + 8*hh of A and row i >= 8 token i - 8 + 8*hh of B.
+//     A operand (K): lane reads row n, dims kk*32 + 8j .. +8 (16 bytes).
+//     B operand (Q): head n, dims kk*32 + 8j .. +8.
+//     Result: lane (head n, j) holds rows 4j+e, i.e. block j/2, tokens
+//     4*(j%2) + e + 8*hh (e = 0..3).
+//   PV: O (16 heads x 16 dims) += P (heads x 32 tokens) . V (32 tokens x dims)
+//     with lane (n, j) holding k-slots {S_hh0[e], S_hh1[e]}: 8 tokens of block
+//     j/2, namely 4*(j%2) + {0..3} and 8 + 4*(j%2) + {0..3}.  In the V tile
+//     the 16 token slots of each dim row are stored in the order 0-3, 8-11,
+//     4-7, 12-15, so those 8 tokens are 16 contiguous bytes at
+//     dim*32 + 16*(j%2): one 16-byte load per lane and tile.
+//   O result: lane (dim t*16 + n, j) holds heads 4j + e.
+// K tile (block, head) bytes: [D/8 chunks][16 tokens][8 dims] -> chunk
+// kk*4 + j, token r at (kk*4 + j)*256 + 16*r.
 //
-// One wave per (partition, KV head, sequence).  The wave keeps NBUF blocks in
-// flight in a register ring: the loads of block i + NBUF are issued right
-// after block i is consumed.  Loads are issued unconditionally so that the
-// wait counts are static; past the end of the partition (and for a table
-// entry out of range) they re-read an already fetched, valid block, which
-// costs no HBM traffic.
-template <typename T, int D, int NBUF, bool kSmallGroup>
+// One wave per (KV head, partition, sequence).  NPAIR block pairs are in
+// flight in a register ring; the loop is peeled so the steady state issues
+// its loads unconditionally (static wait counts) and the tail issues none.
+template <typename T, int D, int NPAIR, bool kSmallGroup>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
   constexpr int NKK = D / 32;
   constexpr int NTL = D / 16;
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
 
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x % pr.Hkv, p = blockIdx.x / pr.Hkv, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int n = lane & 15, j = lane >> 4;
   const int G = pr.G;
@@ -284,6 +325,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
   const int tok0 = p * pr.P, tok1 = min(L, tok0 + pr.P);
   const int blk0 = tok0 / kBlockSize;
   const int nblk = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
+  const int npair = (nblk + 1) >> 1;
 
   uint4 qv[NKK];
   {
@@ -300,12 +342,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
   const int64_t block_stride = static_cast<int64_t>(pr.Hkv) * kTileBytes;
   const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks + blk0;
 
-  // Table entries, 64 per register: lane i of `tcur` holds entry c*64 + i of
-  // chunk c = i / 64 currently being prefetched; `tnext` the following chunk.
+  // Table entries, 64 per register (lane i holds entry 64*c + i of chunk c).
   bool bad = false;
   auto load_chunk = [&](int c) -> int {
     const int k = c * 64 + lane;
-    int e = k < nblk ? trow[k] : 0;
+    const int e = k < nblk ? trow[k] : 0;
     const bool lane_bad = k < nblk && (e < 0 || e >= pr.num_blocks);
     if (__any(lane_bad)) bad = true;
     return lane_bad ? 0 : e;
@@ -313,12 +354,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
   int chunk = 0;
   int tcur = load_chunk(0);
   int tnext = nblk > 64 ? load_chunk(1) : 0;
-  // physical block of logical block k of the partition (k < nblk), else the
-  // partition's last block, already read (no new HBM traffic).
+  // Physical block of partition block k (k increases across calls); k >= nblk
+  // (the missing half of a last, odd pair) maps to block nblk-1, whose lines
+  // are being fetched by the same instruction anyway.
   auto phys_of = [&](int k) -> int {
-    if (k >= nblk) return __builtin_amdgcn_readlane(tcur, (nblk - 1) & 63);
+    if (k >= nblk) k = nblk - 1;
     const int c = k >> 6;
-    if (c != chunk) {          // crossed into the next chunk (k increases by one)
+    if (c != chunk) {
       chunk = c;
       tcur = tnext;
       tnext = (c + 1) * 64 < nblk ? load_chunk(c + 1) : 0;
@@ -326,17 +368,20 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
     return __builtin_amdgcn_readlane(tcur, k & 63);
   };
 
-  uint4 kb[NBUF][NKK];
-  uint2 vb[NBUF][NTL];
-  auto issue = [&](int u, int phys) {
-    const char* kt = kbase + phys * block_stride;
-    const char* vt = vbase + phys * block_stride;
+  uint4 kb[NPAIR][2][NKK];
+  uint4 vb[NPAIR][NTL];
+  auto issue = [&](int u, int q) {
+    const int pa = phys_of(2 * q), pb = phys_of(2 * q + 1);
+    const int mine = (n < 8) ? pa : pb;             // K row block of this lane
+    const char* kt = kbase + mine * block_stride + (n & 7) * 16 + j * 256;
+    const char* vt = vbase + ((j >> 1) ? pb : pa) * block_stride + n * 32 + (j & 1) * 16;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      kb[u][kk] = *reinterpret_cast<const uint4*>(kt + kk * 1024 + lane * 16);
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int t = 0; t < NTL; ++t)
-      vb[u][t] = *reinterpret_cast<const uint2*>(vt + t * 512 + n * 32 + j * 8);
+      for (int kk = 0; kk < NKK; ++kk)
+        kb[u][hh][kk] = *reinterpret_cast<const uint4*>(kt + kk * 1024 + hh * 128);
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) vb[u][t] = *reinterpret_cast<const uint4*>(vt + t * 512);
   };
 
   float m_run = -INFINITY, l_lane = 0.f;
@@ -344,79 +389,94 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
 #pragma unroll
   for (int t = 0; t < NTL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  auto compute = [&](int u, int q) {
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < NBUF; ++u) issue(u, phys_of(u));
-
-  for (int i0 = 0; i0 < nblk; i0 += NBUF) {
+    for (int kk = 0; kk < NKK; ++kk) {
+      s0 = Mfma<T>::qk(kb[u][0][kk], qv[kk], s0);
+      s1 = Mfma<T>::qk(kb[u][1][kk], qv[kk], s1);
+    }
+    // position of S_hh[e] in the sequence
+    const int base = (blk0 + 2 * q + (j >> 1)) * kBlockSize + 4 * (j & 1);
+    float sv[8];
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int i = i0 + u;
-      if (i < nblk) {
-        const int blk = blk0 + i;
-        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = (base + e < tok1) ? s0[e] * pr.scale_log2 : -INFINITY;
+      sv[4 + e] = (base + 8 + e < tok1) ? s1[e] * pr.scale_log2 : -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m_run, bm);
+    if (__any(mn != m_run)) {
+      // running max moved for some head: rescale rows 4j+e by 2^(m_old - m_new)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      l_lane *= alpha;
+      if constexpr (kSmallGroup) {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) s = Mfma<T>::qk(kb[u][kk], qv[kk], s);
-        const int pos0 = blk * kBlockSize + 4 * j;
-        float sv[4];
+        for (int e = 0; e < 4; ++e) {
+          const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), e));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[e] = (pos0 + e < tok1) ? s[e] * pr.scale_log2 : -INFINITY;
-        float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m_run, bm);
-        const float alpha = exp2f(m_run - mn);
-        float pe[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pe[e] = exp2f(sv[e] - mn);
-        l_lane = l_lane * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-        m_run = mn;
-        // Rescale the output rows: lane holds heads 4j+e; head h's factor sits
-        // in lane h (n = h).
-        if constexpr (kSmallGroup) {
-          // G <= 4: only rows 0..3 (lanes with j = 0) are real; broadcast the
-          // four factors through scalar registers.
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), e));
-#pragma unroll
-            for (int t = 0; t < NTL; ++t) acc[t][e] *= ah;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ah = __shfl(alpha, 4 * j + e);
-#pragma unroll
-            for (int t = 0; t < NTL; ++t) acc[t][e] *= ah;
-          }
+          for (int t = 0; t < NTL; ++t) acc[t][e] *= ah;
         }
-        uint2 phi, plo;
-        Mfma<T>::split(pe, phi, plo);
-        uint2 vv[NTL];
+      } else {
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) vv[t] = vb[u][t];
-        if (blk * kBlockSize + kBlockSize > tok1) {
-          // last block of the sequence: zero V of positions >= L so that
-          // garbage (even NaN) in unused slots cannot reach the output via 0*v.
-          const int nv = tok1 - blk * kBlockSize;
-          const uint32_t m0 =
-              (4 * j + 0 < nv ? 0x0000FFFFu : 0u) | (4 * j + 1 < nv ? 0xFFFF0000u : 0u);
-          const uint32_t m1 =
-              (4 * j + 2 < nv ? 0x0000FFFFu : 0u) | (4 * j + 3 < nv ? 0xFFFF0000u : 0u);
+        for (int e = 0; e < 4; ++e) {
+          const float ah = __shfl(alpha, 4 * j + e);
 #pragma unroll
-          for (int t = 0; t < NTL; ++t) {
-            vv[t].x &= m0;
-            vv[t].y &= m1;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-          acc[t] = Mfma<T>::pv(phi, vv[t], acc[t]);
-          acc[t] = Mfma<T>::pv(plo, vv[t], acc[t]);
+          for (int t = 0; t < NTL; ++t) acc[t][e] *= ah;
         }
       }
-      issue(u, phys_of(i + NBUF));
+      m_run = mn;
+    }
+    float pe[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - mn);
+    l_lane += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+    uint4 phi, plo;
+    Mfma<T>::split8(pe, phi, plo);
+    uint4 vmask = make_uint4(~0u, ~0u, ~0u, ~0u);
+    if ((blk0 + 2 * q + 2) * kBlockSize > tok1) {
+      // the pair reaches past the end of the sequence: zero V of positions
+      // >= L so unused slots (even NaN) cannot reach the output through 0*v
+      vmask.x = (base + 0 < tok1 ? 0x0000FFFFu : 0u) | (base + 1 < tok1 ? 0xFFFF0000u : 0u);
+      vmask.y = (base + 2 < tok1 ? 0x0000FFFFu : 0u) | (base + 3 < tok1 ? 0xFFFF0000u : 0u);
+      vmask.z = (base + 8 < tok1 ? 0x0000FFFFu : 0u) | (base + 9 < tok1 ? 0xFFFF0000u : 0u);
+      vmask.w = (base + 10 < tok1 ? 0x0000FFFFu : 0u) | (base + 11 < tok1 ? 0xFFFF0000u : 0u);
+    }
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      const uint4 vv = make_uint4(vb[u][t].x & vmask.x, vb[u][t].y & vmask.y,
+                                  vb[u][t].z & vmask.z, vb[u][t].w & vmask.w);
+      acc[t] = Mfma<T>::pv8(phi, vv, acc[t]);
+      acc[t] = Mfma<T>::pv8(plo, vv, acc[t]);
+    }
+  };
+
+  // prologue: first min(NPAIR, npair) pairs in flight
+#pragma unroll
+  for (int u = 0; u < NPAIR; ++u)
+    if (u < npair) issue(u, u);
+  int q0 = 0;
+  for (; q0 + 2 * NPAIR <= npair; q0 += NPAIR) {
+#pragma unroll
+    for (int u = 0; u < NPAIR; ++u) {
+      compute(u, q0 + u);
+      issue(u, q0 + u + NPAIR);
     }
   }
+  // tail: at most 2*NPAIR - 1 pairs left, the first min(NPAIR, left) in flight
+#pragma unroll
+  for (int u = 0; u < NPAIR; ++u) {
+    if (q0 + u < npair) {
+      compute(u, q0 + u);
+      if (q0 + u + NPAIR < npair) issue(u, q0 + u + NPAIR);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NPAIR; ++u)
+    if (q0 + NPAIR + u < npair) compute(u, q0 + NPAIR + u);
 
   l_lane += __shfl_xor(l_lane, 16);
   l_lane += __shfl_xor(l_lane, 32);
@@ -434,11 +494,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
     const float lh = __shfl(l_lane, h);
     if (h < G) {
       const int64_t row = static_cast<int64_t>(b) * pr.Hq + g * G + h;
+      const float inv = 1.0f / lh;
 #pragma unroll
       for (int t = 0; t < NTL; ++t) {
         const int d = t * 16 + n;
         if (np == 1)
-          pr.out[row * D + d] = acc[t][e] / lh;
+          pr.out[row * D + d] = acc[t][e] * inv;
         else
           pr.part_acc[(row * pr.maxP + p) * D + d] = acc[t][e];
       }
@@ -511,7 +572,7 @@ Path path_from_env() {
 }
 
 constexpr int kDefaultPartition = 256;
-constexpr int kPrefetch = 4;
+constexpr int kPairsInFlight = 2;
 
 bool decode_args_ok(int B, int Hq, int Hkv, int D, int max_ctx, int P, pa_dtype dt) {
   return B >= 0 && B <= 65535 && Hkv > 0 && Hkv <= 65535 && Hq > 0 && Hq % Hkv == 0 &&
@@ -533,13 +594,15 @@ size_t workspace_bytes(int B, int Hq, int D, int maxP) {
 
 template <typename T, int D>
 void launch_partitions(const Params& pr, bool generic, hipStream_t s) {
-  dim3 grid(pr.maxP, pr.Hkv, pr.B);
+  // matrix-core kernel: x = KV head + Hkv * partition (the heads of one
+  // partition are dispatched together), z = sequence
+  dim3 grid_m(pr.Hkv * pr.maxP, 1, pr.B);
   if (generic)
-    decode_generic_kernel<T, D><<<grid, 256, 0, s>>>(pr);
+    decode_generic_kernel<T, D><<<dim3(pr.maxP, pr.Hkv, pr.B), 256, 0, s>>>(pr);
   else if (pr.G <= 4)
-    decode_mfma_kernel<T, D, kPrefetch, true><<<grid, 64, 0, s>>>(pr);
+    decode_mfma_kernel<T, D, kPairsInFlight, true><<<grid_m, 64, 0, s>>>(pr);
   else
-    decode_mfma_kernel<T, D, kPrefetch, false><<<grid, 64, 0, s>>>(pr);
+    decode_mfma_kernel<T, D, kPairsInFlight, false><<<grid_m, 64, 0, s>>>(pr);
 }
 
 template <>

@@ -65,7 +65,9 @@ def test_worked_example_100_tokens():
 
 # ------------------------------------------------------------------ layout --
 # Offsets enumerated by hand from the layout statement:
-#   K: (((b*H + h)*(D/x) + d//x)*bs + t)*x + d%x ;  V: ((b*H + h)*D + d)*bs + t
+#   K: (((b*H + h)*(D/x) + d//x)*bs + t)*x + d%x
+#   V: ((b*H + h)*D + d)*bs + slot(t), slot(t) = t with bits 2 and 3 exchanged
+#      (slot(4) = 8, slot(9) = 5, slot(11) = 7; 0-3 and 12-15 stay put)
 LAYOUT_CASES = [
     # dtype, H, D, (b, h, t, d), K offset, V offset
     ("bf16", 2, 16, (1, 1, 3, 10), 922, 931),   # K: ((3*2+1)*16+3)*8+2 ; V: (3*16+10)*16+3
@@ -73,6 +75,10 @@ LAYOUT_CASES = [
     ("bf16", 2, 16, (0, 0, 0, 8), 128, 128),
     ("bf16", 2, 16, (2, 0, 15, 15), 1279, 1279),
     ("f32", 1, 8, (1, 0, 2, 5), 201, 210),      # K: ((1*2+1)*16+2)*4+1 ; V: (1*8+5)*16+2
+    ("bf16", 2, 16, (0, 1, 4, 3), 291, 312),    # K: ((1*2+0)*16+4)*8+3 ; V: (1*16+3)*16+8
+    ("bf16", 2, 16, (1, 0, 9, 12), 716, 709),   # K: ((2*2+1)*16+9)*8+4 ; V: (2*16+12)*16+5
+    ("bf16", 2, 16, (0, 0, 11, 0), 88, 7),      # K: (0*16+11)*8+0      ; V: 0*16+7
+    ("f32", 1, 8, (0, 0, 6, 1), 25, 26),        # K: (0*16+6)*4+1       ; V: 1*16+10
 ]
 
 
