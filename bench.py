@@ -2,8 +2,10 @@
 """Decode-step benchmark of the paged KV cache on one MI355X.
 
 A step is one pass of the whole device path over one batch: copy-on-write block
-copies (when the step's reservation produced any), append of the batch's new
-tokens into their slots, the decode partition pass and the log-sum-exp merge.
+copies (when the step's reservation produced any), then pa_decode_step, which
+appends the batch's new tokens into their slots and attends (on the even-split
+path the append happens inside the attention kernel), then the log-sum-exp
+merge.
 The host reservation (slots, copy pairs, block tables) is done by the C++
 block manager before the timed region, and the same step is replayed every
 iteration (append and copy are idempotent, so every replay does the full work).
@@ -42,6 +44,9 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
+    ap.add_argument("--fused-step", action="store_true",
+                    help="run each step as one pa_decode_step call (append fused into the "
+                         "attention kernel on the even split) and time that call")
     ap.add_argument("--no-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -144,10 +149,24 @@ def main():
     cache = pk.PagedKVCache(case.num_blocks, case.num_kv_heads, case.head_dim, td, dev,
                             free_order=case.free_order, fill=0.0)
     cache.replay(case.script, case.rows, case.k_tok, case.v_tok)
-    # host reservation for the step (C++ block manager), timed on its own
+    # host reservation for the step (C++ block manager), timed on its own on a
+    # replica manager: slots + copy pairs + block-table export for the batch
+    replica = pk.BlockManager(case.num_blocks, 16, case.free_order)
+    for op in case.script:
+        if op[0] == "add":
+            replica.add_seq(op[1], op[2])
+        elif op[0] == "extend":
+            replica.extend(op[1], op[2])
+        elif op[0] == "fork":
+            replica.fork(op[1], op[2])
+        else:
+            replica.free_seq(op[1])
+    mb_plan = max(-(-int(x) // 16) for x in case.lens)
     t0 = time.perf_counter()
-    plan = cache.plan_step(case.batch)
+    replica.append_slots(case.batch)
+    replica.block_tables(case.batch, mb_plan)
     host_plan_us = (time.perf_counter() - t0) * 1e6
+    plan = cache.plan_step(case.batch)
     nr = torch.as_tensor(case.new_rows(), device=dev)
     k_new = case.k_tok.index_select(0, nr).contiguous()
     v_new = case.v_tok.index_select(0, nr).contiguous()
@@ -175,38 +194,48 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     calls = []
     for kp, vp in layers:
-        dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
-               plan.d_tables.data_ptr(), plan.d_lens.data_ptr(), B, Hq, Hkv, D, 16, N, MB,
-               plan.max_context_len, case.scale, P, dt, ws.data_ptr(), ws.numel(), stream)
+        # pa_decode_step: append of the step's tokens + attention (+ merge)
+        dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), k_new.data_ptr(),
+               v_new.data_ptr(), plan.d_slots.data_ptr(), plan.d_tables.data_ptr(),
+               plan.d_lens.data_ptr(), B, Hq, Hkv, D, 16, N, MB, plan.max_context_len,
+               case.scale, P, dt, ws.data_ptr(), ws.numel(), stream)
+        dec_sep = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                   plan.d_tables.data_ptr(), plan.d_lens.data_ptr(), B, Hq, Hkv, D, 16, N, MB,
+                   plan.max_context_len, case.scale, P, dt, ws.data_ptr(), ws.numel(), stream)
+        app = (kp.data_ptr(), vp.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+               plan.d_slots.data_ptr(), B, N, Hkv, D, 16, dt, stream)
         calls.append((
             (kp.data_ptr(), vp.data_ptr(), plan.d_cows.data_ptr(), ncow, N, Hkv, D, 16, dt,
              stream),
-            (kp.data_ptr(), vp.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
-             plan.d_slots.data_ptr(), B, N, Hkv, D, 16, dt, stream),
-            dec))
-    f_copy, f_app = L.pa_copy_blocks, L.pa_cache_append
-    f_part, f_merge = L.pa_decode_partial, L.pa_decode_merge
+            dec, app, dec_sep))
+    f_copy, f_step = L.pa_copy_blocks, L.pa_decode_step
+    f_app, f_part, f_merge = L.pa_cache_append, L.pa_decode_partial, L.pa_decode_merge
 
     def step(i, ev=None):
-        c_copy, c_app, c_dec = calls[i % len(calls)]
+        c_copy, c_dec, c_app, c_dec_sep = calls[i % len(calls)]
         if ncow:
             check(f_copy(*c_copy), "pa_copy_blocks")
+        if args.fused_step:
+            if ev is not None:
+                ev[0].record()
+            check(f_step(*c_dec), "pa_decode_step")
+            if ev is not None:
+                ev[1].record()
+            return
         check(f_app(*c_app), "pa_cache_append")
         if ev is not None:
             ev[0].record()
-        check(f_part(*c_dec), "pa_decode_partial")
+        check(f_part(*c_dec_sep), "pa_decode_partial")     # the attention kernel
         if ev is not None:
             ev[1].record()
-        check(f_merge(*c_dec), "pa_decode_merge")
-        if ev is not None:
-            ev[2].record()
+        check(f_merge(*c_dec_sep), "pa_decode_merge")
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    evs = None if args.no_events else [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    evs = None if args.no_events else [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                                        for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -240,13 +269,18 @@ def main():
            "host_plan_us": round(host_plan_us, 1),
            "wall_ms_timed_region": round(wall_ms, 3)}
     if evs:
-        part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        dec_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+        part_ms = dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         tables_bytes = int(sum(-(-int(x) // 16) for x in case.lens)) * 4
         alg = kv_bytes + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
         achieved = alg / (part_ms * 1e-3) / 1e9
-        res["decode_us"] = round(dec_ms * 1e3, 3)
-        res["roofline"] = {"kernel": "decode partition pass (pa_decode_partial)",
+        res["attention_kernel_us"] = round(dec_ms * 1e3, 3)
+        if not args.fused_step:
+            kname = "attention partition kernel (pa_decode_partial)"
+        elif P_used == 0:
+            kname = "pa_decode_step: attention kernel with the append fused in, then the merge"
+        else:
+            kname = "pa_decode_step: append, attention and merge kernels"
+        res["roofline"] = {"kernel": kname,
                            "bound": "hbm", "achieved": round(achieved, 2),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),

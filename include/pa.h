@@ -166,15 +166,27 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
                          int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, pa_dtype dtype, void* stream);
 
-/* Partition size (tokens) pa_decode uses for these arguments: the value passed
- * if nonzero (a multiple of block_size), else the library's choice.  Returns 0
- * for invalid arguments. */
+/* How pa_decode splits contexts for these arguments; partition_size is
+ *   > 0 (a multiple of 16): fixed partitions of that many tokens;
+ *   0: the library's choice (fixed partitions of 256 tokens);
+ *   -1: an even split of the batch's work over the GPU's waves (matrix-core
+ *       path only; fp32 and the plain-FMA kernel use the default partitions).
+ * Returns the partition size in tokens for fixed partitions, 0 for the even
+ * split, -1 for invalid arguments.
+ *   Fixed partitions: partition p of a sequence covers tokens
+ *     [p*P, (p+1)*P); each is attended by one wave, merged when more than one.
+ *   Even split: the (sequence, KV head, 32-token pair) units of the whole
+ *     batch are cut into equal contiguous chunks, one per wave; a (sequence,
+ *     head) cut into several chunks is merged the same way; pa_decode_step
+ *     appends inside the attention kernel. */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype);
 
 /* Device workspace bytes pa_decode needs for these arguments (0 when every
- * sequence fits in one partition).  Returns 0 for invalid arguments. */
+ * sequence fits in one partition).  Returns 0 for invalid arguments.  The
+ * workspace holds the partials of split contexts; its contents need no
+ * initialisation and it can be reused call after call. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype);
@@ -184,8 +196,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   out[b][h] = softmax_t(scale * q[b][h] . K_b[t]) weighted sum of V_b[t],
  * t in [0, L), where K_b/V_b are KV head h/G of the tokens reached through
  * block_tables[b] in logical order; accumulation in fp32.  L = 0 gives zeros.
- * Contexts longer than one partition are split into partitions whose partial
- * (max, sum, weighted V) are merged with a log-sum-exp reduction.
+ * The context is split (fixed partitions, or an even split of the batch's
+ * work; see pa_decode_partition_size) and the partial (max, sum, weighted V)
+ * of the pieces are merged with a log-sum-exp reduction.
  *   out: device float [num_seqs][Hq][D].
  *   workspace: device, at least pa_decode_workspace_bytes(...) bytes,
  *   exclusively owned by this call until it completes on `stream`.
@@ -205,8 +218,9 @@ pa_status pa_decode(float* out, const void* q, const void* k_pool, const void* v
  *   pa_decode_partial: the partition kernel.  Sequences that fit in one
  *     partition get their final out rows; longer ones leave per-partition
  *     partials (running max, running sum, weighted V sum) in the workspace.
- *   pa_decode_merge: the log-sum-exp merge of those partials into out (no
- *     launch when every sequence fits in one partition).
+ *   pa_decode_merge: the log-sum-exp merge of those partials into out (with
+ *     the even split it also writes the rows of empty sequences; with fixed
+ *     partitions nothing is launched when every sequence fits in one).
  * pa_decode(...) == pa_decode_partial(...) then pa_decode_merge(...) on the
  * same stream.  Separately, they let a caller time the partition pass or
  * combine partials produced elsewhere (e.g. a context split across devices). */
@@ -224,6 +238,25 @@ pa_status pa_decode_merge(float* out, const void* q, const void* k_pool, const v
                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                           int32_t partition_size, pa_dtype dtype, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* One decode step: appends each sequence's new token and attends, with the
+ * result of pa_cache_append(k_pool, v_pool, k_new, v_new, slot_mapping,
+ * num_seqs, ...) followed by pa_decode(...).  Row b of k_new/v_new
+ * ([num_seqs][Hkv][D], KV dtype) is sequence b's token at position
+ * context_lens[b] - 1, and slot_mapping[b] (device int64) must be the slot of
+ * that position in block_tables[b] (or -1: then the pool is not written but
+ * the token still takes part in the attention).  On the even-split path the
+ * append is done inside the attention kernel (one launch fewer); otherwise
+ * the two kernels run back to back.  Copy-on-write copies of the step must
+ * be issued (pa_copy_blocks) before this call on the same stream. */
+pa_status pa_decode_step(float* out, const void* q, void* k_pool, void* v_pool,
+                         const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                         int32_t partition_size, pa_dtype dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Reassembles the logically contiguous cache through the block tables:
  * k_out/v_out device [num_seqs][Hkv][max_context_len][D] in the KV dtype,

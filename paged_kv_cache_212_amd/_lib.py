@@ -61,6 +61,9 @@ SIGNATURES = {
                                     _i32, _i32, _i32, _f32, _i32, C.c_int, _vp, _sz, _vp]),
     "pa_decode_merge": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _f32, _i32, C.c_int, _vp, _sz, _vp]),
+    "pa_decode_step": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _i32, _f32, _i32, C.c_int, _vp, _sz,
+                                 _vp]),
     "pa_gather_kv": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, C.c_int, _vp]),
 }

@@ -102,13 +102,21 @@ class PagedKVCache:
 
     def step(self, plan: StepPlan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
              out: torch.Tensor | None = None, scale=None, partition_size: int = 0,
-             workspace=None, stream=None):
-        """Copy-on-write, append the new tokens, then decode attention (all on device)."""
+             workspace=None, stream=None, fused: bool = True):
+        """Copy-on-write, append the new tokens, then decode attention (all on device).
+
+        fused: append and attend with one pa_decode_step call; otherwise
+        pa_cache_append then pa_decode."""
         if plan.cows.shape[0]:
             ops.copy_blocks(self.k_pool, self.v_pool, plan.d_cows, stream)
-        ops.cache_append(self.k_pool, self.v_pool, k_new, v_new, plan.d_slots, stream)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        ops.decode(out, q, self.k_pool, self.v_pool, plan.d_tables, plan.d_lens,
-                   plan.max_context_len, scale, partition_size, workspace, stream)
+        if fused:
+            ops.decode_step(out, q, self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
+                            plan.d_tables, plan.d_lens, plan.max_context_len, scale,
+                            partition_size, workspace, stream)
+        else:
+            ops.cache_append(self.k_pool, self.v_pool, k_new, v_new, plan.d_slots, stream)
+            ops.decode(out, q, self.k_pool, self.v_pool, plan.d_tables, plan.d_lens,
+                       plan.max_context_len, scale, partition_size, workspace, stream)
         return out

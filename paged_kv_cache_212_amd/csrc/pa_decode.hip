@@ -26,6 +26,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 
 #include "pa_device.h"
 
@@ -40,6 +41,12 @@ struct Params {
   float* part_m;       // [B][Hq][maxP]   running max (log2 domain) per partition
   float* part_l;       // [B][Hq][maxP]   sum of exp2(s - m)
   float* part_acc;     // [B][Hq][maxP][D] sum of exp2(s - m) * v
+  int* counters;       // [B][Hkv] slots written for a (sequence, KV head) (even split)
+  const void* k_new;   // [B][Hkv][D] new token of each sequence (fused append), or null
+  const void* v_new;
+  const int64_t* slots;  // [B] slot of each new token (fused append)
+  void* kpool_w;       // writable pools (fused append)
+  void* vpool_w;
   const void* q;       // [B][Hq][D]
   const void* kpool;
   const void* vpool;
@@ -284,7 +291,7 @@ struct Mfma<F16> {
   }
 };
 
-// Two blocks (A = logical block 2q, B = 2q+1 of the partition) per iteration.
+// Two blocks (A = block 2q, B = block 2q+1 of the range) per iteration.
 // Lane = 16*j + n (n = lane % 16, j = lane / 16).
 //   QK, half hh in {0,1}: S^T (16 rows x 16 heads) = K rows . Q^T where row
 //     i < 8 is token i + 8*hh of A and row i >= 8 token i - 8 + 8*hh of B.
@@ -301,62 +308,66 @@ struct Mfma<F16> {
 //   O result: lane (dim t*16 + n, j) holds heads 4j + e.
 // K tile (block, head) bytes: [D/8 chunks][16 tokens][8 dims] -> chunk
 // kk*4 + j, token r at (kk*4 + j)*256 + 16*r.
-//
-// One wave per (KV head, partition, sequence).  NPAIR block pairs are in
-// flight in a register ring; the loop is peeled so the steady state issues
-// its loads unconditionally (static wait counts) and the tail issues none.
-template <typename T, int D, int NPAIR, bool kSmallGroup>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
+
+// Online-softmax state of one wave for one (sequence, KV head) range.
+template <int D>
+struct WaveState {
+  float m_run;          // running max of lane's head n (log2 domain)
+  float l_lane;         // this lane's share of the running sum for head n
+  f32x4_t acc[D / 16];  // O rows 4j+e, dims t*16+n
+  bool bad;             // a table entry of the range was out of the pool
+};
+
+// Attends over blocks [blk_begin, blk_begin + nblk) of sequence b, KV head g,
+// masking positions >= tok_end, and accumulates into st.  NPAIR block pairs
+// are kept in flight in a register ring; the loop is peeled so the steady
+// state issues its loads unconditionally (static wait counts) and the tail
+// issues none.
+// with_new: the range ends at the sequence's last position, which holds the
+// step's new token: its K/V are taken from k_new/v_new (substituted in the
+// registers of the last pair) and written into the pool slot.
+template <typename T, int D, int NPAIR, bool kSmallGroup, bool with_new>
+__device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int blk_begin,
+                                             int nblk, int tok_end, WaveState<D>& st) {
   constexpr int NKK = D / 32;
   constexpr int NTL = D / 16;
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
-
-  const int g = blockIdx.x % pr.Hkv, p = blockIdx.x / pr.Hkv, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
   const int G = pr.G;
-  const int L = pr.lens[b];
-  if (!len_valid(L, pr) || L == 0) {
-    if (p == 0) write_trivial_rows(pr, b, g, L);
-    return;
-  }
-  const int np = (L + pr.P - 1) / pr.P;
-  if (p >= np) return;
-  const int tok0 = p * pr.P, tok1 = min(L, tok0 + pr.P);
-  const int blk0 = tok0 / kBlockSize;
-  const int nblk = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
   const int npair = (nblk + 1) >> 1;
 
-  uint4 qv[NKK];
+  // Q operand in LDS, in lane order (lane reads back its own 16 bytes per kk):
+  // keeps 16 registers free for the prefetch ring.
+  __shared__ uint4 s_q[NKK][64];
   {
     const uint16_t* qb = static_cast<const uint16_t*>(pr.q) +
                          (static_cast<int64_t>(b) * pr.Hq + g * G + n) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qv[kk] = n < G ? *reinterpret_cast<const uint4*>(qb + kk * 32 + j * 8)
-                     : make_uint4(0, 0, 0, 0);
+      s_q[kk][lane] = n < G ? *reinterpret_cast<const uint4*>(qb + kk * 32 + j * 8)
+                            : make_uint4(0, 0, 0, 0);
   }
 
   const char* kbase = static_cast<const char*>(pr.kpool) + g * kTileBytes;
   const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
   const int64_t block_stride = static_cast<int64_t>(pr.Hkv) * kTileBytes;
-  const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks + blk0;
+  const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks + blk_begin;
 
   // Table entries, 64 per register (lane i holds entry 64*c + i of chunk c).
-  bool bad = false;
   auto load_chunk = [&](int c) -> int {
     const int k = c * 64 + lane;
     const int e = k < nblk ? trow[k] : 0;
     const bool lane_bad = k < nblk && (e < 0 || e >= pr.num_blocks);
-    if (__any(lane_bad)) bad = true;
+    if (__any(lane_bad)) st.bad = true;
     return lane_bad ? 0 : e;
   };
   int chunk = 0;
   int tcur = load_chunk(0);
   int tnext = nblk > 64 ? load_chunk(1) : 0;
-  // Physical block of partition block k (k increases across calls); k >= nblk
+  // Physical block of range block k (k increases across calls); k >= nblk
   // (the missing half of a last, odd pair) maps to block nblk-1, whose lines
-  // are being fetched by the same instruction anyway.
+  // the same instruction fetches anyway.
   auto phys_of = [&](int k) -> int {
     if (k >= nblk) k = nblk - 1;
     const int c = k >> 6;
@@ -372,8 +383,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
   uint4 vb[NPAIR][NTL];
   auto issue = [&](int u, int q) {
     const int pa = phys_of(2 * q), pb = phys_of(2 * q + 1);
-    const int mine = (n < 8) ? pa : pb;             // K row block of this lane
-    const char* kt = kbase + mine * block_stride + (n & 7) * 16 + j * 256;
+    const char* kt = kbase + ((n < 8) ? pa : pb) * block_stride + (n & 7) * 16 + j * 256;
     const char* vt = vbase + ((j >> 1) ? pb : pa) * block_stride + n * 32 + (j & 1) * 16;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -384,73 +394,131 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
     for (int t = 0; t < NTL; ++t) vb[u][t] = *reinterpret_cast<const uint4*>(vt + t * 512);
   };
 
-  float m_run = -INFINITY, l_lane = 0.f;
-  f32x4_t acc[NTL];
+  // The new token sits at position tok_end - 1, in the range's last pair:
+  // half `sel` (block A or B of the pair), in-block token tn.  Its K/V rows
+  // are staged in LDS at the start of the range, so the substitution into the
+  // last pair's registers costs no global round trip.
+  __shared__ uint32_t s_new[2][D / 2];   // [K|V][D bf16/fp16 values, 2 per word]
+  const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
+  uint32_t stage_k = 0, stage_v = 0;
+  if (with_new && lane < D / 2) {
+    stage_k = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.k_new) + nrow)[lane];
+    stage_v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.v_new) + nrow)[lane];
+  }
+  auto substitute_new = [&](int u) {
+    const int pos = tok_end - 1;
+    const int sel = pos / kBlockSize - blk_begin - 2 * (npair - 1);
+    const int tn = pos % kBlockSize;
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
+    // K: lane row n holds token (n & 7) + 8*hh of block n >> 3
+    if ((n >> 3) == sel && (n & 7) == (tn & 7)) {
 #pragma unroll
-  for (int t = 0; t < NTL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int hh = 0; hh < 2; ++hh)
+        if (hh == (tn >> 3)) {
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk)
+            kb[u][hh][kk] = *reinterpret_cast<const uint4*>(kn + kk * 32 + j * 8);
+        }
+    }
+    // V: lane group j holds block j >> 1, tokens 4*(j & 1) + {0..3} as
+    // elements 0..3 and 8 + 4*(j & 1) + {0..3} as elements 4..7
+    if ((j >> 1) == sel && (j & 1) == ((tn >> 2) & 1)) {
+      const int e = (tn & 3) + 4 * (tn >> 3);
+      const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      const int sh = (e & 1) * 16, dw = e >> 1;
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        const uint32_t val = static_cast<uint32_t>(vn[t * 16 + n]) << sh;
+        uint4& vv = vb[u][t];
+        vv.x = dw == 0 ? ((vv.x & keep) | val) : vv.x;
+        vv.y = dw == 1 ? ((vv.y & keep) | val) : vv.y;
+        vv.z = dw == 2 ? ((vv.z & keep) | val) : vv.z;
+        vv.w = dw == 3 ? ((vv.w & keep) | val) : vv.w;
+      }
+    }
+    // write the token into its pool slot (skipped when out of range)
+    const int64_t slot = pr.slots[b];
+    if (slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
+      const int64_t blk = slot / kBlockSize;
+      const int ts = static_cast<int>(slot % kBlockSize);
+      uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
+      uint16_t* vt = static_cast<uint16_t*>(pr.vpool_w) + tile_base(blk, g, pr.Hkv, D);
+      if (lane < D / 8)
+        *reinterpret_cast<uint4*>(kt + (lane * kBlockSize + ts) * 8) =
+            *reinterpret_cast<const uint4*>(kn + lane * 8);
+#pragma unroll
+      for (int d = lane; d < D; d += 64) vt[d * kBlockSize + v_slot(ts)] = vn[d];
+    }
+  };
 
   auto compute = [&](int u, int q) {
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      s0 = Mfma<T>::qk(kb[u][0][kk], qv[kk], s0);
-      s1 = Mfma<T>::qk(kb[u][1][kk], qv[kk], s1);
+      const uint4 qkk = s_q[kk][lane];
+      s0 = Mfma<T>::qk(kb[u][0][kk], qkk, s0);
+      s1 = Mfma<T>::qk(kb[u][1][kk], qkk, s1);
     }
-    // position of S_hh[e] in the sequence
-    const int base = (blk0 + 2 * q + (j >> 1)) * kBlockSize + 4 * (j & 1);
+    // sequence position of S_hh[e]
+    const int base = (blk_begin + 2 * q + (j >> 1)) * kBlockSize + 4 * (j & 1);
     float sv[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sv[e] = (base + e < tok1) ? s0[e] * pr.scale_log2 : -INFINITY;
-      sv[4 + e] = (base + 8 + e < tok1) ? s1[e] * pr.scale_log2 : -INFINITY;
+      sv[e] = (base + e < tok_end) ? s0[e] * pr.scale_log2 : -INFINITY;
+      sv[4 + e] = (base + 8 + e < tok_end) ? s1[e] * pr.scale_log2 : -INFINITY;
     }
     float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m_run, bm);
-    if (__any(mn != m_run)) {
+    const float mn = fmaxf(st.m_run, bm);
+    if (__any(mn != st.m_run)) {
       // running max moved for some head: rescale rows 4j+e by 2^(m_old - m_new)
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      l_lane *= alpha;
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run - mn);
+      st.l_lane *= alpha;
       if constexpr (kSmallGroup) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), e));
 #pragma unroll
-          for (int t = 0; t < NTL; ++t) acc[t][e] *= ah;
+          for (int t = 0; t < NTL; ++t) st.acc[t][e] *= ah;
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float ah = __shfl(alpha, 4 * j + e);
 #pragma unroll
-          for (int t = 0; t < NTL; ++t) acc[t][e] *= ah;
+          for (int t = 0; t < NTL; ++t) st.acc[t][e] *= ah;
         }
       }
-      m_run = mn;
+      st.m_run = mn;
     }
     float pe[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - mn);
-    l_lane += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+    st.l_lane += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
     uint4 phi, plo;
     Mfma<T>::split8(pe, phi, plo);
-    uint4 vmask = make_uint4(~0u, ~0u, ~0u, ~0u);
-    if ((blk0 + 2 * q + 2) * kBlockSize > tok1) {
-      // the pair reaches past the end of the sequence: zero V of positions
-      // >= L so unused slots (even NaN) cannot reach the output through 0*v
-      vmask.x = (base + 0 < tok1 ? 0x0000FFFFu : 0u) | (base + 1 < tok1 ? 0xFFFF0000u : 0u);
-      vmask.y = (base + 2 < tok1 ? 0x0000FFFFu : 0u) | (base + 3 < tok1 ? 0xFFFF0000u : 0u);
-      vmask.z = (base + 8 < tok1 ? 0x0000FFFFu : 0u) | (base + 9 < tok1 ? 0xFFFF0000u : 0u);
-      vmask.w = (base + 10 < tok1 ? 0x0000FFFFu : 0u) | (base + 11 < tok1 ? 0xFFFF0000u : 0u);
+    if ((blk_begin + 2 * q + 2) * kBlockSize > tok_end) {
+      // the pair reaches past the end of the range: zero V of masked
+      // positions so unused slots (even NaN) cannot reach the output via 0*v
+      const uint32_t mx = (base + 0 < tok_end ? 0x0000FFFFu : 0u) | (base + 1 < tok_end ? 0xFFFF0000u : 0u);
+      const uint32_t my = (base + 2 < tok_end ? 0x0000FFFFu : 0u) | (base + 3 < tok_end ? 0xFFFF0000u : 0u);
+      const uint32_t mz = (base + 8 < tok_end ? 0x0000FFFFu : 0u) | (base + 9 < tok_end ? 0xFFFF0000u : 0u);
+      const uint32_t mw = (base + 10 < tok_end ? 0x0000FFFFu : 0u) | (base + 11 < tok_end ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        vb[u][t].x &= mx;
+        vb[u][t].y &= my;
+        vb[u][t].z &= mz;
+        vb[u][t].w &= mw;
+      }
     }
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
-      const uint4 vv = make_uint4(vb[u][t].x & vmask.x, vb[u][t].y & vmask.y,
-                                  vb[u][t].z & vmask.z, vb[u][t].w & vmask.w);
-      acc[t] = Mfma<T>::pv8(phi, vv, acc[t]);
-      acc[t] = Mfma<T>::pv8(plo, vv, acc[t]);
+      st.acc[t] = Mfma<T>::pv8(phi, vb[u][t], st.acc[t]);
+      st.acc[t] = Mfma<T>::pv8(plo, vb[u][t], st.acc[t]);
     }
   };
 
@@ -458,6 +526,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
 #pragma unroll
   for (int u = 0; u < NPAIR; ++u)
     if (u < npair) issue(u, u);
+  if constexpr (with_new) {
+    if (lane < D / 2) {
+      s_new[0][lane] = stage_k;
+      s_new[1][lane] = stage_v;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
   int q0 = 0;
   for (; q0 + 2 * NPAIR <= npair; q0 += NPAIR) {
 #pragma unroll
@@ -466,48 +541,261 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
       issue(u, q0 + u + NPAIR);
     }
   }
-  // tail: at most 2*NPAIR - 1 pairs left, the first min(NPAIR, left) in flight
+  // tail: at most 2*NPAIR - 1 pairs left, the first min(NPAIR, left) in
+  // flight; the range's last pair is among them
 #pragma unroll
   for (int u = 0; u < NPAIR; ++u) {
     if (q0 + u < npair) {
+      if (with_new && q0 + u == npair - 1) substitute_new(u);
       compute(u, q0 + u);
       if (q0 + u + NPAIR < npair) issue(u, q0 + u + NPAIR);
     }
   }
 #pragma unroll
   for (int u = 0; u < NPAIR; ++u)
-    if (q0 + NPAIR + u < npair) compute(u, q0 + NPAIR + u);
+    if (q0 + NPAIR + u < npair) {
+      if (with_new && q0 + NPAIR + u == npair - 1) substitute_new(u);
+      compute(u, q0 + NPAIR + u);
+    }
+}
 
-  l_lane += __shfl_xor(l_lane, 16);
-  l_lane += __shfl_xor(l_lane, 32);
-  if (bad) {
-    m_run = 0.f;
-    l_lane = __builtin_nanf("");
+template <int D>
+__device__ __forceinline__ void reset_state(WaveState<D>& st) {
+  st.m_run = -INFINITY;
+  st.l_lane = 0.f;
+  st.bad = false;
 #pragma unroll
-    for (int t = 0; t < NTL; ++t) acc[t] = f32x4_t{l_lane, l_lane, l_lane, l_lane};
-  }
+  for (int t = 0; t < D / 16; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
 
+// Writes the wave's result for (b, g): the normalised output rows when the
+// range covered the whole sequence (slot < 0), else the partial
+// (max, sum, weighted V) into slot `slot` of the workspace rows.
+template <int D>
+__device__ __forceinline__ void emit_state(const Params& pr, int b, int g, int slot,
+                                           WaveState<D>& st) {
+  constexpr int NTL = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, j = lane >> 4;
+  const int G = pr.G;
+  float l = st.l_lane;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  float m = st.m_run;
+  if (st.bad) {
+    m = 0.f;
+    l = __builtin_nanf("");
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) st.acc[t] = f32x4_t{l, l, l, l};
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int h = 4 * j + e;
-    const float mh = __shfl(m_run, h);
-    const float lh = __shfl(l_lane, h);
+    const float mh = __shfl(m, h);
+    const float lh = __shfl(l, h);
     if (h < G) {
       const int64_t row = static_cast<int64_t>(b) * pr.Hq + g * G + h;
       const float inv = 1.0f / lh;
 #pragma unroll
       for (int t = 0; t < NTL; ++t) {
         const int d = t * 16 + n;
-        if (np == 1)
-          pr.out[row * D + d] = acc[t][e] * inv;
+        if (slot < 0)
+          pr.out[row * D + d] = st.acc[t][e] * inv;
         else
-          pr.part_acc[(row * pr.maxP + p) * D + d] = acc[t][e];
+          pr.part_acc[(row * pr.maxP + slot) * D + d] = st.acc[t][e];
       }
-      if (np > 1 && n == 0) {
-        pr.part_m[row * pr.maxP + p] = mh;
-        pr.part_l[row * pr.maxP + p] = lh;
+      if (slot >= 0 && n == 0) {
+        pr.part_m[row * pr.maxP + slot] = mh;
+        pr.part_l[row * pr.maxP + slot] = lh;
       }
     }
+  }
+}
+
+// Fixed partitions: one wave per (KV head, partition, sequence); grid
+// x = head + Hkv * partition (the heads of a partition are dispatched
+// together), z = sequence.
+template <typename T, int D, int NPAIR, bool kSmallGroup>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
+  const int g = blockIdx.x % pr.Hkv, p = blockIdx.x / pr.Hkv, b = blockIdx.z;
+  const int L = pr.lens[b];
+  if (!len_valid(L, pr) || L == 0) {
+    if (p == 0) write_trivial_rows(pr, b, g, L);
+    return;
+  }
+  const int np = (L + pr.P - 1) / pr.P;
+  if (p >= np) return;
+  const int tok0 = p * pr.P, tok1 = min(L, tok0 + pr.P);
+  WaveState<D> st;
+  reset_state(st);
+  attend_range<T, D, NPAIR, kSmallGroup, false>(pr, b, g, tok0 / kBlockSize,
+                                                (tok1 - tok0 + kBlockSize - 1) / kBlockSize,
+                                                tok1, st);
+  emit_state(pr, b, g, np == 1 ? -1 : p, st);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split.  The work of a step is the list of units (sequence b, KV
+// head g, block pair q), ordered by b, then g, then q.  Sequence b owns
+// Hkv * npair(b) consecutive units.  With W waves the list is cut into W
+// equal chunks of C units (C >= kMinChunkPairs); each wave attends over its
+// chunk, which may cover the end of one (b, g) range and the start of the
+// next.  A (b, g) range cut into several chunks leaves one partial per chunk,
+// merged by merge_split_kernel; a range inside one chunk is written final.
+// ---------------------------------------------------------------------------
+constexpr int kMinChunkPairs = 4;
+
+__device__ __forceinline__ int pairs_of(int L, const Params& pr) {
+  return (len_valid(L, pr) && L > 0) ? ((L + kBlockSize - 1) / kBlockSize + 1) >> 1 : 0;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+struct SplitPlan {
+  int total;  // units
+  int C;      // units per chunk
+  int chunks; // chunks with work
+};
+
+__device__ __forceinline__ SplitPlan split_plan(const Params& pr, int W) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int c = 0; c < pr.B; c += 64) {
+    const int b = c + lane;
+    total += wave_sum(b < pr.B ? pairs_of(pr.lens[b], pr) : 0);
+  }
+  total *= pr.Hkv;
+  SplitPlan sp;
+  sp.total = total;
+  sp.C = max(kMinChunkPairs, (total + W - 1) / W);
+  sp.chunks = (total + sp.C - 1) / sp.C;
+  return sp;
+}
+
+// First unit of sequence b (units of all sequences before b).
+__device__ __forceinline__ int units_before(const Params& pr, int b) {
+  const int lane = threadIdx.x & 63;
+  int acc = 0;
+  for (int c = 0; c < b; c += 64) {
+    const int s = c + lane;
+    acc += wave_sum(s < b ? pairs_of(pr.lens[s], pr) : 0);
+  }
+  return acc * pr.Hkv;
+}
+
+// The sequence whose units contain unit u, and the first unit of that
+// sequence (u < total).
+__device__ __forceinline__ void locate(const Params& pr, int u, int& b_out, int& base_out) {
+  const int lane = threadIdx.x & 63;
+  int carried = 0;
+  for (int c = 0; c < pr.B; c += 64) {
+    const int b = c + lane;
+    const int units = (b < pr.B ? pairs_of(pr.lens[b], pr) : 0) * pr.Hkv;
+    const int incl = carried + wave_incl_scan(units);
+    const uint64_t hit = __ballot(b < pr.B && incl > u);
+    if (hit) {
+      const int k = __builtin_ctzll(hit);
+      b_out = c + k;
+      base_out = __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(units, k);
+      return;
+    }
+    carried = __builtin_amdgcn_readlane(incl, 63);
+  }
+  b_out = pr.B;
+  base_out = carried;
+}
+
+template <typename T, int D, int NPAIR, bool kSmallGroup>
+__global__ __launch_bounds__(64, 2) void decode_split_kernel(Params pr) {
+  const int w = blockIdx.x;
+  const SplitPlan sp = split_plan(pr, gridDim.x);
+  if (w >= sp.chunks) return;
+  const int u_begin = w * sp.C, u_end = min(sp.total, u_begin + sp.C);
+  int b, base;
+  locate(pr, u_begin, b, base);
+  int u = u_begin;
+  WaveState<D> st;
+  while (u < u_end) {
+    const int L = pr.lens[b];
+    const int npb = pairs_of(L, pr);
+    const int g = (u - base) / npb;
+    const int q0 = (u - base) - g * npb;
+    const int range_first = base + g * npb;                  // first unit of (b, g)
+    const int seg_end = min(u_end, range_first + npb);
+    const int nq = seg_end - u;
+    const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
+    const int blk_begin = 2 * q0;
+    const int nblk = min(2 * (q0 + nq), nblk_seq) - blk_begin;
+    const int tok_end = min(L, (blk_begin + nblk) * kBlockSize);
+    reset_state(st);
+    if (pr.k_new != nullptr && tok_end == L)
+      attend_range<T, D, NPAIR, kSmallGroup, true>(pr, b, g, blk_begin, nblk, tok_end, st);
+    else
+      attend_range<T, D, NPAIR, kSmallGroup, false>(pr, b, g, blk_begin, nblk, tok_end, st);
+    const int first_chunk = range_first / sp.C;
+    const int nslots = (range_first + npb - 1) / sp.C - first_chunk + 1;
+    emit_state(pr, b, g, nslots == 1 ? -1 : w - first_chunk, st);
+    // the wave holding the range's first unit records how many slots the
+    // merge has to combine
+    if (u == range_first && (threadIdx.x & 63) == 0)
+      pr.counters[static_cast<int64_t>(b) * pr.Hkv + g] = nslots;
+    u = seg_end;
+    if (u >= base + pr.Hkv * npb) {                           // next sequence with work
+      base = u;
+      do {
+        ++b;
+      } while (b < pr.B && pairs_of(pr.lens[b], pr) == 0);
+    }
+  }
+}
+
+// Merge for the balanced split: grid (Hkv, B), 256 threads; merges the G
+// query-head rows of (b, g) over the slots the partition kernel recorded, and
+// writes the rows of empty (zeros) and out-of-bounds (NaN) sequences, which
+// own no units.
+template <int D>
+__global__ __launch_bounds__(256) void merge_split_kernel(Params pr) {
+  constexpr int NT = 256;
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int G = pr.G;
+  const int L = pr.lens[b];
+  const int64_t row0 = static_cast<int64_t>(b) * pr.Hq + g * G;
+  if (!len_valid(L, pr) || L == 0) {
+    const float v = (L == 0) ? 0.f : __builtin_nanf("");
+    for (int i = tid; i < G * D; i += NT) pr.out[row0 * D + i] = v;
+    return;
+  }
+  const int ns = pr.counters[static_cast<int64_t>(b) * pr.Hkv + g];
+  if (ns <= 1) return;                                         // written final
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D, d = i % D;
+    const int64_t row = row0 + h;
+    const float* pm = pr.part_m + row * pr.maxP;
+    const float* pl = pr.part_l + row * pr.maxP;
+    const float* pa = pr.part_acc + row * pr.maxP * D + d;
+    float M = -INFINITY;
+    for (int k = 0; k < ns; ++k) M = fmaxf(M, pm[k]);
+    float num = 0.f, den = 0.f;
+    for (int k = 0; k < ns; ++k) {
+      const float wgt = exp2f(pm[k] - M);
+      den = fmaf(wgt, pl[k], den);
+      num = fmaf(wgt, pa[static_cast<int64_t>(k) * D], num);
+    }
+    pr.out[row * D + d] = num / den;
   }
 }
 
@@ -571,25 +859,68 @@ Path path_from_env() {
   return (v && std::strcmp(v, "generic") == 0) ? Path::kGeneric : Path::kAuto;
 }
 
-constexpr int kDefaultPartition = 256;
+constexpr int kDefaultPartition = 256;  // fixed-partition size when none is given
 constexpr int kPairsInFlight = 2;
+constexpr int kSplitWavesPerCU = 8;     // balanced split: grid = CUs * this
+
+constexpr int kEvenSplit = -1;          // partition_size value selecting the even split
+
+bool partition_ok(int P) { return P == kEvenSplit || (P >= 0 && P % kBlockSize == 0); }
 
 bool decode_args_ok(int B, int Hq, int Hkv, int D, int max_ctx, int P, pa_dtype dt) {
   return B >= 0 && B <= 65535 && Hkv > 0 && Hkv <= 65535 && Hq > 0 && Hq % Hkv == 0 &&
-         Hq / Hkv <= kMaxGroup && (D == 64 || D == 128) && max_ctx >= 0 && P >= 0 &&
-         P % kBlockSize == 0 && dtype_ok(dt);
+         Hq / Hkv <= kMaxGroup && (D == 64 || D == 128) && max_ctx >= 0 && partition_ok(P) &&
+         dtype_ok(dt);
 }
-
-int resolve_partition(int P) { return P > 0 ? P : kDefaultPartition; }
-
-int num_partitions(int max_ctx, int P) { return max_ctx <= 0 ? 1 : (max_ctx + P - 1) / P; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t workspace_bytes(int B, int Hq, int D, int maxP) {
+// Workspace: part_m, part_l, part_acc rows (maxP slots per (sequence, query
+// head)), then one int per (sequence, KV head) (slots written, even split),
+// each region 256-byte aligned.
+size_t workspace_bytes(int B, int Hq, int Hkv, int D, int maxP) {
   if (maxP <= 1) return 0;
   const size_t rows = static_cast<size_t>(B) * Hq * maxP;
-  return 2 * align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
+  return 2 * align256(rows * sizeof(float)) + align256(rows * D * sizeof(float)) +
+         align256(static_cast<size_t>(B) * Hkv * sizeof(int));
+}
+
+// Waves of the balanced-split grid for the current device.
+int split_waves() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus * kSplitWavesPerCU;
+}
+
+// How a call is executed: the balanced split (matrix-core path, no partition
+// size given) or fixed partitions of P tokens; maxP = workspace slots per
+// (sequence, query head) row.
+struct LaunchPlan {
+  bool split;
+  bool generic;
+  int P;
+  int maxP;
+  int W;
+};
+
+LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_env) {
+  LaunchPlan lp{};
+  lp.generic = dt == PA_F32 || generic_env;
+  lp.split = partition_size == kEvenSplit && !lp.generic;
+  if (lp.split) {
+    lp.W = split_waves();
+    const int max_pairs = ((max_ctx + kBlockSize - 1) / kBlockSize + 1) / 2;
+    lp.P = 0;
+    lp.maxP = max_pairs == 0 ? 1 : std::min((max_pairs + kMinChunkPairs - 1) / kMinChunkPairs + 1,
+                                            lp.W);
+  } else {
+    lp.P = partition_size > 0 ? partition_size : kDefaultPartition;  // 0 or -1 on fp32
+    lp.maxP = max_ctx <= 0 ? 1 : (max_ctx + lp.P - 1) / lp.P;
+  }
+  return lp;
 }
 
 template <typename T, int D>
@@ -614,25 +945,51 @@ void launch_partitions<F32, 128>(const Params& pr, bool, hipStream_t s) {
   decode_generic_kernel<F32, 128><<<dim3(pr.maxP, pr.Hkv, pr.B), 256, 0, s>>>(pr);
 }
 
+template <typename T, int D>
+void launch_split(const Params& pr, int W, hipStream_t s) {
+  if (pr.G <= 4)
+    decode_split_kernel<T, D, kPairsInFlight, true><<<W, 64, 0, s>>>(pr);
+  else
+    decode_split_kernel<T, D, kPairsInFlight, false><<<W, 64, 0, s>>>(pr);
+}
+
 enum class Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
 
 template <int D>
-void launch_phases(const Params& pr, pa_dtype dt, bool generic, Phase ph, hipStream_t s) {
-  if (static_cast<int>(ph) & static_cast<int>(Phase::kPartitions)) {
+void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph,
+                   hipStream_t s) {
+  const bool first = static_cast<int>(ph) & static_cast<int>(Phase::kPartitions);
+  const bool second = static_cast<int>(ph) & static_cast<int>(Phase::kMerge);
+  if (lp.split) {
+    if (first) {
+      if (dt == PA_F16)
+        launch_split<F16, D>(pr, lp.W, s);
+      else
+        launch_split<BF16, D>(pr, lp.W, s);
+    }
+    if (second) merge_split_kernel<D><<<dim3(pr.Hkv, pr.B), 256, 0, s>>>(pr);
+    return;
+  }
+  if (first) {
     switch (dt) {
       case PA_F32: launch_partitions<F32, D>(pr, true, s); break;
-      case PA_F16: launch_partitions<F16, D>(pr, generic, s); break;
-      case PA_BF16: launch_partitions<BF16, D>(pr, generic, s); break;
+      case PA_F16: launch_partitions<F16, D>(pr, lp.generic, s); break;
+      case PA_BF16: launch_partitions<BF16, D>(pr, lp.generic, s); break;
     }
   }
-  if ((static_cast<int>(ph) & static_cast<int>(Phase::kMerge)) && pr.maxP > 1)
-    merge_kernel<D><<<dim3(pr.Hq, pr.B), 256, 0, s>>>(pr);
+  if (second && pr.maxP > 1) merge_kernel<D><<<dim3(pr.Hq, pr.B), 256, 0, s>>>(pr);
 }
 
 // Validates the arguments shared by pa_decode / pa_decode_partial /
 // pa_decode_merge and launches the requested phases.
-pa_status run_decode(const char* fn, Phase ph, float* out, const void* q, const void* k_pool,
-                     const void* v_pool, const int32_t* block_tables,
+struct NewTokens {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slots;
+};
+
+pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, const void* q,
+                     const void* k_pool, const void* v_pool, const int32_t* block_tables,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
@@ -653,8 +1010,8 @@ pa_status run_decode(const char* fn, Phase ph, float* out, const void* q, const 
     return fail(PA_ERR_INVALID_ARG, "%s: num_seqs/num_kv_heads out of range", fn);
   if (num_blocks <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
     return fail(PA_ERR_INVALID_ARG, "%s: negative or zero size", fn);
-  if (partition_size < 0 || partition_size % kBlockSize != 0)
-    return fail(PA_ERR_INVALID_ARG, "%s: partition_size %d not a multiple of 16", fn,
+  if (!partition_ok(partition_size))
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_size %d (a multiple of 16, 0 or -1)", fn,
                 partition_size);
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
@@ -665,9 +1022,13 @@ pa_status run_decode(const char* fn, Phase ph, float* out, const void* q, const 
        reinterpret_cast<uintptr_t>(v_pool)) & 15)
     return fail(PA_ERR_INVALID_ARG, "%s: q and pools must be 16-byte aligned", fn);
 
-  const int P = resolve_partition(partition_size);
-  const int maxP = num_partitions(max_context_len, P);
-  const size_t need = workspace_bytes(num_seqs, num_q_heads, head_dim, maxP);
+  if (nt && (!nt->k_new || !nt->v_new || !nt->slots))
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL new-token pointer", fn);
+  if (nt && (reinterpret_cast<uintptr_t>(nt->k_new) & 15))
+    return fail(PA_ERR_INVALID_ARG, "%s: k_new must be 16-byte aligned", fn);
+  const LaunchPlan lp = make_plan(max_context_len, partition_size, dtype,
+                                  path_from_env() == Path::kGeneric);
+  const size_t need = workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
   if (need > 0 && (!workspace || workspace_bytes_given < need))
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace ? workspace_bytes_given : size_t(0));
@@ -689,22 +1050,39 @@ pa_status run_decode(const char* fn, Phase ph, float* out, const void* q, const 
   pr.num_blocks = num_blocks;
   pr.max_blocks = max_blocks_per_seq;
   pr.max_ctx = max_context_len;
-  pr.P = P;
-  pr.maxP = maxP;
+  pr.P = lp.P;
+  pr.maxP = lp.maxP;
   pr.scale_log2 = scale * kLog2e;
   if (need > 0) {
-    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * maxP;
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * lp.maxP;
     char* ws = static_cast<char*>(workspace);
     pr.part_m = reinterpret_cast<float*>(ws);
     pr.part_l = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
     pr.part_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+    pr.counters = reinterpret_cast<int*>(ws + 2 * align256(rows * sizeof(float)) +
+                                         align256(rows * head_dim * sizeof(float)));
   }
-  const bool generic = path_from_env() == Path::kGeneric;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nt) {
+    if (lp.split) {
+      // append fused into the partition kernel
+      pr.k_new = nt->k_new;
+      pr.v_new = nt->v_new;
+      pr.slots = nt->slots;
+      pr.kpool_w = const_cast<void*>(k_pool);
+      pr.vpool_w = const_cast<void*>(v_pool);
+    } else {
+      const pa_status st = pa_cache_append(const_cast<void*>(k_pool), const_cast<void*>(v_pool),
+                                           nt->k_new, nt->v_new, nt->slots, num_seqs,
+                                           num_blocks, num_kv_heads, head_dim, block_size,
+                                           dtype, stream);
+      if (st != PA_OK) return st;
+    }
+  }
   if (head_dim == 64)
-    launch_phases<64>(pr, dtype, generic, ph, s);
+    launch_phases<64>(pr, dtype, lp, ph, s);
   else
-    launch_phases<128>(pr, dtype, generic, ph, s);
+    launch_phases<128>(pr, dtype, lp, ph, s);
   return launch_status(fn);
 }
 
@@ -719,8 +1097,8 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_head
                                             pa_dtype dtype) {
   if (!decode_args_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                       partition_size, dtype))
-    return 0;
-  return resolve_partition(partition_size);
+    return -1;
+  return make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric).P;
 }
 
 extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -730,8 +1108,9 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
   if (!decode_args_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                       partition_size, dtype))
     return 0;
-  const int P = resolve_partition(partition_size);
-  return workspace_bytes(num_seqs, num_q_heads, head_dim, num_partitions(max_context_len, P));
+  const LaunchPlan lp =
+      make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric);
+  return workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
 }
 
 #define PA_DECODE_ARGS                                                                      \
@@ -747,13 +1126,30 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
       partition_size, dtype, workspace, workspace_bytes_given, stream
 
 extern "C" pa_status pa_decode(PA_DECODE_ARGS) {
-  return run_decode("pa_decode", Phase::kBoth, PA_DECODE_FWD);
+  return run_decode("pa_decode", Phase::kBoth, nullptr, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_partial(PA_DECODE_ARGS) {
-  return run_decode("pa_decode_partial", Phase::kPartitions, PA_DECODE_FWD);
+  return run_decode("pa_decode_partial", Phase::kPartitions, nullptr, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_merge(PA_DECODE_ARGS) {
-  return run_decode("pa_decode_merge", Phase::kMerge, PA_DECODE_FWD);
+  return run_decode("pa_decode_merge", Phase::kMerge, nullptr, PA_DECODE_FWD);
+}
+
+extern "C" pa_status pa_decode_step(float* out, const void* q, void* k_pool, void* v_pool,
+                                    const void* k_new, const void* v_new,
+                                    const int64_t* slot_mapping, const int32_t* block_tables,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    float scale, int32_t partition_size, pa_dtype dtype,
+                                    void* workspace, size_t workspace_bytes_given,
+                                    void* stream) {
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  return run_decode("pa_decode_step", Phase::kBoth, &nt, out, q, k_pool, v_pool, block_tables,
+                    context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                    num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
+                    dtype, workspace, workspace_bytes_given, stream);
 }

@@ -102,13 +102,17 @@ def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_
                      partition_size, dtype, device="cuda"):
     n = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                partition_size, dtype)
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+EVEN_SPLIT = -1   # partition_size value selecting the even split of the batch's work
 
 
 def decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale=None,
            partition_size=0, workspace=None, stream=None, phase="both"):
     """out [B][Hq][D] float32 = paged decode attention of q [B][Hq][D].
 
+    partition_size: > 0 fixed partitions, 0 library default, EVEN_SPLIT (-1).
     phase: "both" (pa_decode), "partial" (pa_decode_partial) or "merge"
     (pa_decode_merge)."""
     fn = {"both": "pa_decode", "partial": "pa_decode_partial", "merge": "pa_decode_merge"}[phase]
@@ -134,6 +138,44 @@ def decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, 
                           int(partition_size), pa_dtype(q.dtype), _dev(workspace, "workspace"),
                           workspace.numel() * workspace.element_size(), _stream(stream)),
           fn)
+    return out
+
+
+def decode_step(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables,
+                context_lens, max_context_len, scale=None, partition_size=0, workspace=None,
+                stream=None):
+    """Append each sequence's new token (row b of k_new/v_new, slot slot_mapping[b]) and
+    decode, in one call (pa_decode_step)."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    B, Hq = q.shape[0], q.shape[1]
+    if q.shape != (B, Hq, D) or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [B][Hq][D] in the pool dtype")
+    if k_new.shape != (B, H, D) or v_new.shape != (B, H, D) or k_new.dtype != k_pool.dtype \
+            or v_new.dtype != k_pool.dtype:
+        raise ValueError("k_new/v_new must be [B][Hkv][D] in the pool dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (B,):
+        raise ValueError("slot_mapping must be int64 [B]")
+    if out.shape != (B, Hq, D) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [B][Hq][D]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    scale = D ** -0.5 if scale is None else float(scale)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size, q.dtype,
+                                     q.device)
+    check(lib().pa_decode_step(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                               _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+                               _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
+                               _dev(block_tables, "block_tables"),
+                               _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
+                               block_tables.shape[1], int(max_context_len), scale,
+                               int(partition_size), pa_dtype(q.dtype),
+                               _dev(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+          "pa_decode_step")
     return out
 
 

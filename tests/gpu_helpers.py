@@ -27,7 +27,7 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None):
+def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None, fused=True):
     """Replays the case's set-up and runs one step on the GPU.
 
     Returns dict(plan=StepPlan, out=np fp32, k_pool/v_pool=np bits, cache=PagedKVCache).
@@ -45,7 +45,7 @@ def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None):
     k_new, v_new = k_tok.index_select(0, nr), v_tok.index_select(0, nr)
     q = case.q.to(dev)
     ps = case.partition_size if partition_size is None else partition_size
-    out = cache.step(plan, q, k_new, v_new, partition_size=ps)
+    out = cache.step(plan, q, k_new, v_new, partition_size=ps, fused=fused)
     torch.cuda.synchronize()
     return {"plan": plan, "out": out.cpu().numpy(), "cache": cache, "q": q,
             "k_pool": bits_of(cache.k_pool, case.dtype),

@@ -74,16 +74,19 @@ def test_device_calls_reject_bad_scalars_without_launching():
 
 def test_workspace_and_partition_queries():
     h = pk.lib()
-    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_BF16) > 0
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_BF16) == 256   # default
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, -1, PA_BF16) == 0    # even split
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, -1, PA_F32) == 256   # fixed on fp32
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, -2, PA_BF16) == -1
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 256, PA_BF16) == 256
-    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 100, PA_BF16) == 0
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 100, PA_BF16) == -1
     # one partition -> no workspace
     assert h.pa_decode_workspace_bytes(4, 8, 2, 64, 256, 512, PA_F32) == 0
     # 3 partitions of 512: m, l and acc rows, each region 256-byte aligned
     rows = 4 * 8 * 3
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert h.pa_decode_workspace_bytes(4, 8, 2, 64, 1100, 512, PA_F32) == \
-        2 * al(rows * 4) + al(rows * 64 * 4)
+        2 * al(rows * 4) + al(rows * 64 * 4) + al(4 * 2 * 4)
 
 
 def _c_apply(bm, op):

@@ -47,12 +47,23 @@ def _compare_full(case, ref, got, tol):
 
 
 @pytest.mark.parametrize("kernel", KERNELS, indirect=True)
+@pytest.mark.parametrize("fused", [True, False], ids=["decode_step", "append+decode"])
 @pytest.mark.parametrize("name", CONFIG_NAMES)
-def test_small_configs_match_oracle(name, kernel):
+def test_small_configs_match_oracle(name, fused, kernel):
     case = small_case(name)
-    say(f"[parity small] {name} kernel={kernel} lens={case.lens.tolist()}")
+    say(f"[parity small] {name} kernel={kernel} fused={fused} lens={case.lens.tolist()}")
     ref = _oracle_poisoned(case)
-    got = run_gpu_step(case)
+    got = run_gpu_step(case, fused=fused)
+    _compare_full(case, ref, got, TOL[case.dtype])
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["decode_step", "append+decode"])
+@pytest.mark.parametrize("name", [n for n in CONFIG_NAMES if n != "tiny_fp32"])
+def test_small_configs_even_split(name, fused):
+    case = small_case(name)
+    say(f"[parity small, even split] {name} fused={fused}")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case, partition_size=-1, fused=fused)
     _compare_full(case, ref, got, TOL[case.dtype])
 
 
@@ -156,7 +167,8 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 511, 512, 513, 1023, 1024, 
 
 @pytest.mark.parametrize("kernel", KERNELS, indirect=True)
 @pytest.mark.parametrize("dtype,hq,hkv,d,ps", [
-    ("bf16", 32, 8, 128, 0), ("bf16", 32, 8, 128, 16), ("bf16", 16, 1, 64, 512),
+    ("bf16", 32, 8, 128, 0), ("bf16", 32, 8, 128, -1), ("bf16", 32, 8, 128, 16),
+    ("bf16", 16, 1, 64, 512),
     ("f16", 8, 8, 128, 512), ("f16", 16, 2, 64, 256), ("bf16", 4, 2, 64, 1024),
     ("f32", 4, 4, 64, 512), ("f32", 8, 2, 128, 0), ("bf16", 2, 2, 128, 4096)])
 def test_edge_lengths_and_shapes(dtype, hq, hkv, d, ps, kernel):
@@ -168,12 +180,13 @@ def test_edge_lengths_and_shapes(dtype, hq, hkv, d, ps, kernel):
 
 
 @pytest.mark.parametrize("kernel", KERNELS, indirect=True)
-def test_bad_table_entry_and_length_give_nan_rows(kernel):
+@pytest.mark.parametrize("ps", [256, -1])
+def test_bad_table_entry_and_length_give_nan_rows(kernel, ps):
     """Out-of-range table entries and lengths are caught by the kernels' own
     bounds checks (no access outside the pools) and flagged with NaN rows."""
     pk = require_gpu()
-    case = custom_case(41, "bf16", [40, 300, 700, 20, 33], 8, 2, 128, partition_size=256)
-    say(f"[errors] bad table entry / length kernel={kernel}")
+    case = custom_case(41, "bf16", [40, 300, 700, 20, 33], 8, 2, 128, partition_size=ps)
+    say(f"[errors] bad table entry / length kernel={kernel} P={ps}")
     got = run_gpu_step(case)
     cache, plan = got["cache"], got["plan"]
     tables = plan.d_tables.clone()
@@ -184,11 +197,52 @@ def test_bad_table_entry_and_length_give_nan_rows(kernel):
     lens[4] = 0                                 # seq 4: empty row -> zeros
     out = torch.empty_like(torch.from_numpy(got["out"])).cuda()
     pk.ops.decode(out, got["q"], cache.k_pool, cache.v_pool, tables, lens, plan.max_context_len,
-                  partition_size=256)
+                  partition_size=ps)
     o = out.cpu().numpy()
     assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and np.isnan(o[3]).all()
     assert np.array_equal(o[0], got["out"][0])
     assert np.array_equal(o[4], np.zeros_like(o[4]))
+
+
+SPLIT_LENS = {
+    "one_long": [8000],
+    "many_short": list(np.random.default_rng(3).integers(1, 41, size=300)),
+    "mixed": [33] * 7 + [4000, 1, 17, 2500],
+}
+
+
+@pytest.mark.parametrize("lens", list(SPLIT_LENS), ids=list(SPLIT_LENS))
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 16, 2, 64),
+                                            ("bf16", 16, 16, 128)])
+def test_even_split_shapes(lens, dtype, hq, hkv, d):
+    """The even split of the batch's work across waves (partition_size 0):
+    ranges cut over many chunks, chunks holding many whole sequences."""
+    case = custom_case(51, dtype, SPLIT_LENS[lens], hq, hkv, d, partition_size=-1)
+    say(f"[split] {lens} {dtype} Hq={hq} Hkv={hkv} D={d}")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case)
+    _compare_full(case, ref, got, TOL[dtype])
+
+
+def test_workspace_reused_across_calls():
+    """One (uninitialised) workspace serves call after call, alternating
+    batches with different splits."""
+    pk = require_gpu()
+    say("[workspace] reuse across calls")
+    a = custom_case(61, "bf16", [900, 33, 2500, 70], 32, 8, 128)
+    b = custom_case(62, "bf16", [1800, 5, 640, 1200], 32, 8, 128)
+    ra, rb = _oracle_poisoned(a), _oracle_poisoned(b)
+    ga, gb = run_gpu_step(a), run_gpu_step(b)
+    ws = pk.ops.decode_workspace(4, 32, 8, 128, 2600, -1, torch.bfloat16)
+    ws.fill_(0xAB)
+    for _ in range(3):
+        for case, got, ref in ((a, ga, ra), (b, gb, rb)):
+            plan, cache = got["plan"], got["cache"]
+            out = torch.empty(4, 32, 128, device="cuda")
+            pk.ops.decode(out, got["q"], cache.k_pool, cache.v_pool, plan.d_tables, plan.d_lens,
+                          2600, partition_size=-1, workspace=ws)
+            torch.cuda.synchronize()
+            assert max_err(out.cpu().numpy(), ref["out"]) <= TOL["bf16"]
 
 
 def test_append_skips_negative_and_out_of_range_slots():
