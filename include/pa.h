@@ -36,10 +36,9 @@
  * 8 for fp16/bf16; Hkv = num_kv_heads, D = head_dim):
  *   K pool: [num_blocks][Hkv][D/x][bs][x]   element (b,h,t,d) at
  *           (((b*Hkv + h)*(D/x) + d/x)*bs + t)*x + d%x
- *   V pool: [num_blocks][Hkv][D][bs]        element (b,h,t,d) at
- *           ((b*Hkv + h)*D + d)*bs + slot(t), where slot(t) exchanges bits 2
- *           and 3 of t: each 16-slot row holds tokens 0-3, 8-11, 4-7, 12-15
- *           (so the matrix-core kernel reads 8 tokens with one 16-byte load)
+ *   V pool: [num_blocks][Hkv][bs/x][D][x]   element (b,h,t,d) at
+ *           (((b*Hkv + h)*(bs/x) + t/x)*D + d)*x + t%x
+ *           (one 16-byte load gives x consecutive tokens of one dim)
  * A token at logical position p of a sequence lives in physical block
  * table[p / bs] at in-block offset t = p % bs; its slot number is
  * table[p / bs]*bs + p % bs.

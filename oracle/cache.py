@@ -6,10 +6,9 @@ byte layout).  With ``x = 16 / element_bytes`` (4 for fp32, 8 for fp16/bf16):
 * K pool: ``[num_blocks][num_kv_heads][head_dim / x][block_size][x]`` —
   element (block b, head h, in-block token t, dim d) sits at
   ``(((b*H + h)*(D/x) + d//x)*bs + t)*x + d%x``;
-* V pool: ``[num_blocks][num_kv_heads][head_dim][block_size]`` with the 16
-  token slots of every dim row holding tokens 0-3, 8-11, 4-7, 12-15 in that
-  order — element (b, h, t, d) sits at ``((b*H + h)*D + d)*bs + slot(t)``
-  where slot(t) exchanges bits 2 and 3 of t.
+* V pool: ``[num_blocks][num_kv_heads][block_size / x][head_dim][x]`` —
+  element (b, h, t, d) sits at ``(((b*H + h)*(bs/x) + t//x)*D + d)*x + t%x``
+  (each dim row holds x consecutive tokens).
 
 A token at logical position p of a sequence lives in physical block
 ``table[p // bs]`` at in-block offset ``p % bs`` (page 1, section
@@ -27,26 +26,21 @@ def x_of(dtype: str) -> int:
     return 4 if dtype == "f32" else 8
 
 
-def v_slot(t):
-    """Position of in-block token t inside a V row: bits 2 and 3 of t exchanged."""
-    return (t & 3) | ((t & 4) << 1) | ((t & 8) >> 1)
-
-
 def k_offset(b, h, t, d, H, D, bs, x):
     """Flat element index of K(b, h, t, d) in the K pool."""
     return (((b * H + h) * (D // x) + d // x) * bs + t) * x + d % x
 
 
-def v_offset(b, h, t, d, H, D, bs):
+def v_offset(b, h, t, d, H, D, bs, x):
     """Flat element index of V(b, h, t, d) in the V pool."""
-    return ((b * H + h) * D + d) * bs + v_slot(t)
+    return (((b * H + h) * (bs // x) + t // x) * D + d) * x + t % x
 
 
 def new_pools(num_blocks, H, D, bs, dtype, fill=0):
     x = x_of(dtype)
     bd = bits_dtype(dtype)
     k = np.full((num_blocks, H, D // x, bs, x), fill, dtype=bd)
-    v = np.full((num_blocks, H, D, bs), fill, dtype=bd)
+    v = np.full((num_blocks, H, bs // x, D, x), fill, dtype=bd)
     return k, v
 
 
@@ -68,7 +62,7 @@ def append_ref(k_pool, v_pool, k_new_bits, v_new_bits, slots, bs):
             continue
         b, t = int(s) // bs, int(s) % bs
         k_pool[b, :, :, t, :] = k_new_bits[i].reshape(H, Dx, x)
-        v_pool[b, :, :, v_slot(t)] = v_new_bits[i].reshape(H, D)
+        v_pool[b, :, t // x, :, t % x] = v_new_bits[i].reshape(H, D)
 
 
 def copy_ref(k_pool, v_pool, pairs):
@@ -86,7 +80,7 @@ def gather_ref(k_pool, v_pool, table, L, bs):
     blk = np.asarray(table, dtype=np.int64)[pos // bs]     # physical block of position p
     off = pos % bs                                           # token inside that block
     K = k_pool[blk, :, :, off, :]                            # [L][H][D/x][x]
-    V = v_pool[blk, :, :, v_slot(off)]                       # [L][H][D]
+    V = v_pool[blk, :, off // x, :, off % x]                 # [L][H][D]
     K = np.ascontiguousarray(K.reshape(L, H, D).transpose(1, 0, 2))
     V = np.ascontiguousarray(V.transpose(1, 0, 2))
     return K, V

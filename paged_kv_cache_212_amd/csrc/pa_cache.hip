@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void append_kernel(typename T::bits* __restric
   const int nelem = Hkv * D;
   for (int e = threadIdx.x; e < nelem; e += blockDim.x) {
     const int h = e / D, d = e % D;
-    vpool[tile_base(blk, h, Hkv, D) + v_elem(t, d)] = vsrc[e];
+    vpool[tile_base(blk, h, Hkv, D) + v_elem<T>(t, d, D)] = vsrc[e];
   }
 }
 
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void gather_kernel(typename T::bits* __restric
       if (blk_ok) {
         const int64_t base = tile_base(phys, g, Hkv, D);
         kv = kpool[base + k_elem<T>(t, d)];
-        vv = vpool[base + v_elem(t, d)];
+        vv = vpool[base + v_elem<T>(t, d, D)];
       } else {
         kv = vv = static_cast<bits>(~bits(0));  // bad table entry
       }

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(Params pr) {
           const int phys = trow[pos / kBlockSize];
           if (phys < 0 || phys >= pr.num_blocks) continue;
           const bits* vt = vp + tile_base(phys, g, pr.Hkv, D);
-          a = fmaf(ss[h][t], T::to_float(vt[v_elem(pos % kBlockSize, d)]), a);
+          a = fmaf(ss[h][t], T::to_float(vt[v_elem<T>(pos % kBlockSize, d, D)]), a);
         }
         acc[k] = a;
       }
@@ -198,6 +198,13 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load of K/V (each tile is read once per step): the
+// non-temporal hint keeps the stream from displacing cached lines.
+__device__ __forceinline__ uint4 load_stream(const char* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(p)));
+}
 
 template <typename T>
 struct Mfma;
@@ -293,18 +300,17 @@ struct Mfma<F16> {
 
 // Two blocks (A = block 2q, B = block 2q+1 of the range) per iteration.
 // Lane = 16*j + n (n = lane % 16, j = lane / 16).
-//   QK, half hh in {0,1}: S^T (16 rows x 16 heads) = K rows . Q^T where row
-//     i < 8 is token i + 8*hh of A and row i >= 8 token i - 8 + 8*hh of B.
+//   QK, half hh in {0,1}: S^T (16 rows x 16 heads) = K rows . Q^T where row r
+//     is token 8*((r/4)%2) + 4*hh + r%4 of block r/8 (A for r < 8, else B).
 //     A operand (K): lane reads row n, dims kk*32 + 8j .. +8 (16 bytes).
 //     B operand (Q): head n, dims kk*32 + 8j .. +8.
 //     Result: lane (head n, j) holds rows 4j+e, i.e. block j/2, tokens
-//     4*(j%2) + e + 8*hh (e = 0..3).
+//     8*(j%2) + 4*hh + e (e = 0..3).
 //   PV: O (16 heads x 16 dims) += P (heads x 32 tokens) . V (32 tokens x dims)
-//     with lane (n, j) holding k-slots {S_hh0[e], S_hh1[e]}: 8 tokens of block
-//     j/2, namely 4*(j%2) + {0..3} and 8 + 4*(j%2) + {0..3}.  In the V tile
-//     the 16 token slots of each dim row are stored in the order 0-3, 8-11,
-//     4-7, 12-15, so those 8 tokens are 16 contiguous bytes at
-//     dim*32 + 16*(j%2): one 16-byte load per lane and tile.
+//     with lane (n, j) holding k-slots {S_hh0[e], S_hh1[e]}: tokens
+//     8*(j%2) + 0..7 of block j/2, in order.  The V tile stores each dim's 8
+//     tokens of a half block as 16 contiguous bytes (half h, dim d at byte
+//     (h*D + d)*16): one 16-byte load per lane and 16-dim tile.
 //   O result: lane (dim t*16 + n, j) holds heads 4j + e.
 // K tile (block, head) bytes: [D/8 chunks][16 tokens][8 dims] -> chunk
 // kk*4 + j, token r at (kk*4 + j)*256 + 16*r.
@@ -383,15 +389,16 @@ __device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int
   uint4 vb[NPAIR][NTL];
   auto issue = [&](int u, int q) {
     const int pa = phys_of(2 * q), pb = phys_of(2 * q + 1);
-    const char* kt = kbase + ((n < 8) ? pa : pb) * block_stride + (n & 7) * 16 + j * 256;
-    const char* vt = vbase + ((j >> 1) ? pb : pa) * block_stride + n * 32 + (j & 1) * 16;
+    const char* kt = kbase + ((n < 8) ? pa : pb) * block_stride + (n & 3) * 16 +
+                     ((n >> 2) & 1) * 128 + j * 256;
+    const char* vt = vbase + ((j >> 1) ? pb : pa) * block_stride + ((j & 1) * D + n) * 16;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
-        kb[u][hh][kk] = *reinterpret_cast<const uint4*>(kt + kk * 1024 + hh * 128);
+        kb[u][hh][kk] = load_stream(kt + kk * 1024 + hh * 64);
 #pragma unroll
-    for (int t = 0; t < NTL; ++t) vb[u][t] = *reinterpret_cast<const uint4*>(vt + t * 512);
+    for (int t = 0; t < NTL; ++t) vb[u][t] = load_stream(vt + t * 256);
   };
 
   // The new token sits at position tok_end - 1, in the range's last pair:
@@ -411,20 +418,19 @@ __device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int
     const int tn = pos % kBlockSize;
     const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
     const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
-    // K: lane row n holds token (n & 7) + 8*hh of block n >> 3
-    if ((n >> 3) == sel && (n & 7) == (tn & 7)) {
+    // K: lane row n holds token 8*((n >> 2) & 1) + 4*hh + (n & 3) of block n >> 3
+    if ((n >> 3) == sel && (n & 3) == (tn & 3) && ((n >> 2) & 1) == (tn >> 3)) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        if (hh == (tn >> 3)) {
+        if (hh == ((tn >> 2) & 1)) {
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk)
             kb[u][hh][kk] = *reinterpret_cast<const uint4*>(kn + kk * 32 + j * 8);
         }
     }
-    // V: lane group j holds block j >> 1, tokens 4*(j & 1) + {0..3} as
-    // elements 0..3 and 8 + 4*(j & 1) + {0..3} as elements 4..7
-    if ((j >> 1) == sel && (j & 1) == ((tn >> 2) & 1)) {
-      const int e = (tn & 3) + 4 * (tn >> 3);
+    // V: lane group j holds block j >> 1, tokens 8*(j & 1) + e as element e
+    if ((j >> 1) == sel && (j & 1) == (tn >> 3)) {
+      const int e = tn & 7;
       const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
       const int sh = (e & 1) * 16, dw = e >> 1;
 #pragma unroll
@@ -448,7 +454,7 @@ __device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int
         *reinterpret_cast<uint4*>(kt + (lane * kBlockSize + ts) * 8) =
             *reinterpret_cast<const uint4*>(kn + lane * 8);
 #pragma unroll
-      for (int d = lane; d < D; d += 64) vt[d * kBlockSize + v_slot(ts)] = vn[d];
+      for (int d = lane; d < D; d += 64) vt[((ts >> 3) * D + d) * 8 + (ts & 7)] = vn[d];
     }
   };
 
@@ -460,13 +466,13 @@ __device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int
       s0 = Mfma<T>::qk(kb[u][0][kk], qkk, s0);
       s1 = Mfma<T>::qk(kb[u][1][kk], qkk, s1);
     }
-    // sequence position of S_hh[e]
-    const int base = (blk_begin + 2 * q + (j >> 1)) * kBlockSize + 4 * (j & 1);
+    // sequence position of S_hh[e]: base + 4*hh + e
+    const int base = (blk_begin + 2 * q + (j >> 1)) * kBlockSize + 8 * (j & 1);
     float sv[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sv[e] = (base + e < tok_end) ? s0[e] * pr.scale_log2 : -INFINITY;
-      sv[4 + e] = (base + 8 + e < tok_end) ? s1[e] * pr.scale_log2 : -INFINITY;
+      sv[4 + e] = (base + 4 + e < tok_end) ? s1[e] * pr.scale_log2 : -INFINITY;
     }
     float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
@@ -505,8 +511,8 @@ __device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int
       // positions so unused slots (even NaN) cannot reach the output via 0*v
       const uint32_t mx = (base + 0 < tok_end ? 0x0000FFFFu : 0u) | (base + 1 < tok_end ? 0xFFFF0000u : 0u);
       const uint32_t my = (base + 2 < tok_end ? 0x0000FFFFu : 0u) | (base + 3 < tok_end ? 0xFFFF0000u : 0u);
-      const uint32_t mz = (base + 8 < tok_end ? 0x0000FFFFu : 0u) | (base + 9 < tok_end ? 0xFFFF0000u : 0u);
-      const uint32_t mw = (base + 10 < tok_end ? 0x0000FFFFu : 0u) | (base + 11 < tok_end ? 0xFFFF0000u : 0u);
+      const uint32_t mz = (base + 4 < tok_end ? 0x0000FFFFu : 0u) | (base + 5 < tok_end ? 0xFFFF0000u : 0u);
+      const uint32_t mw = (base + 6 < tok_end ? 0x0000FFFFu : 0u) | (base + 7 < tok_end ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int t = 0; t < NTL; ++t) {
         vb[u][t].x &= mx;
@@ -612,12 +618,473 @@ __device__ __forceinline__ void emit_state(const Params& pr, int b, int g, int s
   }
 }
 
+// The 16x16 engine as a policy for the wave kernels below.
+template <typename T, int D, int NPAIR, bool kSmallGroup>
+struct Engine16 {
+  using State = WaveState<D>;
+  struct Pre {};
+  static constexpr int kUnitBlocks = 2;  // blocks per step (one pair)
+  __device__ static void prologue(const Params&, int, int, int, Pre&) {}
+  template <bool with_new>
+  __device__ static void attend(const Params& pr, int b, int g, int blk_begin, int nblk,
+                                int tok_end, State& st, const Pre&) {
+    attend_range<T, D, NPAIR, kSmallGroup, with_new>(pr, b, g, blk_begin, nblk, tok_end, st);
+  }
+  __device__ static void reset(State& st) { reset_state(st); }
+  __device__ static void emit(const Params& pr, int b, int g, int slot, State& st) {
+    emit_state(pr, b, g, slot, st);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Matrix-core engine for G <= 4 on the 4x4x4 16-block MFMA
+// (v_mfma_f32_4x4x4_16b: sixteen independent 4x4x4 products per instruction,
+// block k on lanes 4k..4k+3; with CBSZ=4 / ABID=a every block uses the A
+// operand of block a).
+//
+// One step covers a quad of 4 consecutive blocks (64 tokens); lane l owns
+// token l of the quad (block l/16, in-block token l%16).
+//   QK: S (4 heads x 64 tokens) = Q . K^T over D/4 k-steps of 4 dims.  Step
+//     s takes A = Q broadcast from block s%16 (register s/16 holds, at lane
+//     4a+i, head i's dims 4*(16*(s/16) + a) .. +3) and B = K (lane l: dims
+//     4s..4s+3 of token l).  Result: lane l holds S[head e][token l], e=0..3.
+//   A 4x4 transpose inside each lane quad (DPP) turns that into lane 4a+i
+//     holding S[head i][token 4a+e]: the softmax runs per lane over 4 tokens
+//     of one head, and the probabilities are already the A operand of P.V.
+//   PV: O (4 heads x 64 dims) += P (4 heads x 4 tokens) . V (4 tokens x 64
+//     dims) for k-step a = tokens 4a..4a+3, A broadcast from block a, B lane
+//     l = V[tokens 4a..4a+3][dim 64t + l]: half of one 16-byte load of the
+//     V tile (8 consecutive tokens of a dim are contiguous).  O: lane l
+//     holds dim 64t + l of heads e = 0..3.
+// K loads: lane l reads 16-byte chunks c of token l (D/8 loads; per
+// instruction 4 runs of 256 contiguous bytes).  V loads: per (block, half,
+// 64-dim tile) one 16-byte load per lane, 1 KiB contiguous per instruction.
+// ---------------------------------------------------------------------------
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// Calls f(integral_constant<int, i>) for i = 0..N-1 (indices usable as
+// instruction immediates).
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+template <typename T>
+struct Mfma4;
+
+template <>
+struct Mfma4<BF16> {
+  template <int ABID>
+  __device__ static inline f32x4_t mma(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                  __builtin_bit_cast(i16x4_t, b), c, 4, ABID, 0);
+  }
+  __device__ static inline void split(const float pe[4], uint2& hi, uint2& lo) {
+    Mfma<BF16>::split(pe, hi, lo);
+  }
+};
+
+template <>
+struct Mfma4<F16> {
+  template <int ABID>
+  __device__ static inline f32x4_t mma(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(f16x4_t, a),
+                                              __builtin_bit_cast(f16x4_t, b), c, 4, ABID, 0);
+  }
+  __device__ static inline void split(const float pe[4], uint2& hi, uint2& lo) {
+    Mfma<F16>::split(pe, hi, lo);
+  }
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+// 4x4 transpose across each lane quad: afterwards lane 4a+i holds in m[e]
+// what lane 4a+e held in m[i].  Two 2x2 exchanges (lane bit 1 with element
+// bit 1, then lane bit 0 with element bit 0).
+__device__ __forceinline__ void quad_transpose(float (&m)[4]) {
+  const int lane = threadIdx.x & 63;
+  const bool b1 = lane & 2, b0 = lane & 1;
+  float s0 = b1 ? m[0] : m[2], s1 = b1 ? m[1] : m[3];
+  float r0 = dpp<kDppQuadXor2>(s0), r1 = dpp<kDppQuadXor2>(s1);
+  if (b1) {
+    m[0] = r0;
+    m[1] = r1;
+  } else {
+    m[2] = r0;
+    m[3] = r1;
+  }
+  s0 = b0 ? m[0] : m[1];
+  s1 = b0 ? m[2] : m[3];
+  r0 = dpp<kDppQuadXor1>(s0);
+  r1 = dpp<kDppQuadXor1>(s1);
+  if (b0) {
+    m[0] = r0;
+    m[2] = r1;
+  } else {
+    m[1] = r0;
+    m[3] = r1;
+  }
+}
+
+// Max / sum over the 16 lanes that share lane % 4.
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<kDppRowRor4>(v));
+  v = fmaxf(v, dpp<kDppRowRor8>(v));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp<kDppRowRor4>(v);
+  v += dpp<kDppRowRor8>(v);
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+template <int D>
+struct WaveState4 {
+  float m_run;           // running max (log2 domain) of head lane%4
+  float l_lane;          // this lane's share of head lane%4's running sum
+  f32x4_t acc[D / 64];   // O: lane l = dim 64t + l, element e = head e
+  bool bad;              // a table entry of the range was out of the pool
+};
+
+// Loads a range's first dependencies before its length is known: Q (A
+// operand of QK: lane 4a+i holds head i, dims 64r + 4a .. +3) and the raw
+// table entries blk_begin + lane of sequence b (in bounds of the table row;
+// attend4 validates the ones it uses).
+template <int D>
+struct Prologue4 {
+  uint2 qr[D / 64];
+  int tab;
+};
+
+template <int D>
+__device__ __forceinline__ void prologue4(const Params& pr, int b, int g, int blk_begin,
+                                          Prologue4<D>& pre) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 3;
+  const uint16_t* qb = static_cast<const uint16_t*>(pr.q) +
+                       (static_cast<int64_t>(b) * pr.Hq + g * pr.G + i) * D + 4 * (lane >> 2);
+#pragma unroll
+  for (int r = 0; r < D / 64; ++r)
+    pre.qr[r] = i < pr.G ? *reinterpret_cast<const uint2*>(qb + 64 * r) : make_uint2(0, 0);
+  const int k = blk_begin + lane;
+  pre.tab = k < pr.max_blocks ? pr.tables[static_cast<int64_t>(b) * pr.max_blocks + k] : 0;
+}
+
+template <typename T, int D, bool with_new>
+__device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_begin, int nblk,
+                                        int tok_end, WaveState4<D>& st, const Prologue4<D>& pre) {
+  constexpr int NC = D / 8;    // 16-byte K chunks per token
+  constexpr int NT = D / 64;   // 64-dim output tiles
+  constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
+  const int lane = threadIdx.x & 63;
+  const int G = pr.G;
+  const int nquad = (nblk + 3) >> 2;
+
+  const uint2* qr = pre.qr;
+
+  const char* kbase = static_cast<const char*>(pr.kpool) + g * kTileBytes;
+  const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
+  const int64_t block_stride = static_cast<int64_t>(pr.Hkv) * kTileBytes;
+  const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks + blk_begin;
+
+  // Table entries, 64 per register (lane i holds entry 64*c + i of chunk c).
+  auto load_chunk = [&](int c) -> int {
+    const int k = c * 64 + lane;
+    const int e = k < nblk ? trow[k] : 0;
+    const bool lane_bad = k < nblk && (e < 0 || e >= pr.num_blocks);
+    if (__any(lane_bad)) st.bad = true;
+    return lane_bad ? 0 : e;
+  };
+  int chunk = 0;
+  int tcur;
+  {
+    const bool lane_bad = lane < nblk && (pre.tab < 0 || pre.tab >= pr.num_blocks);
+    if (__any(lane_bad)) st.bad = true;
+    tcur = lane_bad ? 0 : pre.tab;
+  }
+  int tnext = nblk > 64 ? load_chunk(1) : 0;
+  // Physical blocks of quad qd (qd increases across calls; the 4 entries of a
+  // quad never straddle a 64-entry chunk); blocks past the range map to its
+  // last block.
+  auto quad_phys = [&](int qd, int (&ph)[4]) {
+    const int c = qd >> 4;
+    if (c != chunk) {
+      chunk = c;
+      tcur = tnext;
+      tnext = (c + 1) * 64 < nblk ? load_chunk(c + 1) : 0;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      ph[kb] = __builtin_amdgcn_readlane(tcur, min(4 * qd + kb, nblk - 1) & 63);
+  };
+
+  uint4 kr[NC];
+  uint4 vr[4][2][NT];
+  int ph[4];
+  auto issue_k = [&]() {
+    const int kb = lane >> 4;
+    const int p = kb == 0 ? ph[0] : kb == 1 ? ph[1] : kb == 2 ? ph[2] : ph[3];
+    const char* kt = kbase + p * block_stride + (lane & 15) * 16;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c] = load_stream(kt + c * 256);
+  };
+  auto issue_v = [&]() {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const char* vt = vbase + ph[kb] * block_stride + lane * 16;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          vr[kb][h][t] = load_stream(vt + (h * D + 64 * t) * 16);
+    }
+  };
+
+  // New token of the step (fused append): staged in LDS at the start, put
+  // into the last quad's registers and written to its pool slot.
+  __shared__ uint32_t s_new[2][D / 2];
+  uint32_t stage_k = 0, stage_v = 0;
+  if (with_new && lane < D / 2) {
+    const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
+    stage_k = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.k_new) + nrow)[lane];
+    stage_v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.v_new) + nrow)[lane];
+  }
+  auto substitute_new = [&]() {
+    const int qt = tok_end - 1 - (blk_begin + 4 * (nquad - 1)) * kBlockSize;  // 0..63
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
+    if (lane == qt) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kr[c] = *reinterpret_cast<const uint4*>(kn + c * 8);
+    }
+    const int kb = qt >> 4, h = (qt >> 3) & 1, e = qt & 7;
+    const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    const int sh = (e & 1) * 16, dw = e >> 1;
+#pragma unroll
+    for (int KB = 0; KB < 4; ++KB)
+#pragma unroll
+      for (int H = 0; H < 2; ++H)
+        if (KB == kb && H == h) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const uint32_t val = static_cast<uint32_t>(vn[64 * t + lane]) << sh;
+            uint4& vv = vr[KB][H][t];
+            vv.x = dw == 0 ? ((vv.x & keep) | val) : vv.x;
+            vv.y = dw == 1 ? ((vv.y & keep) | val) : vv.y;
+            vv.z = dw == 2 ? ((vv.z & keep) | val) : vv.z;
+            vv.w = dw == 3 ? ((vv.w & keep) | val) : vv.w;
+          }
+        }
+    const int64_t slot = pr.slots[b];
+    if (slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
+      const int64_t blk = slot / kBlockSize;
+      const int ts = static_cast<int>(slot % kBlockSize);
+      uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
+      uint16_t* vt = static_cast<uint16_t*>(pr.vpool_w) + tile_base(blk, g, pr.Hkv, D);
+      if (lane < NC)
+        *reinterpret_cast<uint4*>(kt + (lane * kBlockSize + ts) * 8) =
+            *reinterpret_cast<const uint4*>(kn + lane * 8);
+#pragma unroll
+      for (int d = lane; d < D; d += 64) vt[((ts >> 3) * D + d) * 8 + (ts & 7)] = vn[d];
+    }
+  };
+
+  auto qk_softmax = [&](int qd, uint2& phi, uint2& plo) {
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    unroll<D / 4>([&](auto ic) {
+      constexpr int s = decltype(ic)::value;
+      const uint4& kc = kr[s / 2];
+      const uint2 kv = (s & 1) ? make_uint2(kc.z, kc.w) : make_uint2(kc.x, kc.y);
+      if constexpr (s & 1)
+        s1 = Mfma4<T>::template mma<s % 16>(qr[s / 16], kv, s1);
+      else
+        s0 = Mfma4<T>::template mma<s % 16>(qr[s / 16], kv, s0);
+    });
+    const int qpos = (blk_begin + 4 * qd) * kBlockSize;   // position of the quad's token 0
+    const bool valid = qpos + lane < tok_end;
+    float sv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[e] = valid ? (s0[e] + s1[e]) * pr.scale_log2 : -INFINITY;
+    quad_transpose(sv);   // lane 4a+i: head i, tokens 4a+e
+    const float lm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    if (__any(lm > st.m_run)) {
+      // the running max moved for some head: rescale by 2^(m_old - m_new)
+      const float mn = fmaxf(st.m_run, max16(lm));
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run - mn);
+      st.l_lane *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), e));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) st.acc[t][e] *= ah;
+      }
+      st.m_run = mn;
+    }
+    float pe[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - st.m_run);
+    st.l_lane += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    Mfma4<T>::split(pe, phi, plo);
+  };
+
+  // last: the quad may reach past the end of the range (only the range's last
+  // quad can)
+  auto pv = [&](int qd, uint2 phi, uint2 plo, auto last) {
+    const int qpos = (blk_begin + 4 * qd) * kBlockSize;
+    if (decltype(last)::value && qpos + 4 * kBlockSize > tok_end) {
+      // the quad reaches past the end of the range: zero V of masked
+      // positions so unused slots (even NaN) cannot reach the output via 0*v
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int nv = tok_end - (qpos + 16 * kb + 8 * h);   // valid tokens of the 8
+          const uint32_t m0 = (nv > 0 ? 0x0000FFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
+          const uint32_t m1 = (nv > 2 ? 0x0000FFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
+          const uint32_t m2 = (nv > 4 ? 0x0000FFFFu : 0u) | (nv > 5 ? 0xFFFF0000u : 0u);
+          const uint32_t m3 = (nv > 6 ? 0x0000FFFFu : 0u) | (nv > 7 ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            vr[kb][h][t].x &= m0;
+            vr[kb][h][t].y &= m1;
+            vr[kb][h][t].z &= m2;
+            vr[kb][h][t].w &= m3;
+          }
+        }
+    }
+    unroll<16>([&](auto ic) {
+      constexpr int a = decltype(ic)::value;   // tokens 4a..4a+3
+      constexpr int kb = a >> 2, h = (a >> 1) & 1;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint4& v = vr[kb][h][t];
+        const uint2 vv = (a & 1) ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
+        st.acc[t] = Mfma4<T>::template mma<a>(phi, vv, st.acc[t]);
+        st.acc[t] = Mfma4<T>::template mma<a>(plo, vv, st.acc[t]);
+      }
+    });
+  };
+
+  quad_phys(0, ph);
+  issue_k();
+  issue_v();
+  if constexpr (with_new) {
+    if (lane < D / 2) {
+      s_new[0][lane] = stage_k;
+      s_new[1][lane] = stage_v;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // steady state: K of the next quad is issued once QK has consumed the
+  // current one, V of the next quad once P.V has.  The scheduling barriers
+  // keep the compiler from hoisting the loads above the matrix ops that still
+  // read their destination registers (which would cost register copies).
+  for (int qd = 0; qd + 1 < nquad; ++qd) {
+    uint2 phi, plo;
+    qk_softmax(qd, phi, plo);
+    __builtin_amdgcn_sched_barrier(0);
+    quad_phys(qd + 1, ph);
+    issue_k();
+    __builtin_amdgcn_sched_barrier(0);
+    pv(qd, phi, plo, std::false_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    issue_v();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (with_new) substitute_new();
+  uint2 phi, plo;
+  qk_softmax(nquad - 1, phi, plo);
+  pv(nquad - 1, phi, plo, std::true_type{});
+}
+
+template <int D>
+__device__ __forceinline__ void reset_state4(WaveState4<D>& st) {
+  st.m_run = -INFINITY;
+  st.l_lane = 0.f;
+  st.bad = false;
+#pragma unroll
+  for (int t = 0; t < D / 64; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int D>
+__device__ __forceinline__ void emit_state4(const Params& pr, int b, int g, int slot,
+                                            WaveState4<D>& st) {
+  constexpr int NT = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int G = pr.G;
+  float l = sum16(st.l_lane);
+  float m = st.m_run;
+  if (st.bad) {
+    m = 0.f;
+    l = __builtin_nanf("");
+#pragma unroll
+    for (int t = 0; t < NT; ++t) st.acc[t] = f32x4_t{l, l, l, l};
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (e < G) {
+      const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), e));
+      const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), e));
+      const int64_t row = static_cast<int64_t>(b) * pr.Hq + g * G + e;
+      const float inv = 1.0f / lh;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int d = 64 * t + lane;
+        if (slot < 0)
+          pr.out[row * D + d] = st.acc[t][e] * inv;
+        else
+          pr.part_acc[(row * pr.maxP + slot) * D + d] = st.acc[t][e];
+      }
+      if (slot >= 0 && lane == 0) {
+        pr.part_m[row * pr.maxP + slot] = mh;
+        pr.part_l[row * pr.maxP + slot] = lh;
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+struct Engine4 {
+  using State = WaveState4<D>;
+  using Pre = Prologue4<D>;
+  static constexpr int kUnitBlocks = 4;  // blocks per step (one quad)
+  __device__ static void prologue(const Params& pr, int b, int g, int blk_begin, Pre& pre) {
+    prologue4<D>(pr, b, g, blk_begin, pre);
+  }
+  template <bool with_new>
+  __device__ static void attend(const Params& pr, int b, int g, int blk_begin, int nblk,
+                                int tok_end, State& st, const Pre& pre) {
+    attend4<T, D, with_new>(pr, b, g, blk_begin, nblk, tok_end, st, pre);
+  }
+  __device__ static void reset(State& st) { reset_state4(st); }
+  __device__ static void emit(const Params& pr, int b, int g, int slot, State& st) {
+    emit_state4(pr, b, g, slot, st);
+  }
+};
+
 // Fixed partitions: one wave per (KV head, partition, sequence); grid
 // x = head + Hkv * partition (the heads of a partition are dispatched
-// together), z = sequence.
-template <typename T, int D, int NPAIR, bool kSmallGroup>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
+// together), z = sequence.  kFused: the partition holding the sequence's
+// last position also appends the step's new token.
+template <typename Eng, bool kFused, int kWaves>
+__global__ __launch_bounds__(64, kWaves) void decode_fixed_kernel(Params pr) {
   const int g = blockIdx.x % pr.Hkv, p = blockIdx.x / pr.Hkv, b = blockIdx.z;
+  // Q and the partition's table entries are fetched together with the
+  // length, not after it (each dependent round trip costs a full memory
+  // latency under load).
+  typename Eng::Pre pre;
+  Eng::prologue(pr, b, g, p * (pr.P / kBlockSize), pre);
   const int L = pr.lens[b];
   if (!len_valid(L, pr) || L == 0) {
     if (p == 0) write_trivial_rows(pr, b, g, L);
@@ -626,27 +1093,31 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(Params pr) {
   const int np = (L + pr.P - 1) / pr.P;
   if (p >= np) return;
   const int tok0 = p * pr.P, tok1 = min(L, tok0 + pr.P);
-  WaveState<D> st;
-  reset_state(st);
-  attend_range<T, D, NPAIR, kSmallGroup, false>(pr, b, g, tok0 / kBlockSize,
-                                                (tok1 - tok0 + kBlockSize - 1) / kBlockSize,
-                                                tok1, st);
-  emit_state(pr, b, g, np == 1 ? -1 : p, st);
+  const int blk0 = tok0 / kBlockSize, nblk = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
+  typename Eng::State st;
+  Eng::reset(st);
+  if (kFused && p == np - 1)
+    Eng::template attend<true>(pr, b, g, blk0, nblk, tok1, st, pre);
+  else
+    Eng::template attend<false>(pr, b, g, blk0, nblk, tok1, st, pre);
+  Eng::emit(pr, b, g, np == 1 ? -1 : p, st);
 }
 
 // ---------------------------------------------------------------------------
 // Balanced split.  The work of a step is the list of units (sequence b, KV
-// head g, block pair q), ordered by b, then g, then q.  Sequence b owns
-// Hkv * npair(b) consecutive units.  With W waves the list is cut into W
-// equal chunks of C units (C >= kMinChunkPairs); each wave attends over its
-// chunk, which may cover the end of one (b, g) range and the start of the
-// next.  A (b, g) range cut into several chunks leaves one partial per chunk,
-// merged by merge_split_kernel; a range inside one chunk is written final.
+// head g, run of U consecutive blocks, U = the engine's step), ordered by b,
+// then g, then unit.  Sequence b owns Hkv * units(b) consecutive units.  With
+// W waves the list is cut into W equal chunks of C units (C >= kMinChunkUnits
+// steps' worth); each wave attends over its chunk, which may cover the end of
+// one (b, g) range and the start of the next.  A (b, g) range cut into
+// several chunks leaves one partial per chunk, merged by merge_split_kernel;
+// a range inside one chunk is written final.
 // ---------------------------------------------------------------------------
-constexpr int kMinChunkPairs = 4;
+constexpr int kMinChunkBlocks = 8;
 
-__device__ __forceinline__ int pairs_of(int L, const Params& pr) {
-  return (len_valid(L, pr) && L > 0) ? ((L + kBlockSize - 1) / kBlockSize + 1) >> 1 : 0;
+template <int U>
+__device__ __forceinline__ int units_of(int L, const Params& pr) {
+  return (len_valid(L, pr) && L > 0) ? ((L + kBlockSize - 1) / kBlockSize + U - 1) / U : 0;
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
@@ -671,40 +1142,31 @@ struct SplitPlan {
   int chunks; // chunks with work
 };
 
+template <int U>
 __device__ __forceinline__ SplitPlan split_plan(const Params& pr, int W) {
   const int lane = threadIdx.x & 63;
   int total = 0;
   for (int c = 0; c < pr.B; c += 64) {
     const int b = c + lane;
-    total += wave_sum(b < pr.B ? pairs_of(pr.lens[b], pr) : 0);
+    total += wave_sum(b < pr.B ? units_of<U>(pr.lens[b], pr) : 0);
   }
   total *= pr.Hkv;
   SplitPlan sp;
   sp.total = total;
-  sp.C = max(kMinChunkPairs, (total + W - 1) / W);
+  sp.C = max((kMinChunkBlocks + U - 1) / U, (total + W - 1) / W);
   sp.chunks = (total + sp.C - 1) / sp.C;
   return sp;
 }
 
-// First unit of sequence b (units of all sequences before b).
-__device__ __forceinline__ int units_before(const Params& pr, int b) {
-  const int lane = threadIdx.x & 63;
-  int acc = 0;
-  for (int c = 0; c < b; c += 64) {
-    const int s = c + lane;
-    acc += wave_sum(s < b ? pairs_of(pr.lens[s], pr) : 0);
-  }
-  return acc * pr.Hkv;
-}
-
 // The sequence whose units contain unit u, and the first unit of that
 // sequence (u < total).
+template <int U>
 __device__ __forceinline__ void locate(const Params& pr, int u, int& b_out, int& base_out) {
   const int lane = threadIdx.x & 63;
   int carried = 0;
   for (int c = 0; c < pr.B; c += 64) {
     const int b = c + lane;
-    const int units = (b < pr.B ? pairs_of(pr.lens[b], pr) : 0) * pr.Hkv;
+    const int units = (b < pr.B ? units_of<U>(pr.lens[b], pr) : 0) * pr.Hkv;
     const int incl = carried + wave_incl_scan(units);
     const uint64_t hit = __ballot(b < pr.B && incl > u);
     if (hit) {
@@ -719,46 +1181,74 @@ __device__ __forceinline__ void locate(const Params& pr, int u, int& b_out, int&
   base_out = carried;
 }
 
-template <typename T, int D, int NPAIR, bool kSmallGroup>
-__global__ __launch_bounds__(64, 2) void decode_split_kernel(Params pr) {
+// Context length of sequence b: from the register copy (lane b) when the
+// batch fits one wave, else from memory.
+__device__ __forceinline__ int len_of(const Params& pr, int lens_reg, int b) {
+  return pr.B <= 64 ? __builtin_amdgcn_readlane(lens_reg, b) : pr.lens[b];
+}
+
+template <typename Eng, int kWaves>
+__global__ __launch_bounds__(64, kWaves) void decode_split_kernel(Params pr) {
+  constexpr int U = Eng::kUnitBlocks;
+  const int lane = threadIdx.x & 63;
   const int w = blockIdx.x;
-  const SplitPlan sp = split_plan(pr, gridDim.x);
-  if (w >= sp.chunks) return;
-  const int u_begin = w * sp.C, u_end = min(sp.total, u_begin + sp.C);
+  const int W = gridDim.x;
+  SplitPlan sp;
   int b, base;
-  locate(pr, u_begin, b, base);
+  int lens_reg = 0;
+  if (pr.B <= 64) {
+    // one pass: the batch's lengths stay in a register for the whole kernel
+    lens_reg = lane < pr.B ? pr.lens[lane] : 0;
+    const int units = (lane < pr.B ? units_of<U>(lens_reg, pr) : 0) * pr.Hkv;
+    sp.total = wave_sum(units);
+    sp.C = max((kMinChunkBlocks + U - 1) / U, (sp.total + W - 1) / W);
+    sp.chunks = (sp.total + sp.C - 1) / sp.C;
+    if (w >= sp.chunks) return;
+    const int incl = wave_incl_scan(units);
+    const uint64_t hit = __ballot(lane < pr.B && incl > w * sp.C);
+    const int k = __builtin_ctzll(hit);   // hit != 0: w * C < total
+    b = k;
+    base = __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(units, k);
+  } else {
+    sp = split_plan<U>(pr, W);
+    if (w >= sp.chunks) return;
+    locate<U>(pr, w * sp.C, b, base);
+  }
+  const int u_begin = w * sp.C, u_end = min(sp.total, u_begin + sp.C);
   int u = u_begin;
-  WaveState<D> st;
+  typename Eng::State st;
   while (u < u_end) {
-    const int L = pr.lens[b];
-    const int npb = pairs_of(L, pr);
-    const int g = (u - base) / npb;
-    const int q0 = (u - base) - g * npb;
-    const int range_first = base + g * npb;                  // first unit of (b, g)
-    const int seg_end = min(u_end, range_first + npb);
+    const int L = len_of(pr, lens_reg, b);
+    const int nub = units_of<U>(L, pr);
+    const int g = (u - base) / nub;
+    const int q0 = (u - base) - g * nub;
+    const int range_first = base + g * nub;                  // first unit of (b, g)
+    const int seg_end = min(u_end, range_first + nub);
     const int nq = seg_end - u;
     const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
-    const int blk_begin = 2 * q0;
-    const int nblk = min(2 * (q0 + nq), nblk_seq) - blk_begin;
+    const int blk_begin = U * q0;
+    const int nblk = min(U * (q0 + nq), nblk_seq) - blk_begin;
     const int tok_end = min(L, (blk_begin + nblk) * kBlockSize);
-    reset_state(st);
+    Eng::reset(st);
+    typename Eng::Pre pre;
+    Eng::prologue(pr, b, g, blk_begin, pre);
     if (pr.k_new != nullptr && tok_end == L)
-      attend_range<T, D, NPAIR, kSmallGroup, true>(pr, b, g, blk_begin, nblk, tok_end, st);
+      Eng::template attend<true>(pr, b, g, blk_begin, nblk, tok_end, st, pre);
     else
-      attend_range<T, D, NPAIR, kSmallGroup, false>(pr, b, g, blk_begin, nblk, tok_end, st);
+      Eng::template attend<false>(pr, b, g, blk_begin, nblk, tok_end, st, pre);
     const int first_chunk = range_first / sp.C;
-    const int nslots = (range_first + npb - 1) / sp.C - first_chunk + 1;
-    emit_state(pr, b, g, nslots == 1 ? -1 : w - first_chunk, st);
+    const int nslots = (range_first + nub - 1) / sp.C - first_chunk + 1;
+    Eng::emit(pr, b, g, nslots == 1 ? -1 : w - first_chunk, st);
     // the wave holding the range's first unit records how many slots the
     // merge has to combine
-    if (u == range_first && (threadIdx.x & 63) == 0)
+    if (u == range_first && lane == 0)
       pr.counters[static_cast<int64_t>(b) * pr.Hkv + g] = nslots;
     u = seg_end;
-    if (u >= base + pr.Hkv * npb) {                           // next sequence with work
+    if (u >= base + pr.Hkv * nub) {                           // next sequence with work
       base = u;
       do {
         ++b;
-      } while (b < pr.B && pairs_of(pr.lens[b], pr) == 0);
+      } while (b < pr.B && units_of<U>(len_of(pr, lens_reg, b), pr) == 0);
     }
   }
 }
@@ -861,6 +1351,7 @@ Path path_from_env() {
 
 constexpr int kDefaultPartition = 256;  // fixed-partition size when none is given
 constexpr int kPairsInFlight = 2;
+constexpr int kFixedWaves4 = 3;         // waves per SIMD the 4x4x4 fixed kernel is built for
 constexpr int kSplitWavesPerCU = 8;     // balanced split: grid = CUs * this
 
 constexpr int kEvenSplit = -1;          // partition_size value selecting the even split
@@ -912,10 +1403,12 @@ LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_
   lp.split = partition_size == kEvenSplit && !lp.generic;
   if (lp.split) {
     lp.W = split_waves();
-    const int max_pairs = ((max_ctx + kBlockSize - 1) / kBlockSize + 1) / 2;
+    // a range of nblk blocks is cut into at most ceil(nblk / kMinChunkBlocks) + 1
+    // chunks (chunks hold at least kMinChunkBlocks blocks' worth of units)
+    const int max_blk = (max_ctx + kBlockSize - 1) / kBlockSize;
     lp.P = 0;
-    lp.maxP = max_pairs == 0 ? 1 : std::min((max_pairs + kMinChunkPairs - 1) / kMinChunkPairs + 1,
-                                            lp.W);
+    lp.maxP = max_blk == 0 ? 1 : std::min((max_blk + kMinChunkBlocks - 1) / kMinChunkBlocks + 1,
+                                          lp.W);
   } else {
     lp.P = partition_size > 0 ? partition_size : kDefaultPartition;  // 0 or -1 on fp32
     lp.maxP = max_ctx <= 0 ? 1 : (max_ctx + lp.P - 1) / lp.P;
@@ -924,33 +1417,35 @@ LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_
 }
 
 template <typename T, int D>
-void launch_partitions(const Params& pr, bool generic, hipStream_t s) {
-  // matrix-core kernel: x = KV head + Hkv * partition (the heads of one
+void launch_partitions(const Params& pr, bool generic, bool fused, hipStream_t s) {
+  // matrix-core kernels: x = KV head + Hkv * partition (the heads of one
   // partition are dispatched together), z = sequence
   dim3 grid_m(pr.Hkv * pr.maxP, 1, pr.B);
   if (generic)
     decode_generic_kernel<T, D><<<dim3(pr.maxP, pr.Hkv, pr.B), 256, 0, s>>>(pr);
+  else if (pr.G <= 4 && fused)
+    decode_fixed_kernel<Engine4<T, D>, true, kFixedWaves4><<<grid_m, 64, 0, s>>>(pr);
   else if (pr.G <= 4)
-    decode_mfma_kernel<T, D, kPairsInFlight, true><<<grid_m, 64, 0, s>>>(pr);
+    decode_fixed_kernel<Engine4<T, D>, false, kFixedWaves4><<<grid_m, 64, 0, s>>>(pr);
   else
-    decode_mfma_kernel<T, D, kPairsInFlight, false><<<grid_m, 64, 0, s>>>(pr);
+    decode_fixed_kernel<Engine16<T, D, kPairsInFlight, false>, false, 1><<<grid_m, 64, 0, s>>>(pr);
 }
 
 template <>
-void launch_partitions<F32, 64>(const Params& pr, bool, hipStream_t s) {
+void launch_partitions<F32, 64>(const Params& pr, bool, bool, hipStream_t s) {
   decode_generic_kernel<F32, 64><<<dim3(pr.maxP, pr.Hkv, pr.B), 256, 0, s>>>(pr);
 }
 template <>
-void launch_partitions<F32, 128>(const Params& pr, bool, hipStream_t s) {
+void launch_partitions<F32, 128>(const Params& pr, bool, bool, hipStream_t s) {
   decode_generic_kernel<F32, 128><<<dim3(pr.maxP, pr.Hkv, pr.B), 256, 0, s>>>(pr);
 }
 
 template <typename T, int D>
 void launch_split(const Params& pr, int W, hipStream_t s) {
   if (pr.G <= 4)
-    decode_split_kernel<T, D, kPairsInFlight, true><<<W, 64, 0, s>>>(pr);
+    decode_split_kernel<Engine4<T, D>, 2><<<W, 64, 0, s>>>(pr);
   else
-    decode_split_kernel<T, D, kPairsInFlight, false><<<W, 64, 0, s>>>(pr);
+    decode_split_kernel<Engine16<T, D, kPairsInFlight, false>, 1><<<W, 64, 0, s>>>(pr);
 }
 
 enum class Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
@@ -972,13 +1467,17 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
   }
   if (first) {
     switch (dt) {
-      case PA_F32: launch_partitions<F32, D>(pr, true, s); break;
-      case PA_F16: launch_partitions<F16, D>(pr, lp.generic, s); break;
-      case PA_BF16: launch_partitions<BF16, D>(pr, lp.generic, s); break;
+      case PA_F32: launch_partitions<F32, D>(pr, true, false, s); break;
+      case PA_F16: launch_partitions<F16, D>(pr, lp.generic, pr.k_new != nullptr, s); break;
+      case PA_BF16: launch_partitions<BF16, D>(pr, lp.generic, pr.k_new != nullptr, s); break;
     }
   }
   if (second && pr.maxP > 1) merge_kernel<D><<<dim3(pr.Hq, pr.B), 256, 0, s>>>(pr);
 }
+
+// Whether the partition kernel of this plan appends the step's new tokens
+// itself (pa_decode_step); otherwise pa_cache_append runs first.
+bool fuses_append(const LaunchPlan& lp, int G) { return !lp.generic && (lp.split || G <= 4); }
 
 // Validates the arguments shared by pa_decode / pa_decode_partial /
 // pa_decode_merge and launches the requested phases.
@@ -1064,7 +1563,7 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (nt) {
-    if (lp.split) {
+    if (fuses_append(lp, pr.G)) {
       // append fused into the partition kernel
       pr.k_new = nt->k_new;
       pr.v_new = nt->v_new;

@@ -38,17 +38,16 @@ struct BF16 {
 
 // Element offsets inside one (block, kv-head) tile of D*16 elements.
 //   K tile: [D/x][16][x]
-//   V tile: [D][16] with the 16 token slots of a dim row in the order 0-3,
-//           8-11, 4-7, 12-15 (token t at slot t with bits 2 and 3 exchanged),
-//           so that tokens {0-3, 8-11} and {4-7, 12-15} are 8 adjacent slots.
-__device__ __host__ inline int v_slot(int t) { return (t & 3) | ((t & 4) << 1) | ((t & 8) >> 1); }
+//   V tile: [16/x][D][x]  (tokens 0..x-1 as D rows of x tokens, then the
+//           next x tokens): one 16-byte load gives x consecutive tokens of a dim.
 template <typename T>
 __device__ __host__ inline int64_t k_elem(int t, int d) {
   return (static_cast<int64_t>(d / T::kVecElems) * kBlockSize + t) * T::kVecElems +
          d % T::kVecElems;
 }
-__device__ __host__ inline int64_t v_elem(int t, int d) {
-  return static_cast<int64_t>(d) * kBlockSize + v_slot(t);
+template <typename T>
+__device__ __host__ inline int64_t v_elem(int t, int d, int D) {
+  return (static_cast<int64_t>(t / T::kVecElems) * D + d) * T::kVecElems + t % T::kVecElems;
 }
 // First element of the (block, kv-head) tile.
 __device__ __host__ inline int64_t tile_base(int64_t block, int head, int num_kv_heads, int D) {

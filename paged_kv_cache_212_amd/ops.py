@@ -35,11 +35,12 @@ def _dev(t: torch.Tensor, name: str):
 
 def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
               device="cuda", fill=None):
-    """K pool [N][Hkv][D/x][16][x] and V pool [N][Hkv][D][16] (x = 16 bytes / element)."""
+    """K pool [N][Hkv][D/x][16][x] and V pool [N][Hkv][16/x][D][x] (x = 16 bytes / element)."""
     x = 16 // torch.empty((), dtype=dtype).element_size()
     k = torch.empty((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x), dtype=dtype,
                     device=device)
-    v = torch.empty((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), dtype=dtype, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE // x, head_dim, x), dtype=dtype,
+                    device=device)
     if fill is not None:
         k.fill_(fill)
         v.fill_(fill)
@@ -48,8 +49,10 @@ def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dt
 
 def _pool_dims(k_pool: torch.Tensor, v_pool: torch.Tensor):
     N, H = k_pool.shape[0], k_pool.shape[1]
-    D = v_pool.shape[2]
-    if v_pool.shape != (N, H, D, BLOCK_SIZE) or k_pool.dtype != v_pool.dtype:
+    D = v_pool.shape[3] if v_pool.dim() == 5 else -1
+    x = 16 // k_pool.element_size()
+    if k_pool.shape != (N, H, D // x, BLOCK_SIZE, x) or \
+            v_pool.shape != (N, H, BLOCK_SIZE // x, D, x) or k_pool.dtype != v_pool.dtype:
         raise ValueError("k_pool/v_pool shapes or dtypes do not match the pool layout")
     if k_pool.numel() != v_pool.numel():
         raise ValueError("k_pool and v_pool sizes differ")

@@ -170,7 +170,8 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 511, 512, 513, 1023, 1024, 
     ("bf16", 32, 8, 128, 0), ("bf16", 32, 8, 128, -1), ("bf16", 32, 8, 128, 16),
     ("bf16", 16, 1, 64, 512),
     ("f16", 8, 8, 128, 512), ("f16", 16, 2, 64, 256), ("bf16", 4, 2, 64, 1024),
-    ("f32", 4, 4, 64, 512), ("f32", 8, 2, 128, 0), ("bf16", 2, 2, 128, 4096)])
+    ("f32", 4, 4, 64, 512), ("f32", 8, 2, 128, 0), ("bf16", 2, 2, 128, 4096),
+    ("bf16", 12, 4, 128, 256), ("f16", 6, 2, 64, -1)])
 def test_edge_lengths_and_shapes(dtype, hq, hkv, d, ps, kernel):
     case = custom_case(31, dtype, EDGE_LENS, hq, hkv, d, partition_size=ps, boost_prob=0.02)
     say(f"[edge] {dtype} Hq={hq} Hkv={hkv} D={d} P={ps} kernel={kernel}")
@@ -213,7 +214,7 @@ SPLIT_LENS = {
 
 @pytest.mark.parametrize("lens", list(SPLIT_LENS), ids=list(SPLIT_LENS))
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 16, 2, 64),
-                                            ("bf16", 16, 16, 128)])
+                                            ("bf16", 16, 16, 128), ("f16", 24, 8, 128)])
 def test_even_split_shapes(lens, dtype, hq, hkv, d):
     """The even split of the batch's work across waves (partition_size 0):
     ranges cut over many chunks, chunks holding many whole sequences."""

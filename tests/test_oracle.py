@@ -64,21 +64,20 @@ def test_worked_example_100_tokens():
 
 
 # ------------------------------------------------------------------ layout --
-# Offsets enumerated by hand from the layout statement:
+# Offsets enumerated by hand from the layout statement (bs = 16, x = 16 / elt):
 #   K: (((b*H + h)*(D/x) + d//x)*bs + t)*x + d%x
-#   V: ((b*H + h)*D + d)*bs + slot(t), slot(t) = t with bits 2 and 3 exchanged
-#      (slot(4) = 8, slot(9) = 5, slot(11) = 7; 0-3 and 12-15 stay put)
+#   V: (((b*H + h)*(bs/x) + t//x)*D + d)*x + t%x
 LAYOUT_CASES = [
     # dtype, H, D, (b, h, t, d), K offset, V offset
-    ("bf16", 2, 16, (1, 1, 3, 10), 922, 931),   # K: ((3*2+1)*16+3)*8+2 ; V: (3*16+10)*16+3
-    ("bf16", 2, 16, (0, 0, 1, 0), 8, 1),
-    ("bf16", 2, 16, (0, 0, 0, 8), 128, 128),
-    ("bf16", 2, 16, (2, 0, 15, 15), 1279, 1279),
-    ("f32", 1, 8, (1, 0, 2, 5), 201, 210),      # K: ((1*2+1)*16+2)*4+1 ; V: (1*8+5)*16+2
-    ("bf16", 2, 16, (0, 1, 4, 3), 291, 312),    # K: ((1*2+0)*16+4)*8+3 ; V: (1*16+3)*16+8
-    ("bf16", 2, 16, (1, 0, 9, 12), 716, 709),   # K: ((2*2+1)*16+9)*8+4 ; V: (2*16+12)*16+5
-    ("bf16", 2, 16, (0, 0, 11, 0), 88, 7),      # K: (0*16+11)*8+0      ; V: 0*16+7
-    ("f32", 1, 8, (0, 0, 6, 1), 25, 26),        # K: (0*16+6)*4+1       ; V: 1*16+10
+    ("bf16", 2, 16, (1, 1, 3, 10), 922, 851),   # K: ((3*2+1)*16+3)*8+2 ; V: ((3*2+0)*16+10)*8+3
+    ("bf16", 2, 16, (0, 0, 1, 0), 8, 1),        # K: (0*16+1)*8         ; V: 0*8+1
+    ("bf16", 2, 16, (0, 0, 0, 8), 128, 64),     # K: ((0*2+1)*16+0)*8   ; V: (0*16+8)*8
+    ("bf16", 2, 16, (2, 0, 15, 15), 1279, 1279),  # both: last element of tile (4*256 - 1 + 256)
+    ("f32", 1, 8, (1, 0, 2, 5), 201, 150),      # K: ((1*2+1)*16+2)*4+1 ; V: ((1*4+0)*8+5)*4+2
+    ("bf16", 2, 16, (0, 1, 4, 3), 291, 284),    # K: ((1*2+0)*16+4)*8+3 ; V: ((1*2+0)*16+3)*8+4
+    ("bf16", 2, 16, (1, 0, 9, 12), 716, 737),   # K: ((2*2+1)*16+9)*8+4 ; V: ((2*2+1)*16+12)*8+1
+    ("bf16", 2, 16, (0, 0, 11, 0), 88, 131),    # K: (0*16+11)*8+0      ; V: ((0*2+1)*16+0)*8+3
+    ("f32", 1, 8, (0, 0, 6, 1), 25, 38),        # K: (0*16+6)*4+1       ; V: ((0*4+1)*8+1)*4+2
 ]
 
 
@@ -87,7 +86,7 @@ def test_layout_offsets_and_append(dtype, H, D, idx, ko, vo):
     b, h, t, d = idx
     x = 4 if dtype == "f32" else 8
     assert k_offset(b, h, t, d, H, D, 16, x) == ko
-    assert v_offset(b, h, t, d, H, D, 16) == vo
+    assert v_offset(b, h, t, d, H, D, 16, x) == vo
     kp, vp = new_pools(4, H, D, 16, dtype)
     bd = kp.dtype
     tok = np.array([[[1000 + 100 * hh + dd for dd in range(D)] for hh in range(H)]], dtype=bd)
