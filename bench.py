@@ -2,10 +2,11 @@
 """Decode-step benchmark of the paged KV cache on one MI355X.
 
 A step is one pass of the whole device path over one batch: copy-on-write block
-copies (when the step's reservation produced any), then pa_decode_step, which
-appends the batch's new tokens into their slots and attends (on the even-split
-path the append happens inside the attention kernel), then the log-sum-exp
-merge.
+copies (when the step's reservation produced any), then pa_decode_step_partial,
+whose attention kernel also appends the batch's new tokens into their slots,
+then pa_decode_merge, the log-sum-exp merge of the partition partials (the two
+calls together are pa_decode_step).  The attention kernel is timed with HIP
+events on the launch stream.
 The host reservation (slots, copy pairs, block tables) is done by the C++
 block manager before the timed region, and the same step is replayed every
 iteration (append and copy are idempotent, so every replay does the full work).
@@ -44,9 +45,11 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
-    ap.add_argument("--fused-step", action="store_true",
-                    help="run each step as one pa_decode_step call (append fused into the "
-                         "attention kernel on the even split) and time that call")
+    ap.add_argument("--mode", choices=("phased", "separate", "step"), default="phased",
+                    help="phased: pa_decode_step_partial (append fused into the attention "
+                         "kernel, timed) then pa_decode_merge; separate: pa_cache_append, "
+                         "pa_decode_partial (timed), pa_decode_merge; step: one "
+                         "pa_decode_step call (timed as a whole)")
     ap.add_argument("--no-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -208,26 +211,30 @@ def main():
             (kp.data_ptr(), vp.data_ptr(), plan.d_cows.data_ptr(), ncow, N, Hkv, D, 16, dt,
              stream),
             dec, app, dec_sep))
-    f_copy, f_step = L.pa_copy_blocks, L.pa_decode_step
+    f_copy, f_step, f_step_part = L.pa_copy_blocks, L.pa_decode_step, L.pa_decode_step_partial
     f_app, f_part, f_merge = L.pa_cache_append, L.pa_decode_partial, L.pa_decode_merge
+    f_time = L.pa_time_next_attention
 
     def step(i, ev=None):
         c_copy, c_dec, c_app, c_dec_sep = calls[i % len(calls)]
         if ncow:
             check(f_copy(*c_copy), "pa_copy_blocks")
-        if args.fused_step:
+        if args.mode == "step":
             if ev is not None:
                 ev[0].record()
             check(f_step(*c_dec), "pa_decode_step")
             if ev is not None:
                 ev[1].record()
             return
-        check(f_app(*c_app), "pa_cache_append")
+        if args.mode == "separate":
+            check(f_app(*c_app), "pa_cache_append")
         if ev is not None:
-            ev[0].record()
-        check(f_part(*c_dec_sep), "pa_decode_partial")     # the attention kernel
-        if ev is not None:
-            ev[1].record()
+            # the attention kernel's own dispatch records the two events
+            check(f_time(ev[0].cuda_event, ev[1].cuda_event), "pa_time_next_attention")
+        if args.mode == "separate":
+            check(f_part(*c_dec_sep), "pa_decode_partial")     # the attention kernel
+        else:
+            check(f_step_part(*c_dec), "pa_decode_step_partial")   # append + attention
         check(f_merge(*c_dec_sep), "pa_decode_merge")
 
     for i in range(args.warmup):
@@ -237,6 +244,11 @@ def main():
 
     evs = None if args.no_events else [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                                        for _ in range(args.steps)]
+    if evs:
+        for pair in evs:           # torch creates the HIP events on first record
+            for e in pair:
+                e.record()
+        torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -274,12 +286,12 @@ def main():
         alg = kv_bytes + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
         achieved = alg / (part_ms * 1e-3) / 1e9
         res["attention_kernel_us"] = round(dec_ms * 1e3, 3)
-        if not args.fused_step:
+        if args.mode == "separate":
             kname = "attention partition kernel (pa_decode_partial)"
-        elif P_used == 0:
-            kname = "pa_decode_step: attention kernel with the append fused in, then the merge"
+        elif args.mode == "phased":
+            kname = "attention partition kernel with the append fused in (pa_decode_step_partial)"
         else:
-            kname = "pa_decode_step: append, attention and merge kernels"
+            kname = "pa_decode_step as a whole (attention kernel and merge)"
         res["roofline"] = {"kernel": kname,
                            "bound": "hbm", "achieved": round(achieved, 2),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -167,17 +167,20 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
 
 /* How pa_decode splits contexts for these arguments; partition_size is
  *   > 0 (a multiple of 16): fixed partitions of that many tokens;
- *   0: the library's choice (fixed partitions of 256 tokens);
- *   -1: an even split of the batch's work over the GPU's waves (matrix-core
- *       path only; fp32 and the plain-FMA kernel use the default partitions).
+ *   0: the library's choice: the even split on the matrix-core path
+ *      (fp16/bf16), fixed partitions of 256 tokens for fp32 and the plain-FMA
+ *      kernel;
+ *   -1: the even split (matrix-core path only; fp32 and the plain-FMA kernel
+ *       use 256-token partitions).
  * Returns the partition size in tokens for fixed partitions, 0 for the even
  * split, -1 for invalid arguments.
  *   Fixed partitions: partition p of a sequence covers tokens
  *     [p*P, (p+1)*P); each is attended by one wave, merged when more than one.
- *   Even split: the (sequence, KV head, 32-token pair) units of the whole
- *     batch are cut into equal contiguous chunks, one per wave; a (sequence,
- *     head) cut into several chunks is merged the same way; pa_decode_step
- *     appends inside the attention kernel. */
+ *   Even split: the batch's work, as (sequence, KV head, run of 4 blocks)
+ *     units (2 blocks when more than 4 query heads share a KV head), is cut
+ *     into equal contiguous chunks, one per wave of a grid of 4 waves per
+ *     compute unit; a (sequence, head) cut into several chunks is merged the
+ *     same way. */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype);
@@ -242,12 +245,21 @@ pa_status pa_decode_merge(float* out, const void* q, const void* k_pool, const v
  * result of pa_cache_append(k_pool, v_pool, k_new, v_new, slot_mapping,
  * num_seqs, ...) followed by pa_decode(...).  Row b of k_new/v_new
  * ([num_seqs][Hkv][D], KV dtype) is sequence b's token at position
- * context_lens[b] - 1, and slot_mapping[b] (device int64) must be the slot of
- * that position in block_tables[b] (or -1: then the pool is not written but
- * the token still takes part in the attention).  On the even-split path the
- * append is done inside the attention kernel (one launch fewer); otherwise
- * the two kernels run back to back.  Copy-on-write copies of the step must
- * be issued (pa_copy_blocks) before this call on the same stream. */
+ * context_lens[b] - 1, and slot_mapping[b] (device int64) is the slot of
+ * that position in block_tables[b], or -1 to skip the write (position
+ * context_lens[b] - 1 is then attended with the pool's current content).  A
+ * slot elsewhere in the pool gets the token written there, but then out is
+ * only defined when that slot is not attended by the step.  On the
+ * matrix-core path (fp16/bf16 with at most 4 query heads per KV head, or the
+ * even split) the append is done inside the attention kernel, one launch
+ * fewer; there a sequence whose length fails the bounds checks (NaN out
+ * rows) or is 0 gets no pool write.  Otherwise the two kernels run back to
+ * back.  Copy-on-write copies of the step must be issued (pa_copy_blocks)
+ * before this call on the same stream.
+ *   pa_decode_step_partial: the first phase of pa_decode_step (append and
+ *     partition kernel, as pa_decode_partial); follow it with pa_decode_merge
+ *     with the same arguments and workspace.  pa_decode_step(...) ==
+ *     pa_decode_step_partial(...) then pa_decode_merge(...). */
 pa_status pa_decode_step(float* out, const void* q, void* k_pool, void* v_pool,
                          const void* k_new, const void* v_new, const int64_t* slot_mapping,
                          const int32_t* block_tables, const int32_t* context_lens,
@@ -256,6 +268,25 @@ pa_status pa_decode_step(float* out, const void* q, void* k_pool, void* v_pool,
                          int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                          int32_t partition_size, pa_dtype dtype, void* workspace,
                          size_t workspace_bytes, void* stream);
+pa_status pa_decode_step_partial(float* out, const void* q, void* k_pool, void* v_pool,
+                                 const void* k_new, const void* v_new,
+                                 const int64_t* slot_mapping, const int32_t* block_tables,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 float scale, int32_t partition_size, pa_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement hook: the next attention kernel launched by a decode call
+ * (pa_decode, pa_decode_partial, pa_decode_step or pa_decode_step_partial)
+ * on this host thread records start_event when it starts executing and
+ * stop_event when it finishes, attached to the kernel's own dispatch, so
+ * hipEventElapsedTime(start, stop) is that kernel's duration.  The events are
+ * hipEvent_t handles created by the caller (with timing enabled); they are
+ * consumed by the next decode call whether or not it launches an attention
+ * kernel.  Both NULL disarms; one NULL is PA_ERR_INVALID_ARG. */
+pa_status pa_time_next_attention(void* start_event, void* stop_event);
 
 /* Reassembles the logically contiguous cache through the block tables:
  * k_out/v_out device [num_seqs][Hkv][max_context_len][D] in the KV dtype,

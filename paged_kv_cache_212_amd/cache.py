@@ -102,16 +102,28 @@ class PagedKVCache:
 
     def step(self, plan: StepPlan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
              out: torch.Tensor | None = None, scale=None, partition_size: int = 0,
-             workspace=None, stream=None, fused: bool = True):
+             workspace=None, stream=None, fused=True):
         """Copy-on-write, append the new tokens, then decode attention (all on device).
 
-        fused: append and attend with one pa_decode_step call; otherwise
-        pa_cache_append then pa_decode."""
+        fused: True -> one pa_decode_step call; "phased" -> pa_decode_step_partial
+        then pa_decode_merge; False -> pa_cache_append then pa_decode."""
         if plan.cows.shape[0]:
             ops.copy_blocks(self.k_pool, self.v_pool, plan.d_cows, stream)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        if fused:
+        if fused == "phased":
+            B, Hq, D = q.shape
+            if workspace is None:
+                workspace = ops.decode_workspace(B, Hq, self.num_kv_heads, D,
+                                                 plan.max_context_len, partition_size, q.dtype,
+                                                 q.device)
+            ops.decode_step(out, q, self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
+                            plan.d_tables, plan.d_lens, plan.max_context_len, scale,
+                            partition_size, workspace, stream, phase="partial")
+            ops.decode(out, q, self.k_pool, self.v_pool, plan.d_tables, plan.d_lens,
+                       plan.max_context_len, scale, partition_size, workspace, stream,
+                       phase="merge")
+        elif fused:
             ops.decode_step(out, q, self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
                             plan.d_tables, plan.d_lens, plan.max_context_len, scale,
                             partition_size, workspace, stream)

@@ -22,6 +22,7 @@
 // Scores are kept in the log2 domain (scale * log2(e) folded in) and
 // exponentiated with exp2.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 #include <cstdlib>
@@ -412,14 +413,22 @@ __device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int
     stage_k = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.k_new) + nrow)[lane];
     stage_v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.v_new) + nrow)[lane];
   }
+  // Appends the new token with the effect of pa_cache_append then the
+  // attention over the pool: the token is written to its slot (skipped when
+  // out of the pool), and it replaces the loaded values of position
+  // tok_end - 1 only when the slot is the table's slot of that position.
   auto substitute_new = [&](int u) {
     const int pos = tok_end - 1;
     const int sel = pos / kBlockSize - blk_begin - 2 * (npair - 1);
     const int tn = pos % kBlockSize;
     const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
     const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
+    const int64_t slot = pr.slots[b];
+    const bool in_pool = slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize;
+    const bool at_table =
+        in_pool && slot == static_cast<int64_t>(phys_of(2 * (npair - 1) + sel)) * kBlockSize + tn;
     // K: lane row n holds token 8*((n >> 2) & 1) + 4*hh + (n & 3) of block n >> 3
-    if ((n >> 3) == sel && (n & 3) == (tn & 3) && ((n >> 2) & 1) == (tn >> 3)) {
+    if (at_table && (n >> 3) == sel && (n & 3) == (tn & 3) && ((n >> 2) & 1) == (tn >> 3)) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
         if (hh == ((tn >> 2) & 1)) {
@@ -429,7 +438,7 @@ __device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int
         }
     }
     // V: lane group j holds block j >> 1, tokens 8*(j & 1) + e as element e
-    if ((j >> 1) == sel && (j & 1) == (tn >> 3)) {
+    if (at_table && (j >> 1) == sel && (j & 1) == (tn >> 3)) {
       const int e = tn & 7;
       const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
       const int sh = (e & 1) * 16, dw = e >> 1;
@@ -443,9 +452,8 @@ __device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int
         vv.w = dw == 3 ? ((vv.w & keep) | val) : vv.w;
       }
     }
-    // write the token into its pool slot (skipped when out of range)
-    const int64_t slot = pr.slots[b];
-    if (slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
+    // write the token into its pool slot
+    if (in_pool) {
       const int64_t blk = slot / kBlockSize;
       const int ts = static_cast<int>(slot % kBlockSize);
       uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
@@ -625,10 +633,12 @@ struct Engine16 {
   struct Pre {};
   static constexpr int kUnitBlocks = 2;  // blocks per step (one pair)
   __device__ static void prologue(const Params&, int, int, int, Pre&) {}
-  template <bool with_new>
-  __device__ static void attend(const Params& pr, int b, int g, int blk_begin, int nblk,
-                                int tok_end, State& st, const Pre&) {
-    attend_range<T, D, NPAIR, kSmallGroup, with_new>(pr, b, g, blk_begin, nblk, tok_end, st);
+  __device__ static void attend_rt(const Params& pr, int b, int g, int blk_begin, int nblk,
+                                   int tok_end, State& st, const Pre&, bool with_new) {
+    if (with_new)
+      attend_range<T, D, NPAIR, kSmallGroup, true>(pr, b, g, blk_begin, nblk, tok_end, st);
+    else
+      attend_range<T, D, NPAIR, kSmallGroup, false>(pr, b, g, blk_begin, nblk, tok_end, st);
   }
   __device__ static void reset(State& st) { reset_state(st); }
   __device__ static void emit(const Params& pr, int b, int g, int slot, State& st) {
@@ -781,9 +791,13 @@ __device__ __forceinline__ void prologue4(const Params& pr, int b, int g, int bl
   pre.tab = k < pr.max_blocks ? pr.tables[static_cast<int64_t>(b) * pr.max_blocks + k] : 0;
 }
 
-template <typename T, int D, bool with_new>
+// with_new (uniform): the range ends at the sequence's last position, which
+// holds the step's new token (fused append).  A run-time flag rather than a
+// template parameter, so the kernel carries one copy of the loop.
+template <typename T, int D>
 __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_begin, int nblk,
-                                        int tok_end, WaveState4<D>& st, const Prologue4<D>& pre) {
+                                        int tok_end, WaveState4<D>& st, const Prologue4<D>& pre,
+                                        bool with_new) {
   constexpr int NC = D / 8;    // 16-byte K chunks per token
   constexpr int NT = D / 64;   // 64-dim output tiles
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
@@ -855,11 +869,18 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   // into the last quad's registers and written to its pool slot.
   __shared__ uint32_t s_new[2][D / 2];
   uint32_t stage_k = 0, stage_v = 0;
-  if (with_new && lane < D / 2) {
-    const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
-    stage_k = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.k_new) + nrow)[lane];
-    stage_v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.v_new) + nrow)[lane];
+  int64_t new_slot = -1;
+  if (with_new) {
+    // fetched with the first quad's loads, not at the end of the range
+    new_slot = pr.slots[b];
+    if (lane < D / 2) {
+      const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
+      stage_k = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.k_new) + nrow)[lane];
+      stage_v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.v_new) + nrow)[lane];
+    }
   }
+  // Puts the new token into the last quad's registers (its pool slot may
+  // still hold an older value for this wave's loads).
   auto substitute_new = [&]() {
     const int qt = tok_end - 1 - (blk_begin + 4 * (nquad - 1)) * kBlockSize;  // 0..63
     const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
@@ -886,8 +907,45 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
             vv.w = dw == 3 ? ((vv.w & keep) | val) : vv.w;
           }
         }
-    const int64_t slot = pr.slots[b];
-    if (slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
+  };
+  // Appends the new token (position tok_end - 1, in the last quad), with the
+  // effect of pa_cache_append then the attention over the pool:
+  //   * slot == the table's slot of that position (the caller's contract):
+  //     the token goes into the last quad's registers, and the wave holds its
+  //     whole half block (8 tokens, all dims): as loaded, with the token put
+  //     in.  Writing that back as whole 128-byte lines stores the token and
+  //     rewrites the other tokens' current bytes unchanged (2-byte V stores
+  //     would leave 16 partly written lines per head);
+  //   * any other slot in the pool: the token alone is written there,
+  //     element by element, and the position is attended as loaded;
+  //   * slot out of the pool (-1): nothing is written.
+  auto append_new = [&]() {
+    const int64_t slot = new_slot;
+    if (slot < 0 || slot >= static_cast<int64_t>(pr.num_blocks) * kBlockSize) return;
+    const int qt = tok_end - 1 - (blk_begin + 4 * (nquad - 1)) * kBlockSize;  // 0..63
+    const int kb = qt >> 4, h = (qt >> 3) & 1;
+    const int phys = kb == 0 ? ph[0] : kb == 1 ? ph[1] : kb == 2 ? ph[2] : ph[3];
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
+    if (slot == static_cast<int64_t>(phys) * kBlockSize + (qt & 15)) {
+      substitute_new();
+      const int64_t tile = (static_cast<int64_t>(phys) * pr.Hkv + g) * kTileBytes;
+      char* kt = static_cast<char*>(pr.kpool_w) + tile + (lane & 15) * 16;
+      if ((lane >> 3) == (qt >> 3)) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) *reinterpret_cast<uint4*>(kt + c * 256) = kr[c];
+      }
+      char* vt = static_cast<char*>(pr.vpool_w) + tile + lane * 16;
+#pragma unroll
+      for (int KB = 0; KB < 4; ++KB)
+#pragma unroll
+        for (int H = 0; H < 2; ++H)
+          if (KB == kb && H == h) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+              *reinterpret_cast<uint4*>(vt + (H * D + 64 * t) * 16) = vr[KB][H][t];
+          }
+    } else {
       const int64_t blk = slot / kBlockSize;
       const int ts = static_cast<int>(slot % kBlockSize);
       uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
@@ -979,7 +1037,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   quad_phys(0, ph);
   issue_k();
   issue_v();
-  if constexpr (with_new) {
+  if (with_new) {
     if (lane < D / 2) {
       s_new[0][lane] = stage_k;
       s_new[1][lane] = stage_v;
@@ -1002,7 +1060,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     issue_v();
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (with_new) substitute_new();
+  if (with_new) append_new();
   uint2 phi, plo;
   qk_softmax(nquad - 1, phi, plo);
   pv(nquad - 1, phi, plo, std::true_type{});
@@ -1062,10 +1120,9 @@ struct Engine4 {
   __device__ static void prologue(const Params& pr, int b, int g, int blk_begin, Pre& pre) {
     prologue4<D>(pr, b, g, blk_begin, pre);
   }
-  template <bool with_new>
-  __device__ static void attend(const Params& pr, int b, int g, int blk_begin, int nblk,
-                                int tok_end, State& st, const Pre& pre) {
-    attend4<T, D, with_new>(pr, b, g, blk_begin, nblk, tok_end, st, pre);
+  __device__ static void attend_rt(const Params& pr, int b, int g, int blk_begin, int nblk,
+                                   int tok_end, State& st, const Pre& pre, bool with_new) {
+    attend4<T, D>(pr, b, g, blk_begin, nblk, tok_end, st, pre, with_new);
   }
   __device__ static void reset(State& st) { reset_state4(st); }
   __device__ static void emit(const Params& pr, int b, int g, int slot, State& st) {
@@ -1096,10 +1153,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_fixed_kernel(Params pr) {
   const int blk0 = tok0 / kBlockSize, nblk = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
   typename Eng::State st;
   Eng::reset(st);
-  if (kFused && p == np - 1)
-    Eng::template attend<true>(pr, b, g, blk0, nblk, tok1, st, pre);
-  else
-    Eng::template attend<false>(pr, b, g, blk0, nblk, tok1, st, pre);
+  Eng::attend_rt(pr, b, g, blk0, nblk, tok1, st, pre, kFused && p == np - 1);
   Eng::emit(pr, b, g, np == 1 ? -1 : p, st);
 }
 
@@ -1110,7 +1164,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_fixed_kernel(Params pr) {
 // W waves the list is cut into W equal chunks of C units (C >= kMinChunkUnits
 // steps' worth); each wave attends over its chunk, which may cover the end of
 // one (b, g) range and the start of the next.  A (b, g) range cut into
-// several chunks leaves one partial per chunk, merged by merge_split_kernel;
+// several chunks leaves one partial per chunk, merged by merge_kernel;
 // a range inside one chunk is written final.
 // ---------------------------------------------------------------------------
 constexpr int kMinChunkBlocks = 8;
@@ -1232,10 +1286,8 @@ __global__ __launch_bounds__(64, kWaves) void decode_split_kernel(Params pr) {
     Eng::reset(st);
     typename Eng::Pre pre;
     Eng::prologue(pr, b, g, blk_begin, pre);
-    if (pr.k_new != nullptr && tok_end == L)
-      Eng::template attend<true>(pr, b, g, blk_begin, nblk, tok_end, st, pre);
-    else
-      Eng::template attend<false>(pr, b, g, blk_begin, nblk, tok_end, st, pre);
+    Eng::attend_rt(pr, b, g, blk_begin, nblk, tok_end, st, pre,
+                   pr.k_new != nullptr && tok_end == L);
     const int first_chunk = range_first / sp.C;
     const int nslots = (range_first + nub - 1) / sp.C - first_chunk + 1;
     Eng::emit(pr, b, g, nslots == 1 ? -1 : w - first_chunk, st);
@@ -1253,91 +1305,90 @@ __global__ __launch_bounds__(64, kWaves) void decode_split_kernel(Params pr) {
   }
 }
 
-// Merge for the balanced split: grid (Hkv, B), 256 threads; merges the G
-// query-head rows of (b, g) over the slots the partition kernel recorded, and
-// writes the rows of empty (zeros) and out-of-bounds (NaN) sequences, which
-// own no units.
-template <int D>
-__global__ __launch_bounds__(256) void merge_split_kernel(Params pr) {
-  constexpr int NT = 256;
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int G = pr.G;
-  const int L = pr.lens[b];
-  const int64_t row0 = static_cast<int64_t>(b) * pr.Hq + g * G;
-  if (!len_valid(L, pr) || L == 0) {
-    const float v = (L == 0) ? 0.f : __builtin_nanf("");
-    for (int i = tid; i < G * D; i += NT) pr.out[row0 * D + i] = v;
-    return;
-  }
-  const int ns = pr.counters[static_cast<int64_t>(b) * pr.Hkv + g];
-  if (ns <= 1) return;                                         // written final
-  for (int i = tid; i < G * D; i += NT) {
-    const int h = i / D, d = i % D;
-    const int64_t row = row0 + h;
-    const float* pm = pr.part_m + row * pr.maxP;
-    const float* pl = pr.part_l + row * pr.maxP;
-    const float* pa = pr.part_acc + row * pr.maxP * D + d;
-    float M = -INFINITY;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, pm[k]);
-    float num = 0.f, den = 0.f;
-    for (int k = 0; k < ns; ++k) {
-      const float wgt = exp2f(pm[k] - M);
-      den = fmaf(wgt, pl[k], den);
-      num = fmaf(wgt, pa[static_cast<int64_t>(k) * D], num);
-    }
-    pr.out[row * D + d] = num / den;
-  }
-}
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of a row's partials: grid (Hq, B), D threads (thread d
+// owns output dim d of query head h of sequence b).
+//   out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k
+// The length, the slot count and the first kMergeBatch slots are loaded
+// together (slots are in bounds of the row's maxP workspace slots; values of
+// slots beyond the row's count are never used), so a row with at most
+// kMergeBatch partials costs one memory round trip.  Later slots are folded
+// in batches with the running maximum rescaled.
+//   kSplit: slot counts come from the balanced-split kernel's counters, and
+//   the rows of empty (zeros) and out-of-bounds (NaN) sequences, which own
+//   no work there, are written here; otherwise a sequence of length L has
+//   ceil(L / P) partitions.
+// ---------------------------------------------------------------------------
+constexpr int kMergeBatch = 8;
 
-// ---------------------------------------------------------------------------
-// Log-sum-exp merge of partition partials: grid (Hq, B), 256 threads.
-//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(Params pr) {
-  constexpr int NT = 256, SPLIT = NT / D;
-  __shared__ float red[NT / 64];
-  __shared__ float part[SPLIT][D];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int L = pr.lens[b];
-  if (!len_valid(L, pr) || L == 0) return;
-  const int np = (L + pr.P - 1) / pr.P;
-  if (np <= 1) return;
+template <int D, bool kSplit>
+__global__ __launch_bounds__(D) void merge_kernel(Params pr) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int64_t row = static_cast<int64_t>(b) * pr.Hq + h;
   const float* pm = pr.part_m + row * pr.maxP;
   const float* pl = pr.part_l + row * pr.maxP;
-  const float* pa = pr.part_acc + row * pr.maxP * D;
-
-  float M = -INFINITY;
-  for (int i = tid; i < np; i += NT) M = fmaxf(M, pm[i]);
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = red[0];
+  const float* pa = pr.part_acc + row * pr.maxP * D + d;
+  const int L = pr.lens[b];
+  // maxP == 1: no workspace (every row is written final or trivial)
+  const bool have_ws = pr.maxP > 1;
+  const int ns_split =
+      (kSplit && have_ws) ? pr.counters[static_cast<int64_t>(b) * pr.Hkv + h / pr.G] : 0;
+  const int kfirst = have_ws ? min(kMergeBatch, pr.maxP) : 0;
+  float m[kMergeBatch], l[kMergeBatch], a[kMergeBatch];
 #pragma unroll
-  for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
-
-  float den = 0.f;
-  for (int i = tid; i < np; i += NT) den = fmaf(exp2f(pm[i] - M), pl[i], den);
-  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
-  if ((tid & 63) == 0) red[tid >> 6] = den;
-  __syncthreads();
-  den = 0.f;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) den += red[w];
-
-  const int d = tid % D, s = tid / D;
-  float a = 0.f;
-  for (int i = s; i < np; i += SPLIT) a = fmaf(exp2f(pm[i] - M), pa[static_cast<int64_t>(i) * D + d], a);
-  part[s][d] = a;
-  __syncthreads();
-  if (s == 0) {
-    float tot = 0.f;
-#pragma unroll
-    for (int k = 0; k < SPLIT; ++k) tot += part[k][d];
-    pr.out[row * D + d] = tot / den;
+  for (int k = 0; k < kMergeBatch; ++k) {
+    if (k < kfirst) {
+      m[k] = pm[k];
+      l[k] = pl[k];
+      a[k] = pa[static_cast<int64_t>(k) * D];
+    }
   }
+  if (!len_valid(L, pr) || L == 0) {
+    if (kSplit) pr.out[row * D + d] = (L == 0) ? 0.f : __builtin_nanf("");
+    return;
+  }
+  const int ns = kSplit ? ns_split : (L + pr.P - 1) / pr.P;
+  if (ns <= 1 || !have_ws) return;                            // written final
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k)
+    if (k < ns) M = fmaxf(M, m[k]);
+  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    if (k < ns) {
+      const float wgt = exp2f(m[k] - M);
+      den = fmaf(wgt, l[k], den);
+      num = fmaf(wgt, a[k], num);
+    }
+  }
+  for (int k0 = kMergeBatch; k0 < ns; k0 += kMergeBatch) {
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (k0 + k < ns) {
+        m[k] = pm[k0 + k];
+        l[k] = pl[k0 + k];
+        a[k] = pa[static_cast<int64_t>(k0 + k) * D];
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (k0 + k < ns) Mb = fmaxf(Mb, m[k]);
+    const float r = exp2f(M - Mb);
+    num *= r;
+    den *= r;
+    M = Mb;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (k0 + k < ns) {
+        const float wgt = exp2f(m[k] - M);
+        den = fmaf(wgt, l[k], den);
+        num = fmaf(wgt, a[k], num);
+      }
+    }
+  }
+  pr.out[row * D + d] = num / den;
 }
 
 // Kernel selection: PA_DECODE_KERNEL=generic forces the plain-FMA kernel for
@@ -1349,10 +1400,10 @@ Path path_from_env() {
   return (v && std::strcmp(v, "generic") == 0) ? Path::kGeneric : Path::kAuto;
 }
 
-constexpr int kDefaultPartition = 256;  // fixed-partition size when none is given
+constexpr int kDefaultPartition = 256;  // fixed-partition size of the plain-FMA kernel
 constexpr int kPairsInFlight = 2;
 constexpr int kFixedWaves4 = 3;         // waves per SIMD the 4x4x4 fixed kernel is built for
-constexpr int kSplitWavesPerCU = 8;     // balanced split: grid = CUs * this
+constexpr int kSplitWavesPerCU = 4;     // balanced split: grid = CUs * this (one wave per SIMD)
 
 constexpr int kEvenSplit = -1;          // partition_size value selecting the even split
 
@@ -1400,7 +1451,8 @@ struct LaunchPlan {
 LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_env) {
   LaunchPlan lp{};
   lp.generic = dt == PA_F32 || generic_env;
-  lp.split = partition_size == kEvenSplit && !lp.generic;
+  // default (0) on the matrix-core path: the even split
+  lp.split = (partition_size == kEvenSplit || partition_size == 0) && !lp.generic;
   if (lp.split) {
     lp.W = split_waves();
     // a range of nblk blocks is cut into at most ceil(nblk / kMinChunkBlocks) + 1
@@ -1416,36 +1468,59 @@ LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_
   return lp;
 }
 
+// Events armed by pa_time_next_attention for the next attention kernel of
+// this host thread; consumed (and cleared) by the next decode call.
+struct TimingEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+thread_local TimingEvents t_armed;
+thread_local TimingEvents t_call;   // the events of the call in progress
+
+// Launches an attention kernel; with events armed for the call, they are
+// recorded by the kernel's own dispatch (start and end of its execution).
+template <typename K>
+void launch_attention(K kernel, dim3 grid, dim3 block, hipStream_t s, const Params& pr) {
+  if (t_call.start != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t_call.start, t_call.stop, 0, pr);
+    t_call = TimingEvents{};
+  } else {
+    kernel<<<grid, block, 0, s>>>(pr);
+  }
+}
+
 template <typename T, int D>
 void launch_partitions(const Params& pr, bool generic, bool fused, hipStream_t s) {
   // matrix-core kernels: x = KV head + Hkv * partition (the heads of one
   // partition are dispatched together), z = sequence
   dim3 grid_m(pr.Hkv * pr.maxP, 1, pr.B);
   if (generic)
-    decode_generic_kernel<T, D><<<dim3(pr.maxP, pr.Hkv, pr.B), 256, 0, s>>>(pr);
+    launch_attention(decode_generic_kernel<T, D>, dim3(pr.maxP, pr.Hkv, pr.B), 256, s, pr);
   else if (pr.G <= 4 && fused)
-    decode_fixed_kernel<Engine4<T, D>, true, kFixedWaves4><<<grid_m, 64, 0, s>>>(pr);
+    launch_attention(decode_fixed_kernel<Engine4<T, D>, true, kFixedWaves4>, grid_m, 64, s, pr);
   else if (pr.G <= 4)
-    decode_fixed_kernel<Engine4<T, D>, false, kFixedWaves4><<<grid_m, 64, 0, s>>>(pr);
+    launch_attention(decode_fixed_kernel<Engine4<T, D>, false, kFixedWaves4>, grid_m, 64, s, pr);
   else
-    decode_fixed_kernel<Engine16<T, D, kPairsInFlight, false>, false, 1><<<grid_m, 64, 0, s>>>(pr);
+    launch_attention(decode_fixed_kernel<Engine16<T, D, kPairsInFlight, false>, false, 1>,
+                     grid_m, 64, s, pr);
 }
 
 template <>
 void launch_partitions<F32, 64>(const Params& pr, bool, bool, hipStream_t s) {
-  decode_generic_kernel<F32, 64><<<dim3(pr.maxP, pr.Hkv, pr.B), 256, 0, s>>>(pr);
+  launch_attention(decode_generic_kernel<F32, 64>, dim3(pr.maxP, pr.Hkv, pr.B), 256, s, pr);
 }
 template <>
 void launch_partitions<F32, 128>(const Params& pr, bool, bool, hipStream_t s) {
-  decode_generic_kernel<F32, 128><<<dim3(pr.maxP, pr.Hkv, pr.B), 256, 0, s>>>(pr);
+  launch_attention(decode_generic_kernel<F32, 128>, dim3(pr.maxP, pr.Hkv, pr.B), 256, s, pr);
 }
 
 template <typename T, int D>
 void launch_split(const Params& pr, int W, hipStream_t s) {
   if (pr.G <= 4)
-    decode_split_kernel<Engine4<T, D>, 2><<<W, 64, 0, s>>>(pr);
+    launch_attention(decode_split_kernel<Engine4<T, D>, 2>, W, 64, s, pr);
   else
-    decode_split_kernel<Engine16<T, D, kPairsInFlight, false>, 1><<<W, 64, 0, s>>>(pr);
+    launch_attention(decode_split_kernel<Engine16<T, D, kPairsInFlight, false>, 1>, W, 64, s,
+                     pr);
 }
 
 enum class Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
@@ -1462,7 +1537,7 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
       else
         launch_split<BF16, D>(pr, lp.W, s);
     }
-    if (second) merge_split_kernel<D><<<dim3(pr.Hkv, pr.B), 256, 0, s>>>(pr);
+    if (second) merge_kernel<D, true><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
     return;
   }
   if (first) {
@@ -1472,7 +1547,7 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
       case PA_BF16: launch_partitions<BF16, D>(pr, lp.generic, pr.k_new != nullptr, s); break;
     }
   }
-  if (second && pr.maxP > 1) merge_kernel<D><<<dim3(pr.Hq, pr.B), 256, 0, s>>>(pr);
+  if (second && pr.maxP > 1) merge_kernel<D, false><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
 }
 
 // Whether the partition kernel of this plan appends the step's new tokens
@@ -1494,6 +1569,8 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, 
                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                      float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
                      size_t workspace_bytes_given, void* stream) {
+  t_call = t_armed;   // armed events apply to this call only
+  t_armed = TimingEvents{};
   if (block_size != kBlockSize)
     return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, block_size);
   if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
@@ -1590,6 +1667,13 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, 
 
 using namespace pa;
 
+extern "C" pa_status pa_time_next_attention(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "pa_time_next_attention: give both events or neither");
+  t_armed = TimingEvents{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  return ok();
+}
+
 extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                             int32_t num_kv_heads, int32_t head_dim,
                                             int32_t max_context_len, int32_t partition_size,
@@ -1636,19 +1720,24 @@ extern "C" pa_status pa_decode_merge(PA_DECODE_ARGS) {
   return run_decode("pa_decode_merge", Phase::kMerge, nullptr, PA_DECODE_FWD);
 }
 
-extern "C" pa_status pa_decode_step(float* out, const void* q, void* k_pool, void* v_pool,
-                                    const void* k_new, const void* v_new,
-                                    const int64_t* slot_mapping, const int32_t* block_tables,
-                                    const int32_t* context_lens, int32_t num_seqs,
-                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                    int32_t block_size, int32_t num_blocks,
-                                    int32_t max_blocks_per_seq, int32_t max_context_len,
-                                    float scale, int32_t partition_size, pa_dtype dtype,
-                                    void* workspace, size_t workspace_bytes_given,
-                                    void* stream) {
+#define PA_STEP_ARGS                                                                        \
+  float *out, const void *q, void *k_pool, void *v_pool, const void *k_new, const void *v_new, \
+      const int64_t *slot_mapping, const int32_t *block_tables, const int32_t *context_lens,  \
+      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,          \
+      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,                     \
+      int32_t max_context_len, float scale, int32_t partition_size, pa_dtype dtype,           \
+      void *workspace, size_t workspace_bytes_given, void *stream
+#define PA_STEP_FWD                                                                         \
+  out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,    \
+      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,           \
+      partition_size, dtype, workspace, workspace_bytes_given, stream
+
+extern "C" pa_status pa_decode_step(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step", Phase::kBoth, &nt, out, q, k_pool, v_pool, block_tables,
-                    context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                    num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
-                    dtype, workspace, workspace_bytes_given, stream);
+  return run_decode("pa_decode_step", Phase::kBoth, &nt, PA_STEP_FWD);
+}
+
+extern "C" pa_status pa_decode_step_partial(PA_STEP_ARGS) {
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  return run_decode("pa_decode_step_partial", Phase::kPartitions, &nt, PA_STEP_FWD);
 }

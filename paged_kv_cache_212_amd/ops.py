@@ -146,9 +146,13 @@ def decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, 
 
 def decode_step(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables,
                 context_lens, max_context_len, scale=None, partition_size=0, workspace=None,
-                stream=None):
+                stream=None, phase="both"):
     """Append each sequence's new token (row b of k_new/v_new, slot slot_mapping[b]) and
-    decode, in one call (pa_decode_step)."""
+    decode, in one call (pa_decode_step).
+
+    phase: "both" (pa_decode_step) or "partial" (pa_decode_step_partial; finish
+    with decode(..., phase="merge") on the same workspace)."""
+    fn = {"both": "pa_decode_step", "partial": "pa_decode_step_partial"}[phase]
     N, H, D = _pool_dims(k_pool, v_pool)
     B, Hq = q.shape[0], q.shape[1]
     if q.shape != (B, Hq, D) or q.dtype != k_pool.dtype:
@@ -169,16 +173,16 @@ def decode_step(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables
     if workspace is None:
         workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size, q.dtype,
                                      q.device)
-    check(lib().pa_decode_step(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
-                               _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
-                               _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
-                               _dev(block_tables, "block_tables"),
-                               _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
-                               block_tables.shape[1], int(max_context_len), scale,
-                               int(partition_size), pa_dtype(q.dtype),
-                               _dev(workspace, "workspace"),
-                               workspace.numel() * workspace.element_size(), _stream(stream)),
-          "pa_decode_step")
+    check(getattr(lib(), fn)(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                             _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+                             _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
+                             _dev(block_tables, "block_tables"),
+                             _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
+                             block_tables.shape[1], int(max_context_len), scale,
+                             int(partition_size), pa_dtype(q.dtype),
+                             _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(stream)),
+          fn)
     return out
 
 

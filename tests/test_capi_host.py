@@ -63,6 +63,9 @@ def test_device_calls_reject_bad_scalars_without_launching():
     fake = C.c_void_p(1 << 20)
     assert h.pa_decode(fake, fake, fake, fake, fake, fake, 2, 8, 2, 128, 16, 10, 400, 6000, 0.1,
                        512, PA_BF16, nul, 0, nul) == PA_ERR_WORKSPACE
+    assert h.pa_decode_step_partial(nul, nul, nul, nul, nul, nul, nul, nul, nul, 1, 8, 2, 128,
+                                    16, 10, 4, 64, 0.1, 0, PA_BF16, nul, 0,
+                                    nul) == PA_ERR_INVALID_ARG
     assert h.pa_cache_append(nul, nul, nul, nul, nul, 4, 10, 8, 128, 16, PA_BF16,
                              nul) == PA_ERR_INVALID_ARG
     assert h.pa_cache_append(nul, nul, nul, nul, nul, 0, 10, 8, 128, 16, PA_BF16, nul) == 0
@@ -72,9 +75,17 @@ def test_device_calls_reject_bad_scalars_without_launching():
                           nul) == PA_ERR_INVALID_ARG
 
 
+def test_timing_hook_arguments():
+    h = pk.lib()
+    assert h.pa_time_next_attention(None, C.c_void_p(16)) == PA_ERR_INVALID_ARG
+    assert h.pa_time_next_attention(C.c_void_p(16), None) == PA_ERR_INVALID_ARG
+    assert h.pa_time_next_attention(None, None) == 0      # disarm
+
+
 def test_workspace_and_partition_queries():
     h = pk.lib()
-    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_BF16) == 256   # default
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_BF16) == 0     # default: split
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_F32) == 256    # fp32 default
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, -1, PA_BF16) == 0    # even split
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, -1, PA_F32) == 256   # fixed on fp32
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, -2, PA_BF16) == -1

@@ -47,7 +47,8 @@ def _compare_full(case, ref, got, tol):
 
 
 @pytest.mark.parametrize("kernel", KERNELS, indirect=True)
-@pytest.mark.parametrize("fused", [True, False], ids=["decode_step", "append+decode"])
+@pytest.mark.parametrize("fused", [True, "phased", False],
+                         ids=["decode_step", "step_partial+merge", "append+decode"])
 @pytest.mark.parametrize("name", CONFIG_NAMES)
 def test_small_configs_match_oracle(name, fused, kernel):
     case = small_case(name)
@@ -57,13 +58,16 @@ def test_small_configs_match_oracle(name, fused, kernel):
     _compare_full(case, ref, got, TOL[case.dtype])
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["decode_step", "append+decode"])
+@pytest.mark.parametrize("fused", [True, "phased", False],
+                         ids=["decode_step", "step_partial+merge", "append+decode"])
+@pytest.mark.parametrize("ps", [-1, 64, 256])
 @pytest.mark.parametrize("name", [n for n in CONFIG_NAMES if n != "tiny_fp32"])
-def test_small_configs_even_split(name, fused):
+def test_small_configs_explicit_partitions(name, fused, ps):
+    """The even split (-1) and fixed partitions, whatever the case's default."""
     case = small_case(name)
-    say(f"[parity small, even split] {name} fused={fused}")
+    say(f"[parity small, partition_size {ps}] {name} fused={fused}")
     ref = _oracle_poisoned(case)
-    got = run_gpu_step(case, partition_size=-1, fused=fused)
+    got = run_gpu_step(case, partition_size=ps, fused=fused)
     _compare_full(case, ref, got, TOL[case.dtype])
 
 
@@ -291,3 +295,73 @@ def test_gather_matches_oracle_table_walk():
         K, V = gather_ref(ref["k_pool"], ref["v_pool"], ref["tables"][i], L, 16)
         assert np.array_equal(kg[i, :, :L], K) and np.array_equal(vg[i, :, :L], V)
         assert not kg[i, :, L:].any() and not vg[i, :, L:].any()
+
+
+@pytest.mark.parametrize("ps", [0, -1])
+def test_timing_events_bracket_the_attention_kernel(ps):
+    """Events armed with pa_time_next_attention are recorded by the attention
+    kernel's dispatch: a positive duration no longer than the whole call's, and
+    the call's result is unchanged."""
+    pk = require_gpu()
+    case = custom_case(71, "bf16", [700, 1500, 90, 2048], 32, 8, 128, partition_size=ps)
+    say(f"[timing hook] P={ps}")
+    got = run_gpu_step(case, fused=False)
+    cache, plan = got["cache"], got["plan"]
+    out = torch.empty_like(torch.from_numpy(got["out"])).cuda()
+    e0, e1, w0, w1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (e0, e1):
+        e.record()
+    torch.cuda.synchronize()
+    w0.record()
+    assert pk.lib().pa_time_next_attention(e0.cuda_event, e1.cuda_event) == 0
+    pk.ops.decode(out, got["q"], cache.k_pool, cache.v_pool, plan.d_tables, plan.d_lens,
+                  plan.max_context_len, partition_size=ps)
+    w1.record()
+    torch.cuda.synchronize()
+    k_ms, call_ms = e0.elapsed_time(e1), w0.elapsed_time(w1)
+    assert 0 < k_ms <= call_ms, (k_ms, call_ms)
+    assert np.array_equal(out.cpu().numpy(), got["out"])
+
+
+@pytest.mark.parametrize("hq,hkv,ps", [(32, 8, 0), (32, 8, 256), (16, 2, -1), (8, 8, 64)])
+def test_step_slot_cases_match_append_then_decode(hq, hkv, ps):
+    """pa_decode_step == pa_cache_append then pa_decode for every slot value:
+    the table's slot, -1 (no write; the position is attended as stored) and a
+    slot in a block no table references (written; not attended)."""
+    pk = require_gpu()
+    case = custom_case(81, "bf16", [40, 300, 700, 20, 33, 129], hq, hkv, 128,
+                       partition_size=ps)
+    say(f"[step slots] Hq={hq} Hkv={hkv} P={ps}")
+    dev = torch.device("cuda")
+    k_tok, v_tok = case.k_tok.to(dev), case.v_tok.to(dev)
+    caches = []
+    for _ in range(2):
+        c = pk.PagedKVCache(case.num_blocks, hkv, 128, torch.bfloat16, dev,
+                            free_order=case.free_order, fill=float("nan"))
+        c.replay(case.script, case.rows, k_tok, v_tok)
+        caches.append((c, c.plan_step(case.batch)))
+    (c1, p1), (c2, p2) = caches
+    assert np.array_equal(p1.tables, p2.tables) and np.array_equal(p1.slots, p2.slots)
+    unused = sorted(set(range(case.num_blocks)) - set(p1.tables[p1.tables >= 0].tolist()))
+    slots = p1.d_slots.clone()
+    slots[1] = -1
+    slots[3] = unused[0] * 16 + 5
+    nr = torch.as_tensor(case.new_rows(), device=dev)
+    k_new, v_new = k_tok.index_select(0, nr), v_tok.index_select(0, nr)
+    q = case.q.to(dev)
+    o1 = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    o2 = torch.empty_like(o1)
+    pk.ops.decode_step(o1, q, c1.k_pool, c1.v_pool, k_new, v_new, slots, p1.d_tables,
+                       p1.d_lens, p1.max_context_len, partition_size=ps)
+    pk.ops.cache_append(c2.k_pool, c2.v_pool, k_new, v_new, slots)
+    pk.ops.decode(o2, q, c2.k_pool, c2.v_pool, p2.d_tables, p2.d_lens, p2.max_context_len,
+                  partition_size=ps)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(c1.k_pool, "bf16"), bits_of(c2.k_pool, "bf16"))
+    assert np.array_equal(bits_of(c1.v_pool, "bf16"), bits_of(c2.v_pool, "bf16"))
+    a, b = o1.cpu().numpy(), o2.cpu().numpy()
+    # sequences 1 and 3: their last position is never written (NaN-poisoned pool)
+    for i in (1, 3):
+        assert np.isnan(a[i]).all() and np.isnan(b[i]).all()
+    keep = [i for i in range(case.num_seqs) if i not in (1, 3)]
+    assert max_err(a[keep], b[keep]) <= 1e-6
