@@ -283,7 +283,12 @@ def main():
     if evs:
         part_ms = dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         tables_bytes = int(sum(-(-int(x) // 16) for x in case.lens)) * 4
+        # K/V of every attended token, q, the table entries walked, the lengths and
+        # the fp32 output; with the append fused in, also the new tokens read
+        # (k_new, v_new) and written (their pool slots) and the slot indices
         alg = kv_bytes + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
+        if args.mode == "phased":
+            alg += 4 * k_new.numel() * k_new.element_size() + B * 8
         achieved = alg / (part_ms * 1e-3) / 1e9
         res["attention_kernel_us"] = round(dec_ms * 1e3, 3)
         if args.mode == "separate":

@@ -363,5 +363,7 @@ def test_step_slot_cases_match_append_then_decode(hq, hkv, ps):
     # sequences 1 and 3: their last position is never written (NaN-poisoned pool)
     for i in (1, 3):
         assert np.isnan(a[i]).all() and np.isnan(b[i]).all()
+    # same inputs, fp32 sums in a different order (the fused path may attend
+    # the new token's quad first): agreement far inside the 1e-2 oracle bar
     keep = [i for i in range(case.num_seqs) if i not in (1, 3)]
-    assert max_err(a[keep], b[keep]) <= 1e-6
+    assert max_err(a[keep], b[keep]) <= 1e-4
