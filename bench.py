@@ -3,9 +3,9 @@
 
 A step is one pass of the whole device path over one batch: copy-on-write block
 copies (when the step's reservation produced any), then pa_decode_step_partial,
-whose attention kernel also appends the batch's new tokens into their slots,
-then pa_decode_merge, the log-sum-exp merge of the partition partials (the two
-calls together are pa_decode_step).  The attention kernel is timed with HIP
+the attention kernel, which attends the batch's new tokens from k_new/v_new,
+then pa_decode_step_merge, whose kernel combines the partials and writes the
+new tokens into their slots (the two calls together are pa_decode_step).  The attention kernel is timed with HIP
 events on the launch stream.
 The host reservation (slots, copy pairs, block tables) is done by the C++
 block manager before the timed region, and the same step is replayed every
@@ -211,7 +211,8 @@ def main():
             (kp.data_ptr(), vp.data_ptr(), plan.d_cows.data_ptr(), ncow, N, Hkv, D, 16, dt,
              stream),
             dec, app, dec_sep))
-    f_copy, f_step, f_step_part = L.pa_copy_blocks, L.pa_decode_step, L.pa_decode_step_partial
+    f_copy, f_step = L.pa_copy_blocks, L.pa_decode_step
+    f_step_part, f_step_merge = L.pa_decode_step_partial, L.pa_decode_step_merge
     f_app, f_part, f_merge = L.pa_cache_append, L.pa_decode_partial, L.pa_decode_merge
     f_time = L.pa_time_next_attention
 
@@ -233,9 +234,10 @@ def main():
             check(f_time(ev[0].cuda_event, ev[1].cuda_event), "pa_time_next_attention")
         if args.mode == "separate":
             check(f_part(*c_dec_sep), "pa_decode_partial")     # the attention kernel
+            check(f_merge(*c_dec_sep), "pa_decode_merge")
         else:
-            check(f_step_part(*c_dec), "pa_decode_step_partial")   # append + attention
-        check(f_merge(*c_dec_sep), "pa_decode_merge")
+            check(f_step_part(*c_dec), "pa_decode_step_partial")   # attention (+ new tokens)
+            check(f_step_merge(*c_dec), "pa_decode_step_merge")    # merge + new-token writes
 
     for i in range(args.warmup):
         step(i)
@@ -284,17 +286,17 @@ def main():
         part_ms = dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         tables_bytes = int(sum(-(-int(x) // 16) for x in case.lens)) * 4
         # K/V of every attended token, q, the table entries walked, the lengths and
-        # the fp32 output; with the append fused in, also the new tokens read
-        # (k_new, v_new) and written (their pool slots) and the slot indices
+        # the fp32 output; in the phased step the kernel also reads the new
+        # tokens (k_new, v_new) and the slot indices
         alg = kv_bytes + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
         if args.mode == "phased":
-            alg += 4 * k_new.numel() * k_new.element_size() + B * 8
+            alg += 2 * k_new.numel() * k_new.element_size() + B * 8
         achieved = alg / (part_ms * 1e-3) / 1e9
         res["attention_kernel_us"] = round(dec_ms * 1e3, 3)
         if args.mode == "separate":
             kname = "attention partition kernel (pa_decode_partial)"
         elif args.mode == "phased":
-            kname = "attention partition kernel with the append fused in (pa_decode_step_partial)"
+            kname = "attention kernel of pa_decode_step_partial (new tokens fused in)"
         else:
             kname = "pa_decode_step as a whole (attention kernel and merge)"
         res["roofline"] = {"kernel": kname,

@@ -256,10 +256,13 @@ pa_status pa_decode_merge(float* out, const void* q, const void* k_pool, const v
  * rows) or is 0 gets no pool write.  Otherwise the two kernels run back to
  * back.  Copy-on-write copies of the step must be issued (pa_copy_blocks)
  * before this call on the same stream.
- *   pa_decode_step_partial: the first phase of pa_decode_step (append and
- *     partition kernel, as pa_decode_partial); follow it with pa_decode_merge
- *     with the same arguments and workspace.  pa_decode_step(...) ==
- *     pa_decode_step_partial(...) then pa_decode_merge(...). */
+ *   pa_decode_step_partial / pa_decode_step_merge: the two phases of
+ *     pa_decode_step (same arguments and workspace, on the same stream):
+ *     pa_decode_step(...) == pa_decode_step_partial(...) then
+ *     pa_decode_step_merge(...).  When the merge phase launches a kernel
+ *     (even split, or sequences longer than one fixed partition) that kernel
+ *     writes the new tokens to their slots and the attention kernel only
+ *     attends them; otherwise the attention kernel writes them. */
 pa_status pa_decode_step(float* out, const void* q, void* k_pool, void* v_pool,
                          const void* k_new, const void* v_new, const int64_t* slot_mapping,
                          const int32_t* block_tables, const int32_t* context_lens,
@@ -277,6 +280,15 @@ pa_status pa_decode_step_partial(float* out, const void* q, void* k_pool, void* 
                                  int32_t max_blocks_per_seq, int32_t max_context_len,
                                  float scale, int32_t partition_size, pa_dtype dtype,
                                  void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_decode_step_merge(float* out, const void* q, void* k_pool, void* v_pool,
+                               const void* k_new, const void* v_new,
+                               const int64_t* slot_mapping, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                               int32_t partition_size, pa_dtype dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Measurement hook: the next attention kernel launched by a decode call
  * (pa_decode, pa_decode_partial, pa_decode_step or pa_decode_step_partial)

@@ -106,7 +106,7 @@ class PagedKVCache:
         """Copy-on-write, append the new tokens, then decode attention (all on device).
 
         fused: True -> one pa_decode_step call; "phased" -> pa_decode_step_partial
-        then pa_decode_merge; False -> pa_cache_append then pa_decode."""
+        then pa_decode_step_merge; False -> pa_cache_append then pa_decode."""
         if plan.cows.shape[0]:
             ops.copy_blocks(self.k_pool, self.v_pool, plan.d_cows, stream)
         if out is None:
@@ -120,9 +120,9 @@ class PagedKVCache:
             ops.decode_step(out, q, self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
                             plan.d_tables, plan.d_lens, plan.max_context_len, scale,
                             partition_size, workspace, stream, phase="partial")
-            ops.decode(out, q, self.k_pool, self.v_pool, plan.d_tables, plan.d_lens,
-                       plan.max_context_len, scale, partition_size, workspace, stream,
-                       phase="merge")
+            ops.decode_step(out, q, self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
+                            plan.d_tables, plan.d_lens, plan.max_context_len, scale,
+                            partition_size, workspace, stream, phase="merge")
         elif fused:
             ops.decode_step(out, q, self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
                             plan.d_tables, plan.d_lens, plan.max_context_len, scale,

@@ -48,6 +48,8 @@ struct Params {
   const int64_t* slots;  // [B] slot of each new token (fused append)
   void* kpool_w;       // writable pools (fused append)
   void* vpool_w;
+  int write_new_in_merge;  // fused append: the merge kernel writes the new tokens
+                           // to their slots (the attention kernel only uses them)
   const void* q;       // [B][Hq][D]
   const void* kpool;
   const void* vpool;
@@ -452,8 +454,8 @@ __device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int
         vv.w = dw == 3 ? ((vv.w & keep) | val) : vv.w;
       }
     }
-    // write the token into its pool slot
-    if (in_pool) {
+    // write the token into its pool slot (or leave it to the merge kernel)
+    if (in_pool && !pr.write_new_in_merge) {
       const int64_t blk = slot / kBlockSize;
       const int ts = static_cast<int>(slot % kBlockSize);
       uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
@@ -929,6 +931,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
     if (slot == static_cast<int64_t>(phys) * kBlockSize + (qt & 15)) {
       substitute_new();
+      if (pr.write_new_in_merge) return;
       const int64_t tile = (static_cast<int64_t>(phys) * pr.Hkv + g) * kTileBytes;
       char* kt = static_cast<char*>(pr.kpool_w) + tile + (lane & 15) * 16;
       if ((lane >> 3) == (qt >> 3)) {
@@ -945,7 +948,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
             for (int t = 0; t < NT; ++t)
               *reinterpret_cast<uint4*>(vt + (H * D + 64 * t) * 16) = vr[KB][H][t];
           }
-    } else {
+    } else if (!pr.write_new_in_merge) {
       const int64_t blk = slot / kBlockSize;
       const int ts = static_cast<int>(slot % kBlockSize);
       uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
@@ -1343,9 +1346,32 @@ __global__ __launch_bounds__(D) void merge_kernel(Params pr) {
       a[k] = pa[static_cast<int64_t>(k) * D];
     }
   }
+  // Fused append of pa_decode_step: the first query head's workgroup of each
+  // (sequence, KV head) writes the new token (16-bit K/V) into its slot; its
+  // loads go out with the partials'.
+  const bool appends = pr.write_new_in_merge && h % pr.G == 0;
+  const int g = h / pr.G;
+  int64_t slot = -1;
+  uint4 kchunk = make_uint4(0, 0, 0, 0);
+  uint16_t vval = 0;
+  if (appends) {
+    slot = pr.slots[b];
+    const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
+    if (d < D / 8)
+      kchunk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pr.k_new) + nrow + d * 8);
+    vval = static_cast<const uint16_t*>(pr.v_new)[nrow + d];
+  }
   if (!len_valid(L, pr) || L == 0) {
     if (kSplit) pr.out[row * D + d] = (L == 0) ? 0.f : __builtin_nanf("");
     return;
+  }
+  if (appends && slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
+    const int64_t blk = slot / kBlockSize;
+    const int ts = static_cast<int>(slot % kBlockSize);
+    uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
+    uint16_t* vt = static_cast<uint16_t*>(pr.vpool_w) + tile_base(blk, g, pr.Hkv, D);
+    if (d < D / 8) *reinterpret_cast<uint4*>(kt + (d * kBlockSize + ts) * 8) = kchunk;
+    vt[((ts >> 3) * D + d) * 8 + (ts & 7)] = vval;
   }
   const int ns = kSplit ? ns_split : (L + pr.P - 1) / pr.P;
   if (ns <= 1 || !have_ws) return;                            // written final
@@ -1641,13 +1667,16 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (nt) {
     if (fuses_append(lp, pr.G)) {
-      // append fused into the partition kernel
+      // append fused: the attention kernel uses the new tokens; the merge
+      // kernel writes them to the pool when a merge kernel runs, else the
+      // attention kernel does
       pr.k_new = nt->k_new;
       pr.v_new = nt->v_new;
       pr.slots = nt->slots;
       pr.kpool_w = const_cast<void*>(k_pool);
       pr.vpool_w = const_cast<void*>(v_pool);
-    } else {
+      pr.write_new_in_merge = lp.split || lp.maxP > 1;
+    } else if (static_cast<int>(ph) & static_cast<int>(Phase::kPartitions)) {
       const pa_status st = pa_cache_append(const_cast<void*>(k_pool), const_cast<void*>(v_pool),
                                            nt->k_new, nt->v_new, nt->slots, num_seqs,
                                            num_blocks, num_kv_heads, head_dim, block_size,
@@ -1740,4 +1769,9 @@ extern "C" pa_status pa_decode_step(PA_STEP_ARGS) {
 extern "C" pa_status pa_decode_step_partial(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
   return run_decode("pa_decode_step_partial", Phase::kPartitions, &nt, PA_STEP_FWD);
+}
+
+extern "C" pa_status pa_decode_step_merge(PA_STEP_ARGS) {
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  return run_decode("pa_decode_step_merge", Phase::kMerge, &nt, PA_STEP_FWD);
 }

@@ -150,9 +150,10 @@ def decode_step(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables
     """Append each sequence's new token (row b of k_new/v_new, slot slot_mapping[b]) and
     decode, in one call (pa_decode_step).
 
-    phase: "both" (pa_decode_step) or "partial" (pa_decode_step_partial; finish
-    with decode(..., phase="merge") on the same workspace)."""
-    fn = {"both": "pa_decode_step", "partial": "pa_decode_step_partial"}[phase]
+    phase: "both" (pa_decode_step), or "partial" then "merge"
+    (pa_decode_step_partial, pa_decode_step_merge; same arguments and workspace)."""
+    fn = {"both": "pa_decode_step", "partial": "pa_decode_step_partial",
+          "merge": "pa_decode_step_merge"}[phase]
     N, H, D = _pool_dims(k_pool, v_pool)
     B, Hq = q.shape[0], q.shape[1]
     if q.shape != (B, Hq, D) or q.dtype != k_pool.dtype:

@@ -66,6 +66,9 @@ def test_device_calls_reject_bad_scalars_without_launching():
     assert h.pa_decode_step_partial(nul, nul, nul, nul, nul, nul, nul, nul, nul, 1, 8, 2, 128,
                                     16, 10, 4, 64, 0.1, 0, PA_BF16, nul, 0,
                                     nul) == PA_ERR_INVALID_ARG
+    assert h.pa_decode_step_merge(nul, nul, nul, nul, nul, nul, nul, nul, nul, 1, 8, 2, 128,
+                                  16, 10, 4, 64, 0.1, 0, PA_BF16, nul, 0,
+                                  nul) == PA_ERR_INVALID_ARG
     assert h.pa_cache_append(nul, nul, nul, nul, nul, 4, 10, 8, 128, 16, PA_BF16,
                              nul) == PA_ERR_INVALID_ARG
     assert h.pa_cache_append(nul, nul, nul, nul, nul, 0, 10, 8, 128, 16, PA_BF16, nul) == 0
