@@ -89,6 +89,29 @@ def traffic_for(workload: str):
     return e.get("hbm_bytes_per_launch")
 
 
+def stream_read_context(torch, dev):
+    """Context figure: the chip's streaming-read bandwidth on the same GPU
+    (pa_stream_read over a 2 GiB buffer, 5 timed passes after 2 warm-up)."""
+    from paged_kv_cache_212_amd._lib import check, lib
+    n = 2 << 30
+    x = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        check(lib().pa_stream_read(x.data_ptr(), n, sink.data_ptr(), s), "pa_stream_read")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        check(lib().pa_stream_read(x.data_ptr(), n, sink.data_ptr(), s), "pa_stream_read")
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x
+    torch.cuda.empty_cache()
+    return {"gbs": round(gbs, 1), "how": "pa_stream_read over a 2 GiB buffer"}
+
+
 def cpu_baseline(case, budget_s: float):
     """The fp64 oracle on the same step: copy pairs, append, decode_ref.
 
@@ -216,9 +239,9 @@ def main():
     f_app, f_part, f_merge = L.pa_cache_append, L.pa_decode_partial, L.pa_decode_merge
     f_time = L.pa_time_next_attention
 
-    def step(i, ev=None):
+    def step(i, ev=None, with_copy=True):
         c_copy, c_dec, c_app, c_dec_sep = calls[i % len(calls)]
-        if ncow:
+        if ncow and with_copy:
             check(f_copy(*c_copy), "pa_copy_blocks")
         if args.mode == "step":
             if ev is not None:
@@ -265,8 +288,30 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr,
           flush=True)
 
+    decode_only_us = ms_step * 1e3
+    if ncow:
+        # the same loop without the copy-on-write copies: decode alone
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.steps):
+            step(i, None, with_copy=False)
+        end.record()
+        torch.cuda.synchronize()
+        decode_only_us = start.elapsed_time(end) / args.steps * 1e3
+
     kv_bytes = case.kv_bytes()
     value = kv_bytes / (ms_step * 1e-3) / 1e9
+    # unique K/V bytes: blocks shared by several sequences (copy-on-write
+    # prefixes) are counted once, at their largest filled length
+    fill = np.zeros(N, dtype=np.int64)
+    for b_i, L_i in enumerate(plan.lens.tolist()):
+        nb = -(-int(L_i) // 16)
+        if nb:
+            f = np.full(nb, 16, dtype=np.int64)
+            f[-1] = int(L_i) - 16 * (nb - 1)
+            np.maximum.at(fill, plan.tables[b_i, :nb], f)
+    kv_unique = int(fill.sum()) * Hkv * 2 * D * q.element_size()
+    stream_ctx = stream_read_context(torch, dev)
     res = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -278,12 +323,25 @@ def main():
                       "cow_copies": ncow, "layers_rotated": args.layers,
                       "parallelism": "single GPU"},
            "us_per_step": round(ms_step * 1e3, 3),
+           "decode_only_us_per_step": round(decode_only_us, 3),
            "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
            "kv_bytes_per_step": kv_bytes,
+           "kv_bytes_unique_per_step": kv_unique,
+           "value_unique_gbs": round(kv_unique / (ms_step * 1e-3) / 1e9, 2),
+           "stream_read_context": stream_ctx,
            "host_plan_us": round(host_plan_us, 1),
            "wall_ms_timed_region": round(wall_ms, 3)}
     if evs:
-        part_ms = dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        kern_us = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+        part_ms = dec_ms = float(kern_us.mean()) * 1e-3
+        res["attention_kernel_us_p10_p50_p90"] = [round(float(x), 3) for x in
+                                                  np.percentile(kern_us, [10, 50, 90])]
+        if args.mode != "step":
+            # start-to-start of consecutive attention kernels: one step each
+            per = np.array([evs[i][0].elapsed_time(evs[i + 1][0])
+                            for i in range(len(evs) - 1)]) * 1e3
+            res["step_us_p10_p50_p90"] = [round(float(x), 3) for x in
+                                          np.percentile(per, [10, 50, 90])]
         tables_bytes = int(sum(-(-int(x) // 16) for x in case.lens)) * 4
         # K/V of every attended token, q, the table entries walked, the lengths and
         # the fp32 output; in the phased step the kernel also reads the new
@@ -306,6 +364,7 @@ def main():
                            "traffic": traffic_for(case.name),
                            "launch_us": round(part_ms * 1e3, 3),
                            "algorithmic_bytes": alg}
+        res["attention_vs_stream_read"] = round(achieved / stream_ctx["gbs"], 4)
     if cpu_case is not None:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cpu_case, args.cpu_seconds)

@@ -300,6 +300,15 @@ pa_status pa_decode_step_merge(float* out, const void* q, void* k_pool, void* v_
  * kernel.  Both NULL disarms; one NULL is PA_ERR_INVALID_ARG. */
 pa_status pa_time_next_attention(void* start_event, void* stop_event);
 
+/* Measurement utility: streams `bytes` bytes of device buffer `buf` (16-byte
+ * aligned, a multiple of 16) through the vector memory path with 16-byte
+ * non-temporal loads over a grid of 8 x 256-thread workgroups per compute
+ * unit, and discards them (device int `sink` is written only for a buffer
+ * whose 16-byte words XOR to one specific pattern).  Its time gives the chip's
+ * streaming-read bandwidth, the reference the decode kernels are set against.
+ * Asynchronous on `stream`. */
+pa_status pa_stream_read(const void* buf, size_t bytes, int32_t* sink, void* stream);
+
 /* Reassembles the logically contiguous cache through the block tables:
  * k_out/v_out device [num_seqs][Hkv][max_context_len][D] in the KV dtype,
  * positions >= context_lens[b] zero-filled.  Uses the same table walk as

@@ -1272,39 +1272,64 @@ __global__ __launch_bounds__(64, kWaves) void decode_split_kernel(Params pr) {
     locate<U>(pr, w * sp.C, b, base);
   }
   const int u_begin = w * sp.C, u_end = min(sp.total, u_begin + sp.C);
-  int u = u_begin;
+  // A segment is the part of the chunk inside one (b, g) range.
+  struct Seg {
+    int b, g, base, L, nub, range_first, seg_end, blk_begin, nblk, tok_end;
+  };
+  auto make_seg = [&](int u, int b, int base) {
+    Seg sg;
+    sg.b = b;
+    sg.base = base;
+    sg.L = len_of(pr, lens_reg, b);
+    sg.nub = units_of<U>(sg.L, pr);
+    sg.g = (u - base) / sg.nub;
+    const int q0 = (u - base) - sg.g * sg.nub;
+    sg.range_first = base + sg.g * sg.nub;                   // first unit of (b, g)
+    sg.seg_end = min(u_end, sg.range_first + sg.nub);
+    const int nblk_seq = (sg.L + kBlockSize - 1) / kBlockSize;
+    sg.blk_begin = U * q0;
+    sg.nblk = min(U * (q0 + sg.seg_end - u), nblk_seq) - sg.blk_begin;
+    sg.tok_end = min(sg.L, (sg.blk_begin + sg.nblk) * kBlockSize);
+    return sg;
+  };
+  // The segment after cur (which ends before u_end).
+  auto next_seg = [&](const Seg& cur) {
+    int b2 = cur.b, base2 = cur.base;
+    if (cur.seg_end >= cur.base + pr.Hkv * cur.nub) {        // next sequence with work
+      base2 = cur.seg_end;
+      do {
+        ++b2;
+      } while (b2 < pr.B && units_of<U>(len_of(pr, lens_reg, b2), pr) == 0);
+    }
+    return make_seg(cur.seg_end, b2, base2);
+  };
+  Seg cur = make_seg(u_begin, b, base);
+  typename Eng::Pre pre;
+  Eng::prologue(pr, cur.b, cur.g, cur.blk_begin, pre);
   typename Eng::State st;
-  while (u < u_end) {
-    const int L = len_of(pr, lens_reg, b);
-    const int nub = units_of<U>(L, pr);
-    const int g = (u - base) / nub;
-    const int q0 = (u - base) - g * nub;
-    const int range_first = base + g * nub;                  // first unit of (b, g)
-    const int seg_end = min(u_end, range_first + nub);
-    const int nq = seg_end - u;
-    const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
-    const int blk_begin = U * q0;
-    const int nblk = min(U * (q0 + nq), nblk_seq) - blk_begin;
-    const int tok_end = min(L, (blk_begin + nblk) * kBlockSize);
+  while (true) {
+    // the next segment's Q and table entries are fetched while this one
+    // streams, so the switch costs no dependent round trip
+    const bool more = cur.seg_end < u_end;
+    Seg nxt = cur;
+    typename Eng::Pre pre_next;
+    if (more) {
+      nxt = next_seg(cur);
+      Eng::prologue(pr, nxt.b, nxt.g, nxt.blk_begin, pre_next);
+    }
     Eng::reset(st);
-    typename Eng::Pre pre;
-    Eng::prologue(pr, b, g, blk_begin, pre);
-    Eng::attend_rt(pr, b, g, blk_begin, nblk, tok_end, st, pre,
-                   pr.k_new != nullptr && tok_end == L);
-    const int first_chunk = range_first / sp.C;
-    const int nslots = (range_first + nub - 1) / sp.C - first_chunk + 1;
-    Eng::emit(pr, b, g, nslots == 1 ? -1 : w - first_chunk, st);
+    Eng::attend_rt(pr, cur.b, cur.g, cur.blk_begin, cur.nblk, cur.tok_end, st, pre,
+                   pr.k_new != nullptr && cur.tok_end == cur.L);
+    const int first_chunk = cur.range_first / sp.C;
+    const int nslots = (cur.range_first + cur.nub - 1) / sp.C - first_chunk + 1;
+    Eng::emit(pr, cur.b, cur.g, nslots == 1 ? -1 : w - first_chunk, st);
     // the wave holding the range's first unit records how many slots the
     // merge has to combine
-    if (u == range_first && lane == 0)
-      pr.counters[static_cast<int64_t>(b) * pr.Hkv + g] = nslots;
-    u = seg_end;
-    if (u >= base + pr.Hkv * nub) {                           // next sequence with work
-      base = u;
-      do {
-        ++b;
-      } while (b < pr.B && units_of<U>(len_of(pr, lens_reg, b), pr) == 0);
-    }
+    if (cur.blk_begin == 0 && lane == 0)
+      pr.counters[static_cast<int64_t>(cur.b) * pr.Hkv + cur.g] = nslots;
+    if (!more) break;
+    cur = nxt;
+    pre = pre_next;
   }
 }
 

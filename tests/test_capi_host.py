@@ -78,6 +78,14 @@ def test_device_calls_reject_bad_scalars_without_launching():
                           nul) == PA_ERR_INVALID_ARG
 
 
+def test_stream_read_rejects_bad_buffers():
+    h = pk.lib()
+    assert h.pa_stream_read(None, 16, C.c_void_p(16), None) == PA_ERR_INVALID_ARG
+    assert h.pa_stream_read(C.c_void_p(16), 24, C.c_void_p(16), None) == PA_ERR_INVALID_ARG
+    assert h.pa_stream_read(C.c_void_p(8), 16, C.c_void_p(16), None) == PA_ERR_INVALID_ARG
+    assert h.pa_stream_read(C.c_void_p(16), 0, C.c_void_p(16), None) == 0
+
+
 def test_timing_hook_arguments():
     h = pk.lib()
     assert h.pa_time_next_attention(None, C.c_void_p(16)) == PA_ERR_INVALID_ARG

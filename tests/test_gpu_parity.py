@@ -367,3 +367,16 @@ def test_step_slot_cases_match_append_then_decode(hq, hkv, ps):
     # the new token's quad first): agreement far inside the 1e-2 oracle bar
     keep = [i for i in range(case.num_seqs) if i not in (1, 3)]
     assert max_err(a[keep], b[keep]) <= 1e-4
+
+
+def test_stream_read_probe_runs():
+    """The streaming-read utility reads the whole buffer and leaves the sink
+    alone for a buffer of identical words."""
+    pk = require_gpu()
+    say("[stream read] 64 MiB")
+    x = torch.ones((64 << 20) // 4, dtype=torch.int32, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    assert pk.lib().pa_stream_read(x.data_ptr(), 64 << 20, sink.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
