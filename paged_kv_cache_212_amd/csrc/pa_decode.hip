@@ -883,14 +883,30 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   }
   // Puts the new token into the last quad's registers (its pool slot may
   // still hold an older value for this wave's loads).
-  auto substitute_new = [&]() {
-    const int qt = tok_end - 1 - (blk_begin + 4 * (nquad - 1)) * kBlockSize;  // 0..63
+  // The new token sits at position tok_end - 1, in the last quad: lane qt
+  // of the quad (block qt / 16), V half h = (qt / 8) % 2, element qt % 8.
+  // It enters the attention only when its slot is the table's slot of that
+  // position (the caller's contract), so that pa_decode_step has the effect
+  // of pa_cache_append then the attention over the pool for every slot.
+  const int qt = tok_end - 1 - (blk_begin + 4 * (nquad - 1)) * kBlockSize;  // 0..63
+  // (the token is in the range's last block, nblk - 1, whose table entry is
+  // in the current chunk once the last quad is issued)
+  auto new_phys = [&]() { return __builtin_amdgcn_readlane(tcur, (nblk - 1) & 63); };
+  auto new_at_table = [&]() {
+    const int phys = new_phys();
+    return new_slot >= 0 && new_slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize &&
+           new_slot == static_cast<int64_t>(phys) * kBlockSize + (qt & 15);
+  };
+  // K before the last quad's QK, V before its P.V (so QK does not wait for V).
+  auto substitute_k = [&]() {
     const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
-    const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
     if (lane == qt) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) kr[c] = *reinterpret_cast<const uint4*>(kn + c * 8);
     }
+  };
+  auto substitute_v = [&]() {
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
     const int kb = qt >> 4, h = (qt >> 3) & 1, e = qt & 7;
     const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
     const int sh = (e & 1) * 16, dw = e >> 1;
@@ -910,28 +926,22 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
           }
         }
   };
-  // Appends the new token (position tok_end - 1, in the last quad), with the
-  // effect of pa_cache_append then the attention over the pool:
-  //   * slot == the table's slot of that position (the caller's contract):
-  //     the token goes into the last quad's registers, and the wave holds its
-  //     whole half block (8 tokens, all dims): as loaded, with the token put
-  //     in.  Writing that back as whole 128-byte lines stores the token and
-  //     rewrites the other tokens' current bytes unchanged (2-byte V stores
-  //     would leave 16 partly written lines per head);
-  //   * any other slot in the pool: the token alone is written there,
-  //     element by element, and the position is attended as loaded;
-  //   * slot out of the pool (-1): nothing is written.
-  auto append_new = [&]() {
+  // Pool write of the new token, unless the merge kernel does it:
+  //   * at the table's slot: the wave holds the token's whole half block (8
+  //     tokens, all dims: as loaded, with the token put in); writing that
+  //     back as whole 128-byte lines stores the token and rewrites the other
+  //     tokens' current bytes unchanged (2-byte V stores would leave 16
+  //     partly written lines per head);
+  //   * any other slot in the pool: the token alone, element by element;
+  //   * slot out of the pool (-1): nothing.
+  auto write_new = [&](bool at_table) {
     const int64_t slot = new_slot;
-    if (slot < 0 || slot >= static_cast<int64_t>(pr.num_blocks) * kBlockSize) return;
-    const int qt = tok_end - 1 - (blk_begin + 4 * (nquad - 1)) * kBlockSize;  // 0..63
+    if (pr.write_new_in_merge || slot < 0 ||
+        slot >= static_cast<int64_t>(pr.num_blocks) * kBlockSize)
+      return;
     const int kb = qt >> 4, h = (qt >> 3) & 1;
-    const int phys = kb == 0 ? ph[0] : kb == 1 ? ph[1] : kb == 2 ? ph[2] : ph[3];
-    const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
-    const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
-    if (slot == static_cast<int64_t>(phys) * kBlockSize + (qt & 15)) {
-      substitute_new();
-      if (pr.write_new_in_merge) return;
+    const int phys = new_phys();
+    if (at_table) {
       const int64_t tile = (static_cast<int64_t>(phys) * pr.Hkv + g) * kTileBytes;
       char* kt = static_cast<char*>(pr.kpool_w) + tile + (lane & 15) * 16;
       if ((lane >> 3) == (qt >> 3)) {
@@ -948,7 +958,9 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
             for (int t = 0; t < NT; ++t)
               *reinterpret_cast<uint4*>(vt + (H * D + 64 * t) * 16) = vr[KB][H][t];
           }
-    } else if (!pr.write_new_in_merge) {
+    } else {
+      const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
+      const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
       const int64_t blk = slot / kBlockSize;
       const int ts = static_cast<int>(slot % kBlockSize);
       uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
@@ -1063,9 +1075,14 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     issue_v();
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (with_new) append_new();
+  const bool at_table = with_new && new_at_table();
+  if (at_table) substitute_k();
   uint2 phi, plo;
   qk_softmax(nquad - 1, phi, plo);
+  if (with_new) {
+    if (at_table) substitute_v();
+    write_new(at_table);
+  }
   pv(nquad - 1, phi, plo, std::true_type{});
 }
 
