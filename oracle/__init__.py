@@ -24,6 +24,10 @@ over the cached keys and values; the pages state that paging leaves the result
 of attention unchanged, so the oracle is that plain definition evaluated over
 the K/V reassembled through the block table.
 
+``prefill_ref`` (oracle/prefill.py) extends the decode step to a chunk of
+query tokens per sequence attending causally over the paged cache (prefill,
+chunked prefill); with one token per sequence it is the decode step.
+
 Pinning: every function here is pinned by ``tests/test_oracle*.py`` against
 values not produced by the oracle itself (brute force over the unpaged token
 rows, torch's scaled_dot_product_attention in fp64, closed forms, a worked
@@ -35,4 +39,5 @@ from .allocator import AllocatorModel, AllocError  # noqa: F401
 from .cache import (new_pools, append_ref, copy_ref, gather_ref, k_offset,  # noqa: F401
                     v_offset)
 from .attention import decode_ref, dense_ref, partitioned_ref, merge_partials  # noqa: F401
+from .prefill import prefill_ref  # noqa: F401
 from .run import run_case, oracle_sequence_out  # noqa: F401

@@ -235,3 +235,27 @@ def custom_case(seed, dtype, lens, hq, hkv, d, device="cpu", *, num_blocks=None,
     return _independent(f"custom_{dtype}_{hq}x{hkv}x{d}", seed, dtype, lens, hq, hkv, d, device,
                         num_blocks=num_blocks, q_std=q_std, boost_prob=boost_prob,
                         partition_size=partition_size, rng=rng)
+
+
+def prefill_case(seed, dtype, lens, qlens, hq, hkv, d, device="cpu", *, num_blocks=None,
+                 pool_factor=1.2):
+    """Seeded inputs for attending a chunk of query tokens per sequence
+    (prefill, chunked prefill): the decode case of the same sequences, whose
+    set-up and step append leave all lens[b] tokens in the cache, plus query
+    rows q [T][hq][d] for the last qlens[b] positions of each sequence and
+    their row offsets query_start [B+1] (T = query_start[-1]).
+
+    Returns (case, q, query_start)."""
+    lens = np.asarray(lens, dtype=np.int64)
+    qlens = np.asarray(qlens, dtype=np.int64)
+    if qlens.shape != lens.shape or (qlens < 0).any() or (qlens > lens).any():
+        raise ValueError("qlens must be in [0, lens] per sequence")
+    case = custom_case(seed, dtype, lens, hq, hkv, d, device, num_blocks=num_blocks,
+                       pool_factor=pool_factor)
+    query_start = np.zeros(len(lens) + 1, dtype=np.int64)
+    query_start[1:] = np.cumsum(qlens)
+    g = torch.Generator(device=device)
+    g.manual_seed(1_000_003 * seed + 29)
+    q = torch.randn((int(query_start[-1]), hq, d), generator=g, device=device,
+                    dtype=torch.float32).to(TORCH_DTYPE[dtype])
+    return case, q, query_start
