@@ -290,6 +290,38 @@ pa_status pa_decode_step_merge(float* out, const void* q, void* k_pool, void* v_
                                int32_t partition_size, pa_dtype dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Attention of a chunk of query tokens per sequence over the paged cache
+ * (prefill of a prompt, chunked prefill on top of a cached prefix, or decode
+ * with one token).  Sequence b holds L = context_lens[b] tokens in its blocks
+ * (the chunk's own K/V included: append them with pa_cache_append first);
+ * its query rows are query_start[b] .. query_start[b+1]-1 of q, and row
+ * query_start[b] + i is the token at position L - n_b + i
+ * (n_b = query_start[b+1] - query_start[b] <= L).  For each such row and
+ * query head h:
+ *   out[row][h] = softmax_t(scale * q[row][h] . K_b[t]) weighted sum of
+ *                 V_b[t], t in [0, L - n_b + i]
+ * (causal), K_b/V_b being KV head h/G reached through block_tables[b] in
+ * logical order (page 3, abeam.tech review, sections 「KV キャッシュマネージャ」
+ * and 「モデル構造ではなくサービング基盤の変更」; the prompt phase as its own
+ * stage: 「今後注目すべき方向性」).  Accumulation in fp32.
+ *   q: device [num_tokens][Hq][D], KV dtype; out: device float
+ *   [num_tokens][Hq][D]; query_start: device int32 [num_seqs + 1],
+ *   non-decreasing from 0 to num_tokens; max_query_len: an upper bound of n_b
+ *   (sizes the launch); max_context_len: upper bound of context_lens.
+ * Supported: fp16/bf16 KV (matrix cores), block_size 16, head_dim 64 or 128,
+ * Hq a multiple of Hkv.  Rows of a sequence whose length or chunk fails the
+ * bounds checks (L > max_context_len, n_b > L or > max_query_len), or whose
+ * table holds an entry outside the pool, are NaN; a sequence whose
+ * query_start entries are out of order or out of [0, num_tokens] gets no
+ * rows written.  Asynchronous on `stream`. */
+pa_status pa_prefill(float* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                     int32_t max_context_len, int32_t max_query_len, float scale,
+                     pa_dtype dtype, void* stream);
+
 /* Measurement hook: the next attention kernel launched by a decode call
  * (pa_decode, pa_decode_partial, pa_decode_step or pa_decode_step_partial)
  * on this host thread records start_event when it starts executing and

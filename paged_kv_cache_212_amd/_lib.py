@@ -70,6 +70,8 @@ SIGNATURES = {
     "pa_decode_step_merge": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, C.c_int,
                                        _vp, _sz, _vp]),
+    "pa_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                             _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp]),
     "pa_time_next_attention": (C.c_int, [_vp, _vp]),
     "pa_stream_read": (C.c_int, [_vp, _sz, _vp, _vp]),
     "pa_gather_kv": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,

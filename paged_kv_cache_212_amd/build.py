@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa212.so")
 
 ARCH = "gfx950"
-SOURCES = ["pa_status.cpp", "block_manager.cpp", "pa_cache.hip", "pa_decode.hip"]
+SOURCES = ["pa_status.cpp", "block_manager.cpp", "pa_cache.hip", "pa_decode.hip",
+           "pa_prefill.hip"]
 
 
 def hipcc() -> str:

@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "pa_device.h"
+#include "pa_mfma.h"
 
 namespace pa {
 namespace {
@@ -196,111 +197,6 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(Params pr) {
 // ---------------------------------------------------------------------------
 // Matrix-core partition kernel.
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// 16-byte streaming load of K/V (each tile is read once per step): the
-// non-temporal hint keeps the stream from displacing cached lines.
-__device__ __forceinline__ uint4 load_stream(const char* p) {
-  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(p)));
-}
-
-template <typename T>
-struct Mfma;
-
-template <>
-struct Mfma<BF16> {
-  // S^T tile (16 tokens x 16 heads) += K (16 tokens x 32 dims) . Q^T (32 dims x 16 heads)
-  __device__ static inline f32x4_t qk(uint4 k, uint4 q, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k),
-                                                   __builtin_bit_cast(bf16x8_t, q), c, 0, 0, 0);
-  }
-  // O tile (16 heads x 16 dims) += P (16 heads x 16 tokens) . V (16 tokens x 16 dims)
-  __device__ static inline f32x4_t pv(uint2 p, uint2 v, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, p),
-                                                     __builtin_bit_cast(i16x4_t, v), c, 0, 0, 0);
-  }
-  // O tile (16 heads x 16 dims) += P (16 heads x 32 tokens) . V (32 tokens x 16 dims)
-  __device__ static inline f32x4_t pv8(uint4 p, uint4 v, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, p),
-                                                   __builtin_bit_cast(bf16x8_t, v), c, 0, 0, 0);
-  }
-  __device__ static inline void split8(const float pe[8], uint4& hi, uint4& lo) {
-    uint32_t h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t u = __float_as_uint(pe[e]);
-      h[e] = u >> 16;
-      const float r = pe[e] - __uint_as_float(u & 0xFFFF0000u);
-      l[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r));
-    }
-    hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                    h[6] | (h[7] << 16));
-    lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                    l[6] | (l[7] << 16));
-  }
-  // p (>= 0) = hi + lo with hi = p truncated to bf16 (exact remainder) and
-  // lo = remainder rounded to bf16.
-  __device__ static inline void split(const float pe[4], uint2& hi, uint2& lo) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t u = __float_as_uint(pe[e]);
-      h[e] = u >> 16;
-      const float r = pe[e] - __uint_as_float(u & 0xFFFF0000u);
-      l[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r));
-    }
-    hi = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    lo = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
-  }
-};
-
-template <>
-struct Mfma<F16> {
-  __device__ static inline f32x4_t pv8(uint4 p, uint4 v, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, p),
-                                                  __builtin_bit_cast(f16x8_t, v), c, 0, 0, 0);
-  }
-  __device__ static inline void split8(const float pe[8], uint4& hi, uint4& lo) {
-    uint32_t h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const _Float16 hh = static_cast<_Float16>(pe[e]);
-      const float r = pe[e] - static_cast<float>(hh);
-      h[e] = __builtin_bit_cast(uint16_t, hh);
-      l[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
-    }
-    hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                    h[6] | (h[7] << 16));
-    lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                    l[6] | (l[7] << 16));
-  }
-  __device__ static inline f32x4_t qk(uint4 k, uint4 q, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, k),
-                                                  __builtin_bit_cast(f16x8_t, q), c, 0, 0, 0);
-  }
-  __device__ static inline f32x4_t pv(uint2 p, uint2 v, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, p),
-                                                 __builtin_bit_cast(f16x4_t, v), c, 0, 0, 0);
-  }
-  __device__ static inline void split(const float pe[4], uint2& hi, uint2& lo) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const _Float16 hh = static_cast<_Float16>(pe[e]);
-      const float r = pe[e] - static_cast<float>(hh);
-      h[e] = __builtin_bit_cast(uint16_t, hh);
-      l[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
-    }
-    hi = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    lo = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
-  }
-};
-
 // Two blocks (A = block 2q, B = block 2q+1 of the range) per iteration.
 // Lane = 16*j + n (n = lane % 16, j = lane / 16).
 //   QK, half hh in {0,1}: S^T (16 rows x 16 heads) = K rows . Q^T where row r

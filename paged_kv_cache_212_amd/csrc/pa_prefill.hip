@@ -1,0 +1,286 @@
+// Attention of a chunk of query tokens per sequence over the paged cache
+// (prefill, chunked prefill) on gfx950.
+//
+// Sequence b holds L = context_lens[b] tokens, the last n_b of which are the
+// chunk; query row query_start[b] + i is the token at position L - n_b + i and
+// attends causally to positions 0 .. its own, read through the block table
+// in logical order (page 3, abeam.tech review, sections 「KV キャッシュマネージャ」
+// and 「モデル構造ではなくサービング基盤の変更」; the review names the prompt
+// phase as a stage of its own in 「今後注目すべき方向性」).  With n_b = 1 it is
+// the decode step.
+//
+// One 64-lane wave per (query head h, tile of 16 query tokens, sequence);
+// lane = 16*j + n.  Per 16-token block of keys:
+//   S^T (16 keys x 16 queries) = K . Q^T on v_mfma_f32_16x16x32: A = K (lane
+//     reads key n, dims kk*32 + 8j .. +8), B = Q (query n, same dims).  Result:
+//     lane (n, j) holds query n against keys 4j + e (e = 0..3).
+//   That is the A operand of O (16 queries x 16 dims) += P (16 queries x 16
+//     keys) . V (16 keys x 16 dims) on v_mfma_f32_16x16x16 (lane: row n,
+//     k = keys 4j + e), so the probabilities need no transpose.  B = V: lane
+//     (n, j) holds dim t*16 + n of keys 4j .. 4j+3, 8 contiguous bytes of the
+//     V tile (8 consecutive tokens of a dim are stored together).  P is split
+//     into a high and a low half-precision part (two MFMAs).
+//   O: lane (n, j) holds dim t*16 + n of queries 4j + e.
+// Online softmax per query in the log2 domain (max and sum across the 4 lane
+// groups with two xor shuffles); the causal mask selects scores to -inf, and
+// V rows at positions >= L are zeroed so unwritten slots never reach O.
+// Blocks are double-buffered: the loads of block kb + 2 are issued once block
+// kb has been consumed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pa_device.h"
+#include "pa_mfma.h"
+
+namespace pa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQTile = 16;  // query tokens per wave
+
+struct PrefillParams {
+  float* out;               // [T][Hq][D]
+  const void* q;            // [T][Hq][D]
+  const void* kpool;
+  const void* vpool;
+  const int32_t* tables;    // [B][max_blocks]
+  const int32_t* lens;      // [B]
+  const int32_t* qstart;    // [B + 1]
+  int B, T, Hq, Hkv, G;
+  int num_blocks, max_blocks, max_ctx, max_qlen;
+  float scale_log2;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void prefill_kernel(PrefillParams pr) {
+  constexpr int NKK = D / 32;     // 32-dim steps of Q.K^T
+  constexpr int NTL = D / 16;     // 16-dim output tiles
+  constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
+  const int h = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, j = lane >> 4;
+  const int g = h / pr.G;
+
+  const int L = pr.lens[b];
+  const int q0 = pr.qstart[b], q1 = pr.qstart[b + 1];
+  const bool rows_ok = q0 >= 0 && q0 <= q1 && q1 <= pr.T;
+  if (!rows_ok) return;                                   // no row can be trusted
+  const int nq = q1 - q0;
+  const int i0 = tile * kQTile;                           // first query of the tile
+  if (i0 >= nq) return;
+  float* orow = pr.out + (static_cast<int64_t>(q0) + i0) * pr.Hq * D + static_cast<int64_t>(h) * D;
+  const bool seq_ok = L >= 0 && L <= pr.max_ctx && L <= pr.max_blocks * kBlockSize &&
+                      nq <= L && nq <= pr.max_qlen;
+  if (!seq_ok) {
+    // length out of the declared bounds: NaN rows
+    for (int idx = lane; idx < kQTile * D; idx += 64) {
+      const int r = idx / D;
+      if (i0 + r < nq) orow[static_cast<int64_t>(r) * pr.Hq * D + idx % D] = __builtin_nanf("");
+    }
+    return;
+  }
+
+  // Q (B operand): query n of the tile, dims kk*32 + 8j .. +8
+  uint4 qr[NKK];
+  {
+    const bool real = i0 + n < nq;
+    const uint16_t* qb = static_cast<const uint16_t*>(pr.q) +
+                         ((static_cast<int64_t>(q0) + i0 + n) * pr.Hq + h) * D + j * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qr[kk] = real ? *reinterpret_cast<const uint4*>(qb + kk * 32) : make_uint4(0, 0, 0, 0);
+  }
+  const int first_pos = L - nq;                           // position of query 0
+  const int qpos = first_pos + i0 + n;                    // this lane's query position
+  const int last_pos = first_pos + min(nq, i0 + kQTile) - 1;
+  const int nblk = last_pos / kBlockSize + 1;             // key blocks the tile needs
+
+  const char* kbase = static_cast<const char*>(pr.kpool) + g * kTileBytes;
+  const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
+  const int64_t block_stride = static_cast<int64_t>(pr.Hkv) * kTileBytes;
+  const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks;
+  bool bad = false;
+  // table entries, 64 per register (lane i: entry 64*c + i of chunk c)
+  auto load_chunk = [&](int c) -> int {
+    const int k = c * 64 + lane;
+    const int e = k < nblk ? trow[k] : 0;
+    const bool lane_bad = k < nblk && (e < 0 || e >= pr.num_blocks);
+    if (__any(lane_bad)) bad = true;
+    return lane_bad ? 0 : e;
+  };
+  int chunk = 0;
+  int tcur = load_chunk(0);
+  auto phys_of = [&](int k) -> int {                     // k increases call by call
+    const int c = k >> 6;
+    if (c != chunk) {
+      chunk = c;
+      tcur = load_chunk(c);
+    }
+    return __builtin_amdgcn_readlane(tcur, k & 63);
+  };
+
+  uint4 kreg[2][NKK];
+  uint2 vreg[2][NTL];
+  auto issue = [&](int u, int kb) {
+    const int64_t off = phys_of(kb) * block_stride;
+    const char* kt = kbase + off + ((j * 16) + n) * 16;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      kreg[u][kk] = load_stream(kt + kk * 64 * 16);
+    const char* vt = vbase + off + ((j >> 1) * D + n) * 16 + (j & 1) * 8;
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+      vreg[u][t] = *reinterpret_cast<const uint2*>(vt + t * 16 * 16);
+  };
+
+  float m_run = -INFINITY, l_lane = 0.f;
+  f32x4_t acc[NTL];
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int u, int kb) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) s = Mfma<T>::qk(kreg[u][kk], qr[kk], s);
+    const int kpos0 = kb * kBlockSize + 4 * j;            // key position of s[0]
+    float sv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[e] = (kpos0 + e <= qpos) ? s[e] * pr.scale_log2 : -INFINITY;
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m_run, bm);
+    if (__any(mn != m_run)) {
+      // a query's running max moved: rescale its O row by 2^(m_old - m_new)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      l_lane *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ar = __shfl(alpha, 4 * j + e);        // alpha of O row 4j + e
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) acc[t][e] *= ar;
+      }
+      m_run = mn;
+    }
+    float pe[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_run);
+    l_lane += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    uint2 phi, plo;
+    Mfma<T>::split(pe, phi, plo);
+    if ((kb + 1) * kBlockSize > L) {
+      // the block reaches past the sequence: zero V of unwritten positions
+      const uint32_t mx = (kpos0 + 0 < L ? 0x0000FFFFu : 0u) | (kpos0 + 1 < L ? 0xFFFF0000u : 0u);
+      const uint32_t my = (kpos0 + 2 < L ? 0x0000FFFFu : 0u) | (kpos0 + 3 < L ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        vreg[u][t].x &= mx;
+        vreg[u][t].y &= my;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      acc[t] = Mfma<T>::pv(phi, vreg[u][t], acc[t]);
+      acc[t] = Mfma<T>::pv(plo, vreg[u][t], acc[t]);
+    }
+  };
+
+  issue(0, 0);
+  if (nblk > 1) issue(1, 1);
+  for (int kb = 0; kb < nblk; kb += 2) {
+    compute(0, kb);
+    if (kb + 2 < nblk) issue(0, kb + 2);
+    if (kb + 1 < nblk) {
+      compute(1, kb + 1);
+      if (kb + 3 < nblk) issue(1, kb + 3);
+    }
+  }
+
+  // l of query n, then of O row 4j + e
+  float l = l_lane;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * j + e;
+    const float lr = __shfl(l, r);
+    if (i0 + r < nq) {
+      const float inv = bad ? __builtin_nanf("") : 1.0f / lr;
+#pragma unroll
+      for (int t = 0; t < NTL; ++t)
+        orow[static_cast<int64_t>(r) * pr.Hq * D + t * 16 + n] = acc[t][e] * inv;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" pa_status pa_prefill(float* out, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start,
+                                int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, int32_t max_query_len, float scale,
+                                pa_dtype dtype, void* stream) {
+  const char* fn = "pa_prefill";
+  if (block_size != kBlockSize)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, block_size);
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (dtype == PA_F32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: fp32 KV (matrix-core path: fp16/bf16 only)", fn);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", fn, head_dim);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      num_q_heads > 65535)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %d / num_kv_heads %d", fn, num_q_heads,
+                num_kv_heads);
+  if (num_seqs < 0 || num_seqs > 65535 || num_tokens < 0 || num_blocks <= 0 ||
+      max_blocks_per_seq < 0 || max_context_len < 0 || max_query_len < 0 ||
+      max_query_len > 65535 * kQTile)
+    return fail(PA_ERR_INVALID_ARG, "%s: size out of range", fn);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pool) |
+       reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return fail(PA_ERR_INVALID_ARG, "%s: q and pools must be 16-byte aligned", fn);
+  PrefillParams pr{};
+  pr.out = out;
+  pr.q = q;
+  pr.kpool = k_pool;
+  pr.vpool = v_pool;
+  pr.tables = block_tables;
+  pr.lens = context_lens;
+  pr.qstart = query_start;
+  pr.B = num_seqs;
+  pr.T = num_tokens;
+  pr.Hq = num_q_heads;
+  pr.Hkv = num_kv_heads;
+  pr.G = num_q_heads / num_kv_heads;
+  pr.num_blocks = num_blocks;
+  pr.max_blocks = max_blocks_per_seq;
+  pr.max_ctx = max_context_len;
+  pr.max_qlen = max_query_len;
+  pr.scale_log2 = scale * kLog2e;
+  const dim3 grid(num_q_heads, (max_query_len + kQTile - 1) / kQTile, num_seqs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PA_BF16) {
+    if (head_dim == 64)
+      prefill_kernel<BF16, 64><<<grid, 64, 0, s>>>(pr);
+    else
+      prefill_kernel<BF16, 128><<<grid, 64, 0, s>>>(pr);
+  } else {
+    if (head_dim == 64)
+      prefill_kernel<F16, 64><<<grid, 64, 0, s>>>(pr);
+    else
+      prefill_kernel<F16, 128><<<grid, 64, 0, s>>>(pr);
+  }
+  return launch_status(fn);
+}

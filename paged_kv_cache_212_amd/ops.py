@@ -187,6 +187,36 @@ def decode_step(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables
     return out
 
 
+def prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, max_context_len,
+            max_query_len, scale=None, stream=None):
+    """out [T][Hq][D] float32 = causal attention of the query rows q [T][Hq][D]
+    over the paged cache (pa_prefill): rows query_start[b] .. query_start[b+1]-1
+    are the last tokens of sequence b, whose context_lens[b] tokens are in the
+    pool already."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    T, Hq = q.shape[0], q.shape[1]
+    B = context_lens.shape[0]
+    if q.shape != (T, Hq, D) or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [T][Hq][D] in the pool dtype")
+    if out.shape != (T, Hq, D) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [T][Hq][D]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.dim() != 1:
+        raise ValueError("context_lens must be int32 [B]")
+    if query_start.dtype != torch.int32 or query_start.shape != (B + 1,):
+        raise ValueError("query_start must be int32 [B + 1]")
+    scale = D ** -0.5 if scale is None else float(scale)
+    check(lib().pa_prefill(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                           _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
+                           _dev(context_lens, "context_lens"), _dev(query_start, "query_start"),
+                           B, T, Hq, H, D, BLOCK_SIZE, N, block_tables.shape[1],
+                           int(max_context_len), int(max_query_len), scale, pa_dtype(q.dtype),
+                           _stream(stream)), "pa_prefill")
+    return out
+
+
 def gather_kv(k_pool, v_pool, block_tables, context_lens, max_context_len, stream=None):
     """Contiguous K, V [B][Hkv][max_context_len][D] reassembled through the tables."""
     N, H, D = _pool_dims(k_pool, v_pool)

@@ -78,6 +78,24 @@ def test_device_calls_reject_bad_scalars_without_launching():
                           nul) == PA_ERR_INVALID_ARG
 
 
+def test_prefill_rejects_bad_scalars_without_launching():
+    h = pk.lib()
+    nul = None
+    args = lambda **kw: [kw.get(k, v) for k, v in (  # noqa: E731
+        ("out", nul), ("q", nul), ("kp", nul), ("vp", nul), ("tab", nul), ("lens", nul),
+        ("qs", nul), ("B", 2), ("T", 8), ("Hq", 8), ("Hkv", 2), ("D", 128), ("bs", 16),
+        ("N", 10), ("MB", 4), ("ctx", 64), ("mq", 8), ("scale", 0.1), ("dt", PA_BF16),
+        ("st", nul))]
+    assert h.pa_prefill(*args(dt=PA_F32)) == PA_ERR_UNSUPPORTED
+    assert h.pa_prefill(*args(D=96)) == PA_ERR_UNSUPPORTED
+    assert h.pa_prefill(*args(bs=8)) == PA_ERR_UNSUPPORTED
+    assert h.pa_prefill(*args(Hkv=3)) == PA_ERR_INVALID_ARG
+    assert h.pa_prefill(*args(scale=-1.0)) == PA_ERR_INVALID_ARG
+    assert h.pa_prefill(*args(mq=-1)) == PA_ERR_INVALID_ARG
+    assert h.pa_prefill(*args()) == PA_ERR_INVALID_ARG          # NULL pointers
+    assert h.pa_prefill(*args(T=0)) == 0                          # nothing to do
+
+
 def test_stream_read_rejects_bad_buffers():
     h = pk.lib()
     assert h.pa_stream_read(None, 16, C.c_void_p(16), None) == PA_ERR_INVALID_ARG
