@@ -50,6 +50,9 @@ def parse():
                          "kernel, timed) then pa_decode_merge; separate: pa_cache_append, "
                          "pa_decode_partial (timed), pa_decode_merge; step: one "
                          "pa_decode_step call (timed as a whole)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure pa_prefill instead (chunked prefill, Llama-3-8B heads: "
+                         "16 sequences of 2048 tokens, the last 512 as the chunk)")
     ap.add_argument("--no-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -143,6 +146,109 @@ def cpu_baseline(case, budget_s: float):
                       f"{case.num_seqs} sequences: copy pairs, append, fp64 decode_ref)"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (no sparsity)
+
+
+def prefill_bench(args):
+    """Chunked prefill over the paged cache: B = 16 sequences of L = 2048
+    tokens (Llama-3-8B heads, bf16, shuffled blocks), whose last n = 512 tokens
+    are the chunk.  One call = one pa_prefill launch; value = causal-attention
+    flops (4*D per attended (query, key, head)) per second."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_212_amd as pk
+    from workloads.configs import prefill_case
+
+    B, L, n, Hq, Hkv, D = 16, 2048, 512, 32, 8, 128
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    case, q, qs = prefill_case(21, "bf16", [L] * B, [n] * B, Hq, Hkv, D, device=dev)
+    cache = pk.PagedKVCache(case.num_blocks, Hkv, D, torch.bfloat16, dev,
+                            free_order=case.free_order, fill=0.0)
+    cache.replay(case.script, case.rows, case.k_tok, case.v_tok)
+    plan = cache.plan_step(case.batch)
+    nr = torch.as_tensor(case.new_rows(), device=dev)
+    pk.ops.cache_append(cache.k_pool, cache.v_pool, case.k_tok.index_select(0, nr).contiguous(),
+                        case.v_tok.index_select(0, nr).contiguous(), plan.d_slots)
+    layers = [(cache.k_pool, cache.v_pool)] + [(cache.k_pool.clone(), cache.v_pool.clone())
+                                               for _ in range(args.layers - 1)]
+    qs_d = torch.as_tensor(qs, dtype=torch.int32, device=dev)
+    out = torch.empty((q.shape[0], Hq, D), dtype=torch.float32, device=dev)
+
+    def call(i):
+        kp, vp = layers[i % len(layers)]
+        pk.ops.prefill(out, q, kp, vp, plan.d_tables, plan.d_lens, qs_d, plan.max_context_len, n)
+
+    steps = max(1, args.steps // 10)
+    for i in range(max(2, args.warmup // 10)):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    attended = B * sum(L - n + i + 1 for i in range(n))        # (query, key) pairs per head
+    flops = 4 * D * Hq * attended
+    tflops = flops / (us * 1e-6) / 1e12
+    kv_unique = B * L * Hkv * 2 * D * 2
+    res = {"metric": "paged chunked-prefill attention TFLOP/s, Llama-3-8B shape",
+           "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+           "us_per_call": round(us, 2), "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": f"chunked prefill: B={B} sequences of L={L} tokens, last "
+                                  f"n={n} as the chunk, Hq={Hq}, Hkv={Hkv}, D={D}, block 16",
+                      "query_tokens": B * n, "attended_pairs_per_head": attended,
+                      "layers_rotated": args.layers},
+           "kv_unique_bytes": kv_unique,
+           "roofline": {"kernel": "prefill_kernel (pa_prefill)", "bound": "mfma",
+                        "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": None}}
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = prefill_cpu_baseline(case, q, qs, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def prefill_cpu_baseline(case, q, qs, budget_s):
+    """The fp64 oracle (prefill_ref) on a bounded sample: query rows of the
+    first sequence, 64 at a time, while the budget lasts; flops counted as in
+    the GPU figure."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import bits_of, run_case
+    from oracle.prefill import prefill_ref
+    import dataclasses
+    cores = len(os.sched_getaffinity(0))
+    cpu_case = dataclasses.replace(case, k_tok=case.k_tok.cpu(), v_tok=case.v_tok.cpu(),
+                                   q=case.q.cpu())
+    ref = run_case(cpu_case, decode=False)
+    qb = bits_of(q.cpu(), "bf16")
+    L, n = int(case.lens[0]), int(qs[1] - qs[0])
+    Hq, D = qb.shape[1], qb.shape[2]
+    flops = 0
+    rows = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while time.perf_counter() - t0 < budget_s and rows < n:
+            k = min(64, n - rows)
+            # rows [rows, rows + k) of sequence 0's chunk: a chunk of k tokens ending
+            # at position L - n + rows + k - 1
+            Lk = L - n + rows + k
+            prefill_ref(qb[rows:rows + k], ref["k_pool"], ref["v_pool"], ref["tables"][:1],
+                        np.array([Lk]), np.array([0, k]), "bf16")
+            flops += 4 * D * Hq * sum(Lk - k + i + 1 for i in range(k))
+            rows += k
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{rows} query rows of sequence 0's chunk, {k if rows else 0} at a time"}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -154,6 +260,9 @@ def main():
                                    "no multi-GPU sharding (see the design notes); run with "
                                    "--gpus 1"}))
         sys.exit(2)
+    if args.prefill:
+        prefill_bench(args)
+        return
 
     import numpy as np
     import torch
