@@ -10,7 +10,8 @@
 // the decode step.
 //
 // One 64-lane wave per (query head h, tile of 16 query tokens, sequence);
-// lane = 16*j + n.  Per 16-token block of keys:
+// lane = 16*j + n.  K/V of a block are re-read by every tile and query head of
+// its KV head, so they use plain (cached) loads.  Per 16-token block of keys:
 //   S^T (16 keys x 16 queries) = K . Q^T on v_mfma_f32_16x16x32: A = K (lane
 //     reads key n, dims kk*32 + 8j .. +8), B = Q (query n, same dims).  Result:
 //     lane (n, j) holds query n against keys 4j + e (e = 0..3).
@@ -49,6 +50,7 @@ struct PrefillParams {
   const int32_t* qstart;    // [B + 1]
   int B, T, Hq, Hkv, G;
   int num_blocks, max_blocks, max_ctx, max_qlen;
+  int ntiles;               // query tiles per sequence
   float scale_log2;
 };
 
@@ -57,10 +59,19 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams pr) {
   constexpr int NKK = D / 32;     // 32-dim steps of Q.K^T
   constexpr int NTL = D / 16;     // 16-dim output tiles
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
-  const int h = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
+  // Workgroup order: KV head fastest, then the query head within its group,
+  // then the tile, then the sequence.  Workgroups are dealt round-robin to the
+  // XCDs, so with Hkv a multiple of their number every query head and tile of
+  // one KV head runs on one XCD and re-reads its K/V from that XCD's L2.
+  int lin = blockIdx.x;
+  const int g = lin % pr.Hkv;
+  lin /= pr.Hkv;
+  const int e_head = lin % pr.G;
+  lin /= pr.G;
+  const int tile = lin % pr.ntiles, b = lin / pr.ntiles;
+  const int h = g * pr.G + e_head;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
-  const int g = h / pr.G;
 
   const int L = pr.lens[b];
   const int q0 = pr.qstart[b], q1 = pr.qstart[b + 1];
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams pr) {
     const char* kt = kbase + off + ((j * 16) + n) * 16;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      kreg[u][kk] = load_stream(kt + kk * 64 * 16);
+      kreg[u][kk] = *reinterpret_cast<const uint4*>(kt + kk * 64 * 16);
     const char* vt = vbase + off + ((j >> 1) * D + n) * 16 + (j & 1) * 8;
 #pragma unroll
     for (int t = 0; t < NTL; ++t)
@@ -269,7 +280,12 @@ extern "C" pa_status pa_prefill(float* out, const void* q, const void* k_pool,
   pr.max_ctx = max_context_len;
   pr.max_qlen = max_query_len;
   pr.scale_log2 = scale * kLog2e;
-  const dim3 grid(num_q_heads, (max_query_len + kQTile - 1) / kQTile, num_seqs);
+  pr.ntiles = (max_query_len + kQTile - 1) / kQTile;
+  const uint64_t nwg = static_cast<uint64_t>(num_q_heads) * pr.ntiles * num_seqs;
+  if (nwg > 0x7fffffffull)
+    return fail(PA_ERR_INVALID_ARG, "%s: %llu workgroups exceed the launch limit", fn,
+                static_cast<unsigned long long>(nwg));
+  const dim3 grid(static_cast<uint32_t>(nwg));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == PA_BF16) {
     if (head_dim == 64)
