@@ -28,6 +28,11 @@ the K/V reassembled through the block table.
 query tokens per sequence attending causally over the paged cache (prefill,
 chunked prefill); with one token per sequence it is the decode step.
 
+``quantize_ref`` (oracle/quant.py) encodes K/V rows into the 8-bit codes of a
+quantized cache (INT8, as page 1 pairs with paging in section
+「他のKVキャッシュ最適化との組み合わせ」, and FP8 E4M3); ``decode_ref`` then
+attends over code * scale.
+
 Pinning: every function here is pinned by ``tests/test_oracle*.py`` against
 values not produced by the oracle itself (brute force over the unpaged token
 rows, torch's scaled_dot_product_attention in fp64, closed forms, a worked
@@ -40,4 +45,5 @@ from .cache import (new_pools, append_ref, copy_ref, gather_ref, k_offset,  # no
                     v_offset)
 from .attention import decode_ref, dense_ref, partitioned_ref, merge_partials  # noqa: F401
 from .prefill import prefill_ref  # noqa: F401
+from .quant import quantize_ref, dequantize_ref  # noqa: F401
 from .run import run_case, oracle_sequence_out  # noqa: F401

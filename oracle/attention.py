@@ -31,23 +31,28 @@ def _softmax_row(s):
     return e / e.sum()
 
 
-def decode_ref(q_bits, k_pool, v_pool, tables, lens, dtype, scale=None, bs=16):
+def decode_ref(q_bits, k_pool, v_pool, tables, lens, dtype, scale=None, bs=16, q_dtype=None,
+               k_scale=1.0, v_scale=1.0):
     """q_bits [B][Hq][D]; pools of stored bits; tables int [B][MB]; lens [B].
 
-    Returns out [B][Hq][D] fp64.
+    ``dtype`` is the pools' dtype, ``q_dtype`` that of q (default: the same).
+    A quantized cache ("i8"/"fp8" codes) holds K = code * k_scale and
+    V = code * v_scale (scales taken as fp32); the attention is the formula
+    above over those values.  Returns out [B][Hq][D] fp64.
     """
     B, Hq, D = q_bits.shape
     Hkv = k_pool.shape[1]
     G = Hq // Hkv
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
-    q = to_f64(q_bits, dtype)
+    q = to_f64(q_bits, dtype if q_dtype is None else q_dtype)
+    ks, vs = float(np.float32(k_scale)), float(np.float32(v_scale))
     out = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
         L = int(lens[b])
         if L == 0:
             continue
         Kb, Vb = gather_ref(k_pool, v_pool, tables[b], L, bs)
-        Kb, Vb = to_f64(Kb, dtype), to_f64(Vb, dtype)
+        Kb, Vb = to_f64(Kb, dtype) * ks, to_f64(Vb, dtype) * vs
         for h in range(Hq):
             g = h // G
             s = scale * (Kb[g] @ q[b, h])            # [L]

@@ -1,7 +1,8 @@
 """Paged KV pools: layout, token append, block copy, and the table walk.
 
 Layout (a choice of this library; the pages describe blocks and tables but no
-byte layout).  With ``x = 16 / element_bytes`` (4 for fp32, 8 for fp16/bf16):
+byte layout).  With ``x = 16 / element_bytes`` (4 for fp32, 8 for fp16/bf16,
+16 for the 8-bit code formats):
 
 * K pool: ``[num_blocks][num_kv_heads][head_dim / x][block_size][x]`` —
   element (block b, head h, in-block token t, dim d) sits at
@@ -13,7 +14,8 @@ byte layout).  With ``x = 16 / element_bytes`` (4 for fp32, 8 for fp16/bf16):
 A token at logical position p of a sequence lives in physical block
 ``table[p // bs]`` at in-block offset ``p % bs`` (page 1, section
 「PagedAttentionの解決策」; page 3, section 「用語解説」, block table entry).
-Pools here hold raw stored bits (uint16 for fp16/bf16, uint32 for fp32).
+Pools here hold raw stored bits (uint16 for fp16/bf16, uint32 for fp32, uint8
+for the 8-bit codes of a quantized cache; see quant.py for how codes are made).
 """
 from __future__ import annotations
 
@@ -23,7 +25,8 @@ from .numerics import bits_dtype
 
 
 def x_of(dtype: str) -> int:
-    return 4 if dtype == "f32" else 8
+    """Elements per 16 bytes."""
+    return 16 // np.dtype(bits_dtype(dtype)).itemsize
 
 
 def k_offset(b, h, t, d, H, D, bs, x):

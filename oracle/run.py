@@ -17,6 +17,7 @@ from .allocator import AllocatorModel
 from .attention import decode_ref
 from .cache import append_ref, copy_ref, new_pools
 from .numerics import bits_of, to_f64
+from .quant import dequantize_ref, quantize_ref
 
 
 def run_script(am: AllocatorModel, script, rows, on_write=None, on_copy=None):
@@ -53,11 +54,16 @@ def run_case(case, with_pools=True, decode=True, pool_fill=0):
     """
     am = AllocatorModel(case.num_blocks, case.block_size, case.free_order)
     res = {}
+    cd = getattr(case, "cache_dtype", None)
     if with_pools:
         kp, vp = new_pools(case.num_blocks, case.num_kv_heads, case.head_dim, case.block_size,
-                           case.dtype, fill=pool_fill)
+                           cd or case.dtype, fill=pool_fill)
         kb = bits_of(case.k_tok, case.dtype)
         vb = bits_of(case.v_tok, case.dtype)
+        if cd is not None:
+            # a quantized cache stores the codes of the token rows
+            kb = quantize_ref(kb, case.dtype, cd, case.k_scale)
+            vb = quantize_ref(vb, case.dtype, cd, case.v_scale)
 
         def on_write(slots, rws):
             append_ref(kp, vp, kb[rws], vb[rws], slots, case.block_size)
@@ -83,7 +89,9 @@ def run_case(case, with_pools=True, decode=True, pool_fill=0):
         res["k_pool"], res["v_pool"] = kp, vp
         if decode:
             res["out"] = decode_ref(bits_of(case.q, case.dtype), kp, vp, tables, lens,
-                                    case.dtype, case.scale, case.block_size)
+                                    cd or case.dtype, case.scale, case.block_size,
+                                    q_dtype=case.dtype, k_scale=case.k_scale,
+                                    v_scale=case.v_scale)
     return res
 
 
@@ -101,6 +109,12 @@ def oracle_sequence_out(case, i):
     idx = torch.as_tensor(rws, device=case.k_tok.device)
     K = to_f64(bits_of(case.k_tok.index_select(0, idx), case.dtype), case.dtype)  # [L][Hkv][D]
     V = to_f64(bits_of(case.v_tok.index_select(0, idx), case.dtype), case.dtype)
+    cd = getattr(case, "cache_dtype", None)
+    if cd is not None:
+        K = dequantize_ref(quantize_ref(bits_of(case.k_tok.index_select(0, idx), case.dtype),
+                                        case.dtype, cd, case.k_scale), cd, case.k_scale)
+        V = dequantize_ref(quantize_ref(bits_of(case.v_tok.index_select(0, idx), case.dtype),
+                                        case.dtype, cd, case.v_scale), cd, case.v_scale)
     q = to_f64(bits_of(case.q[i], case.dtype), case.dtype)                         # [Hq][D]
     G = Hq // case.num_kv_heads
     out = np.empty((Hq, D))

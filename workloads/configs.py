@@ -21,14 +21,15 @@ consumers read the same stored bits.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 import math
 
 import numpy as np
 import torch
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-ELT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+ELT_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "i8": 1}
+CODE_MAX = {"i8": 127.0, "fp8": 448.0}     # largest code magnitude of the 8-bit formats
 
 CONFIG_NAMES = ("tiny_fp32", "llama3_8b_bf16", "opt13b_fp16", "cow_parallel_bf16",
                 "long_context_bf16")
@@ -53,6 +54,17 @@ class Case:
     v_tok: torch.Tensor             # [R][Hkv][D] in the KV dtype
     partition_size: int = 0         # 0 = let the library choose
     notes: dict = field(default_factory=dict)
+    # quantized cache: pools hold 8-bit codes ("i8" / "fp8") of the token rows
+    # (which stay in ``dtype``, as do q and the step's new tokens), K = code *
+    # k_scale, V = code * v_scale.  None: pools hold ``dtype`` itself.
+    cache_dtype: str | None = None
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def kv_dtype(self) -> str:
+        """dtype of the pools' elements."""
+        return self.cache_dtype or self.dtype
 
     @property
     def num_seqs(self) -> int:
@@ -64,7 +76,7 @@ class Case:
 
     @property
     def elt_bytes(self) -> int:
-        return ELT_BYTES[self.dtype]
+        return ELT_BYTES[self.kv_dtype]
 
     def kv_bytes(self) -> int:
         """Logical K+V bytes one decode step reads: sum(L) * Hkv * 2 * D * elt."""
@@ -75,6 +87,20 @@ class Case:
         """Token row written by this step's append, per batch entry."""
         return np.array([self.rows[int(s)][int(L) - 1] for s, L in zip(self.batch, self.lens)],
                         dtype=np.int64)
+
+
+def quantized(case: Case, cache_dtype: str) -> Case:
+    """The same workload over a quantized cache: per-pool scales calibrated on
+    the drawn token rows (largest |value| maps to the format's largest code,
+    computed in fp32)."""
+    if cache_dtype not in CODE_MAX:
+        raise KeyError(cache_dtype)
+    amax_k = float(case.k_tok.abs().max().float())
+    amax_v = float(case.v_tok.abs().max().float())
+    ks = float(np.float32(amax_k) / np.float32(CODE_MAX[cache_dtype]))
+    vs = float(np.float32(amax_v) / np.float32(CODE_MAX[cache_dtype]))
+    name = case.name.rsplit("_", 1)[0] + "_" + cache_dtype + "kv"
+    return replace(case, name=name, cache_dtype=cache_dtype, k_scale=ks, v_scale=vs)
 
 
 def _draw_values(seed: int, nq: tuple, nkv: tuple, dtype: str, device, q_std: float = 1.0,
