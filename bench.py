@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--prefill", action="store_true",
                     help="measure pa_prefill instead (chunked prefill, Llama-3-8B heads: "
                          "16 sequences of 2048 tokens, the last 512 as the chunk)")
+    ap.add_argument("--kv-cache", choices=("fp8", "i8"), default=None,
+                    help="quantized cache: the same workload with 8-bit K/V codes (FP8 E4M3 "
+                         "or INT8, per-pool scales); one pa_decode_step_quant per step "
+                         "(quantizing append, attention kernel timed, merge)")
     ap.add_argument("--no-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -123,21 +127,28 @@ def cpu_baseline(case, budget_s: float):
     import numpy as np
     from threadpoolctl import threadpool_limits
 
-    from oracle import append_ref, bits_of, copy_ref, decode_ref, run_case
+    from oracle import append_ref, bits_of, copy_ref, decode_ref, quantize_ref, run_case
     cores = len(os.sched_getaffinity(0))
+    cd = case.cache_dtype
     with threadpool_limits(limits=cores):
         ref = run_case(case, decode=False)               # set-up state (not timed)
         kp, vp = ref["k_pool"], ref["v_pool"]
-        kb, vb = bits_of(case.k_tok, case.dtype), bits_of(case.v_tok, case.dtype)
         nr = case.new_rows()
+        kb, vb = bits_of(case.k_tok[nr], case.dtype), bits_of(case.v_tok[nr], case.dtype)
         qb = bits_of(case.q, case.dtype)
         times, t_end = [], time.perf_counter() + budget_s
         while not times or time.perf_counter() < t_end:
             t0 = time.perf_counter()
             copy_ref(kp, vp, ref["step_cows"])
-            append_ref(kp, vp, kb[nr], vb[nr], ref["step_slots"], case.block_size)
-            decode_ref(qb, kp, vp, ref["tables"], ref["lens"], case.dtype, case.scale,
-                       case.block_size)
+            if cd is None:
+                append_ref(kp, vp, kb, vb, ref["step_slots"], case.block_size)
+            else:     # quantizing append of the new tokens
+                append_ref(kp, vp, quantize_ref(kb, case.dtype, cd, case.k_scale),
+                           quantize_ref(vb, case.dtype, cd, case.v_scale), ref["step_slots"],
+                           case.block_size)
+            decode_ref(qb, kp, vp, ref["tables"], ref["lens"], case.kv_dtype, case.scale,
+                       case.block_size, q_dtype=case.dtype, k_scale=case.k_scale,
+                       v_scale=case.v_scale)
             times.append(time.perf_counter() - t0)
     sec = float(np.mean(times))
     return {"value": round(case.kv_bytes() / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
@@ -271,18 +282,25 @@ def main():
     from paged_kv_cache_212_amd._lib import check, lib
     from paged_kv_cache_212_amd.ops import pa_dtype
     from workloads import make_case
+    from workloads.configs import quantized
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     case = make_case(args.workload, device=dev)
+    quant = args.kv_cache is not None
+    if quant:
+        case = quantized(case, args.kv_cache)
     P = case.partition_size if args.partition_size is None else args.partition_size
     td = case.k_tok.dtype
+    pool_td = {"fp8": torch.float8_e4m3fn, "i8": torch.int8}.get(args.kv_cache, td)
     print(f"[bench] {case.name}: B={case.num_seqs} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
-          f"D={case.head_dim} {case.dtype} sumL={int(case.lens.sum())} "
+          f"D={case.head_dim} {case.kv_dtype} sumL={int(case.lens.sum())} "
           f"blocks={case.num_blocks}", file=sys.stderr, flush=True)
 
     cache = pk.PagedKVCache(case.num_blocks, case.num_kv_heads, case.head_dim, td, dev,
-                            free_order=case.free_order, fill=0.0)
+                            free_order=case.free_order, fill=0,
+                            cache_dtype=pool_td if quant else None, k_scale=case.k_scale,
+                            v_scale=case.v_scale)
     cache.replay(case.script, case.rows, case.k_tok, case.v_tok)
     # host reservation for the step (C++ block manager), timed on its own on a
     # replica manager: slots + copy pairs + block-table export for the batch
@@ -318,17 +336,27 @@ def main():
     B, Hq, D = q.shape
     Hkv, N = case.num_kv_heads, case.num_blocks
     MB = plan.tables.shape[1]
-    ws = pk.ops.decode_workspace(B, Hq, Hkv, D, plan.max_context_len, P, td, dev)
-    P_used = pk.ops.decode_partition_size(B, Hq, Hkv, D, plan.max_context_len, P, td)
+    ws = pk.ops.decode_workspace(B, Hq, Hkv, D, plan.max_context_len, P, pool_td, dev)
+    P_used = pk.ops.decode_partition_size(B, Hq, Hkv, D, plan.max_context_len, P, pool_td)
     ncow = int(plan.cows.shape[0])
     torch.cuda.synchronize()
 
     # Pre-bound C calls: the loop below only issues launches.
     L = lib()
-    dt = pa_dtype(td)
+    dt = pa_dtype(pool_td)
     stream = torch.cuda.current_stream().cuda_stream
     calls = []
     for kp, vp in layers:
+        if quant:
+            # pa_decode_step_quant: quantizing append + attention (+ merge)
+            dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), k_new.data_ptr(),
+                   v_new.data_ptr(), plan.d_slots.data_ptr(), plan.d_tables.data_ptr(),
+                   plan.d_lens.data_ptr(), B, Hq, Hkv, D, 16, N, MB, plan.max_context_len,
+                   case.scale, P, dt, case.k_scale, case.v_scale, ws.data_ptr(), ws.numel(),
+                   stream)
+            calls.append(((kp.data_ptr(), vp.data_ptr(), plan.d_cows.data_ptr(), ncow, N, Hkv,
+                           D, 16, dt, stream), dec, None, None))
+            continue
         # pa_decode_step: append of the step's tokens + attention (+ merge)
         dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), k_new.data_ptr(),
                v_new.data_ptr(), plan.d_slots.data_ptr(), plan.d_tables.data_ptr(),
@@ -347,11 +375,18 @@ def main():
     f_step_part, f_step_merge = L.pa_decode_step_partial, L.pa_decode_step_merge
     f_app, f_part, f_merge = L.pa_cache_append, L.pa_decode_partial, L.pa_decode_merge
     f_time = L.pa_time_next_attention
+    f_step_quant = L.pa_decode_step_quant
+    mode = "quant" if quant else args.mode
 
     def step(i, ev=None, with_copy=True):
         c_copy, c_dec, c_app, c_dec_sep = calls[i % len(calls)]
         if ncow and with_copy:
             check(f_copy(*c_copy), "pa_copy_blocks")
+        if mode == "quant":
+            if ev is not None:
+                check(f_time(ev[0].cuda_event, ev[1].cuda_event), "pa_time_next_attention")
+            check(f_step_quant(*c_dec), "pa_decode_step_quant")
+            return
         if args.mode == "step":
             if ev is not None:
                 ev[0].record()
@@ -419,14 +454,17 @@ def main():
             f = np.full(nb, 16, dtype=np.int64)
             f[-1] = int(L_i) - 16 * (nb - 1)
             np.maximum.at(fill, plan.tables[b_i, :nb], f)
-    kv_unique = int(fill.sum()) * Hkv * 2 * D * q.element_size()
+    kv_unique = int(fill.sum()) * Hkv * 2 * D * case.elt_bytes
     stream_ctx = stream_read_context(torch, dev)
     res = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": case.dtype, "data": "synthetic",
            "config": {"workload": f"{case.name}: one decode step, B={B}, Hq={Hq}, Hkv={Hkv}, "
-                                  f"D={D}, block 16, {case.dtype} KV, fp32 out",
+                                  f"D={D}, block 16, "
+                                  + (f"{case.kv_dtype} KV codes (per-pool scales, widened "
+                                     f"to bf16 on the matrix cores)" if quant else
+                                     f"{case.dtype} KV") + ", fp32 out",
                       "global_batch": B, "context_tokens": int(case.lens.sum()),
                       "max_context_len": plan.max_context_len, "partition_size": P_used,
                       "cow_copies": ncow, "layers_rotated": args.layers,
@@ -445,7 +483,7 @@ def main():
         part_ms = dec_ms = float(kern_us.mean()) * 1e-3
         res["attention_kernel_us_p10_p50_p90"] = [round(float(x), 3) for x in
                                                   np.percentile(kern_us, [10, 50, 90])]
-        if args.mode != "step":
+        if mode != "step":
             # start-to-start of consecutive attention kernels: one step each
             per = np.array([evs[i][0].elapsed_time(evs[i + 1][0])
                             for i in range(len(evs) - 1)]) * 1e3
@@ -456,11 +494,14 @@ def main():
         # the fp32 output; in the phased step the kernel also reads the new
         # tokens (k_new, v_new) and the slot indices
         alg = kv_bytes + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
-        if args.mode == "phased":
+        if mode == "phased":
             alg += 2 * k_new.numel() * k_new.element_size() + B * 8
         achieved = alg / (part_ms * 1e-3) / 1e9
         res["attention_kernel_us"] = round(dec_ms * 1e3, 3)
-        if args.mode == "separate":
+        if mode == "quant":
+            kname = (f"attention kernel of pa_decode_step_quant ({case.kv_dtype} codes; the "
+                     f"quantizing append is its own kernel)")
+        elif mode == "separate":
             kname = "attention partition kernel (pa_decode_partial)"
         elif args.mode == "phased":
             kname = "attention kernel of pa_decode_step_partial (new tokens fused in)"

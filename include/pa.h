@@ -72,7 +72,21 @@ typedef enum pa_status {
   PA_ERR_WORKSPACE = 7      /* decode workspace missing or too small            */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* Element dtypes.  PA_FP8_E4M3 and PA_INT8 are the 8-bit codes of a
+ * quantized cache (one byte per element; value = code * the pool's scale):
+ *   PA_FP8_E4M3: OCP 8-bit float E4M3 (sign, 4 exponent bits with bias 7,
+ *     3 mantissa bits; 0x7F/0xFF are NaN; no infinity; largest finite 448);
+ *   PA_INT8: two's-complement integer.
+ * Page 1 (jisaku.com glossary, section 「他のKVキャッシュ最適化との組み合わせ」)
+ * pairs paging with an INT8 cache, half the size per block; E4M3 is the
+ * 8-bit float the target GPU converts natively. */
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3,
+  PA_INT8 = 4
+} pa_dtype;
 
 /* Message for the last error on the calling thread ("" if none). */
 const char* pa_last_error(void);
@@ -149,13 +163,32 @@ pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out);
 /* Writes token i's K and V (all heads, bit for bit, no conversion) into slot
  * slot_mapping[i] of the pools (page 3, section 「KV キャッシュマネージャ」:
  * generated tokens go into the sequence's last block).
- *   k_new, v_new: device [num_tokens][Hkv][D]; slot_mapping: device int64
+ *   k_new, v_new: device [num_tokens][Hkv][D] in the pool dtype (for the
+ *   8-bit dtypes: codes, moved as bytes); slot_mapping: device int64
  *   [num_tokens], -1 = skip; slots outside [0, num_blocks*block_size) skipped.
  * Supported: block_size 16, head_dim a multiple of 16 in [16, 256]. */
 pa_status pa_cache_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                           const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           pa_dtype dtype, void* stream);
+
+/* pa_cache_append for a quantized cache: k_new/v_new ([num_tokens][Hkv][D],
+ * device, in src_dtype: PA_F32, PA_F16 or PA_BF16) are encoded into the
+ * codes of cache_dtype (PA_FP8_E4M3 or PA_INT8) with one scale per pool
+ * (K element = code * k_scale, V element = code * v_scale):
+ *   y = fp32(x * r), r = 1/scale rounded to fp32 (computed on the host);
+ *   PA_INT8: code = y rounded half to even, clamped to [-127, 127];
+ *   PA_FP8_E4M3: code = y clamped to [-448, 448], rounded to the nearest
+ *     E4M3 value, ties to the even code; the sign is kept (-0 -> 0x80).
+ * Scale granularity and rounding are not fixed by page 1 (jisaku.com
+ * glossary, section 「他のKVキャッシュ最適化との組み合わせ」); these are the
+ * library's.  Inputs must be finite.  Scales must be positive and finite
+ * (PA_ERR_INVALID_ARG otherwise).  Slots as for pa_cache_append. */
+pa_status pa_cache_append_quant(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, int32_t num_tokens,
+                                int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, pa_dtype cache_dtype, pa_dtype src_dtype,
+                                float k_scale, float v_scale, void* stream);
 
 /* Copy-on-write: for each pair (src, dst) of block_pairs (device int32
  * [num_pairs][2]), block dst := block src in both pools, all heads, bit for
@@ -168,8 +201,8 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
 /* How pa_decode splits contexts for these arguments; partition_size is
  *   > 0 (a multiple of 16): fixed partitions of that many tokens;
  *   0: the library's choice: the even split on the matrix-core path
- *      (fp16/bf16), fixed partitions of 256 tokens for fp32 and the plain-FMA
- *      kernel;
+ *      (fp16/bf16 and the 8-bit dtypes), fixed partitions of 256 tokens for
+ *      fp32 and the plain-FMA kernel;
  *   -1: the even split (matrix-core path only; fp32 and the plain-FMA kernel
  *       use 256-token partitions).
  * Returns the partition size in tokens for fixed partitions, 0 for the even
@@ -208,7 +241,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * Supported: block_size 16; head_dim 64 or 128; Hq a multiple of Hkv with
  * G = Hq/Hkv <= 16.  fp16/bf16 run on the matrix cores, fp32 on plain FMAs;
  * setting the environment variable PA_DECODE_KERNEL=generic makes fp16/bf16
- * use the plain-FMA kernel too (read on every call). */
+ * use the plain-FMA kernel too (read on every call).  8-bit pools are
+ * attended by pa_decode_quant (PA_ERR_INVALID_ARG here). */
 pa_status pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -322,8 +356,45 @@ pa_status pa_prefill(float* out, const void* q, const void* k_pool, const void* 
                      int32_t max_context_len, int32_t max_query_len, float scale,
                      pa_dtype dtype, void* stream);
 
+/* Decode attention over a quantized cache (pools of PA_FP8_E4M3 or
+ * PA_INT8 codes written by pa_cache_append_quant): pa_decode's result with
+ * K_b[t] = k_scale * code and V_b[t] = v_scale * code (page 1, jisaku.com
+ * glossary, section 「他のKVキャッシュ最適化との組み合わせ」: an INT8 cache
+ * halves the bytes per block).  q is bf16 [num_seqs][Hq][D]; the codes are
+ * widened exactly to bf16 on the matrix cores; k_scale is folded into the
+ * softmax scale (fp32 product scale * k_scale) and v_scale into the output.
+ * Other arguments, the workspace and the bounds checks as for pa_decode.
+ * Supported: block_size 16, head_dim 64 or 128, G = Hq/Hkv <= 4
+ * (PA_ERR_UNSUPPORTED otherwise); the 16-bit-only plain-FMA switch
+ * (PA_DECODE_KERNEL) does not apply. */
+pa_status pa_decode_quant(float* out, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                          int32_t partition_size, pa_dtype cache_dtype, float k_scale,
+                          float v_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step over a quantized cache: pa_cache_append_quant(k_pool,
+ * v_pool, k_new, v_new, slot_mapping, num_seqs, ..., cache_dtype, PA_BF16,
+ * k_scale, v_scale) followed by pa_decode_quant(...) on the same stream
+ * (k_new/v_new: bf16 [num_seqs][Hkv][D], sequence b's token at position
+ * context_lens[b] - 1; slot -1 skips the write).  Copy-on-write copies of
+ * the step must be issued before this call on the same stream. */
+pa_status pa_decode_step_quant(float* out, const void* q, void* k_pool, void* v_pool,
+                               const void* k_new, const void* v_new,
+                               const int64_t* slot_mapping, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                               int32_t partition_size, pa_dtype cache_dtype, float k_scale,
+                               float v_scale, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Measurement hook: the next attention kernel launched by a decode call
- * (pa_decode, pa_decode_partial, pa_decode_step or pa_decode_step_partial)
+ * (pa_decode, pa_decode_partial, pa_decode_step, pa_decode_step_partial,
+ * pa_decode_quant or pa_decode_step_quant)
  * on this host thread records start_event when it starts executing and
  * stop_event when it finishes, attached to the kernel's own dispatch, so
  * hipEventElapsedTime(start, stop) is that kernel's duration.  The events are
@@ -342,8 +413,10 @@ pa_status pa_time_next_attention(void* start_event, void* stop_event);
 pa_status pa_stream_read(const void* buf, size_t bytes, int32_t* sink, void* stream);
 
 /* Reassembles the logically contiguous cache through the block tables:
- * k_out/v_out device [num_seqs][Hkv][max_context_len][D] in the KV dtype,
- * positions >= context_lens[b] zero-filled.  Uses the same table walk as
+ * k_out/v_out device [num_seqs][Hkv][max_context_len][D] in the KV dtype
+ * (codes for the 8-bit dtypes), positions >= context_lens[b] zero-filled,
+ * positions of a bad length or table entry all-ones bits (NaN for the float
+ * dtypes).  Uses the same table walk as
  * pa_decode; meant for checks and for handing a sequence to dense code. */
 pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, const int32_t* context_lens,

@@ -16,7 +16,7 @@ PA_ERR_UNKNOWN_SEQ, PA_ERR_SEQ_EXISTS, PA_ERR_HIP, PA_ERR_WORKSPACE = 4, 5, 6, 7
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
                 3: "PA_ERR_OUT_OF_BLOCKS", 4: "PA_ERR_UNKNOWN_SEQ", 5: "PA_ERR_SEQ_EXISTS",
                 6: "PA_ERR_HIP", 7: "PA_ERR_WORKSPACE"}
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3, 4
 
 
 class PAError(RuntimeError):
@@ -52,6 +52,8 @@ SIGNATURES = {
     "pa_bm_stats": (C.c_int, [_vp, C.POINTER(BmStats)]),
     "pa_cache_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int,
                                   _vp]),
+    "pa_cache_append_quant": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        C.c_int, C.c_int, _f32, _f32, _vp]),
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, C.c_int]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, C.c_int]),
@@ -70,6 +72,12 @@ SIGNATURES = {
     "pa_decode_step_merge": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, C.c_int,
                                        _vp, _sz, _vp]),
+    "pa_decode_quant": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _i32, _i32, _f32, _i32, C.c_int, _f32, _f32, _vp, _sz,
+                                  _vp]),
+    "pa_decode_step_quant": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                       _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, C.c_int,
+                                       _f32, _f32, _vp, _sz, _vp]),
     "pa_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                              _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp]),
     "pa_time_next_attention": (C.c_int, [_vp, _vp]),

@@ -31,10 +31,18 @@ class StepPlan:
 
 class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
-                 device="cuda", free_order=None, fill=None):
+                 device="cuda", free_order=None, fill=None, cache_dtype=None, k_scale=1.0,
+                 v_scale=1.0):
+        """dtype: the dtype of the K/V rows written and of q.  cache_dtype
+        (torch.float8_e4m3fn or torch.int8): a quantized cache whose pools hold
+        codes with K = code * k_scale, V = code * v_scale (q, k/v rows: bf16)."""
         self.bm = BlockManager(num_blocks, BLOCK_SIZE, free_order)
-        self.k_pool, self.v_pool = ops.new_pools(num_blocks, num_kv_heads, head_dim, dtype,
-                                                 device, fill)
+        if cache_dtype is not None and cache_dtype not in ops.CODE_DTYPES:
+            raise ValueError("cache_dtype must be torch.float8_e4m3fn or torch.int8")
+        self.cache_dtype = cache_dtype
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.k_pool, self.v_pool = ops.new_pools(num_blocks, num_kv_heads, head_dim,
+                                                 cache_dtype or dtype, device, fill)
         self.num_blocks, self.num_kv_heads, self.head_dim = num_blocks, num_kv_heads, head_dim
         self.dtype, self.device = dtype, torch.device(device)
 
@@ -43,7 +51,12 @@ class PagedKVCache:
 
     # -- sequence set-up ----------------------------------------------------
     def write(self, slots: np.ndarray, k: torch.Tensor, v: torch.Tensor):
-        if len(slots):
+        if not len(slots):
+            return
+        if self.cache_dtype is not None:
+            ops.cache_append_quant(self.k_pool, self.v_pool, k.contiguous(), v.contiguous(),
+                                   self._d(slots.astype(np.int64)), self.k_scale, self.v_scale)
+        else:
             ops.cache_append(self.k_pool, self.v_pool, k.contiguous(), v.contiguous(),
                              self._d(slots.astype(np.int64)))
 
@@ -106,11 +119,26 @@ class PagedKVCache:
         """Copy-on-write, append the new tokens, then decode attention (all on device).
 
         fused: True -> one pa_decode_step call; "phased" -> pa_decode_step_partial
-        then pa_decode_step_merge; False -> pa_cache_append then pa_decode."""
+        then pa_decode_step_merge; False -> pa_cache_append then pa_decode.  A
+        quantized cache: pa_decode_step_quant (fused) or pa_cache_append_quant
+        then pa_decode_quant (False)."""
         if plan.cows.shape[0]:
             ops.copy_blocks(self.k_pool, self.v_pool, plan.d_cows, stream)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if self.cache_dtype is not None:
+            if fused:
+                ops.decode_step_quant(out, q, self.k_pool, self.v_pool, k_new, v_new,
+                                      plan.d_slots, plan.d_tables, plan.d_lens,
+                                      plan.max_context_len, self.k_scale, self.v_scale, scale,
+                                      partition_size, workspace, stream)
+            else:
+                ops.cache_append_quant(self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
+                                       self.k_scale, self.v_scale, stream)
+                ops.decode_quant(out, q, self.k_pool, self.v_pool, plan.d_tables, plan.d_lens,
+                                 plan.max_context_len, self.k_scale, self.v_scale, scale,
+                                 partition_size, workspace, stream)
+            return out
         if fused == "phased":
             B, Hq, D = q.shape
             if workspace is None:

@@ -2,12 +2,16 @@
 // sequence's last block), copy-on-write block copy, and the table-walk gather.
 //
 // All three are pure bit moves (no dtype conversion), so their results are
-// exact.  Append follows page 3 (abeam.tech review), section
+// exact; the quantizing append encodes 16-bit/fp32 values into the 8-bit
+// codes of a quantized cache (page 1, jisaku.com glossary, section
+// 「他のKVキャッシュ最適化との組み合わせ」).  Append follows page 3 (abeam.tech review), section
 // 「KV キャッシュマネージャ」: new tokens fill the sequence's last block; copy
 // follows the same page, section 「用語解説」 (Copy-on-Write): a shared block is
 // duplicated before it is written; the gather follows the block table in
 // logical order (page 1, jisaku.com glossary, section 「PagedAttentionの解決策」).
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 
 #include "pa_device.h"
 
@@ -45,6 +49,70 @@ __global__ __launch_bounds__(256) void append_kernel(typename T::bits* __restric
   for (int e = threadIdx.x; e < nelem; e += blockDim.x) {
     const int h = e / D, d = e % D;
     vpool[tile_base(blk, h, Hkv, D) + v_elem<T>(t, d, D)] = vsrc[e];
+  }
+}
+
+// Encoders of the quantized cache (r = the fp32 reciprocal of the pool's
+// scale): y = x * r in one fp32 rounding, then
+//   I8:   round half to even, clamp to [-127, 127], two's complement byte;
+//   E4M3: clamp to [-448, 448] (the largest finite code), then the hardware
+//         conversion, which rounds to nearest even and keeps the sign.
+template <typename Code>
+struct Encode;
+template <>
+struct Encode<I8> {
+  __device__ static inline uint32_t pair(float a, float b, float r) {
+    const int ca = static_cast<int>(fminf(fmaxf(rintf(a * r), -127.f), 127.f));
+    const int cb = static_cast<int>(fminf(fmaxf(rintf(b * r), -127.f), 127.f));
+    return (static_cast<uint32_t>(ca) & 0xFFu) | ((static_cast<uint32_t>(cb) & 0xFFu) << 8);
+  }
+};
+template <>
+struct Encode<E4M3> {
+  __device__ static inline uint32_t pair(float a, float b, float r) {
+    const float ya = fminf(fmaxf(a * r, -448.f), 448.f);
+    const float yb = fminf(fmaxf(b * r, -448.f), 448.f);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, 0, false)) & 0xFFFFu;
+  }
+};
+
+// Quantizing append: one workgroup per new token.  K: each thread encodes 16
+// consecutive dims of one head (one 16-byte chunk of the pool); V: one byte
+// per element (a V chunk holds 16 tokens of one dim).
+template <typename Src, typename Code>
+__global__ __launch_bounds__(256) void append_quant_kernel(uint8_t* __restrict__ kpool,
+                                                           uint8_t* __restrict__ vpool,
+                                                           const typename Src::bits* __restrict__ knew,
+                                                           const typename Src::bits* __restrict__ vnew,
+                                                           const int64_t* __restrict__ slots,
+                                                           int64_t num_slots_total, int Hkv, int D,
+                                                           float rk, float rv) {
+  using bits = typename Src::bits;
+  const int64_t i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots_total) return;
+  const int64_t blk = slot / kBlockSize;
+  const int t = static_cast<int>(slot % kBlockSize);
+  const int chunks_per_head = D / 16;
+  const bits* ksrc = knew + i * Hkv * static_cast<int64_t>(D);
+  const bits* vsrc = vnew + i * Hkv * static_cast<int64_t>(D);
+  for (int c = threadIdx.x; c < Hkv * chunks_per_head; c += blockDim.x) {
+    const int h = c / chunks_per_head, ch = c % chunks_per_head;
+    const bits* x = ksrc + static_cast<int64_t>(h) * D + ch * 16;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = Encode<Code>::pair(Src::to_float(x[4 * j]), Src::to_float(x[4 * j + 1]), rk);
+      const uint32_t hi = Encode<Code>::pair(Src::to_float(x[4 * j + 2]), Src::to_float(x[4 * j + 3]), rk);
+      w[j] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(kpool + tile_base(blk, h, Hkv, D) + (ch * kBlockSize + t) * 16) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
+    const int h = e / D, d = e % D;
+    const uint32_t code = Encode<Code>::pair(Src::to_float(vsrc[e]), 0.f, rv) & 0xFFu;
+    vpool[tile_base(blk, h, Hkv, D) + v_elem<U8>(t, d, D)] = static_cast<uint8_t>(code);
   }
 }
 
@@ -122,7 +190,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const i32x4_t* __restr
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 pa_status check_common(const char* fn, int num_blocks, int Hkv, int D, int bs, pa_dtype dt) {
-  if (!dtype_ok(dt)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  if (!pool_dtype_ok(dt)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
   if (bs != kBlockSize)
     return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, bs);
   if (num_blocks <= 0 || Hkv <= 0 || D <= 0)
@@ -189,8 +257,59 @@ extern "C" pa_status pa_cache_append(void* k_pool, void* v_pool, const void* k_n
           static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
           total, num_kv_heads, head_dim);
       break;
+    case PA_FP8_E4M3:
+    case PA_INT8:
+      append_kernel<U8><<<grid, block, 0, s>>>(
+          static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+          static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new), slot_mapping,
+          total, num_kv_heads, head_dim);
+      break;
   }
   return launch_status("pa_cache_append");
+}
+
+extern "C" pa_status pa_cache_append_quant(void* k_pool, void* v_pool, const void* k_new,
+                                           const void* v_new, const int64_t* slot_mapping,
+                                           int32_t num_tokens, int32_t num_blocks,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, pa_dtype cache_dtype,
+                                           pa_dtype src_dtype, float k_scale, float v_scale,
+                                           void* stream) {
+  const char* fn = "pa_cache_append_quant";
+  pa_status st = check_common(fn, num_blocks, num_kv_heads, head_dim, block_size, cache_dtype);
+  if (st != PA_OK) return st;
+  if (!code_dtype(cache_dtype))
+    return fail(PA_ERR_INVALID_ARG, "%s: cache dtype %d is not an 8-bit code dtype", fn,
+                (int)cache_dtype);
+  if (!dtype_ok(src_dtype))
+    return fail(PA_ERR_INVALID_ARG, "%s: source dtype %d (fp32, fp16 or bf16)", fn,
+                (int)src_dtype);
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_INVALID_ARG, "%s: scales must be positive and finite", fn);
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_tokens < 0", fn);
+  if (num_tokens == 0) return ok();
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(k_pool)) return fail(PA_ERR_INVALID_ARG, "%s: k_pool must be 16-byte aligned", fn);
+  // the reciprocals, rounded once to fp32 on the host
+  const float rk = 1.0f / k_scale, rv = 1.0f / v_scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t total = static_cast<int64_t>(num_blocks) * kBlockSize;
+  dim3 grid(num_tokens), block(256);
+  uint8_t* kp = static_cast<uint8_t*>(k_pool);
+  uint8_t* vp = static_cast<uint8_t*>(v_pool);
+#define PA_APPEND_Q(SRC, CODE)                                                                 \
+  append_quant_kernel<SRC, CODE><<<grid, block, 0, s>>>(                                      \
+      kp, vp, static_cast<const SRC::bits*>(k_new), static_cast<const SRC::bits*>(v_new),     \
+      slot_mapping, total, num_kv_heads, head_dim, rk, rv)
+  const bool fp8 = cache_dtype == PA_FP8_E4M3;
+  switch (src_dtype) {
+    case PA_F32: if (fp8) PA_APPEND_Q(F32, E4M3); else PA_APPEND_Q(F32, I8); break;
+    case PA_F16: if (fp8) PA_APPEND_Q(F16, E4M3); else PA_APPEND_Q(F16, I8); break;
+    default: if (fp8) PA_APPEND_Q(BF16, E4M3); else PA_APPEND_Q(BF16, I8); break;
+  }
+#undef PA_APPEND_Q
+  return launch_status(fn);
 }
 
 extern "C" pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
@@ -240,6 +359,8 @@ extern "C" pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_pool,
     case PA_F32: PA_GATHER(F32, uint32_t); break;
     case PA_F16: PA_GATHER(F16, uint16_t); break;
     case PA_BF16: PA_GATHER(BF16, uint16_t); break;
+    case PA_FP8_E4M3:
+    case PA_INT8: PA_GATHER(U8, uint8_t); break;
   }
 #undef PA_GATHER
   return launch_status("pa_gather_kv");

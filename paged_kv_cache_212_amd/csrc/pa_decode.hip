@@ -60,6 +60,7 @@ struct Params {
   int num_blocks, max_blocks, max_ctx;
   int P, maxP;
   float scale_log2;
+  float out_scale;     // factor of the final rows (V scale of a quantized cache, else 1)
 };
 
 __device__ inline bool len_valid(int L, const Params& pr) {
@@ -606,6 +607,43 @@ struct Mfma4<F16> {
   }
 };
 
+// Pool formats of the 4x4x4 engine.  Mma: the matrix op (both operands in
+// its 16-bit type); kCodes: the pool holds 8-bit codes, widened exactly to
+// bf16 before each MFMA (widen: 4 codes of a 32-bit word -> 4 bf16 as the
+// uint2 operand, element order kept).
+template <typename KV>
+struct Kv4 {
+  using Mma = Mfma4<KV>;
+  static constexpr bool kCodes = false;
+};
+// bf16 pair from two floats whose values are bf16 values: their high halves.
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+template <>
+struct Kv4<E4M3> {
+  using Mma = Mfma4<BF16>;
+  static constexpr bool kCodes = true;
+  // every E4M3 value (3 mantissa bits, exponents 2^-9 .. 2^8) is a bf16 value
+  __device__ static inline uint2 widen(uint32_t w) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    return make_uint2(bf16_pair(lo[0], lo[1]), bf16_pair(hi[0], hi[1]));
+  }
+};
+template <>
+struct Kv4<I8> {
+  using Mma = Mfma4<BF16>;
+  static constexpr bool kCodes = true;
+  // integers in [-128, 127] have at most 8 significant bits: bf16 values
+  __device__ static inline uint2 widen(uint32_t w) {
+    const int v = static_cast<int>(w);
+    const float f0 = static_cast<float>((v << 24) >> 24), f1 = static_cast<float>((v << 16) >> 24);
+    const float f2 = static_cast<float>((v << 8) >> 24), f3 = static_cast<float>(v >> 24);
+    return make_uint2(bf16_pair(f0, f1), bf16_pair(f2, f3));
+  }
+};
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -696,9 +734,14 @@ template <typename T, int D>
 __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_begin, int nblk,
                                         int tok_end, WaveState4<D>& st, const Prologue4<D>& pre,
                                         bool with_new) {
-  constexpr int NC = D / 8;    // 16-byte K chunks per token
-  constexpr int NT = D / 64;   // 64-dim output tiles
-  constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
+  using Fmt = Kv4<T>;
+  using Mma = typename Fmt::Mma;
+  constexpr bool kCodes = Fmt::kCodes;
+  constexpr int NC = D * T::kBytes / 16;   // 16-byte K chunks per token
+  constexpr int NT = D / 64;               // 64-dim output tiles
+  constexpr int NH = 16 / T::kVecElems;    // V chunks per (block, dim): 2 (16-bit), 1 (codes)
+  constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * T::kBytes;
+  if constexpr (kCodes) with_new = false;  // 8-bit pools: the append runs on its own
   const int lane = threadIdx.x & 63;
   const int G = pr.G;
   const int nquad = (nblk + 3) >> 2;
@@ -742,7 +785,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   };
 
   uint4 kr[NC];
-  uint4 vr[4][2][NT];
+  uint4 vr[4][NH][NT];
   int ph[4];
   auto issue_k = [&]() {
     const int kb = lane >> 4;
@@ -756,7 +799,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     for (int kb = 0; kb < 4; ++kb) {
       const char* vt = vbase + ph[kb] * block_stride + lane * 16;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           vr[kb][h][t] = load_stream(vt + (h * D + 64 * t) * 16);
@@ -809,7 +852,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
 #pragma unroll
     for (int KB = 0; KB < 4; ++KB)
 #pragma unroll
-      for (int H = 0; H < 2; ++H)
+      for (int H = 0; H < NH; ++H)
         if (KB == kb && H == h) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
@@ -848,7 +891,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
 #pragma unroll
       for (int KB = 0; KB < 4; ++KB)
 #pragma unroll
-        for (int H = 0; H < 2; ++H)
+        for (int H = 0; H < NH; ++H)
           if (KB == kb && H == h) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -872,13 +915,19 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   auto qk_softmax = [&](int qd, uint2& phi, uint2& plo) {
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     unroll<D / 4>([&](auto ic) {
-      constexpr int s = decltype(ic)::value;
-      const uint4& kc = kr[s / 2];
-      const uint2 kv = (s & 1) ? make_uint2(kc.z, kc.w) : make_uint2(kc.x, kc.y);
+      constexpr int s = decltype(ic)::value;   // dims 4s .. 4s+3
+      uint2 kv;
+      if constexpr (kCodes) {
+        const uint4& kc = kr[s / 4];
+        kv = Fmt::widen((s & 3) == 0 ? kc.x : (s & 3) == 1 ? kc.y : (s & 3) == 2 ? kc.z : kc.w);
+      } else {
+        const uint4& kc = kr[s / 2];
+        kv = (s & 1) ? make_uint2(kc.z, kc.w) : make_uint2(kc.x, kc.y);
+      }
       if constexpr (s & 1)
-        s1 = Mfma4<T>::template mma<s % 16>(qr[s / 16], kv, s1);
+        s1 = Mma::template mma<s % 16>(qr[s / 16], kv, s1);
       else
-        s0 = Mfma4<T>::template mma<s % 16>(qr[s / 16], kv, s0);
+        s0 = Mma::template mma<s % 16>(qr[s / 16], kv, s0);
     });
     const int qpos = (blk_begin + 4 * qd) * kBlockSize;   // position of the quad's token 0
     const bool valid = qpos + lane < tok_end;
@@ -904,14 +953,31 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
 #pragma unroll
     for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - st.m_run);
     st.l_lane += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-    Mfma4<T>::split(pe, phi, plo);
+    Mma::split(pe, phi, plo);
   };
 
   // last: the quad may reach past the end of the range (only the range's last
   // quad can)
   auto pv = [&](int qd, uint2 phi, uint2 plo, auto last) {
     const int qpos = (blk_begin + 4 * qd) * kBlockSize;
-    if (decltype(last)::value && qpos + 4 * kBlockSize > tok_end) {
+    if (decltype(last)::value && qpos + 4 * kBlockSize > tok_end && kCodes) {
+      // as below, for 16 one-byte tokens per chunk: byte e of word w is
+      // token 4w + e of the block
+      auto keep = [](int n) -> uint32_t {   // bytes 0 .. n-1 of a word
+        return n >= 4 ? 0xFFFFFFFFu : n <= 0 ? 0u : (1u << (8 * n)) - 1u;
+      };
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int nv = tok_end - (qpos + 16 * kb);   // valid tokens of the block
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          vr[kb][0][t].x &= keep(nv);
+          vr[kb][0][t].y &= keep(nv - 4);
+          vr[kb][0][t].z &= keep(nv - 8);
+          vr[kb][0][t].w &= keep(nv - 12);
+        }
+      }
+    } else if (decltype(last)::value && qpos + 4 * kBlockSize > tok_end) {
       // the quad reaches past the end of the range: zero V of masked
       // positions so unused slots (even NaN) cannot reach the output via 0*v
 #pragma unroll
@@ -925,6 +991,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
           const uint32_t m3 = (nv > 6 ? 0x0000FFFFu : 0u) | (nv > 7 ? 0xFFFF0000u : 0u);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
+            if constexpr (kCodes) continue;
             vr[kb][h][t].x &= m0;
             vr[kb][h][t].y &= m1;
             vr[kb][h][t].z &= m2;
@@ -934,13 +1001,19 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     }
     unroll<16>([&](auto ic) {
       constexpr int a = decltype(ic)::value;   // tokens 4a..4a+3
-      constexpr int kb = a >> 2, h = (a >> 1) & 1;
+      constexpr int kb = a >> 2;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint4& v = vr[kb][h][t];
-        const uint2 vv = (a & 1) ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
-        st.acc[t] = Mfma4<T>::template mma<a>(phi, vv, st.acc[t]);
-        st.acc[t] = Mfma4<T>::template mma<a>(plo, vv, st.acc[t]);
+        uint2 vv;
+        if constexpr (kCodes) {
+          const uint4& v = vr[kb][0][t];
+          vv = Fmt::widen((a & 3) == 0 ? v.x : (a & 3) == 1 ? v.y : (a & 3) == 2 ? v.z : v.w);
+        } else {
+          const uint4& v = vr[kb][(a >> 1) & 1][t];
+          vv = (a & 1) ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
+        }
+        st.acc[t] = Mma::template mma<a>(phi, vv, st.acc[t]);
+        st.acc[t] = Mma::template mma<a>(plo, vv, st.acc[t]);
       }
     });
   };
@@ -1011,7 +1084,7 @@ __device__ __forceinline__ void emit_state4(const Params& pr, int b, int g, int 
       const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), e));
       const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), e));
       const int64_t row = static_cast<int64_t>(b) * pr.Hq + g * G + e;
-      const float inv = 1.0f / lh;
+      const float inv = pr.out_scale / lh;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int d = 64 * t + lane;
@@ -1352,7 +1425,7 @@ __global__ __launch_bounds__(D) void merge_kernel(Params pr) {
       }
     }
   }
-  pr.out[row * D + d] = num / den;
+  pr.out[row * D + d] = (num / den) * pr.out_scale;
 }
 
 // Kernel selection: PA_DECODE_KERNEL=generic forces the plain-FMA kernel for
@@ -1373,10 +1446,13 @@ constexpr int kEvenSplit = -1;          // partition_size value selecting the ev
 
 bool partition_ok(int P) { return P == kEvenSplit || (P >= 0 && P % kBlockSize == 0); }
 
+// query heads per KV head the 4x4x4 engine takes (the only one for 8-bit pools)
+constexpr int kMaxGroupCodes = 4;
+
 bool decode_args_ok(int B, int Hq, int Hkv, int D, int max_ctx, int P, pa_dtype dt) {
   return B >= 0 && B <= 65535 && Hkv > 0 && Hkv <= 65535 && Hq > 0 && Hq % Hkv == 0 &&
-         Hq / Hkv <= kMaxGroup && (D == 64 || D == 128) && max_ctx >= 0 && partition_ok(P) &&
-         dtype_ok(dt);
+         Hq / Hkv <= (code_dtype(dt) ? kMaxGroupCodes : kMaxGroup) && (D == 64 || D == 128) &&
+         max_ctx >= 0 && partition_ok(P) && pool_dtype_ok(dt);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1414,7 +1490,7 @@ struct LaunchPlan {
 
 LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_env) {
   LaunchPlan lp{};
-  lp.generic = dt == PA_F32 || generic_env;
+  lp.generic = dt == PA_F32 || (generic_env && !code_dtype(dt));
   // default (0) on the matrix-core path: the even split
   lp.split = (partition_size == kEvenSplit || partition_size == 0) && !lp.generic;
   if (lp.split) {
@@ -1489,11 +1565,29 @@ void launch_split(const Params& pr, int W, hipStream_t s) {
 
 enum class Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
 
+// 8-bit pools (C = E4M3 or I8): the 4x4x4 engine only (G <= 4), never fused
+// with the append.
+template <typename C, int D>
+void launch_code_phases(const Params& pr, const LaunchPlan& lp, bool first, bool second,
+                        hipStream_t s) {
+  if (lp.split) {
+    if (first) launch_attention(decode_split_kernel<Engine4<C, D>, 2>, lp.W, 64, s, pr);
+    if (second) merge_kernel<D, true><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
+    return;
+  }
+  if (first)
+    launch_attention(decode_fixed_kernel<Engine4<C, D>, false, kFixedWaves4>,
+                     dim3(pr.Hkv * pr.maxP, 1, pr.B), 64, s, pr);
+  if (second && pr.maxP > 1) merge_kernel<D, false><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
+}
+
 template <int D>
 void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph,
                    hipStream_t s) {
   const bool first = static_cast<int>(ph) & static_cast<int>(Phase::kPartitions);
   const bool second = static_cast<int>(ph) & static_cast<int>(Phase::kMerge);
+  if (dt == PA_FP8_E4M3) return launch_code_phases<E4M3, D>(pr, lp, first, second, s);
+  if (dt == PA_INT8) return launch_code_phases<I8, D>(pr, lp, first, second, s);
   if (lp.split) {
     if (first) {
       if (dt == PA_F16)
@@ -1516,7 +1610,9 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
 
 // Whether the partition kernel of this plan appends the step's new tokens
 // itself (pa_decode_step); otherwise pa_cache_append runs first.
-bool fuses_append(const LaunchPlan& lp, int G) { return !lp.generic && (lp.split || G <= 4); }
+bool fuses_append(const LaunchPlan& lp, int G, pa_dtype dt) {
+  return !code_dtype(dt) && !lp.generic && (lp.split || G <= 4);
+}
 
 // Validates the arguments shared by pa_decode / pa_decode_partial /
 // pa_decode_merge and launches the requested phases.
@@ -1525,8 +1621,14 @@ struct NewTokens {
   const void* v_new;
   const int64_t* slots;
 };
+// Scales of a quantized cache (pa_decode_quant / pa_decode_step_quant).
+struct CodeScales {
+  float k_scale;
+  float v_scale;
+};
 
-pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, const void* q,
+pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeScales* cs,
+                     float* out, const void* q,
                      const void* k_pool, const void* v_pool, const int32_t* block_tables,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -1537,7 +1639,20 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, 
   t_armed = TimingEvents{};
   if (block_size != kBlockSize)
     return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, block_size);
-  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (cs == nullptr && code_dtype(dtype))
+    return fail(PA_ERR_INVALID_ARG, "%s: 8-bit pools are attended by pa_decode_quant", fn);
+  if (cs != nullptr && !code_dtype(dtype))
+    return fail(PA_ERR_INVALID_ARG, "%s: cache dtype %d is not an 8-bit code dtype", fn,
+                (int)dtype);
+  if (!pool_dtype_ok(dtype))
+    return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (cs != nullptr && (!(cs->k_scale > 0.f) || !(cs->v_scale > 0.f) ||
+                        !std::isfinite(cs->k_scale) || !std::isfinite(cs->v_scale)))
+    return fail(PA_ERR_INVALID_ARG, "%s: scales must be positive and finite", fn);
+  if (cs != nullptr && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+      num_q_heads / num_kv_heads > kMaxGroupCodes)
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (max %d for 8-bit pools)",
+                fn, num_q_heads / num_kv_heads, kMaxGroupCodes);
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", fn, head_dim);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -1592,7 +1707,10 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, 
   pr.max_ctx = max_context_len;
   pr.P = lp.P;
   pr.maxP = lp.maxP;
-  pr.scale_log2 = scale * kLog2e;
+  // a quantized cache: K = k_scale * code (folded into the softmax scale),
+  // V = v_scale * code (applied to the final rows)
+  pr.scale_log2 = (cs ? scale * cs->k_scale : scale) * kLog2e;
+  pr.out_scale = cs ? cs->v_scale : 1.0f;
   if (need > 0) {
     const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * lp.maxP;
     char* ws = static_cast<char*>(workspace);
@@ -1604,7 +1722,7 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (nt) {
-    if (fuses_append(lp, pr.G)) {
+    if (fuses_append(lp, pr.G, dtype)) {
       // append fused: the attention kernel uses the new tokens; the merge
       // kernel writes them to the pool when a merge kernel runs, else the
       // attention kernel does
@@ -1615,10 +1733,14 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, float* out, 
       pr.vpool_w = const_cast<void*>(v_pool);
       pr.write_new_in_merge = lp.split || lp.maxP > 1;
     } else if (static_cast<int>(ph) & static_cast<int>(Phase::kPartitions)) {
-      const pa_status st = pa_cache_append(const_cast<void*>(k_pool), const_cast<void*>(v_pool),
-                                           nt->k_new, nt->v_new, nt->slots, num_seqs,
-                                           num_blocks, num_kv_heads, head_dim, block_size,
-                                           dtype, stream);
+      const pa_status st =
+          cs ? pa_cache_append_quant(const_cast<void*>(k_pool), const_cast<void*>(v_pool),
+                                     nt->k_new, nt->v_new, nt->slots, num_seqs, num_blocks,
+                                     num_kv_heads, head_dim, block_size, dtype, PA_BF16,
+                                     cs->k_scale, cs->v_scale, stream)
+             : pa_cache_append(const_cast<void*>(k_pool), const_cast<void*>(v_pool), nt->k_new,
+                               nt->v_new, nt->slots, num_seqs, num_blocks, num_kv_heads,
+                               head_dim, block_size, dtype, stream);
       if (st != PA_OK) return st;
     }
   }
@@ -1676,15 +1798,15 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
       partition_size, dtype, workspace, workspace_bytes_given, stream
 
 extern "C" pa_status pa_decode(PA_DECODE_ARGS) {
-  return run_decode("pa_decode", Phase::kBoth, nullptr, PA_DECODE_FWD);
+  return run_decode("pa_decode", Phase::kBoth, nullptr, nullptr, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_partial(PA_DECODE_ARGS) {
-  return run_decode("pa_decode_partial", Phase::kPartitions, nullptr, PA_DECODE_FWD);
+  return run_decode("pa_decode_partial", Phase::kPartitions, nullptr, nullptr, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_merge(PA_DECODE_ARGS) {
-  return run_decode("pa_decode_merge", Phase::kMerge, nullptr, PA_DECODE_FWD);
+  return run_decode("pa_decode_merge", Phase::kMerge, nullptr, nullptr, PA_DECODE_FWD);
 }
 
 #define PA_STEP_ARGS                                                                        \
@@ -1701,15 +1823,45 @@ extern "C" pa_status pa_decode_merge(PA_DECODE_ARGS) {
 
 extern "C" pa_status pa_decode_step(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step", Phase::kBoth, &nt, PA_STEP_FWD);
+  return run_decode("pa_decode_step", Phase::kBoth, &nt, nullptr, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_step_partial(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step_partial", Phase::kPartitions, &nt, PA_STEP_FWD);
+  return run_decode("pa_decode_step_partial", Phase::kPartitions, &nt, nullptr, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_step_merge(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step_merge", Phase::kMerge, &nt, PA_STEP_FWD);
+  return run_decode("pa_decode_step_merge", Phase::kMerge, &nt, nullptr, PA_STEP_FWD);
+}
+
+extern "C" pa_status pa_decode_quant(float* out, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, int32_t partition_size, pa_dtype dtype,
+                                     float k_scale, float v_scale, void* workspace,
+                                     size_t workspace_bytes_given, void* stream) {
+  const CodeScales cs{k_scale, v_scale};
+  return run_decode("pa_decode_quant", Phase::kBoth, nullptr, &cs, PA_DECODE_FWD);
+}
+
+extern "C" pa_status pa_decode_step_quant(float* out, const void* q, void* k_pool, void* v_pool,
+                                          const void* k_new, const void* v_new,
+                                          const int64_t* slot_mapping,
+                                          const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size,
+                                          int32_t num_blocks, int32_t max_blocks_per_seq,
+                                          int32_t max_context_len, float scale,
+                                          int32_t partition_size, pa_dtype dtype, float k_scale,
+                                          float v_scale, void* workspace,
+                                          size_t workspace_bytes_given, void* stream) {
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  const CodeScales cs{k_scale, v_scale};
+  return run_decode("pa_decode_step_quant", Phase::kBoth, &nt, &cs, PA_STEP_FWD);
 }

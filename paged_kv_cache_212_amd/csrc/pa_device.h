@@ -36,6 +36,18 @@ struct BF16 {
   }
 };
 
+// One-byte elements: the 8-bit codes of a quantized cache (value = code *
+// the pool's scale).  U8 moves them as bytes; E4M3 (OCP 8-bit float, 4
+// exponent bits with bias 7, 3 mantissa bits, no infinity) and I8 (two's
+// complement) say how the attention widens them.
+struct U8 {
+  using bits = uint8_t;
+  static constexpr int kBytes = 1;
+  static constexpr int kVecElems = 16;
+};
+struct E4M3 : U8 {};
+struct I8 : U8 {};
+
 // Element offsets inside one (block, kv-head) tile of D*16 elements.
 //   K tile: [D/x][16][x]
 //   V tile: [16/x][D][x]  (tokens 0..x-1 as D rows of x tokens, then the
@@ -54,8 +66,12 @@ __device__ __host__ inline int64_t tile_base(int64_t block, int head, int num_kv
   return (block * num_kv_heads + head) * static_cast<int64_t>(D) * kBlockSize;
 }
 
-inline size_t dtype_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : 2; }
+inline bool code_dtype(pa_dtype dt) { return dt == PA_FP8_E4M3 || dt == PA_INT8; }
+inline size_t dtype_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : code_dtype(dt) ? 1 : 2; }
+// floating-point element dtypes (K/V values stored as they are)
 inline bool dtype_ok(pa_dtype dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+// any pool dtype: values or 8-bit codes
+inline bool pool_dtype_ok(pa_dtype dt) { return dtype_ok(dt) || code_dtype(dt); }
 
 // Converts the state after a launch into a status.
 inline pa_status launch_status(const char* what) {

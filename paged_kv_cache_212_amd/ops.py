@@ -8,10 +8,13 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import PA_BF16, PA_F16, PA_F32, check, lib
+from ._lib import PA_BF16, PA_F16, PA_F32, PA_FP8_E4M3, PA_INT8, check, lib
 
 BLOCK_SIZE = 16
-_DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+_DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+       torch.float8_e4m3fn: PA_FP8_E4M3, torch.int8: PA_INT8}
+# pool dtypes of a quantized cache: 8-bit codes, value = code * the pool's scale
+CODE_DTYPES = (torch.float8_e4m3fn, torch.int8)
 
 
 def pa_dtype(t: torch.dtype) -> int:
@@ -72,6 +75,28 @@ def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
                                 _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                                 _dev(slot_mapping, "slot_mapping"), T, N, H, D, BLOCK_SIZE,
                                 pa_dtype(k_pool.dtype), _stream(stream)), "pa_cache_append")
+
+
+def cache_append_quant(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale, v_scale,
+                       stream=None):
+    """Encode k_new/v_new [T][Hkv][D] (fp32/fp16/bf16) into the 8-bit codes of
+    a quantized pool (float8_e4m3fn or int8) at slots slot_mapping [T]:
+    code = round(x / scale) as pa_cache_append_quant defines it."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    if k_pool.dtype not in CODE_DTYPES:
+        raise ValueError("cache_append_quant needs a float8_e4m3fn or int8 pool")
+    T = k_new.shape[0]
+    if k_new.shape != (T, H, D) or v_new.shape != (T, H, D) or k_new.dtype != v_new.dtype \
+            or k_new.dtype in CODE_DTYPES:
+        raise ValueError("k_new/v_new must be [T][Hkv][D] in fp32, fp16 or bf16")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    check(lib().pa_cache_append_quant(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                      _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                      _dev(slot_mapping, "slot_mapping"), T, N, H, D, BLOCK_SIZE,
+                                      pa_dtype(k_pool.dtype), pa_dtype(k_new.dtype),
+                                      float(k_scale), float(v_scale), _stream(stream)),
+          "pa_cache_append_quant")
 
 
 def copy_blocks(k_pool, v_pool, block_pairs, stream=None):
@@ -141,6 +166,77 @@ def decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, 
                           int(partition_size), pa_dtype(q.dtype), _dev(workspace, "workspace"),
                           workspace.numel() * workspace.element_size(), _stream(stream)),
           fn)
+    return out
+
+
+def _check_decode_args(out, q, k_pool, block_tables, context_lens, D, q_dtype):
+    B, Hq = q.shape[0], q.shape[1]
+    if q.shape != (B, Hq, D) or q.dtype != q_dtype:
+        raise ValueError(f"q must be [B][Hq][D] in {q_dtype}")
+    if out.shape != (B, Hq, D) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [B][Hq][D]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    return B, Hq
+
+
+def decode_quant(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, k_scale,
+                 v_scale, scale=None, partition_size=0, workspace=None, stream=None):
+    """Decode attention over a quantized cache (pa_decode_quant): q bf16
+    [B][Hq][D], pools of float8_e4m3fn or int8 codes with K = code * k_scale,
+    V = code * v_scale."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    if k_pool.dtype not in CODE_DTYPES:
+        raise ValueError("decode_quant needs a float8_e4m3fn or int8 pool")
+    B, Hq = _check_decode_args(out, q, k_pool, block_tables, context_lens, D, torch.bfloat16)
+    scale = D ** -0.5 if scale is None else float(scale)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size,
+                                     k_pool.dtype, q.device)
+    check(lib().pa_decode_quant(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                                _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
+                                _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
+                                block_tables.shape[1], int(max_context_len), scale,
+                                int(partition_size), pa_dtype(k_pool.dtype), float(k_scale),
+                                float(v_scale), _dev(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream)),
+          "pa_decode_quant")
+    return out
+
+
+def decode_step_quant(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables,
+                      context_lens, max_context_len, k_scale, v_scale, scale=None,
+                      partition_size=0, workspace=None, stream=None):
+    """Encode each sequence's new token (bf16 rows of k_new/v_new) into its slot
+    and decode over the quantized cache, in one call (pa_decode_step_quant)."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    if k_pool.dtype not in CODE_DTYPES:
+        raise ValueError("decode_step_quant needs a float8_e4m3fn or int8 pool")
+    B, Hq = _check_decode_args(out, q, k_pool, block_tables, context_lens, D, torch.bfloat16)
+    if k_new.shape != (B, H, D) or v_new.shape != (B, H, D) or \
+            k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise ValueError("k_new/v_new must be bf16 [B][Hkv][D]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (B,):
+        raise ValueError("slot_mapping must be int64 [B]")
+    scale = D ** -0.5 if scale is None else float(scale)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size,
+                                     k_pool.dtype, q.device)
+    check(lib().pa_decode_step_quant(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                                     _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+                                     _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
+                                     _dev(block_tables, "block_tables"),
+                                     _dev(context_lens, "context_lens"), B, Hq, H, D,
+                                     BLOCK_SIZE, N, block_tables.shape[1], int(max_context_len),
+                                     scale, int(partition_size), pa_dtype(k_pool.dtype),
+                                     float(k_scale), float(v_scale),
+                                     _dev(workspace, "workspace"),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream)),
+          "pa_decode_step_quant")
     return out
 
 

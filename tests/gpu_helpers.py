@@ -10,7 +10,11 @@ import torch
 
 # canonical NaN bit patterns torch writes for fill_(nan): the oracle pools are
 # poisoned with the same bits so whole pools compare bit for bit
-NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0,
+            # 8-bit pools: E4M3's NaN code; INT8 has no NaN, -128 is a code the
+            # quantizing append never writes (it clamps to +-127)
+            "fp8": 0x7F, "i8": 0x80}
+CODE_TORCH = {"fp8": torch.float8_e4m3fn, "i8": torch.int8}
 TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2}
 
 
@@ -36,8 +40,12 @@ def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None, fused=
     from oracle import bits_of  # test side only: stored-bit views for comparison
     dev = torch.device("cuda")
     td = case.k_tok.dtype
+    cd = getattr(case, "cache_dtype", None)
+    fill = (-128 if cd == "i8" else float("nan")) if poison else 0
     cache = pk.PagedKVCache(case.num_blocks, case.num_kv_heads, case.head_dim, td, dev,
-                            free_order=case.free_order, fill=float("nan") if poison else 0.0)
+                            free_order=case.free_order, fill=fill,
+                            cache_dtype=CODE_TORCH.get(cd), k_scale=case.k_scale,
+                            v_scale=case.v_scale)
     k_tok, v_tok = case.k_tok.to(dev), case.v_tok.to(dev)
     cache.replay(case.script, case.rows, k_tok, v_tok)
     plan = cache.plan_step(case.batch, max_blocks)
@@ -48,8 +56,8 @@ def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None, fused=
     out = cache.step(plan, q, k_new, v_new, partition_size=ps, fused=fused)
     torch.cuda.synchronize()
     return {"plan": plan, "out": out.cpu().numpy(), "cache": cache, "q": q,
-            "k_pool": bits_of(cache.k_pool, case.dtype),
-            "v_pool": bits_of(cache.v_pool, case.dtype)}
+            "k_pool": bits_of(cache.k_pool, case.kv_dtype),
+            "v_pool": bits_of(cache.v_pool, case.kv_dtype)}
 
 
 def max_err(a, b):

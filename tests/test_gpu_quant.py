@@ -1,0 +1,203 @@
+"""GPU parity of the quantized (8-bit) cache: the encoding append bit for bit
+against the oracle's quantize_ref over every finite bf16 / fp16 value and
+hand-made fp32 ties, and decode over the codes (pa_decode_quant,
+pa_decode_step_quant) element by element against decode_ref on pools
+poisoned with a code the append never writes."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import bits_of, run_case
+from oracle.cache import append_ref, gather_ref, new_pools
+from oracle.quant import quantize_ref
+from oracle.run import oracle_sequence_out
+from tests.gpu_helpers import CODE_TORCH, NAN_BITS, TOL, max_err, require_gpu, run_gpu_step, say
+from workloads.configs import custom_case, make_case, quantized, small_case
+
+pytestmark = pytest.mark.gpu
+FMTS = ["fp8", "i8"]
+
+
+def _append_both(fmt, src, k_vals, v_vals, k_scale, v_scale):
+    """GPU pools after cache_append_quant of tokens [T][H][D] into slots 0..T-1,
+    and the oracle's pools for the same writes."""
+    pk = require_gpu()
+    T, H, D = k_vals.shape
+    N = -(-T // 16)
+    kp, vp = pk.ops.new_pools(N, H, D, CODE_TORCH[fmt], "cuda",
+                              fill=-128 if fmt == "i8" else float("nan"))
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    pk.ops.cache_append_quant(kp, vp, k_vals.cuda(), v_vals.cuda(), slots, k_scale, v_scale)
+    torch.cuda.synchronize()
+    okp, ovp = new_pools(N, H, D, 16, fmt, fill=NAN_BITS[fmt])
+    append_ref(okp, ovp, quantize_ref(bits_of(k_vals, src), src, fmt, k_scale),
+               quantize_ref(bits_of(v_vals, src), src, fmt, v_scale), np.arange(T), 16)
+    return bits_of(kp, fmt), bits_of(vp, fmt), okp, ovp
+
+
+def _as_tokens(flat: torch.Tensor, H=2, D=128):
+    n = flat.numel()
+    T = -(-n // (H * D))
+    pad = torch.zeros(T * H * D - n, dtype=flat.dtype)
+    return torch.cat([flat, pad]).reshape(T, H, D)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("scale", [1.0, 0.0371, 3.0, 1.0 / 448, 2.0 ** -6])
+def test_encode_every_finite_bf16(fmt, scale):
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    vals = torch.from_numpy(bits[finite].view(np.int16).copy()).view(torch.bfloat16)
+    k = _as_tokens(vals)
+    v = k.flip(0).contiguous()
+    say(f"[quant append] {fmt} bf16 scale={scale}: {int(finite.sum())} values")
+    gk, gv, ok, ov = _append_both(fmt, "bf16", k, v, scale, scale * 0.75)
+    assert np.array_equal(gk, ok), np.flatnonzero(gk.ravel() != ok.ravel())[:10]
+    assert np.array_equal(gv, ov)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encode_every_finite_fp16(fmt):
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    finite = (bits & 0x7C00) != 0x7C00
+    vals = torch.from_numpy(bits[finite].view(np.int16).copy()).view(torch.float16)
+    k = _as_tokens(vals)
+    say(f"[quant append] {fmt} fp16: {int(finite.sum())} values")
+    gk, gv, ok, ov = _append_both(fmt, "f16", k, k, 0.5, 1.0 / 3.0)
+    assert np.array_equal(gk, ok)
+    assert np.array_equal(gv, ov)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encode_fp32_ties_and_extremes(fmt):
+    """Exact midpoints between neighbouring codes (ties to even), saturation,
+    signed zeros, and random fp32 values, at scale 1 (y = x exactly)."""
+    if fmt == "fp8":
+        from oracle.numerics import E4M3_TABLE
+        pos = torch.from_numpy(E4M3_TABLE[:0x7F].copy())
+        mids = ((pos[1:] + pos[:-1]) / 2).float()
+    else:
+        mids = torch.arange(-127, 127, dtype=torch.float32) + 0.5
+    g = torch.Generator().manual_seed(8)
+    extra = torch.tensor([0.0, -0.0, 448.0, -448.0, 460.0, 464.0, 470.0, 1e6, -1e6, 126.5,
+                          127.4, 127.5, 128.0, -127.5, 2.0 ** -10, -(2.0 ** -10), 1e-30])
+    vals = torch.cat([mids, -mids, extra, torch.randn(40000, generator=g) * 40,
+                      torch.randn(4000, generator=g) * 0.01]).float()
+    k = _as_tokens(vals)
+    say(f"[quant append] {fmt} fp32 ties: {vals.numel()} values")
+    gk, gv, ok, ov = _append_both(fmt, "f32", k, k, 1.0, 1.0)
+    assert np.array_equal(gk, ok)
+    assert np.array_equal(gv, ov)
+
+
+def _oracle_poisoned(case):
+    return run_case(case, pool_fill=NAN_BITS[case.kv_dtype])
+
+
+def _compare_full(case, ref, got):
+    plan = got["plan"]
+    assert np.array_equal(plan.tables, ref["tables"])
+    assert np.array_equal(plan.cows, ref["step_cows"].reshape(-1, 2))
+    assert np.array_equal(got["k_pool"], ref["k_pool"]), "K pool differs"
+    assert np.array_equal(got["v_pool"], ref["v_pool"]), "V pool differs"
+    err = max_err(got["out"], ref["out"])
+    say(f"  {case.name}: max |gpu - oracle| = {err:.3e} (tol {TOL['bf16']})")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "cow_parallel_bf16", "long_context_bf16"])
+@pytest.mark.parametrize("fused,ps", [(True, 0), (False, 0), (True, 64), (False, 256)])
+def test_small_configs_match_oracle(fmt, name, fused, ps):
+    case = quantized(small_case(name), fmt)
+    say(f"[quant decode] {case.name} fused={fused} P={ps}")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case, partition_size=ps, fused=fused)
+    _compare_full(case, ref, got)
+
+
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1023, 1025]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("hq,hkv,d,ps", [(32, 8, 128, 0), (16, 4, 64, 0), (8, 8, 128, 512),
+                                         (12, 4, 128, 16), (6, 3, 64, -1), (2, 1, 128, 256)])
+def test_edge_lengths_and_shapes(fmt, hq, hkv, d, ps):
+    case = quantized(custom_case(61, "bf16", EDGE_LENS, hq, hkv, d, partition_size=ps,
+                                 boost_prob=0.02), fmt)
+    say(f"[quant edge] {fmt} Hq={hq} Hkv={hkv} D={d} P={ps}")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case)
+    _compare_full(case, ref, got)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("ps", [0, 256])
+def test_bad_inputs_give_nan_or_zero_rows(fmt, ps):
+    pk = require_gpu()
+    case = quantized(custom_case(62, "bf16", [40, 300, 700, 20, 33], 8, 2, 128), fmt)
+    say(f"[quant errors] {fmt} P={ps}")
+    got = run_gpu_step(case, partition_size=ps)
+    cache, plan = got["cache"], got["plan"]
+    tables = plan.d_tables.clone()
+    tables[1, 5] = case.num_blocks + 7
+    tables[2, 0] = -3
+    lens = plan.d_lens.clone()
+    lens[3] = plan.max_context_len + 1
+    lens[4] = 0
+    out = torch.full(got["out"].shape, 7.0, device="cuda")
+    pk.ops.decode_quant(out, got["q"], cache.k_pool, cache.v_pool, tables, lens,
+                        plan.max_context_len, case.k_scale, case.v_scale, partition_size=ps)
+    o = out.cpu().numpy()
+    assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and np.isnan(o[3]).all()
+    assert np.array_equal(o[0], got["out"][0])
+    assert np.array_equal(o[4], np.zeros_like(o[4]))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_single_token_context_is_the_scaled_code(fmt):
+    """L = 1: softmax weight 1, out = v_scale * code exactly (one fp32 product)."""
+    case = quantized(custom_case(63, "bf16", [1, 1, 1], 8, 2, 64), fmt)
+    ref = run_case(case)
+    got = run_gpu_step(case)
+    assert np.array_equal(got["out"].astype(np.float64),
+                          ref["out"].astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gather_and_copy_move_codes_bit_for_bit(fmt):
+    pk = require_gpu()
+    case = quantized(small_case("cow_parallel_bf16"), fmt)
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case)
+    assert len(got["plan"].cows) > 0            # the step copied shared blocks
+    cache, plan = got["cache"], got["plan"]
+    kg, vg = pk.ops.gather_kv(cache.k_pool, cache.v_pool, plan.d_tables, plan.d_lens,
+                              plan.max_context_len)
+    kg, vg = bits_of(kg, fmt), bits_of(vg, fmt)
+    for b in range(case.num_seqs):
+        L = int(case.lens[b])
+        K, V = gather_ref(ref["k_pool"], ref["v_pool"], ref["tables"][b], L, 16)
+        assert np.array_equal(kg[b, :, :L], K) and np.array_equal(vg[b, :, :L], V)
+        assert not kg[b, :, L:].any() and not vg[b, :, L:].any()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_full_size_llama3_8b_sampled(fmt):
+    """Llama-3-8B-shaped batch at full size over an 8-bit cache, in the
+    bench's launch configuration; sampled rows against the oracle."""
+    require_gpu()
+    case = quantized(make_case("llama3_8b_bf16", device="cuda"), fmt)
+    say(f"[quant full-size] {case.name}")
+    ref = run_case(case, with_pools=False)
+    got = run_gpu_step(case, poison=False)
+    assert np.array_equal(got["plan"].tables, ref["tables"])
+    rng = np.random.default_rng(17)
+    picks = sorted(set([0, case.num_seqs - 1, int(np.argmax(case.lens))] +
+                       [int(i) for i in rng.choice(case.num_seqs, 2, replace=False)]))
+    for i in picks:
+        want = oracle_sequence_out(case, i)
+        err = max_err(got["out"][i], want)
+        say(f"  seq {i} L={case.lens[i]}: max err {err:.3e}")
+        assert err <= TOL["bf16"]
+    assert not np.isnan(got["out"]).any()
