@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--kv-cache", choices=("fp8", "i8"), default=None,
                     help="quantized cache: the same workload with 8-bit K/V codes (FP8 E4M3 "
                          "or INT8, per-pool scales); one pa_decode_step_quant per step "
-                         "(quantizing append, attention kernel timed, merge)")
+                         "(attention kernel with the new tokens encoded in, timed; merge)")
     ap.add_argument("--no-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -494,13 +494,13 @@ def main():
         # the fp32 output; in the phased step the kernel also reads the new
         # tokens (k_new, v_new) and the slot indices
         alg = kv_bytes + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
-        if mode == "phased":
+        if mode in ("phased", "quant"):
             alg += 2 * k_new.numel() * k_new.element_size() + B * 8
         achieved = alg / (part_ms * 1e-3) / 1e9
         res["attention_kernel_us"] = round(dec_ms * 1e3, 3)
         if mode == "quant":
-            kname = (f"attention kernel of pa_decode_step_quant ({case.kv_dtype} codes; the "
-                     f"quantizing append is its own kernel)")
+            kname = (f"attention kernel of pa_decode_step_quant ({case.kv_dtype} codes; new "
+                     f"tokens encoded and fused in)")
         elif mode == "separate":
             kname = "attention partition kernel (pa_decode_partial)"
         elif args.mode == "phased":

@@ -238,6 +238,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   workspace: device, at least pa_decode_workspace_bytes(...) bytes,
  *   exclusively owned by this call until it completes on `stream`.
  *   max_context_len: upper bound of context_lens (sizes the launch).
+ *   q, the pools (and k_new/v_new of the step calls) must be 16-byte aligned,
+ *   the workspace 256-byte aligned (PA_ERR_INVALID_ARG otherwise).
  * Supported: block_size 16; head_dim 64 or 128; Hq a multiple of Hkv with
  * G = Hq/Hkv <= 16.  fp16/bf16 run on the matrix cores, fp32 on plain FMAs;
  * setting the environment variable PA_DECODE_KERNEL=generic makes fp16/bf16
@@ -375,12 +377,19 @@ pa_status pa_decode_quant(float* out, const void* q, const void* k_pool, const v
                           int32_t partition_size, pa_dtype cache_dtype, float k_scale,
                           float v_scale, void* workspace, size_t workspace_bytes, void* stream);
 
-/* One decode step over a quantized cache: pa_cache_append_quant(k_pool,
- * v_pool, k_new, v_new, slot_mapping, num_seqs, ..., cache_dtype, PA_BF16,
- * k_scale, v_scale) followed by pa_decode_quant(...) on the same stream
- * (k_new/v_new: bf16 [num_seqs][Hkv][D], sequence b's token at position
- * context_lens[b] - 1; slot -1 skips the write).  Copy-on-write copies of
- * the step must be issued before this call on the same stream. */
+/* One decode step over a quantized cache, with the result of
+ * pa_cache_append_quant(k_pool, v_pool, k_new, v_new, slot_mapping,
+ * num_seqs, ..., cache_dtype, PA_BF16, k_scale, v_scale) followed by
+ * pa_decode_quant(...) (k_new/v_new: bf16 [num_seqs][Hkv][D], sequence b's
+ * token at position context_lens[b] - 1).  Slots as for pa_decode_step: the
+ * table's slot, -1 (no write; the position is attended as stored), or a slot
+ * elsewhere in the pool (written; out only defined when it is not attended).
+ * The new tokens are encoded inside the kernels, no separate append launch:
+ * the attention kernel attends their codes, and the merge kernel writes them
+ * when one runs (else the attention kernel does); a sequence whose length
+ * fails the bounds checks (NaN out rows) or is 0 gets no pool write.
+ * Copy-on-write copies of the step must be issued before this call on the
+ * same stream. */
 pa_status pa_decode_step_quant(float* out, const void* q, void* k_pool, void* v_pool,
                                const void* k_new, const void* v_new,
                                const int64_t* slot_mapping, const int32_t* block_tables,

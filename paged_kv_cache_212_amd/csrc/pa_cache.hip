@@ -52,30 +52,6 @@ __global__ __launch_bounds__(256) void append_kernel(typename T::bits* __restric
   }
 }
 
-// Encoders of the quantized cache (r = the fp32 reciprocal of the pool's
-// scale): y = x * r in one fp32 rounding, then
-//   I8:   round half to even, clamp to [-127, 127], two's complement byte;
-//   E4M3: clamp to [-448, 448] (the largest finite code), then the hardware
-//         conversion, which rounds to nearest even and keeps the sign.
-template <typename Code>
-struct Encode;
-template <>
-struct Encode<I8> {
-  __device__ static inline uint32_t pair(float a, float b, float r) {
-    const int ca = static_cast<int>(fminf(fmaxf(rintf(a * r), -127.f), 127.f));
-    const int cb = static_cast<int>(fminf(fmaxf(rintf(b * r), -127.f), 127.f));
-    return (static_cast<uint32_t>(ca) & 0xFFu) | ((static_cast<uint32_t>(cb) & 0xFFu) << 8);
-  }
-};
-template <>
-struct Encode<E4M3> {
-  __device__ static inline uint32_t pair(float a, float b, float r) {
-    const float ya = fminf(fmaxf(a * r, -448.f), 448.f);
-    const float yb = fminf(fmaxf(b * r, -448.f), 448.f);
-    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, 0, false)) & 0xFFFFu;
-  }
-};
-
 // Quantizing append: one workgroup per new token.  K: each thread encodes 16
 // consecutive dims of one head (one 16-byte chunk of the pool); V: one byte
 // per element (a V chunk holds 16 tokens of one dim).

@@ -28,6 +28,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_mfma.h"
@@ -61,6 +62,7 @@ struct Params {
   int P, maxP;
   float scale_log2;
   float out_scale;     // factor of the final rows (V scale of a quantized cache, else 1)
+  float enc_k, enc_v;  // quantized cache, fused append: fp32 reciprocals of the K/V scales
 };
 
 __device__ inline bool len_valid(int L, const Params& pr) {
@@ -741,7 +743,6 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   constexpr int NT = D / 64;               // 64-dim output tiles
   constexpr int NH = 16 / T::kVecElems;    // V chunks per (block, dim): 2 (16-bit), 1 (codes)
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * T::kBytes;
-  if constexpr (kCodes) with_new = false;  // 8-bit pools: the append runs on its own
   const int lane = threadIdx.x & 63;
   const int G = pr.G;
   const int nquad = (nblk + 3) >> 2;
@@ -807,17 +808,24 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   };
 
   // New token of the step (fused append): staged in LDS at the start, put
-  // into the last quad's registers and written to its pool slot.
+  // into the last quad's registers and written to its pool slot.  8-bit
+  // pools stage its codes (encoded from the bf16 rows as the quantizing
+  // append encodes them), D/4 words of 4 codes per pool.
+  // The rows are loaded here and consumed (encoded, stored to LDS) only after
+  // the first quad's loads are issued, so no wait sits in front of them.
+  constexpr int kStageWords = D * T::kBytes / 4;
   __shared__ uint32_t s_new[2][D / 2];
-  uint32_t stage_k = 0, stage_v = 0;
+  // 16-bit pools: one word (2 values) per lane; 8-bit pools: 4 bf16 values
+  using StageT = std::conditional_t<kCodes, uint2, uint32_t>;
+  StageT stage_k{}, stage_v{};
   int64_t new_slot = -1;
   if (with_new) {
     // fetched with the first quad's loads, not at the end of the range
     new_slot = pr.slots[b];
-    if (lane < D / 2) {
+    if (lane < kStageWords) {
       const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
-      stage_k = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.k_new) + nrow)[lane];
-      stage_v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.v_new) + nrow)[lane];
+      stage_k = reinterpret_cast<const StageT*>(static_cast<const uint16_t*>(pr.k_new) + nrow)[lane];
+      stage_v = reinterpret_cast<const StageT*>(static_cast<const uint16_t*>(pr.v_new) + nrow)[lane];
     }
   }
   // Puts the new token into the last quad's registers (its pool slot may
@@ -838,13 +846,37 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   };
   // K before the last quad's QK, V before its P.V (so QK does not wait for V).
   auto substitute_k = [&]() {
-    const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
     if (lane == qt) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kr[c] = *reinterpret_cast<const uint4*>(kn + c * 8);
+      for (int c = 0; c < NC; ++c) kr[c] = reinterpret_cast<const uint4*>(s_new[0])[c];
     }
   };
   auto substitute_v = [&]() {
+    if constexpr (kCodes) {
+      // byte qt % 16 of the block's chunk of each dim 64t + lane.  Masks
+      // applied to every block's registers (not a branch per block, which
+      // the compiler turns into an indexed access through scratch memory).
+      const uint8_t* vn = reinterpret_cast<const uint8_t*>(s_new[1]);
+      const int kb = qt >> 4, e = qt & 15;
+      const uint32_t byte = 0xFFu << ((e & 3) * 8);
+      const int dw = e >> 2;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t val = static_cast<uint32_t>(vn[64 * t + lane]) * 0x01010101u;
+#pragma unroll
+        for (int KB = 0; KB < 4; ++KB) {
+          const uint32_t m = KB == kb ? byte : 0u;
+          const uint32_t mx = dw == 0 ? m : 0u, my = dw == 1 ? m : 0u;
+          const uint32_t mz = dw == 2 ? m : 0u, mw = dw == 3 ? m : 0u;
+          uint4& vv = vr[KB][0][t];
+          vv.x = (vv.x & ~mx) | (val & mx);
+          vv.y = (vv.y & ~my) | (val & my);
+          vv.z = (vv.z & ~mz) | (val & mz);
+          vv.w = (vv.w & ~mw) | (val & mw);
+        }
+      }
+      return;
+    }
     const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
     const int kb = qt >> 4, h = (qt >> 3) & 1, e = qt & 7;
     const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
@@ -874,11 +906,12 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   //   * any other slot in the pool: the token alone, element by element;
   //   * slot out of the pool (-1): nothing.
   auto write_new = [&](bool at_table) {
+    if constexpr (kCodes) return;   // 8-bit pools: the merge kernel writes the codes
     const int64_t slot = new_slot;
     if (pr.write_new_in_merge || slot < 0 ||
         slot >= static_cast<int64_t>(pr.num_blocks) * kBlockSize)
       return;
-    const int kb = qt >> 4, h = (qt >> 3) & 1;
+    const int kb = qt >> 4, h = NH == 2 ? (qt >> 3) & 1 : 0;
     const int phys = new_phys();
     if (at_table) {
       const int64_t tile = (static_cast<int64_t>(phys) * pr.Hkv + g) * kTileBytes;
@@ -1022,9 +1055,14 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   issue_k();
   issue_v();
   if (with_new) {
-    if (lane < D / 2) {
-      s_new[0][lane] = stage_k;
-      s_new[1][lane] = stage_v;
+    if (lane < kStageWords) {
+      if constexpr (kCodes) {
+        s_new[0][lane] = encode4_bf16<T>(stage_k, pr.enc_k);
+        s_new[1][lane] = encode4_bf16<T>(stage_v, pr.enc_v);
+      } else {
+        s_new[0][lane] = stage_k;
+        s_new[1][lane] = stage_v;
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -1335,8 +1373,11 @@ __global__ __launch_bounds__(64, kWaves) void decode_split_kernel(Params pr) {
 // ---------------------------------------------------------------------------
 constexpr int kMergeBatch = 8;
 
-template <int D, bool kSplit>
+// C: void when the pools hold 16-bit values (new tokens moved as bits), else
+// the 8-bit code format the new tokens are encoded into.
+template <int D, bool kSplit, typename C = void>
 __global__ __launch_bounds__(D) void merge_kernel(Params pr) {
+  constexpr bool kCodes = !std::is_void_v<C>;
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int64_t row = static_cast<int64_t>(b) * pr.Hq + h;
   const float* pm = pr.part_m + row * pr.maxP;
@@ -1360,23 +1401,48 @@ __global__ __launch_bounds__(D) void merge_kernel(Params pr) {
   // Fused append of pa_decode_step: the first query head's workgroup of each
   // (sequence, KV head) writes the new token (16-bit K/V) into its slot; its
   // loads go out with the partials'.
+  // 8-bit pools: the bf16 rows are encoded as the quantizing append encodes
+  // them (thread d < D/16 reads 16 K values for one 16-byte chunk of codes).
   const bool appends = pr.write_new_in_merge && h % pr.G == 0;
   const int g = h / pr.G;
   int64_t slot = -1;
-  uint4 kchunk = make_uint4(0, 0, 0, 0);
+  uint4 kchunk = make_uint4(0, 0, 0, 0), kchunk2 = make_uint4(0, 0, 0, 0);
   uint16_t vval = 0;
   if (appends) {
     slot = pr.slots[b];
     const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
-    if (d < D / 8)
-      kchunk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pr.k_new) + nrow + d * 8);
+    const uint16_t* kn = static_cast<const uint16_t*>(pr.k_new) + nrow;
+    if constexpr (kCodes) {
+      if (d < D / 16) {
+        kchunk = *reinterpret_cast<const uint4*>(kn + d * 16);
+        kchunk2 = *reinterpret_cast<const uint4*>(kn + d * 16 + 8);
+      }
+    } else if (d < D / 8) {
+      kchunk = *reinterpret_cast<const uint4*>(kn + d * 8);
+    }
     vval = static_cast<const uint16_t*>(pr.v_new)[nrow + d];
   }
   if (!len_valid(L, pr) || L == 0) {
     if (kSplit) pr.out[row * D + d] = (L == 0) ? 0.f : __builtin_nanf("");
     return;
   }
-  if (appends && slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
+  if (kCodes && appends && slot >= 0 &&
+      slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
+    if constexpr (kCodes) {
+      const int64_t blk = slot / kBlockSize;
+      const int ts = static_cast<int>(slot % kBlockSize);
+      uint8_t* kt = static_cast<uint8_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
+      uint8_t* vt = static_cast<uint8_t*>(pr.vpool_w) + tile_base(blk, g, pr.Hkv, D);
+      if (d < D / 16)
+        *reinterpret_cast<uint4*>(kt + (d * kBlockSize + ts) * 16) =
+            make_uint4(encode4_bf16<C>(make_uint2(kchunk.x, kchunk.y), pr.enc_k),
+                       encode4_bf16<C>(make_uint2(kchunk.z, kchunk.w), pr.enc_k),
+                       encode4_bf16<C>(make_uint2(kchunk2.x, kchunk2.y), pr.enc_k),
+                       encode4_bf16<C>(make_uint2(kchunk2.z, kchunk2.w), pr.enc_k));
+      const float vf = __uint_as_float(static_cast<uint32_t>(vval) << 16);
+      vt[d * kBlockSize + ts] = static_cast<uint8_t>(Encode<C>::pair(vf, 0.f, pr.enc_v));
+    }
+  } else if (appends && slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
     const int64_t blk = slot / kBlockSize;
     const int ts = static_cast<int>(slot % kBlockSize);
     uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
@@ -1565,20 +1631,23 @@ void launch_split(const Params& pr, int W, hipStream_t s) {
 
 enum class Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
 
-// 8-bit pools (C = E4M3 or I8): the 4x4x4 engine only (G <= 4), never fused
-// with the append.
+// 8-bit pools (C = E4M3 or I8): the 4x4x4 engine only (G <= 4).
 template <typename C, int D>
 void launch_code_phases(const Params& pr, const LaunchPlan& lp, bool first, bool second,
                         hipStream_t s) {
   if (lp.split) {
     if (first) launch_attention(decode_split_kernel<Engine4<C, D>, 2>, lp.W, 64, s, pr);
-    if (second) merge_kernel<D, true><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
+    if (second) merge_kernel<D, true, C><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
     return;
   }
-  if (first)
-    launch_attention(decode_fixed_kernel<Engine4<C, D>, false, kFixedWaves4>,
-                     dim3(pr.Hkv * pr.maxP, 1, pr.B), 64, s, pr);
-  if (second && pr.maxP > 1) merge_kernel<D, false><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
+  const dim3 grid(pr.Hkv * pr.maxP, 1, pr.B);
+  if (first && pr.k_new != nullptr)
+    launch_attention(decode_fixed_kernel<Engine4<C, D>, true, kFixedWaves4>, grid, 64, s, pr);
+  else if (first)
+    launch_attention(decode_fixed_kernel<Engine4<C, D>, false, kFixedWaves4>, grid, 64, s, pr);
+  // with the step's new tokens the merge kernel always runs: it writes them
+  if (second && (pr.maxP > 1 || pr.write_new_in_merge))
+    merge_kernel<D, false, C><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
 }
 
 template <int D>
@@ -1610,9 +1679,7 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
 
 // Whether the partition kernel of this plan appends the step's new tokens
 // itself (pa_decode_step); otherwise pa_cache_append runs first.
-bool fuses_append(const LaunchPlan& lp, int G, pa_dtype dt) {
-  return !code_dtype(dt) && !lp.generic && (lp.split || G <= 4);
-}
+bool fuses_append(const LaunchPlan& lp, int G) { return !lp.generic && (lp.split || G <= 4); }
 
 // Validates the arguments shared by pa_decode / pa_decode_partial /
 // pa_decode_merge and launches the requested phases.
@@ -1679,8 +1746,8 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
 
   if (nt && (!nt->k_new || !nt->v_new || !nt->slots))
     return fail(PA_ERR_INVALID_ARG, "%s: NULL new-token pointer", fn);
-  if (nt && (reinterpret_cast<uintptr_t>(nt->k_new) & 15))
-    return fail(PA_ERR_INVALID_ARG, "%s: k_new must be 16-byte aligned", fn);
+  if (nt && ((reinterpret_cast<uintptr_t>(nt->k_new) | reinterpret_cast<uintptr_t>(nt->v_new)) & 15))
+    return fail(PA_ERR_INVALID_ARG, "%s: k_new and v_new must be 16-byte aligned", fn);
   const LaunchPlan lp = make_plan(max_context_len, partition_size, dtype,
                                   path_from_env() == Path::kGeneric);
   const size_t need = workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
@@ -1722,7 +1789,7 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (nt) {
-    if (fuses_append(lp, pr.G, dtype)) {
+    if (fuses_append(lp, pr.G)) {
       // append fused: the attention kernel uses the new tokens; the merge
       // kernel writes them to the pool when a merge kernel runs, else the
       // attention kernel does
@@ -1731,7 +1798,13 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
       pr.slots = nt->slots;
       pr.kpool_w = const_cast<void*>(k_pool);
       pr.vpool_w = const_cast<void*>(v_pool);
-      pr.write_new_in_merge = lp.split || lp.maxP > 1;
+      // 8-bit pools: always the merge kernel (the attention kernel only
+      // attends the encoded tokens)
+      pr.write_new_in_merge = lp.split || lp.maxP > 1 || cs != nullptr;
+      if (cs) {   // the same fp32 reciprocals as pa_cache_append_quant's
+        pr.enc_k = 1.0f / cs->k_scale;
+        pr.enc_v = 1.0f / cs->v_scale;
+      }
     } else if (static_cast<int>(ph) & static_cast<int>(Phase::kPartitions)) {
       const pa_status st =
           cs ? pa_cache_append_quant(const_cast<void*>(k_pool), const_cast<void*>(v_pool),

@@ -48,6 +48,37 @@ struct U8 {
 struct E4M3 : U8 {};
 struct I8 : U8 {};
 
+// Encoders of the quantized cache (r = the fp32 reciprocal of the pool's
+// scale): y = x * r in one fp32 rounding, then
+//   I8:   round half to even, clamp to [-127, 127], two's complement byte;
+//   E4M3: clamp to [-448, 448] (the largest finite code), then the hardware
+//         conversion, which rounds to nearest even and keeps the sign.
+template <typename Code>
+struct Encode;
+template <>
+struct Encode<I8> {
+  __device__ static inline uint32_t pair(float a, float b, float r) {
+    const int ca = static_cast<int>(fminf(fmaxf(rintf(a * r), -127.f), 127.f));
+    const int cb = static_cast<int>(fminf(fmaxf(rintf(b * r), -127.f), 127.f));
+    return (static_cast<uint32_t>(ca) & 0xFFu) | ((static_cast<uint32_t>(cb) & 0xFFu) << 8);
+  }
+};
+template <>
+struct Encode<E4M3> {
+  __device__ static inline uint32_t pair(float a, float b, float r) {
+    const float ya = fminf(fmaxf(a * r, -448.f), 448.f);
+    const float yb = fminf(fmaxf(b * r, -448.f), 448.f);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, 0, false)) & 0xFFFFu;
+  }
+};
+// Codes of four bf16 values (the 16-bit halves of w, low first): byte i = value i.
+template <typename Code>
+__device__ inline uint32_t encode4_bf16(uint2 w, float r) {
+  const float a = __uint_as_float(w.x << 16), b = __uint_as_float(w.x & 0xFFFF0000u);
+  const float c = __uint_as_float(w.y << 16), e = __uint_as_float(w.y & 0xFFFF0000u);
+  return Encode<Code>::pair(a, b, r) | (Encode<Code>::pair(c, e, r) << 16);
+}
+
 // Element offsets inside one (block, kv-head) tile of D*16 elements.
 //   K tile: [D/x][16][x]
 //   V tile: [16/x][D][x]  (tokens 0..x-1 as D rows of x tokens, then the

@@ -201,3 +201,54 @@ def test_full_size_llama3_8b_sampled(fmt):
         say(f"  seq {i} L={case.lens[i]}: max err {err:.3e}")
         assert err <= TOL["bf16"]
     assert not np.isnan(got["out"]).any()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("hq,hkv,ps", [(32, 8, 0), (32, 8, 256), (8, 2, -1), (8, 8, 64)])
+def test_step_slot_cases_match_append_then_decode(fmt, hq, hkv, ps):
+    """pa_decode_step_quant (new tokens encoded inside the attention and merge
+    kernels) == pa_cache_append_quant then pa_decode_quant, for the table's
+    slot, -1 (no write) and a slot in a block no table references."""
+    pk = require_gpu()
+    case = quantized(custom_case(82, "bf16", [40, 300, 700, 20, 33, 129], hq, hkv, 128,
+                                 partition_size=ps), fmt)
+    say(f"[quant step slots] {fmt} Hq={hq} Hkv={hkv} P={ps}")
+    dev = torch.device("cuda")
+    k_tok, v_tok = case.k_tok.to(dev), case.v_tok.to(dev)
+    caches = []
+    for _ in range(2):
+        c = pk.PagedKVCache(case.num_blocks, hkv, 128, torch.bfloat16, dev,
+                            free_order=case.free_order,
+                            fill=-128 if fmt == "i8" else float("nan"),
+                            cache_dtype=CODE_TORCH[fmt], k_scale=case.k_scale,
+                            v_scale=case.v_scale)
+        c.replay(case.script, case.rows, k_tok, v_tok)
+        caches.append((c, c.plan_step(case.batch)))
+    (c1, p1), (c2, p2) = caches
+    unused = sorted(set(range(case.num_blocks)) - set(p1.tables[p1.tables >= 0].tolist()))
+    slots = p1.d_slots.clone()
+    slots[1] = -1
+    slots[3] = unused[0] * 16 + 5
+    nr = torch.as_tensor(case.new_rows(), device=dev)
+    k_new, v_new = k_tok.index_select(0, nr), v_tok.index_select(0, nr)
+    q = case.q.to(dev)
+    o1 = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    o2 = torch.empty_like(o1)
+    pk.ops.decode_step_quant(o1, q, c1.k_pool, c1.v_pool, k_new, v_new, slots, p1.d_tables,
+                             p1.d_lens, p1.max_context_len, case.k_scale, case.v_scale,
+                             partition_size=ps)
+    pk.ops.cache_append_quant(c2.k_pool, c2.v_pool, k_new, v_new, slots, case.k_scale,
+                              case.v_scale)
+    pk.ops.decode_quant(o2, q, c2.k_pool, c2.v_pool, p2.d_tables, p2.d_lens,
+                        p2.max_context_len, case.k_scale, case.v_scale, partition_size=ps)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(c1.k_pool, fmt), bits_of(c2.k_pool, fmt))
+    assert np.array_equal(bits_of(c1.v_pool, fmt), bits_of(c2.v_pool, fmt))
+    a, b = o1.cpu().numpy(), o2.cpu().numpy()
+    keep = list(range(case.num_seqs))
+    if fmt == "fp8":
+        # sequences 1 and 3: their last position is never written (NaN codes)
+        for i in (1, 3):
+            assert np.isnan(a[i]).all() and np.isnan(b[i]).all()
+        keep = [i for i in keep if i not in (1, 3)]
+    assert max_err(a[keep], b[keep]) <= 1e-4
