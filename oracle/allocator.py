@@ -27,6 +27,14 @@ same choices so tables compare bit for bit):
 * batched reservations are all-or-nothing: if the batch needs more blocks
   than are free nothing changes;
 * slot = physical_block * block_size + position % block_size.
+
+Sliding window (page 1, jisaku.com glossary, section
+「他のKVキャッシュ最適化との組み合わせ」: with a sliding window, blocks that
+have left the window can be released to save memory on long contexts):
+``release_before(sid, first_pos)`` drops the sequence's blocks whose every
+slot lies before ``first_pos``.  Reading: their table entries become -1, so
+position p still maps to entry p // block_size; a dropped block is pushed on
+the free list when its count reaches zero, in table order, like ``free_seq``.
 """
 from __future__ import annotations
 
@@ -121,7 +129,8 @@ class AllocatorModel:
         if child in self.tables:
             raise AllocError(SEQ_EXISTS, f"sequence {child} exists")
         for b in table:
-            self.ref[b] += 1
+            if b >= 0:
+                self.ref[b] += 1
         self.tables[child] = list(table)
         self.lens[child] = self.lens[parent]
 
@@ -155,11 +164,32 @@ class AllocatorModel:
     def free_seq(self, sid: int):
         table = self._seq(sid)
         for b in table:
+            if b < 0:
+                continue
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
         del self.tables[sid]
         del self.lens[sid]
+
+    def release_before(self, sid: int, first_pos: int) -> int:
+        """Drops the blocks of sid whose 16 slots all lie before first_pos
+        (clamped to the length); returns the number of entries dropped."""
+        table = self._seq(sid)
+        if first_pos < 0:
+            raise AllocError(INVALID_ARG, "negative position")
+        f = min(int(first_pos), self.lens[sid])
+        n = 0
+        for k in range(f // self.bs):            # block k covers [k*bs, (k+1)*bs)
+            b = table[k]
+            if b < 0:
+                continue
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+            table[k] = -1
+            n += 1
+        return n
 
     def seq_len(self, sid: int) -> int:
         self._seq(sid)
@@ -193,7 +223,8 @@ class AllocatorModel:
         cnt = np.zeros(self.N, dtype=np.int64)
         for t in self.tables.values():
             for b in t:
-                cnt[b] += 1
+                if b >= 0:
+                    cnt[b] += 1
         assert np.array_equal(cnt, self.ref)
         free = set(self.free)
         assert len(free) == len(self.free)

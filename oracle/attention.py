@@ -32,13 +32,16 @@ def _softmax_row(s):
 
 
 def decode_ref(q_bits, k_pool, v_pool, tables, lens, dtype, scale=None, bs=16, q_dtype=None,
-               k_scale=1.0, v_scale=1.0):
+               k_scale=1.0, v_scale=1.0, window=0):
     """q_bits [B][Hq][D]; pools of stored bits; tables int [B][MB]; lens [B].
 
     ``dtype`` is the pools' dtype, ``q_dtype`` that of q (default: the same).
     A quantized cache ("i8"/"fp8" codes) holds K = code * k_scale and
     V = code * v_scale (scales taken as fp32); the attention is the formula
-    above over those values.  Returns out [B][Hq][D] fp64.
+    above over those values.  ``window`` W > 0: sliding-window attention over
+    the last W positions only, t in [max(0, L - W), L) (page 1, section
+    「他のKVキャッシュ最適化との組み合わせ」, SWA; the span is this reading).
+    Returns out [B][Hq][D] fp64.
     """
     B, Hq, D = q_bits.shape
     Hkv = k_pool.shape[1]
@@ -51,7 +54,8 @@ def decode_ref(q_bits, k_pool, v_pool, tables, lens, dtype, scale=None, bs=16, q
         L = int(lens[b])
         if L == 0:
             continue
-        Kb, Vb = gather_ref(k_pool, v_pool, tables[b], L, bs)
+        first = max(0, L - window) if window else 0
+        Kb, Vb = gather_ref(k_pool, v_pool, tables[b], L, bs, first)
         Kb, Vb = to_f64(Kb, dtype) * ks, to_f64(Vb, dtype) * vs
         for h in range(Hq):
             g = h // G

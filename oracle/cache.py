@@ -75,12 +75,16 @@ def copy_ref(k_pool, v_pool, pairs):
         v_pool[dst] = v_pool[src]
 
 
-def gather_ref(k_pool, v_pool, table, L, bs):
-    """Logically contiguous K and V of one sequence: two arrays [H][L][D] of bits."""
+def gather_ref(k_pool, v_pool, table, L, bs, first=0):
+    """Logically contiguous K and V of positions [first, L) of one sequence:
+    two arrays [H][L - first][D] of bits (every block used must be in the table)."""
     H, Dx, _, x = k_pool.shape[1:]
     D = Dx * x
-    pos = np.arange(L, dtype=np.int64)
+    pos = np.arange(first, L, dtype=np.int64)
+    L = L - first
     blk = np.asarray(table, dtype=np.int64)[pos // bs]     # physical block of position p
+    if (blk < 0).any():
+        raise ValueError("position reached through a released table entry")
     off = pos % bs                                           # token inside that block
     K = k_pool[blk, :, :, off, :]                            # [L][H][D/x][x]
     V = v_pool[blk, :, off // x, :, off % x]                 # [L][H][D]

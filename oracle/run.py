@@ -41,6 +41,8 @@ def run_script(am: AllocatorModel, script, rows, on_write=None, on_copy=None):
             am.fork(op[1], op[2])
         elif kind == "free":
             am.free_seq(op[1])
+        elif kind == "release":
+            am.release_before(op[1], op[2])
         else:
             raise ValueError(op)
 
@@ -91,7 +93,7 @@ def run_case(case, with_pools=True, decode=True, pool_fill=0):
             res["out"] = decode_ref(bits_of(case.q, case.dtype), kp, vp, tables, lens,
                                     cd or case.dtype, case.scale, case.block_size,
                                     q_dtype=case.dtype, k_scale=case.k_scale,
-                                    v_scale=case.v_scale)
+                                    v_scale=case.v_scale, window=getattr(case, "window", 0))
     return res
 
 
@@ -105,7 +107,8 @@ def oracle_sequence_out(case, i):
     Hq, D = case.num_q_heads, case.head_dim
     if L == 0:
         return np.zeros((Hq, D))
-    rws = case.rows[sid][:L]
+    W = getattr(case, "window", 0)
+    rws = case.rows[sid][max(0, L - W) if W else 0:L]     # a window keeps the last W
     idx = torch.as_tensor(rws, device=case.k_tok.device)
     K = to_f64(bits_of(case.k_tok.index_select(0, idx), case.dtype), case.dtype)  # [L][Hkv][D]
     V = to_f64(bits_of(case.v_tok.index_select(0, idx), case.dtype), case.dtype)

@@ -60,6 +60,8 @@ class Case:
     cache_dtype: str | None = None
     k_scale: float = 1.0
     v_scale: float = 1.0
+    # sliding window: the step attends the last `window` positions (0 = all)
+    window: int = 0
 
     @property
     def kv_dtype(self) -> str:
@@ -78,9 +80,14 @@ class Case:
     def elt_bytes(self) -> int:
         return ELT_BYTES[self.kv_dtype]
 
+    def attended_lens(self) -> np.ndarray:
+        """Positions each sequence attends: L, or min(L, window) with a window."""
+        L = self.lens.astype(np.int64)
+        return np.minimum(L, self.window) if self.window else L
+
     def kv_bytes(self) -> int:
-        """Logical K+V bytes one decode step reads: sum(L) * Hkv * 2 * D * elt."""
-        return int(self.lens.astype(np.int64).sum()) * self.num_kv_heads * 2 * \
+        """Logical K+V bytes one decode step reads: sum(attended) * Hkv * 2 * D * elt."""
+        return int(self.attended_lens().sum()) * self.num_kv_heads * 2 * \
             self.head_dim * self.elt_bytes
 
     def new_rows(self) -> np.ndarray:
@@ -101,6 +108,32 @@ def quantized(case: Case, cache_dtype: str) -> Case:
     vs = float(np.float32(amax_v) / np.float32(CODE_MAX[cache_dtype]))
     name = case.name.rsplit("_", 1)[0] + "_" + cache_dtype + "kv"
     return replace(case, name=name, cache_dtype=cache_dtype, k_scale=ks, v_scale=vs)
+
+
+def windowed(case: Case, window: int, reuse: bool = True) -> Case:
+    """The same step with sliding-window attention over the last ``window``
+    positions.  Before the step each batch sequence releases the blocks wholly
+    before its window start L - window; with ``reuse``, one new sequence per
+    releasing sequence then takes as many blocks (so those blocks hold other
+    tokens when the step runs).  The new sequences reuse existing token rows
+    and are not decoded."""
+    if window <= 0:
+        raise ValueError("window must be positive")
+    script = list(case.script)
+    rows = dict(case.rows)
+    extra = []
+    for sid, L in zip(case.batch.tolist(), case.lens.tolist()):
+        first = max(0, int(L) - window)
+        script.append(("release", int(sid), first))
+        # blocks wholly before `first` among the L - 1 cached positions
+        nrel = min(first, int(L) - 1) // case.block_size
+        if reuse and nrel:
+            extra.append((300_000 + int(sid), nrel * case.block_size, int(sid)))
+    for new_sid, n, src in extra:
+        rows[new_sid] = case.rows[src][:n]
+        script.append(("add", new_sid, n))
+    name = f"{case.name}_w{window}"
+    return replace(case, name=name, script=script, rows=rows, window=int(window))
 
 
 def _draw_values(seed: int, nq: tuple, nkv: tuple, dtype: str, device, q_std: float = 1.0,
