@@ -147,6 +147,22 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n, int64
 /* Releases a sequence: counts -1, blocks reaching zero return to the pool. */
 pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
 
+/* Sliding window: drops the blocks of a sequence whose block_size slots all
+ * lie before position first_pos (clamped to the sequence's length), i.e.
+ * logical blocks k with (k+1)*block_size <= min(first_pos, len).  Their
+ * table entries become -1 (placeholders: position p still maps to entry
+ * p / block_size, and pa_bm_block_tables exports the -1s); counts -1, blocks
+ * reaching zero return to the pool in table order.  Entries already dropped
+ * are skipped.  *released_out (may be NULL) = entries dropped by this call.
+ * For attention over the last W positions, call it with first_pos = L - W
+ * once the step's length L is reserved; the windowed decode calls never read
+ * the dropped entries (page 1, jisaku.com glossary, section
+ * 「他のKVキャッシュ最適化との組み合わせ」: blocks that left the window are
+ * freed).  The caller orders reuse of a freed block after the last kernel
+ * that read it, as for pa_bm_free_seq (same stream). */
+pa_status pa_bm_release_before(pa_bm* bm, int64_t seq_id, int32_t first_pos,
+                               int32_t* released_out);
+
 /* Block tables of n sequences into tables_out (host, [n][max_blocks], padded
  * with -1) and lengths into lens_out (host, [n], may be NULL). */
 pa_status pa_bm_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
@@ -401,9 +417,40 @@ pa_status pa_decode_step_quant(float* out, const void* q, void* k_pool, void* v_
                                float v_scale, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Sliding-window decode: pa_decode / pa_decode_step with attention over the
+ * last `window` positions of each sequence only, t in
+ * [max(0, L - window), L) (window = 0: all L positions, the plain calls).
+ * Table entries of blocks wholly before L - window are never read, so they
+ * may have been dropped by pa_bm_release_before (page 1, jisaku.com
+ * glossary, section 「他のKVキャッシュ最適化との組み合わせ」: a sliding window
+ * lets blocks that left it be freed).  Fixed partitions count from the
+ * partition holding the window's first position; the workspace is sized as
+ * for pa_decode.  Other arguments, bounds checks and the step's slot rules
+ * as for pa_decode / pa_decode_step.  Supported: fp32/fp16/bf16 pools; on
+ * the matrix cores G = Hq/Hkv <= 4 (PA_ERR_UNSUPPORTED for more; the
+ * plain-FMA kernel takes any G).  window < 0 is PA_ERR_INVALID_ARG. */
+pa_status pa_decode_window(float* out, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                           int32_t window, int32_t partition_size, pa_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_decode_step_window(float* out, const void* q, void* k_pool, void* v_pool,
+                                const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, const int32_t* block_tables,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len,
+                                float scale, int32_t window, int32_t partition_size,
+                                pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Measurement hook: the next attention kernel launched by a decode call
  * (pa_decode, pa_decode_partial, pa_decode_step, pa_decode_step_partial,
- * pa_decode_quant or pa_decode_step_quant)
+ * pa_decode_quant, pa_decode_step_quant, pa_decode_window or
+ * pa_decode_step_window)
  * on this host thread records start_event when it starts executing and
  * stop_event when it finishes, attached to the kernel's own dispatch, so
  * hipEventElapsedTime(start, stop) is that kernel's duration.  The events are

@@ -46,6 +46,7 @@ SIGNATURES = {
     "pa_bm_extend": (C.c_int, [_vp, _i64, _i32, _p_i64, _p_i32, _p_i32]),
     "pa_bm_append_slots": (C.c_int, [_vp, _p_i64, _i32, _p_i64, _p_i32, _p_i32]),
     "pa_bm_free_seq": (C.c_int, [_vp, _i64]),
+    "pa_bm_release_before": (C.c_int, [_vp, _i64, _i32, _p_i32]),
     "pa_bm_block_tables": (C.c_int, [_vp, _p_i64, _i32, _i32, _p_i32, _p_i32]),
     "pa_bm_seq_len": (C.c_int, [_vp, _i64, _p_i32]),
     "pa_bm_refcount": (C.c_int, [_vp, _i32, _p_i32]),
@@ -78,6 +79,11 @@ SIGNATURES = {
     "pa_decode_step_quant": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, C.c_int,
                                        _f32, _f32, _vp, _sz, _vp]),
+    "pa_decode_window": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                   _i32, _i32, _i32, _f32, _i32, _i32, C.c_int, _vp, _sz, _vp]),
+    "pa_decode_step_window": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                        C.c_int, _vp, _sz, _vp]),
     "pa_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                              _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp]),
     "pa_time_next_attention": (C.c_int, [_vp, _vp]),

@@ -63,6 +63,13 @@ class BlockManager:
     def free_seq(self, seq_id: int):
         check(lib().pa_bm_free_seq(self._h, seq_id), "pa_bm_free_seq")
 
+    def release_before(self, seq_id: int, first_pos: int) -> int:
+        """Sliding window: drop the blocks wholly before first_pos (entries -> -1)."""
+        n = C.c_int32(0)
+        check(lib().pa_bm_release_before(self._h, seq_id, int(first_pos), C.byref(n)),
+              "pa_bm_release_before")
+        return int(n.value)
+
     def block_tables(self, seq_ids, max_blocks: int):
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         tables = np.empty((len(ids), max_blocks), dtype=np.int32)

@@ -83,7 +83,8 @@ class PagedKVCache:
 
     def replay(self, script, rows, k_tok: torch.Tensor, v_tok: torch.Tensor):
         """Runs set-up ops ("add", sid, n) / ("extend", sid, n) / ("fork", p, c) /
-        ("free", sid); written tokens are rows[sid][pos] of k_tok / v_tok."""
+        ("free", sid) / ("release", sid, first_pos); written tokens are
+        rows[sid][pos] of k_tok / v_tok."""
         for op in script:
             if op[0] == "add":
                 _, sid, n = op
@@ -98,6 +99,8 @@ class PagedKVCache:
                 self.fork(op[1], op[2])
             elif op[0] == "free":
                 self.free(op[1])
+            elif op[0] == "release":
+                self.bm.release_before(op[1], op[2])
             else:
                 raise ValueError(op)
 
@@ -115,17 +118,32 @@ class PagedKVCache:
 
     def step(self, plan: StepPlan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
              out: torch.Tensor | None = None, scale=None, partition_size: int = 0,
-             workspace=None, stream=None, fused=True):
+             workspace=None, stream=None, fused=True, window: int = 0):
         """Copy-on-write, append the new tokens, then decode attention (all on device).
 
         fused: True -> one pa_decode_step call; "phased" -> pa_decode_step_partial
         then pa_decode_step_merge; False -> pa_cache_append then pa_decode.  A
         quantized cache: pa_decode_step_quant (fused) or pa_cache_append_quant
-        then pa_decode_quant (False)."""
+        then pa_decode_quant (False).  window > 0: sliding-window attention
+        (pa_decode_step_window, or pa_cache_append then pa_decode_window)."""
         if plan.cows.shape[0]:
             ops.copy_blocks(self.k_pool, self.v_pool, plan.d_cows, stream)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if window:
+            # sliding window: fused step, or append then windowed decode
+            if self.cache_dtype is not None:
+                raise ValueError("a sliding window takes fp32/fp16/bf16 pools")
+            if fused:
+                ops.decode_step(out, q, self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
+                                plan.d_tables, plan.d_lens, plan.max_context_len, scale,
+                                partition_size, workspace, stream, window=window)
+            else:
+                ops.cache_append(self.k_pool, self.v_pool, k_new, v_new, plan.d_slots, stream)
+                ops.decode(out, q, self.k_pool, self.v_pool, plan.d_tables, plan.d_lens,
+                           plan.max_context_len, scale, partition_size, workspace, stream,
+                           window=window)
+            return out
         if self.cache_dtype is not None:
             if fused:
                 ops.decode_step_quant(out, q, self.k_pool, self.v_pool, k_new, v_new,

@@ -11,6 +11,12 @@
 //     than once first copies it (the writer moves to the copy).
 // Choices where the pages are silent: LIFO free stack seeded with free_order,
 // blocks released in table order, all-or-nothing batches.
+// Sliding window (page 1, jisaku.com glossary, section
+// 「他のKVキャッシュ最適化との組み合わせ」: blocks that left the window can be
+// freed): pa_bm_release_before drops a sequence's blocks whose slots all lie
+// before a position; their table entries become -1 (placeholders, so
+// position p keeps mapping to entry p / block_size).
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -22,7 +28,7 @@
 
 struct pa_bm {
   struct Seq {
-    std::vector<int32_t> table;  // logical block -> physical block
+    std::vector<int32_t> table;  // logical block -> physical block (-1: released)
     int32_t len = 0;             // tokens written so far
   };
   int32_t num_blocks = 0;
@@ -145,7 +151,8 @@ extern "C" pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) 
   if (bm->seqs.count(child_id)) return fail(PA_ERR_SEQ_EXISTS, "sequence %lld exists",
                                             static_cast<long long>(child_id));
   pa_bm::Seq child = it->second;
-  for (int32_t b : child.table) ++bm->ref[b];
+  for (int32_t b : child.table)
+    if (b >= 0) ++bm->ref[b];
   bm->seqs.emplace(child_id, std::move(child));
   return pa::ok();
 }
@@ -211,8 +218,30 @@ extern "C" pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
   if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld",
                                         static_cast<long long>(seq_id));
   for (int32_t b : it->second.table)
-    if (--bm->ref[b] == 0) bm->free_stack.push_back(b);
+    if (b >= 0 && --bm->ref[b] == 0) bm->free_stack.push_back(b);
   bm->seqs.erase(it);
+  return pa::ok();
+}
+
+extern "C" pa_status pa_bm_release_before(pa_bm* bm, int64_t seq_id, int32_t first_pos,
+                                          int32_t* released_out) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_release_before: bm is NULL");
+  if (first_pos < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_release_before: first_pos < 0");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld",
+                                        static_cast<long long>(seq_id));
+  pa_bm::Seq& s = it->second;
+  // blocks k with (k + 1) * block_size <= min(first_pos, len)
+  const int32_t whole = std::min(first_pos, s.len) / bm->block_size;
+  int32_t n = 0;
+  for (int32_t k = 0; k < whole; ++k) {
+    const int32_t b = s.table[k];
+    if (b < 0) continue;
+    if (--bm->ref[b] == 0) bm->free_stack.push_back(b);
+    s.table[k] = -1;
+    ++n;
+  }
+  if (released_out) *released_out = n;
   return pa::ok();
 }
 

@@ -63,10 +63,18 @@ struct Params {
   float scale_log2;
   float out_scale;     // factor of the final rows (V scale of a quantized cache, else 1)
   float enc_k, enc_v;  // quantized cache, fused append: fp32 reciprocals of the K/V scales
+  int window;          // sliding window: attend the last `window` positions (0: all)
 };
 
 __device__ inline bool len_valid(int L, const Params& pr) {
   return L >= 0 && L <= pr.max_ctx && L <= pr.max_blocks * kBlockSize;
+}
+
+// First position a sequence of length L attends: L - window with a sliding
+// window, else 0.  Table entries of blocks wholly before it are never read
+// (they may have been released).
+__device__ inline int first_pos(int L, const Params& pr) {
+  return pr.window > 0 ? max(0, L - pr.window) : 0;
 }
 
 // Zero rows for empty sequences, NaN rows for sequences whose length is out of
@@ -98,9 +106,11 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(Params pr) {
     if (p == 0) write_trivial_rows(pr, b, g, L);
     return;
   }
-  const int np = (L + pr.P - 1) / pr.P;
+  // partitions count from the one holding the first attended position
+  const int f = first_pos(L, pr), p0 = f / pr.P;
+  const int np = (L + pr.P - 1) / pr.P - p0;
   if (p >= np) return;
-  const int tok0 = p * pr.P, tok1 = min(L, tok0 + pr.P);
+  const int tok0 = max((p + p0) * pr.P, f), tok1 = min(L, (p + p0 + 1) * pr.P);
 
   const bits* q = static_cast<const bits*>(pr.q) +
                   (static_cast<int64_t>(b) * pr.Hq + g * G) * D;
@@ -534,7 +544,8 @@ struct Engine16 {
   struct Pre {};
   static constexpr int kUnitBlocks = 2;  // blocks per step (one pair)
   __device__ static void prologue(const Params&, int, int, int, Pre&) {}
-  __device__ static void attend_rt(const Params& pr, int b, int g, int blk_begin, int nblk,
+  // no sliding window here (the host rejects a window for this engine)
+  __device__ static void attend_rt(const Params& pr, int b, int g, int blk_begin, int nblk, int,
                                    int tok_end, State& st, const Pre&, bool with_new) {
     if (with_new)
       attend_range<T, D, NPAIR, kSmallGroup, true>(pr, b, g, blk_begin, nblk, tok_end, st);
@@ -732,10 +743,12 @@ __device__ __forceinline__ void prologue4(const Params& pr, int b, int g, int bl
 // with_new (uniform): the range ends at the sequence's last position, which
 // holds the step's new token (fused append).  A run-time flag rather than a
 // template parameter, so the kernel carries one copy of the loop.
+// Positions before tok_begin (a sliding window's start inside the range's
+// first block) are masked like positions past tok_end.
 template <typename T, int D>
 __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_begin, int nblk,
-                                        int tok_end, WaveState4<D>& st, const Prologue4<D>& pre,
-                                        bool with_new) {
+                                        int tok_begin, int tok_end, WaveState4<D>& st,
+                                        const Prologue4<D>& pre, bool with_new) {
   using Fmt = Kv4<T>;
   using Mma = typename Fmt::Mma;
   constexpr bool kCodes = Fmt::kCodes;
@@ -963,7 +976,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
         s0 = Mma::template mma<s % 16>(qr[s / 16], kv, s0);
     });
     const int qpos = (blk_begin + 4 * qd) * kBlockSize;   // position of the quad's token 0
-    const bool valid = qpos + lane < tok_end;
+    const bool valid = qpos + lane < tok_end && qpos + lane >= tok_begin;
     float sv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) sv[e] = valid ? (s0[e] + s1[e]) * pr.scale_log2 : -INFINITY;
@@ -1148,8 +1161,9 @@ struct Engine4 {
     prologue4<D>(pr, b, g, blk_begin, pre);
   }
   __device__ static void attend_rt(const Params& pr, int b, int g, int blk_begin, int nblk,
-                                   int tok_end, State& st, const Pre& pre, bool with_new) {
-    attend4<T, D>(pr, b, g, blk_begin, nblk, tok_end, st, pre, with_new);
+                                   int tok_begin, int tok_end, State& st, const Pre& pre,
+                                   bool with_new) {
+    attend4<T, D>(pr, b, g, blk_begin, nblk, tok_begin, tok_end, st, pre, with_new);
   }
   __device__ static void reset(State& st) { reset_state4(st); }
   __device__ static void emit(const Params& pr, int b, int g, int slot, State& st) {
@@ -1174,13 +1188,18 @@ __global__ __launch_bounds__(64, kWaves) void decode_fixed_kernel(Params pr) {
     if (p == 0) write_trivial_rows(pr, b, g, L);
     return;
   }
-  const int np = (L + pr.P - 1) / pr.P;
+  // partitions count from the one holding the first attended position (a
+  // sliding window's start; 0 without a window)
+  const int f = first_pos(L, pr), p0 = f / pr.P;
+  const int np = (L + pr.P - 1) / pr.P - p0;
   if (p >= np) return;
-  const int tok0 = p * pr.P, tok1 = min(L, tok0 + pr.P);
-  const int blk0 = tok0 / kBlockSize, nblk = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
+  const int tok0 = max((p + p0) * pr.P, f), tok1 = min(L, (p + p0 + 1) * pr.P);
+  const int blk0 = tok0 / kBlockSize;
+  const int nblk = (tok1 - blk0 * kBlockSize + kBlockSize - 1) / kBlockSize;
+  if (blk0 != p * (pr.P / kBlockSize)) Eng::prologue(pr, b, g, blk0, pre);   // window only
   typename Eng::State st;
   Eng::reset(st);
-  Eng::attend_rt(pr, b, g, blk0, nblk, tok1, st, pre, kFused && p == np - 1);
+  Eng::attend_rt(pr, b, g, blk0, nblk, tok0, tok1, st, pre, kFused && p == np - 1);
   Eng::emit(pr, b, g, np == 1 ? -1 : p, st);
 }
 
@@ -1196,9 +1215,13 @@ __global__ __launch_bounds__(64, kWaves) void decode_fixed_kernel(Params pr) {
 // ---------------------------------------------------------------------------
 constexpr int kMinChunkBlocks = 8;
 
+// Units of U blocks of a sequence: from the block holding its first attended
+// position to its last block.
 template <int U>
 __device__ __forceinline__ int units_of(int L, const Params& pr) {
-  return (len_valid(L, pr) && L > 0) ? ((L + kBlockSize - 1) / kBlockSize + U - 1) / U : 0;
+  return (len_valid(L, pr) && L > 0)
+             ? ((L + kBlockSize - 1) / kBlockSize - first_pos(L, pr) / kBlockSize + U - 1) / U
+             : 0;
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
@@ -1298,7 +1321,7 @@ __global__ __launch_bounds__(64, kWaves) void decode_split_kernel(Params pr) {
   const int u_begin = w * sp.C, u_end = min(sp.total, u_begin + sp.C);
   // A segment is the part of the chunk inside one (b, g) range.
   struct Seg {
-    int b, g, base, L, nub, range_first, seg_end, blk_begin, nblk, tok_end;
+    int b, g, base, L, nub, range_first, seg_end, blk_begin, nblk, tok_begin, tok_end;
   };
   auto make_seg = [&](int u, int b, int base) {
     Seg sg;
@@ -1311,8 +1334,10 @@ __global__ __launch_bounds__(64, kWaves) void decode_split_kernel(Params pr) {
     sg.range_first = base + sg.g * sg.nub;                   // first unit of (b, g)
     sg.seg_end = min(u_end, sg.range_first + sg.nub);
     const int nblk_seq = (sg.L + kBlockSize - 1) / kBlockSize;
-    sg.blk_begin = U * q0;
-    sg.nblk = min(U * (q0 + sg.seg_end - u), nblk_seq) - sg.blk_begin;
+    sg.tok_begin = first_pos(sg.L, pr);
+    const int fb = sg.tok_begin / kBlockSize;                  // the range's first block
+    sg.blk_begin = fb + U * q0;
+    sg.nblk = min(fb + U * (q0 + sg.seg_end - u), nblk_seq) - sg.blk_begin;
     sg.tok_end = min(sg.L, (sg.blk_begin + sg.nblk) * kBlockSize);
     return sg;
   };
@@ -1342,14 +1367,14 @@ __global__ __launch_bounds__(64, kWaves) void decode_split_kernel(Params pr) {
       Eng::prologue(pr, nxt.b, nxt.g, nxt.blk_begin, pre_next);
     }
     Eng::reset(st);
-    Eng::attend_rt(pr, cur.b, cur.g, cur.blk_begin, cur.nblk, cur.tok_end, st, pre,
-                   pr.k_new != nullptr && cur.tok_end == cur.L);
+    Eng::attend_rt(pr, cur.b, cur.g, cur.blk_begin, cur.nblk, cur.tok_begin, cur.tok_end, st,
+                   pre, pr.k_new != nullptr && cur.tok_end == cur.L);
     const int first_chunk = cur.range_first / sp.C;
     const int nslots = (cur.range_first + cur.nub - 1) / sp.C - first_chunk + 1;
     Eng::emit(pr, cur.b, cur.g, nslots == 1 ? -1 : w - first_chunk, st);
     // the wave holding the range's first unit records how many slots the
     // merge has to combine
-    if (cur.blk_begin == 0 && lane == 0)
+    if (cur.blk_begin == cur.tok_begin / kBlockSize && lane == 0)
       pr.counters[static_cast<int64_t>(cur.b) * pr.Hkv + cur.g] = nslots;
     if (!more) break;
     cur = nxt;
@@ -1450,7 +1475,7 @@ __global__ __launch_bounds__(D) void merge_kernel(Params pr) {
     if (d < D / 8) *reinterpret_cast<uint4*>(kt + (d * kBlockSize + ts) * 8) = kchunk;
     vt[((ts >> 3) * D + d) * 8 + (ts & 7)] = vval;
   }
-  const int ns = kSplit ? ns_split : (L + pr.P - 1) / pr.P;
+  const int ns = kSplit ? ns_split : (L + pr.P - 1) / pr.P - first_pos(L, pr) / pr.P;
   if (ns <= 1 || !have_ws) return;                            // written final
   float M = -INFINITY;
 #pragma unroll
@@ -1695,7 +1720,7 @@ struct CodeScales {
 };
 
 pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeScales* cs,
-                     float* out, const void* q,
+                     int32_t window, float* out, const void* q,
                      const void* k_pool, const void* v_pool, const int32_t* block_tables,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -1737,6 +1762,12 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
                 partition_size);
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window %d < 0", fn, window);
+  if (window > 0 && num_q_heads / num_kv_heads > 4 &&
+      !make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric)
+           .generic)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: a sliding window on the matrix cores needs <= 4 query heads per KV head", fn);
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
@@ -1778,6 +1809,7 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   // V = v_scale * code (applied to the final rows)
   pr.scale_log2 = (cs ? scale * cs->k_scale : scale) * kLog2e;
   pr.out_scale = cs ? cs->v_scale : 1.0f;
+  pr.window = window;
   if (need > 0) {
     const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * lp.maxP;
     char* ws = static_cast<char*>(workspace);
@@ -1871,15 +1903,15 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
       partition_size, dtype, workspace, workspace_bytes_given, stream
 
 extern "C" pa_status pa_decode(PA_DECODE_ARGS) {
-  return run_decode("pa_decode", Phase::kBoth, nullptr, nullptr, PA_DECODE_FWD);
+  return run_decode("pa_decode", Phase::kBoth, nullptr, nullptr, 0, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_partial(PA_DECODE_ARGS) {
-  return run_decode("pa_decode_partial", Phase::kPartitions, nullptr, nullptr, PA_DECODE_FWD);
+  return run_decode("pa_decode_partial", Phase::kPartitions, nullptr, nullptr, 0, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_merge(PA_DECODE_ARGS) {
-  return run_decode("pa_decode_merge", Phase::kMerge, nullptr, nullptr, PA_DECODE_FWD);
+  return run_decode("pa_decode_merge", Phase::kMerge, nullptr, nullptr, 0, PA_DECODE_FWD);
 }
 
 #define PA_STEP_ARGS                                                                        \
@@ -1896,17 +1928,17 @@ extern "C" pa_status pa_decode_merge(PA_DECODE_ARGS) {
 
 extern "C" pa_status pa_decode_step(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step", Phase::kBoth, &nt, nullptr, PA_STEP_FWD);
+  return run_decode("pa_decode_step", Phase::kBoth, &nt, nullptr, 0, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_step_partial(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step_partial", Phase::kPartitions, &nt, nullptr, PA_STEP_FWD);
+  return run_decode("pa_decode_step_partial", Phase::kPartitions, &nt, nullptr, 0, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_step_merge(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step_merge", Phase::kMerge, &nt, nullptr, PA_STEP_FWD);
+  return run_decode("pa_decode_step_merge", Phase::kMerge, &nt, nullptr, 0, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_quant(float* out, const void* q, const void* k_pool,
@@ -1919,7 +1951,7 @@ extern "C" pa_status pa_decode_quant(float* out, const void* q, const void* k_po
                                      float k_scale, float v_scale, void* workspace,
                                      size_t workspace_bytes_given, void* stream) {
   const CodeScales cs{k_scale, v_scale};
-  return run_decode("pa_decode_quant", Phase::kBoth, nullptr, &cs, PA_DECODE_FWD);
+  return run_decode("pa_decode_quant", Phase::kBoth, nullptr, &cs, 0, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_step_quant(float* out, const void* q, void* k_pool, void* v_pool,
@@ -1936,5 +1968,33 @@ extern "C" pa_status pa_decode_step_quant(float* out, const void* q, void* k_poo
                                           size_t workspace_bytes_given, void* stream) {
   const NewTokens nt{k_new, v_new, slot_mapping};
   const CodeScales cs{k_scale, v_scale};
-  return run_decode("pa_decode_step_quant", Phase::kBoth, &nt, &cs, PA_STEP_FWD);
+  return run_decode("pa_decode_step_quant", Phase::kBoth, &nt, &cs, 0, PA_STEP_FWD);
+}
+
+extern "C" pa_status pa_decode_window(float* out, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, int32_t window, int32_t partition_size,
+                                      pa_dtype dtype, void* workspace,
+                                      size_t workspace_bytes_given, void* stream) {
+  return run_decode("pa_decode_window", Phase::kBoth, nullptr, nullptr, window, PA_DECODE_FWD);
+}
+
+extern "C" pa_status pa_decode_step_window(float* out, const void* q, void* k_pool,
+                                           void* v_pool, const void* k_new, const void* v_new,
+                                           const int64_t* slot_mapping,
+                                           const int32_t* block_tables,
+                                           const int32_t* context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t max_blocks_per_seq,
+                                           int32_t max_context_len, float scale, int32_t window,
+                                           int32_t partition_size, pa_dtype dtype,
+                                           void* workspace, size_t workspace_bytes_given,
+                                           void* stream) {
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  return run_decode("pa_decode_step_window", Phase::kBoth, &nt, nullptr, window, PA_STEP_FWD);
 }

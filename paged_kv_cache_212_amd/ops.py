@@ -137,13 +137,19 @@ EVEN_SPLIT = -1   # partition_size value selecting the even split of the batch's
 
 
 def decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale=None,
-           partition_size=0, workspace=None, stream=None, phase="both"):
+           partition_size=0, workspace=None, stream=None, phase="both", window=0):
     """out [B][Hq][D] float32 = paged decode attention of q [B][Hq][D].
 
     partition_size: > 0 fixed partitions, 0 library default, EVEN_SPLIT (-1).
     phase: "both" (pa_decode), "partial" (pa_decode_partial) or "merge"
-    (pa_decode_merge)."""
+    (pa_decode_merge).  window > 0: sliding-window attention over the last
+    `window` positions (pa_decode_window; phase "both" only)."""
     fn = {"both": "pa_decode", "partial": "pa_decode_partial", "merge": "pa_decode_merge"}[phase]
+    if window:
+        if phase != "both":
+            raise ValueError("a sliding window runs both phases in one call")
+        return _decode_window(out, q, k_pool, v_pool, block_tables, context_lens,
+                              max_context_len, scale, window, partition_size, workspace, stream)
     N, H, D = _pool_dims(k_pool, v_pool)
     B, Hq = q.shape[0], q.shape[1]
     if q.shape != (B, Hq, D) or q.dtype != k_pool.dtype:
@@ -240,16 +246,42 @@ def decode_step_quant(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_
     return out
 
 
+def _decode_window(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale,
+                   window, partition_size, workspace, stream):
+    N, H, D = _pool_dims(k_pool, v_pool)
+    if k_pool.dtype in CODE_DTYPES:
+        raise ValueError("sliding-window decode takes fp32/fp16/bf16 pools")
+    B, Hq = _check_decode_args(out, q, k_pool, block_tables, context_lens, D, k_pool.dtype)
+    scale = D ** -0.5 if scale is None else float(scale)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size, q.dtype,
+                                     q.device)
+    check(lib().pa_decode_window(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                                 _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
+                                 _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
+                                 block_tables.shape[1], int(max_context_len), scale,
+                                 int(window), int(partition_size), pa_dtype(q.dtype),
+                                 _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+          "pa_decode_window")
+    return out
+
+
 def decode_step(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables,
                 context_lens, max_context_len, scale=None, partition_size=0, workspace=None,
-                stream=None, phase="both"):
+                stream=None, phase="both", window=0):
     """Append each sequence's new token (row b of k_new/v_new, slot slot_mapping[b]) and
     decode, in one call (pa_decode_step).
 
     phase: "both" (pa_decode_step), or "partial" then "merge"
-    (pa_decode_step_partial, pa_decode_step_merge; same arguments and workspace)."""
+    (pa_decode_step_partial, pa_decode_step_merge; same arguments and workspace).
+    window > 0: sliding-window attention (pa_decode_step_window; phase "both")."""
     fn = {"both": "pa_decode_step", "partial": "pa_decode_step_partial",
           "merge": "pa_decode_step_merge"}[phase]
+    if window and phase != "both":
+        raise ValueError("a sliding window runs both phases in one call")
+    if window:
+        fn = "pa_decode_step_window"
     N, H, D = _pool_dims(k_pool, v_pool)
     B, Hq = q.shape[0], q.shape[1]
     if q.shape != (B, Hq, D) or q.dtype != k_pool.dtype:
@@ -270,12 +302,13 @@ def decode_step(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables
     if workspace is None:
         workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size, q.dtype,
                                      q.device)
+    win = (int(window),) if window else ()
     check(getattr(lib(), fn)(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
                              _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
                              _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
                              _dev(block_tables, "block_tables"),
                              _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
-                             block_tables.shape[1], int(max_context_len), scale,
+                             block_tables.shape[1], int(max_context_len), scale, *win,
                              int(partition_size), pa_dtype(q.dtype),
                              _dev(workspace, "workspace"),
                              workspace.numel() * workspace.element_size(), _stream(stream)),

@@ -53,7 +53,8 @@ def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None, fused=
     k_new, v_new = k_tok.index_select(0, nr), v_tok.index_select(0, nr)
     q = case.q.to(dev)
     ps = case.partition_size if partition_size is None else partition_size
-    out = cache.step(plan, q, k_new, v_new, partition_size=ps, fused=fused)
+    out = cache.step(plan, q, k_new, v_new, partition_size=ps, fused=fused,
+                     window=getattr(case, "window", 0))
     torch.cuda.synchronize()
     return {"plan": plan, "out": out.cpu().numpy(), "cache": cache, "q": q,
             "k_pool": bits_of(cache.k_pool, case.kv_dtype),

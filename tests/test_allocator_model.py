@@ -113,7 +113,8 @@ def test_error_codes():
 
 
 def random_ops(seed, n_ops=400, num_blocks=96):
-    """Seeded op sequence over add/fork/extend/append/free (shared with the C++ test)."""
+    """Seeded op sequence over add/fork/extend/append/release/free (shared with the
+    C++ test)."""
     rng = np.random.default_rng(seed)
     ops, live, next_id = [], [], 0
     for _ in range(n_ops):
@@ -128,9 +129,11 @@ def random_ops(seed, n_ops=400, num_blocks=96):
             next_id += 1
         elif r < 0.5:
             ops.append(("extend", int(rng.choice(live)), int(rng.integers(0, 40))))
-        elif r < 0.85:
+        elif r < 0.8:
             k = int(rng.integers(1, min(len(live), 8) + 1))
             ops.append(("append", [int(s) for s in rng.choice(live, size=k, replace=False)]))
+        elif r < 0.88:
+            ops.append(("release", int(rng.choice(live)), int(rng.integers(0, 90))))
         else:
             s = int(rng.choice(live))
             ops.append(("free", s))
@@ -155,6 +158,8 @@ def apply_model(am, op):
         if op[0] == "free":
             am.free_seq(op[1])
             return ("ok",)
+        if op[0] == "release":
+            return ("ok", am.release_before(op[1], op[2]))
     except AllocError as e:
         return ("err", e.code)
     raise ValueError(op)

@@ -120,6 +120,31 @@ def test_quantized_cache_calls_reject_bad_arguments_without_launching():
         h.pa_decode_workspace_bytes(64, 32, 8, 128, 2048, 0, PA_BF16)
 
 
+def test_window_calls_reject_bad_arguments_without_launching():
+    h = pk.lib()
+    nul = None
+
+    def dw(window=64, hq=8, hkv=2, dt=PA_BF16):
+        return h.pa_decode_window(nul, nul, nul, nul, nul, nul, 1, hq, hkv, 128, 16, 10, 4, 64,
+                                  0.1, window, 0, dt, nul, 0, nul)
+    assert dw(window=-1) == PA_ERR_INVALID_ARG
+    assert dw(hq=32, hkv=4) == PA_ERR_UNSUPPORTED        # G = 8 on the matrix cores
+    assert dw(dt=PA_INT8) == PA_ERR_INVALID_ARG          # 8-bit pools: pa_decode_quant
+    assert dw() == PA_ERR_INVALID_ARG                    # valid scalars, NULL pointers
+    assert dw(window=0) == PA_ERR_INVALID_ARG            # window 0: the plain decode's checks
+    assert h.pa_decode_step_window(nul, nul, nul, nul, nul, nul, nul, nul, nul, 1, 8, 2, 128,
+                                   16, 10, 4, 64, 0.1, 16, 0, PA_BF16, nul, 0,
+                                   nul) == PA_ERR_INVALID_ARG
+    bm = pk.BlockManager(8, 16)
+    bm.add_seq(1, 40)
+    assert bm.release_before(1, 1000) == 2
+    with pytest.raises(pk.PAError):
+        bm.release_before(1, -5)
+    with pytest.raises(pk.PAError):
+        bm.release_before(2, 5)
+    assert bm.block_tables([1], 3)[0].tolist() == [[-1, -1, 2]]
+
+
 def test_prefill_rejects_bad_scalars_without_launching():
     h = pk.lib()
     nul = None
@@ -187,6 +212,8 @@ def _c_apply(bm, op):
         if op[0] == "free":
             bm.free_seq(op[1])
             return ("ok",)
+        if op[0] == "release":
+            return ("ok", bm.release_before(op[1], op[2]))
     except pk.PAError as e:
         return ("err", e.code)
 
