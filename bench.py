@@ -57,6 +57,10 @@ def parse():
                     help="quantized cache: the same workload with 8-bit K/V codes (FP8 E4M3 "
                          "or INT8, per-pool scales); one pa_decode_step_quant per step "
                          "(attention kernel with the new tokens encoded in, timed; merge)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: the step attends the last W positions; the "
+                         "sequences first release their out-of-window blocks "
+                         "(pa_bm_release_before); one pa_decode_step_window per step")
     ap.add_argument("--no-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -148,7 +152,7 @@ def cpu_baseline(case, budget_s: float):
                            case.block_size)
             decode_ref(qb, kp, vp, ref["tables"], ref["lens"], case.kv_dtype, case.scale,
                        case.block_size, q_dtype=case.dtype, k_scale=case.k_scale,
-                       v_scale=case.v_scale)
+                       v_scale=case.v_scale, window=case.window)
             times.append(time.perf_counter() - t0)
     sec = float(np.mean(times))
     return {"value": round(case.kv_bytes() / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
@@ -282,7 +286,7 @@ def main():
     from paged_kv_cache_212_amd._lib import check, lib
     from paged_kv_cache_212_amd.ops import pa_dtype
     from workloads import make_case
-    from workloads.configs import quantized
+    from workloads.configs import quantized, windowed
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
@@ -290,6 +294,15 @@ def main():
     quant = args.kv_cache is not None
     if quant:
         case = quantized(case, args.kv_cache)
+    window = int(args.window)
+    if window and quant:
+        print(json.dumps({"error": "--window takes fp32/fp16/bf16 pools"}))
+        sys.exit(2)
+    if window:
+        case = windowed(case, window, reuse=False)
+        if args.partition_size is None:
+            # a window keeps every range short: the library's even split
+            case.partition_size = 0
     P = case.partition_size if args.partition_size is None else args.partition_size
     td = case.k_tok.dtype
     pool_td = {"fp8": torch.float8_e4m3fn, "i8": torch.int8}.get(args.kv_cache, td)
@@ -312,6 +325,8 @@ def main():
             replica.extend(op[1], op[2])
         elif op[0] == "fork":
             replica.fork(op[1], op[2])
+        elif op[0] == "release":
+            replica.release_before(op[1], op[2])
         else:
             replica.free_seq(op[1])
     mb_plan = max(-(-int(x) // 16) for x in case.lens)
@@ -347,6 +362,15 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     calls = []
     for kp, vp in layers:
+        if window:
+            # pa_decode_step_window: append + attention over the last W positions (+ merge)
+            dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), k_new.data_ptr(),
+                   v_new.data_ptr(), plan.d_slots.data_ptr(), plan.d_tables.data_ptr(),
+                   plan.d_lens.data_ptr(), B, Hq, Hkv, D, 16, N, MB, plan.max_context_len,
+                   case.scale, window, P, dt, ws.data_ptr(), ws.numel(), stream)
+            calls.append(((kp.data_ptr(), vp.data_ptr(), plan.d_cows.data_ptr(), ncow, N, Hkv,
+                           D, 16, dt, stream), dec, None, None))
+            continue
         if quant:
             # pa_decode_step_quant: quantizing append + attention (+ merge)
             dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), k_new.data_ptr(),
@@ -375,17 +399,20 @@ def main():
     f_step_part, f_step_merge = L.pa_decode_step_partial, L.pa_decode_step_merge
     f_app, f_part, f_merge = L.pa_cache_append, L.pa_decode_partial, L.pa_decode_merge
     f_time = L.pa_time_next_attention
-    f_step_quant = L.pa_decode_step_quant
-    mode = "quant" if quant else args.mode
+    f_step_quant, f_step_window = L.pa_decode_step_quant, L.pa_decode_step_window
+    mode = "quant" if quant else "window" if window else args.mode
 
     def step(i, ev=None, with_copy=True):
         c_copy, c_dec, c_app, c_dec_sep = calls[i % len(calls)]
         if ncow and with_copy:
             check(f_copy(*c_copy), "pa_copy_blocks")
-        if mode == "quant":
+        if mode in ("quant", "window"):
             if ev is not None:
                 check(f_time(ev[0].cuda_event, ev[1].cuda_event), "pa_time_next_attention")
-            check(f_step_quant(*c_dec), "pa_decode_step_quant")
+            if mode == "quant":
+                check(f_step_quant(*c_dec), "pa_decode_step_quant")
+            else:
+                check(f_step_window(*c_dec), "pa_decode_step_window")
             return
         if args.mode == "step":
             if ev is not None:
@@ -464,7 +491,9 @@ def main():
                                   f"D={D}, block 16, "
                                   + (f"{case.kv_dtype} KV codes (per-pool scales, widened "
                                      f"to bf16 on the matrix cores)" if quant else
-                                     f"{case.dtype} KV") + ", fp32 out",
+                                     f"{case.dtype} KV") + ", fp32 out"
+                                  + (f", sliding window of {window} positions (out-of-window "
+                                     f"blocks released)" if window else ""),
                       "global_batch": B, "context_tokens": int(case.lens.sum()),
                       "max_context_len": plan.max_context_len, "partition_size": P_used,
                       "cow_copies": ncow, "layers_rotated": args.layers,
@@ -477,6 +506,8 @@ def main():
            "value_unique_gbs": round(kv_unique / (ms_step * 1e-3) / 1e9, 2),
            "stream_read_context": stream_ctx,
            "host_plan_us": round(host_plan_us, 1),
+           "pool_blocks_used": int(cache.bm.stats()["used_blocks"]),
+           "pool_blocks_without_window": int(sum(-(-int(x) // 16) for x in case.lens)),
            "wall_ms_timed_region": round(wall_ms, 3)}
     if evs:
         kern_us = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
@@ -489,18 +520,23 @@ def main():
                             for i in range(len(evs) - 1)]) * 1e3
             res["step_us_p10_p50_p90"] = [round(float(x), 3) for x in
                                           np.percentile(per, [10, 50, 90])]
-        tables_bytes = int(sum(-(-int(x) // 16) for x in case.lens)) * 4
+        # table entries walked: from the block holding the first attended position
+        tables_bytes = int(sum(-(-int(x) // 16) - (int(x) - int(a)) // 16
+                               for x, a in zip(case.lens, case.attended_lens()))) * 4
         # K/V of every attended token, q, the table entries walked, the lengths and
         # the fp32 output; in the phased step the kernel also reads the new
         # tokens (k_new, v_new) and the slot indices
         alg = kv_bytes + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
-        if mode in ("phased", "quant"):
+        if mode in ("phased", "quant", "window"):
             alg += 2 * k_new.numel() * k_new.element_size() + B * 8
         achieved = alg / (part_ms * 1e-3) / 1e9
         res["attention_kernel_us"] = round(dec_ms * 1e3, 3)
         if mode == "quant":
             kname = (f"attention kernel of pa_decode_step_quant ({case.kv_dtype} codes; new "
                      f"tokens encoded and fused in)")
+        elif mode == "window":
+            kname = (f"attention kernel of pa_decode_step_window (last {window} positions; new "
+                     f"tokens fused in)")
         elif mode == "separate":
             kname = "attention partition kernel (pa_decode_partial)"
         elif args.mode == "phased":
