@@ -28,6 +28,11 @@ same choices so tables compare bit for bit):
   than are free nothing changes;
 * slot = physical_block * block_size + position % block_size.
 
+Beam search and parallel sampling (page 3, section
+「並列サンプリングやビームサーチでの共有」): ``reorder`` continues each new
+sequence from a parent of the previous step by fork, then frees the dropped
+ones; the next write into a shared last block copies it.
+
 Sliding window (page 1, jisaku.com glossary, section
 「他のKVキャッシュ最適化との組み合わせ」: with a sliding window, blocks that
 have left the window can be released to save memory on long contexts):
@@ -171,6 +176,37 @@ class AllocatorModel:
                 self.free.append(b)
         del self.tables[sid]
         del self.lens[sid]
+
+    def reorder(self, old_ids, new_ids, parents):
+        """Beam search / parallel sampling step: sequence new_ids[j] continues
+        old_ids[parents[j]].  A new id equal to its parent's id keeps that
+        sequence; any other new id is a fork of the parent (shared blocks,
+        no copy); then every old id that is not among new_ids is freed.
+        Forks come before frees, so a block shared by a dropped parent and
+        its children is never released.  All-or-nothing: ids are checked
+        first (unknown old id, repeated old or new id, parent index out of
+        range, new id already live and not its own parent)."""
+        old_ids = [int(x) for x in old_ids]
+        new_ids = [int(x) for x in new_ids]
+        parents = [int(p) for p in parents]
+        if len(parents) != len(new_ids):
+            raise AllocError(INVALID_ARG, "one parent per new id")
+        if len(set(old_ids)) != len(old_ids) or len(set(new_ids)) != len(new_ids):
+            raise AllocError(INVALID_ARG, "repeated id")
+        for o in old_ids:
+            self._seq(o)
+        for n, p in zip(new_ids, parents):
+            if not 0 <= p < len(old_ids):
+                raise AllocError(INVALID_ARG, "parent index out of range")
+            if n != old_ids[p] and n in self.tables:
+                raise AllocError(SEQ_EXISTS, f"sequence {n} exists")
+        for n, p in zip(new_ids, parents):
+            if n != old_ids[p]:
+                self.fork(old_ids[p], n)
+        keep = set(new_ids)
+        for o in old_ids:
+            if o not in keep:
+                self.free_seq(o)
 
     def release_before(self, sid: int, first_pos: int) -> int:
         """Drops the blocks of sid whose 16 slots all lie before first_pos

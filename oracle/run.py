@@ -43,6 +43,8 @@ def run_script(am: AllocatorModel, script, rows, on_write=None, on_copy=None):
             am.free_seq(op[1])
         elif kind == "release":
             am.release_before(op[1], op[2])
+        elif kind == "reorder":
+            am.reorder(op[1], op[2], op[3])
         else:
             raise ValueError(op)
 

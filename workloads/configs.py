@@ -110,6 +110,72 @@ def quantized(case: Case, cache_dtype: str) -> Case:
     return replace(case, name=name, cache_dtype=cache_dtype, k_scale=ks, v_scale=vs)
 
 
+def beam_case(seed: int, dtype: str, n_prompts: int, beams: int, prompt_len: int, steps: int,
+              hq: int, hkv: int, d: int, device="cpu", *, pool_factor: float = 1.3) -> Case:
+    """Beam search over ``steps`` decode steps, then one more step as the
+    case's step.  Each prompt is written once and forked into ``beams``
+    sequences; at every later step each beam picks a parent among its
+    prompt's beams of the previous step (seeded draws with replacement,
+    sorted), a parent's first child keeps its id, the others are forks under
+    fresh ids, and parents without children are freed (op ``("reorder", old,
+    new, parents)``); then every beam appends one token (op ``("extend",
+    sid, 1)``, with the copy-on-write of a shared last block).  Every
+    (step, beam) token has a row of its own; a beam's rows are its parent's
+    plus its new one."""
+    rng = np.random.default_rng(seed)
+    script, rows = [], {}
+    R = n_prompts * prompt_len
+    next_row = R
+    live = []                                         # per prompt: beam ids
+    next_id = 0
+    for p in range(n_prompts):
+        pid = 10_000_000 + p
+        rows[pid] = np.arange(p * prompt_len, (p + 1) * prompt_len, dtype=np.int64)
+        script.append(("add", pid, prompt_len))
+        ids = []
+        for _ in range(beams):
+            script.append(("fork", pid, next_id))
+            rows[next_id] = rows[pid]
+            ids.append(next_id)
+            next_id += 1
+        script.append(("free", pid))
+        live.append(ids)
+    for t in range(steps + 1):
+        if t > 0:                                    # reorder, then append
+            for p in range(n_prompts):
+                old = live[p]
+                parents = np.sort(rng.integers(0, beams, size=beams))
+                new, seen = [], set()
+                for par in parents.tolist():
+                    if par not in seen:
+                        seen.add(par)
+                        new.append(old[par])
+                    else:
+                        new.append(next_id)
+                        rows[next_id] = rows[old[par]]
+                        next_id += 1
+                script.append(("reorder", list(old), list(new), parents.tolist()))
+                live[p] = new
+        for p in range(n_prompts):
+            for sid in live[p]:
+                rows[sid] = np.concatenate([rows[sid], [next_row]])
+                next_row += 1
+                if t < steps:
+                    script.append(("extend", sid, 1))
+    batch = np.array([sid for ids in live for sid in ids], dtype=np.int64)
+    lens = np.array([len(rows[s]) for s in batch.tolist()], dtype=np.int32)
+    # blocks: prompts once, then at most one new block per beam per 16 steps
+    # plus one copy per beam per step
+    need = n_prompts * -(-prompt_len // 16) + n_prompts * beams * (steps + 2) * 2
+    num_blocks = int(math.ceil(pool_factor * need))
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    B = len(batch)
+    q, k, v = _draw_values(seed, (B, hq, d), (next_row, hkv, d), dtype, device)
+    notes = {"prompts": n_prompts, "beams": beams, "steps": steps}
+    return Case(f"beam_{dtype}_{n_prompts}x{beams}_p{prompt_len}_s{steps}", dtype, hq, hkv, d, 16,
+                num_blocks, free_order, script, batch, lens, rows, q, k, v, 0, notes)
+
+
 def windowed(case: Case, window: int, reuse: bool = True) -> Case:
     """The same step with sliding-window attention over the last ``window``
     positions.  Before the step each batch sequence releases the blocks wholly
