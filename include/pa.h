@@ -147,6 +147,21 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n, int64
 /* Releases a sequence: counts -1, blocks reaching zero return to the pool. */
 pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
 
+/* Beam search / parallel sampling step (page 3, abeam.tech review, section
+ * 「並列サンプリングやビームサーチでの共有」: beams share blocks; a shared block
+ * is copied on write).  Sequence new_ids[j] continues old_ids[parents[j]]:
+ * the same id keeps that sequence, another id becomes a fork of it (shared
+ * blocks, no copy); then every old id not among new_ids is released.  Forks
+ * come before releases, so blocks of a dropped parent live on in its
+ * children.  The next write into a shared last block is copied by
+ * pa_bm_append_slots as usual.  All-or-nothing: PA_ERR_UNKNOWN_SEQ for an
+ * unknown old id, PA_ERR_INVALID_ARG for a repeated old or new id or a parent
+ * index outside [0, num_old), PA_ERR_SEQ_EXISTS for a new id that is live
+ * and not its own parent; nothing changes then.  Host arrays:
+ * old_ids [num_old], new_ids and parents [num_new]. */
+pa_status pa_bm_reorder(pa_bm* bm, const int64_t* old_ids, int32_t num_old,
+                        const int64_t* new_ids, const int32_t* parents, int32_t num_new);
+
 /* Sliding window: drops the blocks of a sequence whose block_size slots all
  * lie before position first_pos (clamped to the sequence's length), i.e.
  * logical blocks k with (k+1)*block_size <= min(first_pos, len).  Their
@@ -213,6 +228,21 @@ pa_status pa_cache_append_quant(void* k_pool, void* v_pool, const void* k_new, c
 pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
                          int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, pa_dtype dtype, void* stream);
+
+/* pa_copy_blocks over the pools of several layers in one launch: for each
+ * layer l < num_layers and pair (src, dst), block dst := block src in
+ * k_pools[l] and v_pools[l] (device arrays of num_layers pool pointers, each
+ * pool laid out as for pa_copy_blocks with the same num_blocks, heads,
+ * head_dim and dtype).  A model with one cache per layer copies a step's
+ * copy-on-write pairs in every layer (page 3, section
+ * 「並列サンプリングやビームサーチでの共有」).  Pairs and layers run
+ * concurrently: no dst may equal another pair's src or dst.  Out-of-range
+ * pairs are skipped; every pool must be 16-byte aligned (not checked: the
+ * pointers are on the device). */
+pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                                const int32_t* block_pairs, int32_t num_pairs,
+                                int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, pa_dtype dtype, void* stream);
 
 /* How pa_decode splits contexts for these arguments; partition_size is
  *   > 0 (a multiple of 16): fixed partitions of that many tokens;

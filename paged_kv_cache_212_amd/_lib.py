@@ -47,6 +47,9 @@ SIGNATURES = {
     "pa_bm_append_slots": (C.c_int, [_vp, _p_i64, _i32, _p_i64, _p_i32, _p_i32]),
     "pa_bm_free_seq": (C.c_int, [_vp, _i64]),
     "pa_bm_release_before": (C.c_int, [_vp, _i64, _i32, _p_i32]),
+    "pa_bm_reorder": (C.c_int, [_vp, _p_i64, _i32, _p_i64, _p_i32, _i32]),
+    "pa_copy_blocks_layers": (C.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        C.c_int, _vp]),
     "pa_bm_block_tables": (C.c_int, [_vp, _p_i64, _i32, _i32, _p_i32, _p_i32]),
     "pa_bm_seq_len": (C.c_int, [_vp, _i64, _p_i32]),
     "pa_bm_refcount": (C.c_int, [_vp, _i32, _p_i32]),

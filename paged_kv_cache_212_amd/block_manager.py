@@ -63,6 +63,17 @@ class BlockManager:
     def free_seq(self, seq_id: int):
         check(lib().pa_bm_free_seq(self._h, seq_id), "pa_bm_free_seq")
 
+    def reorder(self, old_ids, new_ids, parents):
+        """Beam step: new_ids[j] continues old_ids[parents[j]] (fork unless the
+        same id); old ids not among new_ids are released."""
+        o = np.ascontiguousarray(old_ids, dtype=np.int64)
+        n = np.ascontiguousarray(new_ids, dtype=np.int64)
+        p = np.ascontiguousarray(parents, dtype=np.int32)
+        if p.shape != n.shape:
+            raise ValueError("one parent per new id")
+        check(lib().pa_bm_reorder(self._h, _ptr(o, C.c_int64), len(o), _ptr(n, C.c_int64),
+                                  _ptr(p, C.c_int32), len(n)), "pa_bm_reorder")
+
     def release_before(self, seq_id: int, first_pos: int) -> int:
         """Sliding window: drop the blocks wholly before first_pos (entries -> -1)."""
         n = C.c_int32(0)

@@ -83,7 +83,8 @@ class PagedKVCache:
 
     def replay(self, script, rows, k_tok: torch.Tensor, v_tok: torch.Tensor):
         """Runs set-up ops ("add", sid, n) / ("extend", sid, n) / ("fork", p, c) /
-        ("free", sid) / ("release", sid, first_pos); written tokens are
+        ("free", sid) / ("release", sid, first_pos) / ("reorder", old, new,
+        parents); written tokens are
         rows[sid][pos] of k_tok / v_tok."""
         for op in script:
             if op[0] == "add":
@@ -101,6 +102,8 @@ class PagedKVCache:
                 self.free(op[1])
             elif op[0] == "release":
                 self.bm.release_before(op[1], op[2])
+            elif op[0] == "reorder":
+                self.bm.reorder(op[1], op[2], op[3])
             else:
                 raise ValueError(op)
 

@@ -223,6 +223,52 @@ extern "C" pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
   return pa::ok();
 }
 
+extern "C" pa_status pa_bm_reorder(pa_bm* bm, const int64_t* old_ids, int32_t num_old,
+                                   const int64_t* new_ids, const int32_t* parents,
+                                   int32_t num_new) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_reorder: bm is NULL");
+  if (num_old < 0 || num_new < 0 || (num_old > 0 && !old_ids) ||
+      (num_new > 0 && (!new_ids || !parents)))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_reorder: bad count or NULL buffer");
+  // validate everything first: the call is all-or-nothing
+  std::unordered_set<int64_t> olds, news;
+  olds.reserve(2 * num_old + 1);
+  news.reserve(2 * num_new + 1);
+  for (int32_t i = 0; i < num_old; ++i) {
+    if (!bm->seqs.count(old_ids[i]))
+      return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", static_cast<long long>(old_ids[i]));
+    if (!olds.insert(old_ids[i]).second)
+      return fail(PA_ERR_INVALID_ARG, "pa_bm_reorder: old id %lld repeated",
+                  static_cast<long long>(old_ids[i]));
+  }
+  for (int32_t j = 0; j < num_new; ++j) {
+    if (!news.insert(new_ids[j]).second)
+      return fail(PA_ERR_INVALID_ARG, "pa_bm_reorder: new id %lld repeated",
+                  static_cast<long long>(new_ids[j]));
+    if (parents[j] < 0 || parents[j] >= num_old)
+      return fail(PA_ERR_INVALID_ARG, "pa_bm_reorder: parent index %d out of range", parents[j]);
+    if (new_ids[j] != old_ids[parents[j]] && bm->seqs.count(new_ids[j]))
+      return fail(PA_ERR_SEQ_EXISTS, "sequence %lld exists", static_cast<long long>(new_ids[j]));
+  }
+  // forks first, so blocks of dropped parents stay alive for their children
+  for (int32_t j = 0; j < num_new; ++j) {
+    const int64_t parent = old_ids[parents[j]];
+    if (new_ids[j] == parent) continue;
+    pa_bm::Seq child = bm->seqs.find(parent)->second;
+    for (int32_t b : child.table)
+      if (b >= 0) ++bm->ref[b];
+    bm->seqs.emplace(new_ids[j], std::move(child));
+  }
+  for (int32_t i = 0; i < num_old; ++i) {
+    if (news.count(old_ids[i])) continue;
+    auto it = bm->seqs.find(old_ids[i]);
+    for (int32_t b : it->second.table)
+      if (b >= 0 && --bm->ref[b] == 0) bm->free_stack.push_back(b);
+    bm->seqs.erase(it);
+  }
+  return pa::ok();
+}
+
 extern "C" pa_status pa_bm_release_before(pa_bm* bm, int64_t seq_id, int32_t first_pos,
                                           int32_t* released_out) {
   if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_release_before: bm is NULL");

@@ -107,6 +107,20 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kp
   for (int64_t c = threadIdx.x; c < chunks_per_block; c += blockDim.x) d[c] = s[c];
 }
 
+// grid = (num_pairs, 2 * num_layers): y = 2 * layer + (0: K pool, 1: V pool).
+// Each workgroup copies one whole physical block of one pool of one layer.
+__global__ __launch_bounds__(256) void copy_blocks_layers_kernel(
+    uint4* const* __restrict__ kpools, uint4* const* __restrict__ vpools,
+    const int32_t* __restrict__ pairs, int num_blocks, int64_t chunks_per_block) {
+  const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  const int layer = blockIdx.y >> 1;
+  uint4* pool = (blockIdx.y & 1) ? vpools[layer] : kpools[layer];
+  const uint4* s = pool + static_cast<int64_t>(src) * chunks_per_block;
+  uint4* d = pool + static_cast<int64_t>(dst) * chunks_per_block;
+  for (int64_t c = threadIdx.x; c < chunks_per_block; c += blockDim.x) d[c] = s[c];
+}
+
 // grid = (ceil(max_len/16), Hkv, B): one logical block of one head per
 // workgroup, written to [B][Hkv][max_len][D] in logical order.
 template <typename T>
@@ -308,6 +322,28 @@ extern "C" pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* b
       static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), block_pairs, num_blocks,
       block_bytes / 16);
   return launch_status("pa_copy_blocks");
+}
+
+extern "C" pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools,
+                                           int32_t num_layers, const int32_t* block_pairs,
+                                           int32_t num_pairs, int32_t num_blocks,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, pa_dtype dtype, void* stream) {
+  const char* fn = "pa_copy_blocks_layers";
+  pa_status st = check_common(fn, num_blocks, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0 || num_layers < 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: negative count", fn);
+  if (num_layers > 32767) return fail(PA_ERR_INVALID_ARG, "%s: too many layers", fn);
+  if (num_pairs == 0 || num_layers == 0) return ok();
+  if (!k_pools || !v_pools || !block_pairs) return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * kBlockSize *
+                              static_cast<int64_t>(dtype_bytes(dtype));
+  dim3 grid(num_pairs, 2 * num_layers), block(256);
+  copy_blocks_layers_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<uint4* const*>(k_pools), reinterpret_cast<uint4* const*>(v_pools),
+      block_pairs, num_blocks, block_bytes / 16);
+  return launch_status(fn);
 }
 
 extern "C" pa_status pa_gather_kv(void* k_out, void* v_out, const void* k_pool,

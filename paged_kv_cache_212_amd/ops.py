@@ -112,6 +112,34 @@ def copy_blocks(k_pool, v_pool, block_pairs, stream=None):
                                pa_dtype(k_pool.dtype), _stream(stream)), "pa_copy_blocks")
 
 
+def copy_blocks_layers(k_pools, v_pools, block_pairs, stream=None):
+    """block dst := block src in every layer's pools (lists of pool tensors of
+    one shape and dtype), one launch (pa_copy_blocks_layers)."""
+    if len(k_pools) != len(v_pools) or not k_pools:
+        raise ValueError("one K and one V pool per layer")
+    N, H, D = _pool_dims(k_pools[0], v_pools[0])
+    for kp, vp in zip(k_pools, v_pools):
+        if _pool_dims(kp, vp) != (N, H, D) or kp.dtype != k_pools[0].dtype:
+            raise ValueError("all layers' pools must have one shape and dtype")
+        _dev(kp, "k_pool")
+        _dev(vp, "v_pool")
+    n = block_pairs.shape[0]
+    if n == 0:
+        return
+    if block_pairs.dtype != torch.int32 or block_pairs.shape != (n, 2):
+        raise ValueError("block_pairs must be int32 [n][2]")
+    dev = k_pools[0].device
+    kptr = torch.tensor([t.data_ptr() for t in k_pools], dtype=torch.int64, device=dev)
+    vptr = torch.tensor([t.data_ptr() for t in v_pools], dtype=torch.int64, device=dev)
+    check(lib().pa_copy_blocks_layers(kptr.data_ptr(), vptr.data_ptr(), len(k_pools),
+                                      _dev(block_pairs, "block_pairs"), n, N, H, D, BLOCK_SIZE,
+                                      pa_dtype(k_pools[0].dtype), _stream(stream)),
+          "pa_copy_blocks_layers")
+    if stream is not None:   # the pointer arrays stay valid until the copy has run
+        kptr.record_stream(stream)
+        vptr.record_stream(stream)
+
+
 def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                           partition_size, dtype) -> int:
     return int(lib().pa_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -113,8 +113,8 @@ def test_error_codes():
 
 
 def random_ops(seed, n_ops=400, num_blocks=96):
-    """Seeded op sequence over add/fork/extend/append/release/free (shared with the
-    C++ test)."""
+    """Seeded op sequence over add/fork/extend/append/release/reorder/free (shared
+    with the C++ test)."""
     rng = np.random.default_rng(seed)
     ops, live, next_id = [], [], 0
     for _ in range(n_ops):
@@ -134,6 +134,25 @@ def random_ops(seed, n_ops=400, num_blocks=96):
             ops.append(("append", [int(s) for s in rng.choice(live, size=k, replace=False)]))
         elif r < 0.88:
             ops.append(("release", int(rng.choice(live)), int(rng.integers(0, 90))))
+        elif r < 0.93:
+            # a beam step over a few live sequences (sometimes a bad parent index)
+            k = int(rng.integers(1, min(len(live), 4) + 1))
+            old = [int(s) for s in rng.choice(live, size=k, replace=False)]
+            parents = sorted(int(p) for p in rng.integers(0, k, size=k))
+            if rng.random() < 0.1:
+                parents[-1] = k
+            new, seen = [], set()
+            for p in parents:
+                if p < k and p not in seen:
+                    seen.add(p)
+                    new.append(old[p])
+                else:
+                    new.append(next_id)
+                    next_id += 1
+            ops.append(("reorder", old, new, parents))
+            if parents[-1] < k:
+                live = [s for s in live if s not in old or s in new] + \
+                    [s for s in new if s not in old]
         else:
             s = int(rng.choice(live))
             ops.append(("free", s))
@@ -160,6 +179,9 @@ def apply_model(am, op):
             return ("ok",)
         if op[0] == "release":
             return ("ok", am.release_before(op[1], op[2]))
+        if op[0] == "reorder":
+            am.reorder(op[1], op[2], op[3])
+            return ("ok",)
     except AllocError as e:
         return ("err", e.code)
     raise ValueError(op)
@@ -174,7 +196,8 @@ def test_random_ops_keep_invariants(seed):
         r = apply_model(am, op)
         if r[0] == "err":
             n_err += 1
-            assert r[1] in (OUT_OF_BLOCKS, UNKNOWN_SEQ)
+            assert r[1] in (OUT_OF_BLOCKS, UNKNOWN_SEQ) or \
+                (op[0] == "reorder" and r[1] == INVALID_ARG)   # the injected bad parent
         am.check_invariants()
         # every slot of every sequence maps into its own table
         for sid, t in am.tables.items():

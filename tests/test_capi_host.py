@@ -145,6 +145,36 @@ def test_window_calls_reject_bad_arguments_without_launching():
     assert bm.block_tables([1], 3)[0].tolist() == [[-1, -1, 2]]
 
 
+def test_beam_calls_reject_bad_arguments_without_launching():
+    h = pk.lib()
+    nul = None
+    # multi-layer copy: scalar checks before any launch
+    assert h.pa_copy_blocks_layers(nul, nul, 4, nul, 3, 10, 8, 128, 16, 9, nul) == \
+        PA_ERR_INVALID_ARG                                       # unknown dtype
+    assert h.pa_copy_blocks_layers(nul, nul, 4, nul, 3, 10, 8, 128, 8, PA_BF16, nul) == \
+        PA_ERR_UNSUPPORTED                                       # block size 8
+    assert h.pa_copy_blocks_layers(nul, nul, -1, nul, 3, 10, 8, 128, 16, PA_BF16, nul) == \
+        PA_ERR_INVALID_ARG
+    assert h.pa_copy_blocks_layers(nul, nul, 4, nul, 3, 10, 8, 128, 16, PA_BF16, nul) == \
+        PA_ERR_INVALID_ARG                                       # NULL pointers
+    assert h.pa_copy_blocks_layers(nul, nul, 4, nul, 0, 10, 8, 128, 16, PA_BF16, nul) == 0
+    assert h.pa_copy_blocks_layers(nul, nul, 0, nul, 3, 10, 8, 128, 16, PA_INT8, nul) == 0
+    # reorder: all-or-nothing
+    bm = pk.BlockManager(8, 16)
+    bm.add_seq(0, 20)
+    bm.add_seq(1, 3)
+    before = (bm.stats(), bm.block_tables([0, 1], 2))
+    for args in (([0, 9], [0], [0]), ([0, 0], [0], [0]), ([0], [3, 3], [0, 0]),
+                 ([0], [3], [1]), ([0], [1], [0])):
+        with pytest.raises(pk.PAError):
+            bm.reorder(*args)
+        after = (bm.stats(), bm.block_tables([0, 1], 2))
+        assert after[0] == before[0] and np.array_equal(after[1][0], before[1][0])
+    bm.reorder([0, 1], [0, 7], [0, 0])                          # 7 forks 0, 1 is dropped
+    assert bm.block_tables([0, 7], 2)[0].tolist() == [[0, 1], [0, 1]]
+    assert bm.refcount(0) == 2 and bm.refcount(2) == 0
+
+
 def test_prefill_rejects_bad_scalars_without_launching():
     h = pk.lib()
     nul = None
@@ -214,6 +244,9 @@ def _c_apply(bm, op):
             return ("ok",)
         if op[0] == "release":
             return ("ok", bm.release_before(op[1], op[2]))
+        if op[0] == "reorder":
+            bm.reorder(op[1], op[2], op[3])
+            return ("ok",)
     except pk.PAError as e:
         return ("err", e.code)
 
