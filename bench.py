@@ -61,6 +61,10 @@ def parse():
                     help="sliding window: the step attends the last W positions; the "
                          "sequences first release their out-of-window blocks "
                          "(pa_bm_release_before); one pa_decode_step_window per step")
+    ap.add_argument("--beam", action="store_true",
+                    help="measure a beam-search loop instead (16 prompts x 4 beams, "
+                         "reorder + copy-on-write over --beam-layers layers + decode per layer)")
+    ap.add_argument("--beam-layers", type=int, default=8)
     ap.add_argument("--no-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -228,6 +232,157 @@ def prefill_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def beam_bench(args):
+    """Beam search over the paged cache: 16 prompts of 1024 tokens x 4 beams
+    (64 sequences, Llama-3-8B heads, bf16), --beam-layers layers of pools.
+    A step is: host bookkeeping (draw parents, pa_bm_reorder, pa_bm_append_slots,
+    block-table export, upload), pa_copy_blocks_layers over every layer, then
+    one pa_decode_step per layer (new token appended, attention, merge).
+    Reported: µs per step (wall, synchronised each step as a sampler would),
+    the device part, the copy kernel against HBM, and blocks in use against
+    the same beams without sharing."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_212_amd as pk
+    from paged_kv_cache_212_amd._lib import check, lib
+    from paged_kv_cache_212_amd.ops import pa_dtype
+
+    P, K, plen, Hq, Hkv, D = 16, 4, 1024, 32, 8, 128
+    nl = args.beam_layers
+    B = P * K
+    steps, warmup = min(args.steps, 128), min(args.warmup, 16)
+    total_steps = warmup + steps
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    rng = np.random.default_rng(31)
+    N = P * (plen // 16) + B * (total_steps // 16 + 3) * 2 + 64
+    bm = pk.BlockManager(N, 16, rng.permutation(N).astype(np.int32))
+    g = torch.Generator(device=dev).manual_seed(31)
+    pools = [pk.ops.new_pools(N, Hkv, D, torch.bfloat16, dev, fill=0) for _ in range(nl)]
+    ids = []
+    for p in range(P):
+        pid = 1_000_000 + p
+        slots = bm.add_seq(pid, plen)
+        d_slots = torch.from_numpy(slots.astype(np.int64)).to(dev)
+        for kp, vp in pools:
+            kk = torch.randn((plen, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+            vv = torch.randn((plen, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+            pk.ops.cache_append(kp, vp, kk, vv, d_slots)
+        for k in range(K):
+            bm.fork(pid, p * K + k)
+            ids.append(p * K + k)
+        bm.free_seq(pid)
+    next_id = B
+    q = [torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(nl)]
+    k_new = [torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(nl)]
+    v_new = [torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(nl)]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    maxL = plen + total_steps + 1
+    MB = -(-maxL // 16)
+    ws = pk.ops.decode_workspace(B, Hq, Hkv, D, maxL, 0, torch.bfloat16, dev)
+    kptr = torch.tensor([kp.data_ptr() for kp, _ in pools], dtype=torch.int64, device=dev)
+    vptr = torch.tensor([vp.data_ptr() for _, vp in pools], dtype=torch.int64, device=dev)
+    L = lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    dt = pa_dtype(torch.bfloat16)
+    block_bytes = Hkv * 16 * D * 2
+    host_us, cpp_us, wall_us, dev_us, copy_us, ncopies = [], [], [], [], [], []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    # one pinned staging buffer and one upload per step: slots (int64), then
+    # the int32 copy pairs, tables and lengths
+    n32 = 2 * B + B * MB + B
+    stage = torch.empty(B * 8 + n32 * 4, dtype=torch.uint8, pin_memory=True)
+    d_stage = torch.empty_like(stage, device=dev)
+    st_np = stage.numpy()
+    base = np.arange(P)[:, None] * K
+    import gc
+    gc.disable()        # no collector pauses inside the timed host work
+    for t in range(total_steps):
+        w0 = time.perf_counter()
+        # parents per prompt: sorted draws with replacement; a parent's first
+        # child keeps its id, later children get fresh ids
+        par = np.sort(rng.integers(0, K, size=(P, K)), axis=1)
+        first = np.ones((P, K), dtype=bool)
+        first[:, 1:] = par[:, 1:] != par[:, :-1]
+        parents = (base + par).ravel()
+        old = np.asarray(ids, dtype=np.int64)
+        new = old[parents].copy()
+        nfresh = int((~first).sum())
+        new[~first.ravel()] = np.arange(next_id, next_id + nfresh)
+        next_id += nfresh
+        c0 = time.perf_counter()
+        bm.reorder(old, new, parents)
+        ids = new
+        slots, cows = bm.append_slots(ids)
+        tables, lens = bm.block_tables(ids, MB)
+        c1 = time.perf_counter()
+        nc = len(cows)
+        st_np[:B * 8] = slots.view(np.uint8)
+        i32 = st_np[B * 8:].view(np.int32)
+        i32[:2 * nc] = cows.reshape(-1)
+        i32[2 * B:2 * B + B * MB] = tables.reshape(-1)
+        i32[2 * B + B * MB:] = lens
+        d_stage.copy_(stage, non_blocking=True)
+        d_i32 = d_stage[B * 8:].view(torch.int32)
+        d_slots = d_stage[:B * 8].view(torch.int64)
+        d_cows = d_i32[:2 * B]
+        d_tables = d_i32[2 * B:2 * B + B * MB]
+        d_lens = d_i32[2 * B + B * MB:]
+        h1 = time.perf_counter()
+        ev[0].record()
+        ev[1].record()
+        if nc:
+            check(L.pa_copy_blocks_layers(kptr.data_ptr(), vptr.data_ptr(), nl, d_cows.data_ptr(),
+                                          nc, N, Hkv, D, 16, dt, stream), "pa_copy_blocks_layers")
+        ev[2].record()
+        for li, (kp, vp) in enumerate(pools):
+            check(L.pa_decode_step(out.data_ptr(), q[li].data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                                   k_new[li].data_ptr(), v_new[li].data_ptr(), d_slots.data_ptr(),
+                                   d_tables.data_ptr(), d_lens.data_ptr(), B, Hq, Hkv, D, 16, N,
+                                   MB, int(lens.max()), D ** -0.5, 0, dt, ws.data_ptr(),
+                                   ws.numel(), stream), "pa_decode_step")
+        ev[3].record()
+        torch.cuda.synchronize()
+        w1 = time.perf_counter()
+        if t >= warmup:
+            host_us.append((h1 - w0) * 1e6)
+            cpp_us.append((c1 - c0) * 1e6)
+            wall_us.append((w1 - w0) * 1e6)
+            dev_us.append(ev[0].elapsed_time(ev[3]) * 1e3)
+            copy_us.append(ev[1].elapsed_time(ev[2]) * 1e3)
+            ncopies.append(nc)
+    gc.enable()
+    st = bm.stats()
+    unshared = int(sum(-(-int(x) // 16) for x in lens))
+    pairs = float(np.mean(ncopies))
+    copy_bytes = pairs * nl * 2 * block_bytes * 2          # read + write, K and V, all layers
+    copy_gbs = copy_bytes / (float(np.mean(copy_us)) * 1e-6) / 1e9 if pairs else 0.0
+    res = {"metric": f"beam-search decode step over {nl} layers, µs/step (Llama-3-8B heads)",
+           "value": round(float(np.mean(wall_us)), 2), "unit": "us/step", "n_gpus": 1,
+           "steps": steps, "warmup": warmup, "higher_is_better": False, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": f"beam search: {P} prompts of {plen} tokens x {K} beams "
+                                  f"(B={B}), Hq={Hq}, Hkv={Hkv}, D={D}, block 16, {nl} layers, "
+                                  f"parents drawn with replacement each step",
+                      "layers": nl},
+           "host_bookkeeping_us_per_step": round(float(np.mean(host_us)), 2),
+           "host_block_manager_us_per_step": round(float(np.mean(cpp_us)), 2),
+           "wall_host_bm_device_us_p50": [round(float(np.median(x)), 2)
+                                          for x in (wall_us, host_us, cpp_us, dev_us)],
+           "device_us_per_step": round(float(np.mean(dev_us)), 2),
+           "copy_pairs_per_step": round(pairs, 2),
+           "copy_us_per_step": round(float(np.mean(copy_us)), 2),
+           "blocks_used": int(st["used_blocks"]), "blocks_without_sharing": unshared,
+           "shared_blocks": int(st["shared_blocks"]),
+           "roofline": {"kernel": "copy_blocks_layers_kernel (pa_copy_blocks_layers; events "
+                                  "around the launch)",
+                        "bound": "hbm", "achieved": round(copy_gbs, 2), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+                        "traffic": None, "algorithmic_bytes": int(copy_bytes)}}
+    print(json.dumps(res), flush=True)
+
+
 def prefill_cpu_baseline(case, q, qs, budget_s):
     """The fp64 oracle (prefill_ref) on a bounded sample: query rows of the
     first sequence, 64 at a time, while the budget lasts; flops counted as in
@@ -277,6 +432,9 @@ def main():
         sys.exit(2)
     if args.prefill:
         prefill_bench(args)
+        return
+    if args.beam:
+        beam_bench(args)
         return
 
     import numpy as np

@@ -92,8 +92,11 @@ __global__ __launch_bounds__(256) void append_quant_kernel(uint8_t* __restrict__
   }
 }
 
-// grid = (num_pairs, 2): y selects the K or the V pool.  Each workgroup copies
-// one whole physical block (all heads) with 16-byte loads and stores.
+// grid = (num_pairs, 2, slices): y selects the K or the V pool, z a 4 KiB
+// slice of the block (each workgroup moves 256 x 16 bytes, so a pair's copy
+// is spread over many workgroups instead of one streaming the whole block).
+constexpr int kCopySliceChunks = 256;
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kpool,
                                                           uint4* __restrict__ vpool,
                                                           const int32_t* __restrict__ pairs,
@@ -104,11 +107,13 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kp
   uint4* pool = blockIdx.y == 0 ? kpool : vpool;
   const uint4* s = pool + static_cast<int64_t>(src) * chunks_per_block;
   uint4* d = pool + static_cast<int64_t>(dst) * chunks_per_block;
-  for (int64_t c = threadIdx.x; c < chunks_per_block; c += blockDim.x) d[c] = s[c];
+  for (int64_t c = static_cast<int64_t>(blockIdx.z) * kCopySliceChunks + threadIdx.x;
+       c < chunks_per_block; c += static_cast<int64_t>(gridDim.z) * kCopySliceChunks)
+    d[c] = s[c];
 }
 
-// grid = (num_pairs, 2 * num_layers): y = 2 * layer + (0: K pool, 1: V pool).
-// Each workgroup copies one whole physical block of one pool of one layer.
+// grid = (num_pairs, 2 * num_layers, slices): y = 2 * layer + (0: K pool,
+// 1: V pool), z a 4 KiB slice of the block.
 __global__ __launch_bounds__(256) void copy_blocks_layers_kernel(
     uint4* const* __restrict__ kpools, uint4* const* __restrict__ vpools,
     const int32_t* __restrict__ pairs, int num_blocks, int64_t chunks_per_block) {
@@ -118,7 +123,16 @@ __global__ __launch_bounds__(256) void copy_blocks_layers_kernel(
   uint4* pool = (blockIdx.y & 1) ? vpools[layer] : kpools[layer];
   const uint4* s = pool + static_cast<int64_t>(src) * chunks_per_block;
   uint4* d = pool + static_cast<int64_t>(dst) * chunks_per_block;
-  for (int64_t c = threadIdx.x; c < chunks_per_block; c += blockDim.x) d[c] = s[c];
+  for (int64_t c = static_cast<int64_t>(blockIdx.z) * kCopySliceChunks + threadIdx.x;
+       c < chunks_per_block; c += static_cast<int64_t>(gridDim.z) * kCopySliceChunks)
+    d[c] = s[c];
+}
+
+// Slices per block copy (gridDim.z), at most 64 (a block's copy still covers
+// every chunk through the grid-stride loop).
+unsigned copy_slices(int64_t chunks_per_block) {
+  const int64_t n = (chunks_per_block + kCopySliceChunks - 1) / kCopySliceChunks;
+  return static_cast<unsigned>(n < 1 ? 1 : n > 64 ? 64 : n);
 }
 
 // grid = (ceil(max_len/16), Hkv, B): one logical block of one head per
@@ -317,7 +331,7 @@ extern "C" pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* b
     return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: pools must be 16-byte aligned");
   const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * kBlockSize *
                               static_cast<int64_t>(dtype_bytes(dtype));
-  dim3 grid(num_pairs, 2), block(256);
+  dim3 grid(num_pairs, 2, copy_slices(block_bytes / 16)), block(256);
   copy_blocks_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), block_pairs, num_blocks,
       block_bytes / 16);
@@ -339,7 +353,7 @@ extern "C" pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_
   if (!k_pools || !v_pools || !block_pairs) return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * kBlockSize *
                               static_cast<int64_t>(dtype_bytes(dtype));
-  dim3 grid(num_pairs, 2 * num_layers), block(256);
+  dim3 grid(num_pairs, 2 * num_layers, copy_slices(block_bytes / 16)), block(256);
   copy_blocks_layers_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
       reinterpret_cast<uint4* const*>(k_pools), reinterpret_cast<uint4* const*>(v_pools),
       block_pairs, num_blocks, block_bytes / 16);
