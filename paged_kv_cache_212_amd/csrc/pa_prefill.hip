@@ -131,18 +131,34 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams pr) {
     return __builtin_amdgcn_readlane(tcur, k & 63);
   };
 
-  uint4 kreg[2][NKK];
-  uint2 vreg[2][NTL];
-  auto issue = [&](int u, int kb) {
-    const int64_t off = phys_of(kb) * block_stride;
-    const char* kt = kbase + off + ((j * 16) + n) * 16;
+  // Keys are taken 32 at a time, a pair of blocks (2pp, 2pp + 1).  Lane (n,
+  // j) scores query n against keys 4j .. 4j+3 of each block of the pair; as
+  // the A operand of the 16x16x32 P.V its k index 8j + e stands for key
+  // 4j + e of the first block (e < 4) or of the second (e >= 4), and its V
+  // operand is those keys' two 8-byte runs side by side.  A pair past the
+  // tile's last block re-reads that block (its keys are masked).
+  const int npair = (nblk + 1) / 2;
+  uint4 kreg[2][NKK];      // K of the pair's two blocks
+  uint2 vreg[2][NTL];      // V of the pair's two blocks
+  int ph[2];
+  auto issue_k = [&](int pp) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      kreg[u][kk] = *reinterpret_cast<const uint4*>(kt + kk * 64 * 16);
-    const char* vt = vbase + off + ((j >> 1) * D + n) * 16 + (j & 1) * 8;
+    for (int u = 0; u < 2; ++u) {
+      ph[u] = phys_of(min(2 * pp + u, nblk - 1));
+      const char* kt = kbase + ph[u] * block_stride + ((j * 16) + n) * 16;
 #pragma unroll
-    for (int t = 0; t < NTL; ++t)
-      vreg[u][t] = *reinterpret_cast<const uint2*>(vt + t * 16 * 16);
+      for (int kk = 0; kk < NKK; ++kk)
+        kreg[u][kk] = *reinterpret_cast<const uint4*>(kt + kk * 64 * 16);
+    }
+  };
+  auto issue_v = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const char* vt = vbase + ph[u] * block_stride + ((j >> 1) * D + n) * 16 + (j & 1) * 8;
+#pragma unroll
+      for (int t = 0; t < NTL; ++t)
+        vreg[u][t] = *reinterpret_cast<const uint2*>(vt + t * 16 * 16);
+    }
   };
 
   float m_run = -INFINITY, l_lane = 0.f;
@@ -150,15 +166,23 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams pr) {
 #pragma unroll
   for (int t = 0; t < NTL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int u, int kb) {
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  auto qk_softmax = [&](int pp, uint4& phi, uint4& plo) {
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) s = Mfma<T>::qk(kreg[u][kk], qr[kk], s);
-    const int kpos0 = kb * kBlockSize + 4 * j;            // key position of s[0]
-    float sv[4];
+    for (int kk = 0; kk < NKK; ++kk) {
+      s0 = Mfma<T>::qk(kreg[0][kk], qr[kk], s0);
+      s1 = Mfma<T>::qk(kreg[1][kk], qr[kk], s1);
+    }
+    const int kpos0 = 2 * pp * kBlockSize + 4 * j;        // key position of s0[0]
+    float sv[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sv[e] = (kpos0 + e <= qpos) ? s[e] * pr.scale_log2 : -INFINITY;
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = (kpos0 + e <= qpos) ? s0[e] * pr.scale_log2 : -INFINITY;
+      sv[4 + e] = (kpos0 + kBlockSize + e <= qpos) ? s1[e] * pr.scale_log2 : -INFINITY;
+    }
+    float bm = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[e]);
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     const float mn = fmaxf(m_run, bm);
@@ -174,38 +198,52 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams pr) {
       }
       m_run = mn;
     }
-    float pe[4];
+    float pe[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_run);
-    l_lane += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-    uint2 phi, plo;
-    Mfma<T>::split(pe, phi, plo);
-    if ((kb + 1) * kBlockSize > L) {
-      // the block reaches past the sequence: zero V of unwritten positions
-      const uint32_t mx = (kpos0 + 0 < L ? 0x0000FFFFu : 0u) | (kpos0 + 1 < L ? 0xFFFF0000u : 0u);
-      const uint32_t my = (kpos0 + 2 < L ? 0x0000FFFFu : 0u) | (kpos0 + 3 < L ? 0xFFFF0000u : 0u);
+    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_run);
+    l_lane += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+    Mfma<T>::split8(pe, phi, plo);
+  };
+
+  auto pv = [&](int pp, uint4 phi, uint4 plo) {
 #pragma unroll
-      for (int t = 0; t < NTL; ++t) {
-        vreg[u][t].x &= mx;
-        vreg[u][t].y &= my;
+    for (int u = 0; u < 2; ++u) {
+      const int kb = 2 * pp + u;
+      if ((kb + 1) * kBlockSize > L) {
+        // the block reaches past the sequence: zero V of unwritten positions
+        const int kp = kb * kBlockSize + 4 * j;
+        const uint32_t mx = (kp + 0 < L ? 0x0000FFFFu : 0u) | (kp + 1 < L ? 0xFFFF0000u : 0u);
+        const uint32_t my = (kp + 2 < L ? 0x0000FFFFu : 0u) | (kp + 3 < L ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+          vreg[u][t].x &= mx;
+          vreg[u][t].y &= my;
+        }
       }
     }
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
-      acc[t] = Mfma<T>::pv(phi, vreg[u][t], acc[t]);
-      acc[t] = Mfma<T>::pv(plo, vreg[u][t], acc[t]);
+      const uint4 v = make_uint4(vreg[0][t].x, vreg[0][t].y, vreg[1][t].x, vreg[1][t].y);
+      acc[t] = Mfma<T>::pv8(phi, v, acc[t]);
+      acc[t] = Mfma<T>::pv8(plo, v, acc[t]);
     }
   };
 
-  issue(0, 0);
-  if (nblk > 1) issue(1, 1);
-  for (int kb = 0; kb < nblk; kb += 2) {
-    compute(0, kb);
-    if (kb + 2 < nblk) issue(0, kb + 2);
-    if (kb + 1 < nblk) {
-      compute(1, kb + 1);
-      if (kb + 3 < nblk) issue(1, kb + 3);
-    }
+  // K of the next pair is issued once QK has consumed the current one, V of
+  // the next pair once P.V has (scheduling barriers keep the compiler from
+  // hoisting the loads above the matrix ops that still read the registers)
+  issue_k(0);
+  issue_v();
+  for (int pp = 0; pp < npair; ++pp) {
+    uint4 phi, plo;
+    qk_softmax(pp, phi, plo);
+    __builtin_amdgcn_sched_barrier(0);
+    if (pp + 1 < npair) issue_k(pp + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    pv(pp, phi, plo);
+    __builtin_amdgcn_sched_barrier(0);
+    if (pp + 1 < npair) issue_v();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // l of query n, then of O row 4j + e
