@@ -10,7 +10,8 @@
 // the decode step.
 //
 // One 64-lane wave per (query head h, tile of 16 query tokens, sequence);
-// lane = 16*j + n.  K/V of a block are re-read by every tile and query head of
+// lane = 16*j + n; four such waves (four query heads of one KV head) share a
+// workgroup and their K/V through LDS when the group size is a multiple of 4.  K/V of a block are re-read by every tile and query head of
 // its KV head, so they use plain (cached) loads.  Per 16-token block of keys:
 //   S^T (16 keys x 16 queries) = K . Q^T on v_mfma_f32_16x16x32: A = K (lane
 //     reads key n, dims kk*32 + 8j .. +8), B = Q (query n, same dims).  Result:
@@ -54,20 +55,26 @@ struct PrefillParams {
   float scale_log2;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(64) void prefill_kernel(PrefillParams pr) {
+// WPG: waves per workgroup.  1: one query head per workgroup, K/V read by
+// each wave from global memory (L2).  4 (G a multiple of 4): four query heads
+// of one KV head and the same tile per workgroup; each pair of K/V blocks is
+// loaded once, a quarter by each wave, into LDS and read from there by all
+// four (a quarter of the L2 traffic).
+template <typename T, int D, int WPG>
+__global__ __launch_bounds__(64 * WPG) void prefill_kernel(PrefillParams pr) {
   constexpr int NKK = D / 32;     // 32-dim steps of Q.K^T
   constexpr int NTL = D / 16;     // 16-dim output tiles
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
-  // Workgroup order: KV head fastest, then the query head within its group,
-  // then the tile, then the sequence.  Workgroups are dealt round-robin to the
+  constexpr int kTileU4 = static_cast<int>(kTileBytes / 16);   // 16-byte words per tile
+  // Workgroup order: KV head fastest, then the group of WPG query heads, then
+  // the tile, then the sequence.  Workgroups are dealt round-robin to the
   // XCDs, so with Hkv a multiple of their number every query head and tile of
   // one KV head runs on one XCD and re-reads its K/V from that XCD's L2.
   int lin = blockIdx.x;
   const int g = lin % pr.Hkv;
   lin /= pr.Hkv;
-  const int e_head = lin % pr.G;
-  lin /= pr.G;
+  const int e_head = (lin % (pr.G / WPG)) * WPG + (threadIdx.x >> 6);
+  lin /= pr.G / WPG;
   const int tile = lin % pr.ntiles, b = lin / pr.ntiles;
   const int h = g * pr.G + e_head;
   const int lane = threadIdx.x & 63;
@@ -141,6 +148,40 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams pr) {
   uint4 kreg[2][NKK];      // K of the pair's two blocks
   uint2 vreg[2][NTL];      // V of the pair's two blocks
   int ph[2];
+  // LDS staging (WPG > 1): two buffers of a pair's [K0 | K1 | V0 | V1] tiles.
+  // Word c of a buffer (16 bytes) is moved by thread c % (64 * WPG) straight
+  // from global memory into LDS (global_load_lds: lane i of a wave writes the
+  // wave's LDS base + 16 i), so no registers hold the staged data.
+  constexpr int kStage = WPG > 1 ? 4 * kTileU4 / (64 * WPG) : 1;
+  __shared__ uint4 lds[WPG > 1 ? 2 : 1][4][WPG > 1 ? kTileU4 : 1];
+  auto gload_lds = [&](int pp, int buf) {
+    const int p0 = phys_of(min(2 * pp, nblk - 1)), p1 = phys_of(min(2 * pp + 1, nblk - 1));
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) {
+      const int c = static_cast<int>(threadIdx.x) + r * 64 * WPG;
+      const int part = c / kTileU4, idx = c % kTileU4;
+      const char* src = (part < 2 ? kbase : vbase) + ((part & 1) ? p1 : p0) * block_stride +
+                        idx * 16;
+      uint4* dst = &lds[buf][0][0] + (c - lane);        // the wave's first word
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+  };
+  auto lread_k = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kreg[u][kk] = lds[buf][u][(j * 16 + n) + kk * 64];
+  };
+  auto lread_v = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint2* vt = reinterpret_cast<const uint2*>(lds[buf][2 + u]) +
+                        (((j >> 1) * D + n) * 16 + (j & 1) * 8) / 8;
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) vreg[u][t] = vt[t * 16 * 16 / 8];
+    }
+  };
   auto issue_k = [&](int pp) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -229,21 +270,42 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillParams pr) {
     }
   };
 
-  // K of the next pair is issued once QK has consumed the current one, V of
-  // the next pair once P.V has (scheduling barriers keep the compiler from
-  // hoisting the loads above the matrix ops that still read the registers)
-  issue_k(0);
-  issue_v();
-  for (int pp = 0; pp < npair; ++pp) {
-    uint4 phi, plo;
-    qk_softmax(pp, phi, plo);
-    __builtin_amdgcn_sched_barrier(0);
-    if (pp + 1 < npair) issue_k(pp + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    pv(pp, phi, plo);
-    __builtin_amdgcn_sched_barrier(0);
-    if (pp + 1 < npair) issue_v();
-    __builtin_amdgcn_sched_barrier(0);
+  if constexpr (WPG == 1) {
+    // K of the next pair is issued once QK has consumed the current one, V of
+    // the next pair once P.V has (scheduling barriers keep the compiler from
+    // hoisting the loads above the matrix ops that still read the registers)
+    issue_k(0);
+    issue_v();
+    for (int pp = 0; pp < npair; ++pp) {
+      uint4 phi, plo;
+      qk_softmax(pp, phi, plo);
+      __builtin_amdgcn_sched_barrier(0);
+      if (pp + 1 < npair) issue_k(pp + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(pp, phi, plo);
+      __builtin_amdgcn_sched_barrier(0);
+      if (pp + 1 < npair) issue_v();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // pair pp + 1 travels global -> LDS (the other buffer) while pair pp is
+    // computed from LDS; one barrier per pair orders both the buffer's writes
+    // before its reads and the reads before the rewrite two pairs later
+    // (every wave of the workgroup runs the same npair)
+    gload_lds(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int pp = 0; pp < npair; ++pp) {
+      // the other buffer was last read in the previous pair, before the barrier
+      if (pp + 1 < npair) gload_lds(pp + 1, (pp + 1) & 1);
+      lread_k(pp & 1);
+      uint4 phi, plo;
+      qk_softmax(pp, phi, plo);
+      lread_v(pp & 1);
+      pv(pp, phi, plo);
+      __builtin_amdgcn_s_waitcnt(0);    // this wave's LDS-bound loads have landed
+      __syncthreads();                   // ... and every wave's
+    }
   }
 
   // l of query n, then of O row 4j + e
@@ -319,22 +381,21 @@ extern "C" pa_status pa_prefill(float* out, const void* q, const void* k_pool,
   pr.max_qlen = max_query_len;
   pr.scale_log2 = scale * kLog2e;
   pr.ntiles = (max_query_len + kQTile - 1) / kQTile;
-  const uint64_t nwg = static_cast<uint64_t>(num_q_heads) * pr.ntiles * num_seqs;
+  // four query heads per workgroup when the group size allows it
+  const int wpg = pr.G % 4 == 0 ? 4 : 1;
+  const uint64_t nwg = static_cast<uint64_t>(num_q_heads / wpg) * pr.ntiles * num_seqs;
   if (nwg > 0x7fffffffull)
     return fail(PA_ERR_INVALID_ARG, "%s: %llu workgroups exceed the launch limit", fn,
                 static_cast<unsigned long long>(nwg));
   const dim3 grid(static_cast<uint32_t>(nwg));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == PA_BF16) {
-    if (head_dim == 64)
-      prefill_kernel<BF16, 64><<<grid, 64, 0, s>>>(pr);
-    else
-      prefill_kernel<BF16, 128><<<grid, 64, 0, s>>>(pr);
-  } else {
-    if (head_dim == 64)
-      prefill_kernel<F16, 64><<<grid, 64, 0, s>>>(pr);
-    else
-      prefill_kernel<F16, 128><<<grid, 64, 0, s>>>(pr);
-  }
+#define PA_PREFILL(TAG, DIM)                                               \
+  (wpg == 4 ? (prefill_kernel<TAG, DIM, 4><<<grid, 256, 0, s>>>(pr), 0)    \
+            : (prefill_kernel<TAG, DIM, 1><<<grid, 64, 0, s>>>(pr), 0))
+  if (dtype == PA_BF16)
+    head_dim == 64 ? PA_PREFILL(BF16, 64) : PA_PREFILL(BF16, 128);
+  else
+    head_dim == 64 ? PA_PREFILL(F16, 64) : PA_PREFILL(F16, 128);
+#undef PA_PREFILL
   return launch_status(fn);
 }
