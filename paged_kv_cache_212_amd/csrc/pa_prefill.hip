@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_mfma.h"
@@ -61,7 +62,7 @@ struct PrefillParams {
 // loaded once, a quarter by each wave, into LDS and read from there by all
 // four (a quarter of the L2 traffic).
 template <typename T, int D, int WPG>
-__global__ __launch_bounds__(64 * WPG) void prefill_kernel(PrefillParams pr) {
+__global__ __launch_bounds__(64 * WPG, WPG > 1 ? 3 : 1) void prefill_kernel(PrefillParams pr) {
   constexpr int NKK = D / 32;     // 32-dim steps of Q.K^T
   constexpr int NTL = D / 16;     // 16-dim output tiles
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
@@ -118,25 +119,26 @@ __global__ __launch_bounds__(64 * WPG) void prefill_kernel(PrefillParams pr) {
   const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
   const int64_t block_stride = static_cast<int64_t>(pr.Hkv) * kTileBytes;
   const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks;
+  // Every table entry the tile reads is checked once, up front; an entry out
+  // of the pool turns the tile's rows into NaN.  (Sequence and tile are the
+  // same for every wave of a workgroup, so the early return is uniform.)
   bool bad = false;
-  // table entries, 64 per register (lane i: entry 64*c + i of chunk c)
-  auto load_chunk = [&](int c) -> int {
-    const int k = c * 64 + lane;
+  for (int k = lane; k - lane < nblk; k += 64) {
     const int e = k < nblk ? trow[k] : 0;
-    const bool lane_bad = k < nblk && (e < 0 || e >= pr.num_blocks);
-    if (__any(lane_bad)) bad = true;
-    return lane_bad ? 0 : e;
-  };
-  int chunk = 0;
-  int tcur = load_chunk(0);
-  auto phys_of = [&](int k) -> int {                     // k increases call by call
-    const int c = k >> 6;
-    if (c != chunk) {
-      chunk = c;
-      tcur = load_chunk(c);
+    if (__any(e < 0 || e >= pr.num_blocks)) bad = true;
+  }
+  if (bad) {
+    for (int idx = lane; idx < kQTile * D; idx += 64) {
+      const int r = idx / D;
+      if (i0 + r < nq) orow[static_cast<int64_t>(r) * pr.Hq * D + idx % D] = __builtin_nanf("");
     }
-    return __builtin_amdgcn_readlane(tcur, k & 63);
-  };
+    return;
+  }
+  // The entries are then read one at a time with scalar loads (the index is
+  // the same in every lane): these wait on their own counter, so taking an
+  // entry does not drain the K/V loads still in flight.
+  const auto* trow_s = (const __attribute__((address_space(4))) int32_t*)trow;
+  auto phys_of = [&](int k) -> int { return trow_s[k]; };
 
   // Keys are taken 32 at a time, a pair of blocks (2pp, 2pp + 1).  Lane (n,
   // j) scores query n against keys 4j .. 4j+3 of each block of the pair; as
@@ -148,13 +150,24 @@ __global__ __launch_bounds__(64 * WPG) void prefill_kernel(PrefillParams pr) {
   uint4 kreg[2][NKK];      // K of the pair's two blocks
   uint2 vreg[2][NTL];      // V of the pair's two blocks
   int ph[2];
-  // LDS staging (WPG > 1): two buffers of a pair's [K0 | K1 | V0 | V1] tiles.
+  // LDS staging (WPG > 1): kBufs buffers of a pair's [K0 | K1 | V0 | V1] tiles.
   // Word c of a buffer (16 bytes) is moved by thread c % (64 * WPG) straight
   // from global memory into LDS (global_load_lds: lane i of a wave writes the
   // wave's LDS base + 16 i), so no registers hold the staged data.
-  constexpr int kStage = WPG > 1 ? 4 * kTileU4 / (64 * WPG) : 1;
-  __shared__ uint4 lds[WPG > 1 ? 2 : 1][4][WPG > 1 ? kTileU4 : 1];
-  auto gload_lds = [&](int pp, int buf) {
+  constexpr int kStage = WPG > 1 ? 4 * kTileU4 / (64 * WPG) : 1;   // loads per thread per pair
+  constexpr int kBufs = 3;      // pairs in LDS: the one computed and two in flight
+  // three separate arrays, so the compiler can tell a buffer being filled
+  // from the one being read and need not wait for the fill before the reads
+  __shared__ uint4 lds0[4][WPG > 1 ? kTileU4 : 1];
+  __shared__ uint4 lds1[4][WPG > 1 ? kTileU4 : 1];
+  __shared__ uint4 lds2[4][WPG > 1 ? kTileU4 : 1];
+  auto buf_of = [&](auto bc) -> uint4(*)[WPG > 1 ? kTileU4 : 1] {
+    constexpr int bi = decltype(bc)::value;
+    if constexpr (bi == 0) return lds0;
+    else if constexpr (bi == 1) return lds1;
+    else return lds2;
+  };
+  auto gload_lds = [&](int pp, auto bc) {
     const int p0 = phys_of(min(2 * pp, nblk - 1)), p1 = phys_of(min(2 * pp + 1, nblk - 1));
 #pragma unroll
     for (int r = 0; r < kStage; ++r) {
@@ -162,21 +175,21 @@ __global__ __launch_bounds__(64 * WPG) void prefill_kernel(PrefillParams pr) {
       const int part = c / kTileU4, idx = c % kTileU4;
       const char* src = (part < 2 ? kbase : vbase) + ((part & 1) ? p1 : p0) * block_stride +
                         idx * 16;
-      uint4* dst = &lds[buf][0][0] + (c - lane);        // the wave's first word
+      uint4* dst = &buf_of(bc)[0][0] + (c - lane);      // the wave's first word
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
-  auto lread_k = [&](int buf) {
+  auto lread_k = [&](auto bc) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kreg[u][kk] = lds[buf][u][(j * 16 + n) + kk * 64];
+      for (int kk = 0; kk < NKK; ++kk) kreg[u][kk] = buf_of(bc)[u][(j * 16 + n) + kk * 64];
   };
-  auto lread_v = [&](int buf) {
+  auto lread_v = [&](auto bc) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const uint2* vt = reinterpret_cast<const uint2*>(lds[buf][2 + u]) +
+      const uint2* vt = reinterpret_cast<const uint2*>(buf_of(bc)[2 + u]) +
                         (((j >> 1) * D + n) * 16 + (j & 1) * 8) / 8;
 #pragma unroll
       for (int t = 0; t < NTL; ++t) vreg[u][t] = vt[t * 16 * 16 / 8];
@@ -288,23 +301,51 @@ __global__ __launch_bounds__(64 * WPG) void prefill_kernel(PrefillParams pr) {
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    // pair pp + 1 travels global -> LDS (the other buffer) while pair pp is
-    // computed from LDS; one barrier per pair orders both the buffer's writes
-    // before its reads and the reads before the rewrite two pairs later
-    // (every wave of the workgroup runs the same npair)
-    gload_lds(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+    // pairs pp + 1 and pp + 2 travel global -> LDS while pair pp is computed
+    // from LDS; one barrier per pair orders both a buffer's writes before its
+    // reads and its reads before the rewrite three pairs later (every wave of
+    // the workgroup runs the same npair).  The only vector-memory operations
+    // in the loop are these loads, so "at most kStage outstanding" means the
+    // next pair's have landed.
+    // s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt left at its
+    // no-wait maximum 7, lgkmcnt 0 so that this wave's LDS reads of the pair
+    // have returned before the barrier lets a refill of that buffer start
+    constexpr int kWaitNext = (kStage & 0xF) | (7 << 4) | ((kStage >> 4) << 14);
+    constexpr int kWaitAll = 7 << 4;
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
+    gload_lds(0, B0{});
+    if (npair > 1) {
+      gload_lds(1, B1{});
+      __builtin_amdgcn_s_waitcnt(kWaitNext);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+    }
     __syncthreads();
-    for (int pp = 0; pp < npair; ++pp) {
-      // the other buffer was last read in the previous pair, before the barrier
-      if (pp + 1 < npair) gload_lds(pp + 1, (pp + 1) & 1);
-      lread_k(pp & 1);
+    // pair pp in buffer pp % 3; the loop is unrolled by three so that every
+    // buffer index is a constant
+    auto step = [&](int pp, auto cur, auto fill) {
+      // the buffer filled here was last read in pair pp - 1, before the barrier
+      if (pp + 2 < npair) gload_lds(pp + 2, fill);
+      lread_k(cur);
       uint4 phi, plo;
       qk_softmax(pp, phi, plo);
-      lread_v(pp & 1);
+      lread_v(cur);
       pv(pp, phi, plo);
-      __builtin_amdgcn_s_waitcnt(0);    // this wave's LDS-bound loads have landed
-      __syncthreads();                   // ... and every wave's
+      if (pp + 2 < npair)
+        __builtin_amdgcn_s_waitcnt(kWaitNext);    // this wave's pair pp + 1 has landed
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+      // ... and every wave's.  A bare barrier: the fence of __syncthreads
+      // would also drain the loads of pair pp + 2.  The clobber keeps the
+      // compiler from moving LDS reads across it.
+      asm volatile("s_barrier" ::: "memory");
+    };
+    for (int pp = 0; pp < npair; pp += 3) {
+      step(pp, B0{}, B2{});
+      if (pp + 1 < npair) step(pp + 1, B1{}, B0{});
+      if (pp + 2 < npair) step(pp + 2, B2{}, B1{});
     }
   }
 
@@ -317,7 +358,7 @@ __global__ __launch_bounds__(64 * WPG) void prefill_kernel(PrefillParams pr) {
     const int r = 4 * j + e;
     const float lr = __shfl(l, r);
     if (i0 + r < nq) {
-      const float inv = bad ? __builtin_nanf("") : 1.0f / lr;
+      const float inv = 1.0f / lr;
 #pragma unroll
       for (int t = 0; t < NTL; ++t)
         orow[static_cast<int64_t>(r) * pr.Hq * D + t * 16 + n] = acc[t][e] * inv;
