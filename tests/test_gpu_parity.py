@@ -229,25 +229,40 @@ def test_even_split_shapes(lens, dtype, hq, hkv, d):
     _compare_full(case, ref, got, TOL[dtype])
 
 
+@pytest.mark.parametrize("fused", [True, "phased"])
+def test_even_split_one_context_in_many_pieces(fused):
+    """One 100 000-token context with a single KV head: the even split cuts
+    it into hundreds of pieces (more than a wave has lanes, many batches of
+    the merge's fold)."""
+    case = custom_case(52, "bf16", [100000], 4, 1, 128, partition_size=-1)
+    say(f"[split] one context over many workgroups fused={fused}")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case, fused=fused)
+    _compare_full(case, ref, got, TOL["bf16"])
+
+
 def test_workspace_reused_across_calls():
-    """One (uninitialised) workspace serves call after call, alternating
-    batches with different splits."""
+    """One uninitialised workspace serves call after call: batches of
+    different sizes and splits, one-call and two-phase decodes alternating."""
     pk = require_gpu()
     say("[workspace] reuse across calls")
     a = custom_case(61, "bf16", [900, 33, 2500, 70], 32, 8, 128)
-    b = custom_case(62, "bf16", [1800, 5, 640, 1200], 32, 8, 128)
+    b = custom_case(62, "bf16", [1800, 5, 640, 1200, 1500, 17], 32, 8, 128)
     ra, rb = _oracle_poisoned(a), _oracle_poisoned(b)
     ga, gb = run_gpu_step(a), run_gpu_step(b)
-    ws = pk.ops.decode_workspace(4, 32, 8, 128, 2600, -1, torch.bfloat16)
+    ws = pk.ops.decode_workspace(6, 32, 8, 128, 2600, -1, torch.bfloat16)
     ws.fill_(0xAB)
     for _ in range(3):
         for case, got, ref in ((a, ga, ra), (b, gb, rb)):
             plan, cache = got["plan"], got["cache"]
-            out = torch.empty(4, 32, 128, device="cuda")
-            pk.ops.decode(out, got["q"], cache.k_pool, cache.v_pool, plan.d_tables, plan.d_lens,
-                          2600, partition_size=-1, workspace=ws)
-            torch.cuda.synchronize()
-            assert max_err(out.cpu().numpy(), ref["out"]) <= TOL["bf16"]
+            nb = len(case.lens)
+            for phases in (("both",), ("partial", "merge")):
+                out = torch.empty(nb, 32, 128, device="cuda")
+                for ph in phases:
+                    pk.ops.decode(out, got["q"], cache.k_pool, cache.v_pool, plan.d_tables,
+                                  plan.d_lens, 2600, partition_size=-1, workspace=ws, phase=ph)
+                torch.cuda.synchronize()
+                assert max_err(out.cpu().numpy(), ref["out"]) <= TOL["bf16"], phases
 
 
 def test_append_skips_negative_and_out_of_range_slots():
