@@ -9,10 +9,12 @@
 // phase as a stage of its own in 「今後注目すべき方向性」).  With n_b = 1 it is
 // the decode step.
 //
-// One 64-lane wave per (query head h, tile of 16 query tokens, sequence);
-// lane = 16*j + n; four such waves (four query heads of one KV head) share a
-// workgroup and their K/V through LDS when the group size is a multiple of 4.  K/V of a block are re-read by every tile and query head of
-// its KV head, so they use plain (cached) loads.  Per 16-token block of keys:
+// One 64-lane wave per (query head h, tiles of 16 query tokens, sequence);
+// lane = 16*j + n.  When the group size is a multiple of 4, four such waves
+// (four query heads of one KV head) share a workgroup and their K/V through
+// LDS, and each wave takes two consecutive tiles; otherwise one wave, one
+// tile.  K/V of a block are re-read by every tile and query head of its KV
+// head, so they use plain (cached) loads.  Per 16-token block of keys:
 //   S^T (16 keys x 16 queries) = K . Q^T on v_mfma_f32_16x16x32: A = K (lane
 //     reads key n, dims kk*32 + 8j .. +8), B = Q (query n, same dims).  Result:
 //     lane (n, j) holds query n against keys 4j + e (e = 0..3).
@@ -40,7 +42,8 @@ namespace pa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kQTile = 16;  // query tokens per wave
+constexpr int kQTile = 16;     // query tokens per tile
+constexpr int kPairTiles = 2;  // tiles per wave with four query heads per workgroup
 
 struct PrefillParams {
   float* out;               // [T][Hq][D]
@@ -58,11 +61,16 @@ struct PrefillParams {
 
 // WPG: waves per workgroup.  1: one query head per workgroup, K/V read by
 // each wave from global memory (L2).  4 (G a multiple of 4): four query heads
-// of one KV head and the same tile per workgroup; each pair of K/V blocks is
+// of one KV head and the same tiles per workgroup; each pair of K/V blocks is
 // loaded once, a quarter by each wave, into LDS and read from there by all
 // four (a quarter of the L2 traffic).
-template <typename T, int D, int WPG>
-__global__ __launch_bounds__(64 * WPG, WPG > 1 ? 3 : 1) void prefill_kernel(PrefillParams pr) {
+// TQ: consecutive 16-query tiles per wave.  The K/V operands read for a pair
+// of blocks serve all TQ tiles (TQ times the matrix work per LDS read), and
+// the tiles' softmax and matrix chains are independent, so one hides the
+// other's latency.
+template <typename T, int D, int WPG, int TQ>
+__global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void prefill_kernel(
+    PrefillParams pr) {
   constexpr int NKK = D / 32;     // 32-dim steps of Q.K^T
   constexpr int NTL = D / 16;     // 16-dim output tiles
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
@@ -76,7 +84,8 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? 3 : 1) void prefill_kernel(Pref
   lin /= pr.Hkv;
   const int e_head = (lin % (pr.G / WPG)) * WPG + (threadIdx.x >> 6);
   lin /= pr.G / WPG;
-  const int tile = lin % pr.ntiles, b = lin / pr.ntiles;
+  const int ngroups = (pr.ntiles + TQ - 1) / TQ;           // groups of TQ tiles
+  const int tgroup = lin % ngroups, b = lin / ngroups;
   const int h = g * pr.G + e_head;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
@@ -86,34 +95,39 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? 3 : 1) void prefill_kernel(Pref
   const bool rows_ok = q0 >= 0 && q0 <= q1 && q1 <= pr.T;
   if (!rows_ok) return;                                   // no row can be trusted
   const int nq = q1 - q0;
-  const int i0 = tile * kQTile;                           // first query of the tile
+  const int i0 = tgroup * TQ * kQTile;                    // first query of the wave
   if (i0 >= nq) return;
   float* orow = pr.out + (static_cast<int64_t>(q0) + i0) * pr.Hq * D + static_cast<int64_t>(h) * D;
   const bool seq_ok = L >= 0 && L <= pr.max_ctx && L <= pr.max_blocks * kBlockSize &&
                       nq <= L && nq <= pr.max_qlen;
   if (!seq_ok) {
     // length out of the declared bounds: NaN rows
-    for (int idx = lane; idx < kQTile * D; idx += 64) {
+    for (int idx = lane; idx < TQ * kQTile * D; idx += 64) {
       const int r = idx / D;
       if (i0 + r < nq) orow[static_cast<int64_t>(r) * pr.Hq * D + idx % D] = __builtin_nanf("");
     }
     return;
   }
 
-  // Q (B operand): query n of the tile, dims kk*32 + 8j .. +8
-  uint4 qr[NKK];
-  {
-    const bool real = i0 + n < nq;
+  // Q (B operand) of tile t: query 16t + n of the wave, dims kk*32 + 8j .. +8
+  // (queries past the chunk read as zero; their rows are not written)
+  uint4 qr[TQ][NKK];
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) {
+    const bool real = i0 + kQTile * t + n < nq;
     const uint16_t* qb = static_cast<const uint16_t*>(pr.q) +
-                         ((static_cast<int64_t>(q0) + i0 + n) * pr.Hq + h) * D + j * 8;
+                         ((static_cast<int64_t>(q0) + i0 + kQTile * t + n) * pr.Hq + h) * D +
+                         j * 8;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qr[kk] = real ? *reinterpret_cast<const uint4*>(qb + kk * 32) : make_uint4(0, 0, 0, 0);
+      qr[t][kk] = real ? *reinterpret_cast<const uint4*>(qb + kk * 32) : make_uint4(0, 0, 0, 0);
   }
   const int first_pos = L - nq;                           // position of query 0
-  const int qpos = first_pos + i0 + n;                    // this lane's query position
-  const int last_pos = first_pos + min(nq, i0 + kQTile) - 1;
-  const int nblk = last_pos / kBlockSize + 1;             // key blocks the tile needs
+  int qpos[TQ];                                           // this lane's query positions
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) qpos[t] = first_pos + i0 + kQTile * t + n;
+  const int last_pos = first_pos + min(nq, i0 + TQ * kQTile) - 1;
+  const int nblk = last_pos / kBlockSize + 1;             // key blocks the wave needs
 
   const char* kbase = static_cast<const char*>(pr.kpool) + g * kTileBytes;
   const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
@@ -128,7 +142,7 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? 3 : 1) void prefill_kernel(Pref
     if (__any(e < 0 || e >= pr.num_blocks)) bad = true;
   }
   if (bad) {
-    for (int idx = lane; idx < kQTile * D; idx += 64) {
+    for (int idx = lane; idx < TQ * kQTile * D; idx += 64) {
       const int r = idx / D;
       if (i0 + r < nq) orow[static_cast<int64_t>(r) * pr.Hq * D + idx % D] = __builtin_nanf("");
     }
@@ -155,17 +169,20 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? 3 : 1) void prefill_kernel(Pref
   // from global memory into LDS (global_load_lds: lane i of a wave writes the
   // wave's LDS base + 16 i), so no registers hold the staged data.
   constexpr int kStage = WPG > 1 ? 4 * kTileU4 / (64 * WPG) : 1;   // loads per thread per pair
-  constexpr int kBufs = 3;      // pairs in LDS: the one computed and two in flight
-  // three separate arrays, so the compiler can tell a buffer being filled
-  // from the one being read and need not wait for the fill before the reads
+  // kBufs pairs in LDS: the one computed and kBufs - 1 in flight.  Separate
+  // arrays, so the compiler can tell a buffer being filled from the one being
+  // read and need not wait for the fill before the reads.
+  constexpr int kBufs = 4;
   __shared__ uint4 lds0[4][WPG > 1 ? kTileU4 : 1];
   __shared__ uint4 lds1[4][WPG > 1 ? kTileU4 : 1];
   __shared__ uint4 lds2[4][WPG > 1 ? kTileU4 : 1];
+  __shared__ uint4 lds3[4][WPG > 1 ? kTileU4 : 1];
   auto buf_of = [&](auto bc) -> uint4(*)[WPG > 1 ? kTileU4 : 1] {
     constexpr int bi = decltype(bc)::value;
     if constexpr (bi == 0) return lds0;
     else if constexpr (bi == 1) return lds1;
-    else return lds2;
+    else if constexpr (bi == 2) return lds2;
+    else return lds3;
   };
   auto gload_lds = [&](int pp, auto bc) {
     const int p0 = phys_of(min(2 * pp, nblk - 1)), p1 = phys_of(min(2 * pp + 1, nblk - 1));
@@ -215,51 +232,76 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? 3 : 1) void prefill_kernel(Pref
     }
   };
 
-  float m_run = -INFINITY, l_lane = 0.f;
-  f32x4_t acc[NTL];
+  float m_run[TQ], l_lane[TQ];
+  f32x4_t acc[TQ][NTL];
 #pragma unroll
-  for (int t = 0; t < NTL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TQ; ++t) {
+    m_run[t] = -INFINITY;
+    l_lane[t] = 0.f;
+#pragma unroll
+    for (int d = 0; d < NTL; ++d) acc[t][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
-  auto qk_softmax = [&](int pp, uint4& phi, uint4& plo) {
+  // scores of tile t against the pair's 32 keys, online softmax update,
+  // probabilities split into the two half-precision parts of P.V's A operand.
+  // The running max is kept in the log2 domain (scale * log2(e) applied);
+  // the max of a pair is taken over the raw scores (the scale is positive)
+  // and each weight is exp2(s * scale - m) with one fused multiply-add.  The
+  // causal mask is applied only to pairs that reach past the tile's first
+  // query position (the tile's earlier pairs hold no later key).
+  auto qk_softmax = [&](int pp, int t, uint4& phi, uint4& plo) {
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      s0 = Mfma<T>::qk(kreg[0][kk], qr[kk], s0);
-      s1 = Mfma<T>::qk(kreg[1][kk], qr[kk], s1);
+      s0 = Mfma<T>::qk(kreg[0][kk], qr[t][kk], s0);
+      s1 = Mfma<T>::qk(kreg[1][kk], qr[t][kk], s1);
     }
     const int kpos0 = 2 * pp * kBlockSize + 4 * j;        // key position of s0[0]
     float sv[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sv[e] = (kpos0 + e <= qpos) ? s0[e] * pr.scale_log2 : -INFINITY;
-      sv[4 + e] = (kpos0 + kBlockSize + e <= qpos) ? s1[e] * pr.scale_log2 : -INFINITY;
+      sv[e] = s0[e];
+      sv[4 + e] = s1[e];
+    }
+    // the tile's first query position: first_pos + i0 + 16t (uniform)
+    if ((2 * pp + 2) * kBlockSize - 1 > first_pos + i0 + kQTile * t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[e] = (kpos0 + e <= qpos[t]) ? sv[e] : -INFINITY;
+        sv[4 + e] = (kpos0 + kBlockSize + e <= qpos[t]) ? sv[4 + e] : -INFINITY;
+      }
     }
     float bm = sv[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[e]);
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m_run, bm);
-    if (__any(mn != m_run)) {
+    // a tile whose queries all precede the pair keeps m = -inf rows only
+    // while no key was valid; the first pair holds key 0, valid for every
+    // query, so m_run is finite from there on
+    const float mn = fmaxf(m_run[t], bm * pr.scale_log2);
+    if (__any(mn != m_run[t])) {
       // a query's running max moved: rescale its O row by 2^(m_old - m_new)
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      l_lane *= alpha;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[t] - mn);
+      l_lane[t] *= alpha;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float ar = __shfl(alpha, 4 * j + e);        // alpha of O row 4j + e
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) acc[t][e] *= ar;
+        for (int d = 0; d < NTL; ++d) acc[t][d][e] *= ar;
       }
-      m_run = mn;
+      m_run[t] = mn;
     }
     float pe[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_run);
-    l_lane += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+    for (int e = 0; e < 8; ++e)
+      pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], pr.scale_log2, -m_run[t]));
+    l_lane[t] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
     Mfma<T>::split8(pe, phi, plo);
   };
 
-  auto pv = [&](int pp, uint4 phi, uint4 plo) {
+  // V rows at positions >= L are zeroed, so unwritten slots never reach O
+  auto mask_v = [&](int pp) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int kb = 2 * pp + u;
@@ -269,21 +311,24 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? 3 : 1) void prefill_kernel(Pref
         const uint32_t mx = (kp + 0 < L ? 0x0000FFFFu : 0u) | (kp + 1 < L ? 0xFFFF0000u : 0u);
         const uint32_t my = (kp + 2 < L ? 0x0000FFFFu : 0u) | (kp + 3 < L ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-          vreg[u][t].x &= mx;
-          vreg[u][t].y &= my;
+        for (int d = 0; d < NTL; ++d) {
+          vreg[u][d].x &= mx;
+          vreg[u][d].y &= my;
         }
       }
     }
+  };
+  auto pv = [&](int t, uint4 phi, uint4 plo) {
 #pragma unroll
-    for (int t = 0; t < NTL; ++t) {
-      const uint4 v = make_uint4(vreg[0][t].x, vreg[0][t].y, vreg[1][t].x, vreg[1][t].y);
-      acc[t] = Mfma<T>::pv8(phi, v, acc[t]);
-      acc[t] = Mfma<T>::pv8(plo, v, acc[t]);
+    for (int d = 0; d < NTL; ++d) {
+      const uint4 v = make_uint4(vreg[0][d].x, vreg[0][d].y, vreg[1][d].x, vreg[1][d].y);
+      acc[t][d] = Mfma<T>::pv8(phi, v, acc[t][d]);
+      acc[t][d] = Mfma<T>::pv8(plo, v, acc[t][d]);
     }
   };
 
   if constexpr (WPG == 1) {
+    static_assert(TQ == 1, "one-wave workgroups take one tile");
     // K of the next pair is issued once QK has consumed the current one, V of
     // the next pair once P.V has (scheduling barriers keep the compiler from
     // hoisting the loads above the matrix ops that still read the registers)
@@ -291,77 +336,93 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? 3 : 1) void prefill_kernel(Pref
     issue_v();
     for (int pp = 0; pp < npair; ++pp) {
       uint4 phi, plo;
-      qk_softmax(pp, phi, plo);
+      qk_softmax(pp, 0, phi, plo);
       __builtin_amdgcn_sched_barrier(0);
       if (pp + 1 < npair) issue_k(pp + 1);
       __builtin_amdgcn_sched_barrier(0);
-      pv(pp, phi, plo);
+      mask_v(pp);
+      pv(0, phi, plo);
       __builtin_amdgcn_sched_barrier(0);
       if (pp + 1 < npair) issue_v();
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    // pairs pp + 1 and pp + 2 travel global -> LDS while pair pp is computed
-    // from LDS; one barrier per pair orders both a buffer's writes before its
-    // reads and its reads before the rewrite three pairs later (every wave of
-    // the workgroup runs the same npair).  The only vector-memory operations
-    // in the loop are these loads, so "at most kStage outstanding" means the
-    // next pair's have landed.
+    // pairs pp + 1 .. pp + kBufs - 1 travel global -> LDS while pair pp is
+    // computed from LDS; one barrier per pair orders both a buffer's writes
+    // before its reads and its reads before the rewrite kBufs pairs later
+    // (every wave of the workgroup runs the same npair).  The only
+    // vector-memory operations in the loop are these loads, and they complete
+    // in order, so "at most k * kStage outstanding" means every pair but the
+    // last k issued has landed.
     // s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt left at its
     // no-wait maximum 7, lgkmcnt 0 so that this wave's LDS reads of the pair
     // have returned before the barrier lets a refill of that buffer start
-    constexpr int kWaitNext = (kStage & 0xF) | (7 << 4) | ((kStage >> 4) << 14);
-    constexpr int kWaitAll = 7 << 4;
+    constexpr auto wait_imm = [](int vm) { return (vm & 0xF) | (7 << 4) | ((vm >> 4) << 14); };
+    static_assert(2 * kStage < 64, "vmcnt immediate");
+    // wait until at most `ahead` pairs issued after the next one are in flight
+    auto wait_pairs = [&](int ahead) {
+      if (ahead >= 2)
+        __builtin_amdgcn_s_waitcnt(wait_imm(2 * kStage));
+      else if (ahead == 1)
+        __builtin_amdgcn_s_waitcnt(wait_imm(kStage));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_imm(0));
+    };
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
     using B2 = std::integral_constant<int, 2>;
+    using B3 = std::integral_constant<int, 3>;
+    static_assert(kBufs == 4, "the pair loop below is unrolled for four buffers");
     gload_lds(0, B0{});
-    if (npair > 1) {
-      gload_lds(1, B1{});
-      __builtin_amdgcn_s_waitcnt(kWaitNext);
-    } else {
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-    }
+    if (npair > 1) gload_lds(1, B1{});
+    if (npair > 2) gload_lds(2, B2{});
+    wait_pairs(min(npair - 1, 2));   // pair 0 has landed
     __syncthreads();
-    // pair pp in buffer pp % 3; the loop is unrolled by three so that every
+    // pair pp in buffer pp % 4; the loop is unrolled by four so that every
     // buffer index is a constant
     auto step = [&](int pp, auto cur, auto fill) {
       // the buffer filled here was last read in pair pp - 1, before the barrier
-      if (pp + 2 < npair) gload_lds(pp + 2, fill);
+      if (pp + 3 < npair) gload_lds(pp + 3, fill);
       lread_k(cur);
-      uint4 phi, plo;
-      qk_softmax(pp, phi, plo);
+      uint4 phi[TQ], plo[TQ];
+#pragma unroll
+      for (int t = 0; t < TQ; ++t) qk_softmax(pp, t, phi[t], plo[t]);
       lread_v(cur);
-      pv(pp, phi, plo);
-      if (pp + 2 < npair)
-        __builtin_amdgcn_s_waitcnt(kWaitNext);    // this wave's pair pp + 1 has landed
-      else
-        __builtin_amdgcn_s_waitcnt(kWaitAll);
+      mask_v(pp);
+#pragma unroll
+      for (int t = 0; t < TQ; ++t) pv(t, phi[t], plo[t]);
+      // this wave's pair pp + 1 has landed (pairs pp + 2, pp + 3 may still
+      // travel) ...
+      wait_pairs(min(npair - 1, pp + 3) - (pp + 1));
       // ... and every wave's.  A bare barrier: the fence of __syncthreads
-      // would also drain the loads of pair pp + 2.  The clobber keeps the
+      // would also drain the loads still in flight.  The clobber keeps the
       // compiler from moving LDS reads across it.
       asm volatile("s_barrier" ::: "memory");
     };
-    for (int pp = 0; pp < npair; pp += 3) {
-      step(pp, B0{}, B2{});
+    for (int pp = 0; pp < npair; pp += 4) {
+      step(pp, B0{}, B3{});
       if (pp + 1 < npair) step(pp + 1, B1{}, B0{});
       if (pp + 2 < npair) step(pp + 2, B2{}, B1{});
+      if (pp + 3 < npair) step(pp + 3, B3{}, B2{});
     }
   }
 
-  // l of query n, then of O row 4j + e
-  float l = l_lane;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  // l of query n, then of O row 4j + e, for each tile
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = 4 * j + e;
-    const float lr = __shfl(l, r);
-    if (i0 + r < nq) {
-      const float inv = 1.0f / lr;
+  for (int t = 0; t < TQ; ++t) {
+    float l = l_lane[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
 #pragma unroll
-      for (int t = 0; t < NTL; ++t)
-        orow[static_cast<int64_t>(r) * pr.Hq * D + t * 16 + n] = acc[t][e] * inv;
+    for (int e = 0; e < 4; ++e) {
+      const int r = kQTile * t + 4 * j + e;               // row of the wave's queries
+      const float lr = __shfl(l, 4 * j + e);
+      if (i0 + r < nq) {
+        const float inv = 1.0f / lr;
+#pragma unroll
+        for (int d = 0; d < NTL; ++d)
+          orow[static_cast<int64_t>(r) * pr.Hq * D + d * 16 + n] = acc[t][d][e] * inv;
+      }
     }
   }
 }
@@ -422,17 +483,20 @@ extern "C" pa_status pa_prefill(float* out, const void* q, const void* k_pool,
   pr.max_qlen = max_query_len;
   pr.scale_log2 = scale * kLog2e;
   pr.ntiles = (max_query_len + kQTile - 1) / kQTile;
-  // four query heads per workgroup when the group size allows it
+  // four query heads per workgroup when the group size allows it, each wave
+  // then taking kPairTiles consecutive query tiles
   const int wpg = pr.G % 4 == 0 ? 4 : 1;
-  const uint64_t nwg = static_cast<uint64_t>(num_q_heads / wpg) * pr.ntiles * num_seqs;
+  const int tq = wpg == 4 ? kPairTiles : 1;
+  const uint64_t nwg = static_cast<uint64_t>(num_q_heads / wpg) *
+                       ((pr.ntiles + tq - 1) / tq) * num_seqs;
   if (nwg > 0x7fffffffull)
     return fail(PA_ERR_INVALID_ARG, "%s: %llu workgroups exceed the launch limit", fn,
                 static_cast<unsigned long long>(nwg));
   const dim3 grid(static_cast<uint32_t>(nwg));
   hipStream_t s = static_cast<hipStream_t>(stream);
-#define PA_PREFILL(TAG, DIM)                                               \
-  (wpg == 4 ? (prefill_kernel<TAG, DIM, 4><<<grid, 256, 0, s>>>(pr), 0)    \
-            : (prefill_kernel<TAG, DIM, 1><<<grid, 64, 0, s>>>(pr), 0))
+#define PA_PREFILL(TAG, DIM)                                                        \
+  (wpg == 4 ? (prefill_kernel<TAG, DIM, 4, kPairTiles><<<grid, 256, 0, s>>>(pr), 0) \
+            : (prefill_kernel<TAG, DIM, 1, 1><<<grid, 64, 0, s>>>(pr), 0))
   if (dtype == PA_BF16)
     head_dim == 64 ? PA_PREFILL(BF16, 64) : PA_PREFILL(BF16, 128);
   else
