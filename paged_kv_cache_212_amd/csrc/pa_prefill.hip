@@ -44,6 +44,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQTile = 16;     // query tokens per tile
 constexpr int kPairTiles = 2;  // tiles per wave with four query heads per workgroup
+constexpr float kRescaleSlack = 8.f;  // log2-domain headroom before the running max moves
 
 struct PrefillParams {
   float* out;               // [T][Hq][D]
@@ -278,9 +279,13 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     // a tile whose queries all precede the pair keeps m = -inf rows only
     // while no key was valid; the first pair holds key 0, valid for every
-    // query, so m_run is finite from there on
+    // query, so m_run is finite from there on.
+    // Lazy rescaling: m_run is only a reference (numerator and denominator
+    // share it), so it moves only when some row's max exceeds it by more
+    // than kRescaleSlack; weights then stay below 2^kRescaleSlack, far inside
+    // fp32 and with the same relative precision in the hi/lo split.
     const float mn = fmaxf(m_run[t], bm * pr.scale_log2);
-    if (__any(mn != m_run[t])) {
+    if (__any(mn > m_run[t] + kRescaleSlack)) {
       // a query's running max moved: rescale its O row by 2^(m_old - m_new)
       const float alpha = __builtin_amdgcn_exp2f(m_run[t] - mn);
       l_lane[t] *= alpha;

@@ -13,9 +13,9 @@ from workloads.configs import prefill_case
 pytestmark = pytest.mark.gpu
 
 
-def _run(seed, dtype, lens, qlens, hq, hkv, d, max_qlen=None, tables_hook=None):
+def _run(seed, dtype, lens, qlens, hq, hkv, d, max_qlen=None, tables_hook=None, **kw):
     pk = require_gpu()
-    case, q, qs = prefill_case(seed, dtype, lens, qlens, hq, hkv, d)
+    case, q, qs = prefill_case(seed, dtype, lens, qlens, hq, hkv, d, **kw)
     got = run_gpu_step(case)                       # set-up + step: all lens[b] tokens cached
     plan, cache = got["plan"], got["cache"]
     dev = torch.device("cuda")
@@ -55,6 +55,20 @@ CASES = [
 def test_prefill_matches_oracle(dtype, lens, qlens, hq, hkv, d):
     say(f"[prefill] {dtype} lens={lens} qlens={qlens} Hq={hq} Hkv={hkv} D={d}")
     case, q, qs, got = _run(11, dtype, lens, qlens, hq, hkv, d)
+    want = _oracle(case, q, qs, dtype)
+    err = max_err(got, want)
+    say(f"  max |gpu - oracle| = {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_peaked_scores_match_oracle(dtype):
+    """1% of the key vectors scaled x8 (as in the long-context workload): the
+    scores span a wide range, so the running max moves by large steps and the
+    kernel's accumulator rescaling is exercised."""
+    say(f"[prefill] peaked scores {dtype}")
+    case, q, qs, got = _run(13, dtype, [1500, 700, 2048], [1500, 300, 512], 32, 8, 128,
+                            boost_prob=0.01)
     want = _oracle(case, q, qs, dtype)
     err = max_err(got, want)
     say(f"  max |gpu - oracle| = {err:.3e}")

@@ -363,12 +363,13 @@ def custom_case(seed, dtype, lens, hq, hkv, d, device="cpu", *, num_blocks=None,
 
 
 def prefill_case(seed, dtype, lens, qlens, hq, hkv, d, device="cpu", *, num_blocks=None,
-                 pool_factor=1.2):
+                 pool_factor=1.2, boost_prob=0.0):
     """Seeded inputs for attending a chunk of query tokens per sequence
     (prefill, chunked prefill): the decode case of the same sequences, whose
     set-up and step append leave all lens[b] tokens in the cache, plus query
     rows q [T][hq][d] for the last qlens[b] positions of each sequence and
-    their row offsets query_start [B+1] (T = query_start[-1]).
+    their row offsets query_start [B+1] (T = query_start[-1]).  boost_prob:
+    as in custom_case (key vectors scaled x8 with that probability).
 
     Returns (case, q, query_start)."""
     lens = np.asarray(lens, dtype=np.int64)
@@ -376,7 +377,7 @@ def prefill_case(seed, dtype, lens, qlens, hq, hkv, d, device="cpu", *, num_bloc
     if qlens.shape != lens.shape or (qlens < 0).any() or (qlens > lens).any():
         raise ValueError("qlens must be in [0, lens] per sequence")
     case = custom_case(seed, dtype, lens, hq, hkv, d, device, num_blocks=num_blocks,
-                       pool_factor=pool_factor)
+                       pool_factor=pool_factor, boost_prob=boost_prob)
     query_start = np.zeros(len(lens) + 1, dtype=np.int64)
     query_start[1:] = np.cumsum(qlens)
     g = torch.Generator(device=device)
