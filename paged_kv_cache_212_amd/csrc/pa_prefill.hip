@@ -170,7 +170,7 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
   // from global memory into LDS (global_load_lds: lane i of a wave writes the
   // wave's LDS base + 16 i), so no registers hold the staged data.
   constexpr int kStage = WPG > 1 ? 4 * kTileU4 / (64 * WPG) : 1;   // loads per thread per pair
-  // kBufs pairs in LDS: the one computed and kBufs - 1 in flight.  Separate
+  // kBufs pairs in LDS: the two computed and the two in flight.  Separate
   // arrays, so the compiler can tell a buffer being filled from the one being
   // read and need not wait for the fill before the reads.
   constexpr int kBufs = 4;
@@ -352,42 +352,23 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    // pairs pp + 1 .. pp + kBufs - 1 travel global -> LDS while pair pp is
-    // computed from LDS; one barrier per pair orders both a buffer's writes
-    // before its reads and its reads before the rewrite kBufs pairs later
-    // (every wave of the workgroup runs the same npair).  The only
-    // vector-memory operations in the loop are these loads, and they complete
-    // in order, so "at most k * kStage outstanding" means every pair but the
-    // last k issued has landed.
-    // s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt left at its
-    // no-wait maximum 7, lgkmcnt 0 so that this wave's LDS reads of the pair
-    // have returned before the barrier lets a refill of that buffer start
-    constexpr auto wait_imm = [](int vm) { return (vm & 0xF) | (7 << 4) | ((vm >> 4) << 14); };
-    static_assert(2 * kStage < 64, "vmcnt immediate");
-    // wait until at most `ahead` pairs issued after the next one are in flight
-    auto wait_pairs = [&](int ahead) {
-      if (ahead >= 2)
-        __builtin_amdgcn_s_waitcnt(wait_imm(2 * kStage));
-      else if (ahead == 1)
-        __builtin_amdgcn_s_waitcnt(wait_imm(kStage));
-      else
-        __builtin_amdgcn_s_waitcnt(wait_imm(0));
-    };
+    // Pairs are taken two at a time: while pairs pp and pp + 1 are computed
+    // from LDS, pairs pp + 2 and pp + 3 travel global -> LDS into the two
+    // buffers read in the previous double step.  One wait and one barrier
+    // per double step order both the buffers' writes before their reads and
+    // their reads before the rewrite (every wave of the workgroup runs the
+    // same npair).  The only vector-memory operations in the loop are these
+    // loads.
+    // s_waitcnt immediate: vmcnt 0, expcnt left at its no-wait maximum 7,
+    // lgkmcnt 0 so that this wave's LDS reads have returned before the
+    // barrier lets a refill of those buffers start
+    constexpr int kWaitAll = 7 << 4;
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
     using B2 = std::integral_constant<int, 2>;
     using B3 = std::integral_constant<int, 3>;
-    static_assert(kBufs == 4, "the pair loop below is unrolled for four buffers");
-    gload_lds(0, B0{});
-    if (npair > 1) gload_lds(1, B1{});
-    if (npair > 2) gload_lds(2, B2{});
-    wait_pairs(min(npair - 1, 2));   // pair 0 has landed
-    __syncthreads();
-    // pair pp in buffer pp % 4; the loop is unrolled by four so that every
-    // buffer index is a constant
-    auto step = [&](int pp, auto cur, auto fill) {
-      // the buffer filled here was last read in pair pp - 1, before the barrier
-      if (pp + 3 < npair) gload_lds(pp + 3, fill);
+    static_assert(kBufs == 4, "the pair loop below is written for four buffers");
+    auto compute = [&](int pp, auto cur) {
       lread_k(cur);
       uint4 phi[TQ], plo[TQ];
 #pragma unroll
@@ -396,19 +377,26 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
       mask_v(pp);
 #pragma unroll
       for (int t = 0; t < TQ; ++t) pv(t, phi[t], plo[t]);
-      // this wave's pair pp + 1 has landed (pairs pp + 2, pp + 3 may still
-      // travel) ...
-      wait_pairs(min(npair - 1, pp + 3) - (pp + 1));
-      // ... and every wave's.  A bare barrier: the fence of __syncthreads
-      // would also drain the loads still in flight.  The clobber keeps the
-      // compiler from moving LDS reads across it.
+    };
+    auto dstep = [&](int pp, auto ca, auto cb, auto fa, auto fb) {
+      if (pp + 2 < npair) gload_lds(pp + 2, fa);
+      if (pp + 3 < npair) gload_lds(pp + 3, fb);
+      compute(pp, ca);
+      if (pp + 1 < npair) compute(pp + 1, cb);
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      // a bare barrier: the clobber keeps the compiler from moving LDS reads
+      // across it
       asm volatile("s_barrier" ::: "memory");
     };
+    gload_lds(0, B0{});
+    if (npair > 1) gload_lds(1, B1{});
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __syncthreads();
+    // pair pp in buffer pp % 4; unrolled by four pairs so that every buffer
+    // index is a constant
     for (int pp = 0; pp < npair; pp += 4) {
-      step(pp, B0{}, B3{});
-      if (pp + 1 < npair) step(pp + 1, B1{}, B0{});
-      if (pp + 2 < npair) step(pp + 2, B2{}, B1{});
-      if (pp + 3 < npair) step(pp + 3, B3{}, B2{});
+      dstep(pp, B0{}, B1{}, B2{}, B3{});
+      if (pp + 2 < npair) dstep(pp + 2, B2{}, B3{}, B0{}, B1{});
     }
   }
 
