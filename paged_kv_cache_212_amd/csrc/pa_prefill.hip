@@ -60,6 +60,21 @@ struct PrefillParams {
   float scale_log2;
 };
 
+// max(v of lane l, v of lane l ^ 16) and of lane l ^ 32.  v_permlane16_swap /
+// v_permlane32_swap of a register with itself give every lane both values of
+// its pair (lanes with bit 4, resp. bit 5, clear then set): a VALU exchange,
+// no LDS round trip.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // WPG: waves per workgroup.  1: one query head per workgroup, K/V read by
 // each wave from global memory (L2).  4 (G a multiple of 4): four query heads
 // of one KV head and the same tiles per workgroup; each pair of K/V blocks is
@@ -275,8 +290,8 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     float bm = sv[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[e]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = max_xor16(bm);
+    bm = max_xor32(bm);
     // a tile whose queries all precede the pair keeps m = -inf rows only
     // while no key was valid; the first pair holds key 0, valid for every
     // query, so m_run is finite from there on.
