@@ -60,6 +60,10 @@ struct PrefillParams {
   float scale_log2;
 };
 
+// LDS slot of V chunk c: the low three bits XORed with bits 4..6 (an
+// involution that permutes each group of 16 chunks).
+__device__ __forceinline__ int vswz(int c) { return c ^ ((c >> 4) & 7); }
+
 // max(v of lane l, v of lane l ^ 16) and of lane l ^ 32.  v_permlane16_swap /
 // v_permlane32_swap of a register with itself give every lane both values of
 // its pair (lanes with bit 4, resp. bit 5, clear then set): a VALU exchange,
@@ -206,8 +210,10 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     for (int r = 0; r < kStage; ++r) {
       const int c = static_cast<int>(threadIdx.x) + r * 64 * WPG;
       const int part = c / kTileU4, idx = c % kTileU4;
+      // V tiles: LDS slot idx holds chunk vswz(idx) (see lread_v)
+      const int sidx = part < 2 ? idx : vswz(idx);
       const char* src = (part < 2 ? kbase : vbase) + ((part & 1) ? p1 : p0) * block_stride +
-                        idx * 16;
+                        sidx * 16;
       uint4* dst = &buf_of(bc)[0][0] + (c - lane);      // the wave's first word
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
@@ -219,13 +225,18 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) kreg[u][kk] = buf_of(bc)[u][(j * 16 + n) + kk * 64];
   };
+  // V chunk c (16 bytes: 8 tokens of one dim) sits in LDS slot vswz(c).  A
+  // lane reads dim n of the 8 tiles t (chunks 16t + n, 256 bytes apart: one
+  // bank); swizzled, tile t's chunk moves by (n ^ t) - n slots, so the 8 reads
+  // of a lane fall in 8 different banks, while one read of a tile still covers
+  // 16 distinct slots.
   auto lread_v = [&](auto bc) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const uint2* vt = reinterpret_cast<const uint2*>(buf_of(bc)[2 + u]) +
-                        (((j >> 1) * D + n) * 16 + (j & 1) * 8) / 8;
+      const uint2* vt = reinterpret_cast<const uint2*>(buf_of(bc)[2 + u]);
 #pragma unroll
-      for (int t = 0; t < NTL; ++t) vreg[u][t] = vt[t * 16 * 16 / 8];
+      for (int t = 0; t < NTL; ++t)
+        vreg[u][t] = vt[vswz((j >> 1) * D + t * 16 + n) * 2 + (j & 1)];
     }
   };
   auto issue_k = [&](int pp) {
