@@ -14,22 +14,26 @@
 // (four query heads of one KV head) share a workgroup and their K/V through
 // LDS, and each wave takes two consecutive tiles; otherwise one wave, one
 // tile.  K/V of a block are re-read by every tile and query head of its KV
-// head, so they use plain (cached) loads.  Per 16-token block of keys:
-//   S^T (16 keys x 16 queries) = K . Q^T on v_mfma_f32_16x16x32: A = K (lane
-//     reads key n, dims kk*32 + 8j .. +8), B = Q (query n, same dims).  Result:
-//     lane (n, j) holds query n against keys 4j + e (e = 0..3).
-//   That is the A operand of O (16 queries x 16 dims) += P (16 queries x 16
-//     keys) . V (16 keys x 16 dims) on v_mfma_f32_16x16x16 (lane: row n,
-//     k = keys 4j + e), so the probabilities need no transpose.  B = V: lane
-//     (n, j) holds dim t*16 + n of keys 4j .. 4j+3, 8 contiguous bytes of the
-//     V tile (8 consecutive tokens of a dim are stored together).  P is split
-//     into a high and a low half-precision part (two MFMAs).
+// head, so they use plain (cached) loads.  Keys go in pairs of 16-token blocks
+// (32 keys); per pair and tile:
+//   S^T (16 keys x 16 queries) = K . Q^T on v_mfma_f32_16x16x32, one chain
+//     per block: A = K (lane reads key n, dims kk*32 + 8j .. +8), B = Q (query
+//     n, same dims).  Result: lane (n, j) holds query n against keys 4j + e
+//     (e = 0..3) of the block.
+//   That is the A operand of O (16 queries x 16 dims) += P (16 queries x 32
+//     keys) . V (32 keys x 16 dims) on v_mfma_f32_16x16x32 (lane: row n; k
+//     index 8j + e is key 4j + e of the first block for e < 4, of the second
+//     for e >= 4), so the probabilities need no transpose.  B = V: lane (n, j)
+//     holds dim t*16 + n of keys 4j .. 4j+3 of both blocks, 8 contiguous bytes
+//     of each V tile (8 consecutive tokens of a dim are stored together).  P is
+//     split into a high and a low half-precision part (two MFMAs).
 //   O: lane (n, j) holds dim t*16 + n of queries 4j + e.
-// Online softmax per query in the log2 domain (max and sum across the 4 lane
-// groups with two xor shuffles); the causal mask selects scores to -inf, and
-// V rows at positions >= L are zeroed so unwritten slots never reach O.
-// Blocks are double-buffered: the loads of block kb + 2 are issued once block
-// kb has been consumed.
+// Online softmax per query in the log2 domain (max across the 4 lane groups
+// with lane swaps, lazy rescaling); the causal mask selects scores to -inf,
+// and V rows at positions >= L are zeroed so unwritten slots never reach O.
+// With four query heads per workgroup the pairs travel global -> LDS two
+// pairs ahead (four LDS buffers, one barrier per two pairs); a one-wave
+// workgroup double-buffers them in registers.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
