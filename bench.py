@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -92,7 +93,12 @@ def copy_calibration():
 
 
 def kernel_src_hash() -> str:
-    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the decode kernels' source with comments and whitespace removed,
+    so that only a change to the code itself invalidates stored counters."""
+    src = open(DECODE_SRC, encoding="utf-8").read()
+    src = re.sub(r"//[^\n]*", "", src)
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()[:16]
 
 
 def traffic_for(workload: str):

@@ -1,24 +1,28 @@
 // PagedAttention decode on gfx950.
 //
-// For every sequence b, KV head g and partition p (a run of P tokens), one
-// workgroup walks the block table from logical to physical blocks and reads
-// the 16-token K and V tiles it needs, in logical order (page 3, abeam.tech
-// review, sections 「用語解説」 (block table) and
-// 「モデル構造ではなくサービング基盤の変更」: the kernel follows the table to read
-// the KV it needs).  It computes softmax(scale * q.K^T) V for the G query
-// heads that share KV head g with an online (running max, running sum)
-// softmax.  A sequence longer than one partition leaves per-partition
-// (max, sum, weighted V) partials that merge_kernel combines with a
-// log-sum-exp reduction; paging changes where K/V live, not the result (page 3,
-// section 「よくある質問」; page 4, FAQ).
+// For every sequence b and KV head g, waves walk the block table from
+// logical to physical blocks and read the 16-token K and V tiles they need,
+// in logical order (page 3, abeam.tech review, sections 「用語解説」 (block
+// table) and 「モデル構造ではなくサービング基盤の変更」: the kernel follows the
+// table to read the KV it needs).  They compute softmax(scale * q.K^T) V for
+// the G query heads that share KV head g with an online (running max,
+// running sum) softmax.  A context cut into pieces leaves per-piece (max,
+// sum, weighted V) partials that merge_kernel combines with a log-sum-exp
+// reduction; paging changes where K/V live, not the result (page 3, section
+// 「よくある質問」; page 4, FAQ).
 //
-// Two partition kernels:
-//   * decode_mfma_kernel (fp16/bf16, G <= 16): one 64-lane wave per block at a
-//     time; S^T = K.Q^T on a 16x16x32 MFMA (tokens x heads), P.V on 16x16x16
-//     MFMAs (heads x dims) with P split into a high and a low half-precision
-//     part so the weights keep ~16 (bf16) / ~22 (fp16) significant bits.
-//   * decode_generic_kernel (any dtype): plain fp32 FMAs, one thread per
-//     (head, token) score and per (head, dim) output.
+// Work distribution:
+//   * decode_split_kernel: the batch's (sequence, KV head, run of blocks)
+//     units cut into equal chunks, one per wave (4 waves per workgroup, one
+//     workgroup per compute unit);
+//   * decode_fixed_kernel: one wave per (KV head, fixed partition, sequence).
+// Engines (one wave attends one (b, g) range of blocks):
+//   * attend4 (fp16/bf16 and 8-bit codes, G <= 4): 4 blocks per step on the
+//     4x4x4 16-block MFMA with broadcast operands;
+//   * attend_range (fp16/bf16, G <= 16): 2 blocks per step on 16x16x32 MFMAs.
+//   P.V takes P split into a high and a low half-precision part, so the
+//   weights keep ~16 (bf16) / ~22 (fp16) significant bits.
+//   * decode_generic_kernel (any dtype, fp32 pools): plain fp32 FMAs.
 // Scores are kept in the log2 domain (scale * log2(e) folded in) and
 // exponentiated with exp2.
 #include <hip/hip_runtime.h>
