@@ -166,6 +166,21 @@ def test_single_token_context_returns_value_exactly(dtype, kernel):
         assert np.array_equal(got["out"][i].astype(np.float64), np.repeat(v, 4, axis=0))
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["decode_step", "append+decode"])
+def test_max_batch_single_token_contexts(fused):
+    """The largest batch the C ABI takes (65535 sequences), one token each:
+    every (sequence, head) is its own range of the even split (hundreds per
+    wave, the batch walked from memory), and each row must equal its token's
+    V exactly."""
+    B = 65535
+    case = custom_case(23, "bf16", [1] * B, 4, 1, 64)
+    say(f"[max batch] B={B} L=1 fused={fused}")
+    got = run_gpu_step(case, fused=fused)
+    idx = np.array([case.rows[int(case.batch[i])][0] for i in range(B)])
+    v = to_f64(bits_of(case.v_tok[torch.as_tensor(idx)], "bf16"), "bf16")     # [B][1][64]
+    assert np.array_equal(got["out"].astype(np.float64), np.repeat(v, 4, axis=1))
+
+
 EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 511, 512, 513, 1023, 1024, 1025, 1600]
 
 
