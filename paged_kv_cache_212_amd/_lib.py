@@ -39,18 +39,20 @@ _p_i32, _p_i64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
 SIGNATURES = {
     "pa_last_error": (C.c_char_p, []),
     "pa_version": (C.c_char_p, []),
-    "pa_bm_create": (C.c_int, [_i32, _i32, _p_i32, C.POINTER(_vp)]),
+    # array arguments of the block manager are passed as addresses (c_void_p):
+    # a typed ctypes pointer per call costs more than the C call itself
+    "pa_bm_create": (C.c_int, [_i32, _i32, _vp, C.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),
-    "pa_bm_add_seq": (C.c_int, [_vp, _i64, _i32, _p_i64]),
+    "pa_bm_add_seq": (C.c_int, [_vp, _i64, _i32, _vp]),
     "pa_bm_fork": (C.c_int, [_vp, _i64, _i64]),
-    "pa_bm_extend": (C.c_int, [_vp, _i64, _i32, _p_i64, _p_i32, _p_i32]),
-    "pa_bm_append_slots": (C.c_int, [_vp, _p_i64, _i32, _p_i64, _p_i32, _p_i32]),
+    "pa_bm_extend": (C.c_int, [_vp, _i64, _i32, _vp, _vp, _p_i32]),
+    "pa_bm_append_slots": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _p_i32]),
     "pa_bm_free_seq": (C.c_int, [_vp, _i64]),
     "pa_bm_release_before": (C.c_int, [_vp, _i64, _i32, _p_i32]),
-    "pa_bm_reorder": (C.c_int, [_vp, _p_i64, _i32, _p_i64, _p_i32, _i32]),
+    "pa_bm_reorder": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32]),
     "pa_copy_blocks_layers": (C.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                         C.c_int, _vp]),
-    "pa_bm_block_tables": (C.c_int, [_vp, _p_i64, _i32, _i32, _p_i32, _p_i32]),
+    "pa_bm_block_tables": (C.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "pa_bm_seq_len": (C.c_int, [_vp, _i64, _p_i32]),
     "pa_bm_refcount": (C.c_int, [_vp, _i32, _p_i32]),
     "pa_bm_stats": (C.c_int, [_vp, C.POINTER(BmStats)]),

@@ -9,7 +9,10 @@ from ._lib import BmStats, check, lib
 
 
 def _ptr(a: np.ndarray, ctype):
-    return a.ctypes.data_as(C.POINTER(ctype))
+    """Address of a contiguous array of `ctype` elements (the C arguments are
+    c_void_p; the element type is checked here)."""
+    assert a.dtype.itemsize == C.sizeof(ctype) and a.flags.c_contiguous
+    return a.ctypes.data
 
 
 class BlockManager:
