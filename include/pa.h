@@ -247,8 +247,9 @@ pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools, int3
 /* How pa_decode splits contexts for these arguments; partition_size is
  *   > 0 (a multiple of 16): fixed partitions of that many tokens;
  *   0: the library's choice: the even split on the matrix-core path
- *      (fp16/bf16 and the 8-bit dtypes), fixed partitions of 256 tokens for
- *      fp32 and the plain-FMA kernel;
+ *      (fp16/bf16 and the 8-bit dtypes) with at most 4 query heads per KV
+ *      head; fixed partitions of 256 tokens for more query heads per KV head
+ *      (faster there), for fp32 and for the plain-FMA kernel;
  *   -1: the even split (matrix-core path only; fp32 and the plain-FMA kernel
  *       use 256-token partitions).
  * Returns the partition size in tokens for fixed partitions, 0 for the even

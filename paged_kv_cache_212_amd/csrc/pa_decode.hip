@@ -1590,11 +1590,14 @@ struct LaunchPlan {
   int W;
 };
 
-LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_env) {
+// G: query heads per KV head.
+LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_env, int G) {
   LaunchPlan lp{};
   lp.generic = dt == PA_F32 || (generic_env && !code_dtype(dt));
-  // default (0) on the matrix-core path: the even split
-  lp.split = (partition_size == kEvenSplit || partition_size == 0) && !lp.generic;
+  // default (0) on the matrix-core path: the even split for G <= 4 (4x4x4
+  // engine); fixed partitions for G > 4, whose 16x16-engine split kernel
+  // spills (measured with 64/8 heads, D = 128: 131 us against 82 us)
+  lp.split = (partition_size == kEvenSplit || (partition_size == 0 && G <= 4)) && !lp.generic;
   if (lp.split) {
     lp.W = split_waves();
     // a range of nblk blocks is cut into at most ceil(nblk / kMinChunkBlocks) + 1
@@ -1778,7 +1781,8 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
     return fail(PA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window %d < 0", fn, window);
   if (window > 0 && num_q_heads / num_kv_heads > 4 &&
-      !make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric)
+      !make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric,
+                 num_q_heads / num_kv_heads)
            .generic)
     return fail(PA_ERR_UNSUPPORTED,
                 "%s: a sliding window on the matrix cores needs <= 4 query heads per KV head", fn);
@@ -1794,7 +1798,7 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   if (nt && ((reinterpret_cast<uintptr_t>(nt->k_new) | reinterpret_cast<uintptr_t>(nt->v_new)) & 15))
     return fail(PA_ERR_INVALID_ARG, "%s: k_new and v_new must be 16-byte aligned", fn);
   const LaunchPlan lp = make_plan(max_context_len, partition_size, dtype,
-                                  path_from_env() == Path::kGeneric);
+                                  path_from_env() == Path::kGeneric, num_q_heads / num_kv_heads);
   const size_t need = workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
   if (need > 0 && (!workspace || workspace_bytes_given < need))
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -1889,7 +1893,9 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_head
   if (!decode_args_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                       partition_size, dtype))
     return -1;
-  return make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric).P;
+  return make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric,
+                   num_q_heads / num_kv_heads)
+      .P;
 }
 
 extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -1900,7 +1906,8 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
                       partition_size, dtype))
     return 0;
   const LaunchPlan lp =
-      make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric);
+      make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric,
+                num_q_heads / num_kv_heads);
   return workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
 }
 

@@ -217,6 +217,11 @@ def test_workspace_and_partition_queries():
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, -2, PA_BF16) == -1
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 256, PA_BF16) == 256
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 100, PA_BF16) == -1
+    # more than 4 query heads per KV head: fixed partitions by default, the
+    # even split on request
+    assert h.pa_decode_partition_size(64, 64, 8, 128, 2048, 0, PA_BF16) == 256
+    assert h.pa_decode_partition_size(64, 64, 8, 128, 2048, -1, PA_BF16) == 0
+    assert h.pa_decode_partition_size(64, 128, 8, 128, 2048, 0, PA_F16) == 256
     # one partition -> no workspace
     assert h.pa_decode_workspace_bytes(4, 8, 2, 64, 256, 512, PA_F32) == 0
     # 3 partitions of 512: m, l and acc rows, each region 256-byte aligned
