@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_bf16")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--q-heads", type=int, default=0,
+                    help="llama3_8b_bf16 with this many query heads over its 8 KV heads "
+                         "(e.g. 64: 8 query heads per KV head)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--mode", choices=("phased", "separate", "step"), default="step",
@@ -458,7 +461,13 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    case = make_case(args.workload, device=dev)
+    if args.q_heads and args.workload != "llama3_8b_bf16":
+        print(json.dumps({"error": "--q-heads applies to the llama3_8b_bf16 workload"}))
+        sys.exit(2)
+    case = make_case(args.workload, device=dev,
+                     **({"q_heads": args.q_heads} if args.q_heads else {}))
+    if args.q_heads:
+        case.name = f"{case.name}_hq{args.q_heads}"
     quant = args.kv_cache is not None
     if quant:
         case = quantized(case, args.kv_cache)

@@ -247,8 +247,8 @@ pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools, int3
 /* How pa_decode splits contexts for these arguments; partition_size is
  *   > 0 (a multiple of 16): fixed partitions of that many tokens;
  *   0: the library's choice: the even split on the matrix-core path
- *      (fp16/bf16 and the 8-bit dtypes) with at most 4 query heads per KV
- *      head; fixed partitions of 256 tokens for more query heads per KV head
+ *      (fp16/bf16 with at most 8 query heads per KV head, the 8-bit dtypes);
+ *      fixed partitions of 256 tokens for more query heads per KV head
  *      (faster there), for fp32 and for the plain-FMA kernel;
  *   -1: the even split (matrix-core path only; fp32 and the plain-FMA kernel
  *       use 256-token partitions).
@@ -257,7 +257,7 @@ pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools, int3
  *   Fixed partitions: partition p of a sequence covers tokens
  *     [p*P, (p+1)*P); each is attended by one wave, merged when more than one.
  *   Even split: the batch's work, as (sequence, KV head, run of 4 blocks)
- *     units (2 blocks when more than 4 query heads share a KV head), is cut
+ *     units (2 blocks when more than 8 query heads share a KV head), is cut
  *     into equal contiguous chunks, one per wave of a grid of 4 waves per
  *     compute unit; a (sequence, head) cut into several chunks is merged the
  *     same way. */
@@ -333,7 +333,7 @@ pa_status pa_decode_merge(float* out, const void* q, const void* k_pool, const v
  * context_lens[b] - 1 is then attended with the pool's current content).  A
  * slot elsewhere in the pool gets the token written there, but then out is
  * only defined when that slot is not attended by the step.  On the
- * matrix-core path (fp16/bf16 with at most 4 query heads per KV head, or the
+ * matrix-core path (fp16/bf16 with at most 8 query heads per KV head, or the
  * even split) the append is done inside the attention kernel, one launch
  * fewer; there a sequence whose length fails the bounds checks (NaN out
  * rows) or is 0 gets no pool write.  Otherwise the two kernels run back to
@@ -413,7 +413,7 @@ pa_status pa_prefill(float* out, const void* q, const void* k_pool, const void* 
  * widened exactly to bf16 on the matrix cores; k_scale is folded into the
  * softmax scale (fp32 product scale * k_scale) and v_scale into the output.
  * Other arguments, the workspace and the bounds checks as for pa_decode.
- * Supported: block_size 16, head_dim 64 or 128, G = Hq/Hkv <= 4
+ * Supported: block_size 16, head_dim 64 or 128, G = Hq/Hkv <= 8
  * (PA_ERR_UNSUPPORTED otherwise); the 16-bit-only plain-FMA switch
  * (PA_DECODE_KERNEL) does not apply. */
 pa_status pa_decode_quant(float* out, const void* q, const void* k_pool, const void* v_pool,
@@ -458,7 +458,7 @@ pa_status pa_decode_step_quant(float* out, const void* q, void* k_pool, void* v_
  * partition holding the window's first position; the workspace is sized as
  * for pa_decode.  Other arguments, bounds checks and the step's slot rules
  * as for pa_decode / pa_decode_step.  Supported: fp32/fp16/bf16 pools; on
- * the matrix cores G = Hq/Hkv <= 4 (PA_ERR_UNSUPPORTED for more; the
+ * the matrix cores G = Hq/Hkv <= 8 (PA_ERR_UNSUPPORTED for more; the
  * plain-FMA kernel takes any G).  window < 0 is PA_ERR_INVALID_ARG. */
 pa_status pa_decode_window(float* out, const void* q, const void* k_pool, const void* v_pool,
                            const int32_t* block_tables, const int32_t* context_lens,

@@ -17,8 +17,9 @@
 //     workgroup per compute unit);
 //   * decode_fixed_kernel: one wave per (KV head, fixed partition, sequence).
 // Engines (one wave attends one (b, g) range of blocks):
-//   * attend4 (fp16/bf16 and 8-bit codes, G <= 4): 4 blocks per step on the
-//     4x4x4 16-block MFMA with broadcast operands;
+//   * attend4 (fp16/bf16 and 8-bit codes, G <= 8): 4 blocks per step on the
+//     4x4x4 16-block MFMA with broadcast operands, one or two groups of 4
+//     query heads per K/V load;
 //   * attend_range (fp16/bf16, G <= 16): 2 blocks per step on 16x16x32 MFMAs.
 //   P.V takes P split into a high and a low half-precision part, so the
 //   weights keep ~16 (bf16) / ~22 (fp16) significant bits.
@@ -563,7 +564,7 @@ struct Engine16 {
 };
 
 // ---------------------------------------------------------------------------
-// Matrix-core engine for G <= 4 on the 4x4x4 16-block MFMA
+// Matrix-core engine for G <= 4 (one head group; G <= 8 with two) on the 4x4x4 16-block MFMA
 // (v_mfma_f32_4x4x4_16b: sixteen independent 4x4x4 products per instruction,
 // block k on lanes 4k..4k+3; with CBSZ=4 / ABID=a every block uses the A
 // operand of block a).
@@ -712,34 +713,39 @@ __device__ __forceinline__ float sum16(float v) {
   return v + __shfl_xor(v, 32);
 }
 
-template <int D>
+// NG groups of 4 query heads share each K/V load (NG = 2: G = 5..8); group
+// n holds heads 4n .. 4n+3 of the KV head's G.
+template <int D, int NG = 1>
 struct WaveState4 {
-  float m_run;           // running max (log2 domain) of head lane%4
-  float l_lane;          // this lane's share of head lane%4's running sum
-  f32x4_t acc[D / 64];   // O: lane l = dim 64t + l, element e = head e
-  bool bad;              // a table entry of the range was out of the pool
+  float m_run[NG];           // running max (log2 domain) of head 4n + lane%4
+  float l_lane[NG];          // this lane's share of that head's running sum
+  f32x4_t acc[NG][D / 64];   // O: lane l = dim 64t + l, element e = head 4n + e
+  bool bad;                  // a table entry of the range was out of the pool
 };
 
 // Loads a range's first dependencies before its length is known: Q (A
 // operand of QK: lane 4a+i holds head i, dims 64r + 4a .. +3) and the raw
 // table entries blk_begin + lane of sequence b (in bounds of the table row;
 // attend4 validates the ones it uses).
-template <int D>
+template <int D, int NG = 1>
 struct Prologue4 {
-  uint2 qr[D / 64];
+  uint2 qr[NG][D / 64];
   int tab;
 };
 
-template <int D>
+template <int D, int NG>
 __device__ __forceinline__ void prologue4(const Params& pr, int b, int g, int blk_begin,
-                                          Prologue4<D>& pre) {
+                                          Prologue4<D, NG>& pre) {
   const int lane = threadIdx.x & 63;
-  const int i = lane & 3;
-  const uint16_t* qb = static_cast<const uint16_t*>(pr.q) +
-                       (static_cast<int64_t>(b) * pr.Hq + g * pr.G + i) * D + 4 * (lane >> 2);
 #pragma unroll
-  for (int r = 0; r < D / 64; ++r)
-    pre.qr[r] = i < pr.G ? *reinterpret_cast<const uint2*>(qb + 64 * r) : make_uint2(0, 0);
+  for (int n = 0; n < NG; ++n) {
+    const int i = 4 * n + (lane & 3);   // head of the KV head's group
+    const uint16_t* qb = static_cast<const uint16_t*>(pr.q) +
+                         (static_cast<int64_t>(b) * pr.Hq + g * pr.G + i) * D + 4 * (lane >> 2);
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r)
+      pre.qr[n][r] = i < pr.G ? *reinterpret_cast<const uint2*>(qb + 64 * r) : make_uint2(0, 0);
+  }
   const int k = blk_begin + lane;
   pre.tab = k < pr.max_blocks ? pr.tables[static_cast<int64_t>(b) * pr.max_blocks + k] : 0;
 }
@@ -749,10 +755,10 @@ __device__ __forceinline__ void prologue4(const Params& pr, int b, int g, int bl
 // template parameter, so the kernel carries one copy of the loop.
 // Positions before tok_begin (a sliding window's start inside the range's
 // first block) are masked like positions past tok_end.
-template <typename T, int D>
+template <typename T, int D, int NG>
 __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_begin, int nblk,
-                                        int tok_begin, int tok_end, WaveState4<D>& st,
-                                        const Prologue4<D>& pre, bool with_new) {
+                                        int tok_begin, int tok_end, WaveState4<D, NG>& st,
+                                        const Prologue4<D, NG>& pre, bool with_new) {
   using Fmt = Kv4<T>;
   using Mma = typename Fmt::Mma;
   constexpr bool kCodes = Fmt::kCodes;
@@ -761,10 +767,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   constexpr int NH = 16 / T::kVecElems;    // V chunks per (block, dim): 2 (16-bit), 1 (codes)
   constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * T::kBytes;
   const int lane = threadIdx.x & 63;
-  const int G = pr.G;
   const int nquad = (nblk + 3) >> 2;
-
-  const uint2* qr = pre.qr;
 
   const char* kbase = static_cast<const char*>(pr.kpool) + g * kTileBytes;
   const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
@@ -965,8 +968,10 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     }
   };
 
-  auto qk_softmax = [&](int qd, uint2& phi, uint2& plo) {
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  auto qk_softmax = [&](int qd, uint2 (&phi)[NG], uint2 (&plo)[NG]) {
+    f32x4_t s0[NG], s1[NG];
+#pragma unroll
+    for (int n = 0; n < NG; ++n) s0[n] = s1[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     unroll<D / 4>([&](auto ic) {
       constexpr int s = decltype(ic)::value;   // dims 4s .. 4s+3
       uint2 kv;
@@ -977,41 +982,48 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
         const uint4& kc = kr[s / 2];
         kv = (s & 1) ? make_uint2(kc.z, kc.w) : make_uint2(kc.x, kc.y);
       }
-      if constexpr (s & 1)
-        s1 = Mma::template mma<s % 16>(qr[s / 16], kv, s1);
-      else
-        s0 = Mma::template mma<s % 16>(qr[s / 16], kv, s0);
+#pragma unroll
+      for (int n = 0; n < NG; ++n) {
+        if constexpr (s & 1)
+          s1[n] = Mma::template mma<s % 16>(pre.qr[n][s / 16], kv, s1[n]);
+        else
+          s0[n] = Mma::template mma<s % 16>(pre.qr[n][s / 16], kv, s0[n]);
+      }
     });
     const int qpos = (blk_begin + 4 * qd) * kBlockSize;   // position of the quad's token 0
     const bool valid = qpos + lane < tok_end && qpos + lane >= tok_begin;
-    float sv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sv[e] = valid ? (s0[e] + s1[e]) * pr.scale_log2 : -INFINITY;
-    quad_transpose(sv);   // lane 4a+i: head i, tokens 4a+e
-    const float lm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    if (__any(lm > st.m_run)) {
-      // the running max moved for some head: rescale by 2^(m_old - m_new)
-      const float mn = fmaxf(st.m_run, max16(lm));
-      const float alpha = __builtin_amdgcn_exp2f(st.m_run - mn);
-      st.l_lane *= alpha;
+    for (int n = 0; n < NG; ++n) {
+      float sv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), e));
+      for (int e = 0; e < 4; ++e)
+        sv[e] = valid ? (s0[n][e] + s1[n][e]) * pr.scale_log2 : -INFINITY;
+      quad_transpose(sv);   // lane 4a+i: head 4n+i, tokens 4a+e
+      const float lm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      if (__any(lm > st.m_run[n])) {
+        // the running max moved for some head: rescale by 2^(m_old - m_new)
+        const float mn = fmaxf(st.m_run[n], max16(lm));
+        const float alpha = __builtin_amdgcn_exp2f(st.m_run[n] - mn);
+        st.l_lane[n] *= alpha;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) st.acc[t][e] *= ah;
+        for (int e = 0; e < 4; ++e) {
+          const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), e));
+#pragma unroll
+          for (int t = 0; t < NT; ++t) st.acc[n][t][e] *= ah;
+        }
+        st.m_run[n] = mn;
       }
-      st.m_run = mn;
-    }
-    float pe[4];
+      float pe[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - st.m_run);
-    st.l_lane += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-    Mma::split(pe, phi, plo);
+      for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - st.m_run[n]);
+      st.l_lane[n] += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+      Mma::split(pe, phi[n], plo[n]);
+    }
   };
 
   // last: the quad may reach past the end of the range (only the range's last
   // quad can)
-  auto pv = [&](int qd, uint2 phi, uint2 plo, auto last) {
+  auto pv = [&](int qd, const uint2 (&phi)[NG], const uint2 (&plo)[NG], auto last) {
     const int qpos = (blk_begin + 4 * qd) * kBlockSize;
     if (decltype(last)::value && qpos + 4 * kBlockSize > tok_end && kCodes) {
       // as below, for 16 one-byte tokens per chunk: byte e of word w is
@@ -1065,8 +1077,11 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
           const uint4& v = vr[kb][(a >> 1) & 1][t];
           vv = (a & 1) ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
         }
-        st.acc[t] = Mma::template mma<a>(phi, vv, st.acc[t]);
-        st.acc[t] = Mma::template mma<a>(plo, vv, st.acc[t]);
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+          st.acc[n][t] = Mma::template mma<a>(phi[n], vv, st.acc[n][t]);
+          st.acc[n][t] = Mma::template mma<a>(plo[n], vv, st.acc[n][t]);
+        }
       }
     });
   };
@@ -1091,7 +1106,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   // keep the compiler from hoisting the loads above the matrix ops that still
   // read their destination registers (which would cost register copies).
   for (int qd = 0; qd + 1 < nquad; ++qd) {
-    uint2 phi, plo;
+    uint2 phi[NG], plo[NG];
     qk_softmax(qd, phi, plo);
     __builtin_amdgcn_sched_barrier(0);
     quad_phys(qd + 1, ph);
@@ -1104,7 +1119,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   }
   const bool at_table = with_new && new_at_table();
   if (at_table) substitute_k();
-  uint2 phi, plo;
+  uint2 phi[NG], plo[NG];
   qk_softmax(nquad - 1, phi, plo);
   if (with_new) {
     if (at_table) substitute_v();
@@ -1113,64 +1128,73 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   pv(nquad - 1, phi, plo, std::true_type{});
 }
 
-template <int D>
-__device__ __forceinline__ void reset_state4(WaveState4<D>& st) {
-  st.m_run = -INFINITY;
-  st.l_lane = 0.f;
+template <int D, int NG>
+__device__ __forceinline__ void reset_state4(WaveState4<D, NG>& st) {
+#pragma unroll
+  for (int n = 0; n < NG; ++n) {
+    st.m_run[n] = -INFINITY;
+    st.l_lane[n] = 0.f;
+  }
   st.bad = false;
 #pragma unroll
-  for (int t = 0; t < D / 64; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NG; ++n)
+#pragma unroll
+    for (int t = 0; t < D / 64; ++t) st.acc[n][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-template <int D>
+template <int D, int NG>
 __device__ __forceinline__ void emit_state4(const Params& pr, int b, int g, int slot,
-                                            WaveState4<D>& st) {
+                                            WaveState4<D, NG>& st) {
   constexpr int NT = D / 64;
   const int lane = threadIdx.x & 63;
   const int G = pr.G;
-  float l = sum16(st.l_lane);
-  float m = st.m_run;
-  if (st.bad) {
-    m = 0.f;
-    l = __builtin_nanf("");
 #pragma unroll
-    for (int t = 0; t < NT; ++t) st.acc[t] = f32x4_t{l, l, l, l};
-  }
+  for (int n = 0; n < NG; ++n) {
+    float l = sum16(st.l_lane[n]);
+    float m = st.m_run[n];
+    if (st.bad) {
+      m = 0.f;
+      l = __builtin_nanf("");
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (e < G) {
-      const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), e));
-      const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), e));
-      const int64_t row = static_cast<int64_t>(b) * pr.Hq + g * G + e;
-      const float inv = pr.out_scale / lh;
+      for (int t = 0; t < NT; ++t) st.acc[n][t] = f32x4_t{l, l, l, l};
+    }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int d = 64 * t + lane;
-        if (slot < 0)
-          pr.out[row * D + d] = st.acc[t][e] * inv;
-        else
-          pr.part_acc[(row * pr.maxP + slot) * D + d] = st.acc[t][e];
-      }
-      if (slot >= 0 && lane == 0) {
-        pr.part_m[row * pr.maxP + slot] = mh;
-        pr.part_l[row * pr.maxP + slot] = lh;
+    for (int e = 0; e < 4; ++e) {
+      if (4 * n + e < G) {
+        const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), e));
+        const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), e));
+        const int64_t row = static_cast<int64_t>(b) * pr.Hq + g * G + 4 * n + e;
+        const float inv = pr.out_scale / lh;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int d = 64 * t + lane;
+          if (slot < 0)
+            pr.out[row * D + d] = st.acc[n][t][e] * inv;
+          else
+            pr.part_acc[(row * pr.maxP + slot) * D + d] = st.acc[n][t][e];
+        }
+        if (slot >= 0 && lane == 0) {
+          pr.part_m[row * pr.maxP + slot] = mh;
+          pr.part_l[row * pr.maxP + slot] = lh;
+        }
       }
     }
   }
 }
 
-template <typename T, int D>
+// NG = 1: G <= 4; NG = 2: G = 5..8 (two head groups per K/V load).
+template <typename T, int D, int NG = 1>
 struct Engine4 {
-  using State = WaveState4<D>;
-  using Pre = Prologue4<D>;
+  using State = WaveState4<D, NG>;
+  using Pre = Prologue4<D, NG>;
   static constexpr int kUnitBlocks = 4;  // blocks per step (one quad)
   __device__ static void prologue(const Params& pr, int b, int g, int blk_begin, Pre& pre) {
-    prologue4<D>(pr, b, g, blk_begin, pre);
+    prologue4<D, NG>(pr, b, g, blk_begin, pre);
   }
   __device__ static void attend_rt(const Params& pr, int b, int g, int blk_begin, int nblk,
                                    int tok_begin, int tok_end, State& st, const Pre& pre,
                                    bool with_new) {
-    attend4<T, D>(pr, b, g, blk_begin, nblk, tok_begin, tok_end, st, pre, with_new);
+    attend4<T, D, NG>(pr, b, g, blk_begin, nblk, tok_begin, tok_end, st, pre, with_new);
   }
   __device__ static void reset(State& st) { reset_state4(st); }
   __device__ static void emit(const Params& pr, int b, int g, int slot, State& st) {
@@ -1548,8 +1572,9 @@ constexpr int kEvenSplit = -1;          // partition_size value selecting the ev
 
 bool partition_ok(int P) { return P == kEvenSplit || (P >= 0 && P % kBlockSize == 0); }
 
-// query heads per KV head the 4x4x4 engine takes (the only one for 8-bit pools)
-constexpr int kMaxGroupCodes = 4;
+// query heads per KV head the 4x4x4 engine takes (two groups of 4; the only
+// engine for 8-bit pools and for sliding windows on the matrix cores)
+constexpr int kMaxGroupCodes = 8;
 
 bool decode_args_ok(int B, int Hq, int Hkv, int D, int max_ctx, int P, pa_dtype dt) {
   return B >= 0 && B <= 65535 && Hkv > 0 && Hkv <= 65535 && Hq > 0 && Hq % Hkv == 0 &&
@@ -1594,10 +1619,11 @@ struct LaunchPlan {
 LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_env, int G) {
   LaunchPlan lp{};
   lp.generic = dt == PA_F32 || (generic_env && !code_dtype(dt));
-  // default (0) on the matrix-core path: the even split for G <= 4 (4x4x4
-  // engine); fixed partitions for G > 4, whose 16x16-engine split kernel
-  // spills (measured with 64/8 heads, D = 128: 131 us against 82 us)
-  lp.split = (partition_size == kEvenSplit || (partition_size == 0 && G <= 4)) && !lp.generic;
+  // default (0) on the matrix-core path: the even split for G <= 8 (4x4x4
+  // engine, one or two head groups); fixed partitions for G > 8, whose
+  // 16x16-engine split kernel spills (measured with 64/8 heads, D = 128, on
+  // that engine: 131 us against 82 us)
+  lp.split = (partition_size == kEvenSplit || (partition_size == 0 && G <= 8)) && !lp.generic;
   if (lp.split) {
     lp.W = split_waves();
     // a range of nblk blocks is cut into at most ceil(nblk / kMinChunkBlocks) + 1
@@ -1634,6 +1660,18 @@ void launch_attention(K kernel, dim3 grid, dim3 block, hipStream_t s, const Para
   }
 }
 
+// Fixed partitions on the 4x4x4 engine with NG head groups.
+// (two head groups: 2 waves per SIMD, whose 256 registers hold both
+// groups' state without spilling at D = 128)
+template <typename T, int D, int NG>
+void launch_fixed4(const Params& pr, bool fused, dim3 grid, hipStream_t s) {
+  constexpr int kWaves = NG == 1 ? kFixedWaves4 : 2;
+  if (fused)
+    launch_attention(decode_fixed_kernel<Engine4<T, D, NG>, true, kWaves>, grid, 64, s, pr);
+  else
+    launch_attention(decode_fixed_kernel<Engine4<T, D, NG>, false, kWaves>, grid, 64, s, pr);
+}
+
 template <typename T, int D>
 void launch_partitions(const Params& pr, bool generic, bool fused, hipStream_t s) {
   // matrix-core kernels: x = KV head + Hkv * partition (the heads of one
@@ -1641,10 +1679,10 @@ void launch_partitions(const Params& pr, bool generic, bool fused, hipStream_t s
   dim3 grid_m(pr.Hkv * pr.maxP, 1, pr.B);
   if (generic)
     launch_attention(decode_generic_kernel<T, D>, dim3(pr.maxP, pr.Hkv, pr.B), 256, s, pr);
-  else if (pr.G <= 4 && fused)
-    launch_attention(decode_fixed_kernel<Engine4<T, D>, true, kFixedWaves4>, grid_m, 64, s, pr);
   else if (pr.G <= 4)
-    launch_attention(decode_fixed_kernel<Engine4<T, D>, false, kFixedWaves4>, grid_m, 64, s, pr);
+    launch_fixed4<T, D, 1>(pr, fused, grid_m, s);
+  else if (pr.G <= 8)
+    launch_fixed4<T, D, 2>(pr, fused, grid_m, s);
   else
     launch_attention(decode_fixed_kernel<Engine16<T, D, kPairsInFlight, false>, false, 1>,
                      grid_m, 64, s, pr);
@@ -1664,6 +1702,9 @@ void launch_split(const Params& pr, int W, hipStream_t s) {
   if (pr.G <= 4)
     launch_attention(decode_split_kernel<Engine4<T, D>, 1>, W / kSplitWavesPerGroup,
                      64 * kSplitWavesPerGroup, s, pr);
+  else if (pr.G <= 8)
+    launch_attention(decode_split_kernel<Engine4<T, D, 2>, 1>, W / kSplitWavesPerGroup,
+                     64 * kSplitWavesPerGroup, s, pr);
   else
     launch_attention(decode_split_kernel<Engine16<T, D, kPairsInFlight, false>, 1>, W, 64, s,
                      pr);
@@ -1671,22 +1712,25 @@ void launch_split(const Params& pr, int W, hipStream_t s) {
 
 enum class Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
 
-// 8-bit pools (C = E4M3 or I8): the 4x4x4 engine only (G <= 4).
+// 8-bit pools (C = E4M3 or I8): the 4x4x4 engine only (G <= 8).
 template <typename C, int D>
 void launch_code_phases(const Params& pr, const LaunchPlan& lp, bool first, bool second,
                         hipStream_t s) {
   if (lp.split) {
-    if (first)
+    if (first && pr.G <= 4)
       launch_attention(decode_split_kernel<Engine4<C, D>, 1>, lp.W / kSplitWavesPerGroup,
+                       64 * kSplitWavesPerGroup, s, pr);
+    else if (first)
+      launch_attention(decode_split_kernel<Engine4<C, D, 2>, 1>, lp.W / kSplitWavesPerGroup,
                        64 * kSplitWavesPerGroup, s, pr);
     if (second) merge_kernel<D, true, C><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
     return;
   }
   const dim3 grid(pr.Hkv * pr.maxP, 1, pr.B);
-  if (first && pr.k_new != nullptr)
-    launch_attention(decode_fixed_kernel<Engine4<C, D>, true, kFixedWaves4>, grid, 64, s, pr);
+  if (first && pr.G <= 4)
+    launch_fixed4<C, D, 1>(pr, pr.k_new != nullptr, grid, s);
   else if (first)
-    launch_attention(decode_fixed_kernel<Engine4<C, D>, false, kFixedWaves4>, grid, 64, s, pr);
+    launch_fixed4<C, D, 2>(pr, pr.k_new != nullptr, grid, s);
   // with the step's new tokens the merge kernel always runs: it writes them
   if (second && (pr.maxP > 1 || pr.write_new_in_merge))
     merge_kernel<D, false, C><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
@@ -1721,7 +1765,7 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
 
 // Whether the partition kernel of this plan appends the step's new tokens
 // itself (pa_decode_step); otherwise pa_cache_append runs first.
-bool fuses_append(const LaunchPlan& lp, int G) { return !lp.generic && (lp.split || G <= 4); }
+bool fuses_append(const LaunchPlan& lp, int G) { return !lp.generic && (lp.split || G <= 8); }
 
 // Validates the arguments shared by pa_decode / pa_decode_partial /
 // pa_decode_merge and launches the requested phases.
@@ -1780,12 +1824,13 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window %d < 0", fn, window);
-  if (window > 0 && num_q_heads / num_kv_heads > 4 &&
+  if (window > 0 && num_q_heads / num_kv_heads > kMaxGroupCodes &&
       !make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric,
                  num_q_heads / num_kv_heads)
            .generic)
     return fail(PA_ERR_UNSUPPORTED,
-                "%s: a sliding window on the matrix cores needs <= 4 query heads per KV head", fn);
+                "%s: a sliding window on the matrix cores needs <= %d query heads per KV head",
+                fn, kMaxGroupCodes);
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);

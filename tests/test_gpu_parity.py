@@ -190,7 +190,10 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 511, 512, 513, 1023, 1024, 
     ("bf16", 16, 1, 64, 512),
     ("f16", 8, 8, 128, 512), ("f16", 16, 2, 64, 256), ("bf16", 4, 2, 64, 1024),
     ("f32", 4, 4, 64, 512), ("f32", 8, 2, 128, 0), ("bf16", 2, 2, 128, 4096),
-    ("bf16", 12, 4, 128, 256), ("f16", 6, 2, 64, -1)])
+    ("bf16", 12, 4, 128, 256), ("f16", 6, 2, 64, -1),
+    # 5..8 query heads per KV head: two head groups per K/V load
+    ("bf16", 64, 8, 128, -1), ("bf16", 64, 8, 128, 0), ("f16", 40, 8, 64, 0),
+    ("bf16", 12, 2, 128, 256), ("f16", 14, 2, 128, -1), ("bf16", 8, 1, 64, 16)])
 def test_edge_lengths_and_shapes(dtype, hq, hkv, d, ps, kernel):
     case = custom_case(31, dtype, EDGE_LENS, hq, hkv, d, partition_size=ps, boost_prob=0.02)
     say(f"[edge] {dtype} Hq={hq} Hkv={hkv} D={d} P={ps} kernel={kernel}")
@@ -201,12 +204,13 @@ def test_edge_lengths_and_shapes(dtype, hq, hkv, d, ps, kernel):
 
 @pytest.mark.parametrize("kernel", KERNELS, indirect=True)
 @pytest.mark.parametrize("ps", [256, -1])
-def test_bad_table_entry_and_length_give_nan_rows(kernel, ps):
+@pytest.mark.parametrize("hq", [8, 16])
+def test_bad_table_entry_and_length_give_nan_rows(kernel, ps, hq):
     """Out-of-range table entries and lengths are caught by the kernels' own
     bounds checks (no access outside the pools) and flagged with NaN rows."""
     pk = require_gpu()
-    case = custom_case(41, "bf16", [40, 300, 700, 20, 33], 8, 2, 128, partition_size=ps)
-    say(f"[errors] bad table entry / length kernel={kernel} P={ps}")
+    case = custom_case(41, "bf16", [40, 300, 700, 20, 33], hq, 2, 128, partition_size=ps)
+    say(f"[errors] bad table entry / length kernel={kernel} P={ps} Hq={hq}")
     got = run_gpu_step(case)
     cache, plan = got["cache"], got["plan"]
     tables = plan.d_tables.clone()
@@ -233,7 +237,8 @@ SPLIT_LENS = {
 
 @pytest.mark.parametrize("lens", list(SPLIT_LENS), ids=list(SPLIT_LENS))
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 16, 2, 64),
-                                            ("bf16", 16, 16, 128), ("f16", 24, 8, 128)])
+                                            ("bf16", 16, 16, 128), ("f16", 24, 8, 128),
+                                            ("bf16", 64, 8, 128), ("f16", 28, 4, 64)])
 def test_even_split_shapes(lens, dtype, hq, hkv, d):
     """The even split of the batch's work across waves (partition_size 0):
     ranges cut over many chunks, chunks holding many whole sequences."""
@@ -353,7 +358,8 @@ def test_timing_events_bracket_the_attention_kernel(ps):
     assert np.array_equal(out.cpu().numpy(), got["out"])
 
 
-@pytest.mark.parametrize("hq,hkv,ps", [(32, 8, 0), (32, 8, 256), (16, 2, -1), (8, 8, 64)])
+@pytest.mark.parametrize("hq,hkv,ps", [(32, 8, 0), (32, 8, 256), (16, 2, -1), (8, 8, 64),
+                                       (64, 8, -1), (48, 8, 256), (64, 8, 0)])
 def test_step_slot_cases_match_append_then_decode(hq, hkv, ps):
     """pa_decode_step == pa_cache_append then pa_decode for every slot value:
     the table's slot, -1 (no write; the position is attended as stored) and a

@@ -121,7 +121,8 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1023, 1025
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("hq,hkv,d,ps", [(32, 8, 128, 0), (16, 4, 64, 0), (8, 8, 128, 512),
-                                         (12, 4, 128, 16), (6, 3, 64, -1), (2, 1, 128, 256)])
+                                         (12, 4, 128, 16), (6, 3, 64, -1), (2, 1, 128, 256),
+                                         (64, 8, 128, 0), (40, 8, 64, 256), (14, 2, 128, -1)])
 def test_edge_lengths_and_shapes(fmt, hq, hkv, d, ps):
     case = quantized(custom_case(61, "bf16", EDGE_LENS, hq, hkv, d, partition_size=ps,
                                  boost_prob=0.02), fmt)
@@ -204,7 +205,8 @@ def test_full_size_llama3_8b_sampled(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("hq,hkv,ps", [(32, 8, 0), (32, 8, 256), (8, 2, -1), (8, 8, 64)])
+@pytest.mark.parametrize("hq,hkv,ps", [(32, 8, 0), (32, 8, 256), (8, 2, -1), (8, 8, 64),
+                                       (64, 8, 0), (48, 8, 256)])
 def test_step_slot_cases_match_append_then_decode(fmt, hq, hkv, ps):
     """pa_decode_step_quant (new tokens encoded inside the attention and merge
     kernels) == pa_cache_append_quant then pa_decode_quant, for the table's

@@ -299,7 +299,9 @@ def _parallel_sampling(name, seed, dtype, n_prompts, n_samples, prompt_len, tail
 
 
 def make_case(name: str, seed: int | None = None, device="cpu", **kw) -> Case:
-    """One of the five decode workloads at full size."""
+    """One of the five decode workloads at full size.  q_heads (Llama-3-8B
+    shape only): the number of query heads over the same 8 KV heads and
+    lengths (default 32)."""
     idx = CONFIG_NAMES.index(name) + 1
     seed = idx if seed is None else seed
     rng = np.random.default_rng(seed)
@@ -309,7 +311,8 @@ def make_case(name: str, seed: int | None = None, device="cpu", **kw) -> Case:
                             num_blocks=16, rng=rng)
     if name == "llama3_8b_bf16":
         lens = rng.integers(256, 2048 + 1, size=64)
-        return _independent(name, seed, "bf16", lens, 32, 8, 128, device, rng=rng)
+        return _independent(name, seed, "bf16", lens, kw.get("q_heads", 32), 8, 128, device,
+                            rng=rng)
     if name == "opt13b_fp16":
         z = rng.standard_normal(256)
         lens = np.clip(np.rint(600.0 * np.exp(0.9 * z)), 16, 2048).astype(np.int64)
