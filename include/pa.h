@@ -247,9 +247,8 @@ pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools, int3
 /* How pa_decode splits contexts for these arguments; partition_size is
  *   > 0 (a multiple of 16): fixed partitions of that many tokens;
  *   0: the library's choice: the even split on the matrix-core path
- *      (fp16/bf16 with at most 8 query heads per KV head, the 8-bit dtypes);
- *      fixed partitions of 256 tokens for more query heads per KV head
- *      (faster there), for fp32 and for the plain-FMA kernel;
+ *      (fp16/bf16 and the 8-bit dtypes); fixed partitions of 256 tokens for
+ *      fp32 and for the plain-FMA kernel;
  *   -1: the even split (matrix-core path only; fp32 and the plain-FMA kernel
  *       use 256-token partitions).
  * Returns the partition size in tokens for fixed partitions, 0 for the even
@@ -257,10 +256,9 @@ pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools, int3
  *   Fixed partitions: partition p of a sequence covers tokens
  *     [p*P, (p+1)*P); each is attended by one wave, merged when more than one.
  *   Even split: the batch's work, as (sequence, KV head, run of 4 blocks)
- *     units (2 blocks when more than 8 query heads share a KV head), is cut
- *     into equal contiguous chunks, one per wave of a grid of 4 waves per
- *     compute unit; a (sequence, head) cut into several chunks is merged the
- *     same way. */
+ *     units, is cut into equal contiguous chunks, one per wave of a grid of
+ *     4 waves per compute unit; a (sequence, head) cut into several chunks
+ *     is merged the same way. */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype);
@@ -333,10 +331,9 @@ pa_status pa_decode_merge(float* out, const void* q, const void* k_pool, const v
  * context_lens[b] - 1 is then attended with the pool's current content).  A
  * slot elsewhere in the pool gets the token written there, but then out is
  * only defined when that slot is not attended by the step.  On the
- * matrix-core path (fp16/bf16 with at most 8 query heads per KV head, or the
- * even split) the append is done inside the attention kernel, one launch
- * fewer; there a sequence whose length fails the bounds checks (NaN out
- * rows) or is 0 gets no pool write.  Otherwise the two kernels run back to
+ * matrix-core path (fp16/bf16 and the 8-bit dtypes) the append is done
+ * inside the attention kernel, one launch fewer; there a sequence whose
+ * length fails the bounds checks (NaN out rows) or is 0 gets no pool write.  Otherwise the two kernels run back to
  * back.  Copy-on-write copies of the step must be issued (pa_copy_blocks)
  * before this call on the same stream.
  *   pa_decode_step_partial / pa_decode_step_merge: the two phases of
@@ -413,7 +410,7 @@ pa_status pa_prefill(float* out, const void* q, const void* k_pool, const void* 
  * widened exactly to bf16 on the matrix cores; k_scale is folded into the
  * softmax scale (fp32 product scale * k_scale) and v_scale into the output.
  * Other arguments, the workspace and the bounds checks as for pa_decode.
- * Supported: block_size 16, head_dim 64 or 128, G = Hq/Hkv <= 8
+ * Supported: block_size 16, head_dim 64 or 128, G = Hq/Hkv <= 16
  * (PA_ERR_UNSUPPORTED otherwise); the 16-bit-only plain-FMA switch
  * (PA_DECODE_KERNEL) does not apply. */
 pa_status pa_decode_quant(float* out, const void* q, const void* k_pool, const void* v_pool,
@@ -457,9 +454,8 @@ pa_status pa_decode_step_quant(float* out, const void* q, void* k_pool, void* v_
  * lets blocks that left it be freed).  Fixed partitions count from the
  * partition holding the window's first position; the workspace is sized as
  * for pa_decode.  Other arguments, bounds checks and the step's slot rules
- * as for pa_decode / pa_decode_step.  Supported: fp32/fp16/bf16 pools; on
- * the matrix cores G = Hq/Hkv <= 8 (PA_ERR_UNSUPPORTED for more; the
- * plain-FMA kernel takes any G).  window < 0 is PA_ERR_INVALID_ARG. */
+ * as for pa_decode / pa_decode_step.  Supported: fp32/fp16/bf16 pools,
+ * G = Hq/Hkv <= 16.  window < 0 is PA_ERR_INVALID_ARG. */
 pa_status pa_decode_window(float* out, const void* q, const void* k_pool, const void* v_pool,
                            const int32_t* block_tables, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

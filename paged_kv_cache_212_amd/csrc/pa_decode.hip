@@ -17,12 +17,11 @@
 //     workgroup per compute unit);
 //   * decode_fixed_kernel: one wave per (KV head, fixed partition, sequence).
 // Engines (one wave attends one (b, g) range of blocks):
-//   * attend4 (fp16/bf16 and 8-bit codes, G <= 8): 4 blocks per step on the
-//     4x4x4 16-block MFMA with broadcast operands, one or two groups of 4
-//     query heads per K/V load;
-//   * attend_range (fp16/bf16, G <= 16): 2 blocks per step on 16x16x32 MFMAs.
-//   P.V takes P split into a high and a low half-precision part, so the
-//   weights keep ~16 (bf16) / ~22 (fp16) significant bits.
+//   * attend4 (fp16/bf16 and 8-bit codes, G <= 16): 4 blocks per step on the
+//     4x4x4 16-block MFMA with broadcast operands, ceil(G / 4) groups of 4
+//     query heads per K/V load.  P.V takes P split into a high and a low
+//     half-precision part, so the weights keep ~16 (bf16) / ~22 (fp16)
+//     significant bits.
 //   * decode_generic_kernel (any dtype, fp32 pools): plain fp32 FMAs.
 // Scores are kept in the log2 domain (scale * log2(e) folded in) and
 // exponentiated with exp2.
@@ -213,358 +212,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(Params pr) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core partition kernel.
-// ---------------------------------------------------------------------------
-// Two blocks (A = block 2q, B = block 2q+1 of the range) per iteration.
-// Lane = 16*j + n (n = lane % 16, j = lane / 16).
-//   QK, half hh in {0,1}: S^T (16 rows x 16 heads) = K rows . Q^T where row r
-//     is token 8*((r/4)%2) + 4*hh + r%4 of block r/8 (A for r < 8, else B).
-//     A operand (K): lane reads row n, dims kk*32 + 8j .. +8 (16 bytes).
-//     B operand (Q): head n, dims kk*32 + 8j .. +8.
-//     Result: lane (head n, j) holds rows 4j+e, i.e. block j/2, tokens
-//     8*(j%2) + 4*hh + e (e = 0..3).
-//   PV: O (16 heads x 16 dims) += P (heads x 32 tokens) . V (32 tokens x dims)
-//     with lane (n, j) holding k-slots {S_hh0[e], S_hh1[e]}: tokens
-//     8*(j%2) + 0..7 of block j/2, in order.  The V tile stores each dim's 8
-//     tokens of a half block as 16 contiguous bytes (half h, dim d at byte
-//     (h*D + d)*16): one 16-byte load per lane and 16-dim tile.
-//   O result: lane (dim t*16 + n, j) holds heads 4j + e.
-// K tile (block, head) bytes: [D/8 chunks][16 tokens][8 dims] -> chunk
-// kk*4 + j, token r at (kk*4 + j)*256 + 16*r.
-
-// Online-softmax state of one wave for one (sequence, KV head) range.
-template <int D>
-struct WaveState {
-  float m_run;          // running max of lane's head n (log2 domain)
-  float l_lane;         // this lane's share of the running sum for head n
-  f32x4_t acc[D / 16];  // O rows 4j+e, dims t*16+n
-  bool bad;             // a table entry of the range was out of the pool
-};
-
-// Attends over blocks [blk_begin, blk_begin + nblk) of sequence b, KV head g,
-// masking positions >= tok_end, and accumulates into st.  NPAIR block pairs
-// are kept in flight in a register ring; the loop is peeled so the steady
-// state issues its loads unconditionally (static wait counts) and the tail
-// issues none.
-// with_new: the range ends at the sequence's last position, which holds the
-// step's new token: its K/V are taken from k_new/v_new (substituted in the
-// registers of the last pair) and written into the pool slot.
-template <typename T, int D, int NPAIR, bool kSmallGroup, bool with_new>
-__device__ __forceinline__ void attend_range(const Params& pr, int b, int g, int blk_begin,
-                                             int nblk, int tok_end, WaveState<D>& st) {
-  constexpr int NKK = D / 32;
-  constexpr int NTL = D / 16;
-  constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, j = lane >> 4;
-  const int G = pr.G;
-  const int npair = (nblk + 1) >> 1;
-
-  // Q operand in LDS, in lane order (lane reads back its own 16 bytes per kk):
-  // keeps 16 registers free for the prefetch ring.
-  __shared__ uint4 s_q[NKK][64];
-  {
-    const uint16_t* qb = static_cast<const uint16_t*>(pr.q) +
-                         (static_cast<int64_t>(b) * pr.Hq + g * G + n) * D;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      s_q[kk][lane] = n < G ? *reinterpret_cast<const uint4*>(qb + kk * 32 + j * 8)
-                            : make_uint4(0, 0, 0, 0);
-  }
-
-  const char* kbase = static_cast<const char*>(pr.kpool) + g * kTileBytes;
-  const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
-  const int64_t block_stride = static_cast<int64_t>(pr.Hkv) * kTileBytes;
-  const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks + blk_begin;
-
-  // Table entries, 64 per register (lane i holds entry 64*c + i of chunk c).
-  auto load_chunk = [&](int c) -> int {
-    const int k = c * 64 + lane;
-    const int e = k < nblk ? trow[k] : 0;
-    const bool lane_bad = k < nblk && (e < 0 || e >= pr.num_blocks);
-    if (__any(lane_bad)) st.bad = true;
-    return lane_bad ? 0 : e;
-  };
-  int chunk = 0;
-  int tcur = load_chunk(0);
-  int tnext = nblk > 64 ? load_chunk(1) : 0;
-  // Physical block of range block k (k increases across calls); k >= nblk
-  // (the missing half of a last, odd pair) maps to block nblk-1, whose lines
-  // the same instruction fetches anyway.
-  auto phys_of = [&](int k) -> int {
-    if (k >= nblk) k = nblk - 1;
-    const int c = k >> 6;
-    if (c != chunk) {
-      chunk = c;
-      tcur = tnext;
-      tnext = (c + 1) * 64 < nblk ? load_chunk(c + 1) : 0;
-    }
-    return __builtin_amdgcn_readlane(tcur, k & 63);
-  };
-
-  uint4 kb[NPAIR][2][NKK];
-  uint4 vb[NPAIR][NTL];
-  auto issue = [&](int u, int q) {
-    const int pa = phys_of(2 * q), pb = phys_of(2 * q + 1);
-    const char* kt = kbase + ((n < 8) ? pa : pb) * block_stride + (n & 3) * 16 +
-                     ((n >> 2) & 1) * 128 + j * 256;
-    const char* vt = vbase + ((j >> 1) ? pb : pa) * block_stride + ((j & 1) * D + n) * 16;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        kb[u][hh][kk] = load_stream(kt + kk * 1024 + hh * 64);
-#pragma unroll
-    for (int t = 0; t < NTL; ++t) vb[u][t] = load_stream(vt + t * 256);
-  };
-
-  // The new token sits at position tok_end - 1, in the range's last pair:
-  // half `sel` (block A or B of the pair), in-block token tn.  Its K/V rows
-  // are staged in LDS at the start of the range, so the substitution into the
-  // last pair's registers costs no global round trip.
-  __shared__ uint32_t s_new[2][D / 2];   // [K|V][D bf16/fp16 values, 2 per word]
-  const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
-  uint32_t stage_k = 0, stage_v = 0;
-  if (with_new && lane < D / 2) {
-    stage_k = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.k_new) + nrow)[lane];
-    stage_v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pr.v_new) + nrow)[lane];
-  }
-  // Appends the new token with the effect of pa_cache_append then the
-  // attention over the pool: the token is written to its slot (skipped when
-  // out of the pool), and it replaces the loaded values of position
-  // tok_end - 1 only when the slot is the table's slot of that position.
-  auto substitute_new = [&](int u) {
-    const int pos = tok_end - 1;
-    const int sel = pos / kBlockSize - blk_begin - 2 * (npair - 1);
-    const int tn = pos % kBlockSize;
-    const uint16_t* kn = reinterpret_cast<const uint16_t*>(s_new[0]);
-    const uint16_t* vn = reinterpret_cast<const uint16_t*>(s_new[1]);
-    const int64_t slot = pr.slots[b];
-    const bool in_pool = slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize;
-    const bool at_table =
-        in_pool && slot == static_cast<int64_t>(phys_of(2 * (npair - 1) + sel)) * kBlockSize + tn;
-    // K: lane row n holds token 8*((n >> 2) & 1) + 4*hh + (n & 3) of block n >> 3
-    if (at_table && (n >> 3) == sel && (n & 3) == (tn & 3) && ((n >> 2) & 1) == (tn >> 3)) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        if (hh == ((tn >> 2) & 1)) {
-#pragma unroll
-          for (int kk = 0; kk < NKK; ++kk)
-            kb[u][hh][kk] = *reinterpret_cast<const uint4*>(kn + kk * 32 + j * 8);
-        }
-    }
-    // V: lane group j holds block j >> 1, tokens 8*(j & 1) + e as element e
-    if (at_table && (j >> 1) == sel && (j & 1) == (tn >> 3)) {
-      const int e = tn & 7;
-      const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      const int sh = (e & 1) * 16, dw = e >> 1;
-#pragma unroll
-      for (int t = 0; t < NTL; ++t) {
-        const uint32_t val = static_cast<uint32_t>(vn[t * 16 + n]) << sh;
-        uint4& vv = vb[u][t];
-        vv.x = dw == 0 ? ((vv.x & keep) | val) : vv.x;
-        vv.y = dw == 1 ? ((vv.y & keep) | val) : vv.y;
-        vv.z = dw == 2 ? ((vv.z & keep) | val) : vv.z;
-        vv.w = dw == 3 ? ((vv.w & keep) | val) : vv.w;
-      }
-    }
-    // write the token into its pool slot (or leave it to the merge kernel)
-    if (in_pool && !pr.write_new_in_merge) {
-      const int64_t blk = slot / kBlockSize;
-      const int ts = static_cast<int>(slot % kBlockSize);
-      uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
-      uint16_t* vt = static_cast<uint16_t*>(pr.vpool_w) + tile_base(blk, g, pr.Hkv, D);
-      if (lane < D / 8)
-        *reinterpret_cast<uint4*>(kt + (lane * kBlockSize + ts) * 8) =
-            *reinterpret_cast<const uint4*>(kn + lane * 8);
-#pragma unroll
-      for (int d = lane; d < D; d += 64) vt[((ts >> 3) * D + d) * 8 + (ts & 7)] = vn[d];
-    }
-  };
-
-  auto compute = [&](int u, int q) {
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const uint4 qkk = s_q[kk][lane];
-      s0 = Mfma<T>::qk(kb[u][0][kk], qkk, s0);
-      s1 = Mfma<T>::qk(kb[u][1][kk], qkk, s1);
-    }
-    // sequence position of S_hh[e]: base + 4*hh + e
-    const int base = (blk_begin + 2 * q + (j >> 1)) * kBlockSize + 8 * (j & 1);
-    float sv[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = (base + e < tok_end) ? s0[e] * pr.scale_log2 : -INFINITY;
-      sv[4 + e] = (base + 4 + e < tok_end) ? s1[e] * pr.scale_log2 : -INFINITY;
-    }
-    float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(st.m_run, bm);
-    if (__any(mn != st.m_run)) {
-      // running max moved for some head: rescale rows 4j+e by 2^(m_old - m_new)
-      const float alpha = __builtin_amdgcn_exp2f(st.m_run - mn);
-      st.l_lane *= alpha;
-      if constexpr (kSmallGroup) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), e));
-#pragma unroll
-          for (int t = 0; t < NTL; ++t) st.acc[t][e] *= ah;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ah = __shfl(alpha, 4 * j + e);
-#pragma unroll
-          for (int t = 0; t < NTL; ++t) st.acc[t][e] *= ah;
-        }
-      }
-      st.m_run = mn;
-    }
-    float pe[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(sv[e] - mn);
-    st.l_lane += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-    uint4 phi, plo;
-    Mfma<T>::split8(pe, phi, plo);
-    if ((blk_begin + 2 * q + 2) * kBlockSize > tok_end) {
-      // the pair reaches past the end of the range: zero V of masked
-      // positions so unused slots (even NaN) cannot reach the output via 0*v
-      const uint32_t mx = (base + 0 < tok_end ? 0x0000FFFFu : 0u) | (base + 1 < tok_end ? 0xFFFF0000u : 0u);
-      const uint32_t my = (base + 2 < tok_end ? 0x0000FFFFu : 0u) | (base + 3 < tok_end ? 0xFFFF0000u : 0u);
-      const uint32_t mz = (base + 4 < tok_end ? 0x0000FFFFu : 0u) | (base + 5 < tok_end ? 0xFFFF0000u : 0u);
-      const uint32_t mw = (base + 6 < tok_end ? 0x0000FFFFu : 0u) | (base + 7 < tok_end ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int t = 0; t < NTL; ++t) {
-        vb[u][t].x &= mx;
-        vb[u][t].y &= my;
-        vb[u][t].z &= mz;
-        vb[u][t].w &= mw;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NTL; ++t) {
-      st.acc[t] = Mfma<T>::pv8(phi, vb[u][t], st.acc[t]);
-      st.acc[t] = Mfma<T>::pv8(plo, vb[u][t], st.acc[t]);
-    }
-  };
-
-  // prologue: first min(NPAIR, npair) pairs in flight
-#pragma unroll
-  for (int u = 0; u < NPAIR; ++u)
-    if (u < npair) issue(u, u);
-  if constexpr (with_new) {
-    if (lane < D / 2) {
-      s_new[0][lane] = stage_k;
-      s_new[1][lane] = stage_v;
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-  int q0 = 0;
-  for (; q0 + 2 * NPAIR <= npair; q0 += NPAIR) {
-#pragma unroll
-    for (int u = 0; u < NPAIR; ++u) {
-      compute(u, q0 + u);
-      issue(u, q0 + u + NPAIR);
-    }
-  }
-  // tail: at most 2*NPAIR - 1 pairs left, the first min(NPAIR, left) in
-  // flight; the range's last pair is among them
-#pragma unroll
-  for (int u = 0; u < NPAIR; ++u) {
-    if (q0 + u < npair) {
-      if (with_new && q0 + u == npair - 1) substitute_new(u);
-      compute(u, q0 + u);
-      if (q0 + u + NPAIR < npair) issue(u, q0 + u + NPAIR);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < NPAIR; ++u)
-    if (q0 + NPAIR + u < npair) {
-      if (with_new && q0 + NPAIR + u == npair - 1) substitute_new(u);
-      compute(u, q0 + NPAIR + u);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void reset_state(WaveState<D>& st) {
-  st.m_run = -INFINITY;
-  st.l_lane = 0.f;
-  st.bad = false;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-}
-
-// Writes the wave's result for (b, g): the normalised output rows when the
-// range covered the whole sequence (slot < 0), else the partial
-// (max, sum, weighted V) into slot `slot` of the workspace rows.
-template <int D>
-__device__ __forceinline__ void emit_state(const Params& pr, int b, int g, int slot,
-                                           WaveState<D>& st) {
-  constexpr int NTL = D / 16;
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, j = lane >> 4;
-  const int G = pr.G;
-  float l = st.l_lane;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  float m = st.m_run;
-  if (st.bad) {
-    m = 0.f;
-    l = __builtin_nanf("");
-#pragma unroll
-    for (int t = 0; t < NTL; ++t) st.acc[t] = f32x4_t{l, l, l, l};
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int h = 4 * j + e;
-    const float mh = __shfl(m, h);
-    const float lh = __shfl(l, h);
-    if (h < G) {
-      const int64_t row = static_cast<int64_t>(b) * pr.Hq + g * G + h;
-      const float inv = 1.0f / lh;
-#pragma unroll
-      for (int t = 0; t < NTL; ++t) {
-        const int d = t * 16 + n;
-        if (slot < 0)
-          pr.out[row * D + d] = st.acc[t][e] * inv;
-        else
-          pr.part_acc[(row * pr.maxP + slot) * D + d] = st.acc[t][e];
-      }
-      if (slot >= 0 && n == 0) {
-        pr.part_m[row * pr.maxP + slot] = mh;
-        pr.part_l[row * pr.maxP + slot] = lh;
-      }
-    }
-  }
-}
-
-// The 16x16 engine as a policy for the wave kernels below.
-template <typename T, int D, int NPAIR, bool kSmallGroup>
-struct Engine16 {
-  using State = WaveState<D>;
-  struct Pre {};
-  static constexpr int kUnitBlocks = 2;  // blocks per step (one pair)
-  __device__ static void prologue(const Params&, int, int, int, Pre&) {}
-  // no sliding window here (the host rejects a window for this engine)
-  __device__ static void attend_rt(const Params& pr, int b, int g, int blk_begin, int nblk, int,
-                                   int tok_end, State& st, const Pre&, bool with_new) {
-    if (with_new)
-      attend_range<T, D, NPAIR, kSmallGroup, true>(pr, b, g, blk_begin, nblk, tok_end, st);
-    else
-      attend_range<T, D, NPAIR, kSmallGroup, false>(pr, b, g, blk_begin, nblk, tok_end, st);
-  }
-  __device__ static void reset(State& st) { reset_state(st); }
-  __device__ static void emit(const Params& pr, int b, int g, int slot, State& st) {
-    emit_state(pr, b, g, slot, st);
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Matrix-core engine for G <= 4 (one head group; G <= 8 with two) on the 4x4x4 16-block MFMA
+// Matrix-core engine on the 4x4x4 16-block MFMA: NG groups of 4 query heads
+// (G <= 4 * NG) per K/V load
 // (v_mfma_f32_4x4x4_16b: sixteen independent 4x4x4 products per instruction,
 // block k on lanes 4k..4k+3; with CBSZ=4 / ABID=a every block uses the A
 // operand of block a).
@@ -713,8 +362,8 @@ __device__ __forceinline__ float sum16(float v) {
   return v + __shfl_xor(v, 32);
 }
 
-// NG groups of 4 query heads share each K/V load (NG = 2: G = 5..8); group
-// n holds heads 4n .. 4n+3 of the KV head's G.
+// NG groups of 4 query heads share each K/V load (G <= 4 * NG); group n
+// holds heads 4n .. 4n+3 of the KV head's G.
 template <int D, int NG = 1>
 struct WaveState4 {
   float m_run[NG];           // running max (log2 domain) of head 4n + lane%4
@@ -1182,7 +831,7 @@ __device__ __forceinline__ void emit_state4(const Params& pr, int b, int g, int 
   }
 }
 
-// NG = 1: G <= 4; NG = 2: G = 5..8 (two head groups per K/V load).
+// NG head groups per K/V load: G <= 4 * NG.
 template <typename T, int D, int NG = 1>
 struct Engine4 {
   using State = WaveState4<D, NG>;
@@ -1322,9 +971,9 @@ __device__ __forceinline__ int len_of(const Params& pr, int lens_reg, int b) {
   return pr.B <= 64 ? __builtin_amdgcn_readlane(lens_reg, b) : pr.lens[b];
 }
 
-// Workgroups of one wave (16x16 engine) or of kSplitWavesPerGroup waves (one
-// per SIMD of a compute unit: 4x as few workgroups to dispatch, measured
-// 1.5 us faster on the Llama-3-8B step); wave w of W takes chunk w.
+// Workgroups of kSplitWavesPerGroup waves (one per SIMD of a compute unit:
+// 4x as few workgroups to dispatch as one-wave workgroups, measured 1.5 us
+// faster on the Llama-3-8B step); wave w of W takes chunk w.
 template <typename Eng, int kWaves>
 __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
   constexpr int U = Eng::kUnitBlocks;
@@ -1563,7 +1212,6 @@ Path path_from_env() {
 }
 
 constexpr int kDefaultPartition = 256;  // fixed-partition size of the plain-FMA kernel
-constexpr int kPairsInFlight = 2;
 constexpr int kFixedWaves4 = 3;         // waves per SIMD the 4x4x4 fixed kernel is built for
 constexpr int kSplitWavesPerCU = 4;     // balanced split: grid = CUs * this (one wave per SIMD)
 constexpr int kSplitWavesPerGroup = 4;  // waves per workgroup of the 4x4x4 split kernel
@@ -1572,13 +1220,9 @@ constexpr int kEvenSplit = -1;          // partition_size value selecting the ev
 
 bool partition_ok(int P) { return P == kEvenSplit || (P >= 0 && P % kBlockSize == 0); }
 
-// query heads per KV head the 4x4x4 engine takes (two groups of 4; the only
-// engine for 8-bit pools and for sliding windows on the matrix cores)
-constexpr int kMaxGroupCodes = 8;
-
 bool decode_args_ok(int B, int Hq, int Hkv, int D, int max_ctx, int P, pa_dtype dt) {
   return B >= 0 && B <= 65535 && Hkv > 0 && Hkv <= 65535 && Hq > 0 && Hq % Hkv == 0 &&
-         Hq / Hkv <= (code_dtype(dt) ? kMaxGroupCodes : kMaxGroup) && (D == 64 || D == 128) &&
+         Hq / Hkv <= kMaxGroup && (D == 64 || D == 128) &&
          max_ctx >= 0 && partition_ok(P) && pool_dtype_ok(dt);
 }
 
@@ -1615,15 +1259,11 @@ struct LaunchPlan {
   int W;
 };
 
-// G: query heads per KV head.
-LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_env, int G) {
+LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_env) {
   LaunchPlan lp{};
   lp.generic = dt == PA_F32 || (generic_env && !code_dtype(dt));
-  // default (0) on the matrix-core path: the even split for G <= 8 (4x4x4
-  // engine, one or two head groups); fixed partitions for G > 8, whose
-  // 16x16-engine split kernel spills (measured with 64/8 heads, D = 128, on
-  // that engine: 131 us against 82 us)
-  lp.split = (partition_size == kEvenSplit || (partition_size == 0 && G <= 8)) && !lp.generic;
+  // default (0) on the matrix-core path: the even split
+  lp.split = (partition_size == kEvenSplit || partition_size == 0) && !lp.generic;
   if (lp.split) {
     lp.W = split_waves();
     // a range of nblk blocks is cut into at most ceil(nblk / kMinChunkBlocks) + 1
@@ -1662,30 +1302,53 @@ void launch_attention(K kernel, dim3 grid, dim3 block, hipStream_t s, const Para
 
 // Fixed partitions on the 4x4x4 engine with NG head groups.
 // (two head groups: 2 waves per SIMD, whose 256 registers hold both
-// groups' state without spilling at D = 128)
+// groups' state without spilling at D = 128; three or four: 1 wave per SIMD)
 template <typename T, int D, int NG>
-void launch_fixed4(const Params& pr, bool fused, dim3 grid, hipStream_t s) {
-  constexpr int kWaves = NG == 1 ? kFixedWaves4 : 2;
+void launch_fixed4(const Params& pr, bool fused, hipStream_t s) {
+  constexpr int kWaves = NG == 1 ? kFixedWaves4 : NG == 2 ? 2 : 1;
+  // x = KV head + Hkv * partition (the heads of one partition are dispatched
+  // together), z = sequence
+  const dim3 grid(pr.Hkv * pr.maxP, 1, pr.B);
   if (fused)
     launch_attention(decode_fixed_kernel<Engine4<T, D, NG>, true, kWaves>, grid, 64, s, pr);
   else
     launch_attention(decode_fixed_kernel<Engine4<T, D, NG>, false, kWaves>, grid, 64, s, pr);
 }
 
+// The even split over W waves on the 4x4x4 engine with NG head groups.
+template <typename T, int D, int NG>
+void launch_split4(const Params& pr, int W, hipStream_t s) {
+  launch_attention(decode_split_kernel<Engine4<T, D, NG>, 1>, W / kSplitWavesPerGroup,
+                   64 * kSplitWavesPerGroup, s, pr);
+}
+
+// The matrix-core attention kernel for G = Hq / Hkv <= kMaxGroup: ceil(G / 4)
+// head groups, on the even split (split) or fixed partitions (fused: the
+// kernel appends the step's new tokens).
+template <typename T, int D, int NG>
+void launch_matrix_ng(const Params& pr, bool split, int W, bool fused, hipStream_t s) {
+  if (split)
+    launch_split4<T, D, NG>(pr, W, s);
+  else
+    launch_fixed4<T, D, NG>(pr, fused, s);
+}
+template <typename T, int D>
+void launch_matrix(const Params& pr, bool split, int W, bool fused, hipStream_t s) {
+  static_assert(kMaxGroup == 16, "head groups 1..4 cover G <= 16");
+  switch ((pr.G + 3) / 4) {
+    case 1: launch_matrix_ng<T, D, 1>(pr, split, W, fused, s); break;
+    case 2: launch_matrix_ng<T, D, 2>(pr, split, W, fused, s); break;
+    case 3: launch_matrix_ng<T, D, 3>(pr, split, W, fused, s); break;
+    default: launch_matrix_ng<T, D, 4>(pr, split, W, fused, s); break;
+  }
+}
+
 template <typename T, int D>
 void launch_partitions(const Params& pr, bool generic, bool fused, hipStream_t s) {
-  // matrix-core kernels: x = KV head + Hkv * partition (the heads of one
-  // partition are dispatched together), z = sequence
-  dim3 grid_m(pr.Hkv * pr.maxP, 1, pr.B);
   if (generic)
     launch_attention(decode_generic_kernel<T, D>, dim3(pr.maxP, pr.Hkv, pr.B), 256, s, pr);
-  else if (pr.G <= 4)
-    launch_fixed4<T, D, 1>(pr, fused, grid_m, s);
-  else if (pr.G <= 8)
-    launch_fixed4<T, D, 2>(pr, fused, grid_m, s);
   else
-    launch_attention(decode_fixed_kernel<Engine16<T, D, kPairsInFlight, false>, false, 1>,
-                     grid_m, 64, s, pr);
+    launch_matrix<T, D>(pr, false, 0, fused, s);
 }
 
 template <>
@@ -1697,40 +1360,17 @@ void launch_partitions<F32, 128>(const Params& pr, bool, bool, hipStream_t s) {
   launch_attention(decode_generic_kernel<F32, 128>, dim3(pr.maxP, pr.Hkv, pr.B), 256, s, pr);
 }
 
-template <typename T, int D>
-void launch_split(const Params& pr, int W, hipStream_t s) {
-  if (pr.G <= 4)
-    launch_attention(decode_split_kernel<Engine4<T, D>, 1>, W / kSplitWavesPerGroup,
-                     64 * kSplitWavesPerGroup, s, pr);
-  else if (pr.G <= 8)
-    launch_attention(decode_split_kernel<Engine4<T, D, 2>, 1>, W / kSplitWavesPerGroup,
-                     64 * kSplitWavesPerGroup, s, pr);
-  else
-    launch_attention(decode_split_kernel<Engine16<T, D, kPairsInFlight, false>, 1>, W, 64, s,
-                     pr);
-}
-
 enum class Phase { kPartitions = 1, kMerge = 2, kBoth = 3 };
 
-// 8-bit pools (C = E4M3 or I8): the 4x4x4 engine only (G <= 8).
+// 8-bit pools (C = E4M3 or I8): the 4x4x4 engine.
 template <typename C, int D>
 void launch_code_phases(const Params& pr, const LaunchPlan& lp, bool first, bool second,
                         hipStream_t s) {
+  if (first) launch_matrix<C, D>(pr, lp.split, lp.W, pr.k_new != nullptr, s);
   if (lp.split) {
-    if (first && pr.G <= 4)
-      launch_attention(decode_split_kernel<Engine4<C, D>, 1>, lp.W / kSplitWavesPerGroup,
-                       64 * kSplitWavesPerGroup, s, pr);
-    else if (first)
-      launch_attention(decode_split_kernel<Engine4<C, D, 2>, 1>, lp.W / kSplitWavesPerGroup,
-                       64 * kSplitWavesPerGroup, s, pr);
     if (second) merge_kernel<D, true, C><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
     return;
   }
-  const dim3 grid(pr.Hkv * pr.maxP, 1, pr.B);
-  if (first && pr.G <= 4)
-    launch_fixed4<C, D, 1>(pr, pr.k_new != nullptr, grid, s);
-  else if (first)
-    launch_fixed4<C, D, 2>(pr, pr.k_new != nullptr, grid, s);
   // with the step's new tokens the merge kernel always runs: it writes them
   if (second && (pr.maxP > 1 || pr.write_new_in_merge))
     merge_kernel<D, false, C><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
@@ -1746,9 +1386,9 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
   if (lp.split) {
     if (first) {
       if (dt == PA_F16)
-        launch_split<F16, D>(pr, lp.W, s);
+        launch_matrix<F16, D>(pr, true, lp.W, false, s);
       else
-        launch_split<BF16, D>(pr, lp.W, s);
+        launch_matrix<BF16, D>(pr, true, lp.W, false, s);
     }
     if (second) merge_kernel<D, true><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
     return;
@@ -1765,7 +1405,7 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
 
 // Whether the partition kernel of this plan appends the step's new tokens
 // itself (pa_decode_step); otherwise pa_cache_append runs first.
-bool fuses_append(const LaunchPlan& lp, int G) { return !lp.generic && (lp.split || G <= 8); }
+bool fuses_append(const LaunchPlan& lp) { return !lp.generic; }
 
 // Validates the arguments shared by pa_decode / pa_decode_partial /
 // pa_decode_merge and launches the requested phases.
@@ -1802,10 +1442,6 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   if (cs != nullptr && (!(cs->k_scale > 0.f) || !(cs->v_scale > 0.f) ||
                         !std::isfinite(cs->k_scale) || !std::isfinite(cs->v_scale)))
     return fail(PA_ERR_INVALID_ARG, "%s: scales must be positive and finite", fn);
-  if (cs != nullptr && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
-      num_q_heads / num_kv_heads > kMaxGroupCodes)
-    return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (max %d for 8-bit pools)",
-                fn, num_q_heads / num_kv_heads, kMaxGroupCodes);
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", fn, head_dim);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -1824,13 +1460,6 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window %d < 0", fn, window);
-  if (window > 0 && num_q_heads / num_kv_heads > kMaxGroupCodes &&
-      !make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric,
-                 num_q_heads / num_kv_heads)
-           .generic)
-    return fail(PA_ERR_UNSUPPORTED,
-                "%s: a sliding window on the matrix cores needs <= %d query heads per KV head",
-                fn, kMaxGroupCodes);
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
@@ -1843,7 +1472,7 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   if (nt && ((reinterpret_cast<uintptr_t>(nt->k_new) | reinterpret_cast<uintptr_t>(nt->v_new)) & 15))
     return fail(PA_ERR_INVALID_ARG, "%s: k_new and v_new must be 16-byte aligned", fn);
   const LaunchPlan lp = make_plan(max_context_len, partition_size, dtype,
-                                  path_from_env() == Path::kGeneric, num_q_heads / num_kv_heads);
+                                  path_from_env() == Path::kGeneric);
   const size_t need = workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
   if (need > 0 && (!workspace || workspace_bytes_given < need))
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -1884,7 +1513,7 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (nt) {
-    if (fuses_append(lp, pr.G)) {
+    if (fuses_append(lp)) {
       // append fused: the attention kernel uses the new tokens; the merge
       // kernel writes them to the pool when a merge kernel runs, else the
       // attention kernel does
@@ -1938,8 +1567,7 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_head
   if (!decode_args_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                       partition_size, dtype))
     return -1;
-  return make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric,
-                   num_q_heads / num_kv_heads)
+  return make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric)
       .P;
 }
 
@@ -1951,8 +1579,7 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
                       partition_size, dtype))
     return 0;
   const LaunchPlan lp =
-      make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric,
-                num_q_heads / num_kv_heads);
+      make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric);
   return workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
 }
 

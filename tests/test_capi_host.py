@@ -87,7 +87,8 @@ def test_quantized_cache_calls_reject_bad_arguments_without_launching():
         return fn(nul, nul, nul, nul, nul, nul, 1, hq, hkv, 128, 16, 10, 4, 64, 0.1, 0, dt, ks,
                   vs, nul, 0, nul)
     assert dq(dt=PA_BF16) == PA_ERR_INVALID_ARG          # not an 8-bit pool
-    assert dq(hq=32) == PA_ERR_UNSUPPORTED                # G = 16 > 8
+    assert dq(hq=34) == PA_ERR_UNSUPPORTED                # G = 17 > 16
+    assert dq(hq=32) == PA_ERR_INVALID_ARG                # G = 16: NULL pointers
     assert dq(ks=0.0) == PA_ERR_INVALID_ARG
     assert dq(vs=float("inf")) == PA_ERR_INVALID_ARG
     assert dq() == PA_ERR_INVALID_ARG                     # valid scalars, NULL pointers
@@ -112,11 +113,11 @@ def test_quantized_cache_calls_reject_bad_arguments_without_launching():
     # byte moves accept the 8-bit dtypes
     assert h.pa_cache_append(nul, nul, nul, nul, nul, 0, 10, 8, 128, 16, PA_INT8, nul) == 0
     assert h.pa_copy_blocks(nul, nul, nul, 0, 10, 8, 128, 16, PA_FP8_E4M3, nul) == 0
-    # queries: the even split by default; G > 8 invalid for 8-bit pools
+    # queries: the even split by default; G > 16 invalid
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_FP8_E4M3) == 0
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 512, PA_INT8) == 512
-    assert h.pa_decode_partition_size(64, 64, 8, 128, 2048, 0, PA_INT8) == 0
-    assert h.pa_decode_partition_size(64, 128, 8, 128, 2048, 0, PA_INT8) == -1
+    assert h.pa_decode_partition_size(64, 128, 8, 128, 2048, 0, PA_INT8) == 0
+    assert h.pa_decode_partition_size(64, 136, 8, 128, 2048, 0, PA_INT8) == -1
     assert h.pa_decode_workspace_bytes(64, 32, 8, 128, 2048, 0, PA_INT8) == \
         h.pa_decode_workspace_bytes(64, 32, 8, 128, 2048, 0, PA_BF16)
 
@@ -129,7 +130,8 @@ def test_window_calls_reject_bad_arguments_without_launching():
         return h.pa_decode_window(nul, nul, nul, nul, nul, nul, 1, hq, hkv, 128, 16, 10, 4, 64,
                                   0.1, window, 0, dt, nul, 0, nul)
     assert dw(window=-1) == PA_ERR_INVALID_ARG
-    assert dw(hq=64, hkv=4) == PA_ERR_UNSUPPORTED        # G = 16 on the matrix cores
+    assert dw(hq=68, hkv=4) == PA_ERR_UNSUPPORTED        # G = 17 > 16
+    assert dw(hq=64, hkv=4) == PA_ERR_INVALID_ARG        # G = 16: NULL pointers
     assert dw(dt=PA_INT8) == PA_ERR_INVALID_ARG          # 8-bit pools: pa_decode_quant
     assert dw() == PA_ERR_INVALID_ARG                    # valid scalars, NULL pointers
     assert dw(window=0) == PA_ERR_INVALID_ARG            # window 0: the plain decode's checks
@@ -218,13 +220,12 @@ def test_workspace_and_partition_queries():
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, -2, PA_BF16) == -1
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 256, PA_BF16) == 256
     assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 100, PA_BF16) == -1
-    # 5..8 query heads per KV head: the even split by default (two head
-    # groups on the 4x4x4 engine); more: fixed partitions by default, the
-    # even split on request
+    # up to 16 query heads per KV head: the even split by default (one to
+    # four head groups per K/V load on the matrix cores)
     assert h.pa_decode_partition_size(64, 64, 8, 128, 2048, 0, PA_BF16) == 0
     assert h.pa_decode_partition_size(64, 40, 8, 64, 2048, 0, PA_F16) == 0
-    assert h.pa_decode_partition_size(64, 128, 8, 128, 2048, 0, PA_F16) == 256
-    assert h.pa_decode_partition_size(64, 128, 8, 128, 2048, -1, PA_F16) == 0
+    assert h.pa_decode_partition_size(64, 128, 8, 128, 2048, 0, PA_F16) == 0
+    assert h.pa_decode_partition_size(64, 136, 8, 128, 2048, 0, PA_F16) == -1
     # one partition -> no workspace
     assert h.pa_decode_workspace_bytes(4, 8, 2, 64, 256, 512, PA_F32) == 0
     # 3 partitions of 512: m, l and acc rows, each region 256-byte aligned

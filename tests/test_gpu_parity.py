@@ -193,7 +193,10 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 511, 512, 513, 1023, 1024, 
     ("bf16", 12, 4, 128, 256), ("f16", 6, 2, 64, -1),
     # 5..8 query heads per KV head: two head groups per K/V load
     ("bf16", 64, 8, 128, -1), ("bf16", 64, 8, 128, 0), ("f16", 40, 8, 64, 0),
-    ("bf16", 12, 2, 128, 256), ("f16", 14, 2, 128, -1), ("bf16", 8, 1, 64, 16)])
+    ("bf16", 12, 2, 128, 256), ("f16", 14, 2, 128, -1), ("bf16", 8, 1, 64, 16),
+    # 9..16: three or four head groups
+    ("bf16", 96, 8, 128, -1), ("f16", 24, 2, 64, 0), ("bf16", 16, 1, 128, -1),
+    ("f16", 128, 8, 128, 0), ("bf16", 40, 4, 64, 64)])
 def test_edge_lengths_and_shapes(dtype, hq, hkv, d, ps, kernel):
     case = custom_case(31, dtype, EDGE_LENS, hq, hkv, d, partition_size=ps, boost_prob=0.02)
     say(f"[edge] {dtype} Hq={hq} Hkv={hkv} D={d} P={ps} kernel={kernel}")
@@ -238,7 +241,8 @@ SPLIT_LENS = {
 @pytest.mark.parametrize("lens", list(SPLIT_LENS), ids=list(SPLIT_LENS))
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 16, 2, 64),
                                             ("bf16", 16, 16, 128), ("f16", 24, 8, 128),
-                                            ("bf16", 64, 8, 128), ("f16", 28, 4, 64)])
+                                            ("bf16", 64, 8, 128), ("f16", 28, 4, 64),
+                                            ("bf16", 128, 8, 128), ("f16", 44, 4, 64)])
 def test_even_split_shapes(lens, dtype, hq, hkv, d):
     """The even split of the batch's work across waves (partition_size 0):
     ranges cut over many chunks, chunks holding many whole sequences."""
@@ -359,7 +363,8 @@ def test_timing_events_bracket_the_attention_kernel(ps):
 
 
 @pytest.mark.parametrize("hq,hkv,ps", [(32, 8, 0), (32, 8, 256), (16, 2, -1), (8, 8, 64),
-                                       (64, 8, -1), (48, 8, 256), (64, 8, 0)])
+                                       (64, 8, -1), (48, 8, 256), (64, 8, 0), (96, 8, -1),
+                                       (128, 8, 0)])
 def test_step_slot_cases_match_append_then_decode(hq, hkv, ps):
     """pa_decode_step == pa_cache_append then pa_decode for every slot value:
     the table's slot, -1 (no write; the position is attended as stored) and a

@@ -122,7 +122,8 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1023, 1025
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("hq,hkv,d,ps", [(32, 8, 128, 0), (16, 4, 64, 0), (8, 8, 128, 512),
                                          (12, 4, 128, 16), (6, 3, 64, -1), (2, 1, 128, 256),
-                                         (64, 8, 128, 0), (40, 8, 64, 256), (14, 2, 128, -1)])
+                                         (64, 8, 128, 0), (40, 8, 64, 256), (14, 2, 128, -1),
+                                         (96, 8, 128, 0), (32, 2, 64, -1), (26, 2, 128, 128)])
 def test_edge_lengths_and_shapes(fmt, hq, hkv, d, ps):
     case = quantized(custom_case(61, "bf16", EDGE_LENS, hq, hkv, d, partition_size=ps,
                                  boost_prob=0.02), fmt)

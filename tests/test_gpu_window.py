@@ -58,7 +58,8 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 600]
 @pytest.mark.parametrize("dtype,hq,hkv,d,ps", [("bf16", 32, 8, 128, 0), ("f16", 16, 4, 64, 0),
                                               ("bf16", 8, 8, 128, 64), ("f32", 8, 2, 64, 0),
                                               ("bf16", 12, 4, 128, 16), ("f16", 6, 3, 64, -1),
-                                              ("bf16", 64, 8, 128, 0), ("f16", 14, 2, 64, 64)])
+                                              ("bf16", 64, 8, 128, 0), ("f16", 14, 2, 64, 64),
+                                              ("bf16", 32, 2, 64, -1), ("f16", 96, 8, 128, 256)])
 @pytest.mark.parametrize("W", [1, 15, 16, 17, 64, 250])
 def test_edge_windows(dtype, hq, hkv, d, ps, W, kernel):
     case = windowed(custom_case(71, dtype, EDGE_LENS, hq, hkv, d, partition_size=ps), W)
@@ -73,14 +74,6 @@ def test_plain_fma_kernel_takes_large_groups(monkeypatch):
     case = windowed(custom_case(72, "bf16", [40, 300, 129], 32, 2, 64), 50)
     ref = run_case(case, pool_fill=NAN_BITS["bf16"])
     _check(case, run_gpu_step(case), ref)
-
-
-def test_matrix_cores_reject_window_with_large_groups():
-    pk = require_gpu()
-    case = windowed(custom_case(73, "bf16", [40, 70], 32, 2, 64), 32)
-    with pytest.raises(pk.PAError) as e:
-        run_gpu_step(case)
-    assert e.value.code == 2                     # PA_ERR_UNSUPPORTED
 
 
 def test_window_covering_everything_equals_plain_decode():
