@@ -464,6 +464,14 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
 #pragma unroll
     for (int c = 0; c < NC; ++c) kr[c] = load_stream(kt + c * 256);
   };
+  auto issue_v_block = [&](int kb) {
+    const char* vt = vbase + ph[kb] * block_stride + lane * 16;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        vr[kb][h][t] = load_stream(vt + (h * D + 64 * t) * 16);
+  };
   auto issue_v = [&]() {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -672,7 +680,10 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
 
   // last: the quad may reach past the end of the range (only the range's last
   // quad can)
-  auto pv = [&](int qd, const uint2 (&phi)[NG], const uint2 (&plo)[NG], auto last) {
+  // refill: V of the next quad (blocks in ph) is loaded block by block as
+  // soon as P.V has consumed the block's registers.
+  auto pv = [&](int qd, const uint2 (&phi)[NG], const uint2 (&plo)[NG], auto last,
+                auto refill) {
     const int qpos = (blk_begin + 4 * qd) * kBlockSize;
     if (decltype(last)::value && qpos + 4 * kBlockSize > tok_end && kCodes) {
       // as below, for 16 one-byte tokens per chunk: byte e of word w is
@@ -732,6 +743,11 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
           st.acc[n][t] = Mma::template mma<a>(plo[n], vv, st.acc[n][t]);
         }
       }
+      if constexpr (decltype(refill)::value && (a & 3) == 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v_block(kb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     });
   };
 
@@ -761,9 +777,15 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     quad_phys(qd + 1, ph);
     issue_k();
     __builtin_amdgcn_sched_barrier(0);
-    pv(qd, phi, plo, std::false_type{});
-    __builtin_amdgcn_sched_barrier(0);
-    issue_v();
+    if constexpr (NG >= 2) {
+      // several head groups: the P.V of a quad is long enough that loading
+      // the next quad's V block by block shortens the wait for it
+      pv(qd, phi, plo, std::false_type{}, std::true_type{});
+    } else {
+      pv(qd, phi, plo, std::false_type{}, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      issue_v();
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   const bool at_table = with_new && new_at_table();
@@ -774,7 +796,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     if (at_table) substitute_v();
     write_new(at_table);
   }
-  pv(nquad - 1, phi, plo, std::true_type{});
+  pv(nquad - 1, phi, plo, std::true_type{}, std::false_type{});
 }
 
 template <int D, int NG>
