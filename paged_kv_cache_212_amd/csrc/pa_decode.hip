@@ -777,9 +777,10 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     quad_phys(qd + 1, ph);
     issue_k();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NG >= 2) {
-      // several head groups: the P.V of a quad is long enough that loading
-      // the next quad's V block by block shortens the wait for it
+    if constexpr (NG >= 2 || !kCodes) {
+      // loading the next quad's V block by block as P.V frees each block
+      // shortens the wait for it (measured: 16-bit pools, and 8-bit pools
+      // with several head groups; 8-bit pools with one group lost time)
       pv(qd, phi, plo, std::false_type{}, std::true_type{});
     } else {
       pv(qd, phi, plo, std::false_type{}, std::false_type{});
