@@ -49,12 +49,14 @@ def prefill_ref(q_bits, k_pool, v_pool, tables, lens, query_start, dtype, scale=
             continue
         Kb, Vb = gather_ref(k_pool, v_pool, tables[b], L, bs)
         Kb, Vb = to_f64(Kb, dtype), to_f64(Vb, dtype)
-        for i in range(n):
-            p = L - n + i                     # position of this query token
-            row = int(qs[b]) + i
-            for h in range(Hq):
-                g = h // G
-                s = scale * (Kb[g, :p + 1] @ q[row, h])
-                w = np.exp(s - s.max())
-                out[row, h] = (w / w.sum()) @ Vb[g, :p + 1]
+        r0 = int(qs[b])
+        pos = L - n + np.arange(n)            # position of each query token
+        # key t is visible to the query at position p when t <= p (causal)
+        visible = np.arange(L)[None, :] <= pos[:, None]          # [n][L]
+        for h in range(Hq):
+            g = h // G
+            s = scale * (q[r0:r0 + n, h] @ Kb[g].T)                # [n][L]
+            s = np.where(visible, s, -np.inf)
+            w = np.exp(s - s.max(axis=1, keepdims=True))           # 0 where not visible
+            out[r0:r0 + n, h] = (w / w.sum(axis=1, keepdims=True)) @ Vb[g]
     return out
