@@ -118,33 +118,75 @@ typedef struct pa_bm_stats_t {
   int64_t slack_slots;   /* sum over sequences of blocks*block_size - length */
 } pa_bm_stats_t;
 
-/* Creates a manager for num_blocks blocks of block_size tokens.  free_order
- * (host, [num_blocks]) is copied.  *out receives the handle. */
+/* Creates a manager for num_blocks blocks of block_size tokens: the pool of
+ * same-size physical blocks reserved up front, which the manager hands out
+ * to sequences (page 3, abeam.tech review, section 「KV キャッシュマネージャ」;
+ * block_size as a parameter, 16 by default: page 1, jisaku.com glossary,
+ * section 「PagedAttentionの解決策」).  free_order (host, [num_blocks]) is
+ * copied; NULL = ascending.  *out receives the handle.  PA_ERR_INVALID_ARG
+ * for num_blocks <= 0, block_size <= 0, or a free_order that is not a
+ * permutation of [0, num_blocks); nothing is allocated then. */
 pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
                        pa_bm** out);
 void pa_bm_destroy(pa_bm* bm);
 
-/* New sequence with num_tokens tokens; writes their slots to slots_out
- * (host, [num_tokens], may be NULL). */
+/* New sequence with num_tokens tokens: ceil(num_tokens / block_size) blocks
+ * are taken from the free list, their ids become the sequence's block table
+ * (logical block k -> physical block table[k], page 1, jisaku.com glossary,
+ * section 「PagedAttentionの解決策」; page 3, abeam.tech review, section
+ * 「用語解説」, ブロックテーブル).  Slot of position p: table[p / block_size]
+ * * block_size + p % block_size, written to slots_out (host, [num_tokens],
+ * may be NULL).  PA_ERR_SEQ_EXISTS for a live id, PA_ERR_OUT_OF_BLOCKS when
+ * the free list is too short, PA_ERR_INVALID_ARG for num_tokens < 0; no
+ * change then. */
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id, int32_t num_tokens, int64_t* slots_out);
 
-/* child shares every block of parent (reference counts +1); no block is taken. */
+/* child shares every block of parent: it gets a copy of parent's block
+ * table, every block's reference count goes up by one, and no block is
+ * taken or copied (page 2, hubblespacetelescope blog, section
+ * 「OSの知恵をGPUへ…」, third bullet: sharing by reference count, no memory
+ * copy; page 3, abeam.tech review, section 「並列サンプリングやビームサーチでの共有」).
+ * PA_ERR_UNKNOWN_SEQ for an unknown parent, PA_ERR_SEQ_EXISTS for a live
+ * child id; no change then. */
 pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id);
 
-/* Reserves the next num_tokens positions of one sequence.  slots_out (host,
- * [num_tokens], may be NULL); cow_pairs_out (host, [1][2] at most, may be NULL
- * only if no copy can arise) receives (src, dst) block pairs to copy before
- * writing; *num_cow_out their count (0 or 1). */
+/* Reserves the next num_tokens positions of one sequence (a prompt chunk, or
+ * several generated tokens): tokens fill the last block, and a new block is
+ * taken each time a position starts one (page 2, hubblespacetelescope blog,
+ * section 「OSの知恵をGPUへ…」, first bullet; page 3, abeam.tech review,
+ * section 「KV キャッシュマネージャ」).  A shared last block that would be
+ * written is first copied (copy-on-write, page 3, section 「用語解説」).
+ * slots_out (host, [num_tokens], may be NULL); cow_pairs_out (host, [1][2]
+ * at most, may be NULL only if no copy can arise) receives (src, dst) block
+ * pairs to copy before writing; *num_cow_out their count (0 or 1).
+ * PA_ERR_UNKNOWN_SEQ / PA_ERR_OUT_OF_BLOCKS: no change. */
 pa_status pa_bm_extend(pa_bm* bm, int64_t seq_id, int32_t num_tokens, int64_t* slots_out,
                        int32_t* cow_pairs_out, int32_t* num_cow_out);
 
-/* Decode-step reservation: one more position for each of n distinct sequences,
- * in the order given.  slots_out (host, [n]); cow_pairs_out (host, [n][2]);
- * *num_cow_out = number of pairs written. */
+/* Decode-step reservation: one more position for each of n distinct
+ * sequences, in the order given (page 3, abeam.tech review, section
+ * 「KV キャッシュマネージャ」: generated tokens go into the last block, and a
+ * full block is followed by a newly taken one, with the table updated).
+ * Position p = the sequence's length before the call: a new block when
+ * p % block_size == 0; otherwise block table[p / block_size], copied first
+ * when its reference count is above one (the writer copies, the last holder
+ * writes in place: page 3, section 「並列サンプリングやビームサーチでの共有」;
+ * page 2, hubblespacetelescope blog, section 「OSの知恵をGPUへ…」, third
+ * bullet).  slots_out (host, [n]) receives each position's slot;
+ * cow_pairs_out (host, [n][2]) the (src, dst) block pairs the caller copies
+ * (pa_copy_blocks) before the writes; *num_cow_out = number of pairs.
+ * All-or-nothing: the blocks the whole batch needs (new tail blocks plus
+ * copies) are counted first, and PA_ERR_OUT_OF_BLOCKS leaves the manager
+ * unchanged; PA_ERR_UNKNOWN_SEQ or PA_ERR_INVALID_ARG (a repeated id) too. */
 pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n, int64_t* slots_out,
                              int32_t* cow_pairs_out, int32_t* num_cow_out);
 
-/* Releases a sequence: counts -1, blocks reaching zero return to the pool. */
+/* Releases a finished sequence: each of its blocks' reference counts drops
+ * by one, and blocks reaching zero return to the free list, in table order
+ * (page 3, abeam.tech review, section 「KV キャッシュマネージャ」: at the end
+ * of a request only its blocks are handed back).  PA_ERR_UNKNOWN_SEQ: no
+ * change.  The caller orders reuse of a freed block after the last kernel
+ * that reads it (same stream). */
 pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
 
 /* Beam search / parallel sampling step (page 3, abeam.tech review, section
@@ -179,12 +221,28 @@ pa_status pa_bm_release_before(pa_bm* bm, int64_t seq_id, int32_t first_pos,
                                int32_t* released_out);
 
 /* Block tables of n sequences into tables_out (host, [n][max_blocks], padded
- * with -1) and lengths into lens_out (host, [n], may be NULL). */
+ * with -1) and lengths into lens_out (host, [n], may be NULL): the logical ->
+ * physical map the attention kernels walk (page 3, abeam.tech review,
+ * section 「用語解説」, ブロックテーブル: the kernel reads the KV it needs
+ * by following the table).  PA_ERR_INVALID_ARG when a table is longer than
+ * max_blocks; PA_ERR_UNKNOWN_SEQ for an unknown id; outputs unspecified
+ * then. */
 pa_status pa_bm_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
                              int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
 
+/* Length (tokens) of a live sequence; PA_ERR_UNKNOWN_SEQ otherwise. */
 pa_status pa_bm_seq_len(const pa_bm* bm, int64_t seq_id, int32_t* len_out);
+/* Reference count of a block: the number of block tables that hold it (page
+ * 2, hubblespacetelescope blog, section 「OSの知恵をGPUへ…」, third bullet:
+ * shared blocks are tracked by reference count); 0 for a free block.
+ * PA_ERR_INVALID_ARG for an id outside [0, num_blocks). */
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block_id, int32_t* count_out);
+/* Pool occupancy (pa_bm_stats_t above).  slack_slots is the paging waste:
+ * unused slots in the sequences' blocks, at most block_size - 1 per sequence
+ * (page 2, hubblespacetelescope blog, section 「OSの知恵をGPUへ…」, second
+ * bullet); num_blocks and the counts mirror the block accounting a serving
+ * engine reports at start-up (page 1, jisaku.com glossary, section
+ * 「vLLMのメモリ管理確認」). */
 pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out);
 
 /* ------------------------------------------------------------------------
@@ -244,6 +302,21 @@ pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools, int3
                                 int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t block_size, pa_dtype dtype, void* stream);
 
+/* Kernel family of the fp16/bf16 decode calls, process wide:
+ * PA_KERNEL_AUTO (the default) runs them on the matrix cores,
+ * PA_KERNEL_GENERIC on the plain-FMA kernel (fixed partitions of 256
+ * tokens by default), so that both can be checked against each other.  The
+ * choice also sizes the workspace (pa_decode_workspace_bytes) and the
+ * partition size (pa_decode_partition_size): change it only between calls,
+ * with no decode call in flight that was sized under the other choice.
+ * Returns the previous choice; an unknown value sets PA_ERR_INVALID_ARG in
+ * pa_last_error() and changes nothing. */
+typedef enum pa_decode_kernel {
+  PA_KERNEL_AUTO = 0,
+  PA_KERNEL_GENERIC = 1
+} pa_decode_kernel;
+pa_decode_kernel pa_set_decode_kernel(pa_decode_kernel kernel);
+
 /* How pa_decode splits contexts for these arguments; partition_size is
  *   > 0 (a multiple of 16): fixed partitions of that many tokens;
  *   0: the library's choice: the even split on the matrix-core path
@@ -271,8 +344,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype);
 
-/* Decode attention over a paged cache: for each sequence b (length
- * L = context_lens[b]) and query head h,
+/* Decode attention over a paged cache (page 3, abeam.tech review, section
+ * 「モデル構造ではなくサービング基盤の変更」: the kernel follows the block table
+ * to read K/V in logical order, and the result is ordinary attention:
+ * section 「よくある質問」; page 4, pro-knowledge-base FAQ).  The attention
+ * formula itself is not on the pages: scaled dot-product attention of one
+ * query per sequence.  For each sequence b (length L = context_lens[b]) and
+ * query head h,
  *   out[b][h] = softmax_t(scale * q[b][h] . K_b[t]) weighted sum of V_b[t],
  * t in [0, L), where K_b/V_b are KV head h/G of the tokens reached through
  * block_tables[b] in logical order; accumulation in fp32.  L = 0 gives zeros.
@@ -287,9 +365,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   the workspace 256-byte aligned (PA_ERR_INVALID_ARG otherwise).
  * Supported: block_size 16; head_dim 64 or 128; Hq a multiple of Hkv with
  * G = Hq/Hkv <= 16.  fp16/bf16 run on the matrix cores, fp32 on plain FMAs;
- * setting the environment variable PA_DECODE_KERNEL=generic makes fp16/bf16
- * use the plain-FMA kernel too (read on every call).  8-bit pools are
- * attended by pa_decode_quant (PA_ERR_INVALID_ARG here). */
+ * pa_set_decode_kernel(PA_KERNEL_GENERIC) makes fp16/bf16 use the plain-FMA
+ * kernel too.  8-bit pools are attended by pa_decode_quant
+ * (PA_ERR_INVALID_ARG here).  Errors: PA_ERR_UNSUPPORTED for block_size,
+ * head_dim or G outside the supported set; PA_ERR_INVALID_ARG for other bad
+ * scalars, NULL or misaligned pointers; PA_ERR_WORKSPACE for a missing or
+ * short workspace; PA_ERR_HIP for a failed launch.  Nothing is launched on
+ * an error. */
 pa_status pa_decode(float* out, const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -411,8 +493,8 @@ pa_status pa_prefill(float* out, const void* q, const void* k_pool, const void* 
  * softmax scale (fp32 product scale * k_scale) and v_scale into the output.
  * Other arguments, the workspace and the bounds checks as for pa_decode.
  * Supported: block_size 16, head_dim 64 or 128, G = Hq/Hkv <= 16
- * (PA_ERR_UNSUPPORTED otherwise); the 16-bit-only plain-FMA switch
- * (PA_DECODE_KERNEL) does not apply. */
+ * (PA_ERR_UNSUPPORTED otherwise); pa_set_decode_kernel does not apply
+ * (there is no plain-FMA kernel for codes). */
 pa_status pa_decode_quant(float* out, const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* block_tables, const int32_t* context_lens,
                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

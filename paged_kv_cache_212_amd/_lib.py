@@ -17,6 +17,7 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
                 3: "PA_ERR_OUT_OF_BLOCKS", 4: "PA_ERR_UNKNOWN_SEQ", 5: "PA_ERR_SEQ_EXISTS",
                 6: "PA_ERR_HIP", 7: "PA_ERR_WORKSPACE"}
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3, 4
+PA_KERNEL_AUTO, PA_KERNEL_GENERIC = 0, 1
 
 
 class PAError(RuntimeError):
@@ -92,6 +93,7 @@ SIGNATURES = {
     "pa_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                              _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp]),
     "pa_time_next_attention": (C.c_int, [_vp, _vp]),
+    "pa_set_decode_kernel": (C.c_int, [C.c_int]),
     "pa_stream_read": (C.c_int, [_vp, _sz, _vp, _vp]),
     "pa_gather_kv": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, C.c_int, _vp]),

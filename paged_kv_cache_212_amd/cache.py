@@ -132,7 +132,14 @@ class PagedKVCache:
         if plan.cows.shape[0]:
             ops.copy_blocks(self.k_pool, self.v_pool, plan.d_cows, stream)
         if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+            # from the launch stream's pool of the caching allocator: memory
+            # freed by work on another stream is not handed to this launch
+            # before that work is done
+            if stream is None:
+                out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+            else:
+                with torch.cuda.stream(stream):
+                    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         if window:
             # sliding window: fused step, or append then windowed decode
             if self.cache_dtype is not None:
@@ -165,7 +172,7 @@ class PagedKVCache:
             if workspace is None:
                 workspace = ops.decode_workspace(B, Hq, self.num_kv_heads, D,
                                                  plan.max_context_len, partition_size, q.dtype,
-                                                 q.device)
+                                                 q.device, stream)
             ops.decode_step(out, q, self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
                             plan.d_tables, plan.d_lens, plan.max_context_len, scale,
                             partition_size, workspace, stream, phase="partial")

@@ -32,6 +32,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -1225,14 +1226,12 @@ __global__ __launch_bounds__(D) void merge_kernel(Params pr) {
   pr.out[row * D + d] = (num / den) * pr.out_scale;
 }
 
-// Kernel selection: PA_DECODE_KERNEL=generic forces the plain-FMA kernel for
-// every dtype (used by tests to check both kernels); default picks the
-// matrix-core kernel for fp16/bf16.
-enum class Path { kAuto, kGeneric };
-Path path_from_env() {
-  const char* v = std::getenv("PA_DECODE_KERNEL");
-  return (v && std::strcmp(v, "generic") == 0) ? Path::kGeneric : Path::kAuto;
-}
+// Kernel family of the decode calls, set by pa_set_decode_kernel (process
+// wide; PA_KERNEL_GENERIC makes fp16/bf16 take the plain-FMA kernel too, so
+// both kernels can be checked).  Read once per call, never from the
+// environment.
+std::atomic<int> g_decode_kernel{PA_KERNEL_AUTO};
+bool generic_selected() { return g_decode_kernel.load(std::memory_order_relaxed) == PA_KERNEL_GENERIC; }
 
 constexpr int kDefaultPartition = 256;  // fixed-partition size of the plain-FMA kernel
 constexpr int kFixedWaves4 = 3;         // waves per SIMD the 4x4x4 fixed kernel is built for
@@ -1495,7 +1494,7 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   if (nt && ((reinterpret_cast<uintptr_t>(nt->k_new) | reinterpret_cast<uintptr_t>(nt->v_new)) & 15))
     return fail(PA_ERR_INVALID_ARG, "%s: k_new and v_new must be 16-byte aligned", fn);
   const LaunchPlan lp = make_plan(max_context_len, partition_size, dtype,
-                                  path_from_env() == Path::kGeneric);
+                                  generic_selected());
   const size_t need = workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
   if (need > 0 && (!workspace || workspace_bytes_given < need))
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -1576,6 +1575,14 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
 
 using namespace pa;
 
+extern "C" pa_decode_kernel pa_set_decode_kernel(pa_decode_kernel kernel) {
+  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_GENERIC) {
+    fail(PA_ERR_INVALID_ARG, "pa_set_decode_kernel: unknown kernel %d", (int)kernel);
+    return static_cast<pa_decode_kernel>(g_decode_kernel.load());
+  }
+  return static_cast<pa_decode_kernel>(g_decode_kernel.exchange(kernel));
+}
+
 extern "C" pa_status pa_time_next_attention(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr))
     return fail(PA_ERR_INVALID_ARG, "pa_time_next_attention: give both events or neither");
@@ -1590,7 +1597,7 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_head
   if (!decode_args_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                       partition_size, dtype))
     return -1;
-  return make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric)
+  return make_plan(max_context_len, partition_size, dtype, generic_selected())
       .P;
 }
 
@@ -1602,7 +1609,7 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
                       partition_size, dtype))
     return 0;
   const LaunchPlan lp =
-      make_plan(max_context_len, partition_size, dtype, path_from_env() == Path::kGeneric);
+      make_plan(max_context_len, partition_size, dtype, generic_selected());
   return workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
 }
 

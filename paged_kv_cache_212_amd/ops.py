@@ -8,7 +8,8 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import PA_BF16, PA_F16, PA_F32, PA_FP8_E4M3, PA_INT8, check, lib
+from ._lib import (PA_BF16, PA_F16, PA_F32, PA_FP8_E4M3, PA_INT8, PA_KERNEL_AUTO,
+                   PA_KERNEL_GENERIC, check, lib)
 
 BLOCK_SIZE = 16
 _DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
@@ -140,6 +141,19 @@ def copy_blocks_layers(k_pools, v_pools, block_pairs, stream=None):
         vptr.record_stream(stream)
 
 
+_KERNELS = {"auto": PA_KERNEL_AUTO, "generic": PA_KERNEL_GENERIC}
+
+
+def set_decode_kernel(kernel: str) -> str:
+    """Kernel family of the fp16/bf16 decode calls (pa_set_decode_kernel):
+    "auto" (matrix cores) or "generic" (plain FMAs).  Returns the previous
+    choice.  Change it only between calls: it also sizes the workspace."""
+    if kernel not in _KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(_KERNELS)}")
+    prev = int(lib().pa_set_decode_kernel(_KERNELS[kernel]))
+    return {v: k for k, v in _KERNELS.items()}[prev]
+
+
 def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                           partition_size, dtype) -> int:
     return int(lib().pa_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -155,10 +169,17 @@ def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_co
 
 
 def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                     partition_size, dtype, device="cuda"):
+                     partition_size, dtype, device="cuda", stream=None):
+    """Workspace tensor for the decode calls.  With ``stream`` (a
+    torch.cuda.Stream) the memory comes from that stream's pool of torch's
+    caching allocator, so once the tensor is dropped it is handed out again
+    only to work ordered after the calls made on ``stream``."""
     n = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                partition_size, dtype)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    if stream is None:
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 EVEN_SPLIT = -1   # partition_size value selecting the even split of the batch's work
@@ -192,7 +213,7 @@ def decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, 
     scale = D ** -0.5 if scale is None else float(scale)
     if workspace is None:
         workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size, q.dtype,
-                                     q.device)
+                                     q.device, stream)
     check(getattr(lib(), fn)(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
                           _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
                           _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
@@ -229,7 +250,7 @@ def decode_quant(out, q, k_pool, v_pool, block_tables, context_lens, max_context
     scale = D ** -0.5 if scale is None else float(scale)
     if workspace is None:
         workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size,
-                                     k_pool.dtype, q.device)
+                                     k_pool.dtype, q.device, stream)
     check(lib().pa_decode_quant(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
                                 _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
                                 _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
@@ -258,7 +279,7 @@ def decode_step_quant(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_
     scale = D ** -0.5 if scale is None else float(scale)
     if workspace is None:
         workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size,
-                                     k_pool.dtype, q.device)
+                                     k_pool.dtype, q.device, stream)
     check(lib().pa_decode_step_quant(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
                                      _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
                                      _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
@@ -283,7 +304,7 @@ def _decode_window(out, q, k_pool, v_pool, block_tables, context_lens, max_conte
     scale = D ** -0.5 if scale is None else float(scale)
     if workspace is None:
         workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size, q.dtype,
-                                     q.device)
+                                     q.device, stream)
     check(lib().pa_decode_window(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
                                  _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables"),
                                  _dev(context_lens, "context_lens"), B, Hq, H, D, BLOCK_SIZE, N,
@@ -329,7 +350,7 @@ def decode_step(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables
     scale = D ** -0.5 if scale is None else float(scale)
     if workspace is None:
         workspace = decode_workspace(B, Hq, H, D, max_context_len, partition_size, q.dtype,
-                                     q.device)
+                                     q.device, stream)
     win = (int(window),) if window else ()
     check(getattr(lib(), fn)(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
                              _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),

@@ -16,6 +16,23 @@ NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0,
             "fp8": 0x7F, "i8": 0x80}
 CODE_TORCH = {"fp8": torch.float8_e4m3fn, "i8": torch.int8}
 TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2}
+# Regression bar of the random-value runs with 16-bit pools, kept beside the
+# 1e-2 contract.  The kernels accumulate in fp32 and feed P . V with P split
+# into a high and a low 16-bit part (|p - hi - lo| <= 2^-16 |p|), so each
+# weight carries a relative error below 2^-16; numerator and denominator then
+# move by at most that fraction of max |v| (about 6 for unit normals at these
+# sizes): 1.8e-4 if every rounding had the same sign.  The roundings are
+# unbiased and average out: measured on MI355X the largest decode error over
+# every test, full sizes included, is 1.9e-5.  1e-4 keeps 5x of room and sits
+# below what one dropped or doubled token of a 2048-token context does to a
+# row (5.7e-4 in the median).
+REG_TOL = {"f32": 1e-5, "f16": 1e-4, "bf16": 1e-4}
+# Position-coded runs (workloads.configs.position_coded): every row is an
+# exact mean of 0/64 entries, so the only error left is the final division
+# and scaling (a few fp32 ulps of values below 64); one dropped, doubled or
+# misplaced token moves some element by at least 64 / L >= 4.8e-4 for
+# contexts up to 131072 tokens.
+CODED_TOL = 2e-5
 
 
 def require_gpu():
@@ -31,10 +48,12 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None, fused=True):
+def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None, fused=True,
+                 pools=True):
     """Replays the case's set-up and runs one step on the GPU.
 
-    Returns dict(plan=StepPlan, out=np fp32, k_pool/v_pool=np bits, cache=PagedKVCache).
+    Returns dict(plan=StepPlan, out=np fp32, k_pool/v_pool=np bits (only with
+    ``pools``), cache=PagedKVCache).
     """
     pk = require_gpu()
     from oracle import bits_of  # test side only: stored-bit views for comparison
@@ -56,9 +75,11 @@ def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None, fused=
     out = cache.step(plan, q, k_new, v_new, partition_size=ps, fused=fused,
                      window=getattr(case, "window", 0))
     torch.cuda.synchronize()
-    return {"plan": plan, "out": out.cpu().numpy(), "cache": cache, "q": q,
-            "k_pool": bits_of(cache.k_pool, case.kv_dtype),
-            "v_pool": bits_of(cache.v_pool, case.kv_dtype)}
+    res = {"plan": plan, "out": out.cpu().numpy(), "cache": cache, "q": q}
+    if pools:
+        res["k_pool"] = bits_of(cache.k_pool, case.kv_dtype)
+        res["v_pool"] = bits_of(cache.v_pool, case.kv_dtype)
+    return res
 
 
 def max_err(a, b):

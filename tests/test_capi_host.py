@@ -360,3 +360,28 @@ def test_cpp_replays_workload_scripts_like_model():
         ta, la = am.block_tables(case.batch, mb)
         tb, lb = bm.block_tables(case.batch, mb)
         assert np.array_equal(ta, tb) and np.array_equal(la, lb)
+
+
+def test_decode_kernel_choice_is_an_explicit_setting():
+    """The plain-FMA switch is set through pa_set_decode_kernel, not read from
+    the environment: it changes the plan pa_decode_partition_size reports
+    (even split 0 on the matrix cores, 256-token partitions on plain FMAs),
+    returns the previous choice and rejects unknown values unchanged."""
+    h = pk.lib()
+    os.environ["PA_DECODE_KERNEL"] = "generic"       # no longer consulted
+    try:
+        assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_BF16) == 0
+    finally:
+        del os.environ["PA_DECODE_KERNEL"]
+    assert pk.ops.set_decode_kernel("generic") == "auto"
+    try:
+        assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_BF16) == 256
+        ws_generic = h.pa_decode_workspace_bytes(64, 32, 8, 128, 2048, 0, PA_BF16)
+        assert h.pa_set_decode_kernel(7) == 1       # unknown: unchanged, reported
+        assert b"unknown kernel" in h.pa_last_error()
+    finally:
+        assert pk.ops.set_decode_kernel("auto") == "generic"
+    assert h.pa_decode_partition_size(64, 32, 8, 128, 2048, 0, PA_BF16) == 0
+    assert h.pa_decode_workspace_bytes(64, 32, 8, 128, 2048, 0, PA_BF16) != ws_generic
+    with pytest.raises(ValueError):
+        pk.ops.set_decode_kernel("fast")

@@ -10,9 +10,10 @@ import torch
 
 from oracle import (bits_of, copy_ref, gather_ref, new_pools, run_case, to_f64)
 from oracle.run import oracle_sequence_out
-from tests.gpu_helpers import NAN_BITS, TOL, max_err, require_gpu, run_gpu_step, say
+from tests.gpu_helpers import (CODED_TOL, NAN_BITS, REG_TOL, TOL, max_err, require_gpu,
+                               run_gpu_step, say)
 from workloads import make_case, small_case
-from workloads.configs import CONFIG_NAMES, Case, custom_case
+from workloads.configs import CONFIG_NAMES, Case, custom_case, position_coded
 
 pytestmark = pytest.mark.gpu
 
@@ -20,12 +21,13 @@ KERNELS = ["auto", "generic"]
 
 
 @pytest.fixture
-def kernel(request, monkeypatch):
-    if request.param == "generic":
-        monkeypatch.setenv("PA_DECODE_KERNEL", "generic")
-    else:
-        monkeypatch.delenv("PA_DECODE_KERNEL", raising=False)
-    return request.param
+def kernel(request):
+    """Runs the test on the matrix-core ("auto") or plain-FMA ("generic")
+    decode kernels (pa_set_decode_kernel), restoring the default after."""
+    pk = require_gpu()
+    prev = pk.ops.set_decode_kernel(request.param)
+    yield request.param
+    pk.ops.set_decode_kernel(prev)
 
 
 def _oracle_poisoned(case):
@@ -44,6 +46,7 @@ def _compare_full(case, ref, got, tol):
     err = max_err(got["out"], ref["out"])
     say(f"  {case.name} {case.dtype}: max |gpu - oracle| = {err:.3e} (tol {tol})")
     assert err <= tol
+    assert err <= REG_TOL[case.dtype], "beyond the regression bar"
 
 
 @pytest.mark.parametrize("kernel", KERNELS, indirect=True)
@@ -76,52 +79,6 @@ def test_tiny_config_full_size(kernel):
     case = make_case("tiny_fp32")
     say(f"[parity full] tiny_fp32 kernel={kernel}")
     _compare_full(case, _oracle_poisoned(case), run_gpu_step(case), TOL["f32"])
-
-
-def _sample_indices(case, k=3, seed=0):
-    L = case.lens
-    picks = {0, case.num_seqs - 1, int(np.argmax(L)), int(np.argmin(L))}
-    rng = np.random.default_rng(seed)
-    picks |= set(int(i) for i in rng.choice(case.num_seqs, size=min(k, case.num_seqs),
-                                            replace=False))
-    return sorted(picks)
-
-
-@pytest.mark.parametrize("name,kw", [("llama3_8b_bf16", {}), ("opt13b_fp16", {}),
-                                     ("cow_parallel_bf16", {}),
-                                     ("cow_parallel_bf16", {"parked_forks": False}),
-                                     ("long_context_bf16", {})])
-def test_full_size_configs_sampled(name, kw):
-    """Full-size workloads in the bench's launch configuration: every table,
-    slot and copy pair bit-exact; sampled sequences' outputs within tolerance
-    and their gathered K/V bit-exact."""
-    require_gpu()
-    import paged_kv_cache_212_amd as pk
-    say(f"[parity full-size] {name} {kw}: generating on GPU")
-    case = make_case(name, device="cuda", **kw)
-    ref = run_case(case, with_pools=False)
-    got = run_gpu_step(case, poison=False)
-    plan = got["plan"]
-    assert np.array_equal(plan.slots, ref["step_slots"])
-    assert np.array_equal(plan.cows, ref["step_cows"].reshape(-1, 2))
-    assert np.array_equal(plan.tables, ref["tables"])
-    assert np.array_equal(plan.lens, ref["lens"])
-    say(f"  tables/slots/cows bit-exact; {len(plan.cows)} copies; sum L = {case.lens.sum()}")
-    cache = got["cache"]
-    for i in _sample_indices(case):
-        want = oracle_sequence_out(case, i)
-        err = max_err(got["out"][i], want)
-        say(f"  seq {i} L={case.lens[i]}: max err {err:.3e}")
-        assert err <= TOL[case.dtype]
-        L = int(case.lens[i])
-        kg, vg = pk.ops.gather_kv(cache.k_pool, cache.v_pool, plan.d_tables[i:i + 1].contiguous(),
-                                  plan.d_lens[i:i + 1].contiguous(), L)
-        idx = torch.as_tensor(case.rows[int(case.batch[i])][:L], device="cuda")
-        assert torch.equal(kg[0].transpose(0, 1).contiguous().view(torch.int16),
-                           case.k_tok.index_select(0, idx).view(torch.int16))
-        assert torch.equal(vg[0].transpose(0, 1).contiguous().view(torch.int16),
-                           case.v_tok.index_select(0, idx).view(torch.int16))
-    assert not np.isnan(got["out"]).any()
 
 
 def _with(case, **changes):
@@ -203,6 +160,40 @@ def test_edge_lengths_and_shapes(dtype, hq, hkv, d, ps, kernel):
     ref = _oracle_poisoned(case)
     got = run_gpu_step(case)
     _compare_full(case, ref, got, TOL[dtype])
+
+
+@pytest.mark.parametrize("kernel", KERNELS, indirect=True)
+@pytest.mark.parametrize("dtype,hq,hkv,d,ps", [
+    ("bf16", 32, 8, 128, -1), ("bf16", 32, 8, 128, 16), ("bf16", 32, 8, 128, 512),
+    ("f16", 40, 40, 128, -1), ("f16", 16, 2, 64, 256), ("bf16", 64, 8, 128, -1),
+    ("bf16", 128, 8, 128, 0), ("f16", 24, 2, 64, 64), ("f32", 8, 2, 128, 0)])
+def test_edge_lengths_position_coded(dtype, hq, hkv, d, ps, kernel):
+    """Block- and partition-edge lengths with position-coded values: each row
+    is an exact mean, so one token dropped or doubled at a block, quad, piece
+    or partition boundary fails."""
+    case = position_coded(custom_case(33, dtype, EDGE_LENS, hq, hkv, d, partition_size=ps))
+    say(f"[edge coded] {dtype} Hq={hq} Hkv={hkv} D={d} P={ps} kernel={kernel}")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case)
+    _compare_full(case, ref, got, CODED_TOL if dtype != "f32" else TOL["f32"])
+
+
+SPLIT_LENS_CODED = {
+    "one_long": [8000],
+    "many_short": list(np.random.default_rng(4).integers(1, 41, size=300)),
+    "mixed": [33] * 7 + [4000, 1, 17, 2500],
+}
+
+
+@pytest.mark.parametrize("lens", list(SPLIT_LENS_CODED), ids=list(SPLIT_LENS_CODED))
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (16, 16, 128), (96, 8, 128), (28, 4, 64)])
+def test_even_split_position_coded(lens, hq, hkv, d):
+    case = position_coded(custom_case(53, "bf16", SPLIT_LENS_CODED[lens], hq, hkv, d,
+                                      partition_size=-1))
+    say(f"[split coded] {lens} Hq={hq} Hkv={hkv} D={d}")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case)
+    _compare_full(case, ref, got, CODED_TOL)
 
 
 @pytest.mark.parametrize("kernel", KERNELS, indirect=True)

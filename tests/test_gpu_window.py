@@ -8,7 +8,7 @@ import torch
 
 from oracle import run_case
 from oracle.run import oracle_sequence_out
-from tests.gpu_helpers import NAN_BITS, TOL, max_err, require_gpu, run_gpu_step, say
+from tests.gpu_helpers import NAN_BITS, REG_TOL, TOL, max_err, require_gpu, run_gpu_step, say
 from workloads import make_case, small_case
 from workloads.configs import custom_case, windowed
 
@@ -16,12 +16,13 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture
-def kernel(request, monkeypatch):
-    if request.param == "generic":
-        monkeypatch.setenv("PA_DECODE_KERNEL", "generic")
-    else:
-        monkeypatch.delenv("PA_DECODE_KERNEL", raising=False)
-    return request.param
+def kernel(request):
+    """Runs the test on the matrix-core ("auto") or plain-FMA ("generic")
+    decode kernels (pa_set_decode_kernel), restoring the default after."""
+    pk = require_gpu()
+    prev = pk.ops.set_decode_kernel(request.param)
+    yield request.param
+    pk.ops.set_decode_kernel(prev)
 
 
 def _check(case, got, ref):
@@ -33,6 +34,7 @@ def _check(case, got, ref):
     err = max_err(got["out"], ref["out"])
     say(f"  {case.name}: max |gpu - oracle| = {err:.3e}")
     assert err <= TOL[case.dtype]
+    assert err <= REG_TOL[case.dtype], "beyond the regression bar"
 
 
 @pytest.mark.parametrize("kernel", ["auto", "generic"], indirect=True)
@@ -69,8 +71,8 @@ def test_edge_windows(dtype, hq, hkv, d, ps, W, kernel):
     _check(case, got, ref)
 
 
-def test_plain_fma_kernel_takes_large_groups(monkeypatch):
-    monkeypatch.setenv("PA_DECODE_KERNEL", "generic")
+@pytest.mark.parametrize("kernel", ["generic"], indirect=True)
+def test_plain_fma_kernel_takes_large_groups(kernel):
     case = windowed(custom_case(72, "bf16", [40, 300, 129], 32, 2, 64), 50)
     ref = run_case(case, pool_fill=NAN_BITS["bf16"])
     _check(case, run_gpu_step(case), ref)
@@ -87,21 +89,21 @@ def test_window_covering_everything_equals_plain_decode():
     assert np.array_equal(out.cpu().numpy(), got["out"])
 
 
-def test_full_size_long_context_window_sampled():
+@pytest.mark.timeout(900)
+def test_full_size_long_context_window_every_row():
     """The long-context workload (16 sequences of 32K-131K tokens) with a
-    4096-token window, in the bench's configuration: every table bit-exact,
-    out-of-window blocks released, sampled rows against the oracle."""
+    4096-token window, in the bench's configuration (the library's default
+    split, poisoned pools): every table bit-exact, only the window's blocks
+    resident, every row against the oracle, every window gathered bit-exact."""
+    from tests.test_gpu_fullsize import check_every_gather, check_every_row
     require_gpu()
     case = windowed(make_case("long_context_bf16", device="cuda"), 4096, reuse=False)
     say(f"[window full-size] {case.name}")
     ref = run_case(case, with_pools=False)
-    got = run_gpu_step(case, poison=False)
+    got = run_gpu_step(case, partition_size=0, pools=False)
     assert np.array_equal(got["plan"].tables, ref["tables"])
     # only the window's blocks stay resident: at most 4096/16 + 1 per sequence
     st = got["cache"].bm.stats()
     assert st["used_blocks"] == ref["stats"]["used_blocks"] <= 16 * (4096 // 16 + 1)
-    for i in (0, 7, 15):
-        want = oracle_sequence_out(case, i)
-        err = max_err(got["out"][i], want)
-        say(f"  seq {i} L={case.lens[i]}: max err {err:.3e}")
-        assert err <= TOL["bf16"]
+    check_every_row(case, got["out"], REG_TOL["bf16"], "long context W=4096")
+    check_every_gather(case, got)

@@ -388,3 +388,60 @@ def prefill_case(seed, dtype, lens, qlens, hq, hkv, d, device="cpu", *, num_bloc
     q = torch.randn((int(query_start[-1]), hq, d), generator=g, device=device,
                     dtype=torch.float32).to(TORCH_DTYPE[dtype])
     return case, q, query_start
+
+
+CODE_UNIT = 64.0   # the magnitude of every non-zero entry of a position-coded case
+
+
+def position_coded(case: Case, seed: int = 0, mark_prob: float = 1.0 / 16) -> Case:
+    """The same step (lengths, set-up, tables, pool) with q, K and V replaced
+    by exact patterns of 0 and +-64, so that every output row is a plain
+    average of stored V rows and a dropped, doubled or misplaced token
+    changes it by far more than rounding does.
+
+    * V: row r, KV head g holds 64 * bit i of r in dim i (i < bits of the
+      largest row) and 64 * bit j of g in the next dims; other dims 0.  A V
+      row thus names its token row and head.
+    * K: zero, except that with probability ``mark_prob`` each (row, head)
+      gets +64 in dim 0 ("set A"), else with the same probability -64 in dim
+      0 ("set B"), and independently +64 in dim 1 ("set C").
+    * q: query head h gets, by h % 4: +64 e_0, -64 e_0, +64 e_1, or 0.
+
+    Scores are then 0 or +-4096 * scale, so a head's weights are 1 on its
+    marked rows and underflow to 0 elsewhere (all rows when none is marked,
+    and always for q = 0): each output row is the mean of a set of V rows,
+    sums of 0/64 entries that fp32 holds exactly.  Marks are drawn with a
+    seeded torch.Generator on the case's device.
+    """
+    dev = case.k_tok.device
+    R, Hkv, D = case.k_tok.shape
+    td = case.k_tok.dtype
+    nbits = max(1, int(R - 1).bit_length())
+    gbits = max(1, int(Hkv - 1).bit_length())
+    if nbits + gbits > D or D < 2:
+        raise ValueError("head_dim too small for the row code")
+    r = torch.arange(R, device=dev, dtype=torch.int64)
+    g = torch.arange(Hkv, device=dev, dtype=torch.int64)
+    v = torch.zeros((R, Hkv, D), device=dev, dtype=torch.float32)
+    for i in range(nbits):
+        v[:, :, i] = ((r >> i) & 1).to(torch.float32)[:, None] * CODE_UNIT
+    for j in range(gbits):
+        v[:, :, nbits + j] = ((g >> j) & 1).to(torch.float32)[None, :] * CODE_UNIT
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7_919 * seed + 3)
+    u0 = torch.rand((R, Hkv), generator=gen, device=dev)
+    u1 = torch.rand((R, Hkv), generator=gen, device=dev)
+    k = torch.zeros((R, Hkv, D), device=dev, dtype=torch.float32)
+    k[:, :, 0] = torch.where(u0 < mark_prob, CODE_UNIT,
+                             torch.where(u0 < 2 * mark_prob, -CODE_UNIT, 0.0))
+    k[:, :, 1] = torch.where(u1 < mark_prob, CODE_UNIT, 0.0)
+    B, Hq, _ = case.q.shape
+    q = torch.zeros((B, Hq, D), device=case.q.device, dtype=torch.float32)
+    kind = torch.arange(Hq, device=case.q.device) % 4
+    q[:, kind == 0, 0] = CODE_UNIT
+    q[:, kind == 1, 0] = -CODE_UNIT
+    q[:, kind == 2, 1] = CODE_UNIT
+    notes = dict(case.notes)
+    notes["position_coded"] = {"row_bits": nbits, "head_bits": gbits, "mark_prob": mark_prob}
+    return replace(case, name=case.name + "_coded", q=q.to(td), k_tok=k.to(td), v_tok=v.to(td),
+                   notes=notes)
