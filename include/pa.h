@@ -452,6 +452,31 @@ pa_status pa_decode_step_merge(float* out, const void* q, void* k_pool, void* v_
                                int32_t partition_size, pa_dtype dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* pa_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and result as pa_decode_step without the workspace: the
+ * partials of split contexts go to a fixed device array inside the library
+ * (64 MiB, `static __device__`; each device holds its own copy from the
+ * library's load until the process ends; its address is looked up on the
+ * first call on each device, with that device current).  The call itself
+ * allocates nothing and needs no initialised memory.  The current device must
+ * be the one `stream` runs on.  Sizes whose partials exceed the array
+ * (pa_decode_workspace_bytes(...) > 64 MiB, e.g. 16 contexts of 131072
+ * tokens on the even split) return PA_ERR_WORKSPACE before any device call;
+ * use pa_decode_step with a workspace for those.  Every call on one device
+ * shares that device's array, which keeps the last call's contents: calls
+ * that overlap on one device (different streams or threads without ordering)
+ * race and give wrong rows; calls on one stream are ordered. */
+pa_status pa_decode_step_noalloc(float* out, const void* q, void* k_pool, void* v_pool,
+                                 const void* k_new, const void* v_new,
+                                 const int64_t* slot_mapping, const int32_t* block_tables,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 float scale, int32_t partition_size, pa_dtype dtype,
+                                 void* stream);
+
 /* Attention of a chunk of query tokens per sequence over the paged cache
  * (prefill of a prompt, chunked prefill on top of a cached prefix, or decode
  * with one token).  Sequence b holds L = context_lens[b] tokens in its blocks

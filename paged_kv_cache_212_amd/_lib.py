@@ -79,6 +79,9 @@ SIGNATURES = {
     "pa_decode_step_merge": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, C.c_int,
                                        _vp, _sz, _vp]),
+    "pa_decode_step_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                         C.c_int, _vp]),
     "pa_decode_quant": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _f32, _i32, C.c_int, _f32, _f32, _vp, _sz,
                                   _vp]),

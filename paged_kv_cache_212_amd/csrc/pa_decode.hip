@@ -33,6 +33,7 @@
 #include <cstring>
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -1570,6 +1571,43 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   return launch_status(fn);
 }
 
+// ---------------------------------------------------------------------------
+// Fixed device scratch of pa_decode_step_noalloc, for callers that cannot
+// allocate device memory.  Each device holds its own copy of the array from
+// the library's load until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address is looked
+// up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on each device).
+pa_status scratch_of_current_device(const char* fn, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess)
+    return fail(PA_ERR_HIP, "%s: hipGetDevice failed", fn);
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(PA_ERR_UNSUPPORTED, "%s: device %d beyond the %d with a scratch address slot", fn,
+                dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(PA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -1652,6 +1690,32 @@ extern "C" pa_status pa_decode_merge(PA_DECODE_ARGS) {
 extern "C" pa_status pa_decode_step(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
   return run_decode("pa_decode_step", Phase::kBoth, &nt, nullptr, 0, PA_STEP_FWD);
+}
+
+extern "C" pa_status pa_decode_step_noalloc(
+    float* out, const void* q, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+    const int64_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float scale, int32_t partition_size, pa_dtype dtype,
+    void* stream) {
+  const char* fn = "pa_decode_step_noalloc";
+  // the partials this call needs, checked against the array before any
+  // device call (0 for invalid arguments: run_decode reports those)
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len, partition_size, dtype);
+  if (need > kScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "%s: these sizes need %zu bytes of partials; the static scratch holds %zu "
+                "(use pa_decode_step with a workspace)", fn, need, kScratchBytes);
+  void* workspace = nullptr;
+  if (need > 0 && num_seqs > 0) {
+    const pa_status st = scratch_of_current_device(fn, &workspace);
+    if (st != PA_OK) return st;
+  }
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  const size_t workspace_bytes_given = workspace ? kScratchBytes : 0;
+  return run_decode(fn, Phase::kBoth, &nt, nullptr, 0, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_step_partial(PA_STEP_ARGS) {

@@ -365,6 +365,32 @@ def decode_step(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables
     return out
 
 
+def decode_step_noalloc(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables,
+                        context_lens, max_context_len, scale=None, partition_size=0,
+                        stream=None):
+    """pa_decode_step without a workspace (pa_decode_step_noalloc): the
+    partials go to the library's fixed device array; nothing is allocated,
+    here or in the library.  Calls that overlap on one device race."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    B, Hq = _check_decode_args(out, q, k_pool, block_tables, context_lens, D, k_pool.dtype)
+    if k_new.shape != (B, H, D) or v_new.shape != (B, H, D) or k_new.dtype != k_pool.dtype \
+            or v_new.dtype != k_pool.dtype:
+        raise ValueError("k_new/v_new must be [B][Hkv][D] in the pool dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (B,):
+        raise ValueError("slot_mapping must be int64 [B]")
+    scale = D ** -0.5 if scale is None else float(scale)
+    check(lib().pa_decode_step_noalloc(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                                       _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+                                       _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
+                                       _dev(block_tables, "block_tables"),
+                                       _dev(context_lens, "context_lens"), B, Hq, H, D,
+                                       BLOCK_SIZE, N, block_tables.shape[1],
+                                       int(max_context_len), scale, int(partition_size),
+                                       pa_dtype(q.dtype), _stream(stream)),
+          "pa_decode_step_noalloc")
+    return out
+
+
 def prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, max_context_len,
             max_query_len, scale=None, stream=None):
     """out [T][Hq][D] float32 = causal attention of the query rows q [T][Hq][D]

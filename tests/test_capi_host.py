@@ -385,3 +385,21 @@ def test_decode_kernel_choice_is_an_explicit_setting():
     assert h.pa_decode_workspace_bytes(64, 32, 8, 128, 2048, 0, PA_BF16) != ws_generic
     with pytest.raises(ValueError):
         pk.ops.set_decode_kernel("fast")
+
+
+def test_noalloc_step_rejects_sizes_beyond_its_scratch_before_any_device_call():
+    """pa_decode_step_noalloc checks the partials it needs against its fixed
+    64 MiB array before touching the device: 16 contexts of 131072 tokens on
+    the even split need more, and are refused with PA_ERR_WORKSPACE (NULL
+    pointers: nothing was launched); bad scalars still get their own error."""
+    h = pk.lib()
+    nul = None
+    need = h.pa_decode_workspace_bytes(16, 32, 8, 128, 131072, -1, PA_BF16)
+    assert need > 64 << 20
+    assert h.pa_decode_step_noalloc(nul, nul, nul, nul, nul, nul, nul, nul, nul, 16, 32, 8, 128,
+                                    16, 100, 8192, 131072, 0.1, -1, PA_BF16,
+                                    nul) == PA_ERR_WORKSPACE
+    assert b"static scratch" in h.pa_last_error()
+    assert h.pa_decode_step_noalloc(nul, nul, nul, nul, nul, nul, nul, nul, nul, 16, 32, 8, 96,
+                                    16, 100, 8192, 2048, 0.1, -1, PA_BF16,
+                                    nul) == PA_ERR_UNSUPPORTED
