@@ -33,6 +33,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape"
+# metric label of every other workload (the headline metric is the Llama-3-8B one)
+WORKLOAD_LABEL = {
+    "llama3_8b_bf16": "Llama-3-8B shape",
+    "opt13b_fp16": "OPT-13B shape (MHA, 40 heads, fp16)",
+    "cow_parallel_bf16": "Llama-3-8B heads, parallel sampling with shared prompt blocks",
+    "long_context_bf16": "Llama-3-8B heads, long contexts (32K-131K tokens)",
+    "tiny_fp32": "tiny fp32 case",
+}
+
+
+def metric_for(workload: str, variant: str = "") -> str:
+    if workload == "llama3_8b_bf16" and not variant:
+        return METRIC
+    label = WORKLOAD_LABEL.get(workload, workload)
+    return ("paged decode attention KV GB/s (% of HBM peak) + µs/step, " + label
+            + (f", {variant}" if variant else ""))
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_212_amd", "csrc", "pa_decode.hip")
@@ -45,6 +61,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="llama3_8b_bf16")
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--cow-literal", action="store_true",
+                    help="cow_parallel_bf16 read literally: block-aligned prompts, no parked "
+                         "forks, so the step makes no copy-on-write copy")
+    ap.add_argument("--shared-prefix", type=int, default=0, metavar="M",
+                    help="prefixes shared by groups of sequences (forks of one prompt) of at "
+                         "least M blocks are attended once per group: one "
+                         "pa_decode_step_shared per step, planned on the host before the "
+                         "timed region (0 = off)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--q-heads", type=int, default=0,
                     help="llama3_8b_bf16 with this many query heads over its 8 KV heads "
@@ -464,8 +488,15 @@ def main():
     if args.q_heads and args.workload != "llama3_8b_bf16":
         print(json.dumps({"error": "--q-heads applies to the llama3_8b_bf16 workload"}))
         sys.exit(2)
-    case = make_case(args.workload, device=dev,
-                     **({"q_heads": args.q_heads} if args.q_heads else {}))
+    if args.cow_literal and args.workload != "cow_parallel_bf16":
+        print(json.dumps({"error": "--cow-literal applies to the cow_parallel_bf16 workload"}))
+        sys.exit(2)
+    kw = {"q_heads": args.q_heads} if args.q_heads else {}
+    if args.cow_literal:
+        kw["parked_forks"] = False
+    case = make_case(args.workload, device=dev, **kw)
+    if args.cow_literal:
+        case.name = f"{case.name}_literal"
     if args.q_heads:
         case.name = f"{case.name}_hq{args.q_heads}"
     quant = args.kv_cache is not None
@@ -474,6 +505,11 @@ def main():
     window = int(args.window)
     if window and quant:
         print(json.dumps({"error": "--window takes fp32/fp16/bf16 pools"}))
+        sys.exit(2)
+    if args.shared_prefix and (quant or window or args.mode != "step" or
+                               args.partition_size not in (None, 0, -1)):
+        print(json.dumps({"error": "--shared-prefix takes the fused step over fp16/bf16 pools, "
+                                   "no window, the even split"}))
         sys.exit(2)
     if window:
         case = windowed(case, window, reuse=False)
@@ -531,6 +567,18 @@ def main():
     ws = pk.ops.decode_workspace(B, Hq, Hkv, D, plan.max_context_len, P, pool_td, dev)
     P_used = pk.ops.decode_partition_size(B, Hq, Hkv, D, plan.max_context_len, P, pool_td)
     ncow = int(plan.cows.shape[0])
+    shared = None
+    if args.shared_prefix:
+        # the host plan of the shared prefixes, timed on its own (it is made once
+        # per step for all layers, from the tables the reservation exported)
+        t0 = time.perf_counter()
+        sh_pre, sh_rows, sh_start, sh_mg = pk.ops.shared_prefix_plan(plan.tables, plan.lens,
+                                                                     args.shared_prefix)
+        host_shared_plan_us = (time.perf_counter() - t0) * 1e6
+        shared = cache.shared_plan(plan, args.shared_prefix)
+        ws_sh = pk.ops.decode_shared_workspace(B, Hq, Hkv, D, plan.max_context_len, pool_td,
+                                               dev)
+        P_used = -1
     torch.cuda.synchronize()
 
     # Pre-bound C calls: the loop below only issues launches.
@@ -558,6 +606,18 @@ def main():
             calls.append(((kp.data_ptr(), vp.data_ptr(), plan.d_cows.data_ptr(), ncow, N, Hkv,
                            D, 16, dt, stream), dec, None, None))
             continue
+        if shared is not None:
+            # pa_decode_step_shared: prefix pass + the rest on the even split + merge
+            pre_d, rows_d, start_d, mg = shared
+            dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                   k_new.data_ptr(), v_new.data_ptr(), plan.d_slots.data_ptr(),
+                   plan.d_tables.data_ptr(), plan.d_lens.data_ptr(), pre_d.data_ptr(),
+                   rows_d.data_ptr() if rows_d.numel() else None, start_d.data_ptr(),
+                   start_d.numel() - 1, rows_d.numel(), mg, B, Hq, Hkv, D, 16, N, MB,
+                   plan.max_context_len, case.scale, dt, ws_sh.data_ptr(), ws_sh.numel(), stream)
+            calls.append(((kp.data_ptr(), vp.data_ptr(), plan.d_cows.data_ptr(), ncow, N, Hkv,
+                           D, 16, dt, stream), dec, None, None))
+            continue
         # pa_decode_step: append of the step's tokens + attention (+ merge)
         dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), k_new.data_ptr(),
                v_new.data_ptr(), plan.d_slots.data_ptr(), plan.d_tables.data_ptr(),
@@ -577,17 +637,23 @@ def main():
     f_app, f_part, f_merge = L.pa_cache_append, L.pa_decode_partial, L.pa_decode_merge
     f_time = L.pa_time_next_attention
     f_step_quant, f_step_window = L.pa_decode_step_quant, L.pa_decode_step_window
-    mode = "quant" if quant else "window" if window else args.mode
+    f_step_shared = L.pa_decode_step_shared if shared is not None else None
+    mode = ("quant" if quant else "window" if window else "shared" if shared is not None
+            else args.mode)
 
     def step(i, ev=None, with_copy=True):
         c_copy, c_dec, c_app, c_dec_sep = calls[i % len(calls)]
         if ncow and with_copy:
             check(f_copy(*c_copy), "pa_copy_blocks")
-        if mode in ("quant", "window"):
+        if mode in ("quant", "window", "shared"):
             if ev is not None:
+                # shared: the events land on the even split's kernel (the
+                # private rest), not on the prefix pass before it
                 check(f_time(ev[0].cuda_event, ev[1].cuda_event), "pa_time_next_attention")
             if mode == "quant":
                 check(f_step_quant(*c_dec), "pa_decode_step_quant")
+            elif mode == "shared":
+                check(f_step_shared(*c_dec), "pa_decode_step_shared")
             else:
                 check(f_step_window(*c_dec), "pa_decode_step_window")
             return
@@ -669,7 +735,18 @@ def main():
             np.maximum.at(fill, plan.tables[b_i, :nb], f)
     kv_unique = int(fill.sum()) * Hkv * 2 * D * case.elt_bytes
     stream_ctx = stream_read_context(torch, dev)
-    res = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+    variant = ", ".join(x for x in (
+        f"{Hq} query heads" if args.q_heads else "",
+        f"{case.kv_dtype} KV codes" if quant else "",
+        f"sliding window {window}" if window else "",
+        "literal reading (no copies)" if args.cow_literal else "",
+        f"shared prefixes of >= {args.shared_prefix} blocks attended once per group"
+        if shared is not None else "") if x)
+    # paging waste: unused slots in the blocks the batch's tables hold
+    bm_stats = cache.bm.stats()
+    slack = int(bm_stats["slack_slots"])
+    res = {"metric": metric_for(args.workload, variant), "value": round(value, 2),
+           "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": case.dtype, "data": "synthetic",
@@ -692,9 +769,25 @@ def main():
            "value_unique_gbs": round(kv_unique / (ms_step * 1e-3) / 1e9, 2),
            "stream_read_context": stream_ctx,
            "host_plan_us": round(host_plan_us, 1),
-           "pool_blocks_used": int(cache.bm.stats()["used_blocks"]),
+           "pool_blocks_used": int(bm_stats["used_blocks"]),
+           "paging_slack_slots": slack,
+           "paging_waste_pct": round(100.0 * slack / max(1, slack + int(bm_stats["tokens"])), 3),
+           "paging_max_slack_per_seq": int(max(-(-int(x) // 16) * 16 - int(x)
+                                               for x in case.lens)),
            "pool_blocks_without_window": int(sum(-(-int(x) // 16) for x in case.lens)),
            "wall_ms_timed_region": round(wall_ms, 3)}
+    if shared is not None:
+        ng = len(sh_start) - 1
+        pre_tok = int(sum(int(sh_pre[int(sh_rows[sh_start[g]])]) for g in range(ng)))
+        res["shared_prefix"] = {
+            "groups": ng, "members": int(len(sh_rows)), "largest_group": int(sh_mg),
+            "min_shared_blocks": args.shared_prefix,
+            # K/V read by the prefix pass: each group's prefix once
+            "prefix_kv_bytes": pre_tok * Hkv * 2 * D * case.elt_bytes,
+            # K/V read by the even split: every sequence after its prefix
+            "rest_kv_bytes": int((case.attended_lens().astype(np.int64) -
+                                  sh_pre.astype(np.int64)).sum()) * Hkv * 2 * D * case.elt_bytes,
+            "host_plan_us": round(host_shared_plan_us, 1)}
     if evs:
         kern_us = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
         part_ms = dec_ms = float(kern_us.mean()) * 1e-3
@@ -708,13 +801,18 @@ def main():
                                                          np.percentile(per, [10, 50, 90])]
         res["us_per_step_with_kernel_events"] = round(ms_step_ev * 1e3, 3)
         # table entries walked: from the block holding the first attended position
+        att = case.attended_lens().astype(np.int64)
+        if shared is not None:
+            # the even split's kernel attends each sequence after its shared prefix
+            att = att - sh_pre.astype(np.int64)
         tables_bytes = int(sum(-(-int(x) // 16) - (int(x) - int(a)) // 16
-                               for x, a in zip(case.lens, case.attended_lens()))) * 4
+                               for x, a in zip(case.lens, att))) * 4
         # K/V of every attended token, q, the table entries walked, the lengths and
         # the fp32 output; in the phased step the kernel also reads the new
         # tokens (k_new, v_new) and the slot indices
-        alg = kv_bytes + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
-        if mode in ("phased", "quant", "window", "step"):
+        kv_att = int(att.sum()) * Hkv * 2 * D * case.elt_bytes
+        alg = kv_att + q.numel() * q.element_size() + tables_bytes + B * 4 + out.numel() * 4
+        if mode in ("phased", "quant", "window", "step", "shared"):
             alg += 2 * k_new.numel() * k_new.element_size() + B * 8
         achieved = alg / (part_ms * 1e-3) / 1e9
         res["attention_kernel_us"] = round(dec_ms * 1e3, 3)
@@ -724,6 +822,9 @@ def main():
         elif mode == "window":
             kname = (f"attention kernel of pa_decode_step_window (last {window} positions; new "
                      f"tokens fused in)")
+        elif mode == "shared":
+            kname = ("attention kernel of pa_decode_step_shared (each sequence after its shared "
+                     "prefix, even split; new tokens fused in)")
         elif mode == "separate":
             kname = "attention partition kernel (pa_decode_partial)"
         elif args.mode == "phased":

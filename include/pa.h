@@ -477,6 +477,80 @@ pa_status pa_decode_step_noalloc(float* out, const void* q, void* k_pool, void* 
                                  float scale, int32_t partition_size, pa_dtype dtype,
                                  void* stream);
 
+/* Shared-prefix plan of a decode batch (host): sequences whose block tables
+ * begin with the same physical blocks hold the same tokens there (blocks are
+ * shared by forks, e.g. the samples of one prompt: page 2,
+ * hubblespacetelescope blog, section 「OSの知恵をGPUへ…」, third bullet;
+ * page 3, abeam.tech review, section 「並列サンプリングやビームサーチでの共有」),
+ * so their queries can attend those blocks together, reading each once.
+ * Sequences are grouped by their first physical block, in batch order; a
+ * group's shared prefix is the longest run of table entries common to all
+ * its members, capped so that each member keeps at least its last position
+ * after it; groups of one member or with fewer than min_shared_blocks
+ * shared blocks are dropped.  Inputs (host): tables [n][max_blocks] and
+ * lens [n] as exported by pa_bm_block_tables for the step (after its
+ * reservation).  Outputs (host): prefix_len_out [n] = tokens of the
+ * sequence's shared prefix (a multiple of block_size, 0 = none);
+ * group_rows_out [n] = the grouped members' batch indices, group g being
+ * group_rows_out[group_start_out[g] .. group_start_out[g+1]-1];
+ * group_start_out [n+1]; *num_groups_out; *max_group_out = the largest
+ * group.  PA_ERR_INVALID_ARG for bad sizes or NULL pointers. */
+pa_status pa_shared_prefix_plan(const int32_t* tables, const int32_t* lens, int32_t n,
+                                int32_t max_blocks, int32_t block_size,
+                                int32_t min_shared_blocks, int32_t* prefix_len_out,
+                                int32_t* group_rows_out, int32_t* group_start_out,
+                                int32_t* num_groups_out, int32_t* max_group_out);
+
+/* Workspace bytes of pa_decode_step_shared (0 for invalid arguments). */
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_context_len, pa_dtype dtype);
+
+/* pa_decode_step where groups of sequences share a prefix of blocks (a
+ * plan from pa_shared_prefix_plan, on the device): the result of
+ * pa_decode_step, with each shared block read once per KV head instead of
+ * once per sequence (page 2, hubblespacetelescope blog, section
+ * 「OSの知恵をGPUへ…」, third bullet: shared blocks are held once by
+ * reference count; page 3, abeam.tech review, section
+ * 「並列サンプリングやビームサーチでの共有」).  Three passes on `stream`:
+ *   1. per group and KV head, the members' queries (members x query heads
+ *      of that KV head) attend the shared prefix [0, prefix_len) through
+ *      the first member's table, on the matrix cores; the normalised rows
+ *      and their softmax maxima and sums go to the workspace;
+ *   2. the even split attends each sequence from its prefix_len (0 for
+ *      sequences in no group) to its end, with the step's new tokens fused
+ *      in as in pa_decode_step;
+ *   3. the log-sum-exp merge folds the prefix rows with the rest.
+ *   prefix_len: device int32 [num_seqs], a multiple of 16 below
+ *   context_lens[b] for members, 0 otherwise; group_rows: device int32
+ *   [num_rows] batch indices; group_start: device int32 [num_groups + 1],
+ *   non-decreasing from 0 to num_rows; all members of a group have the same
+ *   prefix_len and the same table entries before it (the plan guarantees
+ *   it).  These are checked on the device: a sequence with a nonzero
+ *   prefix_len gets a NaN row when that length is not a multiple of 16
+ *   below its context length, when it is in no group, when its prefix_len
+ *   or prefix blocks differ from its group's first member's, or when that
+ *   member's length or table is out of bounds.  max_group_size: the largest
+ *   group.  workspace: at least pa_decode_shared_workspace_bytes(...)
+ *   bytes, 256-byte aligned; needs no initialisation; calls that share it
+ *   must not overlap.
+ * Other arguments and the slot rules as for pa_decode_step.  Supported:
+ * fp16/bf16 pools on the matrix cores (PA_ERR_UNSUPPORTED for other dtypes
+ * or under pa_set_decode_kernel(PA_KERNEL_GENERIC)), block_size 16, head_dim
+ * 64 or 128, G <= 16.  With no group it is pa_decode_step on the even
+ * split. */
+pa_status pa_decode_step_shared(float* out, const void* q, void* k_pool, void* v_pool,
+                                const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* prefix_len,
+                                const int32_t* group_rows, const int32_t* group_start,
+                                int32_t num_groups, int32_t num_rows, int32_t max_group_size,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Attention of a chunk of query tokens per sequence over the paged cache
  * (prefill of a prompt, chunked prefill on top of a cached prefix, or decode
  * with one token).  Sequence b holds L = context_lens[b] tokens in its blocks

@@ -82,6 +82,12 @@ SIGNATURES = {
     "pa_decode_step_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                          C.c_int, _vp]),
+    "pa_shared_prefix_plan": (C.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _p_i32,
+                                        _p_i32]),
+    "pa_decode_shared_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, C.c_int]),
+    "pa_decode_step_shared": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _f32, C.c_int, _vp, _sz, _vp]),
     "pa_decode_quant": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _f32, _i32, C.c_int, _f32, _f32, _vp, _sz,
                                   _vp]),

@@ -119,16 +119,25 @@ class PagedKVCache:
                         self._d(slots), self._d(cows.reshape(-1, 2)), self._d(tables),
                         self._d(lens))
 
+    def shared_plan(self, plan: StepPlan, min_shared_blocks: int = 4):
+        """Groups of the step's sequences that share a prefix of blocks
+        (pa_shared_prefix_plan on the step's tables), on the device:
+        (prefix_len, group_rows, group_start, max_group)."""
+        pre, rows, start, mg = ops.shared_prefix_plan(plan.tables, plan.lens, min_shared_blocks)
+        return self._d(pre), self._d(rows), self._d(start), mg
+
     def step(self, plan: StepPlan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
              out: torch.Tensor | None = None, scale=None, partition_size: int = 0,
-             workspace=None, stream=None, fused=True, window: int = 0):
+             workspace=None, stream=None, fused=True, window: int = 0, shared=None):
         """Copy-on-write, append the new tokens, then decode attention (all on device).
 
         fused: True -> one pa_decode_step call; "phased" -> pa_decode_step_partial
         then pa_decode_step_merge; False -> pa_cache_append then pa_decode.  A
         quantized cache: pa_decode_step_quant (fused) or pa_cache_append_quant
         then pa_decode_quant (False).  window > 0: sliding-window attention
-        (pa_decode_step_window, or pa_cache_append then pa_decode_window)."""
+        (pa_decode_step_window, or pa_cache_append then pa_decode_window).
+        shared: a shared_plan(...) result: pa_decode_step_shared, each shared
+        prefix attended once per group (fp16/bf16 pools, fused step)."""
         if plan.cows.shape[0]:
             ops.copy_blocks(self.k_pool, self.v_pool, plan.d_cows, stream)
         if out is None:
@@ -140,6 +149,14 @@ class PagedKVCache:
             else:
                 with torch.cuda.stream(stream):
                     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if shared is not None:
+            if window or self.cache_dtype is not None or fused is not True:
+                raise ValueError("shared prefixes take the fused step over fp16/bf16 pools")
+            pre, rows, start, mg = shared
+            ops.decode_step_shared(out, q, self.k_pool, self.v_pool, k_new, v_new, plan.d_slots,
+                                   plan.d_tables, plan.d_lens, plan.max_context_len, pre, rows,
+                                   start, mg, scale, workspace, stream)
+            return out
         if window:
             # sliding window: fused step, or append then windowed decode
             if self.cache_dtype is not None:

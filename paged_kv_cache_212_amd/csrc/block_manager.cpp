@@ -351,3 +351,75 @@ extern "C" pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out) {
   *out = st;
   return pa::ok();
 }
+
+// Shared-prefix plan of a decode batch (host).  Sequences whose block tables
+// begin with the same physical blocks hold the same tokens there (a block is
+// shared only by forks, which share their parent's positions), so their
+// queries can attend those blocks together, each block read once.  Sequences
+// are grouped by their first physical block, in batch order; a group's
+// shared prefix is the longest run of equal entries common to all its
+// members, capped so that every member keeps at least one position of its
+// own (the step's new token) after it.  Groups with fewer than two members
+// or a prefix under min_shared_blocks are dropped.
+extern "C" pa_status pa_shared_prefix_plan(const int32_t* tables, const int32_t* lens, int32_t n,
+                                           int32_t max_blocks, int32_t block_size,
+                                           int32_t min_shared_blocks, int32_t* prefix_len_out,
+                                           int32_t* group_rows_out, int32_t* group_start_out,
+                                           int32_t* num_groups_out, int32_t* max_group_out) {
+  if (n < 0 || max_blocks < 0 || block_size <= 0 || min_shared_blocks < 1)
+    return fail(PA_ERR_INVALID_ARG, "pa_shared_prefix_plan: bad sizes");
+  if (n > 0 && (!tables || !lens || !prefix_len_out || !group_rows_out || !group_start_out ||
+                !num_groups_out || !max_group_out))
+    return fail(PA_ERR_INVALID_ARG, "pa_shared_prefix_plan: NULL pointer");
+  if (n == 0) {
+    if (num_groups_out) *num_groups_out = 0;
+    if (max_group_out) *max_group_out = 0;
+    if (group_start_out) group_start_out[0] = 0;
+    return pa::ok();
+  }
+  std::vector<int32_t> order;                       // first blocks, in order of appearance
+  std::unordered_map<int32_t, std::vector<int32_t>> by_first;
+  for (int32_t i = 0; i < n; ++i) {
+    prefix_len_out[i] = 0;
+    const int64_t L = lens[i];
+    if (max_blocks < 1 || L <= static_cast<int64_t>(block_size) * min_shared_blocks) continue;
+    const int32_t first = tables[static_cast<int64_t>(i) * max_blocks];
+    if (first < 0) continue;
+    auto it = by_first.find(first);
+    if (it == by_first.end()) {
+      order.push_back(first);
+      by_first.emplace(first, std::vector<int32_t>{i});
+    } else {
+      it->second.push_back(i);
+    }
+  }
+  int32_t ng = 0, nrows = 0, max_group = 0;
+  group_start_out[0] = 0;
+  for (int32_t first : order) {
+    const std::vector<int32_t>& m = by_first[first];
+    if (m.size() < 2) continue;
+    // every member keeps at least one own position after the prefix
+    int64_t cap = max_blocks;
+    for (int32_t i : m) cap = std::min<int64_t>(cap, (static_cast<int64_t>(lens[i]) - 1) / block_size);
+    int64_t P = 0;
+    while (P < cap) {
+      const int32_t e = tables[static_cast<int64_t>(m[0]) * max_blocks + P];
+      if (e < 0) break;
+      bool same = true;
+      for (size_t k = 1; k < m.size() && same; ++k)
+        same = tables[static_cast<int64_t>(m[k]) * max_blocks + P] == e;
+      if (!same) break;
+      ++P;
+    }
+    if (P < min_shared_blocks) continue;
+    for (int32_t i : m) {
+      prefix_len_out[i] = static_cast<int32_t>(P * block_size);
+      group_rows_out[nrows++] = i;
+    }
+    max_group = std::max<int32_t>(max_group, static_cast<int32_t>(m.size()));
+    group_start_out[++ng] = nrows;
+  }
+  *num_groups_out = ng;
+  *max_group_out = max_group;
+  return pa::ok();
+}

@@ -70,18 +70,40 @@ struct Params {
   float out_scale;     // factor of the final rows (V scale of a quantized cache, else 1)
   float enc_k, enc_v;  // quantized cache, fused append: fp32 reciprocals of the K/V scales
   int window;          // sliding window: attend the last `window` positions (0: all)
+  // Shared prefixes (pa_decode_step_shared): prefix[b] positions of sequence
+  // b were attended by the prefix pass in pre_pieces key ranges, whose
+  // partials are in slot p of pre_out (unnormalised weighted sums of V) and
+  // pre_ml (log2-domain max and sum of 2^(s - max)), each slot it wrote
+  // stamped with the call's epoch; the even split attends the rest and the
+  // merge folds them all (null: no prefix pass).
+  const int32_t* prefix;       // [B]
+  const float* pre_out;        // [pre_pieces][B][Hq][D]
+  const float2* pre_ml;        // [pre_pieces][B][Hq]
+  const uint32_t* pre_stamp;   // [pre_pieces][B]
+  uint32_t epoch;
+  int pre_pieces;
 };
 
 __device__ inline bool len_valid(int L, const Params& pr) {
   return L >= 0 && L <= pr.max_ctx && L <= pr.max_blocks * kBlockSize;
 }
 
-// First position a sequence of length L attends: L - window with a sliding
-// window, else 0.  Table entries of blocks wholly before it are never read
-// (they may have been released).
-__device__ inline int first_pos(int L, const Params& pr) {
+// Whether `pre` is a usable shared prefix of a sequence of length L: a
+// whole number of blocks, leaving at least the sequence's last position.
+__device__ inline bool prefix_ok(int pre, int L) {
+  return pre > 0 && pre < L && pre % kBlockSize == 0;
+}
+
+// First position a sequence of length L attends: the end of its shared
+// prefix when a prefix pass attended that (pre; an unusable one counts as
+// none here, and the merge turns the row into NaN), else L - window with a
+// sliding window, else 0.  Table entries of blocks wholly before it are never
+// read (they may have been released).
+__device__ inline int first_pos(int L, const Params& pr, int pre = 0) {
+  if (prefix_ok(pre, L)) return pre;
   return pr.window > 0 ? max(0, L - pr.window) : 0;
 }
+__device__ inline int prefix_of(const Params& pr, int b) { return pr.prefix ? pr.prefix[b] : 0; }
 
 // Zero rows for empty sequences, NaN rows for sequences whose length is out of
 // the declared bounds.  Done by partition 0's workgroup only.
@@ -923,9 +945,10 @@ constexpr int kMinChunkBlocks = 8;
 // Units of U blocks of a sequence: from the block holding its first attended
 // position to its last block.
 template <int U>
-__device__ __forceinline__ int units_of(int L, const Params& pr) {
+__device__ __forceinline__ int units_of(int L, const Params& pr, int pre = 0) {
   return (len_valid(L, pr) && L > 0)
-             ? ((L + kBlockSize - 1) / kBlockSize - first_pos(L, pr) / kBlockSize + U - 1) / U
+             ? ((L + kBlockSize - 1) / kBlockSize - first_pos(L, pr, pre) / kBlockSize + U - 1) /
+                   U
              : 0;
 }
 
@@ -957,7 +980,7 @@ __device__ __forceinline__ SplitPlan split_plan(const Params& pr, int W) {
   int total = 0;
   for (int c = 0; c < pr.B; c += 64) {
     const int b = c + lane;
-    total += wave_sum(b < pr.B ? units_of<U>(pr.lens[b], pr) : 0);
+    total += wave_sum(b < pr.B ? units_of<U>(pr.lens[b], pr, prefix_of(pr, b)) : 0);
   }
   total *= pr.Hkv;
   SplitPlan sp;
@@ -975,7 +998,7 @@ __device__ __forceinline__ void locate(const Params& pr, int u, int& b_out, int&
   int carried = 0;
   for (int c = 0; c < pr.B; c += 64) {
     const int b = c + lane;
-    const int units = (b < pr.B ? units_of<U>(pr.lens[b], pr) : 0) * pr.Hkv;
+    const int units = (b < pr.B ? units_of<U>(pr.lens[b], pr, prefix_of(pr, b)) : 0) * pr.Hkv;
     const int incl = carried + wave_incl_scan(units);
     const uint64_t hit = __ballot(b < pr.B && incl > u);
     if (hit) {
@@ -1007,11 +1030,13 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
   const int W = gridDim.x * (blockDim.x >> 6);
   SplitPlan sp;
   int b, base;
-  int lens_reg = 0;
+  int lens_reg = 0, pre_reg = 0;
   if (pr.B <= 64) {
-    // one pass: the batch's lengths stay in a register for the whole kernel
+    // one pass: the batch's lengths (and shared prefixes) stay in registers
+    // for the whole kernel
     lens_reg = lane < pr.B ? pr.lens[lane] : 0;
-    const int units = (lane < pr.B ? units_of<U>(lens_reg, pr) : 0) * pr.Hkv;
+    pre_reg = (lane < pr.B && pr.prefix) ? pr.prefix[lane] : 0;
+    const int units = (lane < pr.B ? units_of<U>(lens_reg, pr, pre_reg) : 0) * pr.Hkv;
     sp.total = wave_sum(units);
     sp.C = max((kMinChunkBlocks + U - 1) / U, (sp.total + W - 1) / W);
     sp.chunks = (sp.total + sp.C - 1) / sp.C;
@@ -1029,20 +1054,24 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
   const int u_begin = w * sp.C, u_end = min(sp.total, u_begin + sp.C);
   // A segment is the part of the chunk inside one (b, g) range.
   struct Seg {
-    int b, g, base, L, nub, range_first, seg_end, blk_begin, nblk, tok_begin, tok_end;
+    int b, g, base, L, pre, nub, range_first, seg_end, blk_begin, nblk, tok_begin, tok_end;
+  };
+  auto pre_of = [&](int b) {
+    return pr.B <= 64 ? __builtin_amdgcn_readlane(pre_reg, b) : prefix_of(pr, b);
   };
   auto make_seg = [&](int u, int b, int base) {
     Seg sg;
     sg.b = b;
     sg.base = base;
     sg.L = len_of(pr, lens_reg, b);
-    sg.nub = units_of<U>(sg.L, pr);
+    sg.pre = pre_of(b);
+    sg.nub = units_of<U>(sg.L, pr, sg.pre);
     sg.g = (u - base) / sg.nub;
     const int q0 = (u - base) - sg.g * sg.nub;
     sg.range_first = base + sg.g * sg.nub;                   // first unit of (b, g)
     sg.seg_end = min(u_end, sg.range_first + sg.nub);
     const int nblk_seq = (sg.L + kBlockSize - 1) / kBlockSize;
-    sg.tok_begin = first_pos(sg.L, pr);
+    sg.tok_begin = first_pos(sg.L, pr, sg.pre);
     const int fb = sg.tok_begin / kBlockSize;                  // the range's first block
     sg.blk_begin = fb + U * q0;
     sg.nblk = min(fb + U * (q0 + sg.seg_end - u), nblk_seq) - sg.blk_begin;
@@ -1056,7 +1085,7 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
       base2 = cur.seg_end;
       do {
         ++b2;
-      } while (b2 < pr.B && units_of<U>(len_of(pr, lens_reg, b2), pr) == 0);
+      } while (b2 < pr.B && units_of<U>(len_of(pr, lens_reg, b2), pr, pre_of(b2)) == 0);
     }
     return make_seg(cur.seg_end, b2, base2);
   };
@@ -1079,7 +1108,9 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
                    pre, pr.k_new != nullptr && cur.tok_end == cur.L);
     const int first_chunk = cur.range_first / sp.C;
     const int nslots = (cur.range_first + cur.nub - 1) / sp.C - first_chunk + 1;
-    Eng::emit(pr, cur.b, cur.g, nslots == 1 ? -1 : w - first_chunk, st);
+    // a sequence with a shared prefix always leaves a partial: the merge
+    // folds it with the prefix pass's row
+    Eng::emit(pr, cur.b, cur.g, (nslots == 1 && cur.pre == 0) ? -1 : w - first_chunk, st);
     // the wave holding the range's first unit records how many slots the
     // merge has to combine
     if (cur.blk_begin == cur.tok_begin / kBlockSize && lane == 0)
@@ -1091,120 +1122,229 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of a row's partials: grid (Hq, B), D threads (thread d
-// owns output dim d of query head h of sequence b).
+// Log-sum-exp merge of a row's partials: one wave per (sequence b, query
+// head h), four heads per workgroup, grid (ceil(Hq / 4), B); lane i owns
+// output dims E*i .. E*i + E - 1 (E = D / 64).
 //   out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k
-// The length, the slot count and the first kMergeBatch slots are loaded
-// together (slots are in bounds of the row's maxP workspace slots; values of
-// slots beyond the row's count are never used), so a row with at most
-// kMergeBatch partials costs one memory round trip.  Later slots are folded
-// in batches with the running maximum rescaled.
+// The values every lane of the wave needs (the length, the slot count, the
+// slots' maxima and sums, the prefix partials' pairs) are scalar loads.  The
+// first kMergeSpec slots' weighted sums are loaded with them, before the slot
+// count is known (slots are in bounds of the row's maxP workspace slots;
+// values beyond the row's count are never used); the rest of a batch of
+// kMergeBatch, only those the row holds, once the count is in.  Later slots
+// are folded in batches with the running maximum rescaled.
 //   kSplit: slot counts come from the balanced-split kernel's counters, and
 //   the rows of empty (zeros) and out-of-bounds (NaN) sequences, which own
 //   no work there, are written here; otherwise a sequence of length L has
 //   ceil(L / P) partitions.
 // ---------------------------------------------------------------------------
 constexpr int kMergeBatch = 8;
+constexpr int kMergeSpec = 2;
+constexpr int kMergeRowsPerGroup = 4;
+
+// A value read at the same address by every lane of the wave, through the
+// scalar data cache (the address must be wave-uniform).
+template <typename V>
+__device__ __forceinline__ V uniform_load(const V* p) {
+  return *(const __attribute__((address_space(4))) V*)p;
+}
+
+// E consecutive floats of a row (E = 1 or 2).
+template <int E>
+__device__ __forceinline__ void load_row(float (&v)[E], const float* p) {
+  if constexpr (E == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+  } else {
+    v[0] = *p;
+  }
+}
+template <int E>
+__device__ __forceinline__ void store_row(float* p, const float (&v)[E]) {
+  if constexpr (E == 2)
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  else
+    *p = v[0];
+}
 
 // C: void when the pools hold 16-bit values (new tokens moved as bits), else
 // the 8-bit code format the new tokens are encoded into.
 template <int D, bool kSplit, typename C = void>
-__global__ __launch_bounds__(D) void merge_kernel(Params pr) {
+__global__ __launch_bounds__(64 * kMergeRowsPerGroup) void merge_kernel(Params pr) {
   constexpr bool kCodes = !std::is_void_v<C>;
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kMergeRowsPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (h >= pr.Hq) return;
+  const int d0 = lane * E;
   const int64_t row = static_cast<int64_t>(b) * pr.Hq + h;
-  const float* pm = pr.part_m + row * pr.maxP;
-  const float* pl = pr.part_l + row * pr.maxP;
-  const float* pa = pr.part_acc + row * pr.maxP * D + d;
-  const int L = pr.lens[b];
+  const int g = h / pr.G;
+  const int L = uniform_load(pr.lens + b);
   // maxP == 1: no workspace (every row is written final or trivial)
   const bool have_ws = pr.maxP > 1;
   const int ns_split =
-      (kSplit && have_ws) ? pr.counters[static_cast<int64_t>(b) * pr.Hkv + h / pr.G] : 0;
+      (kSplit && have_ws) ? uniform_load(pr.counters + static_cast<int64_t>(b) * pr.Hkv + g) : 0;
   const int kfirst = have_ws ? min(kMergeBatch, pr.maxP) : 0;
-  float m[kMergeBatch], l[kMergeBatch], a[kMergeBatch];
+  const float* pm = pr.part_m + row * pr.maxP;
+  const float* pl = pr.part_l + row * pr.maxP;
+  const float* pa = pr.part_acc + row * pr.maxP * D + d0;
+  float m[kMergeBatch], l[kMergeBatch], a[kMergeBatch][E];
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k) {
     if (k < kfirst) {
-      m[k] = pm[k];
-      l[k] = pl[k];
-      a[k] = pa[static_cast<int64_t>(k) * D];
+      m[k] = uniform_load(pm + k);
+      l[k] = uniform_load(pl + k);
     }
   }
-  // Fused append of pa_decode_step: the first query head's workgroup of each
-  // (sequence, KV head) writes the new token (16-bit K/V) into its slot; its
-  // loads go out with the partials'.
-  // 8-bit pools: the bf16 rows are encoded as the quantizing append encodes
-  // them (thread d < D/16 reads 16 K values for one 16-byte chunk of codes).
+#pragma unroll
+  for (int k = 0; k < kMergeSpec; ++k)
+    if (k < kfirst) load_row<E>(a[k], pa + static_cast<int64_t>(k) * D);
+  // shared prefix: the prefix pass's partials (loaded with the others; rows
+  // without a prefix do not use them)
+  const int pre = (kSplit && pr.prefix) ? uniform_load(pr.prefix + b) : 0;
+  float2 pre_ml[kMaxPrefixPieces];
+  float pre_o[kMaxPrefixPieces][E];
+  bool stamped = true;
+  if (kSplit && pr.prefix) {
+    const int64_t plane = static_cast<int64_t>(pr.B) * pr.Hq;   // rows per piece
+#pragma unroll
+    for (int p = 0; p < kMaxPrefixPieces; ++p) {
+      if (p < pr.pre_pieces) {
+        const float* ml = reinterpret_cast<const float*>(pr.pre_ml + p * plane + row);
+        pre_ml[p] = make_float2(uniform_load(ml), uniform_load(ml + 1));
+        load_row<E>(pre_o[p], pr.pre_out + (p * plane + row) * D + d0);
+        stamped = stamped &&
+                  uniform_load(pr.pre_stamp + static_cast<int64_t>(p) * pr.B + b) == pr.epoch;
+      }
+    }
+  }
+  // Fused append of pa_decode_step: the wave of the first query head of each
+  // (sequence, KV head) writes the new token into its slot; its loads go out
+  // with the partials'.  16-bit pools: lanes below D/8 move one 16-byte K
+  // chunk each, every lane its E V values.  8-bit pools: the bf16 rows are
+  // encoded as the quantizing append encodes them (lanes below D/16 read 16 K
+  // values for one 16-byte chunk of codes).
   const bool appends = pr.write_new_in_merge && h % pr.G == 0;
-  const int g = h / pr.G;
   int64_t slot = -1;
   uint4 kchunk = make_uint4(0, 0, 0, 0), kchunk2 = make_uint4(0, 0, 0, 0);
-  uint16_t vval = 0;
+  uint16_t vval[E];
   if (appends) {
-    slot = pr.slots[b];
+    slot = uniform_load(pr.slots + b);
     const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
     const uint16_t* kn = static_cast<const uint16_t*>(pr.k_new) + nrow;
     if constexpr (kCodes) {
-      if (d < D / 16) {
-        kchunk = *reinterpret_cast<const uint4*>(kn + d * 16);
-        kchunk2 = *reinterpret_cast<const uint4*>(kn + d * 16 + 8);
+      if (lane < D / 16) {
+        kchunk = *reinterpret_cast<const uint4*>(kn + lane * 16);
+        kchunk2 = *reinterpret_cast<const uint4*>(kn + lane * 16 + 8);
       }
-    } else if (d < D / 8) {
-      kchunk = *reinterpret_cast<const uint4*>(kn + d * 8);
+    } else if (lane < D / 8) {
+      kchunk = *reinterpret_cast<const uint4*>(kn + lane * 8);
     }
-    vval = static_cast<const uint16_t*>(pr.v_new)[nrow + d];
+    const uint16_t* vn = static_cast<const uint16_t*>(pr.v_new) + nrow + d0;
+    if constexpr (E == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(vn);
+      vval[0] = static_cast<uint16_t>(w & 0xFFFFu);
+      vval[1] = static_cast<uint16_t>(w >> 16);
+    } else {
+      vval[0] = vn[0];
+    }
   }
+  float* orow = pr.out + row * D + d0;
   if (!len_valid(L, pr) || L == 0) {
-    if (kSplit) pr.out[row * D + d] = (L == 0) ? 0.f : __builtin_nanf("");
+    // (an empty sequence given a shared prefix has no usable one: NaN)
+    if (kSplit) {
+      const float v = (L == 0 && pre == 0) ? 0.f : __builtin_nanf("");
+      float r[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) r[e] = v;
+      store_row<E>(orow, r);
+    }
     return;
   }
-  if (kCodes && appends && slot >= 0 &&
-      slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
+  if (appends && slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
+    const int64_t blk = slot / kBlockSize;
+    const int ts = static_cast<int>(slot % kBlockSize);
     if constexpr (kCodes) {
-      const int64_t blk = slot / kBlockSize;
-      const int ts = static_cast<int>(slot % kBlockSize);
       uint8_t* kt = static_cast<uint8_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
       uint8_t* vt = static_cast<uint8_t*>(pr.vpool_w) + tile_base(blk, g, pr.Hkv, D);
-      if (d < D / 16)
-        *reinterpret_cast<uint4*>(kt + (d * kBlockSize + ts) * 16) =
+      if (lane < D / 16)
+        *reinterpret_cast<uint4*>(kt + (lane * kBlockSize + ts) * 16) =
             make_uint4(encode4_bf16<C>(make_uint2(kchunk.x, kchunk.y), pr.enc_k),
                        encode4_bf16<C>(make_uint2(kchunk.z, kchunk.w), pr.enc_k),
                        encode4_bf16<C>(make_uint2(kchunk2.x, kchunk2.y), pr.enc_k),
                        encode4_bf16<C>(make_uint2(kchunk2.z, kchunk2.w), pr.enc_k));
-      const float vf = __uint_as_float(static_cast<uint32_t>(vval) << 16);
-      vt[d * kBlockSize + ts] = static_cast<uint8_t>(Encode<C>::pair(vf, 0.f, pr.enc_v));
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float vf = __uint_as_float(static_cast<uint32_t>(vval[e]) << 16);
+        vt[(d0 + e) * kBlockSize + ts] = static_cast<uint8_t>(Encode<C>::pair(vf, 0.f, pr.enc_v));
+      }
+    } else {
+      uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
+      uint16_t* vt = static_cast<uint16_t*>(pr.vpool_w) + tile_base(blk, g, pr.Hkv, D);
+      if (lane < D / 8) *reinterpret_cast<uint4*>(kt + (lane * kBlockSize + ts) * 8) = kchunk;
+#pragma unroll
+      for (int e = 0; e < E; ++e) vt[((ts >> 3) * D + d0 + e) * 8 + (ts & 7)] = vval[e];
     }
-  } else if (appends && slot >= 0 && slot < static_cast<int64_t>(pr.num_blocks) * kBlockSize) {
-    const int64_t blk = slot / kBlockSize;
-    const int ts = static_cast<int>(slot % kBlockSize);
-    uint16_t* kt = static_cast<uint16_t*>(pr.kpool_w) + tile_base(blk, g, pr.Hkv, D);
-    uint16_t* vt = static_cast<uint16_t*>(pr.vpool_w) + tile_base(blk, g, pr.Hkv, D);
-    if (d < D / 8) *reinterpret_cast<uint4*>(kt + (d * kBlockSize + ts) * 8) = kchunk;
-    vt[((ts >> 3) * D + d) * 8 + (ts & 7)] = vval;
   }
   const int ns = kSplit ? ns_split : (L + pr.P - 1) / pr.P - first_pos(L, pr) / pr.P;
-  if (ns <= 1 || !have_ws) return;                            // written final
+  const bool has_pre = pre != 0;
+  // an unusable prefix length, or a prefix the prefix pass did not attend
+  // in this call (the sequence in no group, or its prefix not its group's)
+  if (has_pre && (!prefix_ok(pre, L) || !stamped)) {
+    float r[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) r[e] = __builtin_nanf("");
+    store_row<E>(orow, r);
+    return;
+  }
+  if (!has_pre && (ns <= 1 || !have_ws)) return;             // written final
+  // the rest of the first batch: only the slots the row holds
+#pragma unroll
+  for (int k = kMergeSpec; k < kMergeBatch; ++k)
+    if (k < kfirst && k < ns) load_row<E>(a[k], pa + static_cast<int64_t>(k) * D);
   float M = -INFINITY;
+  if (has_pre) {
+#pragma unroll
+    for (int p = 0; p < kMaxPrefixPieces; ++p)
+      if (p < pr.pre_pieces) M = fmaxf(M, pre_ml[p].x);
+  }
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k)
     if (k < ns) M = fmaxf(M, m[k]);
-  float num = 0.f, den = 0.f;
+  float num[E], den = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) num[e] = 0.f;
+  // each prefix piece counts as one more partial (an empty piece has max
+  // -inf and sum 0: weight 0)
+  if (has_pre) {
+#pragma unroll
+    for (int p = 0; p < kMaxPrefixPieces; ++p) {
+      if (p < pr.pre_pieces) {
+        const float wgt = exp2f(pre_ml[p].x - M);
+        den = fmaf(wgt, pre_ml[p].y, den);
+#pragma unroll
+        for (int e = 0; e < E; ++e) num[e] = fmaf(wgt, pre_o[p][e], num[e]);
+      }
+    }
+  }
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k) {
     if (k < ns) {
       const float wgt = exp2f(m[k] - M);
       den = fmaf(wgt, l[k], den);
-      num = fmaf(wgt, a[k], num);
+#pragma unroll
+      for (int e = 0; e < E; ++e) num[e] = fmaf(wgt, a[k][e], num[e]);
     }
   }
   for (int k0 = kMergeBatch; k0 < ns; k0 += kMergeBatch) {
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       if (k0 + k < ns) {
-        m[k] = pm[k0 + k];
-        l[k] = pl[k0 + k];
-        a[k] = pa[static_cast<int64_t>(k0 + k) * D];
+        m[k] = uniform_load(pm + k0 + k);
+        l[k] = uniform_load(pl + k0 + k);
+        load_row<E>(a[k], pa + static_cast<int64_t>(k0 + k) * D);
       }
     }
     float Mb = M;
@@ -1212,7 +1352,8 @@ __global__ __launch_bounds__(D) void merge_kernel(Params pr) {
     for (int k = 0; k < kMergeBatch; ++k)
       if (k0 + k < ns) Mb = fmaxf(Mb, m[k]);
     const float r = exp2f(M - Mb);
-    num *= r;
+#pragma unroll
+    for (int e = 0; e < E; ++e) num[e] *= r;
     den *= r;
     M = Mb;
 #pragma unroll
@@ -1220,11 +1361,22 @@ __global__ __launch_bounds__(D) void merge_kernel(Params pr) {
       if (k0 + k < ns) {
         const float wgt = exp2f(m[k] - M);
         den = fmaf(wgt, l[k], den);
-        num = fmaf(wgt, a[k], num);
+#pragma unroll
+        for (int e = 0; e < E; ++e) num[e] = fmaf(wgt, a[k][e], num[e]);
       }
     }
   }
-  pr.out[row * D + d] = (num / den) * pr.out_scale;
+  float r[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) r[e] = (num[e] / den) * pr.out_scale;
+  store_row<E>(orow, r);
+}
+
+// Merge launch: one wave per (sequence, query head).
+template <int D, bool kSplit, typename C = void>
+void launch_merge(const Params& pr, hipStream_t s) {
+  const dim3 grid((pr.Hq + kMergeRowsPerGroup - 1) / kMergeRowsPerGroup, pr.B);
+  merge_kernel<D, kSplit, C><<<grid, 64 * kMergeRowsPerGroup, 0, s>>>(pr);
 }
 
 // Kernel family of the decode calls, set by pa_set_decode_kernel (process
@@ -1391,12 +1543,12 @@ void launch_code_phases(const Params& pr, const LaunchPlan& lp, bool first, bool
                         hipStream_t s) {
   if (first) launch_matrix<C, D>(pr, lp.split, lp.W, pr.k_new != nullptr, s);
   if (lp.split) {
-    if (second) merge_kernel<D, true, C><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
+    if (second) launch_merge<D, true, C>(pr, s);
     return;
   }
   // with the step's new tokens the merge kernel always runs: it writes them
   if (second && (pr.maxP > 1 || pr.write_new_in_merge))
-    merge_kernel<D, false, C><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
+    launch_merge<D, false, C>(pr, s);
 }
 
 template <int D>
@@ -1413,7 +1565,7 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
       else
         launch_matrix<BF16, D>(pr, true, lp.W, false, s);
     }
-    if (second) merge_kernel<D, true><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
+    if (second) launch_merge<D, true>(pr, s);
     return;
   }
   if (first) {
@@ -1423,7 +1575,7 @@ void launch_phases(const Params& pr, pa_dtype dt, const LaunchPlan& lp, Phase ph
       case PA_BF16: launch_partitions<BF16, D>(pr, lp.generic, pr.k_new != nullptr, s); break;
     }
   }
-  if (second && pr.maxP > 1) merge_kernel<D, false><<<dim3(pr.Hq, pr.B), D, 0, s>>>(pr);
+  if (second && pr.maxP > 1) launch_merge<D, false>(pr, s);
 }
 
 // Whether the partition kernel of this plan appends the step's new tokens
@@ -1443,8 +1595,19 @@ struct CodeScales {
   float v_scale;
 };
 
+// Shared prefixes of pa_decode_step_shared: the prefix pass's outputs.
+struct SharedPrefix {
+  const int32_t* prefix;
+  const float* pre_out;
+  const float2* pre_ml;
+  const uint32_t* pre_stamp;
+  uint32_t epoch;
+  int pieces;
+  hipEvent_t join;   // recorded after the prefix pass on another stream: the merge waits
+};
+
 pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeScales* cs,
-                     int32_t window, float* out, const void* q,
+                     int32_t window, const SharedPrefix* shp, float* out, const void* q,
                      const void* k_pool, const void* v_pool, const int32_t* block_tables,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -1496,6 +1659,9 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
     return fail(PA_ERR_INVALID_ARG, "%s: k_new and v_new must be 16-byte aligned", fn);
   const LaunchPlan lp = make_plan(max_context_len, partition_size, dtype,
                                   generic_selected());
+  if (shp && !lp.split)
+    return fail(PA_ERR_UNSUPPORTED, "%s: shared prefixes need the even split on the matrix cores",
+                fn);
   const size_t need = workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
   if (need > 0 && (!workspace || workspace_bytes_given < need))
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -1525,6 +1691,14 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   pr.scale_log2 = (cs ? scale * cs->k_scale : scale) * kLog2e;
   pr.out_scale = cs ? cs->v_scale : 1.0f;
   pr.window = window;
+  if (shp) {
+    pr.prefix = shp->prefix;
+    pr.pre_out = shp->pre_out;
+    pr.pre_ml = shp->pre_ml;
+    pr.pre_stamp = shp->pre_stamp;
+    pr.epoch = shp->epoch;
+    pr.pre_pieces = shp->pieces;
+  }
   if (need > 0) {
     const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * lp.maxP;
     char* ws = static_cast<char*>(workspace);
@@ -1564,10 +1738,22 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
       if (st != PA_OK) return st;
     }
   }
-  if (head_dim == 64)
-    launch_phases<64>(pr, dtype, lp, ph, s);
-  else
-    launch_phases<128>(pr, dtype, lp, ph, s);
+  auto phases = [&](Phase p) {
+    if (head_dim == 64)
+      launch_phases<64>(pr, dtype, lp, p, s);
+    else
+      launch_phases<128>(pr, dtype, lp, p, s);
+  };
+  if (shp && shp->join && ph == Phase::kBoth) {
+    // the prefix pass runs beside the attention kernel; the merge needs both
+    phases(Phase::kPartitions);
+    const hipError_t e = hipStreamWaitEvent(s, shp->join, 0);
+    if (e != hipSuccess)
+      return fail(PA_ERR_HIP, "%s: hipStreamWaitEvent: %s", fn, hipGetErrorString(e));
+    phases(Phase::kMerge);
+  } else {
+    phases(ph);
+  }
   return launch_status(fn);
 }
 
@@ -1664,15 +1850,15 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
       partition_size, dtype, workspace, workspace_bytes_given, stream
 
 extern "C" pa_status pa_decode(PA_DECODE_ARGS) {
-  return run_decode("pa_decode", Phase::kBoth, nullptr, nullptr, 0, PA_DECODE_FWD);
+  return run_decode("pa_decode", Phase::kBoth, nullptr, nullptr, 0, nullptr, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_partial(PA_DECODE_ARGS) {
-  return run_decode("pa_decode_partial", Phase::kPartitions, nullptr, nullptr, 0, PA_DECODE_FWD);
+  return run_decode("pa_decode_partial", Phase::kPartitions, nullptr, nullptr, 0, nullptr, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_merge(PA_DECODE_ARGS) {
-  return run_decode("pa_decode_merge", Phase::kMerge, nullptr, nullptr, 0, PA_DECODE_FWD);
+  return run_decode("pa_decode_merge", Phase::kMerge, nullptr, nullptr, 0, nullptr, PA_DECODE_FWD);
 }
 
 #define PA_STEP_ARGS                                                                        \
@@ -1689,7 +1875,7 @@ extern "C" pa_status pa_decode_merge(PA_DECODE_ARGS) {
 
 extern "C" pa_status pa_decode_step(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step", Phase::kBoth, &nt, nullptr, 0, PA_STEP_FWD);
+  return run_decode("pa_decode_step", Phase::kBoth, &nt, nullptr, 0, nullptr, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_step_noalloc(
@@ -1715,17 +1901,181 @@ extern "C" pa_status pa_decode_step_noalloc(
   }
   const NewTokens nt{k_new, v_new, slot_mapping};
   const size_t workspace_bytes_given = workspace ? kScratchBytes : 0;
-  return run_decode(fn, Phase::kBoth, &nt, nullptr, 0, PA_STEP_FWD);
+  return run_decode(fn, Phase::kBoth, &nt, nullptr, 0, nullptr, PA_STEP_FWD);
+}
+
+// Side stream of pa_decode_step_shared, per device: the prefix pass runs on it
+// beside the attention kernel on the caller's stream (both are bound by
+// memory latency at these sizes, so running together they overlap their
+// waits).  `fork` is recorded on the caller's stream and waited by the side
+// stream; `join` is recorded after the prefix pass and waited by the
+// caller's stream before the merge.  Created on the first call on each device
+// (default priority, non-blocking), kept until the process ends.  The events
+// are shared by every call on the device, so one call's fork-to-wait sequence
+// is enqueued under g_side_mu.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxScratchDevices];
+
+// The current device's side stream (g_side_mu held by the caller).
+pa_status side_stream_of_current_device(const char* fn, SideStream** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(PA_ERR_UNSUPPORTED, "%s: device %d beyond the %d supported", fn, dev,
+                kMaxScratchDevices);
+  SideStream& ss = g_side[dev];
+  if (ss.stream == nullptr) {
+    SideStream n;
+    e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.stream) (void)hipStreamDestroy(n.stream);
+      return fail(PA_ERR_HIP, "%s: side stream set-up: %s", fn, hipGetErrorString(e));
+    }
+    ss = n;
+  }
+  *out = &ss;
+  return ok();
+}
+
+// Workspace of pa_decode_step_shared: the even split's partials, then the
+// prefix pass's rows, their (max, sum) pairs and per-sequence stamps.
+struct SharedWorkspace {
+  size_t split, pre_out, pre_ml, stamp, total;   // byte offsets of the parts; total size
+};
+SharedWorkspace shared_workspace_parts(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t max_ctx, pa_dtype dtype) {
+  SharedWorkspace w{};
+  w.split = 0;
+  w.pre_out = align256(pa_decode_workspace_bytes(B, Hq, Hkv, D, max_ctx, kEvenSplit, dtype));
+  const size_t P = kMaxPrefixPieces;
+  w.pre_ml = w.pre_out + align256(P * B * Hq * D * sizeof(float));
+  w.stamp = w.pre_ml + align256(P * B * Hq * sizeof(float2));
+  w.total = w.stamp + align256(P * B * sizeof(uint32_t));
+  return w;
+}
+
+// Epoch of each pa_decode_step_shared call (never 0: a fresh workspace may
+// hold zeros).
+std::atomic<uint32_t> g_shared_epoch{0};
+uint32_t next_epoch() {
+  uint32_t e = g_shared_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  while (e == 0) e = g_shared_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
+
+extern "C" size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim,
+                                                   int32_t max_context_len, pa_dtype dtype) {
+  if (!decode_args_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                      kEvenSplit, dtype))
+    return 0;
+  return shared_workspace_parts(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                dtype)
+      .total;
+}
+
+extern "C" pa_status pa_decode_step_shared(
+    float* out, const void* q, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+    const int64_t* slot_mapping, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* prefix_len, const int32_t* group_rows, const int32_t* group_start,
+    int32_t num_groups, int32_t num_rows, int32_t max_group_size, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+    pa_dtype dtype, void* workspace, size_t workspace_bytes_given, void* stream) {
+  const char* fn = "pa_decode_step_shared";
+  if (dtype != PA_BF16 && dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d (fp16/bf16 pools only)", fn, (int)dtype);
+  if (generic_selected())
+    return fail(PA_ERR_UNSUPPORTED, "%s: needs the matrix-core kernels", fn);
+  if (num_groups < 0 || num_rows < 0 || max_group_size < 0 || num_rows > num_seqs ||
+      (num_groups > 0 && (num_rows < 2 * num_groups || max_group_size < 2 ||
+                          max_group_size > num_rows)))
+    return fail(PA_ERR_INVALID_ARG, "%s: bad group counts", fn);
+  if (num_seqs > 0 && !decode_args_ok(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                      max_context_len, kEvenSplit, dtype))
+    return fail(PA_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (num_seqs > 0 && (!prefix_len || (num_groups > 0 && (!group_rows || !group_start))))
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL prefix or group pointer", fn);
+  const SharedWorkspace wp =
+      num_seqs > 0 ? shared_workspace_parts(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            max_context_len, dtype)
+                   : SharedWorkspace{};
+  const size_t need = wp.total;
+  if (need > 0 && (!workspace || workspace_bytes_given < need))
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes_given : size_t(0));
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  if (num_seqs == 0) return ok();
+  char* ws = static_cast<char*>(workspace);
+  float* pre_out = reinterpret_cast<float*>(ws + wp.pre_out);
+  float2* pre_ml = reinterpret_cast<float2*>(ws + wp.pre_ml);
+  uint32_t* pre_stamp = reinterpret_cast<uint32_t*>(ws + wp.stamp);
+  const uint32_t epoch = next_epoch();
+  // The step's new tokens are never in a shared prefix (every member keeps
+  // its last position, and its last block is its own), so the prefix pass
+  // reads nothing the step writes; it runs on the side stream, after the
+  // caller's earlier work (copy-on-write copies) and beside the attention
+  // kernel, and the merge waits for it.
+  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+  hipEvent_t join = nullptr;
+  const int pieces = num_groups > 0 ? shared_prefix_pieces(num_groups, max_group_size, num_q_heads,
+                                                           num_kv_heads, max_context_len)
+                                    : 1;
+  if (num_groups > 0) {
+    if (block_size != kBlockSize)
+      return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, block_size);
+    if (!q || !k_pool || !v_pool || !block_tables)
+      return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    lock.lock();
+    SideStream* ss = nullptr;
+    pa_status st = side_stream_of_current_device(fn, &ss);
+    if (st != PA_OK) return st;
+    hipStream_t cs = static_cast<hipStream_t>(stream);
+    hipError_t e = hipEventRecord(ss->fork, cs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: fork: %s", fn, hipGetErrorString(e));
+    st = launch_shared_prefix(pre_out, reinterpret_cast<float*>(pre_ml), pre_stamp, epoch, pieces, q,
+                              k_pool, v_pool, block_tables, prefix_len, group_rows, group_start,
+                              num_groups, num_rows, max_group_size, num_seqs, num_q_heads,
+                              num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
+                              max_context_len, scale, dtype, ss->stream);
+    if (st != PA_OK) return st;
+    e = hipEventRecord(ss->join, ss->stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: join: %s", fn, hipGetErrorString(e));
+    join = ss->join;
+  }
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  const SharedPrefix shp{prefix_len, pre_out, pre_ml, pre_stamp, epoch, pieces, join};
+  const int32_t partition_size = kEvenSplit;
+  const pa_status st =
+      run_decode(fn, Phase::kBoth, &nt, nullptr, 0, &shp, out, q, k_pool, v_pool, block_tables,
+                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                 num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size, dtype,
+                 workspace, wp.pre_out, stream);
+  // on an error the caller's stream still waits for the prefix pass, so
+  // nothing it frees afterwards is still being written
+  if (st != PA_OK && join) (void)hipStreamWaitEvent(static_cast<hipStream_t>(stream), join, 0);
+  return st;
 }
 
 extern "C" pa_status pa_decode_step_partial(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step_partial", Phase::kPartitions, &nt, nullptr, 0, PA_STEP_FWD);
+  return run_decode("pa_decode_step_partial", Phase::kPartitions, &nt, nullptr, 0, nullptr, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_step_merge(PA_STEP_ARGS) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step_merge", Phase::kMerge, &nt, nullptr, 0, PA_STEP_FWD);
+  return run_decode("pa_decode_step_merge", Phase::kMerge, &nt, nullptr, 0, nullptr, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_quant(float* out, const void* q, const void* k_pool,
@@ -1738,7 +2088,7 @@ extern "C" pa_status pa_decode_quant(float* out, const void* q, const void* k_po
                                      float k_scale, float v_scale, void* workspace,
                                      size_t workspace_bytes_given, void* stream) {
   const CodeScales cs{k_scale, v_scale};
-  return run_decode("pa_decode_quant", Phase::kBoth, nullptr, &cs, 0, PA_DECODE_FWD);
+  return run_decode("pa_decode_quant", Phase::kBoth, nullptr, &cs, 0, nullptr, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_step_quant(float* out, const void* q, void* k_pool, void* v_pool,
@@ -1755,7 +2105,7 @@ extern "C" pa_status pa_decode_step_quant(float* out, const void* q, void* k_poo
                                           size_t workspace_bytes_given, void* stream) {
   const NewTokens nt{k_new, v_new, slot_mapping};
   const CodeScales cs{k_scale, v_scale};
-  return run_decode("pa_decode_step_quant", Phase::kBoth, &nt, &cs, 0, PA_STEP_FWD);
+  return run_decode("pa_decode_step_quant", Phase::kBoth, &nt, &cs, 0, nullptr, PA_STEP_FWD);
 }
 
 extern "C" pa_status pa_decode_window(float* out, const void* q, const void* k_pool,
@@ -1767,7 +2117,7 @@ extern "C" pa_status pa_decode_window(float* out, const void* q, const void* k_p
                                       float scale, int32_t window, int32_t partition_size,
                                       pa_dtype dtype, void* workspace,
                                       size_t workspace_bytes_given, void* stream) {
-  return run_decode("pa_decode_window", Phase::kBoth, nullptr, nullptr, window, PA_DECODE_FWD);
+  return run_decode("pa_decode_window", Phase::kBoth, nullptr, nullptr, window, nullptr, PA_DECODE_FWD);
 }
 
 extern "C" pa_status pa_decode_step_window(float* out, const void* q, void* k_pool,
@@ -1783,5 +2133,5 @@ extern "C" pa_status pa_decode_step_window(float* out, const void* q, void* k_po
                                            void* workspace, size_t workspace_bytes_given,
                                            void* stream) {
   const NewTokens nt{k_new, v_new, slot_mapping};
-  return run_decode("pa_decode_step_window", Phase::kBoth, &nt, nullptr, window, PA_STEP_FWD);
+  return run_decode("pa_decode_step_window", Phase::kBoth, &nt, nullptr, window, nullptr, PA_STEP_FWD);
 }

@@ -36,6 +36,7 @@
 // workgroup double-buffers them in registers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -62,6 +63,26 @@ struct PrefillParams {
   int num_blocks, max_blocks, max_ctx, max_qlen;
   int ntiles;               // query tiles per sequence
   float scale_log2;
+  // Shared-prefix mode (decode over prefixes shared by several sequences):
+  // "sequence" b is piece b % pieces of group b / pieces, whose query rows
+  // qstart[g] .. qstart[g+1]-1 are batch sequences rows[r].  The group's
+  // prefix is the first prefix_len[rows[qstart[g]]] positions of that
+  // member's table; piece p takes its key blocks from p * nb / pieces to
+  // (p + 1) * nb / pieces (rounded down to even; nb blocks in all), with no
+  // causal mask (every row sees the whole piece).  Each row's partial goes
+  // to slot p at the member's batch row: the unnormalised weighted sum of V
+  // to pre_out, the log2-domain (max, sum of 2^(s - max)) to pre_ml, and the
+  // call's epoch to pre_stamp.  A row whose member is out of the batch, or
+  // whose prefix length or prefix blocks differ from the group's, is not
+  // written (nor is any row of a group whose length or table is unusable).
+  const int32_t* rows;      // [T] batch index of each row
+  const int32_t* prefix_len;  // [num_seqs] prefix tokens per batch sequence
+  float* pre_out;           // [pieces][num_seqs][Hq][D]
+  float2* pre_ml;           // [pieces][num_seqs][Hq]
+  uint32_t* pre_stamp;      // [pieces][num_seqs]
+  uint32_t epoch;
+  int num_seqs;
+  int pieces;
 };
 
 // LDS slot of V chunk c: the low three bits XORed with bits 4..6 (an
@@ -92,7 +113,7 @@ __device__ __forceinline__ float max_xor32(float v) {
 // of blocks serve all TQ tiles (TQ times the matrix work per LDS read), and
 // the tiles' softmax and matrix chains are independent, so one hides the
 // other's latency.
-template <typename T, int D, int WPG, int TQ>
+template <typename T, int D, int WPG, int TQ, bool kShared = false>
 __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void prefill_kernel(
     PrefillParams pr) {
   constexpr int NKK = D / 32;     // 32-dim steps of Q.K^T
@@ -110,20 +131,41 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
   lin /= pr.G / WPG;
   const int ngroups = (pr.ntiles + TQ - 1) / TQ;           // groups of TQ tiles
   const int tgroup = lin % ngroups, b = lin / ngroups;
+  // shared mode: piece and group
+  const int piece = kShared ? b % pr.pieces : 0;
+  const int grp = kShared ? b / pr.pieces : b;
   const int h = g * pr.G + e_head;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
 
-  const int L = pr.lens[b];
-  const int q0 = pr.qstart[b], q1 = pr.qstart[b + 1];
+  const int q0 = pr.qstart[grp], q1 = pr.qstart[grp + 1];
   const bool rows_ok = q0 >= 0 && q0 <= q1 && q1 <= pr.T;
   if (!rows_ok) return;                                   // no row can be trusted
   const int nq = q1 - q0;
   const int i0 = tgroup * TQ * kQTile;                    // first query of the wave
   if (i0 >= nq) return;
+  // batch row of query i of the sequence (shared mode: the member), and the
+  // table row the keys come from
+  auto in_batch = [&](int64_t r) { return r >= 0 && r < pr.num_seqs; };
+  const int64_t tb = kShared ? pr.rows[q0] : b;
+  if (kShared && !in_batch(tb)) return;
+  const int L = kShared ? pr.prefix_len[tb] : pr.lens[b];
   float* orow = pr.out + (static_cast<int64_t>(q0) + i0) * pr.Hq * D + static_cast<int64_t>(h) * D;
   const bool seq_ok = L >= 0 && L <= pr.max_ctx && L <= pr.max_blocks * kBlockSize &&
-                      nq <= L && nq <= pr.max_qlen;
+                      (kShared ? L >= kBlockSize && L % kBlockSize == 0 : nq <= L) &&
+                      nq <= pr.max_qlen;
+  // shared mode: an unusable group writes nothing (its rows' stamps stay old)
+  if (kShared && !seq_ok) return;
+  // Keys of the wave: positions [kb0 * 16, kb0 * 16 + Lk) (Lk = L but for a
+  // piece of a shared prefix, which is attended like a sequence of Lk
+  // positions with every query after them; a piece may be empty).
+  int kb0 = 0, Lk = L;
+  if constexpr (kShared) {
+    const int nbp = L / kBlockSize;
+    kb0 = (piece * nbp / pr.pieces) & ~1;
+    const int kb1 = piece + 1 == pr.pieces ? nbp : ((piece + 1) * nbp / pr.pieces) & ~1;
+    Lk = (kb1 - kb0) * kBlockSize;
+  }
   if (!seq_ok) {
     // length out of the declared bounds: NaN rows
     for (int idx = lane; idx < TQ * kQTile * D; idx += 64) {
@@ -133,30 +175,58 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     return;
   }
 
+  // Shared mode: the member of query 16t + n of the wave (mrow; -1 past the
+  // group or out of the batch) and whether its prefix is the group's: the
+  // same length and the same blocks (lanes j, j + 4, ... compare entries;
+  // the four lanes of a query OR their findings).
+  int mrow[TQ];
+  bool row_ok[TQ];
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) {
+    mrow[t] = -1;
+    row_ok[t] = true;
+    if constexpr (kShared) {
+      const int i = i0 + kQTile * t + n;
+      const int r = i < nq ? pr.rows[q0 + i] : -1;
+      mrow[t] = in_batch(r) ? r : -1;
+      bool diff = mrow[t] < 0 || pr.prefix_len[max(mrow[t], 0)] != L;
+      if (!diff) {
+        const int32_t* mt = pr.tables + static_cast<int64_t>(mrow[t]) * pr.max_blocks;
+        const int32_t* gt = pr.tables + tb * pr.max_blocks;
+        for (int p = j; p < L / kBlockSize; p += 4) diff |= mt[p] != gt[p];
+      }
+      int dv = diff;
+      dv |= __shfl_xor(dv, 16);
+      dv |= __shfl_xor(dv, 32);
+      row_ok[t] = dv == 0;
+    }
+  }
+
   // Q (B operand) of tile t: query 16t + n of the wave, dims kk*32 + 8j .. +8
   // (queries past the chunk read as zero; their rows are not written)
   uint4 qr[TQ][NKK];
 #pragma unroll
   for (int t = 0; t < TQ; ++t) {
     const bool real = i0 + kQTile * t + n < nq;
-    const uint16_t* qb = static_cast<const uint16_t*>(pr.q) +
-                         ((static_cast<int64_t>(q0) + i0 + kQTile * t + n) * pr.Hq + h) * D +
+    const int64_t qrow = kShared ? max(mrow[t], 0) : static_cast<int64_t>(q0) + i0 + kQTile * t + n;
+    const uint16_t* qb = static_cast<const uint16_t*>(pr.q) + ((real ? qrow : 0) * pr.Hq + h) * D +
                          j * 8;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qr[t][kk] = real ? *reinterpret_cast<const uint4*>(qb + kk * 32) : make_uint4(0, 0, 0, 0);
   }
-  const int first_pos = L - nq;                           // position of query 0
+  // position of query 0; shared mode: every query sits after the piece
+  const int first_pos = kShared ? Lk - 1 : L - nq;
   int qpos[TQ];                                           // this lane's query positions
 #pragma unroll
-  for (int t = 0; t < TQ; ++t) qpos[t] = first_pos + i0 + kQTile * t + n;
-  const int last_pos = first_pos + min(nq, i0 + TQ * kQTile) - 1;
-  const int nblk = last_pos / kBlockSize + 1;             // key blocks the wave needs
+  for (int t = 0; t < TQ; ++t) qpos[t] = kShared ? Lk - 1 : first_pos + i0 + kQTile * t + n;
+  const int last_pos = kShared ? Lk - 1 : first_pos + min(nq, i0 + TQ * kQTile) - 1;
+  const int nblk = Lk > 0 ? last_pos / kBlockSize + 1 : 0;   // key blocks the wave needs
 
   const char* kbase = static_cast<const char*>(pr.kpool) + g * kTileBytes;
   const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
   const int64_t block_stride = static_cast<int64_t>(pr.Hkv) * kTileBytes;
-  const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks;
+  const int32_t* trow = pr.tables + tb * pr.max_blocks + kb0;
   // Every table entry the tile reads is checked once, up front; an entry out
   // of the pool turns the tile's rows into NaN.  (Sequence and tile are the
   // same for every wave of a workgroup, so the early return is uniform.)
@@ -166,6 +236,7 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     if (__any(e < 0 || e >= pr.num_blocks)) bad = true;
   }
   if (bad) {
+    if (kShared) return;                                  // rows not written
     for (int idx = lane; idx < TQ * kQTile * D; idx += 64) {
       const int r = idx / D;
       if (i0 + r < nq) orow[static_cast<int64_t>(r) * pr.Hq * D + idx % D] = __builtin_nanf("");
@@ -294,8 +365,10 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
       sv[e] = s0[e];
       sv[4 + e] = s1[e];
     }
-    // the tile's first query position: first_pos + i0 + 16t (uniform)
-    if ((2 * pp + 2) * kBlockSize - 1 > first_pos + i0 + kQTile * t) {
+    // the tile's first query position: first_pos + i0 + 16t (uniform); in
+    // shared mode every query is at Lk - 1, so only keys past the piece (a
+    // re-read last block) are masked
+    if ((2 * pp + 2) * kBlockSize - 1 > (kShared ? Lk - 1 : first_pos + i0 + kQTile * t)) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         sv[e] = (kpos0 + e <= qpos[t]) ? sv[e] : -INFINITY;
@@ -340,11 +413,11 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int kb = 2 * pp + u;
-      if ((kb + 1) * kBlockSize > L) {
+      if ((kb + 1) * kBlockSize > Lk) {
         // the block reaches past the sequence: zero V of unwritten positions
         const int kp = kb * kBlockSize + 4 * j;
-        const uint32_t mx = (kp + 0 < L ? 0x0000FFFFu : 0u) | (kp + 1 < L ? 0xFFFF0000u : 0u);
-        const uint32_t my = (kp + 2 < L ? 0x0000FFFFu : 0u) | (kp + 3 < L ? 0xFFFF0000u : 0u);
+        const uint32_t mx = (kp + 0 < Lk ? 0x0000FFFFu : 0u) | (kp + 1 < Lk ? 0xFFFF0000u : 0u);
+        const uint32_t my = (kp + 2 < Lk ? 0x0000FFFFu : 0u) | (kp + 3 < Lk ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int d = 0; d < NTL; ++d) {
           vreg[u][d].x &= mx;
@@ -367,8 +440,10 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     // K of the next pair is issued once QK has consumed the current one, V of
     // the next pair once P.V has (scheduling barriers keep the compiler from
     // hoisting the loads above the matrix ops that still read the registers)
-    issue_k(0);
-    issue_v();
+    if (npair > 0) {
+      issue_k(0);
+      issue_v();
+    }
     for (int pp = 0; pp < npair; ++pp) {
       uint4 phi, plo;
       qk_softmax(pp, 0, phi, plo);
@@ -418,7 +493,7 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
       // across it
       asm volatile("s_barrier" ::: "memory");
     };
-    gload_lds(0, B0{});
+    if (npair > 0) gload_lds(0, B0{});
     if (npair > 1) gload_lds(1, B1{});
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
@@ -440,7 +515,27 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     for (int e = 0; e < 4; ++e) {
       const int r = kQTile * t + 4 * j + e;               // row of the wave's queries
       const float lr = __shfl(l, 4 * j + e);
-      if (i0 + r < nq) {
+      if constexpr (kShared) {
+        // (lane swaps in uniform control flow: a swap inside the n == 0
+        // branch below would read inactive lanes)
+        const int mr = __shfl(mrow[t], 4 * j + e);
+        const bool ok = __shfl(static_cast<int>(row_ok[t]), 4 * j + e) != 0;
+        const float mq = __shfl(m_run[t], 4 * j + e);
+        if (i0 + r < nq && ok) {
+          // the piece's partial, unnormalised (an empty piece leaves max
+          // -inf, sum 0 and a zero row, which the merge weighs as nothing)
+          const int64_t slot = static_cast<int64_t>(piece) * pr.num_seqs + mr;
+          float* po = pr.pre_out + (slot * pr.Hq + h) * D;
+#pragma unroll
+          for (int d = 0; d < NTL; ++d) po[d * 16 + n] = acc[t][d][e];
+          // the row's running max and sum (log2 domain; every lane of the
+          // row's quad holds the same max)
+          if (n == 0) {
+            pr.pre_ml[slot * pr.Hq + h] = make_float2(mq, lr);
+            if (h == 0) pr.pre_stamp[slot] = pr.epoch;
+          }
+        }
+      } else if (i0 + r < nq) {
         const float inv = 1.0f / lr;
 #pragma unroll
         for (int d = 0; d < NTL; ++d)
@@ -527,3 +622,87 @@ extern "C" pa_status pa_prefill(float* out, const void* q, const void* k_pool,
 #undef PA_PREFILL
   return launch_status(fn);
 }
+
+namespace pa {
+
+// Workgroups of the prefix pass without pieces, and the number of key-range
+// pieces it is cut into: enough for about kPrefixWorkgroups workgroups (one
+// per compute unit: measured on 32 groups of 8 with 64-block prefixes, four
+// pieces were 15% slower than one, their extra partials costing more in the
+// merge than the shorter pieces saved), at most kMaxPrefixPieces, and pieces
+// of at least 16 blocks on prefixes as long as the longest context.
+constexpr int kPrefixWorkgroups = 256;
+
+int prefix_layout(int num_groups, int max_group, int Hq, int Hkv, int* wpg, int* tq) {
+  const int G = Hq / Hkv;
+  *wpg = G % 4 == 0 ? 4 : 1;
+  const int ntiles = (max_group + kQTile - 1) / kQTile;
+  *tq = (*wpg == 4 && ntiles > 1) ? kPairTiles : 1;
+  return ntiles;
+}
+
+int shared_prefix_pieces(int num_groups, int max_group, int Hq, int Hkv, int max_ctx) {
+  int wpg = 1, tq = 1;
+  const int ntiles = prefix_layout(num_groups, max_group, Hq, Hkv, &wpg, &tq);
+  const int64_t base = static_cast<int64_t>(Hq / wpg) * ((ntiles + tq - 1) / tq) * num_groups;
+  if (base <= 0) return 1;
+  int64_t p = (kPrefixWorkgroups + base - 1) / base;
+  p = std::min<int64_t>(p, kMaxPrefixPieces);
+  p = std::min<int64_t>(p, std::max(1, max_ctx / (16 * kBlockSize)));
+  return static_cast<int>(std::max<int64_t>(p, 1));
+}
+
+pa_status launch_shared_prefix(float* pre_out, float* pre_ml, uint32_t* pre_stamp, uint32_t epoch,
+                               int pieces, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* tables, const int32_t* prefix_len,
+                               const int32_t* group_rows, const int32_t* group_start,
+                               int num_groups, int num_rows, int max_group, int num_seqs, int Hq,
+                               int Hkv, int D, int num_blocks, int max_blocks, int max_ctx,
+                               float scale, pa_dtype dtype, void* stream) {
+  PrefillParams pr{};
+  pr.q = q;
+  pr.kpool = k_pool;
+  pr.vpool = v_pool;
+  pr.tables = tables;
+  pr.qstart = group_start;
+  pr.B = num_groups * pieces;
+  pr.T = num_rows;
+  pr.Hq = Hq;
+  pr.Hkv = Hkv;
+  pr.G = Hq / Hkv;
+  pr.num_blocks = num_blocks;
+  pr.max_blocks = max_blocks;
+  pr.max_ctx = max_ctx;
+  pr.max_qlen = max_group;
+  pr.scale_log2 = scale * kLog2e;
+  pr.rows = group_rows;
+  pr.prefix_len = prefix_len;
+  pr.pre_out = pre_out;
+  pr.pre_ml = reinterpret_cast<float2*>(pre_ml);
+  pr.pre_stamp = pre_stamp;
+  pr.epoch = epoch;
+  pr.num_seqs = num_seqs;
+  pr.pieces = pieces;
+  int wpg = 1, tq = 1;
+  pr.ntiles = prefix_layout(num_groups, max_group, Hq, Hkv, &wpg, &tq);
+  const uint64_t nwg =
+      static_cast<uint64_t>(Hq / wpg) * ((pr.ntiles + tq - 1) / tq) * num_groups * pieces;
+  if (nwg == 0) return ok();
+  if (nwg > 0x7fffffffull)
+    return fail(PA_ERR_INVALID_ARG, "shared prefix pass: %llu workgroups exceed the launch limit",
+                static_cast<unsigned long long>(nwg));
+  const dim3 grid(static_cast<uint32_t>(nwg));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define PA_PREFIX(TAG, DIM)                                                                   \
+  (wpg == 1     ? (prefill_kernel<TAG, DIM, 1, 1, true><<<grid, 64, 0, s>>>(pr), 0)          \
+   : tq == 1    ? (prefill_kernel<TAG, DIM, 4, 1, true><<<grid, 256, 0, s>>>(pr), 0)         \
+                : (prefill_kernel<TAG, DIM, 4, kPairTiles, true><<<grid, 256, 0, s>>>(pr), 0))
+  if (dtype == PA_BF16)
+    D == 64 ? PA_PREFIX(BF16, 64) : PA_PREFIX(BF16, 128);
+  else
+    D == 64 ? PA_PREFIX(F16, 64) : PA_PREFIX(F16, 128);
+#undef PA_PREFIX
+  return launch_status("pa_decode_step_shared (prefix pass)");
+}
+
+}  // namespace pa

@@ -6,6 +6,8 @@ computes.
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import torch
 
 from ._lib import (PA_BF16, PA_F16, PA_F32, PA_FP8_E4M3, PA_INT8, PA_KERNEL_AUTO,
@@ -388,6 +390,80 @@ def decode_step_noalloc(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, bloc
                                        int(max_context_len), scale, int(partition_size),
                                        pa_dtype(q.dtype), _stream(stream)),
           "pa_decode_step_noalloc")
+    return out
+
+
+def shared_prefix_plan(tables, lens, min_shared_blocks=4):
+    """Host plan of pa_shared_prefix_plan over the step's tables (numpy int32
+    [n][max_blocks]) and lengths ([n]): returns (prefix_len [n], group_rows
+    [rows], group_start [groups + 1], max_group) as numpy int32 arrays."""
+    import numpy as np
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    n = int(lens.shape[0])
+    if tables.ndim != 2 or tables.shape[0] != n:
+        raise ValueError("tables must be [n][max_blocks]")
+    prefix = np.zeros(n, dtype=np.int32)
+    rows = np.zeros(max(n, 1), dtype=np.int32)
+    start = np.zeros(n + 1, dtype=np.int32)
+    ng, mg = C.c_int32(0), C.c_int32(0)
+    check(lib().pa_shared_prefix_plan(tables.ctypes.data, lens.ctypes.data, n, tables.shape[1],
+                                      BLOCK_SIZE, int(min_shared_blocks), prefix.ctypes.data,
+                                      rows.ctypes.data, start.ctypes.data, C.byref(ng),
+                                      C.byref(mg)), "pa_shared_prefix_plan")
+    return prefix, rows[:int(start[ng.value])].copy(), start[:ng.value + 1].copy(), mg.value
+
+
+def decode_shared_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                            dtype, device="cuda", stream=None):
+    n = int(lib().pa_decode_shared_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                   max_context_len, pa_dtype(dtype)))
+    if stream is None:
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def decode_step_shared(out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables,
+                       context_lens, max_context_len, prefix_len, group_rows, group_start,
+                       max_group_size, scale=None, workspace=None, stream=None):
+    """pa_decode_step with prefixes shared by groups of sequences attended once
+    per group (pa_decode_step_shared); prefix_len [B], group_rows [rows] and
+    group_start [groups + 1] are device int32 tensors from shared_prefix_plan."""
+    N, H, D = _pool_dims(k_pool, v_pool)
+    B, Hq = _check_decode_args(out, q, k_pool, block_tables, context_lens, D, k_pool.dtype)
+    if k_new.shape != (B, H, D) or v_new.shape != (B, H, D) or k_new.dtype != k_pool.dtype \
+            or v_new.dtype != k_pool.dtype:
+        raise ValueError("k_new/v_new must be [B][Hkv][D] in the pool dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (B,):
+        raise ValueError("slot_mapping must be int64 [B]")
+    for t, name in ((prefix_len, "prefix_len"), (group_rows, "group_rows"),
+                    (group_start, "group_start")):
+        if t.dtype != torch.int32 or t.dim() != 1:
+            raise ValueError(f"{name} must be a 1-D int32 tensor")
+    if prefix_len.shape != (B,):
+        raise ValueError("prefix_len must be int32 [B]")
+    ng = group_start.shape[0] - 1
+    if ng < 0:
+        raise ValueError("group_start must hold num_groups + 1 offsets")
+    scale = D ** -0.5 if scale is None else float(scale)
+    if workspace is None:
+        workspace = decode_shared_workspace(B, Hq, H, D, max_context_len, q.dtype, q.device,
+                                            stream)
+    gr = _dev(group_rows, "group_rows") if group_rows.numel() else None
+    gs = _dev(group_start, "group_start")
+    check(lib().pa_decode_step_shared(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                                      _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+                                      _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
+                                      _dev(block_tables, "block_tables"),
+                                      _dev(context_lens, "context_lens"),
+                                      _dev(prefix_len, "prefix_len"), gr, gs, ng,
+                                      int(group_rows.numel()), int(max_group_size), B, Hq, H, D,
+                                      BLOCK_SIZE, N, block_tables.shape[1],
+                                      int(max_context_len), scale, pa_dtype(q.dtype),
+                                      _dev(workspace, "workspace"),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "pa_decode_step_shared")
     return out
 
 

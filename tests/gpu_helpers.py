@@ -49,11 +49,12 @@ def say(msg):
 
 
 def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None, fused=True,
-                 pools=True):
+                 pools=True, shared=None):
     """Replays the case's set-up and runs one step on the GPU.
 
     Returns dict(plan=StepPlan, out=np fp32, k_pool/v_pool=np bits (only with
-    ``pools``), cache=PagedKVCache).
+    ``pools``), cache=PagedKVCache).  shared=m: pa_decode_step_shared with the
+    shared-prefix plan of the step (groups sharing at least m blocks).
     """
     pk = require_gpu()
     from oracle import bits_of  # test side only: stored-bit views for comparison
@@ -72,10 +73,11 @@ def run_gpu_step(case, partition_size=None, poison=True, max_blocks=None, fused=
     k_new, v_new = k_tok.index_select(0, nr), v_tok.index_select(0, nr)
     q = case.q.to(dev)
     ps = case.partition_size if partition_size is None else partition_size
+    sp = cache.shared_plan(plan, shared) if shared else None
     out = cache.step(plan, q, k_new, v_new, partition_size=ps, fused=fused,
-                     window=getattr(case, "window", 0))
+                     window=getattr(case, "window", 0), shared=sp)
     torch.cuda.synchronize()
-    res = {"plan": plan, "out": out.cpu().numpy(), "cache": cache, "q": q}
+    res = {"plan": plan, "out": out.cpu().numpy(), "cache": cache, "q": q, "shared": sp}
     if pools:
         res["k_pool"] = bits_of(cache.k_pool, case.kv_dtype)
         res["v_pool"] = bits_of(cache.v_pool, case.kv_dtype)

@@ -403,3 +403,87 @@ def test_noalloc_step_rejects_sizes_beyond_its_scratch_before_any_device_call():
     assert h.pa_decode_step_noalloc(nul, nul, nul, nul, nul, nul, nul, nul, nul, 16, 32, 8, 96,
                                     16, 100, 8192, 2048, 0.1, -1, PA_BF16,
                                     nul) == PA_ERR_UNSUPPORTED
+
+
+def _check_shared_plan(tables, lens, prefix, rows, start, mg, min_blocks=4):
+    """Properties every shared-prefix plan must have (host logic)."""
+    n = len(lens)
+    seen = set()
+    assert start[0] == 0 and np.all(np.diff(start) >= 2)
+    assert mg == (int(np.diff(start).max()) if len(start) > 1 else 0)
+    firsts = []
+    for g in range(len(start) - 1):
+        mem = rows[start[g]:start[g + 1]].tolist()
+        assert mem == sorted(mem) and not seen & set(mem)
+        seen |= set(mem)
+        P = int(prefix[mem[0]]) // 16
+        assert P >= min_blocks and all(int(prefix[i]) == 16 * P for i in mem)
+        for i in mem:
+            assert 16 * P < lens[i]                          # the member keeps its own tail
+            assert np.array_equal(tables[i, :P], tables[mem[0], :P]) and (tables[i, :P] >= 0).all()
+        # maximal: the cap is reached, or the next entries differ among members
+        cap = min((int(lens[i]) - 1) // 16 for i in mem)
+        if P < cap:
+            assert len(set(int(tables[i, P]) for i in mem)) > 1 or int(tables[mem[0], P]) < 0
+        firsts.append(int(tables[mem[0], 0]))
+    assert len(firsts) == len(set(firsts))                  # one group per first block
+    for i in range(n):
+        if i not in seen:
+            assert prefix[i] == 0
+    # sequences that start with a grouped first block are in that group
+    for i in range(n):
+        if lens[i] > 16 * min_blocks and int(tables[i, 0]) in firsts:
+            assert i in seen
+
+
+def test_shared_prefix_plan_groups_parallel_samples_by_prompt():
+    from workloads import small_case
+    case = small_case("cow_parallel_bf16")                 # 2 prompts of 64 tokens x 4 samples
+    ref = om_run(case)
+    tables, lens = ref["tables"], ref["lens"]
+    prefix, rows, start, mg = pk.ops.shared_prefix_plan(tables, lens, min_shared_blocks=2)
+    _check_shared_plan(tables, lens, prefix, rows, start, mg, 2)
+    assert len(start) - 1 == 2 and mg == 4
+    assert set(prefix.tolist()) == {64}                     # the whole block-aligned prompt
+
+
+def om_run(case):
+    from oracle import run_case
+    return run_case(case, with_pools=False)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shared_prefix_plan_properties_on_random_fork_trees(seed):
+    rng = np.random.default_rng(seed)
+    am = AllocatorModel(4000, 16, rng.permutation(4000).astype(np.int32))
+    ids = []
+    for p in range(int(rng.integers(1, 6))):
+        root = 1000 * p
+        am.add_seq(root, int(rng.integers(1, 300)))
+        ids.append(root)
+        for c in range(int(rng.integers(0, 5))):
+            parent = int(rng.choice(ids))
+            child = root + c + 1
+            am.fork(parent, child)
+            if rng.random() < 0.7:
+                am.extend(child, int(rng.integers(0, 80)))
+            ids.append(child)
+    batch = [i for i in ids if am.seq_len(i) > 0]
+    rng.shuffle(batch)
+    am.append_slots(batch)
+    mb = max(-(-am.seq_len(i) // 16) for i in batch)
+    tables, lens = am.block_tables(batch, mb)
+    for mn in (1, 2, 4):
+        prefix, rows, start, mg = pk.ops.shared_prefix_plan(tables, lens, min_shared_blocks=mn)
+        _check_shared_plan(tables, lens, prefix, rows, start, mg, mn)
+
+
+def test_shared_prefix_plan_rejects_bad_arguments():
+    h = pk.lib()
+    ng, mg = C.c_int32(), C.c_int32()
+    assert h.pa_shared_prefix_plan(None, None, -1, 4, 16, 1, None, None, None, C.byref(ng),
+                                   C.byref(mg)) == PA_ERR_INVALID_ARG
+    assert h.pa_shared_prefix_plan(None, None, 3, 4, 16, 1, None, None, None, C.byref(ng),
+                                   C.byref(mg)) == PA_ERR_INVALID_ARG
+    assert h.pa_shared_prefix_plan(None, None, 3, 4, 16, 0, None, None, None, C.byref(ng),
+                                   C.byref(mg)) == PA_ERR_INVALID_ARG
