@@ -18,31 +18,88 @@
 namespace pa {
 namespace {
 
+// Whether the x-token group holding `slot` (x = tokens per 16-byte chunk) is
+// appended whole by this call, in order, by consecutive rows: row i holds
+// token slot % x of the group, so rows i - slot % x ... i - slot % x + x - 1
+// must hold the group's slots one after the other.  Such a group is written
+// by its first row in whole 16-byte chunks (x tokens of one dim of V, and x
+// consecutive K chunks: whole lines), the other rows skip it; any other
+// token is written alone, V element by element.  (A run of appended tokens
+// that fills whole groups, as a prompt or a prefill chunk does, thus writes
+// every line of its tiles once and whole.)
+template <int X>
+__device__ inline bool whole_group(const int64_t* __restrict__ slots, int64_t i, int64_t n,
+                                   int64_t slot) {
+  const int k = static_cast<int>(slot % X);
+  const int64_t first = i - k;
+  if (first < 0 || first + X > n) return false;
+  bool ok = true;
+#pragma unroll
+  for (int m = 0; m < X; ++m) ok = ok && slots[first + m] == slot - k + m;
+  return ok;
+}
+
+// 16 bytes from x elements (x * sizeof(element) = 16).
+template <typename B, int X>
+__device__ inline uint4 pack16(const B (&v)[X]) {
+  static_assert(sizeof(B) * X == 16, "a chunk is 16 bytes");
+  uint4 r;
+  __builtin_memcpy(&r, v, 16);
+  return r;
+}
+
 // One workgroup per new token.  K moves in 16-byte chunks (a chunk is x
-// consecutive dims of one head, contiguous in both source and pool); V is
-// transposed into the pool element by element.
+// consecutive dims of one head, contiguous in both source and pool); V goes
+// in whole 16-byte chunks for whole groups (see whole_group), otherwise
+// element by element.  vchunks: the V pool is 16-byte aligned.
 template <typename T>
 __global__ __launch_bounds__(256) void append_kernel(typename T::bits* __restrict__ kpool,
                                                      typename T::bits* __restrict__ vpool,
                                                      const typename T::bits* __restrict__ knew,
                                                      const typename T::bits* __restrict__ vnew,
                                                      const int64_t* __restrict__ slots,
-                                                     int64_t num_slots_total, int Hkv, int D) {
+                                                     int64_t num_slots_total, int Hkv, int D,
+                                                     bool vchunks) {
   using bits = typename T::bits;
+  constexpr int X = T::kVecElems;
   const int64_t i = blockIdx.x;
   const int64_t slot = slots[i];
   if (slot < 0 || slot >= num_slots_total) return;  // skipped or out of range
   const int64_t blk = slot / kBlockSize;
   const int t = static_cast<int>(slot % kBlockSize);
-  const int chunks_per_head = D / T::kVecElems;
+  const int chunks_per_head = D / X;
   const int nchunks = Hkv * chunks_per_head;
-  const bits* ksrc = knew + i * Hkv * static_cast<int64_t>(D);
-  const bits* vsrc = vnew + i * Hkv * static_cast<int64_t>(D);
+  const int64_t row = static_cast<int64_t>(Hkv) * D;   // elements per token row
+  if (vchunks && whole_group<X>(slots, i, gridDim.x, slot)) {
+    if (t % X != 0) return;                          // the group's first row writes it
+    // K: thread c takes chunk c / X of head h for token t + c % X (X
+    // consecutive threads fill X consecutive 16-byte pieces of the tile)
+    for (int c = threadIdx.x; c < nchunks * X; c += blockDim.x) {
+      const int m = c % X, hc = c / X;
+      const int h = hc / chunks_per_head, ch = hc % chunks_per_head;
+      const uint4 val = *reinterpret_cast<const uint4*>(knew + (i + m) * row +
+                                                        static_cast<int64_t>(h) * D + ch * X);
+      bits* dst = kpool + tile_base(blk, h, Hkv, D) + (ch * kBlockSize + t + m) * X;
+      *reinterpret_cast<uint4*>(dst) = val;
+    }
+    // V: one chunk per (head, dim): the dim's X tokens
+    for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
+      const int h = e / D, d = e % D;
+      bits v[X];
+#pragma unroll
+      for (int m = 0; m < X; ++m) v[m] = vnew[(i + m) * row + e];
+      *reinterpret_cast<uint4*>(vpool + tile_base(blk, h, Hkv, D) + v_elem<T>(t, d, D)) =
+          pack16<bits, X>(v);
+    }
+    return;
+  }
+  const bits* ksrc = knew + i * row;
+  const bits* vsrc = vnew + i * row;
   for (int c = threadIdx.x; c < nchunks; c += blockDim.x) {
     const int h = c / chunks_per_head, ch = c % chunks_per_head;
     const uint4 val = *reinterpret_cast<const uint4*>(ksrc + static_cast<int64_t>(h) * D +
-                                                      ch * T::kVecElems);
-    bits* dst = kpool + tile_base(blk, h, Hkv, D) + (ch * kBlockSize + t) * T::kVecElems;
+                                                      ch * X);
+    bits* dst = kpool + tile_base(blk, h, Hkv, D) + (ch * kBlockSize + t) * X;
     *reinterpret_cast<uint4*>(dst) = val;
   }
   const int nelem = Hkv * D;
@@ -54,7 +111,8 @@ __global__ __launch_bounds__(256) void append_kernel(typename T::bits* __restric
 
 // Quantizing append: one workgroup per new token.  K: each thread encodes 16
 // consecutive dims of one head (one 16-byte chunk of the pool); V: one byte
-// per element (a V chunk holds 16 tokens of one dim).
+// per element (a V chunk holds 16 tokens of one dim), or whole chunks when
+// the call appends the block's 16 tokens in order (see whole_group).
 template <typename Src, typename Code>
 __global__ __launch_bounds__(256) void append_quant_kernel(uint8_t* __restrict__ kpool,
                                                            uint8_t* __restrict__ vpool,
@@ -62,19 +120,19 @@ __global__ __launch_bounds__(256) void append_quant_kernel(uint8_t* __restrict__
                                                            const typename Src::bits* __restrict__ vnew,
                                                            const int64_t* __restrict__ slots,
                                                            int64_t num_slots_total, int Hkv, int D,
-                                                           float rk, float rv) {
+                                                           float rk, float rv, bool vchunks) {
   using bits = typename Src::bits;
+  constexpr int X = 16;                               // codes per 16-byte chunk
   const int64_t i = blockIdx.x;
   const int64_t slot = slots[i];
   if (slot < 0 || slot >= num_slots_total) return;
   const int64_t blk = slot / kBlockSize;
   const int t = static_cast<int>(slot % kBlockSize);
   const int chunks_per_head = D / 16;
-  const bits* ksrc = knew + i * Hkv * static_cast<int64_t>(D);
-  const bits* vsrc = vnew + i * Hkv * static_cast<int64_t>(D);
-  for (int c = threadIdx.x; c < Hkv * chunks_per_head; c += blockDim.x) {
-    const int h = c / chunks_per_head, ch = c % chunks_per_head;
-    const bits* x = ksrc + static_cast<int64_t>(h) * D + ch * 16;
+  const int64_t row = static_cast<int64_t>(Hkv) * D;
+  // the codes of 16 consecutive dims of one head of token row r
+  auto k_chunk = [&](int64_t r, int h, int ch) {
+    const bits* x = knew + r * row + static_cast<int64_t>(h) * D + ch * 16;
     uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -82,8 +140,33 @@ __global__ __launch_bounds__(256) void append_quant_kernel(uint8_t* __restrict__
       const uint32_t hi = Encode<Code>::pair(Src::to_float(x[4 * j + 2]), Src::to_float(x[4 * j + 3]), rk);
       w[j] = lo | (hi << 16);
     }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  if (vchunks && whole_group<X>(slots, i, gridDim.x, slot)) {
+    if (t % X != 0) return;                          // the block's first row writes it
+    for (int c = threadIdx.x; c < Hkv * chunks_per_head * X; c += blockDim.x) {
+      const int m = c % X, hc = c / X;
+      const int h = hc / chunks_per_head, ch = hc % chunks_per_head;
+      *reinterpret_cast<uint4*>(kpool + tile_base(blk, h, Hkv, D) + (ch * kBlockSize + t + m) * 16) =
+          k_chunk(i + m, h, ch);
+    }
+    for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
+      const int h = e / D, d = e % D;
+      uint8_t v[X];
+#pragma unroll
+      for (int m = 0; m < X; ++m)
+        v[m] = static_cast<uint8_t>(Encode<Code>::pair(Src::to_float(vnew[(i + m) * row + e]),
+                                                       0.f, rv) & 0xFFu);
+      *reinterpret_cast<uint4*>(vpool + tile_base(blk, h, Hkv, D) + v_elem<U8>(t, d, D)) =
+          pack16<uint8_t, X>(v);
+    }
+    return;
+  }
+  const bits* vsrc = vnew + i * row;
+  for (int c = threadIdx.x; c < Hkv * chunks_per_head; c += blockDim.x) {
+    const int h = c / chunks_per_head, ch = c % chunks_per_head;
     *reinterpret_cast<uint4*>(kpool + tile_base(blk, h, Hkv, D) + (ch * kBlockSize + t) * 16) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+        k_chunk(i, h, ch);
   }
   for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
     const int h = e / D, d = e % D;
@@ -242,31 +325,32 @@ extern "C" pa_status pa_cache_append(void* k_pool, void* v_pool, const void* k_n
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t total = static_cast<int64_t>(num_blocks) * kBlockSize;
   dim3 grid(num_tokens), block(256);
+  const bool vchunks = aligned16(v_pool);
   switch (dtype) {
     case PA_F32:
       append_kernel<F32><<<grid, block, 0, s>>>(
           static_cast<uint32_t*>(k_pool), static_cast<uint32_t*>(v_pool),
           static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new), slot_mapping,
-          total, num_kv_heads, head_dim);
+          total, num_kv_heads, head_dim, vchunks);
       break;
     case PA_F16:
       append_kernel<F16><<<grid, block, 0, s>>>(
           static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
           static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
-          total, num_kv_heads, head_dim);
+          total, num_kv_heads, head_dim, vchunks);
       break;
     case PA_BF16:
       append_kernel<BF16><<<grid, block, 0, s>>>(
           static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
           static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
-          total, num_kv_heads, head_dim);
+          total, num_kv_heads, head_dim, vchunks);
       break;
     case PA_FP8_E4M3:
     case PA_INT8:
       append_kernel<U8><<<grid, block, 0, s>>>(
           static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
           static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new), slot_mapping,
-          total, num_kv_heads, head_dim);
+          total, num_kv_heads, head_dim, vchunks);
       break;
   }
   return launch_status("pa_cache_append");
@@ -302,10 +386,11 @@ extern "C" pa_status pa_cache_append_quant(void* k_pool, void* v_pool, const voi
   dim3 grid(num_tokens), block(256);
   uint8_t* kp = static_cast<uint8_t*>(k_pool);
   uint8_t* vp = static_cast<uint8_t*>(v_pool);
+  const bool vchunks = aligned16(v_pool);
 #define PA_APPEND_Q(SRC, CODE)                                                                 \
   append_quant_kernel<SRC, CODE><<<grid, block, 0, s>>>(                                      \
       kp, vp, static_cast<const SRC::bits*>(k_new), static_cast<const SRC::bits*>(v_new),     \
-      slot_mapping, total, num_kv_heads, head_dim, rk, rv)
+      slot_mapping, total, num_kv_heads, head_dim, rk, rv, vchunks)
   const bool fp8 = cache_dtype == PA_FP8_E4M3;
   switch (src_dtype) {
     case PA_F32: if (fp8) PA_APPEND_Q(F32, E4M3); else PA_APPEND_Q(F32, I8); break;
