@@ -99,6 +99,14 @@ def parse():
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass, which times each attention kernel with "
                          "events attached to its dispatch")
+    ap.add_argument("--record-traffic", nargs=4, default=None,
+                    metavar=("WORKLOAD", "RUN_DIR", "CALIB_DIR", "KERNEL"),
+                    help="store the HBM traffic of KERNEL (a substring of its name) for "
+                         "WORKLOAD in profiles/decode_traffic.json, from rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE csv runs RUN_DIR/FETCH_SIZE and "
+                         "RUN_DIR/WRITE_SIZE of this script, scaled by the same counters over "
+                         "--copy-calibration runs in CALIB_DIR/FETCH_SIZE and "
+                         "CALIB_DIR/WRITE_SIZE, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB elementwise copy 5 times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -117,6 +125,48 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read_per_launch": n * 4,
                       "copy_calibration_bytes_written_per_launch": n * 4, "launches": 5}))
+
+
+def counter_per_dispatch(run_dir: str, counter: str, kernel: str):
+    """Mean over the dispatches of kernels whose name contains `kernel` of a
+    rocprofv3 --pmc counter (csv output, summed over its instances), and the
+    dispatch count."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} samples for kernels matching {kernel!r} in {run_dir}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def record_traffic(workload, run_dir, calib_dir, kernel):
+    """HBM bytes per launch of `kernel` for `workload`: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) scaled by what they read for the copy
+    calibration's known 1 GiB read and 1 GiB written per launch."""
+    cf, _ = counter_per_dispatch(os.path.join(calib_dir, "FETCH_SIZE"), "FETCH_SIZE", "Unary")
+    cw, _ = counter_per_dispatch(os.path.join(calib_dir, "WRITE_SIZE"), "WRITE_SIZE", "Unary")
+    fetch_scale, write_scale = (1 << 30) / (cf * 1024), (1 << 30) / (cw * 1024)
+    f, n = counter_per_dispatch(os.path.join(run_dir, "FETCH_SIZE"), "FETCH_SIZE", kernel)
+    w, _ = counter_per_dispatch(os.path.join(run_dir, "WRITE_SIZE"), "WRITE_SIZE", kernel)
+    rd, wr = f * 1024 * fetch_scale, w * 1024 * write_scale
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        t = {}
+    t[workload] = {"kernel_src_sha256_16": kernel_src_hash(), "kernel": kernel,
+                   "hbm_bytes_per_launch": int(round(rd + wr)), "read_bytes": int(round(rd)),
+                   "write_bytes": int(round(wr)), "fetch_scale": fetch_scale,
+                   "write_scale": write_scale, "fetch_kib_per_dispatch": round(f, 1),
+                   "write_kib_per_dispatch": round(w, 1), "dispatches": n}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(dict(sorted(t.items())), fh, indent=1)
+        fh.write("\n")
+    print(json.dumps({workload: t[workload]}))
 
 
 def kernel_src_hash() -> str:
@@ -461,6 +511,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the decode path has "
@@ -499,6 +552,8 @@ def main():
         case.name = f"{case.name}_literal"
     if args.q_heads:
         case.name = f"{case.name}_hq{args.q_heads}"
+    if args.shared_prefix:
+        case.name = f"{case.name}_shared"
     quant = args.kv_cache is not None
     if quant:
         case = quantized(case, args.kv_cache)
