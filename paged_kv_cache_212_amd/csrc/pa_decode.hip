@@ -315,11 +315,14 @@ template <>
 struct Kv4<E4M3> {
   using Mma = Mfma4<BF16>;
   static constexpr bool kCodes = true;
-  // every E4M3 value (3 mantissa bits, exponents 2^-9 .. 2^8) is a bf16 value
+  // every E4M3 value (3 mantissa bits, exponents 2^-9 .. 2^8) is a bf16 value:
+  // gfx950 converts two codes to a bf16 pair in one instruction (scale 1:
+  // exact).  Measured against two codes to fp32 then a byte permute: 34.1
+  // against 34.5 us for the Llama-3-8B batch's attention kernel.
   __device__ static inline uint2 widen(uint32_t w) {
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-    return make_uint2(bf16_pair(lo[0], lo[1]), bf16_pair(hi[0], hi[1]));
+    return make_uint2(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
   }
 };
 template <>

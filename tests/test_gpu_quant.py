@@ -255,3 +255,36 @@ def test_step_slot_cases_match_append_then_decode(fmt, hq, hkv, ps):
             assert np.isnan(a[i]).all() and np.isnan(b[i]).all()
         keep = [i for i in keep if i not in (1, 3)]
     assert max_err(a[keep], b[keep]) <= 1e-4
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("ps", [0, 64])
+def test_every_code_value_widened_exactly(fmt, ps):
+    """K and V rows made of every finite code value of the format (E4M3: the
+    254 non-NaN codes, subnormals and -0 included; INT8: -127 .. 127), at
+    scale 1 so that each value is its own code: decode over them against the
+    oracle, which widens each code from its field layout.  A code widened to
+    the wrong bf16 value moves some output by far more than the bar."""
+    from dataclasses import replace
+    if fmt == "fp8":
+        vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float()
+        vals = vals[~torch.isnan(vals)]
+    else:
+        vals = torch.arange(-127, 128, dtype=torch.float32)
+    case = custom_case(64, "bf16", [300, 257, 64, 511], 32, 8, 128, partition_size=ps,
+                       q_std=2.0 / float(vals.abs().max()))
+    g = torch.Generator().manual_seed(65)
+    R, H, D = case.k_tok.shape
+    idx_k = torch.randint(0, len(vals), (R, H, D), generator=g)
+    idx_v = torch.randint(0, len(vals), (R, H, D), generator=g)
+    # every value appears in every (head, 64-dim tile) somewhere in K and V
+    flat = torch.arange(R * H * D) % len(vals)
+    idx_k.view(-1)[: len(flat)] = flat[torch.randperm(len(flat), generator=g)]
+    k_tok = vals[idx_k].to(torch.bfloat16)
+    v_tok = vals[idx_v].to(torch.bfloat16)
+    case = replace(case, k_tok=k_tok, v_tok=v_tok, cache_dtype=fmt, k_scale=1.0, v_scale=1.0,
+                   name=f"every_code_{fmt}")
+    say(f"[quant every code] {fmt} P={ps}: {len(vals)} values")
+    ref = _oracle_poisoned(case)
+    got = run_gpu_step(case)
+    _compare_full(case, ref, got)
