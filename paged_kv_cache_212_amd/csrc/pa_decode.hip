@@ -961,6 +961,16 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -1144,6 +1154,7 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
 constexpr int kMergeBatch = 8;
 constexpr int kMergeSpec = 2;
 constexpr int kMergeRowsPerGroup = 4;
+constexpr int kMergeFold = 16;   // weighted sums loaded together on the many-slot path
 
 // A value read at the same address by every lane of the wave, through the
 // scalar data cache (the address must be wave-uniform).
@@ -1303,22 +1314,99 @@ __global__ __launch_bounds__(64 * kMergeRowsPerGroup) void merge_kernel(Params p
     return;
   }
   if (!has_pre && (ns <= 1 || !have_ws)) return;             // written final
-  // the rest of the first batch: only the slots the row holds
-#pragma unroll
-  for (int k = kMergeSpec; k < kMergeBatch; ++k)
-    if (k < kfirst && k < ns) load_row<E>(a[k], pa + static_cast<int64_t>(k) * D);
   float M = -INFINITY;
   if (has_pre) {
 #pragma unroll
     for (int p = 0; p < kMaxPrefixPieces; ++p)
       if (p < pr.pre_pieces) M = fmaxf(M, pre_ml[p].x);
   }
-#pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k)
-    if (k < ns) M = fmaxf(M, m[k]);
   float num[E], den = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) num[e] = 0.f;
+  if (ns <= kMergeBatch) {
+    // the rest of the first batch: only the slots the row holds
+#pragma unroll
+    for (int k = kMergeSpec; k < kMergeBatch; ++k)
+      if (k < kfirst && k < ns) load_row<E>(a[k], pa + static_cast<int64_t>(k) * D);
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (k < ns) M = fmaxf(M, m[k]);
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (k < ns) {
+        const float wgt = exp2f(m[k] - M);
+        den = fmaf(wgt, l[k], den);
+#pragma unroll
+        for (int e = 0; e < E; ++e) num[e] = fmaf(wgt, a[k][e], num[e]);
+      }
+    }
+  } else {
+    // Many slots (long contexts in fixed partitions, or cut into many
+    // chunks).  Slots go in groups of 256, four per lane: their maxima (and
+    // sums) are loaded four at a time per lane, all in flight together; M is
+    // the maximum over every group (a first sweep when there are more than
+    // 256 slots); the weighted sums are then folded 16 slots at a time, their
+    // loads issued together, with nothing to rescale.
+    constexpr int kGroup = 256;
+    auto group_ml = [&](int c0, float (&mv)[4], float (&lv)[4], bool sums) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = c0 + 64 * u + lane;
+        mv[u] = k < ns ? pm[k] : -INFINITY;
+        if (sums) lv[u] = k < ns ? pl[k] : 0.f;
+      }
+    };
+    float mv[4], lv[4];
+    if (ns > kGroup) {
+      float mloc = -INFINITY;
+      for (int c0 = 0; c0 < ns; c0 += kGroup) {
+        group_ml(c0, mv, lv, false);
+        mloc = fmaxf(mloc, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
+      }
+      M = fmaxf(M, wave_max(mloc));
+    }
+    float dloc = 0.f;
+    for (int c0 = 0; c0 < ns; c0 += kGroup) {
+      group_ml(c0, mv, lv, true);
+      if (ns <= kGroup) M = fmaxf(M, wave_max(fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]))));
+      float w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        w[u] = exp2f(mv[u] - M);            // 0 for slots past the row's count
+        dloc = fmaf(w[u], lv[u], dloc);
+      }
+      const int cnt = min(kGroup, ns - c0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        for (int j0 = 0; j0 < 64 && 64 * u + j0 < cnt; j0 += kMergeFold) {
+          const int base = c0 + 64 * u + j0;
+          float av[kMergeFold][E];
+          if (base + kMergeFold <= ns) {
+#pragma unroll
+            for (int f = 0; f < kMergeFold; ++f)
+              load_row<E>(av[f], pa + static_cast<int64_t>(base + f) * D);
+          } else {
+#pragma unroll
+            for (int f = 0; f < kMergeFold; ++f) {
+              if (base + f < ns) {
+                load_row<E>(av[f], pa + static_cast<int64_t>(base + f) * D);
+              } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) av[f][e] = 0.f;
+              }
+            }
+          }
+#pragma unroll
+          for (int f = 0; f < kMergeFold; ++f) {
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[u]), j0 + f));
+#pragma unroll
+            for (int e = 0; e < E; ++e) num[e] = fmaf(wk, av[f][e], num[e]);
+          }
+        }
+      }
+    }
+    den = wave_sum(dloc);
+  }
   // each prefix piece counts as one more partial (an empty piece has max
   // -inf and sum 0: weight 0)
   if (has_pre) {
@@ -1329,43 +1417,6 @@ __global__ __launch_bounds__(64 * kMergeRowsPerGroup) void merge_kernel(Params p
         den = fmaf(wgt, pre_ml[p].y, den);
 #pragma unroll
         for (int e = 0; e < E; ++e) num[e] = fmaf(wgt, pre_o[p][e], num[e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k) {
-    if (k < ns) {
-      const float wgt = exp2f(m[k] - M);
-      den = fmaf(wgt, l[k], den);
-#pragma unroll
-      for (int e = 0; e < E; ++e) num[e] = fmaf(wgt, a[k][e], num[e]);
-    }
-  }
-  for (int k0 = kMergeBatch; k0 < ns; k0 += kMergeBatch) {
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      if (k0 + k < ns) {
-        m[k] = uniform_load(pm + k0 + k);
-        l[k] = uniform_load(pl + k0 + k);
-        load_row<E>(a[k], pa + static_cast<int64_t>(k0 + k) * D);
-      }
-    }
-    float Mb = M;
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k)
-      if (k0 + k < ns) Mb = fmaxf(Mb, m[k]);
-    const float r = exp2f(M - Mb);
-#pragma unroll
-    for (int e = 0; e < E; ++e) num[e] *= r;
-    den *= r;
-    M = Mb;
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      if (k0 + k < ns) {
-        const float wgt = exp2f(m[k] - M);
-        den = fmaf(wgt, l[k], den);
-#pragma unroll
-        for (int e = 0; e < E; ++e) num[e] = fmaf(wgt, a[k][e], num[e]);
       }
     }
   }
