@@ -2050,6 +2050,8 @@ extern "C" pa_status pa_decode_step_shared(
     return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d (fp16/bf16 pools only)", fn, (int)dtype);
   if (generic_selected())
     return fail(PA_ERR_UNSUPPORTED, "%s: needs the matrix-core kernels", fn);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   if (num_groups < 0 || num_rows < 0 || max_group_size < 0 || num_rows > num_seqs ||
       (num_groups > 0 && (num_rows < 2 * num_groups || max_group_size < 2 ||
                           max_group_size > num_rows)))

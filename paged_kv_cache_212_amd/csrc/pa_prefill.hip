@@ -335,77 +335,107 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
   };
 
   float m_run[TQ], l_lane[TQ];
+  float thr[TQ];   // raw score above which the row's max moves m_run
   f32x4_t acc[TQ][NTL];
 #pragma unroll
   for (int t = 0; t < TQ; ++t) {
     m_run[t] = -INFINITY;
+    thr[t] = -INFINITY;
     l_lane[t] = 0.f;
 #pragma unroll
     for (int d = 0; d < NTL; ++d) acc[t][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // scores of tile t against the pair's 32 keys, online softmax update,
-  // probabilities split into the two half-precision parts of P.V's A operand.
-  // The running max is kept in the log2 domain (scale * log2(e) applied);
-  // the max of a pair is taken over the raw scores (the scale is positive)
-  // and each weight is exp2(s * scale - m) with one fused multiply-add.  The
-  // causal mask is applied only to pairs that reach past the tile's first
-  // query position (the tile's earlier pairs hold no later key).
-  auto qk_softmax = [&](int pp, int t, uint4& phi, uint4& plo) {
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  // Scores of the TQ tiles against the pair's 32 keys: 2 * TQ independent
+  // chains of matrix ops issued together.  The causal mask is applied only
+  // to pairs that reach past the first tile's first query position (earlier
+  // pairs hold no later key for any tile; the mask itself is exact per key
+  // and query, so applying it to every tile of such a pair is correct).
+  auto qk_scores = [&](int pp, float (&sv)[TQ][8]) {
+    f32x4_t s0[TQ], s1[TQ];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) s0[t] = s1[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      s0 = Mfma<T>::qk(kreg[0][kk], qr[t][kk], s0);
-      s1 = Mfma<T>::qk(kreg[1][kk], qr[t][kk], s1);
-    }
-    const int kpos0 = 2 * pp * kBlockSize + 4 * j;        // key position of s0[0]
-    float sv[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = s0[e];
-      sv[4 + e] = s1[e];
+      for (int t = 0; t < TQ; ++t) {
+        s0[t] = Mfma<T>::qk(kreg[0][kk], qr[t][kk], s0[t]);
+        s1[t] = Mfma<T>::qk(kreg[1][kk], qr[t][kk], s1[t]);
+      }
     }
-    // the tile's first query position: first_pos + i0 + 16t (uniform); in
+#pragma unroll
+    for (int t = 0; t < TQ; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[t][e] = s0[t][e];
+        sv[t][4 + e] = s1[t][e];
+      }
+    // the first tile's first query position: first_pos + i0 (uniform); in
     // shared mode every query is at Lk - 1, so only keys past the piece (a
     // re-read last block) are masked
-    if ((2 * pp + 2) * kBlockSize - 1 > (kShared ? Lk - 1 : first_pos + i0 + kQTile * t)) {
+    if ((2 * pp + 2) * kBlockSize - 1 > (kShared ? Lk - 1 : first_pos + i0)) {
+      const int kpos0 = 2 * pp * kBlockSize + 4 * j;      // key position of s0[0]
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sv[e] = (kpos0 + e <= qpos[t]) ? sv[e] : -INFINITY;
-        sv[4 + e] = (kpos0 + kBlockSize + e <= qpos[t]) ? sv[4 + e] : -INFINITY;
+      for (int t = 0; t < TQ; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[t][e] = (kpos0 + e <= qpos[t]) ? sv[t][e] : -INFINITY;
+          sv[t][4 + e] = (kpos0 + kBlockSize + e <= qpos[t]) ? sv[t][4 + e] : -INFINITY;
+        }
+    }
+  };
+  // Online softmax update of the TQ tiles from their scores, and P split into
+  // the two half-precision parts of P.V's A operand.  The running max is kept
+  // in the log2 domain (scale * log2(e) applied) and each weight is
+  // exp2(s * scale - m) with one fused multiply-add.
+  // Lazy rescaling: m_run is only a reference (numerator and denominator
+  // share it), so it moves only when some row's max exceeds it by more than
+  // kRescaleSlack; weights then stay below 2^kRescaleSlack, far inside fp32
+  // and with the same relative precision in the hi/lo split.  Whether a row
+  // passes that bound is a compare of each raw score with the row's
+  // threshold (m_run + slack) / scale (the scale is positive), kept beside
+  // m_run; the tiles share one test, and the row max itself (a reduction
+  // across lanes) is taken only when some row passes.  A tile whose queries
+  // all precede the pair keeps m = -inf rows only while no key was valid; the
+  // first pair holds key 0, valid for every query, so m_run is finite from
+  // there on.
+  auto softmax = [&](float (&sv)[TQ][8], uint4 (&phi)[TQ], uint4 (&plo)[TQ]) {
+    bool over = false;
+#pragma unroll
+    for (int t = 0; t < TQ; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) over = over || sv[t][e] > thr[t];
+    if (__any(over)) {
+#pragma unroll
+      for (int t = 0; t < TQ; ++t) {
+        float bm = sv[t][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[t][e]);
+        bm = max_xor16(bm);
+        bm = max_xor32(bm);
+        const float mn = fmaxf(m_run[t], bm * pr.scale_log2);
+        // a query's running max moved: rescale its O row by 2^(m_old - m_new)
+        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - mn);
+        l_lane[t] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ar = __shfl(alpha, 4 * j + e);        // alpha of O row 4j + e
+#pragma unroll
+          for (int d = 0; d < NTL; ++d) acc[t][d][e] *= ar;
+        }
+        m_run[t] = mn;
+        thr[t] = (mn + kRescaleSlack) / pr.scale_log2;
       }
     }
-    float bm = sv[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[e]);
-    bm = max_xor16(bm);
-    bm = max_xor32(bm);
-    // a tile whose queries all precede the pair keeps m = -inf rows only
-    // while no key was valid; the first pair holds key 0, valid for every
-    // query, so m_run is finite from there on.
-    // Lazy rescaling: m_run is only a reference (numerator and denominator
-    // share it), so it moves only when some row's max exceeds it by more
-    // than kRescaleSlack; weights then stay below 2^kRescaleSlack, far inside
-    // fp32 and with the same relative precision in the hi/lo split.
-    const float mn = fmaxf(m_run[t], bm * pr.scale_log2);
-    if (__any(mn > m_run[t] + kRescaleSlack)) {
-      // a query's running max moved: rescale its O row by 2^(m_old - m_new)
-      const float alpha = __builtin_amdgcn_exp2f(m_run[t] - mn);
-      l_lane[t] *= alpha;
+    for (int t = 0; t < TQ; ++t) {
+      float pe[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ar = __shfl(alpha, 4 * j + e);        // alpha of O row 4j + e
-#pragma unroll
-        for (int d = 0; d < NTL; ++d) acc[t][d][e] *= ar;
-      }
-      m_run[t] = mn;
+      for (int e = 0; e < 8; ++e)
+        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], pr.scale_log2, -m_run[t]));
+      l_lane[t] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+      Mfma<T>::split8(pe, phi[t], plo[t]);
     }
-    float pe[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], pr.scale_log2, -m_run[t]));
-    l_lane[t] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-    Mfma<T>::split8(pe, phi, plo);
   };
 
   // V rows at positions >= L are zeroed, so unwritten slots never reach O
@@ -445,13 +475,15 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
       issue_v();
     }
     for (int pp = 0; pp < npair; ++pp) {
-      uint4 phi, plo;
-      qk_softmax(pp, 0, phi, plo);
+      uint4 phi[1], plo[1];
+      float sv[1][8];
+      qk_scores(pp, sv);
+      softmax(sv, phi, plo);
       __builtin_amdgcn_sched_barrier(0);
       if (pp + 1 < npair) issue_k(pp + 1);
       __builtin_amdgcn_sched_barrier(0);
       mask_v(pp);
-      pv(0, phi, plo);
+      pv(0, phi[0], plo[0]);
       __builtin_amdgcn_sched_barrier(0);
       if (pp + 1 < npair) issue_v();
       __builtin_amdgcn_sched_barrier(0);
@@ -476,8 +508,9 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     auto compute = [&](int pp, auto cur) {
       lread_k(cur);
       uint4 phi[TQ], plo[TQ];
-#pragma unroll
-      for (int t = 0; t < TQ; ++t) qk_softmax(pp, t, phi[t], plo[t]);
+      float sv[TQ][8];
+      qk_scores(pp, sv);
+      softmax(sv, phi, plo);
       lread_v(cur);
       mask_v(pp);
 #pragma unroll

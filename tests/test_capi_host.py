@@ -487,3 +487,32 @@ def test_shared_prefix_plan_rejects_bad_arguments():
                                    C.byref(mg)) == PA_ERR_INVALID_ARG
     assert h.pa_shared_prefix_plan(None, None, 3, 4, 16, 0, None, None, None, C.byref(ng),
                                    C.byref(mg)) == PA_ERR_INVALID_ARG
+
+
+def test_decode_step_shared_rejects_bad_arguments_before_any_launch():
+    """pa_decode_step_shared checks its scalars on the host, before the
+    prefix pass or any other device call: an unsupported dtype, a scale that
+    is not positive and finite, inconsistent group counts, a missing prefix
+    array, a short workspace."""
+    from paged_kv_cache_212_amd._lib import PA_F32
+    h = pk.lib()
+    nul = None
+
+    def call(dtype=PA_BF16, scale=0.088, groups=1, rows=2, max_group=2, B=4, prefix=nul,
+             ws=nul, ws_bytes=0):
+        return h.pa_decode_step_shared(nul, nul, nul, nul, nul, nul, nul, nul, nul, prefix, nul,
+                                       nul, groups, rows, max_group, B, 32, 8, 128, 16, 64, 8,
+                                       100, scale, dtype, ws, ws_bytes, nul)
+    assert call(dtype=PA_F32) == PA_ERR_UNSUPPORTED
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(scale=bad) == PA_ERR_INVALID_ARG
+    assert call(groups=1, rows=1) == PA_ERR_INVALID_ARG          # a group of one
+    assert call(groups=2, rows=3) == PA_ERR_INVALID_ARG          # fewer than 2 per group
+    assert call(groups=1, rows=2, max_group=3) == PA_ERR_INVALID_ARG
+    assert call(rows=5) == PA_ERR_INVALID_ARG                    # more rows than sequences
+    assert call() == PA_ERR_INVALID_ARG                          # no prefix array
+    need = h.pa_decode_shared_workspace_bytes(4, 32, 8, 128, 100, PA_BF16)
+    assert need > 0
+    fake = C.c_void_p(256)                                       # never dereferenced
+    assert call(groups=0, rows=0, max_group=0, prefix=fake, ws=fake,
+                ws_bytes=need - 1) == PA_ERR_WORKSPACE
