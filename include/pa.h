@@ -181,6 +181,21 @@ pa_status pa_bm_extend(pa_bm* bm, int64_t seq_id, int32_t num_tokens, int64_t* s
 pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n, int64_t* slots_out,
                              int32_t* cow_pairs_out, int32_t* num_cow_out);
 
+/* One decode step's host work in one call: pa_bm_append_slots for the n
+ * sequences, then pa_bm_block_tables of the same sequences after the
+ * reservation (page 3, abeam.tech review, section 「KV キャッシュマネージャ」:
+ * the manager hands the kernel its block tables).  Outputs (host):
+ * slots_out [n], cow_pairs_out [n][2] and *num_cow_out as for
+ * pa_bm_append_slots; tables_out [n][max_blocks] (padded with -1) and
+ * lens_out [n] as for pa_bm_block_tables; *blocks_needed_out = the longest
+ * table after the reservation.  When that exceeds max_blocks the call
+ * returns PA_ERR_INVALID_ARG with *blocks_needed_out set and changes
+ * nothing, so the caller can grow its buffers and call again; the other
+ * errors are those of pa_bm_append_slots, also with no change. */
+pa_status pa_bm_step(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                     int64_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out,
+                     int32_t* tables_out, int32_t* lens_out, int32_t* blocks_needed_out);
+
 /* Releases a finished sequence: each of its blocks' reference counts drops
  * by one, and blocks reaching zero return to the free list, in table order
  * (page 3, abeam.tech review, section 「KV キャッシュマネージャ」: at the end

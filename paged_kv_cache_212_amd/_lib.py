@@ -54,6 +54,7 @@ SIGNATURES = {
     "pa_copy_blocks_layers": (C.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                         C.c_int, _vp]),
     "pa_bm_block_tables": (C.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "pa_bm_step": (C.c_int, [_vp, _vp, _i32, _i32, _vp, _vp, _p_i32, _vp, _vp, _p_i32]),
     "pa_bm_seq_len": (C.c_int, [_vp, _i64, _p_i32]),
     "pa_bm_refcount": (C.c_int, [_vp, _i32, _p_i32]),
     "pa_bm_stats": (C.c_int, [_vp, C.POINTER(BmStats)]),

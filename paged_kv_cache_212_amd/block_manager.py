@@ -10,9 +10,10 @@ from ._lib import BmStats, check, lib
 
 def _ptr(a: np.ndarray, ctype):
     """Address of a contiguous array of `ctype` elements (the C arguments are
-    c_void_p; the element type is checked here)."""
+    c_void_p; the element type is checked here).  Read from the array
+    interface: `ndarray.ctypes` builds a helper object on every access."""
     assert a.dtype.itemsize == C.sizeof(ctype) and a.flags.c_contiguous
-    return a.ctypes.data
+    return a.__array_interface__["data"][0]
 
 
 class BlockManager:
@@ -29,6 +30,9 @@ class BlockManager:
                                  _ptr(fo, C.c_int32) if fo is not None else None,
                                  C.byref(self._h)), "pa_bm_create")
         self.num_blocks, self.block_size = num_blocks, block_size
+        self._step_fn = None
+        self._step_out = (C.c_int32(0), C.c_int32(0))
+        self._step_ref = (C.byref(self._step_out[0]), C.byref(self._step_out[1]))
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -62,6 +66,39 @@ class BlockManager:
                                        _ptr(slots, C.c_int64), _ptr(pairs, C.c_int32),
                                        C.byref(n)), "pa_bm_append_slots")
         return slots, pairs[:n.value].copy()
+
+    def step(self, seq_ids, capacity: int = 0):
+        """One decode step's host work (pa_bm_step): reserve one position per
+        sequence and export the tables after it.  capacity: table row length
+        to try first (grown and retried when a table is longer).  Returns
+        (slots, cow pairs [n][2], tables [n][blocks needed], lens)."""
+        ids = seq_ids if (isinstance(seq_ids, np.ndarray) and seq_ids.dtype == np.int64
+                          and seq_ids.flags.c_contiguous) else \
+            np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = len(ids)
+        cap = max(int(capacity), 1)
+        slots = np.empty(n, dtype=np.int64)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        lens = np.empty(n, dtype=np.int32)
+        f = self._step_fn
+        if f is None:
+            f = self._step_fn = lib().pa_bm_step
+        ncow, need = self._step_out
+        pi, ps = _ptr(ids, C.c_int64), _ptr(slots, C.c_int64)
+        pp, pl = _ptr(pairs, C.c_int32), _ptr(lens, C.c_int32)
+        while True:
+            tables = np.empty((n, cap), dtype=np.int32)
+            st = f(self._h, pi, n, cap, ps, pp, self._step_ref[0], _ptr(tables, C.c_int32), pl,
+                   self._step_ref[1])
+            if st != 0 and need.value > cap:
+                cap = need.value                    # nothing changed: retry with room
+                continue
+            check(st, "pa_bm_step")
+            break
+        nb = max(need.value, 1)
+        if nb != cap:
+            tables = np.ascontiguousarray(tables[:, :nb])
+        return slots, pairs[:ncow.value].copy(), tables, lens
 
     def free_seq(self, seq_id: int):
         check(lib().pa_bm_free_seq(self._h, seq_id), "pa_bm_free_seq")

@@ -37,6 +37,7 @@ class PagedKVCache:
         (torch.float8_e4m3fn or torch.int8): a quantized cache whose pools hold
         codes with K = code * k_scale, V = code * v_scale (q, k/v rows: bf16)."""
         self.bm = BlockManager(num_blocks, BLOCK_SIZE, free_order)
+        self._table_cap = 1          # table row length tried first by plan_step
         if cache_dtype is not None and cache_dtype not in ops.CODE_DTYPES:
             raise ValueError("cache_dtype must be torch.float8_e4m3fn or torch.int8")
         self.cache_dtype = cache_dtype
@@ -111,10 +112,13 @@ class PagedKVCache:
     def plan_step(self, seq_ids, max_blocks: int | None = None) -> StepPlan:
         """Reserve one position per sequence and export the tables (host work)."""
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
-        slots, cows = self.bm.append_slots(ids)
         if max_blocks is None:
-            max_blocks = max([1] + [-(-self.bm.seq_len(int(s)) // BLOCK_SIZE) for s in ids])
-        tables, lens = self.bm.block_tables(ids, max_blocks)
+            # one call: reserve, then export tables as long as the longest
+            slots, cows, tables, lens = self.bm.step(ids, self._table_cap)
+            self._table_cap = max(self._table_cap, tables.shape[1])
+        else:
+            slots, cows = self.bm.append_slots(ids)
+            tables, lens = self.bm.block_tables(ids, max_blocks)
         return StepPlan(ids, slots, cows, tables, lens, int(lens.max(initial=0)),
                         self._d(slots), self._d(cows.reshape(-1, 2)), self._d(tables),
                         self._d(lens))

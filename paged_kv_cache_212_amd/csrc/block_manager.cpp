@@ -30,7 +30,9 @@ struct pa_bm {
   struct Seq {
     std::vector<int32_t> table;  // logical block -> physical block (-1: released)
     int32_t len = 0;             // tokens written so far
+    uint64_t stamp = 0;          // last pa_bm_step call that named it (repeat check)
   };
+  uint64_t step_gen = 0;         // pa_bm_step calls so far
   int32_t num_blocks = 0;
   int32_t block_size = 0;
   std::vector<int32_t> free_stack;  // back() is the next block handed out
@@ -208,6 +210,58 @@ extern "C" pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32
                 static_cast<long long>(need), bm->free_stack.size());
   int32_t np = 0;
   for (int32_t i = 0; i < n; ++i) bm->write(*seqs[i], 1, slots_out + i, cow_pairs_out, &np);
+  if (num_cow_out) *num_cow_out = np;
+  return pa::ok();
+}
+
+extern "C" pa_status pa_bm_step(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                                int64_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out,
+                                int32_t* tables_out, int32_t* lens_out,
+                                int32_t* blocks_needed_out) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_step: bm is NULL");
+  if (n < 0 || max_blocks < 0 || !blocks_needed_out ||
+      (n > 0 && (!seq_ids || !slots_out || !cow_pairs_out || !tables_out || !lens_out)))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_step: bad n/max_blocks or NULL buffer");
+  // Each sequence looked up once; a repeat is caught by the call's stamp.
+  // The checks all come before any change (all-or-nothing).
+  const uint64_t gen = ++bm->step_gen;
+  std::vector<pa_bm::Seq*> seqs(n);
+  int32_t need_rows = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld",
+                                          static_cast<long long>(seq_ids[i]));
+    pa_bm::Seq& sq = it->second;
+    if (sq.stamp == gen)
+      return fail(PA_ERR_INVALID_ARG, "pa_bm_step: sequence %lld twice in batch",
+                  static_cast<long long>(seq_ids[i]));
+    sq.stamp = gen;
+    if (sq.len == INT32_MAX) return fail(PA_ERR_INVALID_ARG, "length overflow");
+    const int64_t len = static_cast<int64_t>(sq.len) + 1;
+    need_rows = static_cast<int32_t>(
+        std::max<int64_t>(need_rows, (len + bm->block_size - 1) / bm->block_size));
+    seqs[i] = &sq;
+  }
+  *blocks_needed_out = need_rows;
+  if (need_rows > max_blocks)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_step: tables need %d blocks > max_blocks %d",
+                need_rows, max_blocks);
+  std::unordered_map<int32_t, int32_t> pending;
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) need += bm->blocks_needed(*seqs[i], 1, &pending);
+  if (need > static_cast<int64_t>(bm->free_stack.size()))
+    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_step: need %lld blocks, %zu free",
+                static_cast<long long>(need), bm->free_stack.size());
+  int32_t np = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    pa_bm::Seq& sq = *seqs[i];
+    bm->write(sq, 1, slots_out + i, cow_pairs_out, &np);
+    int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks;
+    const size_t nb = sq.table.size();
+    std::memcpy(row, sq.table.data(), nb * sizeof(int32_t));
+    std::fill(row + nb, row + max_blocks, -1);
+    lens_out[i] = sq.len;
+  }
   if (num_cow_out) *num_cow_out = np;
   return pa::ok();
 }

@@ -516,3 +516,73 @@ def test_decode_step_shared_rejects_bad_arguments_before_any_launch():
     fake = C.c_void_p(256)                                       # never dereferenced
     assert call(groups=0, rows=0, max_group=0, prefix=fake, ws=fake,
                 ws_bytes=need - 1) == PA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pa_bm_step_matches_model_append_then_tables(seed):
+    """pa_bm_step against the allocator model over random op sequences: each
+    batch reservation goes through the one-call step (starting from a random,
+    often too small, table width, so the grow-and-retry path runs), and its
+    slots, copy pairs, tables and lengths equal the model's append_slots then
+    block_tables; failures give the model's error code and change nothing."""
+    from tests.test_allocator_model import apply_model
+    ops_, N = random_ops(seed + 100, n_ops=400, num_blocks=80)
+    order = np.random.default_rng(seed + 7).permutation(N)
+    am = AllocatorModel(N, 16, order)
+    bm = pk.BlockManager(N, 16, order)
+    rng = np.random.default_rng(seed)
+    steps = 0
+    for op in ops_:
+        if op[0] != "append":
+            want, got = apply_model(am, op), _c_apply(bm, op)
+            assert (got == ("err", _CODE[want[1]])) if want[0] == "err" else got == want, op
+            continue
+        ids = list(op[1])
+        want = apply_model(am, op)
+        before = bm.stats()
+        try:
+            s, c, t, l = bm.step(ids, int(rng.integers(0, 4)))
+            got = ("ok", s.tolist(), c.tolist())
+        except pk.PAError as e:
+            got = ("err", e.code)
+        if want[0] == "err":
+            assert got == ("err", _CODE[want[1]]), (op, want, got)
+            assert bm.stats() == before
+            continue
+        assert got == want, op
+        steps += 1
+        mb = max([1] + [len(am.tables[i]) for i in ids])
+        t_m, l_m = am.block_tables(ids, mb)
+        assert t.shape == t_m.shape and np.array_equal(t, t_m) and np.array_equal(l, l_m)
+    assert steps > 10
+
+
+def test_pa_bm_step_width_and_argument_errors_change_nothing():
+    h = pk.lib()
+    bm = pk.BlockManager(8, 16)
+    bm.add_seq(1, 32)                       # the step needs a third block
+    bm.add_seq(2, 5)
+    n = 2
+    ids = np.array([1, 2], dtype=np.int64)
+    slots = np.empty(n, np.int64)
+    pairs = np.empty((n, 2), np.int32)
+    tables = np.empty((n, 2), np.int32)
+    lens = np.empty(n, np.int32)
+    ncow, need = C.c_int32(0), C.c_int32(0)
+    before = bm.stats()
+    st = h.pa_bm_step(bm._h, ids.ctypes.data, n, 2, slots.ctypes.data, pairs.ctypes.data,
+                      C.byref(ncow), tables.ctypes.data, lens.ctypes.data, C.byref(need))
+    assert st == PA_ERR_INVALID_ARG and need.value == 3 and bm.stats() == before
+    dup = np.array([2, 2], dtype=np.int64)
+    wide = np.empty((n, 4), np.int32)
+    st = h.pa_bm_step(bm._h, dup.ctypes.data, n, 4, slots.ctypes.data, pairs.ctypes.data,
+                      C.byref(ncow), wide.ctypes.data, lens.ctypes.data, C.byref(need))
+    assert st == PA_ERR_INVALID_ARG and bm.stats() == before
+    unknown = np.array([1, 9], dtype=np.int64)
+    st = h.pa_bm_step(bm._h, unknown.ctypes.data, n, 4, slots.ctypes.data, pairs.ctypes.data,
+                      C.byref(ncow), wide.ctypes.data, lens.ctypes.data, C.byref(need))
+    assert st == PA_ERR_UNKNOWN_SEQ and bm.stats() == before
+    assert h.pa_bm_step(bm._h, ids.ctypes.data, n, 4, None, None, None, None, None,
+                        C.byref(need)) == PA_ERR_INVALID_ARG
+    s, c, t, l = bm.step(ids, 1)
+    assert t.shape == (2, 3) and l.tolist() == [33, 6] and s.tolist()[1] == t[1, 0] * 16 + 5
