@@ -527,11 +527,16 @@ size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * once per sequence (page 2, hubblespacetelescope blog, section
  * 「OSの知恵をGPUへ…」, third bullet: shared blocks are held once by
  * reference count; page 3, abeam.tech review, section
- * 「並列サンプリングやビームサーチでの共有」).  Three passes on `stream`:
+ * 「並列サンプリングやビームサーチでの共有」).  Three passes:
  *   1. per group and KV head, the members' queries (members x query heads
  *      of that KV head) attend the shared prefix [0, prefix_len) through
- *      the first member's table, on the matrix cores; the normalised rows
- *      and their softmax maxima and sums go to the workspace;
+ *      the first member's table, on the matrix cores, possibly cut into a
+ *      few key ranges; each range's unnormalised rows and their softmax
+ *      maxima and sums go to the workspace.  This pass runs on a stream the
+ *      library keeps per device (default priority), after the work already
+ *      queued on `stream` (an event) and beside pass 2; the merge on
+ *      `stream` waits for it (another event), so the call is ordered on
+ *      `stream` like any other;
  *   2. the even split attends each sequence from its prefix_len (0 for
  *      sequences in no group) to its end, with the step's new tokens fused
  *      in as in pa_decode_step;
