@@ -431,10 +431,18 @@ __device__ __forceinline__ void prologue4(const Params& pr, int b, int g, int bl
 // template parameter, so the kernel carries one copy of the loop.
 // Positions before tok_begin (a sliding window's start inside the range's
 // first block) are masked like positions past tok_end.
-template <typename T, int D, int NG>
+// after_start(): called once the range's first loads are out and its start
+// checks are done; the caller issues the next range's prologue there, so
+// that no wait at this range's start stands behind those loads (loads
+// return in order).
+struct NoStartHook {
+  __device__ void operator()() const {}
+};
+template <typename T, int D, int NG, typename StartHook = NoStartHook>
 __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_begin, int nblk,
                                         int tok_begin, int tok_end, WaveState4<D, NG>& st,
-                                        const Prologue4<D, NG>& pre, bool with_new) {
+                                        const Prologue4<D, NG>& pre, bool with_new,
+                                        StartHook after_start = StartHook{}) {
   using Fmt = Kv4<T>;
   using Mma = typename Fmt::Mma;
   constexpr bool kCodes = Fmt::kCodes;
@@ -453,19 +461,19 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   // Table entries, 64 per register (lane i holds entry 64*c + i of chunk c).
   auto load_chunk = [&](int c) -> int {
     const int k = c * 64 + lane;
-    const int e = k < nblk ? trow[k] : 0;
-    const bool lane_bad = k < nblk && (e < 0 || e >= pr.num_blocks);
+    return k < nblk ? trow[k] : 0;
+  };
+  // A chunk is loaded one chunk ahead and checked when it becomes the
+  // current one: checking it at once would make the wave wait for it, and
+  // (loads return in order) for every load issued before it.
+  auto check_chunk = [&](int c, int e) -> int {
+    const bool lane_bad = c * 64 + lane < nblk && (e < 0 || e >= pr.num_blocks);
     if (__any(lane_bad)) st.bad = true;
     return lane_bad ? 0 : e;
   };
   int chunk = 0;
-  int tcur;
-  {
-    const bool lane_bad = lane < nblk && (pre.tab < 0 || pre.tab >= pr.num_blocks);
-    if (__any(lane_bad)) st.bad = true;
-    tcur = lane_bad ? 0 : pre.tab;
-  }
-  int tnext = nblk > 64 ? load_chunk(1) : 0;
+  int tcur = check_chunk(0, pre.tab);
+  int tnext = 0;   // loaded once the first quad's loads are out
   // Physical blocks of quad qd (qd increases across calls; the 4 entries of a
   // quad never straddle a 64-entry chunk); blocks past the range map to its
   // last block.
@@ -473,7 +481,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     const int c = qd >> 4;
     if (c != chunk) {
       chunk = c;
-      tcur = tnext;
+      tcur = check_chunk(c, tnext);
       tnext = (c + 1) * 64 < nblk ? load_chunk(c + 1) : 0;
     }
 #pragma unroll
@@ -511,12 +519,12 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     }
   };
 
-  // New token of the step (fused append): staged in LDS at the start, put
-  // into the last quad's registers and written to its pool slot.  8-bit
-  // pools stage its codes (encoded from the bf16 rows as the quantizing
-  // append encodes them), D/4 words of 4 codes per pool.
-  // The rows are loaded here and consumed (encoded, stored to LDS) only after
-  // the first quad's loads are issued, so no wait sits in front of them.
+  // New token of the step (fused append): its rows are loaded once the
+  // first quad's loads are out, staged in LDS before the last quad, put into
+  // the last quad's registers and written to its pool slot.  8-bit pools
+  // stage its codes (encoded from the bf16 rows as the quantizing append
+  // encodes them), D/4 words of 4 codes per pool.  The slot is read with a
+  // scalar load, which no vector load waits for.
   constexpr int kStageWords = D * T::kBytes / 4;
   // one staging area per wave of the workgroup (the even split runs 4 waves
   // per workgroup)
@@ -526,15 +534,28 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   using StageT = std::conditional_t<kCodes, uint2, uint32_t>;
   StageT stage_k{}, stage_v{};
   int64_t new_slot = -1;
-  if (with_new) {
-    // fetched with the first quad's loads, not at the end of the range
-    new_slot = pr.slots[b];
-    if (lane < kStageWords) {
+  auto load_new = [&]() {
+    if (with_new)
+      new_slot = ((const __attribute__((address_space(4))) int64_t*)
+                      pr.slots)[__builtin_amdgcn_readfirstlane(b)];
+    if (with_new && lane < kStageWords) {
       const int64_t nrow = (static_cast<int64_t>(b) * pr.Hkv + g) * D;
       stage_k = reinterpret_cast<const StageT*>(static_cast<const uint16_t*>(pr.k_new) + nrow)[lane];
       stage_v = reinterpret_cast<const StageT*>(static_cast<const uint16_t*>(pr.v_new) + nrow)[lane];
     }
-  }
+  };
+  auto stage_new = [&]() {
+    if (lane < kStageWords) {
+      if constexpr (kCodes) {
+        s_new[0][lane] = encode4_bf16<T>(stage_k, pr.enc_k);
+        s_new[1][lane] = encode4_bf16<T>(stage_v, pr.enc_v);
+      } else {
+        s_new[0][lane] = stage_k;
+        s_new[1][lane] = stage_v;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
   // Puts the new token into the last quad's registers (its pool slot may
   // still hold an older value for this wave's loads).
   // The new token sits at position tok_end - 1, in the last quad: lane qt
@@ -781,18 +802,11 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
   quad_phys(0, ph);
   issue_k();
   issue_v();
-  if (with_new) {
-    if (lane < kStageWords) {
-      if constexpr (kCodes) {
-        s_new[0][lane] = encode4_bf16<T>(stage_k, pr.enc_k);
-        s_new[1][lane] = encode4_bf16<T>(stage_v, pr.enc_v);
-      } else {
-        s_new[0][lane] = stage_k;
-        s_new[1][lane] = stage_v;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_new();
+  if (nblk > 64) tnext = load_chunk(1);
+  after_start();
+  __builtin_amdgcn_sched_barrier(0);
   // steady state: K of the next quad is issued once QK has consumed the
   // current one, V of the next quad once P.V has.  The scheduling barriers
   // keep the compiler from hoisting the loads above the matrix ops that still
@@ -816,6 +830,7 @@ __device__ __forceinline__ void attend4(const Params& pr, int b, int g, int blk_
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (with_new) stage_new();
   const bool at_table = with_new && new_at_table();
   if (at_table) substitute_k();
   uint2 phi[NG], plo[NG];
@@ -890,11 +905,16 @@ struct Engine4 {
   __device__ static void prologue(const Params& pr, int b, int g, int blk_begin, Pre& pre) {
     prologue4<D, NG>(pr, b, g, blk_begin, pre);
   }
+  template <typename StartHook = NoStartHook>
   __device__ static void attend_rt(const Params& pr, int b, int g, int blk_begin, int nblk,
                                    int tok_begin, int tok_end, State& st, const Pre& pre,
-                                   bool with_new) {
-    attend4<T, D, NG>(pr, b, g, blk_begin, nblk, tok_begin, tok_end, st, pre, with_new);
+                                   bool with_new, StartHook after_start = StartHook{}) {
+    attend4<T, D, NG>(pr, b, g, blk_begin, nblk, tok_begin, tok_end, st, pre, with_new,
+                      after_start);
   }
+  // waits for the prologue's table entries here (an empty asm that reads
+  // the register)
+  __device__ static void settle(const Pre& pre) { asm volatile("" ::"v"(pre.tab)); }
   __device__ static void reset(State& st) { reset_state4(st); }
   __device__ static void emit(const Params& pr, int b, int g, int slot, State& st) {
     emit_state4(pr, b, g, slot, st);
@@ -1105,20 +1125,27 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
   Seg cur = make_seg(u_begin, b, base);
   typename Eng::Pre pre;
   Eng::prologue(pr, cur.b, cur.g, cur.blk_begin, pre);
+  // The table entries a segment checks first are made resident before the
+  // loop and, for the next segment, at the end of each segment (when they
+  // are long in): the wait then never falls at a segment's start, where it
+  // would also wait for the previous segment's partial stores.
+  Eng::settle(pre);
   typename Eng::State st;
   while (true) {
     // the next segment's Q and table entries are fetched while this one
-    // streams, so the switch costs no dependent round trip
+    // streams, so the switch costs no dependent round trip; they go out
+    // once this segment's first loads are out and its start checks done
+    // (a start check issued after them would wait for them too)
     const bool more = cur.seg_end < u_end;
     Seg nxt = cur;
     typename Eng::Pre pre_next;
-    if (more) {
-      nxt = next_seg(cur);
-      Eng::prologue(pr, nxt.b, nxt.g, nxt.blk_begin, pre_next);
-    }
+    if (more) nxt = next_seg(cur);
     Eng::reset(st);
     Eng::attend_rt(pr, cur.b, cur.g, cur.blk_begin, cur.nblk, cur.tok_begin, cur.tok_end, st,
-                   pre, pr.k_new != nullptr && cur.tok_end == cur.L);
+                   pre, pr.k_new != nullptr && cur.tok_end == cur.L, [&]() {
+                     if (more) Eng::prologue(pr, nxt.b, nxt.g, nxt.blk_begin, pre_next);
+                   });
+    if (more) Eng::settle(pre_next);
     const int first_chunk = cur.range_first / sp.C;
     const int nslots = (cur.range_first + cur.nub - 1) / sp.C - first_chunk + 1;
     // a sequence with a shared prefix always leaves a partial: the merge
