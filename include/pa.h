@@ -553,7 +553,10 @@ size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   member's length or table is out of bounds.  max_group_size: the largest
  *   group.  workspace: at least pa_decode_shared_workspace_bytes(...)
  *   bytes, 256-byte aligned; needs no initialisation; calls that share it
- *   must not overlap.
+ *   must not overlap.  The prefix pass stamps each row it writes with a
+ *   per-call number and the merge clears the stamps it reads, so rows left
+ *   from an earlier call, or an earlier replay of a captured call (whose
+ *   number is fixed at capture), are never taken for this call's.
  * Other arguments and the slot rules as for pa_decode_step.  Supported:
  * fp16/bf16 pools on the matrix cores (PA_ERR_UNSUPPORTED for other dtypes
  * or under pa_set_decode_kernel(PA_KERNEL_GENERIC)), block_size 16, head_dim

@@ -79,7 +79,7 @@ struct Params {
   const int32_t* prefix;       // [B]
   const float* pre_out;        // [pre_pieces][B][Hq][D]
   const float2* pre_ml;        // [pre_pieces][B][Hq]
-  const uint32_t* pre_stamp;   // [pre_pieces][B]
+  uint32_t* pre_stamp;         // [pre_pieces][B][Hq] (the merge clears what it reads)
   uint32_t epoch;
   int pre_pieces;
 };
@@ -1256,8 +1256,7 @@ __global__ __launch_bounds__(64 * kMergeRowsPerGroup) void merge_kernel(Params p
         const float* ml = reinterpret_cast<const float*>(pr.pre_ml + p * plane + row);
         pre_ml[p] = make_float2(uniform_load(ml), uniform_load(ml + 1));
         load_row<E>(pre_o[p], pr.pre_out + (p * plane + row) * D + d0);
-        stamped = stamped &&
-                  uniform_load(pr.pre_stamp + static_cast<int64_t>(p) * pr.B + b) == pr.epoch;
+        stamped = stamped && uniform_load(pr.pre_stamp + p * plane + row) == pr.epoch;
       }
     }
   }
@@ -1333,6 +1332,14 @@ __global__ __launch_bounds__(64 * kMergeRowsPerGroup) void merge_kernel(Params p
   const bool has_pre = pre != 0;
   // an unusable prefix length, or a prefix the prefix pass did not attend
   // in this call (the sequence in no group, or its prefix not its group's)
+  if (has_pre && lane == 0) {
+    // the stamps are consumed: a later call (or a later replay of a captured
+    // one, whose epoch is the same) that does not write this row sees 0
+    const int64_t plane = static_cast<int64_t>(pr.B) * pr.Hq;
+#pragma unroll
+    for (int p = 0; p < kMaxPrefixPieces; ++p)
+      if (p < pr.pre_pieces) pr.pre_stamp[p * plane + row] = 0;
+  }
   if (has_pre && (!prefix_ok(pre, L) || !stamped)) {
     float r[E];
 #pragma unroll
@@ -1681,7 +1688,7 @@ struct SharedPrefix {
   const int32_t* prefix;
   const float* pre_out;
   const float2* pre_ml;
-  const uint32_t* pre_stamp;
+  uint32_t* pre_stamp;
   uint32_t epoch;
   int pieces;
   hipEvent_t join;   // recorded after the prefix pass on another stream: the merge waits
@@ -2040,7 +2047,7 @@ SharedWorkspace shared_workspace_parts(int32_t B, int32_t Hq, int32_t Hkv, int32
   const size_t P = kMaxPrefixPieces;
   w.pre_ml = w.pre_out + align256(P * B * Hq * D * sizeof(float));
   w.stamp = w.pre_ml + align256(P * B * Hq * sizeof(float2));
-  w.total = w.stamp + align256(P * B * sizeof(uint32_t));
+  w.total = w.stamp + align256(P * B * Hq * sizeof(uint32_t));
   return w;
 }
 

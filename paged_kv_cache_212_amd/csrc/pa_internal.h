@@ -21,7 +21,7 @@ pa_status ok();
 // first member's table, cut into `pieces` key ranges.  Piece p of each
 // member row writes its partial to slot p: the unnormalised weighted sum of V
 // to pre_out [pieces][B][Hq][D], the log2-domain (max, sum of 2^(s - max))
-// pair to pre_ml [pieces][B][Hq][2] and `epoch` to pre_stamp [pieces][B].
+// pair to pre_ml [pieces][B][Hq][2] and `epoch` to pre_stamp [pieces][B][Hq].
 // Members whose prefix length or prefix blocks differ from the first
 // member's, and every member of a group with an unusable length or table,
 // are left unwritten.  Sizes validated by the caller.

@@ -72,14 +72,15 @@ struct PrefillParams {
   // causal mask (every row sees the whole piece).  Each row's partial goes
   // to slot p at the member's batch row: the unnormalised weighted sum of V
   // to pre_out, the log2-domain (max, sum of 2^(s - max)) to pre_ml, and the
-  // call's epoch to pre_stamp.  A row whose member is out of the batch, or
-  // whose prefix length or prefix blocks differ from the group's, is not
-  // written (nor is any row of a group whose length or table is unusable).
+  // call's epoch to pre_stamp (per row; the merge clears it once read).  A
+  // row whose member is out of the batch, or whose prefix length or prefix
+  // blocks differ from the group's, is not written (nor is any row of a
+  // group whose length or table is unusable).
   const int32_t* rows;      // [T] batch index of each row
   const int32_t* prefix_len;  // [num_seqs] prefix tokens per batch sequence
   float* pre_out;           // [pieces][num_seqs][Hq][D]
   float2* pre_ml;           // [pieces][num_seqs][Hq]
-  uint32_t* pre_stamp;      // [pieces][num_seqs]
+  uint32_t* pre_stamp;      // [pieces][num_seqs][Hq]
   uint32_t epoch;
   int num_seqs;
   int pieces;
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
           // row's quad holds the same max)
           if (n == 0) {
             pr.pre_ml[slot * pr.Hq + h] = make_float2(mq, lr);
-            if (h == 0) pr.pre_stamp[slot] = pr.epoch;
+            pr.pre_stamp[slot * pr.Hq + h] = pr.epoch;
           }
         }
       } else if (i0 + r < nq) {

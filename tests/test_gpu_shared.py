@@ -192,3 +192,89 @@ def test_full_size_parallel_sampling_every_row(kw, coded):
     assert len(start) - 1 == 32 and mg == 8 and set(pre.cpu().tolist()) == {1024}
     check_every_row(case, got["out"], CODED_TOL if coded else REG_TOL["bf16"], case.name)
     check_every_gather(case, got)
+
+
+def _shared_inputs():
+    pk = require_gpu()
+    case = small_case("cow_parallel_bf16", parked_forks=False)
+    got = run_gpu_step(case, shared=2)
+    cache, plan = got["cache"], got["plan"]
+    nr = torch.as_tensor(case.new_rows(), device="cuda")
+    k_new = case.k_tok.cuda().index_select(0, nr).contiguous()
+    v_new = case.v_tok.cuda().index_select(0, nr).contiguous()
+    return pk, case, got, cache, plan, k_new, v_new
+
+
+def test_shared_step_on_a_side_stream_matches_the_default_stream():
+    """The call on a caller's side stream (workspace allocated for that
+    stream): the library forks its prefix pass from that stream and joins it
+    back before the merge; the rows equal the default-stream call's bit for
+    bit."""
+    pk, case, got, cache, plan, k_new, v_new = _shared_inputs()
+    pre, rows, start, mg = got["shared"]
+    ref = torch.empty(got["out"].shape, device="cuda")
+    pk.ops.decode_step_shared(ref, got["q"], cache.k_pool, cache.v_pool, k_new, v_new,
+                              plan.d_slots, plan.d_tables, plan.d_lens, plan.max_context_len,
+                              pre, rows, start, mg)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out = torch.empty(got["out"].shape, device="cuda")
+        pk.ops.decode_step_shared(out, got["q"], cache.k_pool, cache.v_pool, k_new, v_new,
+                                  plan.d_slots, plan.d_tables, plan.d_lens,
+                                  plan.max_context_len, pre, rows, start, mg, stream=side)
+    side.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_shared_step_captured_in_a_graph_replays_like_the_eager_call():
+    """The step captured into a HIP graph (the prefix pass's fork and join are
+    captured as event nodes) and replayed three times, with eager work and
+    synchronisations between the replays: every replay's rows equal the
+    eager call's bit for bit."""
+    pk, case, got, cache, plan, k_new, v_new = _shared_inputs()
+    pre, rows, start, mg = got["shared"]
+    B, Hq, D = got["out"].shape
+    ws = pk.ops.decode_shared_workspace(B, Hq, case.num_kv_heads, D, plan.max_context_len,
+                                        got["q"].dtype)
+    eager = torch.empty((B, Hq, D), device="cuda")
+    pk.ops.decode_step_shared(eager, got["q"], cache.k_pool, cache.v_pool, k_new, v_new,
+                              plan.d_slots, plan.d_tables, plan.d_lens, plan.max_context_len,
+                              pre, rows, start, mg, workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.empty((B, Hq, D), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pk.ops.decode_step_shared(out, got["q"], cache.k_pool, cache.v_pool, k_new, v_new,
+                                  plan.d_slots, plan.d_tables, plan.d_lens,
+                                  plan.max_context_len, pre, rows, start, mg, workspace=ws,
+                                  stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        ws.zero_()                                   # no stale partial or stamp helps
+        junk = torch.randn(1 << 16, device="cuda") * (i + 1)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        del junk
+    # The plan edited in place between replays (the graph keeps its buffers):
+    # group 1 emptied.  Its members keep their prefix lengths, but no prefix
+    # pass writes their rows in this replay; the rows an earlier replay wrote
+    # carry the same epoch (fixed at capture) and must not be taken: their
+    # stamps were cleared by the merge that read them, so these rows are NaN.
+    g1 = [int(r) for r in rows[int(start[1]):int(start[2])]]
+    start[2] = start[1]
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    o, e = out.cpu().numpy(), eager.cpu().numpy()
+    for i in range(B):
+        if i in g1:
+            assert np.isnan(o[i]).all(), f"row {i}"
+        else:
+            assert np.array_equal(o[i], e[i]), f"row {i}"
