@@ -15,6 +15,9 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte streaming load of K/V (each tile is read once per step): the
@@ -43,19 +46,22 @@ struct Mfma<BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, p),
                                                    __builtin_bit_cast(bf16x8_t, v), c, 0, 0, 0);
   }
+  // As split below, for 2 (split2) or 8 weights, two per instruction where
+  // the chip has it: the high parts of two weights are their upper halves
+  // side by side (one byte permute), the two remainders are rounded to bf16
+  // together.
+  __device__ static inline void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
+    hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);   // upper halves of u0, u1
+    const f32x2_t r = {p0 - __uint_as_float(u0 & 0xFFFF0000u),
+                       p1 - __uint_as_float(u1 & 0xFFFF0000u)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+  }
   __device__ static inline void split8(const float pe[8], uint4& hi, uint4& lo) {
-    uint32_t h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t u = __float_as_uint(pe[e]);
-      h[e] = u >> 16;
-      const float r = pe[e] - __uint_as_float(u & 0xFFFF0000u);
-      l[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r));
-    }
-    hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                    h[6] | (h[7] << 16));
-    lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                    l[6] | (l[7] << 16));
+    split2(pe[0], pe[1], hi.x, lo.x);
+    split2(pe[2], pe[3], hi.y, lo.y);
+    split2(pe[4], pe[5], hi.z, lo.z);
+    split2(pe[6], pe[7], hi.w, lo.w);
   }
   // p (>= 0) = hi + lo with hi = p truncated to bf16 (exact remainder) and
   // lo = remainder rounded to bf16.
@@ -79,19 +85,19 @@ struct Mfma<F16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, p),
                                                   __builtin_bit_cast(f16x8_t, v), c, 0, 0, 0);
   }
+  // As split below, for 2 (split2) or 8 weights, rounding two per
+  // instruction.
+  __device__ static inline void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const f16x2_t hh = __builtin_convertvector(f32x2_t{p0, p1}, f16x2_t);
+    const f32x2_t r = {p0 - static_cast<float>(hh[0]), p1 - static_cast<float>(hh[1])};
+    hi = __builtin_bit_cast(uint32_t, hh);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, f16x2_t));
+  }
   __device__ static inline void split8(const float pe[8], uint4& hi, uint4& lo) {
-    uint32_t h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const _Float16 hh = static_cast<_Float16>(pe[e]);
-      const float r = pe[e] - static_cast<float>(hh);
-      h[e] = __builtin_bit_cast(uint16_t, hh);
-      l[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(r));
-    }
-    hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                    h[6] | (h[7] << 16));
-    lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                    l[6] | (l[7] << 16));
+    split2(pe[0], pe[1], hi.x, lo.x);
+    split2(pe[2], pe[3], hi.y, lo.y);
+    split2(pe[4], pe[5], hi.z, lo.z);
+    split2(pe[6], pe[7], hi.w, lo.w);
   }
   __device__ static inline f32x4_t qk(uint4 k, uint4 q, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, k),

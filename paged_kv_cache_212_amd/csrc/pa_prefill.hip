@@ -280,17 +280,23 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     else if constexpr (bi == 2) return lds2;
     else return lds3;
   };
+  // The 64 words a wave moves per load lie in one tile (kTileU4 is a
+  // multiple of 64), so the tile's global base and the LDS destination are
+  // the same for the whole wave (scalar registers); only the 32-bit offset
+  // inside the tile is per lane.
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   auto gload_lds = [&](int pp, auto bc) {
     const int p0 = phys_of(min(2 * pp, nblk - 1)), p1 = phys_of(min(2 * pp + 1, nblk - 1));
 #pragma unroll
     for (int r = 0; r < kStage; ++r) {
-      const int c = static_cast<int>(threadIdx.x) + r * 64 * WPG;
-      const int part = c / kTileU4, idx = c % kTileU4;
+      const int c0 = wv * 64 + r * 64 * WPG;            // the wave's first word
+      const int part = c0 / kTileU4, idx = c0 % kTileU4 + lane;
       // V tiles: LDS slot idx holds chunk vswz(idx) (see lread_v)
       const int sidx = part < 2 ? idx : vswz(idx);
-      const char* src = (part < 2 ? kbase : vbase) + ((part & 1) ? p1 : p0) * block_stride +
-                        sidx * 16;
-      uint4* dst = &buf_of(bc)[0][0] + (c - lane);      // the wave's first word
+      const char* base = (part < 2 ? kbase : vbase) +
+                         static_cast<int64_t>((part & 1) ? p1 : p0) * block_stride;
+      const char* src = base + static_cast<uint32_t>(sidx * 16);
+      uint4* dst = &buf_of(bc)[0][0] + c0;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
@@ -377,12 +383,16 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
     if ((2 * pp + 2) * kBlockSize - 1 > (kShared ? Lk - 1 : first_pos + i0)) {
       const int kpos0 = 2 * pp * kBlockSize + 4 * j;      // key position of s0[0]
 #pragma unroll
-      for (int t = 0; t < TQ; ++t)
+      for (int t = 0; t < TQ; ++t) {
+        // key kpos0 + k is visible to the lane's query iff k <= dq (compares
+        // with constants, all inside this branch)
+        const int dq = qpos[t] - kpos0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sv[t][e] = (kpos0 + e <= qpos[t]) ? sv[t][e] : -INFINITY;
-          sv[t][4 + e] = (kpos0 + kBlockSize + e <= qpos[t]) ? sv[t][4 + e] : -INFINITY;
+          sv[t][e] = e <= dq ? sv[t][e] : -INFINITY;
+          sv[t][4 + e] = kBlockSize + e <= dq ? sv[t][4 + e] : -INFINITY;
         }
+      }
     }
   };
   // Online softmax update of the TQ tiles from their scores, and P split into
@@ -400,12 +410,12 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
   // all precede the pair keeps m = -inf rows only while no key was valid; the
   // first pair holds key 0, valid for every query, so m_run is finite from
   // there on.
-  auto softmax = [&](float (&sv)[TQ][8], uint4 (&phi)[TQ], uint4 (&plo)[TQ]) {
-    bool over = false;
+  auto rescale_test = [&](float (&sv)[TQ][8]) {
+    bool over = false;   // (bitwise: no short-circuit branches)
 #pragma unroll
     for (int t = 0; t < TQ; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) over = over || sv[t][e] > thr[t];
+      for (int e = 0; e < 8; ++e) over |= sv[t][e] > thr[t];
     if (__any(over)) {
 #pragma unroll
       for (int t = 0; t < TQ; ++t) {
@@ -428,15 +438,27 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
         thr[t] = (mn + kRescaleSlack) / pr.scale_log2;
       }
     }
+  };
+  // Weights 2k, 2k + 1 of tile t: their sum, and their parts in word k of
+  // the P.V operands.
+  auto weight_pair = [&](int t, int k, const float (&sv)[TQ][8], uint32_t& hi, uint32_t& lo) {
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][2 * k], pr.scale_log2, -m_run[t]));
+    const float p1 =
+        __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][2 * k + 1], pr.scale_log2, -m_run[t]));
+    Mfma<T>::split2(p0, p1, hi, lo);
+    return p0 + p1;
+  };
+  auto weights = [&](int t, const float (&sv)[TQ][8], uint4& phi, uint4& plo) {
+    const float s0 = weight_pair(t, 0, sv, phi.x, plo.x);
+    const float s1 = weight_pair(t, 1, sv, phi.y, plo.y);
+    const float s2 = weight_pair(t, 2, sv, phi.z, plo.z);
+    const float s3 = weight_pair(t, 3, sv, phi.w, plo.w);
+    l_lane[t] += (s0 + s1) + (s2 + s3);
+  };
+  auto softmax = [&](float (&sv)[TQ][8], uint4 (&phi)[TQ], uint4 (&plo)[TQ]) {
+    rescale_test(sv);
 #pragma unroll
-    for (int t = 0; t < TQ; ++t) {
-      float pe[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], pr.scale_log2, -m_run[t]));
-      l_lane[t] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-      Mfma<T>::split8(pe, phi[t], plo[t]);
-    }
+    for (int t = 0; t < TQ; ++t) weights(t, sv, phi[t], plo[t]);
   };
 
   // V rows at positions >= L are zeroed, so unwritten slots never reach O
@@ -446,9 +468,9 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
       const int kb = 2 * pp + u;
       if ((kb + 1) * kBlockSize > Lk) {
         // the block reaches past the sequence: zero V of unwritten positions
-        const int kp = kb * kBlockSize + 4 * j;
-        const uint32_t mx = (kp + 0 < Lk ? 0x0000FFFFu : 0u) | (kp + 1 < Lk ? 0xFFFF0000u : 0u);
-        const uint32_t my = (kp + 2 < Lk ? 0x0000FFFFu : 0u) | (kp + 3 < Lk ? 0xFFFF0000u : 0u);
+        const int nv = Lk - (kb * kBlockSize + 4 * j);     // the lane's keys k < nv are written
+        const uint32_t mx = (0 < nv ? 0x0000FFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u);
+        const uint32_t my = (2 < nv ? 0x0000FFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int d = 0; d < NTL; ++d) {
           vreg[u][d].x &= mx;
@@ -457,13 +479,34 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
       }
     }
   };
+  auto pv_tile = [&](int t, int d, uint4 phi, uint4 plo) {
+    const uint4 v = make_uint4(vreg[0][d].x, vreg[0][d].y, vreg[1][d].x, vreg[1][d].y);
+    acc[t][d] = Mfma<T>::pv8(phi, v, acc[t][d]);
+    acc[t][d] = Mfma<T>::pv8(plo, v, acc[t][d]);
+  };
   auto pv = [&](int t, uint4 phi, uint4 plo) {
 #pragma unroll
-    for (int d = 0; d < NTL; ++d) {
-      const uint4 v = make_uint4(vreg[0][d].x, vreg[0][d].y, vreg[1][d].x, vreg[1][d].y);
-      acc[t][d] = Mfma<T>::pv8(phi, v, acc[t][d]);
-      acc[t][d] = Mfma<T>::pv8(plo, v, acc[t][d]);
+    for (int d = 0; d < NTL; ++d) pv_tile(t, d, phi, plo);
+  };
+  // P.V of tile t - 1 with the weights of tile t (independent work for the
+  // matrix and the vector units): per weight pair k of tile t, the P.V of
+  // output tiles NTL/4 * k ..; scheduling barriers keep each group together.
+  auto pv_with_weights = [&](int t, const float (&sv)[TQ][8], uint4 (&phi)[TQ],
+                             uint4 (&plo)[TQ]) {
+    constexpr int kPer = NTL / 4;
+    float s[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = kPer * k; d < kPer * (k + 1); ++d) pv_tile(t - 1, d, phi[t - 1], plo[t - 1]);
+      uint32_t h, l;
+      s[k] = weight_pair(t, k, sv, h, l);
+      (k == 0 ? phi[t].x : k == 1 ? phi[t].y : k == 2 ? phi[t].z : phi[t].w) = h;
+      (k == 0 ? plo[t].x : k == 1 ? plo[t].y : k == 2 ? plo[t].z : plo[t].w) = l;
     }
+    __builtin_amdgcn_sched_barrier(0);
+    l_lane[t] += (s[0] + s[1]) + (s[2] + s[3]);
   };
 
   if constexpr (WPG == 1) {
@@ -511,11 +554,13 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
       uint4 phi[TQ], plo[TQ];
       float sv[TQ][8];
       qk_scores(pp, sv);
-      softmax(sv, phi, plo);
+      rescale_test(sv);
       lread_v(cur);
       mask_v(pp);
+      weights(0, sv, phi[0], plo[0]);
 #pragma unroll
-      for (int t = 0; t < TQ; ++t) pv(t, phi[t], plo[t]);
+      for (int t = 1; t < TQ; ++t) pv_with_weights(t, sv, phi, plo);
+      pv(TQ - 1, phi[TQ - 1], plo[TQ - 1]);
     };
     auto dstep = [&](int pp, auto ca, auto cb, auto fa, auto fb) {
       if (pp + 2 < npair) gload_lds(pp + 2, fa);
