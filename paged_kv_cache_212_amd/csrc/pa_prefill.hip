@@ -624,6 +624,389 @@ __global__ __launch_bounds__(64 * WPG, WPG > 1 ? (TQ > 1 ? 2 : 3) : 1) void pref
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Ping-pong prefill (G a multiple of 4): eight waves per workgroup, two per
+// SIMD, in two groups of four (the four query heads of one KV head).  Group
+// 0 takes queries 0 .. 31 of the workgroup's 64-query block, group 1 queries
+// 32 .. 63; both read the same key pairs from LDS.  The work of a key pair is
+// cut into a matrix phase (P.V of the previous pair, then Q.K^T of this one)
+// and a vector phase (causal mask, rescale test, weights and their split),
+// and the groups run them one phase apart with a workgroup barrier between
+// phases: while one wave of a SIMD issues matrix ops, the other issues the
+// vector work, so the matrix pipe and the vector ALU run side by side.
+// Pair m is staged in LDS buffer m % 4 from phase 2m - 4 on; the wait at the
+// end of phase 2m - 1 leaves only pair m + 1's loads in flight.  Every wave
+// runs the same phases and barriers; a wave skips the work of pairs past its
+// own queries (and all of it when its group has no queries).
+// ---------------------------------------------------------------------------
+constexpr int kPPWaves = 8;
+constexpr int kPPQueries = 64;   // query tokens per workgroup
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kPPWaves, 1) void prefill_pp_kernel(PrefillParams pr) {
+  constexpr int TQ = 2;
+  constexpr int NKK = D / 32, NTL = D / 16;
+  constexpr int64_t kTileBytes = static_cast<int64_t>(D) * kBlockSize * 2;
+  constexpr int kTileU4 = static_cast<int>(kTileBytes / 16);
+  constexpr int kStage = 4 * kTileU4 / (64 * kPPWaves);     // loads per thread per pair
+  static_assert(kStage >= 1 && kStage * 64 * kPPWaves == 4 * kTileU4, "pair staging");
+  static_assert(kTileU4 % 64 == 0, "a wave's 64 words lie in one tile");
+
+  int lin = blockIdx.x;
+  const int g = lin % pr.Hkv;
+  lin /= pr.Hkv;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int grp = wave >> 2;
+  const int e_head = (lin % (pr.G / 4)) * 4 + (wave & 3);
+  lin /= pr.G / 4;
+  const int nqb = (pr.ntiles * kQTile + kPPQueries - 1) / kPPQueries;
+  const int qb = lin % nqb, b = lin / nqb;
+  const int h = g * pr.G + e_head;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, j = lane >> 4;
+
+  // (every early return below is uniform over the workgroup)
+  const int q0 = pr.qstart[b], q1 = pr.qstart[b + 1];
+  if (!(q0 >= 0 && q0 <= q1 && q1 <= pr.T)) return;     // no row can be trusted
+  const int nq = q1 - q0;
+  const int iwg = qb * kPPQueries;
+  if (iwg >= nq) return;
+  const int i0 = iwg + TQ * kQTile * grp;                 // the wave's first query
+  const bool active = i0 < nq;                            // (uniform over the group)
+  const int L = pr.lens[b];
+  float* orow = pr.out + (static_cast<int64_t>(q0) + i0) * pr.Hq * D + static_cast<int64_t>(h) * D;
+  auto nan_rows = [&]() {
+    if (!active) return;
+    for (int idx = lane; idx < TQ * kQTile * D; idx += 64) {
+      const int r = idx / D;
+      if (i0 + r < nq) orow[static_cast<int64_t>(r) * pr.Hq * D + idx % D] = __builtin_nanf("");
+    }
+  };
+  const bool seq_ok = L >= 0 && L <= pr.max_ctx && L <= pr.max_blocks * kBlockSize && nq <= L &&
+                      nq <= pr.max_qlen;
+  if (!seq_ok) {
+    nan_rows();   // length out of the declared bounds
+    return;
+  }
+
+  // Q (B operand) of tile t: query 16t + n of the wave, dims kk*32 + 8j .. +8
+  uint4 qr[TQ][NKK];
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) {
+    const int i = i0 + kQTile * t + n;
+    const bool real = i < nq;
+    const uint16_t* qb_ = static_cast<const uint16_t*>(pr.q) +
+                          ((real ? static_cast<int64_t>(q0) + i : 0) * pr.Hq + h) * D + j * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qr[t][kk] = real ? *reinterpret_cast<const uint4*>(qb_ + kk * 32) : make_uint4(0, 0, 0, 0);
+  }
+  const int first_pos = L - nq;                           // position of query 0
+  // key blocks of the workgroup, pairs of the workgroup and of the wave
+  const int nblk = (first_pos + min(nq, iwg + kPPQueries) - 1) / kBlockSize + 1;
+  const int npair = (nblk + 1) / 2;
+  const int npw = active ? ((first_pos + min(nq, i0 + TQ * kQTile) - 1) / kBlockSize + 2) / 2 : 0;
+
+  const char* kbase = static_cast<const char*>(pr.kpool) + g * kTileBytes;
+  const char* vbase = static_cast<const char*>(pr.vpool) + g * kTileBytes;
+  const int64_t block_stride = static_cast<int64_t>(pr.Hkv) * kTileBytes;
+  const int32_t* trow = pr.tables + static_cast<int64_t>(b) * pr.max_blocks;
+  // every table entry the workgroup reads is checked up front (each wave
+  // checks them all, so the outcome is the same in every wave)
+  bool bad = false;
+  for (int k = lane; k - lane < nblk; k += 64) {
+    const int e = k < nblk ? trow[k] : 0;
+    if (__any(e < 0 || e >= pr.num_blocks)) bad = true;
+  }
+  if (bad) {
+    nan_rows();
+    return;
+  }
+  const auto* trow_s = (const __attribute__((address_space(4))) int32_t*)trow;
+  auto phys_of = [&](int k) -> int { return trow_s[k]; };
+
+  // Four pair buffers of [K0 | K1 | V0 | V1] tiles, read at a per-lane
+  // offset plus a constant.  Separate arrays, so the compiler's wait
+  // insertion can tell the buffer being filled from the ones being read (in
+  // one array it waits for every load into LDS before any LDS read).
+  __shared__ uint4 lds0[4 * kTileU4];
+  __shared__ uint4 lds1[4 * kTileU4];
+  __shared__ uint4 lds2[4 * kTileU4];
+  __shared__ uint4 lds3[4 * kTileU4];
+  auto buf_of = [&](auto bc) -> uint4* {
+    constexpr int bi = decltype(bc)::value;
+    if constexpr (bi == 0) return lds0;
+    else if constexpr (bi == 1) return lds1;
+    else if constexpr (bi == 2) return lds2;
+    else return lds3;
+  };
+  // K: lane reads word (j*16 + n) + 64 kk of each K tile
+  const int k_lane = (j * 16 + n) * 16;
+  // V: chunk c sits in slot vswz(c); for the lane's chunks c = A + 16t + n
+  // (A = (j >> 1) * D, t < NTL), slot = (A + n) ^ s ^ t with s = (A / 16) & 7,
+  // so the byte address of tile t is v_lane ^ (t << 4) ^ (t << 8) (bits 8..10
+  // of v_lane are clear).
+  const int v_lane = ((((j >> 1) * D + n) ^ (((j >> 1) * D / 16) & 7)) * 16) + (j & 1) * 8;
+  // Pair pp's [K0 | K1 | V0 | V1] tiles, global -> LDS (V chunks swizzled)
+  auto gload_lds = [&](int pp, auto bc) {
+    if (pp >= npair) return;
+    const int p0 = phys_of(min(2 * pp, nblk - 1)), p1 = phys_of(min(2 * pp + 1, nblk - 1));
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) {
+      const int c0 = wave * 64 + r * 64 * kPPWaves;     // the wave's first word
+      const int part = c0 / kTileU4, idx = c0 % kTileU4 + lane;
+      const int sidx = part < 2 ? idx : vswz(idx);
+      const char* base = (part < 2 ? kbase : vbase) +
+                         static_cast<int64_t>((part & 1) ? p1 : p0) * block_stride;
+      // Issued as written (scalar base, 32-bit lane offset, the wave's LDS
+      // destination in m0; each lane's 16 bytes land at m0 + 16 * lane).
+      // The compiler does not see these loads, so it adds no waits for them
+      // before LDS reads (it cannot tell which buffer they fill): the waits
+      // at the end of each step below are the ones that order them.
+      const uint32_t off = static_cast<uint32_t>(sidx * 16);
+      const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf_of(bc) + c0));
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %1, %2"
+          :
+          : "s"(dst), "v"(off), "s"(base)
+          : "memory", "m0");
+    }
+  };
+
+  float m_run[TQ], l_lane[TQ], thr[TQ];
+  f32x4_t acc[TQ][NTL];
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) {
+    m_run[t] = -INFINITY;
+    thr[t] = -INFINITY;
+    l_lane[t] = 0.f;
+#pragma unroll
+    for (int d = 0; d < NTL; ++d) acc[t][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float sv[TQ][8];          // scores of the pair: matrix phase -> vector phase
+  uint4 phi[TQ], plo[TQ];   // its split weights: vector phase -> next matrix phase
+  // (defined from the start: a value left undefined on the paths that skip
+  // a pair costs registers across the phase branches)
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) {
+    phi[t] = plo[t] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[t][e] = 0.f;
+  }
+
+  // Matrix phase of pair m: P.V of pair m - 1 (weights from the previous
+  // vector phase), then the scores of pair m.
+  auto mfma_phase = [&](int m, auto bk, auto bv) {
+    const bool do_pv = m >= 1 && m - 1 < npw;
+    const bool do_qk = m < npw;
+    if (do_pv) {
+      uint2 vreg[2][NTL];
+      const char* vb = reinterpret_cast<const char*>(buf_of(bv)) + 2 * kTileBytes;
+      // (opaque: the NTL addresses are formed here, one XOR each, rather
+      // than hoisted out of the loop into as many registers)
+      int vl = v_lane;
+      asm volatile("" : "+v"(vl));
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        const char* vt = vb + (vl ^ ((t << 4) | (t << 8)));
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          vreg[u][t] = *reinterpret_cast<const uint2*>(vt + u * static_cast<int>(kTileBytes));
+      }
+      // V rows at positions >= L are zeroed, so unwritten slots never reach O
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int kb = 2 * (m - 1) + u;
+        if ((kb + 1) * kBlockSize > L) {
+          const int nv = (L - kb * kBlockSize) - 4 * j;
+          const uint32_t mx = (0 < nv ? 0x0000FFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u);
+          const uint32_t my = (2 < nv ? 0x0000FFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int d = 0; d < NTL; ++d) {
+            vreg[u][d].x &= mx;
+            vreg[u][d].y &= my;
+          }
+        }
+      }
+      // output tile by output tile, so V registers free up as P.V goes
+#pragma unroll
+      for (int d = 0; d < NTL; ++d) {
+        const uint4 v = make_uint4(vreg[0][d].x, vreg[0][d].y, vreg[1][d].x, vreg[1][d].y);
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) {
+          acc[t][d] = Mfma<T>::pv8(phi[t], v, acc[t][d]);
+          acc[t][d] = Mfma<T>::pv8(plo[t], v, acc[t][d]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_qk) {
+      uint4 kreg[2][NKK];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          kreg[u][kk] = *reinterpret_cast<const uint4*>(
+              reinterpret_cast<const char*>(buf_of(bk)) + u * kTileBytes + k_lane + kk * 1024);
+      f32x4_t s0[TQ], s1[TQ];
+#pragma unroll
+      for (int t = 0; t < TQ; ++t) s0[t] = s1[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) {
+          s0[t] = Mfma<T>::qk(kreg[0][kk], qr[t][kk], s0[t]);
+          s1[t] = Mfma<T>::qk(kreg[1][kk], qr[t][kk], s1[t]);
+        }
+#pragma unroll
+      for (int t = 0; t < TQ; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[t][e] = s0[t][e];
+          sv[t][4 + e] = s1[t][e];
+        }
+    }
+  };
+
+  // Vector phase of pair m: causal mask, lazy rescale (as in prefill_kernel),
+  // weights and their hi/lo split.
+  auto valu_phase = [&](int m) {
+    if (m < 0 || m >= npw) return;
+    if ((2 * m + 2) * kBlockSize - 1 > first_pos + i0) {
+      // lane part of (query position - key position) for query n of a tile
+      // and keys 4j .. of a block (recomputed here: this branch is rare)
+      const int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      const int nj = (ln & 15) - 4 * (ln >> 4);
+#pragma unroll
+      for (int t = 0; t < TQ; ++t) {
+        // key 2m*16 + 4j + k is visible to query 16t + n iff k <= dq
+        const int dq = (first_pos + i0 + kQTile * t - 2 * m * kBlockSize) + nj;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[t][e] = e <= dq ? sv[t][e] : -INFINITY;
+          sv[t][4 + e] = kBlockSize + e <= dq ? sv[t][4 + e] : -INFINITY;
+        }
+      }
+    }
+    bool over = false;
+#pragma unroll
+    for (int t = 0; t < TQ; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) over |= sv[t][e] > thr[t];
+    if (__any(over)) {
+#pragma unroll
+      for (int t = 0; t < TQ; ++t) {
+        float bm = sv[t][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[t][e]);
+        bm = max_xor16(bm);
+        bm = max_xor32(bm);
+        const float mn = fmaxf(m_run[t], bm * pr.scale_log2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - mn);
+        l_lane[t] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ar = __shfl(alpha, 4 * j + e);
+#pragma unroll
+          for (int d = 0; d < NTL; ++d) acc[t][d][e] *= ar;
+        }
+        m_run[t] = mn;
+        thr[t] = (mn + kRescaleSlack) / pr.scale_log2;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) {
+      float pe[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], pr.scale_log2, -m_run[t]));
+      l_lane[t] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+      Mfma<T>::split8(pe, phi[t], plo[t]);
+    }
+  };
+
+  // s_waitcnt immediates (expcnt left at 7): vmcnt 0 and lgkmcnt 0; vmcnt
+  // kStage with lgkmcnt not waited for (15)
+  constexpr int kWaitAll = 7 << 4;
+  constexpr int kWaitStage = kStage | (7 << 4) | (15 << 8);
+  constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  gload_lds(0, B0{});
+  gload_lds(1, B1{});
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __syncthreads();
+  // Step m: phase 2m (group 0: matrix phase of pair m; group 1: vector
+  // phase of pair m - 1), then phase 2m + 1 (group 0: vector phase of pair
+  // m; group 1: matrix phase of pair m), a barrier between them.  Pair m + 2
+  // goes into the buffer of pair m - 2, whose last reader ran in phase
+  // 2m - 1.  Each group runs its own copy of the loop (the same barriers in
+  // the same order), so neither carries the other's branches and register
+  // moves.
+  auto end_step = [&](int m) {
+    if (m + 2 < npair)
+      __builtin_amdgcn_s_waitcnt(kWaitStage);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  auto step0 = [&](int m, auto bc) {
+    constexpr int c = decltype(bc)::value;
+    gload_lds(m + 2, std::integral_constant<int, (c + 2) % 4>{});
+    mfma_phase(m, std::integral_constant<int, c>{}, std::integral_constant<int, (c + 3) % 4>{});
+    asm volatile("s_barrier" ::: "memory");
+    valu_phase(m);
+    end_step(m);
+  };
+  auto step1 = [&](int m, auto bc) {
+    constexpr int c = decltype(bc)::value;
+    gload_lds(m + 2, std::integral_constant<int, (c + 2) % 4>{});
+    valu_phase(m - 1);
+    asm volatile("s_barrier" ::: "memory");
+    mfma_phase(m, std::integral_constant<int, c>{}, std::integral_constant<int, (c + 3) % 4>{});
+    end_step(m);
+  };
+  if (grp == 0) {
+    for (int m = 0; m <= npair; m += 4) {
+      step0(m, B0{});
+      if (m + 1 <= npair) step0(m + 1, B1{});
+      if (m + 2 <= npair) step0(m + 2, B2{});
+      if (m + 3 <= npair) step0(m + 3, B3{});
+    }
+  } else {
+    for (int m = 0; m <= npair; m += 4) {
+      step1(m, B0{});
+      if (m + 1 <= npair) step1(m + 1, B1{});
+      if (m + 2 <= npair) step1(m + 2, B2{});
+      if (m + 3 <= npair) step1(m + 3, B3{});
+    }
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) {
+    float l = l_lane[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = kQTile * t + 4 * j + e;
+      const float lr = __shfl(l, 4 * j + e);
+      if (i0 + r < nq) {
+        const float inv = 1.0f / lr;
+#pragma unroll
+        for (int d = 0; d < NTL; ++d)
+          orow[static_cast<int64_t>(r) * pr.Hq * D + d * 16 + n] = acc[t][d][e] * inv;
+      }
+    }
+  }
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -691,8 +1074,11 @@ extern "C" pa_status pa_prefill(float* out, const void* q, const void* k_pool,
                 static_cast<unsigned long long>(nwg));
   const dim3 grid(static_cast<uint32_t>(nwg));
   hipStream_t s = static_cast<hipStream_t>(stream);
-#define PA_PREFILL(TAG, DIM)                                                        \
-  (wpg == 4 ? (prefill_kernel<TAG, DIM, 4, kPairTiles><<<grid, 256, 0, s>>>(pr), 0) \
+  const uint64_t nwg_pp = static_cast<uint64_t>(num_q_heads / 4) *
+                          ((pr.ntiles * kQTile + kPPQueries - 1) / kPPQueries) * num_seqs;
+  const dim3 grid_pp(static_cast<uint32_t>(nwg_pp));
+#define PA_PREFILL(TAG, DIM)                                                             \
+  (wpg == 4 ? (prefill_pp_kernel<TAG, DIM><<<grid_pp, 64 * kPPWaves, 0, s>>>(pr), 0) \
             : (prefill_kernel<TAG, DIM, 1, 1><<<grid, 64, 0, s>>>(pr), 0))
   if (dtype == PA_BF16)
     head_dim == 64 ? PA_PREFILL(BF16, 64) : PA_PREFILL(BF16, 128);
