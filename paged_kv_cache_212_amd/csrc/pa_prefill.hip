@@ -797,9 +797,11 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void prefill_pp_kernel(PrefillPar
     for (int e = 0; e < 8; ++e) sv[t][e] = 0.f;
   }
 
+  // (The phases are forced inline: each is used at eight places, and an
+  // outlined phase would take its arrays through scratch memory.)
   // Matrix phase of pair m: P.V of pair m - 1 (weights from the previous
   // vector phase), then the scores of pair m.
-  auto mfma_phase = [&](int m, auto bk, auto bv) {
+  auto mfma_phase = [&](int m, auto bk, auto bv) __attribute__((always_inline)) {
     const bool do_pv = m >= 1 && m - 1 < npw;
     const bool do_qk = m < npw;
     if (do_pv) {
@@ -873,7 +875,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void prefill_pp_kernel(PrefillPar
 
   // Vector phase of pair m: causal mask, lazy rescale (as in prefill_kernel),
   // weights and their hi/lo split.
-  auto valu_phase = [&](int m) {
+  auto valu_phase = [&](int m) __attribute__((always_inline)) {
     if (m < 0 || m >= npw) return;
     if ((2 * m + 2) * kBlockSize - 1 > first_pos + i0) {
       // lane part of (query position - key position) for query n of a tile
