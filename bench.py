@@ -310,7 +310,7 @@ def prefill_bench(args):
                       "query_tokens": B * n, "attended_pairs_per_head": attended,
                       "layers_rotated": args.layers},
            "kv_unique_bytes": kv_unique,
-           "roofline": {"kernel": "prefill_kernel (pa_prefill)", "bound": "mfma",
+           "roofline": {"kernel": "prefill_pp_kernel (pa_prefill)", "bound": "mfma",
                         "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                         "traffic": None}}
