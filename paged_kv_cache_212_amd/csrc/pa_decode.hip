@@ -70,6 +70,8 @@ struct Params {
   float out_scale;     // factor of the final rows (V scale of a quantized cache, else 1)
   float enc_k, enc_v;  // quantized cache, fused append: fp32 reciprocals of the K/V scales
   int window;          // sliding window: attend the last `window` positions (0: all)
+  int range_ticks;     // even split: cost of starting a (sequence, KV head) range, in
+                       // kUnitTicks per unit
   // Shared prefixes (pa_decode_step_shared): prefix[b] positions of sequence
   // b were attended by the prefix pass in pre_pieces key ranges, whose
   // partials are in slot p of pre_out (unnormalised weighted sums of V) and
@@ -956,14 +958,28 @@ __global__ __launch_bounds__(64, kWaves) void decode_fixed_kernel(Params pr) {
 // ---------------------------------------------------------------------------
 // Balanced split.  The work of a step is the list of units (sequence b, KV
 // head g, run of U consecutive blocks, U = the engine's step), ordered by b,
-// then g, then unit.  Sequence b owns Hkv * units(b) consecutive units.  With
-// W waves the list is cut into W equal chunks of C units (C >= kMinChunkUnits
-// steps' worth); each wave attends over its chunk, which may cover the end of
-// one (b, g) range and the start of the next.  A (b, g) range cut into
-// several chunks leaves one partial per chunk, merged by merge_kernel;
-// a range inside one chunk is written final.
+// then g, then unit.  The cut balances cost, counted in ticks: a unit costs
+// kUnitTicks, and each (b, g) range costs pr.range_ticks more at its start
+// (a wave that moves to another range mid-chunk pays about that: the row it
+// leaves, the new token at the range's end, the next range's first loads).
+// Range (b, g) occupies ticks [S, S + range_ticks + kUnitTicks * units(b)),
+// its unit k starting at tick S + range_ticks + kUnitTicks * k.  With W waves
+// the ticks are cut into chunks of C (C >= kMinChunkBlocks blocks' worth of
+// units plus one range start); wave w attends the units whose start tick lies
+// in [w * C, (w + 1) * C), which may cover the end of one (b, g) range and
+// the start of the next.  A (b, g) range cut into several chunks leaves one
+// partial per chunk, merged by merge_kernel; a range inside one chunk is
+// written final.
 // ---------------------------------------------------------------------------
 constexpr int kMinChunkBlocks = 8;
+constexpr int kUnitTicks = 8;
+// Cost of a range start.  Per-wave clocks of the Llama-3-8B batch: a wave
+// with one more range took 0.4 of a unit's time longer on 16-bit pools and
+// about one unit's time on 8-bit pools.  The values are the best of a sweep
+// of the kernel time (16-bit: Llama-3-8B, OPT-13B and copy-on-write batches;
+// 8-bit: E4M3 and INT8 pools of the Llama-3-8B batch).
+constexpr int kRangeTicks16 = 9;
+constexpr int kRangeTicksCodes = 12;
 
 // Units of U blocks of a sequence: from the block holding its first attended
 // position to its last block.
@@ -1001,11 +1017,27 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Ticks of one (b, g) range of a sequence of length L (none without units).
+template <int U>
+__device__ __forceinline__ int range_cost(int L, const Params& pr, int pre = 0) {
+  const int nub = units_of<U>(L, pr, pre);
+  return nub > 0 ? pr.range_ticks + kUnitTicks * nub : 0;
+}
+
 struct SplitPlan {
-  int total;  // units
-  int C;      // units per chunk
-  int chunks; // chunks with work
+  int total;  // ticks
+  int C;      // ticks per chunk
+  int chunks; // chunks with work (chunk w holds a unit start iff w * C <= total - kUnitTicks)
 };
+
+template <int U>
+__device__ __forceinline__ SplitPlan make_split(int total, const Params& pr, int W) {
+  SplitPlan sp;
+  sp.total = total;
+  sp.C = max(kUnitTicks * ((kMinChunkBlocks + U - 1) / U) + pr.range_ticks, (total + W - 1) / W);
+  sp.chunks = total > 0 ? (total - kUnitTicks) / sp.C + 1 : 0;
+  return sp;
+}
 
 template <int U>
 __device__ __forceinline__ SplitPlan split_plan(const Params& pr, int W) {
@@ -1013,31 +1045,26 @@ __device__ __forceinline__ SplitPlan split_plan(const Params& pr, int W) {
   int total = 0;
   for (int c = 0; c < pr.B; c += 64) {
     const int b = c + lane;
-    total += wave_sum(b < pr.B ? units_of<U>(pr.lens[b], pr, prefix_of(pr, b)) : 0);
+    total += wave_sum(b < pr.B ? range_cost<U>(pr.lens[b], pr, prefix_of(pr, b)) : 0);
   }
-  total *= pr.Hkv;
-  SplitPlan sp;
-  sp.total = total;
-  sp.C = max((kMinChunkBlocks + U - 1) / U, (total + W - 1) / W);
-  sp.chunks = (total + sp.C - 1) / sp.C;
-  return sp;
+  return make_split<U>(total * pr.Hkv, pr, W);
 }
 
-// The sequence whose units contain unit u, and the first unit of that
-// sequence (u < total).
+// The sequence whose ticks contain tick t, and the first tick of that
+// sequence (t < total).
 template <int U>
-__device__ __forceinline__ void locate(const Params& pr, int u, int& b_out, int& base_out) {
+__device__ __forceinline__ void locate(const Params& pr, int t, int& b_out, int& base_out) {
   const int lane = threadIdx.x & 63;
   int carried = 0;
   for (int c = 0; c < pr.B; c += 64) {
     const int b = c + lane;
-    const int units = (b < pr.B ? units_of<U>(pr.lens[b], pr, prefix_of(pr, b)) : 0) * pr.Hkv;
-    const int incl = carried + wave_incl_scan(units);
-    const uint64_t hit = __ballot(b < pr.B && incl > u);
+    const int cost = (b < pr.B ? range_cost<U>(pr.lens[b], pr, prefix_of(pr, b)) : 0) * pr.Hkv;
+    const int incl = carried + wave_incl_scan(cost);
+    const uint64_t hit = __ballot(b < pr.B && incl > t);
     if (hit) {
       const int k = __builtin_ctzll(hit);
       b_out = c + k;
-      base_out = __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(units, k);
+      base_out = __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(cost, k);
       return;
     }
     carried = __builtin_amdgcn_readlane(incl, 63);
@@ -1069,60 +1096,68 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
     // for the whole kernel
     lens_reg = lane < pr.B ? pr.lens[lane] : 0;
     pre_reg = (lane < pr.B && pr.prefix) ? pr.prefix[lane] : 0;
-    const int units = (lane < pr.B ? units_of<U>(lens_reg, pr, pre_reg) : 0) * pr.Hkv;
-    sp.total = wave_sum(units);
-    sp.C = max((kMinChunkBlocks + U - 1) / U, (sp.total + W - 1) / W);
-    sp.chunks = (sp.total + sp.C - 1) / sp.C;
+    const int cost = (lane < pr.B ? range_cost<U>(lens_reg, pr, pre_reg) : 0) * pr.Hkv;
+    sp = make_split<U>(wave_sum(cost), pr, W);
     if (w >= sp.chunks) return;
-    const int incl = wave_incl_scan(units);
+    const int incl = wave_incl_scan(cost);
     const uint64_t hit = __ballot(lane < pr.B && incl > w * sp.C);
     const int k = __builtin_ctzll(hit);   // hit != 0: w * C < total
     b = k;
-    base = __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(units, k);
+    base = __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(cost, k);
   } else {
     sp = split_plan<U>(pr, W);
     if (w >= sp.chunks) return;
     locate<U>(pr, w * sp.C, b, base);
   }
-  const int u_begin = w * sp.C, u_end = min(sp.total, u_begin + sp.C);
-  // A segment is the part of the chunk inside one (b, g) range.
+  const int t_begin = w * sp.C, t_end = min(sp.total, t_begin + sp.C);
+  // A segment is the part of the chunk inside one (b, g) range: its units
+  // k0 .. k1 - 1.
   struct Seg {
-    int b, g, base, L, pre, nub, range_first, seg_end, blk_begin, nblk, tok_begin, tok_end;
+    int b, g, base, L, pre, nub, rc, rstart, k0, k1, blk_begin, nblk, tok_begin, tok_end;
   };
   auto pre_of = [&](int b) {
     return pr.B <= 64 ? __builtin_amdgcn_readlane(pre_reg, b) : prefix_of(pr, b);
   };
-  auto make_seg = [&](int u, int b, int base) {
+  // units of a range from its tick offset: those starting before tick x
+  auto units_before = [](int x) { return x > 0 ? (x + kUnitTicks - 1) / kUnitTicks : 0; };
+  auto make_seg = [&](int b, int base, int g) {
     Seg sg;
     sg.b = b;
     sg.base = base;
     sg.L = len_of(pr, lens_reg, b);
     sg.pre = pre_of(b);
     sg.nub = units_of<U>(sg.L, pr, sg.pre);
-    sg.g = (u - base) / sg.nub;
-    const int q0 = (u - base) - sg.g * sg.nub;
-    sg.range_first = base + sg.g * sg.nub;                   // first unit of (b, g)
-    sg.seg_end = min(u_end, sg.range_first + sg.nub);
+    sg.rc = pr.range_ticks + kUnitTicks * sg.nub;
+    sg.g = g;
+    sg.rstart = base + g * sg.rc;
+    const int u0 = sg.rstart + pr.range_ticks;                 // start tick of unit 0
+    sg.k0 = min(sg.nub, units_before(t_begin - u0));
+    sg.k1 = min(sg.nub, units_before(t_end - u0));
     const int nblk_seq = (sg.L + kBlockSize - 1) / kBlockSize;
     sg.tok_begin = first_pos(sg.L, pr, sg.pre);
     const int fb = sg.tok_begin / kBlockSize;                  // the range's first block
-    sg.blk_begin = fb + U * q0;
-    sg.nblk = min(fb + U * (q0 + sg.seg_end - u), nblk_seq) - sg.blk_begin;
+    sg.blk_begin = fb + U * sg.k0;
+    sg.nblk = min(fb + U * sg.k1, nblk_seq) - sg.blk_begin;
     sg.tok_end = min(sg.L, (sg.blk_begin + sg.nblk) * kBlockSize);
     return sg;
   };
-  // The segment after cur (which ends before u_end).
+  // The range after cur's, from its first unit (it starts at tick
+  // cur.rstart + cur.rc: sequences without units own no ticks).
   auto next_seg = [&](const Seg& cur) {
-    int b2 = cur.b, base2 = cur.base;
-    if (cur.seg_end >= cur.base + pr.Hkv * cur.nub) {        // next sequence with work
-      base2 = cur.seg_end;
-      do {
-        ++b2;
-      } while (b2 < pr.B && units_of<U>(len_of(pr, lens_reg, b2), pr, pre_of(b2)) == 0);
-    }
-    return make_seg(cur.seg_end, b2, base2);
+    if (cur.g + 1 < pr.Hkv) return make_seg(cur.b, cur.base, cur.g + 1);
+    int b2 = cur.b;
+    do {
+      ++b2;
+    } while (b2 < pr.B && units_of<U>(len_of(pr, lens_reg, b2), pr, pre_of(b2)) == 0);
+    return make_seg(b2, cur.base + pr.Hkv * cur.rc, 0);
   };
-  Seg cur = make_seg(u_begin, b, base);
+  Seg cur = make_seg(b, base, (t_begin - base) / range_cost<U>(len_of(pr, lens_reg, b), pr,
+                                                               pre_of(b)));
+  // t_begin may lie past the last unit start of its range (in the range's
+  // tail or the next one's start ticks): then the chunk starts with the next
+  // range's unit 0 (every chunk holds a unit start: C exceeds the largest gap
+  // between two, kUnitTicks + range_ticks)
+  if (cur.k0 == cur.nub) cur = next_seg(cur);
   typename Eng::Pre pre;
   Eng::prologue(pr, cur.b, cur.g, cur.blk_begin, pre);
   // The table entries a segment checks first are made resident before the
@@ -1136,7 +1171,7 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
     // streams, so the switch costs no dependent round trip; they go out
     // once this segment's first loads are out and its start checks done
     // (a start check issued after them would wait for them too)
-    const bool more = cur.seg_end < u_end;
+    const bool more = cur.k1 == cur.nub && cur.rstart + cur.rc + pr.range_ticks < t_end;
     Seg nxt = cur;
     typename Eng::Pre pre_next;
     if (more) nxt = next_seg(cur);
@@ -1146,14 +1181,15 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
                      if (more) Eng::prologue(pr, nxt.b, nxt.g, nxt.blk_begin, pre_next);
                    });
     if (more) Eng::settle(pre_next);
-    const int first_chunk = cur.range_first / sp.C;
-    const int nslots = (cur.range_first + cur.nub - 1) / sp.C - first_chunk + 1;
+    const int u0 = cur.rstart + pr.range_ticks;
+    const int first_chunk = u0 / sp.C;
+    const int nslots = (u0 + kUnitTicks * (cur.nub - 1)) / sp.C - first_chunk + 1;
     // a sequence with a shared prefix always leaves a partial: the merge
     // folds it with the prefix pass's row
     Eng::emit(pr, cur.b, cur.g, (nslots == 1 && cur.pre == 0) ? -1 : w - first_chunk, st);
     // the wave holding the range's first unit records how many slots the
     // merge has to combine
-    if (cur.blk_begin == cur.tok_begin / kBlockSize && lane == 0)
+    if (cur.k0 == 0 && lane == 0)
       pr.counters[static_cast<int64_t>(cur.b) * pr.Hkv + cur.g] = nslots;
     if (!more) break;
     cur = nxt;
@@ -1779,6 +1815,7 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
   pr.scale_log2 = (cs ? scale * cs->k_scale : scale) * kLog2e;
   pr.out_scale = cs ? cs->v_scale : 1.0f;
   pr.window = window;
+  pr.range_ticks = code_dtype(dtype) ? kRangeTicksCodes : kRangeTicks16;
   if (shp) {
     pr.prefix = shp->prefix;
     pr.pre_out = shp->pre_out;
