@@ -71,34 +71,43 @@ class BlockManager:
         """One decode step's host work (pa_bm_step): reserve one position per
         sequence and export the tables after it.  capacity: table row length
         to try first (grown and retried when a table is longer).  Returns
-        (slots, cow pairs [n][2], tables [n][blocks needed], lens)."""
+        (slots, cow pairs [n][2], tables [n][blocks needed], lens).
+
+        The outputs are views of one fresh int32 block, laid out
+        slots (int64) | lens | pairs | tables, so a call reads one address
+        from numpy (each read costs about a microsecond) and the arrays stay
+        valid after later calls."""
         ids = seq_ids if (isinstance(seq_ids, np.ndarray) and seq_ids.dtype == np.int64
                           and seq_ids.flags.c_contiguous) else \
             np.ascontiguousarray(seq_ids, dtype=np.int64)
         n = len(ids)
         cap = max(int(capacity), 1)
-        slots = np.empty(n, dtype=np.int64)
-        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
-        lens = np.empty(n, dtype=np.int32)
         f = self._step_fn
         if f is None:
             f = self._step_fn = lib().pa_bm_step
         ncow, need = self._step_out
-        pi, ps = _ptr(ids, C.c_int64), _ptr(slots, C.c_int64)
-        pp, pl = _ptr(pairs, C.c_int32), _ptr(lens, C.c_int32)
+        pi = _ptr(ids, C.c_int64)
+        npair = max(n, 1)
+        o_lens, o_pairs = 2 * n, 3 * n                    # int32 offsets
+        o_tab = o_pairs + 2 * npair
         while True:
-            tables = np.empty((n, cap), dtype=np.int32)
-            st = f(self._h, pi, n, cap, ps, pp, self._step_ref[0], _ptr(tables, C.c_int32), pl,
-                   self._step_ref[1])
+            blk = np.empty(o_tab + n * cap, dtype=np.int32)
+            a = blk.__array_interface__["data"][0]     # 16-byte aligned: slots first
+            st = f(self._h, pi, n, cap, a, a + 4 * o_pairs, self._step_ref[0], a + 4 * o_tab,
+                   a + 4 * o_lens, self._step_ref[1])
             if st != 0 and need.value > cap:
                 cap = need.value                    # nothing changed: retry with room
                 continue
             check(st, "pa_bm_step")
             break
         nb = max(need.value, 1)
+        tables = blk[o_tab:].reshape(n, cap)
         if nb != cap:
             tables = np.ascontiguousarray(tables[:, :nb])
-        return slots, pairs[:ncow.value].copy(), tables, lens
+        slots = blk[:o_lens].view(np.int64)
+        lens = blk[o_lens:o_pairs]
+        pairs = blk[o_pairs:o_tab].reshape(npair, 2)[:ncow.value]
+        return slots, pairs, tables, lens
 
     def free_seq(self, seq_id: int):
         check(lib().pa_bm_free_seq(self._h, seq_id), "pa_bm_free_seq")
