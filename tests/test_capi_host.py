@@ -586,3 +586,31 @@ def test_pa_bm_step_width_and_argument_errors_change_nothing():
                         C.byref(need)) == PA_ERR_INVALID_ARG
     s, c, t, l = bm.step(ids, 1)
     assert t.shape == (2, 3) and l.tolist() == [33, 6] and s.tolist()[1] == t[1, 0] * 16 + 5
+
+
+def test_bm_step_outputs_stay_valid_across_calls():
+    """BlockManager.step returns views of one fresh block per call: the arrays
+    of an earlier step keep their values after later steps, have the dtypes
+    and shapes of the C outputs, and agree with append_slots/block_tables on a
+    replica manager."""
+    a = pk.BlockManager(64, 16)
+    b = pk.BlockManager(64, 16)
+    for m in (a, b):
+        m.add_seq(1, 31)
+        m.add_seq(2, 16)
+        m.fork(1, 3)
+    ids = np.array([1, 2, 3], dtype=np.int64)
+    first = a.step(ids, 1)
+    kept = [x.copy() for x in first]
+    s_b, c_b = b.append_slots(ids)
+    t_b, l_b = b.block_tables(ids, first[2].shape[1])
+    for _ in range(5):
+        a.step(ids, 4)
+    for x, y in zip(first, kept):
+        assert np.array_equal(x, y)
+    s, c, t, l = first
+    assert s.dtype == np.int64 and l.dtype == np.int32 and t.dtype == np.int32
+    assert c.dtype == np.int32 and c.ndim == 2 and c.shape[1] == 2
+    assert t.flags.c_contiguous and s.flags.c_contiguous
+    assert np.array_equal(s, s_b) and np.array_equal(c, c_b)
+    assert np.array_equal(t, t_b) and np.array_equal(l, l_b)
