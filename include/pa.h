@@ -339,6 +339,11 @@ pa_decode_kernel pa_set_decode_kernel(pa_decode_kernel kernel);
  *      fp32 and for the plain-FMA kernel;
  *   -1: the even split (matrix-core path only; fp32 and the plain-FMA kernel
  *       use 256-token partitions).
+ * The even split counts the batch's work in 32 bits: it needs
+ *   num_seqs * num_kv_heads * (12 + 8 * ceil(ceil(max_context_len / 16) / 4))
+ * below 2^30.  Beyond that, 0 gives 256-token partitions and -1 is refused
+ * (this returns -1, pa_decode_workspace_bytes 0, and the decode calls
+ * PA_ERR_UNSUPPORTED).
  * Returns the partition size in tokens for fixed partitions, 0 for the even
  * split, -1 for invalid arguments.
  *   Fixed partitions: partition p of a sequence covers tokens

@@ -1553,27 +1553,46 @@ int split_waves() {
 struct LaunchPlan {
   bool split;
   bool generic;
+  bool unfit;   // the even split was asked for and cannot count this batch's work
   int P;
   int maxP;
   int W;
 };
 
-LaunchPlan make_plan(int max_ctx, int partition_size, pa_dtype dt, bool generic_env) {
+// The even split counts the batch's work in 32-bit ticks; it is used only
+// while the largest count these sizes allow (every sequence at max_ctx)
+// stays below 2^30 (chunk ends reach up to twice the count).
+bool split_fits(int num_seqs, int num_kv_heads, int max_ctx) {
+  const int64_t max_blk = (static_cast<int64_t>(max_ctx) + kBlockSize - 1) / kBlockSize;
+  const int64_t range = std::max(kRangeTicks16, kRangeTicksCodes) + kUnitTicks * ((max_blk + 3) / 4);
+  return static_cast<int64_t>(num_seqs) * num_kv_heads * range < (int64_t{1} << 30);
+}
+
+LaunchPlan make_plan(int num_seqs, int num_kv_heads, int max_ctx, int partition_size,
+                     pa_dtype dt, bool generic_env) {
   LaunchPlan lp{};
   lp.generic = dt == PA_F32 || (generic_env && !code_dtype(dt));
-  // default (0) on the matrix-core path: the even split
+  // default (0) on the matrix-core path: the even split, unless the batch is
+  // too large for its count (then fixed partitions; asked for explicitly
+  // (-1), the call is refused)
   lp.split = (partition_size == kEvenSplit || partition_size == 0) && !lp.generic;
+  if (lp.split && !split_fits(num_seqs, num_kv_heads, max_ctx)) {
+    lp.split = false;
+    lp.unfit = partition_size == kEvenSplit;
+  }
   if (lp.split) {
     lp.W = split_waves();
     // a range of nblk blocks is cut into at most ceil(nblk / kMinChunkBlocks) + 1
     // chunks (chunks hold at least kMinChunkBlocks blocks' worth of units)
-    const int max_blk = (max_ctx + kBlockSize - 1) / kBlockSize;
+    const int64_t max_blk = (static_cast<int64_t>(max_ctx) + kBlockSize - 1) / kBlockSize;
     lp.P = 0;
-    lp.maxP = max_blk == 0 ? 1 : std::min((max_blk + kMinChunkBlocks - 1) / kMinChunkBlocks + 1,
-                                          lp.W);
+    lp.maxP = max_blk == 0 ? 1
+                           : static_cast<int>(std::min<int64_t>(
+                                 (max_blk + kMinChunkBlocks - 1) / kMinChunkBlocks + 1, lp.W));
   } else {
     lp.P = partition_size > 0 ? partition_size : kDefaultPartition;  // 0 or -1 on fp32
-    lp.maxP = max_ctx <= 0 ? 1 : (max_ctx + lp.P - 1) / lp.P;
+    lp.maxP = max_ctx <= 0 ? 1
+                           : static_cast<int>((static_cast<int64_t>(max_ctx) + lp.P - 1) / lp.P);
   }
   return lp;
 }
@@ -1781,8 +1800,13 @@ pa_status run_decode(const char* fn, Phase ph, const NewTokens* nt, const CodeSc
     return fail(PA_ERR_INVALID_ARG, "%s: NULL new-token pointer", fn);
   if (nt && ((reinterpret_cast<uintptr_t>(nt->k_new) | reinterpret_cast<uintptr_t>(nt->v_new)) & 15))
     return fail(PA_ERR_INVALID_ARG, "%s: k_new and v_new must be 16-byte aligned", fn);
-  const LaunchPlan lp = make_plan(max_context_len, partition_size, dtype,
+  const LaunchPlan lp = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size, dtype,
                                   generic_selected());
+  if (lp.unfit)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: %d sequences x %d KV heads up to %d positions exceed the even split's "
+                "32-bit work count; give a partition size",
+                fn, num_seqs, num_kv_heads, max_context_len);
   if (shp && !lp.split)
     return fail(PA_ERR_UNSUPPORTED, "%s: shared prefixes need the even split on the matrix cores",
                 fn);
@@ -1946,8 +1970,10 @@ extern "C" int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_head
   if (!decode_args_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                       partition_size, dtype))
     return -1;
-  return make_plan(max_context_len, partition_size, dtype, generic_selected())
-      .P;
+  const LaunchPlan lp =
+      make_plan(num_seqs, num_kv_heads, max_context_len, partition_size, dtype,
+                generic_selected());
+  return lp.unfit ? -1 : lp.P;
 }
 
 extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -1957,8 +1983,9 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
   if (!decode_args_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                       partition_size, dtype))
     return 0;
-  const LaunchPlan lp =
-      make_plan(max_context_len, partition_size, dtype, generic_selected());
+  const LaunchPlan lp = make_plan(num_seqs, num_kv_heads, max_context_len, partition_size,
+                                  dtype, generic_selected());
+  if (lp.unfit) return 0;
   return workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, lp.maxP);
 }
 

@@ -226,6 +226,22 @@ def test_workspace_and_partition_queries():
     assert h.pa_decode_partition_size(64, 40, 8, 64, 2048, 0, PA_F16) == 0
     assert h.pa_decode_partition_size(64, 128, 8, 128, 2048, 0, PA_F16) == 0
     assert h.pa_decode_partition_size(64, 136, 8, 128, 2048, 0, PA_F16) == -1
+    # the even split counts the batch's work in 32 bits (below 2^30 ticks:
+    # 8 per 4-block unit plus at most 12 per (sequence, KV head) range).
+    # Beyond that the default falls back to fixed partitions and an explicit
+    # even split is refused, with no workspace size.
+    units = lambda ctx: (-(-ctx // 16) + 3) // 4  # noqa: E731
+    assert 65535 * 64 * (12 + 8 * units(131072)) >= 1 << 30
+    assert h.pa_decode_partition_size(65535, 64, 64, 128, 131072, 0, PA_BF16) == 256
+    assert h.pa_decode_partition_size(65535, 64, 64, 128, 131072, -1, PA_BF16) == -1
+    assert h.pa_decode_partition_size(65535, 64, 64, 128, 131072, -1, PA_FP8_E4M3) == -1
+    assert h.pa_decode_workspace_bytes(65535, 64, 64, 128, 131072, -1, PA_BF16) == 0
+    assert h.pa_decode_workspace_bytes(65535, 64, 64, 128, 131072, 0, PA_BF16) > 0
+    assert 16 * 8 * (12 + 8 * units(131072)) < 1 << 30     # the long-context batch fits
+    assert h.pa_decode_partition_size(16, 32, 8, 128, 131072, -1, PA_BF16) == 0
+    # max_context_len near the int32 limit: the plan's arithmetic is 64-bit
+    assert h.pa_decode_partition_size(1, 1, 1, 128, 2**31 - 1, 0, PA_BF16) == 0
+    assert h.pa_decode_partition_size(1, 1, 1, 128, 2**31 - 1, 256, PA_BF16) == 256
     # one partition -> no workspace
     assert h.pa_decode_workspace_bytes(4, 8, 2, 64, 256, 512, PA_F32) == 0
     # 3 partitions of 512: m, l and acc rows, each region 256-byte aligned
