@@ -44,13 +44,9 @@
 #include "pa_mfma.h"
 
 namespace pa {
-namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kQTile = 16;     // query tokens per tile
-constexpr int kPairTiles = 2;  // tiles per wave with four query heads per workgroup
-constexpr float kRescaleSlack = 8.f;  // log2-domain headroom before the running max moves
-
+// The arguments of both prefill kernels (also handed to the ping-pong
+// kernel's launcher, which lives in pa_prefill_pp.hip).
 struct PrefillParams {
   float* out;               // [T][Hq][D]
   const void* q;            // [T][Hq][D]
@@ -85,6 +81,19 @@ struct PrefillParams {
   int num_seqs;
   int pieces;
 };
+
+// Launches prefill_pp_kernel<T, D> (defined below; instantiated in
+// pa_prefill_pp.hip, which the build compiles with its own scheduling
+// strategy).
+template <typename T, int D>
+void launch_prefill_pp(dim3 grid, hipStream_t s, const PrefillParams& pr);
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQTile = 16;     // query tokens per tile
+constexpr int kPairTiles = 2;  // tiles per wave with four query heads per workgroup
+constexpr float kRescaleSlack = 8.f;  // log2-domain headroom before the running max moves
 
 // LDS slot of V chunk c: the low three bits XORed with bits 4..6 (an
 // involution that permutes each group of 16 chunks).
@@ -1012,6 +1021,21 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void prefill_pp_kernel(PrefillPar
 }  // namespace
 }  // namespace pa
 
+#ifdef PA_PREFILL_PP_TU
+// Second translation unit (pa_prefill_pp.hip): the ping-pong kernel's
+// launcher and its instances only.
+namespace pa {
+template <typename T, int D>
+void launch_prefill_pp(dim3 grid, hipStream_t s, const PrefillParams& pr) {
+  prefill_pp_kernel<T, D><<<grid, 64 * kPPWaves, 0, s>>>(pr);
+}
+template void launch_prefill_pp<BF16, 64>(dim3, hipStream_t, const PrefillParams&);
+template void launch_prefill_pp<BF16, 128>(dim3, hipStream_t, const PrefillParams&);
+template void launch_prefill_pp<F16, 64>(dim3, hipStream_t, const PrefillParams&);
+template void launch_prefill_pp<F16, 128>(dim3, hipStream_t, const PrefillParams&);
+}  // namespace pa
+#else
+
 using namespace pa;
 
 extern "C" pa_status pa_prefill(float* out, const void* q, const void* k_pool,
@@ -1080,7 +1104,7 @@ extern "C" pa_status pa_prefill(float* out, const void* q, const void* k_pool,
                           ((pr.ntiles * kQTile + kPPQueries - 1) / kPPQueries) * num_seqs;
   const dim3 grid_pp(static_cast<uint32_t>(nwg_pp));
 #define PA_PREFILL(TAG, DIM)                                                             \
-  (wpg == 4 ? (prefill_pp_kernel<TAG, DIM><<<grid_pp, 64 * kPPWaves, 0, s>>>(pr), 0) \
+  (wpg == 4 ? (launch_prefill_pp<TAG, DIM>(grid_pp, s, pr), 0)                       \
             : (prefill_kernel<TAG, DIM, 1, 1><<<grid, 64, 0, s>>>(pr), 0))
   if (dtype == PA_BF16)
     head_dim == 64 ? PA_PREFILL(BF16, 64) : PA_PREFILL(BF16, 128);
@@ -1173,3 +1197,5 @@ pa_status launch_shared_prefix(float* pre_out, float* pre_ml, uint32_t* pre_stam
 }
 
 }  // namespace pa
+
+#endif  // PA_PREFILL_PP_TU
