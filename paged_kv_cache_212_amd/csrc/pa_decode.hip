@@ -969,7 +969,10 @@ __global__ __launch_bounds__(64, kWaves) void decode_fixed_kernel(Params pr) {
 // in [w * C, (w + 1) * C), which may cover the end of one (b, g) range and
 // the start of the next.  A (b, g) range cut into several chunks leaves one
 // partial per chunk, merged by merge_kernel; a range inside one chunk is
-// written final.
+// written final.  When every range has the same number of units (decode
+// steps of beams or samples of equal length), the cut instead gives each
+// range k chunks exactly (chunk and range boundaries then coincide: no wave
+// changes range), by choosing the start charge and C for it.
 // ---------------------------------------------------------------------------
 constexpr int kMinChunkBlocks = 8;
 constexpr int kUnitTicks = 8;
@@ -1017,48 +1020,95 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Ticks of one (b, g) range of a sequence of length L (none without units).
+// Ticks of one (b, g) range of a sequence of length L (none without units),
+// rt ticks charged at its start.
 template <int U>
-__device__ __forceinline__ int range_cost(int L, const Params& pr, int pre = 0) {
+__device__ __forceinline__ int range_cost(int L, int rt, const Params& pr, int pre = 0) {
   const int nub = units_of<U>(L, pr, pre);
-  return nub > 0 ? pr.range_ticks + kUnitTicks * nub : 0;
+  return nub > 0 ? rt + kUnitTicks * nub : 0;
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
 }
 
 struct SplitPlan {
   int total;  // ticks
   int C;      // ticks per chunk
   int chunks; // chunks with work (chunk w holds a unit start iff w * C <= total - kUnitTicks)
+  int rt;     // ticks charged at each range's start
+};
+
+// The batch's units: sequences with work, all their units, and the least and
+// most units of one of their ranges.
+struct UnitStats {
+  int nseq = 0, units = 0, umin = 0x7fffffff, umax = 0;
+  __device__ void add(int nub) {   // one lane's sequence (wave-uniform result)
+    nseq += wave_sum(nub > 0 ? 1 : 0);
+    units += wave_sum(nub);
+    umin = min(umin, wave_min(nub > 0 ? nub : 0x7fffffff));
+    umax = max(umax, wave_max(nub));
+  }
 };
 
 template <int U>
-__device__ __forceinline__ SplitPlan make_split(int total, const Params& pr, int W) {
+__device__ __forceinline__ SplitPlan make_split(const UnitStats& us, const Params& pr, int W) {
+  constexpr int kMinUnits = (kMinChunkBlocks + U - 1) / U;
   SplitPlan sp;
-  sp.total = total;
-  sp.C = max(kUnitTicks * ((kMinChunkBlocks + U - 1) / U) + pr.range_ticks, (total + W - 1) / W);
-  sp.chunks = total > 0 ? (total - kUnitTicks) / sp.C + 1 : 0;
+  const int nranges = us.nseq * pr.Hkv;
+  if (nranges > 0 && us.umin == us.umax) {
+    // every range has nub units: k chunks of u units per range, the first
+    // u*k - nub of them charged at the range's start, so that a range is
+    // exactly k chunks; taken when it keeps 7/8 of the waves busy
+    const int nub = us.umax;
+    for (int k = min(W / nranges, nub / kMinUnits); k >= 2; --k) {
+      const int u = (nub + k - 1) / k;
+      if (u * k - nub < u && 8 * nranges * k >= 7 * W &&
+          static_cast<int64_t>(nranges) * kUnitTicks * u * k < (int64_t{1} << 30)) {
+        sp.rt = kUnitTicks * (u * k - nub);
+        sp.C = kUnitTicks * u;
+        sp.total = nranges * kUnitTicks * u * k;
+        sp.chunks = (sp.total - kUnitTicks) / sp.C + 1;   // nranges * k
+        return sp;
+      }
+    }
+  }
+  sp.rt = pr.range_ticks;
+  sp.total = (kUnitTicks * us.units + sp.rt * us.nseq) * pr.Hkv;
+  sp.C = max(kUnitTicks * kMinUnits + sp.rt, (sp.total + W - 1) / W);
+  sp.chunks = sp.total > 0 ? (sp.total - kUnitTicks) / sp.C + 1 : 0;
   return sp;
 }
 
 template <int U>
 __device__ __forceinline__ SplitPlan split_plan(const Params& pr, int W) {
   const int lane = threadIdx.x & 63;
-  int total = 0;
+  UnitStats us;
   for (int c = 0; c < pr.B; c += 64) {
     const int b = c + lane;
-    total += wave_sum(b < pr.B ? range_cost<U>(pr.lens[b], pr, prefix_of(pr, b)) : 0);
+    us.add(b < pr.B ? units_of<U>(pr.lens[b], pr, prefix_of(pr, b)) : 0);
   }
-  return make_split<U>(total * pr.Hkv, pr, W);
+  return make_split<U>(us, pr, W);
 }
 
 // The sequence whose ticks contain tick t, and the first tick of that
 // sequence (t < total).
 template <int U>
-__device__ __forceinline__ void locate(const Params& pr, int t, int& b_out, int& base_out) {
+__device__ __forceinline__ void locate(const Params& pr, int rt, int t, int& b_out,
+                                       int& base_out) {
   const int lane = threadIdx.x & 63;
   int carried = 0;
   for (int c = 0; c < pr.B; c += 64) {
     const int b = c + lane;
-    const int cost = (b < pr.B ? range_cost<U>(pr.lens[b], pr, prefix_of(pr, b)) : 0) * pr.Hkv;
+    const int cost =
+        (b < pr.B ? range_cost<U>(pr.lens[b], rt, pr, prefix_of(pr, b)) : 0) * pr.Hkv;
     const int incl = carried + wave_incl_scan(cost);
     const uint64_t hit = __ballot(b < pr.B && incl > t);
     if (hit) {
@@ -1096,8 +1146,11 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
     // for the whole kernel
     lens_reg = lane < pr.B ? pr.lens[lane] : 0;
     pre_reg = (lane < pr.B && pr.prefix) ? pr.prefix[lane] : 0;
-    const int cost = (lane < pr.B ? range_cost<U>(lens_reg, pr, pre_reg) : 0) * pr.Hkv;
-    sp = make_split<U>(wave_sum(cost), pr, W);
+    const int nub = lane < pr.B ? units_of<U>(lens_reg, pr, pre_reg) : 0;
+    UnitStats us;
+    us.add(nub);
+    sp = make_split<U>(us, pr, W);
+    const int cost = (nub > 0 ? sp.rt + kUnitTicks * nub : 0) * pr.Hkv;
     if (w >= sp.chunks) return;
     const int incl = wave_incl_scan(cost);
     const uint64_t hit = __ballot(lane < pr.B && incl > w * sp.C);
@@ -1107,7 +1160,7 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
   } else {
     sp = split_plan<U>(pr, W);
     if (w >= sp.chunks) return;
-    locate<U>(pr, w * sp.C, b, base);
+    locate<U>(pr, sp.rt, w * sp.C, b, base);
   }
   const int t_begin = w * sp.C, t_end = min(sp.total, t_begin + sp.C);
   // A segment is the part of the chunk inside one (b, g) range: its units
@@ -1127,10 +1180,10 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
     sg.L = len_of(pr, lens_reg, b);
     sg.pre = pre_of(b);
     sg.nub = units_of<U>(sg.L, pr, sg.pre);
-    sg.rc = pr.range_ticks + kUnitTicks * sg.nub;
+    sg.rc = sp.rt + kUnitTicks * sg.nub;
     sg.g = g;
     sg.rstart = base + g * sg.rc;
-    const int u0 = sg.rstart + pr.range_ticks;                 // start tick of unit 0
+    const int u0 = sg.rstart + sp.rt;                          // start tick of unit 0
     sg.k0 = min(sg.nub, units_before(t_begin - u0));
     sg.k1 = min(sg.nub, units_before(t_end - u0));
     const int nblk_seq = (sg.L + kBlockSize - 1) / kBlockSize;
@@ -1151,8 +1204,8 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
     } while (b2 < pr.B && units_of<U>(len_of(pr, lens_reg, b2), pr, pre_of(b2)) == 0);
     return make_seg(b2, cur.base + pr.Hkv * cur.rc, 0);
   };
-  Seg cur = make_seg(b, base, (t_begin - base) / range_cost<U>(len_of(pr, lens_reg, b), pr,
-                                                               pre_of(b)));
+  Seg cur = make_seg(b, base, (t_begin - base) / range_cost<U>(len_of(pr, lens_reg, b), sp.rt,
+                                                               pr, pre_of(b)));
   // t_begin may lie past the last unit start of its range (in the range's
   // tail or the next one's start ticks): then the chunk starts with the next
   // range's unit 0 (every chunk holds a unit start: C exceeds the largest gap
@@ -1171,7 +1224,7 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
     // streams, so the switch costs no dependent round trip; they go out
     // once this segment's first loads are out and its start checks done
     // (a start check issued after them would wait for them too)
-    const bool more = cur.k1 == cur.nub && cur.rstart + cur.rc + pr.range_ticks < t_end;
+    const bool more = cur.k1 == cur.nub && cur.rstart + cur.rc + sp.rt < t_end;
     Seg nxt = cur;
     typename Eng::Pre pre_next;
     if (more) nxt = next_seg(cur);
@@ -1181,7 +1234,7 @@ __global__ __launch_bounds__(256, kWaves) void decode_split_kernel(Params pr) {
                      if (more) Eng::prologue(pr, nxt.b, nxt.g, nxt.blk_begin, pre_next);
                    });
     if (more) Eng::settle(pre_next);
-    const int u0 = cur.rstart + pr.range_ticks;
+    const int u0 = cur.rstart + sp.rt;
     const int first_chunk = u0 / sp.C;
     const int nslots = (u0 + kUnitTicks * (cur.nub - 1)) / sp.C - first_chunk + 1;
     // a sequence with a shared prefix always leaves a partial: the merge
